@@ -1,0 +1,333 @@
+/*
+ * oracle.c -- plain CPU oracle for the b-bit weight-only quantized linear
+ * layer (WNA16) and its int8-activation variant (W4A8).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library; the GPU library never
+ * does, and the two share no source, header or table.  Everything here is
+ * written for obviousness, not speed: the bitstream is read and written one
+ * bit at a time, arithmetic is fp64 (the int8 activation step is fp32
+ * because that step is defined in fp32, see below), loops are naive.
+ *
+ * Definitions followed (page title, then section):
+ *
+ *  - Packing.  "Qwen3.8-27B-INT6-Mixed-AutoRound" model card, Findings: the
+ *    compressed-tensors pack-quantized layout is dense along in_features,
+ *    ceil(in_features * bits / 32) 32-bit words per output row, so codes of
+ *    5/6/7 bits straddle word boundaries, while the older per-word formula
+ *    (32 // bits codes per word, no straddling) only agrees for widths that
+ *    divide 32.  Reading taken here: stream bit i of a row is bit (i % 32) of
+ *    word i / 32 (little-endian words, so also bit i % 8 of byte i / 8); code
+ *    k occupies stream bits [k*b, k*b + b), least significant bit first;
+ *    each row is its own stream, zero-padded to a whole word.
+ *
+ *  - Symmetric groups.  Same model card, Findings: above four bits there is
+ *    no zero point, so every group is symmetric.  Reading: the signed value
+ *    of an unsigned code c is q = c - 2^(b-1); one scale per group of 128
+ *    consecutive input features (the G128 grouping of "vLLM Quantization",
+ *    Qwen3-8B demo); negative scales are legal (club-3090 discussion #733,
+ *    "Under the hood").
+ *
+ *  - The layer's result.  "vLLM Can Run INT5-7", section 2: variants are
+ *    compared by dequantizing the weights and running the same F.linear, so
+ *    y = A . dequant(W)^T with W of shape [out_features N, in_features K],
+ *    no bias.  Here dequant is done in fp64 and the sum is exact-as-fp64.
+ *
+ *  - W4A8.  club-3090 discussion #733, "Under the hood": activations are
+ *    quantized per token to int8 at run time, int4 weights are widened to
+ *    int8 without loss, the product runs on int8 units.  Reading taken
+ *    (the page gives no formula): s_a = amax_k |a| / 127 in fp32 with IEEE
+ *    division, Aq = clamp(rint(a / s_a), -127, 127) with ties to even, a
+ *    zero row gives s_a = 0 and Aq = 0; per group of 128 the int products
+ *    are summed exactly, then scaled by the group scale, summed over groups
+ *    and scaled by s_a.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_ABI 1
+
+int oracle_abi(void) { return ORACLE_ABI; }
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* 1 on a little-endian host; the byte view of the u32 words relies on it. */
+int oracle_little_endian(void) {
+    const uint32_t probe = 1u;
+    return *(const uint8_t *)&probe == 1u;
+}
+
+int64_t oracle_words_per_row(int64_t K, int b) {
+    return (K * (int64_t)b + 31) / 32;
+}
+
+/* bf16 bit pattern -> double, exactly (bf16 is the top half of an fp32). */
+static double bf16_to_double(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static float bf16_to_float(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Read stream bit i of a row given as bytes. */
+static unsigned get_bit(const uint8_t *row, int64_t i) {
+    return (row[i >> 3] >> (i & 7)) & 1u;
+}
+
+static void set_bit(uint8_t *row, int64_t i) {
+    row[i >> 3] = (uint8_t)(row[i >> 3] | (1u << (i & 7)));
+}
+
+/* Code k of a row: stream bits [k*b, k*b+b), LSB first. */
+static unsigned read_code(const uint8_t *row, int64_t k, int b) {
+    unsigned c = 0;
+    for (int j = 0; j < b; ++j)
+        c |= get_bit(row, k * b + j) << j;
+    return c;
+}
+
+/* codes uint8 [N,K] -> packed u32 [N, words_per_row].  Returns 0, or -1 when
+ * a code does not fit in b bits, or the host is not little-endian. */
+int oracle_pack(const uint8_t *codes, int64_t N, int64_t K, int b, uint32_t *packed) {
+    if (!oracle_little_endian()) return -1;
+    const int64_t W = oracle_words_per_row(K, b);
+    for (int64_t n = 0; n < N; ++n) {
+        uint8_t *row = (uint8_t *)(packed + n * W);
+        memset(row, 0, (size_t)W * 4);
+        for (int64_t k = 0; k < K; ++k) {
+            unsigned c = codes[n * K + k];
+            if (c >> b) return -1;
+            for (int j = 0; j < b; ++j)
+                if ((c >> j) & 1u) set_bit(row, k * b + j);
+        }
+    }
+    return 0;
+}
+
+/* packed u32 [N, words_per_row] -> codes uint8 [N,K]. */
+int oracle_unpack(const uint32_t *packed, int64_t N, int64_t K, int b, uint8_t *codes) {
+    if (!oracle_little_endian()) return -1;
+    const int64_t W = oracle_words_per_row(K, b);
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *row = (const uint8_t *)(packed + n * W);
+        for (int64_t k = 0; k < K; ++k)
+            codes[n * K + k] = (uint8_t)read_code(row, k, b);
+    }
+    return 0;
+}
+
+/* Row n dequantized to fp64: w[k] = s[n, k/group] * (c[n,k] - 2^(b-1)). */
+static void dequant_row(const uint32_t *packed, const uint16_t *scales, int64_t n,
+                        int64_t K, int b, int group, double *w) {
+    const int64_t W = oracle_words_per_row(K, b);
+    const int64_t G = K / group;
+    const uint8_t *row = (const uint8_t *)(packed + n * W);
+    const int zero = 1 << (b - 1);
+    for (int64_t k = 0; k < K; ++k) {
+        const int q = (int)read_code(row, k, b) - zero;
+        w[k] = bf16_to_double(scales[n * G + k / group]) * (double)q;
+    }
+}
+
+/* y[m,n] = sum_k A[m,k] * w[n,k] and mag[m,n] = sum_k |A[m,k] * w[n,k]|,
+ * both fp64, outputs [M, N] row-major.  mag may be NULL. */
+int oracle_wna16(const uint16_t *A, int64_t M, int64_t N, int64_t K,
+                 const uint32_t *packed, const uint16_t *scales, int b, int group,
+                 double *y, double *mag) {
+    if (!oracle_little_endian() || b < 1 || b > 8 || group <= 0 || K % group) return -1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc((size_t)K * sizeof(double));
+        if (!w) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t n = 0; n < N; ++n) {
+            if (!w) continue;
+            dequant_row(packed, scales, n, K, b, group, w);
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0, acc_abs = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const double t = bf16_to_double(A[m * K + k]) * w[k];
+                    acc += t;
+                    acc_abs += fabs(t);
+                }
+                y[m * N + n] = acc;
+                if (mag) mag[m * N + n] = acc_abs;
+            }
+        }
+        free(w);
+    }
+    return err;
+}
+
+/* The same sums at P chosen output positions (m_idx[p], n_idx[p]). */
+int oracle_wna16_points(const uint16_t *A, int64_t M, int64_t N, int64_t K,
+                        const uint32_t *packed, const uint16_t *scales, int b, int group,
+                        const int64_t *m_idx, const int64_t *n_idx, int64_t P,
+                        double *y, double *mag) {
+    if (!oracle_little_endian() || b < 1 || b > 8 || group <= 0 || K % group) return -1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t p = 0; p < P; ++p) {
+            const int64_t m = m_idx[p], n = n_idx[p];
+            if (!w || m < 0 || m >= M || n < 0 || n >= N) {
+#pragma omp atomic write
+                err = -1;
+                continue;
+            }
+            dequant_row(packed, scales, n, K, b, group, w);
+            double acc = 0.0, acc_abs = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double t = bf16_to_double(A[m * K + k]) * w[k];
+                acc += t;
+                acc_abs += fabs(t);
+            }
+            y[p] = acc;
+            if (mag) mag[p] = acc_abs;
+        }
+        free(w);
+    }
+    return err;
+}
+
+/* Per-token int8 activation quantization, fp32:
+ * s_a[m] = max_k |A[m,k]| / 127;  Aq = clamp(rint(A / s_a), -127, 127);
+ * a row of zeros gives s_a = 0 and Aq = 0. */
+int oracle_quant_act_i8(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq, float *sa) {
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = fabsf(bf16_to_float(A[m * K + k]));
+            if (v > amax) amax = v;
+        }
+        const float s = amax / 127.0f;
+        sa[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t qv = 0;
+            if (amax > 0.0f) {
+                float r = rintf(bf16_to_float(A[m * K + k]) / s);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                qv = (int8_t)r;
+            }
+            Aq[m * K + k] = qv;
+        }
+    }
+    return 0;
+}
+
+/* One W4A8 output from an already quantized activation row:
+ * y = s_a * sum_g s[n,g] * (sum_{k in g} Aq[k] * (c[n,k] - 8)),
+ * with the inner sums exact in int64 (they must fit int32) and the rest fp64. */
+static int w4a8_dot(const int8_t *aq_row, float sa, const uint8_t *codes_row,
+                    const uint16_t *s_row, int64_t K, int group, double *y, double *mag) {
+    double acc = 0.0, acc_abs = 0.0;
+    for (int64_t g = 0; g < K / group; ++g) {
+        int64_t ig = 0;
+        for (int64_t k = g * group; k < (g + 1) * group; ++k)
+            ig += (int64_t)aq_row[k] * ((int64_t)codes_row[k] - 8);
+        if (ig > INT32_MAX || ig < INT32_MIN) return -3;
+        const double t = bf16_to_double(s_row[g]) * (double)ig;
+        acc += t;
+        acc_abs += fabs(t);
+    }
+    *y = (double)sa * acc;
+    if (mag) *mag = fabs((double)sa) * acc_abs;
+    return 0;
+}
+
+static void unpack_row(const uint32_t *packed, int64_t n, int64_t K, int b, uint8_t *out) {
+    const uint8_t *row = (const uint8_t *)(packed + n * oracle_words_per_row(K, b));
+    for (int64_t k = 0; k < K; ++k) out[k] = (uint8_t)read_code(row, k, b);
+}
+
+/* Full W4A8 layer (b = 4).  Aq [M,K] and sa [M] are written too (caller
+ * provides them).  y, mag: [M, N] fp64. */
+int oracle_w4a8(const uint16_t *A, int64_t M, int64_t N, int64_t K,
+                const uint32_t *packed, const uint16_t *scales, int group,
+                int8_t *Aq, float *sa, double *y, double *mag) {
+    if (!oracle_little_endian() || group <= 0 || K % group) return -1;
+    oracle_quant_act_i8(A, M, K, Aq, sa);
+    const int64_t G = K / group;
+    int err = 0;
+#pragma omp parallel
+    {
+        uint8_t *c = (uint8_t *)malloc((size_t)K);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t n = 0; n < N; ++n) {
+            if (!c) {
+#pragma omp atomic write
+                err = -2;
+                continue;
+            }
+            unpack_row(packed, n, K, 4, c);
+            for (int64_t m = 0; m < M; ++m) {
+                int r = w4a8_dot(Aq + m * K, sa[m], c, scales + n * G, K, group,
+                                 &y[m * N + n], mag ? &mag[m * N + n] : NULL);
+                if (r) {
+#pragma omp atomic write
+                    err = r;
+                }
+            }
+        }
+        free(c);
+    }
+    return err;
+}
+
+/* W4A8 at P chosen output positions; Aq/sa must come from
+ * oracle_quant_act_i8 on the same A. */
+int oracle_w4a8_points(const int8_t *Aq, const float *sa, int64_t M, int64_t N, int64_t K,
+                       const uint32_t *packed, const uint16_t *scales, int group,
+                       const int64_t *m_idx, const int64_t *n_idx, int64_t P,
+                       double *y, double *mag) {
+    if (!oracle_little_endian() || group <= 0 || K % group) return -1;
+    const int64_t G = K / group;
+    int err = 0;
+#pragma omp parallel
+    {
+        uint8_t *c = (uint8_t *)malloc((size_t)K);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t p = 0; p < P; ++p) {
+            const int64_t m = m_idx[p], n = n_idx[p];
+            if (!c || m < 0 || m >= M || n < 0 || n >= N) {
+#pragma omp atomic write
+                err = -1;
+                continue;
+            }
+            unpack_row(packed, n, K, 4, c);
+            int r = w4a8_dot(Aq + m * K, sa[m], c, scales + n * G, K, group,
+                             &y[p], mag ? &mag[p] : NULL);
+            if (r) {
+#pragma omp atomic write
+                err = r;
+            }
+        }
+        free(c);
+    }
+    return err;
+}
