@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Throughput of the WNA16 quantized linear layer on one MI355X.
+
+Headline (one JSON line on stdout): wq_gemm decode throughput at M = 1,
+K = 5120, N = 17408, b = 5, 6 and 7, in TB/s of algorithmic bytes (packed codes
++ bf16 scales + activations + output).  One step = one wq_gemm call for each
+of the three bit widths.  Weights are the tiled (repacked) layout, rotated over
+--copies device copies per bit width so that the 256 MB Infinity Cache cannot
+serve them; activations and workspaces are resident in HBM before timing.
+The timed steps are captured in one HIP graph and replayed (12 us kernels would
+otherwise measure Python launch overhead).
+
+Also reported on the same line:
+  roofline      the b = 6 decode kernel: algorithmic bytes per launch over its
+                average duration (HIP events on the launch stream), against the
+                8 TB/s HBM peak;
+  cpu_baseline  the CPU oracle (fp64, OpenMP) on the same decode layers;
+  prefill       TFLOP/s of wq_gemm at M = 4096 (up: K 5120 -> N 17408, down:
+                K 17408 -> N 5120, b = 6) against the 2.5 PFLOP/s bf16 peak;
+  w4a8          TOP/s of wq_gemm_a8 at M = 2048 / 8192 (K 5120, N 17408) against
+                the 5.0 POPS int8 peak, with wq_gemm at b = 4 on the same shape.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
+DECODE_N, DECODE_K = 17408, 5120
+DECODE_BITS = (5, 6, 7)
+
+
+def log(msg: str):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(M: int, N: int, K: int, b: int) -> int:
+    return N * (K * b // 32) * 4 + N * (K // 128) * 2 + M * K * 2 + M * N * 2
+
+
+class DecodeLayer:
+    def __init__(self, b: int, copies: int, torch, wq, synth):
+        w = synth.decode(M=1, b=b, N=DECODE_N, K=DECODE_K)
+        self.b, self.w = b, w
+        packed = wq.wq_pack(w.codes, b)
+        packed_d = torch.from_numpy(packed.view(np.int32)).cuda()
+        scales_d = torch.from_numpy(w.scales.view(np.int16)).cuda().view(torch.bfloat16)
+        blob = wq.wq_repack(packed_d, scales_d, w.K, b)
+        self.blobs = [blob] + [blob.clone() for _ in range(copies - 1)]
+        del packed_d, scales_d
+        self.A = torch.from_numpy(w.A.view(np.int16)).cuda().view(torch.bfloat16)
+        self.Y = torch.empty((1, w.N), dtype=torch.bfloat16, device="cuda")
+        nbytes = wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, w.N, w.K, b)
+        self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        self.bytes = algorithmic_bytes(1, w.N, w.K, b)
+
+    def call(self, wq, i: int):
+        wq.wq_gemm(self.A, self.blobs[i % len(self.blobs)], wq.WQ_LAYOUT_TILED, None, self.w.N,
+                   self.b, Y=self.Y, ws=self.ws)
+
+
+def graph_time(torch, fn, reps: int, warmup: int) -> float:
+    """Capture fn() once, replay warmup + reps times; seconds per replay."""
+    fn()  # first call outside capture (device checks, lazy init)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3 / reps
+
+
+def cpu_baseline(oracle, synth, target_s: float):
+    """The oracle on the same decode step (b = 5, 6, 7 at M = 1), repeated
+    until target_s seconds of CPU time have passed."""
+    layers = []
+    for b in DECODE_BITS:
+        w = synth.decode(M=1, b=b, N=DECODE_N, K=DECODE_K)
+        layers.append((w, oracle.pack(w.codes, b)))
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        for w, p in layers:
+            oracle.wna16(w.A, p, w.scales, w.b)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    total = sum(algorithmic_bytes(1, w.N, w.K, w.b) for w, _ in layers)
+    return {"value": total * steps / el / 1e12, "unit": "TB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d full decode steps (M=1, K=5120, N=17408, b=5/6/7) in %.1f s, fp64"
+                      % (steps, el)}
+
+
+def bench_prefill(torch, wq, synth, reps: int):
+    out = {}
+    for name, (K, N) in (("up", (5120, 17408)), ("down", (17408, 5120))):
+        w = synth.prefill(M=4096, N=N, K=K, b=6)
+        packed = wq.wq_pack(w.codes, 6)
+        blob = wq.wq_repack(torch.from_numpy(packed.view(np.int32)).cuda(),
+                            torch.from_numpy(w.scales.view(np.int16)).cuda().view(torch.bfloat16),
+                            K, 6)
+        A = torch.from_numpy(w.A.view(np.int16)).cuda().view(torch.bfloat16)
+        Y = torch.empty((w.M, N), dtype=torch.bfloat16, device="cuda")
+
+        def fn():
+            wq.wq_gemm(A, blob, wq.WQ_LAYOUT_TILED, None, N, 6, Y=Y)
+
+        t = graph_time(torch, fn, reps, 2)
+        tf = 2.0 * w.M * N * K / t / 1e12
+        out[name] = {"M": w.M, "N": N, "K": K, "b": 6, "ms": t * 1e3, "TFLOP/s": tf,
+                     "frac_of_peak": tf / BF16_PEAK_TFLOPS}
+        del blob, A, Y
+    return out
+
+
+def bench_w4a8(torch, wq, synth, reps: int):
+    out = {}
+    w0 = synth.w4a8(M=16)
+    packed = wq.wq_pack(w0.codes, 4)
+    blob = wq.wq_repack(torch.from_numpy(packed.view(np.int32)).cuda(),
+                        torch.from_numpy(w0.scales.view(np.int16)).cuda().view(torch.bfloat16),
+                        w0.K, 4)
+    rng = np.random.default_rng(3)
+    for M in (2048, 8192):
+        A_bits = synth.draw_act(rng, M, w0.K, outlier_frac=0.01)
+        A = torch.from_numpy(A_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        Y = torch.empty((M, w0.N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.zeros(wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, M, w0.N, w0.K, 4),
+                         dtype=torch.uint8, device="cuda")
+
+        def f8():
+            wq.wq_gemm_a8(A, blob, wq.WQ_LAYOUT_TILED, None, w0.N, 4, Y=Y, ws=ws)
+
+        def f16():
+            wq.wq_gemm(A, blob, wq.WQ_LAYOUT_TILED, None, w0.N, 4, Y=Y)
+
+        t8 = graph_time(torch, f8, reps, 2)
+        t16 = graph_time(torch, f16, reps, 2)
+        ops = 2.0 * M * w0.N * w0.K
+        out["M%d" % M] = {"ms": t8 * 1e3, "TOP/s": ops / t8 / 1e12,
+                          "frac_of_int8_peak": ops / t8 / 1e12 / INT8_PEAK_TOPS,
+                          "wna16_b4_ms": t16 * 1e3, "speedup_vs_wna16_b4": t16 / t8}
+        del A, Y, ws
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=8, help="weight copies per bit width")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="skip prefill and W4A8 figures")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only; this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import weight_only_bit_wq_amd as wq
+    from weight_only_bit_wq_amd import synth
+
+    if not torch.cuda.is_available() or not wq.wq_device_supported(0):
+        print("bench.py needs an MI355X (gfx950) GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    log("setting up decode layers (b=5,6,7; %d copies each)" % args.copies)
+    layers = [DecodeLayer(b, args.copies, torch, wq, synth) for b in DECODE_BITS]
+    torch.cuda.synchronize()
+    step_bytes = sum(l.bytes for l in layers)
+
+    def steps_fn(n):
+        def fn():
+            for i in range(n):
+                for l in layers:
+                    l.call(wq, i)
+        return fn
+
+    # Warmup: W steps, untimed; then exactly K steps timed, synchronised on
+    # both sides.  The K steps are one captured graph.
+    fn = steps_fn(args.steps)
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    if args.warmup:
+        wfn = steps_fn(args.warmup)
+        gw = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw):
+            wfn()
+        gw.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    total_s = start.elapsed_time(stop) / 1e3
+    ms_per_step = total_s * 1e3 / args.steps
+    value = step_bytes * args.steps / total_s / 1e12
+    log("decode step: %.2f us, %.3f TB/s" % (ms_per_step * 1e3, value))
+
+    # Roofline of the dominant kernel (b = 6 decode): launches of that kernel
+    # alone, rotating copies, timed with events on its stream.
+    l6 = layers[1]
+    reps = max(64, args.steps)
+    t6 = graph_time(torch, lambda: [l6.call(wq, i) for i in range(reps)], 3, 1) / reps
+    achieved = l6.bytes / t6 / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "decode_kernel<6,1,TiledW>", "us_per_launch": t6 * 1e6,
+                "bytes_per_launch": l6.bytes}
+    log("b=6 decode kernel: %.2f us/launch, %.0f GB/s" % (t6 * 1e6, achieved))
+
+    per_b = {}
+    for l in layers:
+        tb = graph_time(torch, lambda l=l: [l.call(wq, i) for i in range(reps)], 3, 1) / reps
+        per_b["b%d" % l.b] = {"us": tb * 1e6, "TB/s": l.bytes / tb / 1e12,
+                              "frac_of_hbm_peak": l.bytes / tb / 1e9 / HBM_PEAK_GBS}
+    del layers, l6, g
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": "wq_gemm TB/s (M=1, % HBM peak) and TFLOP/s (M=4096, % MFMA peak) at b=5/6/7",
+        "value": value, "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded uniform codes, signed half-normal group scales, N(0,1) bf16 activations)",
+        "config": {"workload": "decode M=1, K=5120, N=17408, b=5/6/7, group 128, tiled layout, "
+                               "%d rotating weight copies per b" % args.copies,
+                   "M": 1, "K": DECODE_K, "N": DECODE_N, "bits": list(DECODE_BITS),
+                   "step": "3 wq_gemm calls (b=5,6,7)", "parallelism": "none (1 GPU)"},
+        "decode_per_b": per_b,
+        "roofline": roofline,
+    }
+    if not args.no_secondary:
+        log("prefill M=4096")
+        result["prefill"] = bench_prefill(torch, wq, synth, reps=10)
+        torch.cuda.empty_cache()
+        log("w4a8 M=2048/8192")
+        result["w4a8"] = bench_w4a8(torch, wq, synth, reps=10)
+    if not args.no_cpu:
+        import oracle
+        log("cpu oracle baseline (~%.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(oracle, synth, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * wq.h -- C ABI of libwq: b-bit weight-only quantized linear layers (WNA16)
+ * and the int8-activation variant (W4A8) for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources are cited by page title and section):
+ *
+ *   y[m, n] = sum_k A[m, k] * s[n, k / 128] * (c[n, k] - 2^(b-1))
+ *
+ *   - A: bf16 activations [M, K] (row-major).
+ *   - c: unsigned b-bit weight codes, b in 2..8; the compressed-tensors WNA16
+ *     scheme accepts every width from 2 to 8 ("vLLM Can Run INT5-7",
+ *     section 1).
+ *   - The codes of one output row are stored as a dense little-endian
+ *     bitstream along K, ceil(K * b / 32) 32-bit words per row, so 5/6/7-bit
+ *     codes straddle word boundaries (model card
+ *     "Qwen3.8-27B-INT6-Mixed-AutoRound", Findings).  Code k occupies stream
+ *     bits [k*b, k*b + b), least significant bit first.
+ *   - Groups are symmetric above four bits (same page, Findings): one bf16
+ *     scale s[n, g] per group of 128 input features, no zero point; the
+ *     signed weight is c - 2^(b-1).  Scales may be negative (club-3090
+ *     discussion #733, "Under the hood").
+ *   - The result is the plain linear layer on the dequantized weights
+ *     ("vLLM Can Run INT5-7", section 2), y = A . W^T, no bias.
+ *
+ * Life cycle ("vLLM Quantization", How it works: create, repack, run):
+ *   wq_pack      host: codes -> dense packed words            (create)
+ *   wq_repack    device: dense words + scales -> tiled blob    (repack)
+ *   wq_gemm      device: y = A . dequant(W)^T                  (run)
+ *   wq_gemm_a8   device: W4A8 run on the same int4 weights and scales
+ *
+ * Conventions for every entry point:
+ *   - Return WQ_OK (0) or a wq_status code; nothing throws or aborts across
+ *     this boundary.  wq_status_str() gives the reason in words.  Invalid
+ *     requests are refused, never silently computed another way.
+ *   - Pointers named *_d are device pointers (hipMalloc'd or torch CUDA
+ *     tensors) and must be 16-byte aligned; pointers without the suffix are
+ *     host pointers.  The caller allocates and owns every buffer; the library
+ *     allocates no device memory.
+ *   - `stream` is a hipStream_t (NULL: the default stream).  Device calls are
+ *     enqueued on it and return without synchronizing.  A launch failure
+ *     returns WQ_ERR_HIP; wq_last_hip_error() gives the hipError_t value
+ *     (thread-local).
+ *   - bf16 values travel as uint16_t bit patterns.
+ *   - Device entry points require a gfx950 device (WQ_ERR_UNSUPPORTED_DEVICE
+ *     otherwise) and group == 128 with K % 128 == 0 (WQ_ERR_BAD_GROUP).
+ *   - Sizes are int64_t; M == 0 is a valid no-op; N, K must be > 0.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WQ_ABI_VERSION 1
+
+typedef enum wq_status {
+    WQ_OK = 0,
+    WQ_ERR_INVALID_ARG = 1,        /* null pointer, N or K <= 0, M < 0, bad enum */
+    WQ_ERR_UNSUPPORTED_BITS = 2,   /* b outside 2..8, or b != 4 for wq_gemm_a8 */
+    WQ_ERR_BAD_GROUP = 3,          /* group != 128 or K % group != 0 */
+    WQ_ERR_MISALIGNED = 4,         /* a device pointer is not 16-byte aligned */
+    WQ_ERR_CODE_RANGE = 5,         /* wq_pack: a code is >= 2^b (never masked) */
+    WQ_ERR_WORKSPACE = 6,          /* workspace missing or smaller than required */
+    WQ_ERR_BAD_LAYOUT = 7,         /* unknown layout, or scales given/missing wrongly */
+    WQ_ERR_UNSUPPORTED_DEVICE = 8, /* current device is not gfx950 */
+    WQ_ERR_HIP = 9                 /* a HIP call or kernel launch failed */
+} wq_status;
+
+/* Weight layouts accepted by the device entry points. */
+typedef enum wq_layout {
+    /* The dense pack-quantized rows exactly as wq_pack writes them:
+     * uint32 [N, ceil(K*b/32)], with the scales in a separate bf16 [N, K/128]
+     * array passed as scales_d. */
+    WQ_LAYOUT_DENSE = 0,
+    /* The repacked blob wq_repack writes.  Rows are taken 64 at a time (the
+     * last block zero-padded); for each 64-row block and each group g the
+     * blob holds one tile of b*1024 + 128 bytes: b planes of 1 KB where plane
+     * j holds, for row r of the block, bytes [16j, 16j + 16) of that row's
+     * group-g stream (b*16 bytes, 128 codes) at offset 16r, followed by the
+     * 64 bf16 scales s[row, g].  Tiles are ordered block-major, then g.
+     * Scales live inside the blob, so scales_d must be NULL. */
+    WQ_LAYOUT_TILED = 1
+} wq_layout;
+
+typedef enum wq_op {
+    WQ_OP_GEMM = 0,     /* wq_gemm */
+    WQ_OP_GEMM_A8 = 1   /* wq_gemm_a8 */
+} wq_op;
+
+typedef enum wq_out_dtype {
+    WQ_OUT_BF16 = 0,    /* bf16 output, round to nearest even */
+    WQ_OUT_F32 = 1      /* fp32 output (wq_gemm_a8 only) */
+} wq_out_dtype;
+
+/* WQ_ABI_VERSION of the loaded library. */
+int wq_abi_version(void);
+
+/* Static text describing a wq_status value ("unknown status" otherwise). */
+const char *wq_status_str(int status);
+
+/* hipError_t of the last WQ_ERR_HIP returned on this thread (0 if none). */
+int wq_last_hip_error(void);
+
+/* 1 if HIP device `device` is a gfx950 the kernels were built for, else 0. */
+int wq_device_supported(int device);
+
+/* Packed row length of the dense layout: ceil(K * b / 32) 32-bit words
+ * (model card "Qwen3.8-27B-INT6-Mixed-AutoRound", Findings: 960 words for
+ * 5120 six-bit codes).  Returns -1 for K < 0 or b outside 1..8. */
+int64_t wq_packed_words_per_row(int64_t K, int b);
+
+/* Host.  Pack unsigned codes uint8 [N, K] (each < 2^b) into the dense layout
+ * uint32 [N, wq_packed_words_per_row(K, b)].  Rows are independent streams,
+ * zero-padded to a whole word.  A code >= 2^b returns WQ_ERR_CODE_RANGE and
+ * leaves `packed` unspecified.  Host pointers; no alignment requirement. */
+int wq_pack(const uint8_t *codes, int64_t N, int64_t K, int b, int group, uint32_t *packed);
+
+/* Host.  Inverse of wq_pack: packed uint32 [N, ceil(K*b/32)] -> uint8 [N, K]. */
+int wq_unpack(const uint32_t *packed, int64_t N, int64_t K, int b, uint8_t *codes);
+
+/* Bytes of a weight buffer in `layout` (dense words only for
+ * WQ_LAYOUT_DENSE; the whole blob, scales included, for WQ_LAYOUT_TILED).
+ * Returns -1 for invalid arguments. */
+int64_t wq_repacked_bytes(int layout, int64_t N, int64_t K, int b, int group);
+
+/* Device.  Repack (the "repack after load" step of "vLLM Quantization", How
+ * it works): dense words packed_d uint32 [N, ceil(K*b/32)] and scales_d bf16
+ * [N, K/128] -> out_d, wq_repacked_bytes(layout, ...) bytes, in `layout`
+ * (only WQ_LAYOUT_TILED is a repack target).  Inputs are not modified. */
+int wq_repack(const uint32_t *packed_d, const uint16_t *scales_d, int64_t N, int64_t K,
+              int b, int group, int layout, void *out_d, void *stream);
+
+/* Device.  Extract the codes of a weight buffer in `layout` into uint8
+ * [N, K] with the same in-register unpacker the GEMM kernels use.  Exposed
+ * so the unpacker can be checked code for code. */
+int wq_unpack_dev(const void *W_d, int layout, int64_t N, int64_t K, int b, int group,
+                  uint8_t *codes_d, void *stream);
+
+/* Workspace bytes wq_gemm (op = WQ_OP_GEMM) or wq_gemm_a8 (WQ_OP_GEMM_A8)
+ * needs for this problem (0 if none; -1 for invalid arguments).  Every
+ * non-empty workspace begins with a 64 KiB region of counters that must be
+ * zero before the first call that uses it; every call leaves that region
+ * zero again, whatever the op or shape, so one workspace (sized for the
+ * largest call) can serve any sequence of calls ordered on one stream.
+ * The rest is scratch.  Calls that may run concurrently need separate
+ * workspaces. */
+int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int group);
+
+/* Device.  WNA16 layer: Y_d bf16 [M, N] = A_d bf16 [M, K] . dequant(W)^T.
+ * W_d is in `layout`; scales_d bf16 [N, K/128] for WQ_LAYOUT_DENSE, NULL for
+ * WQ_LAYOUT_TILED.  Accumulation is fp32 with the integer codes exact and
+ * the group scale applied once per group; the output is rounded to bf16
+ * (nearest even).  ws_d / ws_bytes: see wq_workspace_bytes.  Results are
+ * deterministic (fixed reduction order). */
+int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d, int layout,
+            const uint16_t *scales_d, int b, int group, uint16_t *Y_d, void *ws_d,
+            int64_t ws_bytes, void *stream);
+
+/* Device.  Per-token dynamic int8 activation quantization (club-3090
+ * discussion #733, "Under the hood"), fp32 throughout:
+ *   sa_d[m] = max_k |A[m,k]| / 127   (IEEE division)
+ *   Aq_d[m,k] = clamp(rint(A[m,k] / sa_d[m]), -127, 127)   (ties to even)
+ * A row of zeros gives sa = 0 and Aq = 0.  Aq_d int8 [M, K], sa_d fp32 [M]. */
+int wq_quant_act_i8(const uint16_t *A_d, int64_t M, int64_t K, int8_t *Aq_d, float *sa_d,
+                    void *stream);
+
+/* Device.  W4A8 layer (same page): activations quantized as wq_quant_act_i8
+ * does, int4 codes widened to int8 without loss (c - 8 in [-8, 7]), int8
+ * products summed exactly in int32 per group of 128, then
+ *   Y[m, n] = sa[m] * sum_g s[n, g] * acc_g[m, n]     (fp32)
+ * written as bf16 (out_dtype WQ_OUT_BF16) or fp32 (WQ_OUT_F32).  The same
+ * packed int4 weights and scales as wq_gemm with b = 4 are used; b != 4
+ * returns WQ_ERR_UNSUPPORTED_BITS.  The workspace holds Aq and sa. */
+int wq_gemm_a8(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
+               int layout, const uint16_t *scales_d, int b, int group, void *Y_d,
+               int out_dtype, void *ws_d, int64_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -1,0 +1,158 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads and exports
+every function include/wq.h declares, the host packer agrees with the oracle
+bit for bit, and every argument error is refused with its status before any
+device work (forced from the host with fake, never dereferenced pointers)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_bit_wq_amd as wq
+from weight_only_bit_wq_amd import synth
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(wq.lib_path)
+    names = wq.declared_functions()
+    assert len(names) == 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert wq.wq_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(10):
+        assert wq.wq_status_str(s) != "unknown status"
+    assert wq.wq_status_str(99) == "unknown status"
+    assert "2..8" in wq.wq_status_str(wq.WQ_ERR_UNSUPPORTED_BITS)
+
+
+def test_words_per_row():
+    assert wq.wq_packed_words_per_row(5120, 6) == 960
+    for b in range(1, 9):
+        for K in (0, 1, 7, 128, 5120, 17408):
+            assert wq.wq_packed_words_per_row(K, b) == oracle.words_per_row(K, b)
+    assert wq.wq_packed_words_per_row(128, 9) == -1
+    assert wq.wq_packed_words_per_row(-1, 4) == -1
+
+
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 6, 7, 8])
+def test_host_pack_unpack_match_oracle(b):
+    rng = np.random.default_rng(100 + b)
+    codes = rng.integers(0, 1 << b, size=(37, 640), dtype=np.uint8)
+    packed = wq.wq_pack(codes, b)
+    np.testing.assert_array_equal(packed, oracle.pack(codes, b))
+    np.testing.assert_array_equal(wq.wq_unpack(packed, 640, b), codes)
+    np.testing.assert_array_equal(wq.wq_unpack(oracle.pack(codes, b), 640, b), codes)
+
+
+def test_host_pack_large_threaded_matches_oracle():
+    w = synth.decode(M=1, b=7, N=2048, K=5120)
+    np.testing.assert_array_equal(wq.wq_pack(w.codes, 7), oracle.pack(w.codes, 7))
+
+
+def test_pack_refuses_out_of_range_codes():
+    codes = np.zeros((3, 128), dtype=np.uint8)
+    codes[2, 77] = 32
+    with pytest.raises(wq.WQError) as e:
+        wq.wq_pack(codes, 5)
+    assert e.value.status == wq.WQ_ERR_CODE_RANGE
+    wq.wq_pack(codes, 6)  # fits in 6 bits
+
+
+@pytest.mark.parametrize("b,group,K,status", [
+    (1, 128, 128, wq.WQ_ERR_UNSUPPORTED_BITS),
+    (9, 128, 128, wq.WQ_ERR_UNSUPPORTED_BITS),
+    (6, 64, 128, wq.WQ_ERR_BAD_GROUP),
+    (6, 128, 192, wq.WQ_ERR_BAD_GROUP),
+])
+def test_pack_argument_errors(b, group, K, status):
+    codes = np.zeros((2, K), dtype=np.uint8)
+    out = np.zeros((2, 64), dtype=np.uint32)
+    lib = wq._load()
+    assert lib.wq_pack(wq._ptr(codes), 2, K, b, group, wq._ptr(out)) == status
+
+
+def test_null_pointers_are_refused():
+    lib = wq._load()
+    assert lib.wq_pack(None, 2, 128, 6, 128, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_unpack(None, 2, 128, 6, None) == wq.WQ_ERR_INVALID_ARG
+
+
+# Fake device addresses: validation must reject before anything is touched.
+ALIGNED = 0x7F0000000000
+MISALIGNED = ALIGNED + 8
+
+
+def _gemm(A=ALIGNED, M=1, N=256, K=512, W=ALIGNED, layout=wq.WQ_LAYOUT_TILED, S=None, b=6,
+          group=128, Y=ALIGNED, ws=ALIGNED, ws_bytes=1 << 30):
+    lib = wq._load()
+    c = ctypes.c_void_p
+    return lib.wq_gemm(c(A), M, N, K, c(W), layout, c(S) if S else None, b, group, c(Y),
+                       c(ws) if ws else None, ws_bytes, None)
+
+
+def test_gemm_validation_statuses():
+    assert _gemm(b=1) == wq.WQ_ERR_UNSUPPORTED_BITS
+    assert _gemm(b=9) == wq.WQ_ERR_UNSUPPORTED_BITS
+    assert _gemm(group=64) == wq.WQ_ERR_BAD_GROUP
+    assert _gemm(K=500) == wq.WQ_ERR_BAD_GROUP
+    assert _gemm(N=0) == wq.WQ_ERR_INVALID_ARG
+    assert _gemm(K=0) == wq.WQ_ERR_INVALID_ARG
+    assert _gemm(M=-1) == wq.WQ_ERR_INVALID_ARG
+    assert _gemm(layout=5) == wq.WQ_ERR_BAD_LAYOUT
+    assert _gemm(layout=wq.WQ_LAYOUT_DENSE) == wq.WQ_ERR_BAD_LAYOUT          # scales missing
+    assert _gemm(S=ALIGNED) == wq.WQ_ERR_BAD_LAYOUT                          # scales with TILED
+    assert _gemm(A=0) == wq.WQ_ERR_INVALID_ARG
+    assert _gemm(A=MISALIGNED) == wq.WQ_ERR_MISALIGNED
+    assert _gemm(W=MISALIGNED) == wq.WQ_ERR_MISALIGNED
+    assert _gemm(Y=MISALIGNED) == wq.WQ_ERR_MISALIGNED
+    assert _gemm(M=0, A=0, W=0, Y=0) == wq.WQ_OK                             # empty batch: no-op
+
+
+def test_gemm_workspace_checks():
+    need = wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, 17408, 5120, 6)
+    assert need > 0
+    assert _gemm(M=1, N=17408, K=5120, ws=None, ws_bytes=0) == wq.WQ_ERR_WORKSPACE
+    assert _gemm(M=1, N=17408, K=5120, ws_bytes=need - 1) == wq.WQ_ERR_WORKSPACE
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 0, 17408, 5120, 6) == 0
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, 17408, 5120, 9) == -1
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 64, 17408, 5120, 6) == -1
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 64, 17408, 5120, 4) >= 64 * 5120 + 64 * 4
+    assert wq.wq_workspace_bytes(7, 1, 256, 512, 6) == -1
+
+
+def test_gemm_a8_refuses_other_widths_and_bad_output():
+    lib = wq._load()
+    c = ctypes.c_void_p
+    A = c(ALIGNED)
+    for b in (2, 3, 5, 6, 7, 8):
+        assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, b, 128, A, 0, A, 1 << 30, None) == \
+            wq.WQ_ERR_UNSUPPORTED_BITS
+    assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, 4, 128, A, 7, A, 1 << 30, None) == \
+        wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, 4, 128, A, 0, None, 0, None) == \
+        wq.WQ_ERR_WORKSPACE
+
+
+def test_repack_and_unpack_dev_validation():
+    lib = wq._load()
+    c = ctypes.c_void_p
+    A = c(ALIGNED)
+    assert lib.wq_repack(A, A, 256, 512, 6, 128, wq.WQ_LAYOUT_DENSE, A, None) == wq.WQ_ERR_BAD_LAYOUT
+    assert lib.wq_repack(A, c(MISALIGNED), 256, 512, 6, 128, 1, A, None) == wq.WQ_ERR_MISALIGNED
+    assert lib.wq_repack(A, None, 256, 512, 6, 128, 1, A, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_unpack_dev(A, 3, 256, 512, 6, 128, A, None) == wq.WQ_ERR_BAD_LAYOUT
+    assert lib.wq_unpack_dev(A, 0, 256, 512, 0, 128, A, None) == wq.WQ_ERR_UNSUPPORTED_BITS
+    assert lib.wq_quant_act_i8(A, 4, 100, A, A, None) == wq.WQ_ERR_INVALID_ARG
+
+
+def test_repacked_sizes():
+    b, N, K = 6, 17408, 5120
+    assert wq.wq_repacked_bytes(wq.WQ_LAYOUT_DENSE, N, K, b) == N * 960 * 4
+    tiled = wq.wq_repacked_bytes(wq.WQ_LAYOUT_TILED, N, K, b)
+    # codes plus scales, exactly: no padding at N % 64 == 0
+    assert tiled == N * 960 * 4 + N * (K // 128) * 2
+    assert wq.wq_repacked_bytes(wq.WQ_LAYOUT_TILED, 65, K, b) == 2 * 40 * (6 * 1024 + 128)
+    assert wq.wq_repacked_bytes(2, N, K, b) == -1

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Unpacking is bit-exact; WNA16 outputs meet
+|y - y_ref| <= 4e-3 sum|a w| + 1e-3; W4A8 activation codes are bit-exact and
+its fp32 output is within 1e-5 of the oracle's magnitude sum."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_bit_wq_amd as wq
+from weight_only_bit_wq_amd import synth
+from gpu_util import (Layer, assert_a8, assert_wna16, bf16_values, dev_bf16, dev_words,
+                      host_bf16_bits, sample_points)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = [wq.WQ_LAYOUT_DENSE, wq.WQ_LAYOUT_TILED]
+LNAME = {wq.WQ_LAYOUT_DENSE: "dense", wq.WQ_LAYOUT_TILED: "tiled"}
+BITS = [2, 3, 4, 5, 6, 7, 8]
+
+
+def _workload(M, N, K, b, seed, scales="halfnormal"):
+    rng = np.random.default_rng(seed)
+    codes = synth.draw_codes(rng, N, K, b)
+    if scales == "uniform":
+        sc = synth.draw_scales_uniform(rng, N, K // 128)
+    else:
+        sc = synth.draw_scales_halfnormal_signed(rng, N, K // 128)
+    A = synth.draw_act(rng, M, K)
+    return synth.Workload(A, codes, sc, b)
+
+
+def test_device_is_gfx950():
+    assert torch.cuda.is_available()
+    assert wq.wq_device_supported(torch.cuda.current_device())
+
+
+# --- unpacker / repack ------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("b", BITS)
+def test_unpack_dev_bit_exact(b, layout):
+    w = _workload(1, 200, 384, b, seed=200 + b)  # N ragged w.r.t. 64-row tiles
+    packed = wq.wq_pack(w.codes, b)
+    ref = oracle.unpack(oracle.pack(w.codes, b), w.K, b)
+    np.testing.assert_array_equal(packed, oracle.pack(w.codes, b))
+    L = Layer(w, layout, packed)
+    codes = wq.wq_unpack_dev(L.W_d, layout, w.N, w.K, b)
+    np.testing.assert_array_equal(codes.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("b", [5, 6, 7])
+def test_unpack_dev_decode_shape(b):
+    w = synth.decode(M=1, b=b)
+    L = Layer(w, wq.WQ_LAYOUT_TILED)
+    codes = wq.wq_unpack_dev(L.W_d, wq.WQ_LAYOUT_TILED, w.N, w.K, b).cpu().numpy()
+    rows = np.r_[0:64, w.N - 64:w.N]
+    np.testing.assert_array_equal(codes[rows], oracle.unpack(oracle.pack(w.codes[rows], b), w.K, b))
+    np.testing.assert_array_equal(codes, w.codes)
+
+
+@pytest.mark.parametrize("b", BITS)
+def test_repack_matches_documented_tile_layout(b):
+    w = _workload(1, 130, 256, b, seed=300 + b)
+    L = Layer(w, wq.WQ_LAYOUT_TILED)
+    blob = L.W_d.cpu().numpy()
+    G = w.K // 128
+    tb = 1024 * b + 128
+    assert blob.size == 3 * G * tb
+    dense = L.packed.view(np.uint8).reshape(w.N, -1)
+    for n in (0, 63, 64, 129):
+        for g in range(G):
+            tile = blob[((n // 64) * G + g) * tb:((n // 64) * G + g + 1) * tb]
+            for j in range(b):
+                got = tile[j * 1024 + (n % 64) * 16:j * 1024 + (n % 64) * 16 + 16]
+                np.testing.assert_array_equal(got, dense[n, g * 16 * b + 16 * j:g * 16 * b + 16 * j + 16])
+            s = tile[b * 1024:].view(np.uint16)
+            assert s[n % 64] == w.scales[n, g]
+    # padded rows 130..191 are zero
+    last = blob[(2 * G) * tb:(2 * G + 1) * tb]
+    assert not last[2 * 16:1024].any()
+
+
+# --- WNA16 GEMM -----------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+def test_gemm_tiny_workload(layout):
+    w = synth.tiny(0)
+    y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, w.b), w.scales, w.b)
+    assert_wna16(Layer(w, layout).gemm(), y_ref, mag, "tiny")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 8, 13, 16])
+@pytest.mark.parametrize("b", BITS)
+def test_gemm_decode_path(b, M, layout):
+    w = _workload(M, 300, 1280, b, seed=400 + 10 * b + M)
+    y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
+    assert_wna16(Layer(w, layout).gemm(), y_ref, mag, "decode b=%d M=%d" % (b, M))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("M", [17, 130, 257])
+@pytest.mark.parametrize("b", BITS)
+def test_gemm_prefill_path(b, M, layout):
+    w = _workload(M, 200, 640, b, seed=500 + 10 * b + M)
+    y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
+    assert_wna16(Layer(w, layout).gemm(), y_ref, mag, "prefill b=%d M=%d" % (b, M))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("b", [5, 6, 7])
+def test_gemm_decode_sweep_full_shape(b, M):
+    w = synth.decode(M=M, b=b)
+    y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
+    assert_wna16(Layer(w, wq.WQ_LAYOUT_TILED).gemm(), y_ref, mag, "decode sweep b=%d M=%d" % (b, M))
+
+
+@pytest.mark.parametrize("shape", [(5120, 17408), (17408, 5120)], ids=["up", "down"])
+def test_gemm_prefill_full_shape_sampled(shape):
+    K, N = shape
+    w = synth.prefill(M=4096, N=N, K=K, b=6)
+    L = Layer(w, wq.WQ_LAYOUT_TILED)
+    Y = L.gemm()
+    packed = oracle.pack(w.codes, 6)
+    mi, ni = sample_points(w.M, w.N, 3000, seed=7)
+    y_ref, mag = oracle.wna16_points(w.A, packed, w.scales, 6, mi, ni)
+    assert_wna16(Y[mi, ni], y_ref, mag, "prefill %dx%dx%d" % (w.M, N, K))
+    # whole rows and columns at the tile edges
+    for m in (0, 127, 128, 4095):
+        yr, mg = oracle.wna16_points(w.A, packed, w.scales, 6, np.full(N, m), np.arange(N))
+        assert_wna16(Y[m], yr, mg, "prefill row %d" % m)
+
+
+@pytest.mark.parametrize("M", [2, 20])
+@pytest.mark.parametrize("b", BITS)
+def test_hand_computed_example_exact(b, M):
+    # The 2x3x128 example with a closed form (see tests/golden/hand_2x3x128.txt),
+    # rows repeated to reach the decode (M=2) and prefill (M=20) paths.
+    rows = [r for r in open(__file__.replace("test_gpu_parity.py", "golden/hand_2x3x128.txt"))
+            if r.strip() and not r.startswith("#")]
+    expect = {int(r.split()[0]): np.array([float(v) for v in r.split()[1:]]).reshape(2, 3)
+              for r in rows}[b]
+    K = 128
+    A = np.stack([np.ones(K), (-1.0) ** np.arange(K)]).astype(np.float32)
+    A = np.tile(A, (M // 2, 1))
+    codes = np.stack([np.full(K, (1 << (b - 1)) + 1), np.arange(K) % (1 << b),
+                      np.zeros(K)]).astype(np.uint8)
+    scales = synth.f32_to_bf16_bits(np.array([[1.0], [-0.5], [2.0 ** -7]], dtype=np.float32))
+    w = synth.Workload(synth.f32_to_bf16_bits(A), codes, scales, b)
+    for layout in LAYOUTS:
+        Y = bf16_values(Layer(w, layout).gemm())
+        np.testing.assert_array_equal(Y, np.tile(expect, (M // 2, 1)))
+
+
+@pytest.mark.parametrize("M", [3, 33])
+def test_integer_invariant_b8(M):
+    rng = np.random.default_rng(600 + M)
+    N, K = 96, 512
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    A_int = rng.integers(-16, 17, size=(M, K))
+    w = synth.Workload(synth.f32_to_bf16_bits(A_int.astype(np.float32)), codes,
+                       np.full((N, K // 128), 0x3F80, dtype=np.uint16), 8)
+    ref = (A_int @ (codes.astype(np.int64) - 128).T).astype(np.float32)
+    for layout in LAYOUTS:
+        np.testing.assert_array_equal(Layer(w, layout).gemm(), synth.f32_to_bf16_bits(ref))
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 40])
+def test_negated_scales_negate_output_bitwise(M):
+    w = _workload(M, 256, 1024, 6, seed=700 + M)
+    Y1 = Layer(w, wq.WQ_LAYOUT_TILED).gemm()
+    w2 = synth.Workload(w.A, w.codes, w.scales ^ np.uint16(0x8000), 6)
+    Y2 = Layer(w2, wq.WQ_LAYOUT_TILED).gemm()
+    np.testing.assert_array_equal(Y2, Y1 ^ np.uint16(0x8000))
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_deterministic(M):
+    w = _workload(M, 17408 // 4, 5120, 6, seed=800 + M)
+    L = Layer(w, wq.WQ_LAYOUT_TILED)
+    np.testing.assert_array_equal(L.gemm(), L.gemm())
+
+
+def test_empty_batch_is_noop():
+    w = _workload(1, 64, 128, 6, seed=900)
+    L = Layer(w, wq.WQ_LAYOUT_TILED)
+    A = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    Y = wq.wq_gemm(A, L.W_d, L.layout, None, 64, 6)
+    assert Y.shape == (0, 64)
+
+
+def test_dense_and_tiled_agree_bitwise():
+    w = _workload(8, 1000, 2048, 7, seed=901)
+    np.testing.assert_array_equal(Layer(w, wq.WQ_LAYOUT_DENSE).gemm(),
+                                  Layer(w, wq.WQ_LAYOUT_TILED).gemm())
+
+
+# --- W4A8 ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(1, 128), (7, 5120), (64, 1024), (300, 5120)])
+def test_quant_act_bit_exact(M, K):
+    w = synth.w4a8(M=M, N=8, K=K, seed=3)
+    Aq, sa = wq.wq_quant_act_i8(dev_bf16(w.A))
+    Aq_ref, sa_ref = oracle.quant_act_i8(w.A)
+    np.testing.assert_array_equal(sa.cpu().numpy(), sa_ref)
+    np.testing.assert_array_equal(Aq.cpu().numpy(), Aq_ref)
+
+
+def test_quant_act_zero_row_and_ties():
+    row = np.zeros(256, dtype=np.float32)
+    row[:7] = [127.0, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5]
+    A = synth.f32_to_bf16_bits(np.stack([row, np.zeros(256, dtype=np.float32)]))
+    Aq, sa = wq.wq_quant_act_i8(dev_bf16(A))
+    Aq_ref, sa_ref = oracle.quant_act_i8(A)
+    np.testing.assert_array_equal(sa.cpu().numpy(), sa_ref)
+    np.testing.assert_array_equal(Aq.cpu().numpy(), Aq_ref)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (37, 200, 640), (256, 512, 1024), (130, 96, 5120)])
+def test_gemm_a8_fp32(M, N, K, layout):
+    w = synth.w4a8(M=M, N=N, K=K, seed=1000 + M)
+    y_ref, mag, _, _ = oracle.w4a8(w.A, oracle.pack(w.codes, 4), w.scales)
+    L = Layer(w, layout)
+    assert_a8(L.gemm_a8(wq.WQ_OUT_F32), y_ref, mag, False, "a8 f32 %dx%dx%d" % (M, N, K))
+    assert_a8(L.gemm_a8(wq.WQ_OUT_BF16), y_ref, mag, True, "a8 bf16 %dx%dx%d" % (M, N, K))
+
+
+def test_gemm_a8_on_grid_integer_exact():
+    rng = np.random.default_rng(1100)
+    M, N, K = 40, 64, 512
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    A_int = rng.integers(-127, 128, size=(M, K))
+    A_int[:, 3] = 127
+    w = synth.Workload(synth.f32_to_bf16_bits(A_int.astype(np.float32)), codes,
+                       np.full((N, K // 128), 0x3F80, dtype=np.uint16), 4)
+    ref = (A_int @ (codes.astype(np.int64) - 8).T).astype(np.float64)
+    np.testing.assert_array_equal(Layer(w, wq.WQ_LAYOUT_TILED).gemm_a8(wq.WQ_OUT_F32), ref)
+
+
+@pytest.mark.parametrize("M", [2048])
+def test_gemm_a8_full_shape_sampled(M):
+    w = synth.w4a8(M=M)
+    L = Layer(w, wq.WQ_LAYOUT_TILED)
+    Y = L.gemm_a8(wq.WQ_OUT_F32)
+    Aq, sa = oracle.quant_act_i8(w.A)
+    mi, ni = sample_points(w.M, w.N, 3000, seed=11)
+    y_ref, mag = oracle.w4a8_points(Aq, sa, oracle.pack(w.codes, 4), w.scales, mi, ni)
+    assert_a8(Y[mi, ni], y_ref, mag, False, "a8 full shape")
+
+
+def test_gemm_a8_negated_scales():
+    w = synth.w4a8(M=64, N=128, K=1024, seed=1200)
+    Y1 = Layer(w, wq.WQ_LAYOUT_TILED).gemm_a8(wq.WQ_OUT_F32)
+    w2 = synth.Workload(w.A, w.codes, w.scales ^ np.uint16(0x8000), 4)
+    Y2 = Layer(w2, wq.WQ_LAYOUT_TILED).gemm_a8(wq.WQ_OUT_F32)
+    np.testing.assert_array_equal(Y2, -Y1)
+
+
+def test_workspace_reused_across_shapes_and_ops():
+    # One workspace for a sequence of calls with different split layouts and
+    # a W4A8 call in between: the counter region must stay valid throughout.
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    cases = [(16, 6, 1000, 1280), (1, 3, 300, 1280), (4, 7, 520, 2560), (1, 5, 64, 384)]
+    for M, b, N, K in cases:
+        w = _workload(M, N, K, b, seed=1300 + M + b)
+        L = Layer(w, wq.WQ_LAYOUT_TILED)
+        Y = wq.wq_gemm(dev_bf16(w.A), L.W_d, L.layout, None, N, b, ws=ws)
+        torch.cuda.synchronize()
+        y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
+        assert_wna16(host_bf16_bits(Y), y_ref, mag, "ws reuse b=%d M=%d" % (b, M))
+        w4 = synth.w4a8(M=20, N=64, K=256, seed=1400 + M)
+        L4 = Layer(w4, wq.WQ_LAYOUT_TILED)
+        wq.wq_gemm_a8(dev_bf16(w4.A), L4.W_d, L4.layout, None, 64, 4, ws=ws)
+    torch.cuda.synchronize()
+    assert not ws[:65536].any()

@@ -1,0 +1,293 @@
+// wq_api.hip -- the C ABI declared in include/wq.h: argument validation, the
+// host packer/unpacker, sizes, and dispatch to the device kernels.
+//
+// Every entry point validates before touching memory, returns a wq_status
+// and never throws; device work is only enqueued on the caller's stream.
+#include "wq.h"
+#include "wq_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+constexpr int kGroup = 128;
+constexpr int kMaxDevices = 64;
+
+thread_local int g_last_hip_error = 0;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return WQ_ERR_HIP;
+}
+
+bool valid_bits(int b) { return b >= 2 && b <= 8; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_group(int64_t K, int group) {
+    if (group != kGroup || K % kGroup != 0) return WQ_ERR_BAD_GROUP;
+    return WQ_OK;
+}
+
+// Shapes the kernels index with 32-bit ints.
+bool dims_ok(int64_t M, int64_t N, int64_t K) {
+    return M >= 0 && N > 0 && K > 0 && M < (1ll << 31) && N < (1ll << 31) && K < (1ll << 31);
+}
+
+int query_device(int dev) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 2;
+    return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+}
+
+// The current device must be a gfx950 (result cached per device).
+int check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {  // no usable HIP device at all
+        g_last_hip_error = (int)e;
+        return WQ_ERR_UNSUPPORTED_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return query_device(dev) == 1 ? WQ_OK : WQ_ERR_UNSUPPORTED_DEVICE;
+    int st = g_device_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        st = query_device(dev);
+        g_device_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? WQ_OK : WQ_ERR_UNSUPPORTED_DEVICE;
+}
+
+int64_t words_per_row(int64_t K, int b) { return (K * (int64_t)b + 31) / 32; }
+
+// Run f(row_begin, row_end) over [0, N) on up to 16 host threads.
+template <class F>
+void parallel_rows(int64_t N, int64_t work_per_row, F f) {
+    unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+    int64_t nt = std::min<int64_t>({(int64_t)hw, 16, N});
+    if (N * work_per_row < (1 << 20) || nt <= 1) {
+        f((int64_t)0, N);
+        return;
+    }
+    std::vector<std::thread> th;
+    const int64_t chunk = (N + nt - 1) / nt;
+    for (int64_t t = 0; t < nt; ++t) {
+        const int64_t r0 = t * chunk, r1 = std::min(N, r0 + chunk);
+        if (r0 >= r1) break;
+        th.emplace_back([=] { f(r0, r1); });
+    }
+    for (auto &t : th) t.join();
+}
+
+int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int b) {
+    if (M == 0) return 0;
+    if (M <= wq::kDecodeMaxM) return wq::decode_plan(M, N, K, b).ws_bytes;
+    return wq::prefill_ws_bytes(M, N, K, b);
+}
+
+}  // namespace
+
+extern "C" {
+
+int wq_abi_version(void) { return WQ_ABI_VERSION; }
+
+const char *wq_status_str(int status) {
+    switch (status) {
+        case WQ_OK: return "ok";
+        case WQ_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive N or K, negative M, or unknown enum value)";
+        case WQ_ERR_UNSUPPORTED_BITS: return "unsupported bit width: b must be in 2..8, and wq_gemm_a8 takes only b = 4 (int4 codes)";
+        case WQ_ERR_BAD_GROUP: return "group must be 128 and divide K";
+        case WQ_ERR_MISALIGNED: return "device pointer is not 16-byte aligned";
+        case WQ_ERR_CODE_RANGE: return "a code does not fit in b bits (codes are refused, never masked)";
+        case WQ_ERR_WORKSPACE: return "workspace missing or smaller than wq_workspace_bytes()";
+        case WQ_ERR_BAD_LAYOUT: return "bad layout: unknown value, repack target not TILED, or scales_d given with TILED / missing with DENSE";
+        case WQ_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950 (MI355X)";
+        case WQ_ERR_HIP: return "HIP runtime or kernel launch error (see wq_last_hip_error)";
+    }
+    return "unknown status";
+}
+
+int wq_last_hip_error(void) { return g_last_hip_error; }
+
+int wq_device_supported(int device) {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return 0;
+    return query_device(device) == 1 ? 1 : 0;
+}
+
+int64_t wq_packed_words_per_row(int64_t K, int b) {
+    if (K < 0 || b < 1 || b > 8) return -1;
+    return words_per_row(K, b);
+}
+
+int wq_pack(const uint8_t *codes, int64_t N, int64_t K, int b, int group, uint32_t *packed) {
+    if (!codes || !packed || N < 0 || K <= 0) return WQ_ERR_INVALID_ARG;
+    if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
+    if (int s = check_group(K, group)) return s;
+    const int64_t W = words_per_row(K, b);
+    std::atomic<bool> bad{false};
+    parallel_rows(N, K, [&](int64_t r0, int64_t r1) {
+        for (int64_t n = r0; n < r1 && !bad.load(std::memory_order_relaxed); ++n) {
+            const uint8_t *src = codes + n * K;
+            uint32_t *dst = packed + n * W;
+            uint64_t acc = 0;  // pending stream bits, LSB = next bit
+            int nbits = 0;
+            int64_t wi = 0;
+            uint8_t any_high = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                const uint8_t c = src[k];
+                any_high |= (uint8_t)(c >> b);
+                acc |= (uint64_t)c << nbits;
+                nbits += b;
+                if (nbits >= 32) {
+                    dst[wi++] = (uint32_t)acc;
+                    acc >>= 32;
+                    nbits -= 32;
+                }
+            }
+            if (nbits > 0) dst[wi++] = (uint32_t)acc;
+            if (any_high) bad.store(true);
+        }
+    });
+    return bad.load() ? WQ_ERR_CODE_RANGE : WQ_OK;
+}
+
+int wq_unpack(const uint32_t *packed, int64_t N, int64_t K, int b, uint8_t *codes) {
+    if (!codes || !packed || N < 0 || K <= 0) return WQ_ERR_INVALID_ARG;
+    if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
+    const int64_t W = words_per_row(K, b);
+    const uint32_t mask = (1u << b) - 1u;
+    parallel_rows(N, K, [&](int64_t r0, int64_t r1) {
+        for (int64_t n = r0; n < r1; ++n) {
+            const uint32_t *src = packed + n * W;
+            uint8_t *dst = codes + n * K;
+            uint64_t acc = 0;
+            int nbits = 0;
+            int64_t wi = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                if (nbits < b) {
+                    acc |= (uint64_t)src[wi++] << nbits;
+                    nbits += 32;
+                }
+                dst[k] = (uint8_t)(acc & mask);
+                acc >>= b;
+                nbits -= b;
+            }
+        }
+    });
+    return WQ_OK;
+}
+
+int64_t wq_repacked_bytes(int layout, int64_t N, int64_t K, int b, int group) {
+    if (N <= 0 || K <= 0 || !valid_bits(b) || check_group(K, group) != WQ_OK) return -1;
+    if (layout == WQ_LAYOUT_DENSE) return N * words_per_row(K, b) * 4;
+    if (layout == WQ_LAYOUT_TILED) return (N + 63) / 64 * (K / kGroup) * (int64_t)(1024 * b + 128);
+    return -1;
+}
+
+int wq_repack(const uint32_t *packed_d, const uint16_t *scales_d, int64_t N, int64_t K, int b,
+              int group, int layout, void *out_d, void *stream) {
+    if (!packed_d || !scales_d || !out_d || !dims_ok(0, N, K)) return WQ_ERR_INVALID_ARG;
+    if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
+    if (int s = check_group(K, group)) return s;
+    if (layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
+    if (!aligned16(packed_d) || !aligned16(scales_d) || !aligned16(out_d)) return WQ_ERR_MISALIGNED;
+    if (int s = check_device()) return s;
+    hipError_t e = wq::launch_repack_tiled(packed_d, scales_d, N, K, b, out_d, (hipStream_t)stream);
+    return e == hipSuccess ? WQ_OK : hip_fail(e);
+}
+
+int wq_unpack_dev(const void *W_d, int layout, int64_t N, int64_t K, int b, int group,
+                  uint8_t *codes_d, void *stream) {
+    if (!W_d || !codes_d || !dims_ok(0, N, K)) return WQ_ERR_INVALID_ARG;
+    if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
+    if (int s = check_group(K, group)) return s;
+    if (layout != WQ_LAYOUT_DENSE && layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
+    if (!aligned16(W_d) || !aligned16(codes_d)) return WQ_ERR_MISALIGNED;
+    if (int s = check_device()) return s;
+    hipError_t e = wq::launch_unpack(W_d, layout == WQ_LAYOUT_TILED, nullptr, N, K, b, codes_d,
+                                     (hipStream_t)stream);
+    return e == hipSuccess ? WQ_OK : hip_fail(e);
+}
+
+int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int group) {
+    if (!dims_ok(M, N, K) || !valid_bits(b) || check_group(K, group) != WQ_OK) return -1;
+    if (op == WQ_OP_GEMM) return gemm_ws_bytes(M, N, K, b);
+    if (op == WQ_OP_GEMM_A8) {
+        if (b != 4) return -1;
+        return wq::a8_ws_bytes(M, N, K);
+    }
+    return -1;
+}
+
+int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d, int layout,
+            const uint16_t *scales_d, int b, int group, uint16_t *Y_d, void *ws_d,
+            int64_t ws_bytes, void *stream) {
+    if (!dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
+    if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
+    if (int s = check_group(K, group)) return s;
+    if (layout != WQ_LAYOUT_DENSE && layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
+    if ((layout == WQ_LAYOUT_DENSE) != (scales_d != nullptr)) return WQ_ERR_BAD_LAYOUT;
+    if (M == 0) return WQ_OK;
+    if (!A_d || !W_d || !Y_d) return WQ_ERR_INVALID_ARG;
+    if (!aligned16(A_d) || !aligned16(W_d) || !aligned16(Y_d) ||
+        (scales_d && !aligned16(scales_d)) || (ws_d && !aligned16(ws_d)))
+        return WQ_ERR_MISALIGNED;
+    const int64_t need = gemm_ws_bytes(M, N, K, b);
+    if (need > 0 && (!ws_d || ws_bytes < need)) return WQ_ERR_WORKSPACE;
+    if (int s = check_device()) return s;
+    const bool tiled = layout == WQ_LAYOUT_TILED;
+    hipError_t e;
+    if (M <= wq::kDecodeMaxM) {
+        const wq::DecodePlan p = wq::decode_plan(M, N, K, b);
+        e = wq::launch_decode(A_d, M, N, K, W_d, tiled, scales_d, b, Y_d, ws_d, p,
+                              (hipStream_t)stream);
+    } else {
+        e = wq::launch_prefill(A_d, M, N, K, W_d, tiled, scales_d, b, Y_d, ws_d,
+                               (hipStream_t)stream);
+    }
+    return e == hipSuccess ? WQ_OK : hip_fail(e);
+}
+
+int wq_quant_act_i8(const uint16_t *A_d, int64_t M, int64_t K, int8_t *Aq_d, float *sa_d,
+                    void *stream) {
+    if (M < 0 || K <= 0 || M >= (1ll << 31) || K >= (1ll << 31)) return WQ_ERR_INVALID_ARG;
+    if (M == 0) return WQ_OK;
+    if (!A_d || !Aq_d || !sa_d) return WQ_ERR_INVALID_ARG;
+    if (K % 8 != 0) return WQ_ERR_INVALID_ARG;
+    if (!aligned16(A_d) || !aligned16(Aq_d) || !aligned16(sa_d)) return WQ_ERR_MISALIGNED;
+    if (int s = check_device()) return s;
+    hipError_t e = wq::launch_quant_act(A_d, M, K, Aq_d, sa_d, (hipStream_t)stream);
+    return e == hipSuccess ? WQ_OK : hip_fail(e);
+}
+
+int wq_gemm_a8(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
+               int layout, const uint16_t *scales_d, int b, int group, void *Y_d,
+               int out_dtype, void *ws_d, int64_t ws_bytes, void *stream) {
+    if (!dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
+    if (b != 4) return WQ_ERR_UNSUPPORTED_BITS;
+    if (int s = check_group(K, group)) return s;
+    if (layout != WQ_LAYOUT_DENSE && layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
+    if ((layout == WQ_LAYOUT_DENSE) != (scales_d != nullptr)) return WQ_ERR_BAD_LAYOUT;
+    if (out_dtype != WQ_OUT_BF16 && out_dtype != WQ_OUT_F32) return WQ_ERR_INVALID_ARG;
+    if (M == 0) return WQ_OK;
+    if (!A_d || !W_d || !Y_d) return WQ_ERR_INVALID_ARG;
+    if (!aligned16(A_d) || !aligned16(W_d) || !aligned16(Y_d) ||
+        (scales_d && !aligned16(scales_d)) || (ws_d && !aligned16(ws_d)))
+        return WQ_ERR_MISALIGNED;
+    const int64_t need = wq::a8_ws_bytes(M, N, K);
+    if (!ws_d || ws_bytes < need) return WQ_ERR_WORKSPACE;
+    if (int s = check_device()) return s;
+    hipError_t e = wq::launch_gemm_a8(A_d, M, N, K, W_d, layout == WQ_LAYOUT_TILED, scales_d, Y_d,
+                                      out_dtype == WQ_OUT_F32, ws_d, (hipStream_t)stream);
+    return e == hipSuccess ? WQ_OK : hip_fail(e);
+}
+
+}  // extern "C"

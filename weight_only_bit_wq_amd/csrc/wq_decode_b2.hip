@@ -1,0 +1,9 @@
+// Decode kernels for b = 2 (one bit width per translation unit so the
+// library builds in parallel).
+#include "wq_decode_kernel.h"
+
+namespace wq {
+template hipError_t decode_b<2>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool,
+                                const uint16_t *, uint16_t *, void *, const DecodePlan &,
+                                hipStream_t);
+}  // namespace wq

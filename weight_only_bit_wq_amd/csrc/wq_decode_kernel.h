@@ -1,0 +1,255 @@
+// wq_decode_kernel.h -- WNA16 decode path (M <= 16): HBM-bound skinny GEMM.
+//
+// Small batches only read weights ("vLLM Quantization", Key points: at small
+// batch decode waits on memory, so shrinking weights speeds it up).  The
+// kernel is built so that the packed weights are read exactly once, with
+// 128-bit loads, and everything else hides under that stream.
+//
+// Work decomposition
+//   - A lane owns one output row n and, in turn, whole groups (row, g): the
+//     b 16-byte chunks of a group (128 codes) are loaded into 4b VGPRs and
+//     unpacked in registers.  In the tiled layout the 64 lanes of a wave read
+//     one 1 KB plane per load instruction.
+//   - All lanes of a wave work on the same group g, so the 128 activations
+//     of that group are wave-uniform: they are read with scalar loads and
+//     fed to v_dot2_f32_bf16 as its SGPR operand.
+//   - A workgroup (4 waves) covers 64 rows and `gps` consecutive groups, the
+//     waves interleaving groups; `splits` workgroups share one 64-row block.
+//     Partial sums go to an fp32 workspace and the last workgroup of a block
+//     to finish (atomic ticket) adds them in split order (deterministic) and
+//     writes bf16.  The ticket counter (in the workspace's counter region) is
+//     reset to zero by that workgroup.
+//
+// Arithmetic per pair of codes (b <= 7): v_perm_b32 + packed 16-bit shift
+// pull the two fields (straddling or not) into the two 16-bit halves,
+// v_and_or_b32 masks them and sets the bf16 exponent of 128, giving exactly
+// (128 + c0, 128 + c1); v_dot2_f32_bf16 multiplies by the activation pair and
+// accumulates in fp32.  Per group the constant (128 + 2^(b-1)) * sum(a) is
+// removed and the group scale applied once in fp32:
+//     acc += s[n,g] * (sum_k a_k (128 + c_k) - (128 + 2^(b-1)) sum_k a_k)
+// which is sum_k a_k s (c_k - 2^(b-1)) with the integer codes exact.
+// For b = 8 codes are whole bytes: v_cvt_f32_ubyte{0..3} converts each one
+// and an fp32 FMA accumulates (offset 128).
+#pragma once
+
+#include "wq_device.h"
+#include "wq_launch.h"
+
+namespace wq {
+
+constexpr int kDecodeWaves = 4;
+
+// Activation pairs are read CP at a time per row (one wide scalar load each),
+// so at most 64 SGPRs of activations are live.
+template <int MT>
+struct ChunkPairs {
+    static constexpr int value = MT <= 4 ? 16 : 64 / MT;
+};
+
+template <int N_>
+struct UVec;
+template <>
+struct UVec<4> { typedef unsigned type __attribute__((ext_vector_type(4))); };
+template <>
+struct UVec<8> { typedef unsigned type __attribute__((ext_vector_type(8))); };
+template <>
+struct UVec<16> { typedef unsigned type __attribute__((ext_vector_type(16))); };
+
+// Pairs P0 + I .. P0 + CP - 1 of the group, activations already in av[].
+template <int B, int MT, int CP, int P0, int I>
+struct DotChunk {
+    typedef typename UVec<CP>::type vec;
+    __device__ __forceinline__ static void run(const uint32_t *w, const vec *av, uint32_t mask,
+                                               uint32_t magic, float *d) {
+        const uint32_t wp = code_pair_bf16_plus128<B, P0 + I>(w, mask, magic);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) d[m] = dot2_bf16(av[m][I], wp, d[m]);
+        DotChunk<B, MT, CP, P0, I + 1>::run(w, av, mask, magic, d);
+    }
+};
+template <int B, int MT, int CP, int P0>
+struct DotChunk<B, MT, CP, P0, CP> {
+    typedef typename UVec<CP>::type vec;
+    __device__ __forceinline__ static void run(const uint32_t *, const vec *, uint32_t, uint32_t,
+                                               float *) {}
+};
+
+template <int B, int MT, int P0>
+struct DotPairs {
+    static constexpr int CP = ChunkPairs<MT>::value;
+    typedef typename UVec<CP>::type vec;
+    __device__ __forceinline__ static void run(const uint32_t *w, const uint32_t *a,
+                                               const int *row_off, uint32_t mask,
+                                               uint32_t magic, float *d) {
+        vec av[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) av[m] = *reinterpret_cast<const vec *>(a + row_off[m] + P0);
+        DotChunk<B, MT, CP, P0, 0>::run(w, av, mask, magic, d);
+        DotPairs<B, MT, P0 + CP>::run(w, a, row_off, mask, magic, d);
+    }
+};
+template <int B, int MT>
+struct DotPairs<B, MT, 64> {
+    __device__ __forceinline__ static void run(const uint32_t *, const uint32_t *, const int *,
+                                               uint32_t, uint32_t, float *) {}
+};
+
+// b = 8: codes are whole bytes.  Each byte goes through v_cvt_f32_ubyteN and
+// a pair is packed to bf16 with v_cvt_pk_bf16_f32 (values 0..255 are exact in
+// bf16), then the same dot2 path as narrower codes with offset 128.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bytes_to_bf16x2(uint32_t x, int lo_byte) {
+    f32x2_t f;
+    f.x = (float)((x >> (8 * lo_byte)) & 0xFFu);
+    f.y = (float)((x >> (8 * lo_byte + 8)) & 0xFFu);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+template <int MT>
+__device__ __forceinline__ void dot_bytes(const uint32_t *w, const uint32_t *a,
+                                          const int *row_off, float *d) {
+    constexpr int CP = ChunkPairs<MT>::value;
+    typedef typename UVec<CP>::type vec;
+#pragma unroll
+    for (int p0 = 0; p0 < 64; p0 += CP) {
+        vec av[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) av[m] = *reinterpret_cast<const vec *>(a + row_off[m] + p0);
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+            const int p = p0 + i;
+            const uint32_t wp = bytes_to_bf16x2(w[p >> 1], 2 * (p & 1));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) d[m] = dot2_bf16(av[m][i], wp, d[m]);
+        }
+    }
+}
+
+template <int B, int MT, class WL>
+__global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict__ A, int M,
+                                                     int N, int K, WL wl,
+                                                     uint16_t *__restrict__ Y,
+                                                     float *__restrict__ part,
+                                                     unsigned *__restrict__ counters,
+                                                     int splits, int gps) {
+    __shared__ float red[kDecodeWaves][MT][64];
+    __shared__ unsigned ticket_sh;
+
+    const int G = K / kGroup;
+    const int R = blockIdx.x / splits;
+    const int s = blockIdx.x - R * splits;
+    const int g_begin = s * gps;
+    const int g_end = min(G, g_begin + gps);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int Kp = K / 2;  // activation pairs per row
+    const uint32_t *A2 = reinterpret_cast<const uint32_t *>(A);
+
+    const int64_t n = (int64_t)R * 64 + lane;
+    // Dense rows beyond N do not exist: read row N-1 and drop the result.
+    // Tiled blobs hold zero-padded rows, so nothing to clamp there.
+    const int64_t nr = (WL::kTiled || n < N) ? n : (int64_t)N - 1;
+    constexpr float kOff = (B == 8) ? 128.0f : (float)(128 + (1 << (B - 1)));
+
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    const uint32_t mask = __builtin_amdgcn_readfirstlane(pair_mask<B < 8 ? B : 7>());
+    const uint32_t magic = in_vgpr(kBf16Magic128x2);
+
+    int row_off[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) row_off[m] = min(m, M - 1) * Kp;
+
+    for (int g = g_begin + wave; g < g_end; g += kDecodeWaves) {
+        uint32_t w[4 * B];
+        load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), w);
+        const float sc = bf16_to_f32(wl.scale(nr, g));
+        // Wave-uniform activation pairs of this group for each row m.
+        const uint32_t *a = A2 + (int64_t)g * 64;
+        float d[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) d[m] = 0.0f;
+        if constexpr (B == 8)
+            dot_bytes<MT>(w, a, row_off, d);
+        else
+            DotPairs<B, MT, 0>::run(w, a, row_off, mask, magic, d);
+        // Sum of this group's activations per row m: lane l adds pair l, then
+        // a wave butterfly (identical result in every lane).
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const float asum = wave_sum(dot2_bf16(a[row_off[m] + lane], 0x3F803F80u, 0.0f));
+            acc[m] = fmaf(sc, fmaf(-kOff, asum, d[m]), acc[m]);
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    __syncthreads();
+
+    const int Npad = (int)(gridDim.x / splits) * 64;
+    if (splits == 1) {
+        for (int m = wave; m < MT; m += kDecodeWaves) {
+            const float v = red[0][m][lane] + red[1][m][lane] + red[2][m][lane] + red[3][m][lane];
+            if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(v);
+        }
+        return;
+    }
+
+    for (int m = wave; m < MT; m += kDecodeWaves) {
+        const float v = red[0][m][lane] + red[1][m][lane] + red[2][m][lane] + red[3][m][lane];
+        part[((int64_t)s * MT + m) * Npad + n] = v;
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) ticket_sh = atomicAdd(&counters[R], 1u);
+    __syncthreads();
+    if (ticket_sh != (unsigned)(splits - 1)) return;
+    __threadfence();
+    for (int m = wave; m < MT; m += kDecodeWaves) {
+        float v = 0.0f;
+        for (int t = 0; t < splits; ++t) v += part[((int64_t)t * MT + m) * Npad + n];
+        if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(v);
+    }
+    if (threadIdx.x == 0) counters[R] = 0u;  // leave the counter region zero
+}
+
+template <int B, int MT>
+hipError_t decode_bm(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
+                            bool tiled, const uint16_t *scales, uint16_t *Y, void *ws,
+                            const DecodePlan &p, hipStream_t stream) {
+    const int G = (int)(K / kGroup);
+    float *part = nullptr;
+    unsigned *counters = nullptr;
+    if (p.splits > 1) {
+        counters = static_cast<unsigned *>(ws);
+        part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
+    }
+    const dim3 grid((unsigned)(p.rowblocks * p.splits));
+    if (tiled) {
+        TiledW wl{static_cast<const uint8_t *>(W), G, B};
+        hipLaunchKernelGGL((decode_kernel<B, MT, TiledW>), grid, dim3(256), 0, stream, A,
+                           (int)M, (int)N, (int)K, wl, Y, part, counters, p.splits, p.gps);
+    } else {
+        DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
+        hipLaunchKernelGGL((decode_kernel<B, MT, DenseW>), grid, dim3(256), 0, stream, A,
+                           (int)M, (int)N, (int)K, wl, Y, part, counters, p.splits, p.gps);
+    }
+    return hipGetLastError();
+}
+
+template <int B>
+hipError_t decode_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
+                           bool tiled, const uint16_t *scales, uint16_t *Y, void *ws,
+                           const DecodePlan &p, hipStream_t stream) {
+    switch (p.mt) {
+        case 1: return decode_bm<B, 1>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
+        case 2: return decode_bm<B, 2>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
+        case 4: return decode_bm<B, 4>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
+        case 8: return decode_bm<B, 8>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
+        case 16: return decode_bm<B, 16>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace wq

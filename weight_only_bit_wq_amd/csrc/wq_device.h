@@ -1,0 +1,198 @@
+// wq_device.h -- device-side building blocks shared by the libwq kernels:
+// weight-buffer addressing for the two layouts, the in-register bitstream
+// unpacker and bf16 helpers.
+//
+// Bitstream facts used throughout (model card
+// "Qwen3.8-27B-INT6-Mixed-AutoRound", Findings: dense layout along
+// in_features, ceil(in * bits / 32) words per row):
+//   - a group of 128 codes occupies exactly 128*b bits = 16*b bytes = b
+//     16-byte chunks, and starts 16-byte aligned inside its row, for every b;
+//   - so one lane can own a whole (row, group) with b 128-bit loads, and
+//     codes that straddle 32-bit words never straddle lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+constexpr int kGroup = 128;     // codes per scale group
+constexpr int kTileRows = 64;   // rows per tile in the tiled layout (one wave)
+
+__host__ __device__ constexpr int tile_code_bytes(int b) { return b * 1024; }
+__host__ __device__ constexpr int tile_bytes(int b) { return b * 1024 + 128; }
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Weight addressing.  A "slot" is one (row, group): b chunks of 16 bytes plus
+// one bf16 scale.
+// ---------------------------------------------------------------------------
+
+// Dense rows as written by wq_pack; scales are a separate [N, G] array.
+struct DenseW {
+    static constexpr bool kTiled = false;
+    const uint8_t *w;
+    const uint16_t *s;
+    int64_t row_bytes;  // 4 * ceil(K*b/32) == 16 * b * G
+    int G;
+    int b;
+    __device__ const uint4 *chunks(int64_t n, int g) const {
+        return reinterpret_cast<const uint4 *>(w + n * row_bytes + (int64_t)g * 16 * b);
+    }
+    __device__ int64_t chunk_stride() const { return 1; }  // in uint4 units
+    __device__ uint16_t scale(int64_t n, int g) const { return s[n * G + g]; }
+};
+
+// Tiled blob written by wq_repack: per (64-row block, group) a tile of b
+// planes of 1 KB (plane j: chunk j of each of the 64 rows) + 64 bf16 scales.
+struct TiledW {
+    static constexpr bool kTiled = true;
+    const uint8_t *w;
+    int G;
+    int b;
+    __device__ const uint8_t *tile(int64_t n, int g) const {
+        return w + ((n >> 6) * (int64_t)G + g) * (int64_t)tile_bytes(b);
+    }
+    __device__ const uint4 *chunks(int64_t n, int g) const {
+        return reinterpret_cast<const uint4 *>(tile(n, g) + (n & 63) * 16);
+    }
+    __device__ int64_t chunk_stride() const { return 64; }  // 1 KB in uint4 units
+    __device__ uint16_t scale(int64_t n, int g) const {
+        return reinterpret_cast<const uint16_t *>(tile(n, g) + tile_code_bytes(b))[n & 63];
+    }
+};
+
+// ---------------------------------------------------------------------------
+// In-register unpacker.
+//
+// A slot's 128 codes sit in 4*B 32-bit words w[].  code_pair<B, P>() returns
+// codes 2P and 2P+1 as two 16-bit lanes of one register, (c0 | c1 << 16):
+//   1. v_perm_b32 gathers, from the two words that hold them, the byte pair
+//      starting at each code's first byte into the low and high halves;
+//   2. one packed 16-bit shift drops each half's bit offset inside its byte;
+//   3. the caller masks (and can OR a constant in the same instruction).
+// Every index is a compile-time constant, so this is 2 VALU ops per pair
+// plus the caller's mask, whether or not the codes straddle a word.
+// A code's bits [o, o+B) always fit in the 16-bit window starting at byte
+// o/8 because B <= 9.
+// ---------------------------------------------------------------------------
+
+template <int B, int P>
+struct PairSel {
+    static constexpr int o0 = 2 * P * B;
+    static constexpr int o1 = o0 + B;
+    static constexpr int byte0 = o0 >> 3;
+    static constexpr int byte1 = o1 >> 3;
+    static constexpr int word = byte0 >> 2;          // low word of the window
+    static constexpr int base = 4 * word;
+    static constexpr uint32_t sel = (uint32_t)(byte0 - base) |
+                                    ((uint32_t)(byte0 + 1 - base) << 8) |
+                                    ((uint32_t)(byte1 - base) << 16) |
+                                    ((uint32_t)(byte1 + 1 - base) << 24);
+    static constexpr int sh0 = o0 & 7;
+    static constexpr int sh1 = o1 & 7;
+    static constexpr bool has_hi = word + 1 < 4 * B;  // else the window's top is padding
+    static_assert(byte1 + 1 - base < 8, "pair window exceeds two words");
+};
+
+__device__ __forceinline__ uint32_t pk_shr16(uint32_t x, int s0, int s1) {
+    u16x2 v = __builtin_bit_cast(u16x2, x);
+    u16x2 s = {(unsigned short)s0, (unsigned short)s1};
+    return __builtin_bit_cast(uint32_t, (u16x2)(v >> s));
+}
+
+// Codes 2P, 2P+1 of the slot, unmasked (garbage above bit B of each half).
+template <int B, int P>
+__device__ __forceinline__ uint32_t code_pair_raw(const uint32_t *w) {
+    using S = PairSel<B, P>;
+    const uint32_t lo = w[S::word];
+    const uint32_t hi = S::has_hi ? w[S::word + 1] : 0u;
+    const uint32_t x = __builtin_amdgcn_perm(hi, lo, S::sel);
+    if constexpr (S::sh0 == 0 && S::sh1 == 0) return x;
+    return pk_shr16(x, S::sh0, S::sh1);
+}
+
+template <int B>
+__host__ __device__ constexpr uint32_t pair_mask() {
+    return ((1u << B) - 1u) * 0x00010001u;
+}
+
+// Codes 2P and 2P+1 as (c0 | c1 << 16).
+template <int B, int P>
+__device__ __forceinline__ uint32_t code_pair(const uint32_t *w) {
+    return code_pair_raw<B, P>(w) & pair_mask<B>();
+}
+
+// (x & m) | c in one v_and_or_b32.  gfx9 VOP3 encodings take no literal
+// constants and at most one scalar operand, so the mask comes in an SGPR and
+// the constant in a VGPR (the caller materialises both once).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m_sgpr, uint32_t c_vgpr) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m_sgpr), "v"(c_vgpr));
+    return r;
+}
+
+// For B <= 7: the pair as two bf16 values (128 + c0, 128 + c1), exact.
+// bf16 0x4300 is 128.0 with a zero 7-bit mantissa, so OR-ing a code c < 128
+// into the mantissa gives exactly 128 + c.  `mask` must hold pair_mask<B>()
+// and `magic` kBf16Magic128x2.
+constexpr uint32_t kBf16Magic128x2 = 0x43004300u;
+template <int B, int P>
+__device__ __forceinline__ uint32_t code_pair_bf16_plus128(const uint32_t *w, uint32_t mask,
+                                                           uint32_t magic) {
+    static_assert(B <= 7, "magic-exponent conversion needs codes < 128");
+    return and_or(code_pair_raw<B, P>(w), mask, magic);
+}
+
+// Materialise a constant in a VGPR (opaque to constant folding).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+    return r;
+}
+
+// Load the 4*B words of one slot (B 16-byte chunks, `stride` uint4 apart).
+template <int B>
+__device__ __forceinline__ void load_slot(const uint4 *p, int64_t stride, uint32_t *w) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + j * stride));
+        w[4 * j + 0] = v.x;
+        w[4 * j + 1] = v.y;
+        w[4 * j + 2] = v.z;
+        w[4 * j + 3] = v.w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs finite or inf; NaN kept NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Sum over the 64 lanes of a wave (fixed butterfly order: deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace wq

@@ -1,0 +1,53 @@
+// wq_launch.h -- host-side launchers of the libwq kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+// ---- repack / unpack (wq_unpack.hip) ----
+hipError_t launch_repack_tiled(const uint32_t *packed, const uint16_t *scales, int64_t N,
+                               int64_t K, int b, void *out, hipStream_t stream);
+hipError_t launch_unpack(const void *W, bool tiled, const uint16_t *scales_unused, int64_t N,
+                         int64_t K, int b, uint8_t *codes, hipStream_t stream);
+
+// Every workspace starts with this many bytes of counters that must be zero
+// before a call and are zero again after it (whatever the op or shape), so
+// one workspace can serve any sequence of stream-ordered calls.  Scratch that
+// need not start at zero follows at kWsScratchOffset.
+constexpr int64_t kWsCounterBytes = 65536;
+constexpr int kWsMaxCounters = (int)(kWsCounterBytes / 4);
+constexpr int64_t kWsScratchOffset = kWsCounterBytes;
+
+// ---- decode path, M <= kDecodeMaxM (wq_decode.hip) ----
+constexpr int kDecodeMaxM = 16;
+
+struct DecodePlan {
+    int mt;         // rows of A handled per kernel instance (template M tile)
+    int splits;     // K splits across workgroups
+    int gps;        // groups per split
+    int rowblocks;  // ceil(N / 64)
+    int64_t ws_bytes;
+};
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b);
+
+hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
+                         bool tiled, const uint16_t *scales, int b, uint16_t *Y, void *ws,
+                         const DecodePlan &plan, hipStream_t stream);
+
+// ---- prefill path, M > kDecodeMaxM (wq_prefill.hip) ----
+int64_t prefill_ws_bytes(int64_t M, int64_t N, int64_t K, int b);
+hipError_t launch_prefill(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
+                          bool tiled, const uint16_t *scales, int b, uint16_t *Y, void *ws,
+                          hipStream_t stream);
+
+// ---- W4A8 (wq_a8.hip) ----
+hipError_t launch_quant_act(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq, float *sa,
+                            hipStream_t stream);
+int64_t a8_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
+                          bool tiled, const uint16_t *scales, void *Y, bool out_f32, void *ws,
+                          hipStream_t stream);
+
+}  // namespace wq
