@@ -164,6 +164,64 @@ def bench_w4a8(torch, wq, synth, reps: int):
     return out
 
 
+CAL_BYTES = 64 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "decode_b6_m1_hbm_traffic.md")
+DECODE_SOURCES = ("weight_only_bit_wq_amd/csrc/wq_decode_kernel.h",
+                  "weight_only_bit_wq_amd/csrc/wq_device.h",
+                  "weight_only_bit_wq_amd/csrc/wq_decode.hip")
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the b = 6 decode kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().split()[0]
+    if vals.get("source_hash") != decode_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def pmc_run(torch, wq, synth, copies: int):
+    """Kernels for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE: the b = 6 decode
+    kernel, then two single-purpose kernels of known size (a 64 MiB fill writes
+    64 MiB, a 64 MiB sum reads 64 MiB) to scale the counters."""
+    l6 = DecodeLayer(6, copies, torch, wq, synth)
+    for i in range(16):
+        l6.call(wq, i)
+    torch.cuda.synchronize()
+    bufs = [torch.empty(CAL_BYTES // 4, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    for i in range(16):
+        bufs[i % copies].fill_(1.0)
+    torch.cuda.synchronize()
+    for i in range(16):
+        torch.sum(bufs[i % copies], dim=0, out=out)
+    torch.cuda.synchronize()
+    log("pmc run done: decode b=6 M=1 x16 (%d algorithmic bytes each); fill x16 and sum x16 "
+        "of %d bytes; decode source hash %s" % (l6.bytes, CAL_BYTES, decode_source_hash()))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +231,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip prefill and W4A8 figures")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="no timing: 16 launches of the b=6 decode kernel, then a 64 MiB fill and "
+                         "a 64 MiB sum (known-size references for rocprofv3 --pmc byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -188,6 +249,10 @@ def main():
         print("bench.py needs an MI355X (gfx950) GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.pmc_run:
+        pmc_run(torch, wq, synth, args.copies)
+        return
 
     log("setting up decode layers (b=5,6,7; %d copies each)" % args.copies)
     layers = [DecodeLayer(b, args.copies, torch, wq, synth) for b in DECODE_BITS]
@@ -234,7 +299,7 @@ def main():
     t6 = graph_time(torch, lambda: [l6.call(wq, i) for i in range(reps)], 3, 1) / reps
     achieved = l6.bytes / t6 / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                 "kernel": "decode_kernel<6,1,TiledW>", "us_per_launch": t6 * 1e6,
                 "bytes_per_launch": l6.bytes}
     log("b=6 decode kernel: %.2f us/launch, %.0f GB/s" % (t6 * 1e6, achieved))

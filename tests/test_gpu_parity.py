@@ -275,3 +275,20 @@ def test_workspace_reused_across_shapes_and_ops():
         wq.wq_gemm_a8(dev_bf16(w4.A), L4.W_d, L4.layout, None, 64, 4, ws=ws)
     torch.cuda.synchronize()
     assert not ws[:65536].any()
+
+
+@pytest.mark.parametrize("b,M,K,N", [(6, 1, 5120, 17408), (6, 4, 17408, 5120), (5, 16, 5120, 17408)])
+def test_split_k_handoff_repeated(b, M, K, N):
+    # The split-K partial sums cross workgroups (and XCDs) through device-scope
+    # atomics; 30 back-to-back calls must all equal the first, which matches
+    # the oracle.
+    w = synth.decode(M=M, b=b, N=N, K=K)
+    L = Layer(w, wq.WQ_LAYOUT_TILED)
+    A = dev_bf16(w.A)
+    Y0 = wq.wq_gemm(A, L.W_d, L.layout, None, N, b)
+    outs = [wq.wq_gemm(A, L.W_d, L.layout, None, N, b) for _ in range(30)]
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
+    assert_wna16(host_bf16_bits(Y0), y_ref, mag, "split-K b=%d M=%d" % (b, M))
+    for Y in outs:
+        assert torch.equal(Y.view(torch.int16), Y0.view(torch.int16))

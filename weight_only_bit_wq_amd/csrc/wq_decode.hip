@@ -35,15 +35,28 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b) {
     const int G = (int)(K / kGroupSize);
     p.mt = decode_mt(M);
     p.rowblocks = (int)((N + 63) / 64);
-    // Groups per split: a multiple of the 4 waves, two groups per wave by
-    // default (enough workgroups to fill 256 CUs at the layer shapes used
-    // here).  Row counts beyond the counter region run without splitting.
-    int gps = 8;
-    if (const char *e = std::getenv("WQ_DECODE_GPS")) gps = std::max(1, std::atoi(e));
-    gps = std::min(gps, G);
-    if (p.rowblocks > kWsMaxCounters) gps = G;
-    p.gps = gps;
-    p.splits = (G + gps - 1) / gps;
+    // Measured on MI355X at M = 1 (K 5120 -> N 17408 and K 17408 -> N 5120):
+    // with many 64-row blocks, 8 waves per workgroup and about one group per
+    // wave (K split in chunks of 8 groups); with fewer than 192 row blocks,
+    // 16 waves and K split so that ~240 workgroups are in flight.  Larger M
+    // tiles use fewer waves (LDS reduction table, register pressure).
+    int waves, splits;
+    if (p.rowblocks >= 192) {
+        waves = p.mt <= 8 ? 8 : 4;
+        splits = (G + 7) / 8;
+    } else {
+        waves = p.mt <= 4 ? 16 : (p.mt <= 8 ? 8 : 4);
+        splits = std::max(1, std::min(G / waves, (240 + p.rowblocks - 1) / p.rowblocks));
+    }
+    if (const char *e = std::getenv("WQ_DECODE_WAVES")) waves = std::atoi(e);
+    if (const char *e = std::getenv("WQ_DECODE_SPLITS")) splits = std::max(1, std::atoi(e));
+    if (!(waves == 4 || (waves == 8 && p.mt <= 8) || (waves == 16 && p.mt <= 4)))
+        waves = 4;
+    if (p.rowblocks > kWsMaxCounters) splits = 1;
+    splits = std::min(splits, G);
+    p.waves = waves;
+    p.gps = (G + splits - 1) / splits;
+    p.splits = (G + p.gps - 1) / p.gps;
     if (p.splits > 1)
         p.ws_bytes = kWsScratchOffset + (int64_t)p.splits * p.mt * p.rowblocks * 64 * 4;
     else

@@ -37,7 +37,6 @@
 
 namespace wq {
 
-constexpr int kDecodeWaves = 4;
 
 // Activation pairs are read CP at a time per row (one wide scalar load each),
 // so at most 64 SGPRs of activations are live.
@@ -125,14 +124,15 @@ __device__ __forceinline__ void dot_bytes(const uint32_t *w, const uint32_t *a,
     }
 }
 
-template <int B, int MT, class WL>
-__global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict__ A, int M,
-                                                     int N, int K, WL wl,
-                                                     uint16_t *__restrict__ Y,
-                                                     float *__restrict__ part,
-                                                     unsigned *__restrict__ counters,
-                                                     int splits, int gps) {
-    __shared__ float red[kDecodeWaves][MT][64];
+template <int B, int MT, int W, class WL>
+__global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restrict__ A, int M,
+                                                        int N, int K, WL wl,
+                                                        uint16_t *__restrict__ Y,
+                                                        float *__restrict__ part,
+                                                        unsigned *__restrict__ counters,
+                                                        int splits, int gps) {
+    static_assert(W * MT <= 64, "LDS reduction table");
+    __shared__ float red[W][MT][64];
     __shared__ unsigned ticket_sh;
 
     const int G = K / kGroup;
@@ -161,9 +161,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict_
 #pragma unroll
     for (int m = 0; m < MT; ++m) row_off[m] = min(m, M - 1) * Kp;
 
-    for (int g = g_begin + wave; g < g_end; g += kDecodeWaves) {
-        uint32_t w[4 * B];
-        load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), w);
+    // Each wave walks groups g_begin + wave, + W, ...; the next group's chunks
+    // are loaded before the current one is computed.
+    uint32_t w[4 * B], wn[4 * B];
+    int g = g_begin + wave;
+    if (g < g_end) load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), w);
+    for (; g < g_end; g += W) {
+        const int gn = g + W;
+        if (gn < g_end) load_slot<B>(wl.chunks(nr, gn), wl.chunk_stride(), wn);
         const float sc = bf16_to_f32(wl.scale(nr, g));
         // Wave-uniform activation pairs of this group for each row m.
         const uint32_t *a = A2 + (int64_t)g * 64;
@@ -175,12 +180,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict_
         else
             DotPairs<B, MT, 0>::run(w, a, row_off, mask, magic, d);
         // Sum of this group's activations per row m: lane l adds pair l, then
-        // a wave butterfly (identical result in every lane).
+        // a DPP reduction across the wave (wave-uniform result).
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const float asum = wave_sum(dot2_bf16(a[row_off[m] + lane], 0x3F803F80u, 0.0f));
+            const float asum =
+                wave_sum_uniform(dot2_bf16(a[row_off[m] + lane], 0x3F803F80u, 0.0f));
             acc[m] = fmaf(sc, fmaf(-kOff, asum, d[m]), acc[m]);
         }
+#pragma unroll
+        for (int i = 0; i < 4 * B; ++i) w[i] = wn[i];
     }
 
 #pragma unroll
@@ -189,35 +197,48 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict_
 
     const int Npad = (int)(gridDim.x / splits) * 64;
     if (splits == 1) {
-        for (int m = wave; m < MT; m += kDecodeWaves) {
-            const float v = red[0][m][lane] + red[1][m][lane] + red[2][m][lane] + red[3][m][lane];
+        for (int m = wave; m < MT; m += W) {
+            float v = red[0][m][lane];
+#pragma unroll
+            for (int w2 = 1; w2 < W; ++w2) v += red[w2][m][lane];
             if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(v);
         }
         return;
     }
 
-    for (int m = wave; m < MT; m += kDecodeWaves) {
-        const float v = red[0][m][lane] + red[1][m][lane] + red[2][m][lane] + red[3][m][lane];
-        part[((int64_t)s * MT + m) * Npad + n] = v;
+    // Cross-workgroup reduction.  All shared data moves through device-scope
+    // relaxed atomics (coherent across the XCDs' L2s without the L2
+    // write-back/invalidate an agent-scope fence costs): partials are atomic
+    // stores, the barrier's s_waitcnt completes them before the ticket RMW,
+    // and the last workgroup reads them back with atomic loads.
+    for (int m = wave; m < MT; m += W) {
+        float v = red[0][m][lane];
+#pragma unroll
+        for (int w2 = 1; w2 < W; ++w2) v += red[w2][m][lane];
+        __hip_atomic_store(&part[((int64_t)s * MT + m) * Npad + n], v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) ticket_sh = atomicAdd(&counters[R], 1u);
+    __syncthreads();  // every wave's partial stores have completed
+    if (threadIdx.x == 0)
+        ticket_sh = __hip_atomic_fetch_add(&counters[R], 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket_sh != (unsigned)(splits - 1)) return;
-    __threadfence();
-    for (int m = wave; m < MT; m += kDecodeWaves) {
+    for (int m = wave; m < MT; m += W) {
         float v = 0.0f;
-        for (int t = 0; t < splits; ++t) v += part[((int64_t)t * MT + m) * Npad + n];
+        for (int t = 0; t < splits; ++t)
+            v += __hip_atomic_load(&part[((int64_t)t * MT + m) * Npad + n], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(v);
     }
-    if (threadIdx.x == 0) counters[R] = 0u;  // leave the counter region zero
+    if (threadIdx.x == 0)  // leave the counter region zero
+        __hip_atomic_store(&counters[R], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int B, int MT>
-hipError_t decode_bm(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                            bool tiled, const uint16_t *scales, uint16_t *Y, void *ws,
-                            const DecodePlan &p, hipStream_t stream) {
+template <int B, int MT, int W>
+hipError_t decode_bmw(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W_,
+                      bool tiled, const uint16_t *scales, uint16_t *Y, void *ws,
+                      const DecodePlan &p, hipStream_t stream) {
     const int G = (int)(K / kGroup);
     float *part = nullptr;
     unsigned *counters = nullptr;
@@ -227,15 +248,32 @@ hipError_t decode_bm(const uint16_t *A, int64_t M, int64_t N, int64_t K, const v
     }
     const dim3 grid((unsigned)(p.rowblocks * p.splits));
     if (tiled) {
-        TiledW wl{static_cast<const uint8_t *>(W), G, B};
-        hipLaunchKernelGGL((decode_kernel<B, MT, TiledW>), grid, dim3(256), 0, stream, A,
+        TiledW wl{static_cast<const uint8_t *>(W_), G, B};
+        hipLaunchKernelGGL((decode_kernel<B, MT, W, TiledW>), grid, dim3(64 * W), 0, stream, A,
                            (int)M, (int)N, (int)K, wl, Y, part, counters, p.splits, p.gps);
     } else {
-        DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
-        hipLaunchKernelGGL((decode_kernel<B, MT, DenseW>), grid, dim3(256), 0, stream, A,
+        DenseW wl{static_cast<const uint8_t *>(W_), scales, (int64_t)16 * B * G, G, B};
+        hipLaunchKernelGGL((decode_kernel<B, MT, W, DenseW>), grid, dim3(64 * W), 0, stream, A,
                            (int)M, (int)N, (int)K, wl, Y, part, counters, p.splits, p.gps);
     }
     return hipGetLastError();
+}
+
+template <int B, int MT>
+hipError_t decode_bm(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W_,
+                     bool tiled, const uint16_t *scales, uint16_t *Y, void *ws,
+                     const DecodePlan &p, hipStream_t stream) {
+    if constexpr (MT <= 4) {
+        if (p.waves == 16)
+            return decode_bmw<B, MT, 16>(A, M, N, K, W_, tiled, scales, Y, ws, p, stream);
+    }
+    if constexpr (MT <= 8) {
+        if (p.waves == 8)
+            return decode_bmw<B, MT, 8>(A, M, N, K, W_, tiled, scales, Y, ws, p, stream);
+    }
+    if (p.waves == 4)
+        return decode_bmw<B, MT, 4>(A, M, N, K, W_, tiled, scales, Y, ws, p, stream);
+    return hipErrorInvalidValue;
 }
 
 template <int B>

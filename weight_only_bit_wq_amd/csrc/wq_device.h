@@ -195,4 +195,23 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Wave-uniform sum over the 64 lanes with DPP (no LDS round trips): quad
+// swaps, half-row and row mirrors give every lane its 16-lane row sum, two
+// row broadcasts carry the rows into lane 63, which is read into an SGPR.
+// Fixed order, so the result is deterministic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+    const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false);
+    return x + __int_as_float(t);
+}
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 }  // namespace wq

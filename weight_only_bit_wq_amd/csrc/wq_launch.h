@@ -27,6 +27,7 @@ struct DecodePlan {
     int mt;         // rows of A handled per kernel instance (template M tile)
     int splits;     // K splits across workgroups
     int gps;        // groups per split
+    int waves;      // waves per workgroup (4, 8 or 16; 16 only for mt <= 4, 8 for mt <= 8)
     int rowblocks;  // ceil(N / 64)
     int64_t ws_bytes;
 };
