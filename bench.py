@@ -18,7 +18,10 @@ Also reported on the same line:
   prefill       TFLOP/s of wq_gemm at M = 4096 (up: K 5120 -> N 17408, down:
                 K 17408 -> N 5120, b = 6) against the 2.5 PFLOP/s bf16 peak;
   w4a8          TOP/s of wq_gemm_a8 at M = 2048 / 8192 (K 5120, N 17408) against
-                the 5.0 POPS int8 peak, with wq_gemm at b = 4 on the same shape.
+                the 5.0 POPS int8 peak, with wq_gemm at b = 4 on the same shape;
+  stack         the 64-layer mixed-bit (7 / 5 / 6) stack plus the 8-bit 248320 x
+                5120 vocabulary head (9.98 GB of weights): M = 1 in TB/s, M = 512
+                in TFLOP/s.
 """
 from __future__ import annotations
 
@@ -222,6 +225,31 @@ def pmc_run(torch, wq, synth, copies: int):
         "of %d bytes; decode source hash %s" % (l6.bytes, CAL_BYTES, decode_source_hash()))
 
 
+def bench_stack(torch, wq, reps: int):
+    """The 64-layer mixed-bit stack + 8-bit head: M = 1 (HBM-bound, TB/s of
+    algorithmic bytes) and M = 512 (TFLOP/s).  One forward = 129 wq_gemm calls,
+    captured in one graph."""
+    from weight_only_bit_wq_amd import synth
+    from weight_only_bit_wq_amd.stack import Stack
+    st = Stack(torch, wq)
+    out = {"layers": synth.STACK_LAYERS, "weight_bytes": st.bytes(0)}
+    for M in (1, 512):
+        x = torch.from_numpy(synth.stack_input(M).view(np.int16)).cuda().view(torch.bfloat16)
+        bufs = st.buffers(M)
+        t = graph_time(torch, lambda: st.forward(x, bufs), reps, 1)
+        if M == 1:
+            bps = st.bytes(1) / t
+            out["M1"] = {"ms": t * 1e3, "TB/s": bps / 1e12, "frac_of_hbm_peak": bps / 1e9 / HBM_PEAK_GBS}
+        else:
+            fl = st.flops(M) / t
+            out["M512"] = {"ms": t * 1e3, "TFLOP/s": fl / 1e12,
+                           "frac_of_peak": fl / 1e12 / BF16_PEAK_TFLOPS}
+        del bufs, x
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +359,9 @@ def main():
         torch.cuda.empty_cache()
         log("w4a8 M=2048/8192")
         result["w4a8"] = bench_w4a8(torch, wq, synth, reps=10)
+        torch.cuda.empty_cache()
+        log("stack: 64 mixed-bit layers + 8-bit head, M=1 and 512")
+        result["stack"] = bench_stack(torch, wq, reps=3)
     if not args.no_cpu:
         import oracle
         log("cpu oracle baseline (~%.0f s)" % args.cpu_seconds)

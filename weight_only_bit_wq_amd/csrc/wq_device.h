@@ -44,6 +44,16 @@ struct DenseW {
     }
     __device__ int64_t chunk_stride() const { return 1; }  // in uint4 units
     __device__ uint16_t scale(int64_t n, int g) const { return s[n * G + g]; }
+    // Loop-invariant addressing: slot (n, g) starts at slot0(n) + g *
+    // slot_step() bytes; its dword d at + dword_off(d); its scale at
+    // scale0(n) + g * scale_step() bytes.
+    __device__ const uint8_t *slot0(int64_t n) const { return w + n * row_bytes; }
+    __device__ int64_t slot_step() const { return (int64_t)16 * b; }
+    __device__ static constexpr int dword_off(int d) { return 4 * d; }
+    __device__ const uint8_t *scale0(int64_t n) const {
+        return reinterpret_cast<const uint8_t *>(s + n * G);
+    }
+    __device__ int64_t scale_step() const { return 2; }
 };
 
 // Tiled blob written by wq_repack: per (64-row block, group) a tile of b
@@ -63,6 +73,14 @@ struct TiledW {
     __device__ uint16_t scale(int64_t n, int g) const {
         return reinterpret_cast<const uint16_t *>(tile(n, g) + tile_code_bytes(b))[n & 63];
     }
+    // Loop-invariant addressing (see DenseW).
+    __device__ const uint8_t *slot0(int64_t n) const { return tile(n, 0) + (n & 63) * 16; }
+    __device__ int64_t slot_step() const { return tile_bytes(b); }
+    __device__ static constexpr int dword_off(int d) { return (d >> 2) * 1024 + (d & 3) * 4; }
+    __device__ const uint8_t *scale0(int64_t n) const {
+        return tile(n, 0) + tile_code_bytes(b) + (n & 63) * 2;
+    }
+    __device__ int64_t scale_step() const { return tile_bytes(b); }
 };
 
 // ---------------------------------------------------------------------------

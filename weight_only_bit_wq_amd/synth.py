@@ -146,3 +146,40 @@ def layer_bits(layer: int, n_layers: int = 64) -> int:
     if layer < 10 or layer >= n_layers - 10:
         return 7
     return 5 if layer % 2 == 0 else 6
+
+
+# --- the mixed-bit 64-layer stack with an 8-bit vocabulary head --------------
+
+STACK_LAYERS = 64
+STACK_HIDDEN = 5120
+STACK_INTER = 17408
+STACK_VOCAB = 248320
+
+
+def stack_scale_sigma(K: int, b: int) -> float:
+    """Gain-normalising scale magnitude for chained layers: sigma =
+    1 / (sqrt(K) * rms(q)) with rms(q) = 2^(b-1) / sqrt(3) for uniform codes,
+    so each layer keeps activations at unit scale and 128 chained layers stay
+    finite."""
+    return float(np.sqrt(3.0) / (np.sqrt(K) * (1 << (b - 1))))
+
+
+def stack_weights(b: int, kind: str, seed: int = 4, N: int | None = None,
+                  K: int | None = None):
+    """One weight set of the stack: kind 'up' (K 5120 -> N 17408), 'down'
+    (K 17408 -> N 5120) or 'head' (K 5120 -> N 248320, b = 8).  Codes uniform,
+    scales |N(0, sigma)| with a random sign.  Returns (codes, scales)."""
+    dims = {"up": (STACK_INTER, STACK_HIDDEN), "down": (STACK_HIDDEN, STACK_INTER),
+            "head": (STACK_VOCAB, STACK_HIDDEN)}[kind]
+    N = dims[0] if N is None else N
+    K = dims[1] if K is None else K
+    sub = {"up": 0, "down": 1, "head": 2}[kind]
+    rng = np.random.default_rng([seed, b, sub])
+    codes = draw_codes(rng, N, K, b)
+    scales = draw_scales_halfnormal_signed(rng, N, K // GROUP, sigma=stack_scale_sigma(K, b))
+    return codes, scales
+
+
+def stack_input(M: int, seed: int = 4, K: int = STACK_HIDDEN) -> np.ndarray:
+    """Stack input activations ~N(0, 1), bf16 bits [M, K]."""
+    return draw_act(np.random.default_rng([seed, 99, M]), M, K)
