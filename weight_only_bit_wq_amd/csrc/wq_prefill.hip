@@ -16,11 +16,12 @@
 // multiplies that against s[n, k'/3] as extra "pseudo-groups" with scale 1.
 // No scale or code is ever rounded to bf16.
 //
-// Tiling.  Workgroup 256 (m) x 128 (n), 4 waves as 2 x 2, each wave 128 x 64
-// = 8 x 4 MFMA blocks of 16 x 16.  K runs in stages of 64 (half a group),
-// double-buffered in LDS; the next stage is fetched into registers while the
-// current one is multiplied, then written (A) or unpacked (B) into the other
-// buffer.  Workgroups an XCD runs together share an A row block.
+// Tiling.  Workgroup 256 (m) x 128 (n), 8 waves of 64 x 64 (two per SIMD).
+// K runs in LDS stages of 64 for A and whole groups of 128 for B (unpacked
+// to bf16 in LDS once per workgroup), double-buffered, register-staged.
+// Workgroups an XCD runs together share an A row block.
+#include <type_traits>
+
 #include "wq_device.h"
 #include "wq_launch.h"
 
@@ -32,7 +33,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kPM = 256;          // workgroup rows (m)
 constexpr int kPN = 128;          // workgroup cols (n)
 constexpr int kPK = 64;           // k per LDS stage
-constexpr int kPRow = kPK + 8;    // bf16 per LDS row (16-byte pad)
 constexpr int kPseudoK = 128;     // k' per pseudo-group
 
 // Codes 2P, 2P+1 of a 32-code quarter slot held in B words.
@@ -70,6 +70,30 @@ __device__ __forceinline__ uint32_t quarter_pair(const uint32_t *w, uint32_t mas
         uint32_t x = __builtin_amdgcn_perm(hi, lo, S::sel);
         if constexpr (S::sh0 != 0 || S::sh1 != 0) x = pk_shr16(x, S::sh0, S::sh1);
         return and_or(x, mask, magic);
+    }
+}
+
+// quarter_pair<B, P> for a P that is a constant after unrolling.
+template <int B>
+__device__ __forceinline__ uint32_t quarter_pair_dyn(int p, const uint32_t *w, uint32_t mask,
+                                                     uint32_t magic) {
+    switch (p) {
+        case 0: return quarter_pair<B, 0>(w, mask, magic);
+        case 1: return quarter_pair<B, 1>(w, mask, magic);
+        case 2: return quarter_pair<B, 2>(w, mask, magic);
+        case 3: return quarter_pair<B, 3>(w, mask, magic);
+        case 4: return quarter_pair<B, 4>(w, mask, magic);
+        case 5: return quarter_pair<B, 5>(w, mask, magic);
+        case 6: return quarter_pair<B, 6>(w, mask, magic);
+        case 7: return quarter_pair<B, 7>(w, mask, magic);
+        case 8: return quarter_pair<B, 8>(w, mask, magic);
+        case 9: return quarter_pair<B, 9>(w, mask, magic);
+        case 10: return quarter_pair<B, 10>(w, mask, magic);
+        case 11: return quarter_pair<B, 11>(w, mask, magic);
+        case 12: return quarter_pair<B, 12>(w, mask, magic);
+        case 13: return quarter_pair<B, 13>(w, mask, magic);
+        case 14: return quarter_pair<B, 14>(w, mask, magic);
+        default: return quarter_pair<B, 15>(w, mask, magic);
     }
 }
 
@@ -128,47 +152,84 @@ __global__ __launch_bounds__(256) void group_sum_split_kernel(const uint16_t *__
     }
 }
 
-// One LDS stage (64 k = two 16x16x32 k-steps) of a wave's 8 x 4 blocks.
-// FIRST: the stage opens a group, so the first k-step starts from zero.
-template <bool FIRST>
-__device__ __forceinline__ void compute_stage(const uint16_t *as, const uint16_t *bs, int arow,
-                                              int brow_w, int kq, f32x4_t (&P)[8][4]) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t bfr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8_t *>(
-                &bs[(brow_w + 16 * j) * kPRow + 32 * kk + kq]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(
-                &as[(arow + 16 * i) * kPRow + 32 * kk + kq]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (FIRST && kk == 0)
-                    P[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        af, bfr[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                else
-                    P[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], P[i][j], 0, 0, 0);
-            }
-        }
-    }
+// Workgroup barrier that orders LDS only: global prefetches in flight stay
+// in flight (a full __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// LDS tiles are rows of 16-byte chunks (8 bf16 of k).  Chunk c of row r is
+// stored at position c ^ (r mod 8) (A: 8 chunks per row) or c ^ (r mod 16)
+// (B: 16 chunks per row), so the 16 rows one MFMA operand read touches sit on
+// 16 distinct bank groups and the loaders' row-major writes stay conflict
+// free (no padding).
+__device__ __forceinline__ int swz8(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+__device__ __forceinline__ int swz16(int row, int chunk) {
+    return row * 16 + (chunk ^ (row & 15));
+}
+
+// Dwords [Q*B, Q*B + B) of a slot (its quarter Q: codes 32Q .. 32Q+31) into
+// w[0..B), loaded as runs of consecutive dwords within one 16-byte chunk
+// (dword d sits at WL::dword_off(d); chunks are 16-byte aligned).
+template <class WL, int D, int END>
+struct QuarterLoad {
+    static constexpr int kRun = ((D | 3) + 1 < END ? (D | 3) + 1 : END) - D;
+    __device__ __forceinline__ static void run(const uint8_t *slot, uint32_t *w) {
+        const uint8_t *p = slot + WL::dword_off(D);
+        if constexpr (kRun == 4) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        } else if constexpr (kRun == 2 && (D & 1) == 0) {
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+            w[0] = v.x; w[1] = v.y;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kRun; ++e) w[e] = reinterpret_cast<const uint32_t *>(p)[e];
+        }
+        QuarterLoad<WL, D + kRun, END>::run(slot, w + kRun);
+    }
+};
+template <class WL, int END>
+struct QuarterLoad<WL, END, END> {
+    __device__ __forceinline__ static void run(const uint8_t *, uint32_t *) {}
+};
+
+// Workgroup: 512 threads = 8 waves (two per SIMD) over a 256 (m) x 128 (n)
+// output tile; wave (wm, wn) owns rows 64 wm .. +64 and columns 64 wn .. +64
+// as 4 x 4 MFMA blocks of 16 x 16.  Per block two fp32 sets live in VGPRs:
+// P (the current group) and tot (the folded sum).
+//
+// The NP pseudo-groups run first, unpipelined (A from the pre-pass matrix,
+// B = scales, scale 1).  The G real groups are software-pipelined.  LDS: A
+// per 64-k stage (two buffers, 32 KB each), B per 128-k group (two buffers,
+// 32 KB each), the group scales per group (two buffers).  Group g (stages
+// 2g, 2g+1):
+//   stage 2g:   MFMA (A buf 0, B buf g&1, k 0..63); fold row block 3 of
+//               group g-1; write A stage 2g+1 to A buf 1; fetch A stage
+//               2g+2; unpack group g+1 into B buf (g+1)&1 and its scales
+//               into Ss; fetch the codes of group g+2;            barrier
+//   stage 2g+1: MFMA (A buf 1, B buf g&1, k 64..127); fold row blocks 0..2
+//               of group g; write A stage 2g+2 to A buf 0; fetch A stage
+//               2g+3;                                              barrier
+// Each MFMA is followed by a small slice of the other work, in a fixed
+// order: an MFMA occupies the SIMD's issue port for about two VALU slots
+// and the matrix pipe for four, so about two VALU operations per MFMA issue
+// for free.
 template <int B, class WL>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(const uint16_t *__restrict__ A,
-                                                         const uint16_t *__restrict__ Ap, int M,
-                                                         int N, int K, int Kp, WL wl,
-                                                         uint16_t *__restrict__ Y, int mtiles,
-                                                         int ntiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kPM * kPRow];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPN * kPRow];
+__global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict__ A,
+                                                      const uint16_t *__restrict__ Ap, int M,
+                                                      int N, int K, int Kp, WL wl,
+                                                      uint16_t *__restrict__ Y, int mtiles,
+                                                      int ntiles) {
+    __shared__ u32x4 Asm[2][kPM * 8];   // [stage buffer][256 rows x 8 chunks]
+    __shared__ u32x4 Bsm[2][kPN * 16];  // [group buffer][128 rows x 16 chunks]
     __shared__ float Ss[2][kPN];
 
     const int G = K / kGroup;
-    const int nreal = 2 * G;                      // stages of real groups
-    const int nstages = nreal + 2 * (Kp / kPseudoK);
+    const int NP = Kp / kPseudoK;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -187,150 +248,250 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const uint16_t *__restr
     const uint32_t mask = __builtin_amdgcn_readfirstlane(pair_mask<B < 8 ? B : 7>());
     const uint32_t magic = in_vgpr(kBf16Magic128x2);
 
-    // Loader roles.  A: 256 rows x 64 k = 2048 uint4, 8 per thread: rows
-    // arow0 + 32 i, 16-byte column ac.  Rows beyond M read row M-1 (results
-    // dropped).  B: row brow of the tile, half bpart of the stage's 64 codes
-    // (a quarter slot of 32 codes = B dwords).
-    const int arow0 = tid >> 3, ac = tid & 7;
-    int aoff[8], apoff[8];
+    // A loader: rows ar + 64 i (i < 4), chunk ac.  Rows beyond M read row
+    // M-1 (their results are dropped).
+    const int ac = tid & 7;
+    const int ar = tid >> 3;
+    const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)kPM - 1);
+    int arows[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t m = min(m0 + arow0 + 32 * i, (int64_t)M - 1);
-        aoff[i] = (int)((m - m0) * K) + 8 * ac;
-        apoff[i] = (int)((m - m0) * Kp) + 8 * ac;
-    }
+    for (int i = 0; i < 4; ++i) arows[i] = min(ar + 64 * i, mlim);
     const uint16_t *A_blk = A + m0 * K;
     const uint16_t *Ap_blk = Ap + m0 * Kp;
-    const int brow = tid & 127;
-    const int bpart = tid >> 7;
-    const int64_t bn_row = n0 + brow;
-    const int64_t bn_read = bn_row < N ? bn_row : (int64_t)N - 1;
+    const int a_lds = swz8(ar, ac);  // + 512 i
+
+    // B loader: row brow, quarter bq (wave-uniform) of each group.
+    const int brow = tid & (kPN - 1);
+    const int bq = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const int64_t bn_read = min(n0 + brow, (int64_t)N - 1);
     const uint8_t *bslot0 = wl.slot0(bn_read);
     const uint8_t *bscale0 = wl.scale0(bn_read);
-    const int64_t bstep = wl.slot_step();
-    const int64_t sstep = wl.scale_step();
+    const int bstep = (int)wl.slot_step();
+    const int sstep = (int)wl.scale_step();
 
-    uint4 areg[8];
-    uint32_t breg[16];
-    float sreg = 1.0f;
+    // MFMA operand rows and k-chunk of this lane.
+    const int arow = wm * 64 + (lane & 15);
+    const int bmrow = wn * 64 + (lane & 15);
+    const int q = lane >> 4;
 
-    auto fetch = [&](int s) {
-        const int grp = s >> 1, h = s & 1;
-        if (s < nreal) {
-            const uint16_t *src = A_blk + grp * kGroup + h * kPK;
+    u32x4 areg[4];
+    uint32_t creg[B];
+    f32x4_t tot[4][4], P[4][4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) areg[i] = *reinterpret_cast<const uint4 *>(src + aoff[i]);
-            const uint8_t *slot = bslot0 + grp * bstep;
-            const int qi = 2 * h + bpart;  // quarter of the slot
-            if (qi == 0) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < B; ++e)
-                    breg[e] = *reinterpret_cast<const uint32_t *>(slot + WL::dword_off(e));
-            } else if (qi == 1) {
-#pragma unroll
-                for (int e = 0; e < B; ++e)
-                    breg[e] = *reinterpret_cast<const uint32_t *>(slot + WL::dword_off(B + e));
-            } else if (qi == 2) {
-#pragma unroll
-                for (int e = 0; e < B; ++e)
-                    breg[e] = *reinterpret_cast<const uint32_t *>(slot + WL::dword_off(2 * B + e));
-            } else {
-#pragma unroll
-                for (int e = 0; e < B; ++e)
-                    breg[e] = *reinterpret_cast<const uint32_t *>(slot + WL::dword_off(3 * B + e));
-            }
-            sreg = bf16_to_f32(*reinterpret_cast<const uint16_t *>(bscale0 + grp * sstep));
-        } else {
-            const int kbase = (s - nreal) * kPK;
-            const uint16_t *src = Ap_blk + kbase;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) areg[i] = *reinterpret_cast<const uint4 *>(src + apoff[i]);
-            // S'[n][k'] = s[n][k'/3] for k' < 3G, else 0: 32 values, 16 pairs.
-            const int k0 = kbase + 32 * bpart;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int ka = k0 + 2 * e, kb = ka + 1;
-                const uint32_t sa =
-                    ka < 3 * G ? *reinterpret_cast<const uint16_t *>(bscale0 + (ka / 3) * sstep) : 0u;
-                const uint32_t sb =
-                    kb < 3 * G ? *reinterpret_cast<const uint16_t *>(bscale0 + (kb / 3) * sstep) : 0u;
-                breg[e] = sa | (sb << 16);
-            }
-            sreg = 1.0f;
-        }
-    };
+        for (int j = 0; j < 4; ++j) tot[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto store = [&](int s, int buf) {
-        uint16_t *as = As[buf];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int idx = tid + 256 * i;
-            const int row = idx >> 3, c = idx & 7;
-            *reinterpret_cast<uint4 *>(&as[row * kPRow + 8 * c]) = areg[i];
-        }
-        uint32_t pairs[16];
-        if (s < nreal) {
-            QuarterPairs<B, 0>::run(breg, mask, magic, pairs);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) pairs[e] = breg[e];
-        }
-        uint4 *bs = reinterpret_cast<uint4 *>(&Bs[buf][brow * kPRow + 32 * bpart]);
+    // Real stage s (64 k of group s/2), clamped to the last one.
+    auto load_a = [&](int s) __attribute__((always_inline)) {
+        s = min(s, 2 * G - 1);
+        const uint16_t *src = A_blk + (s >> 1) * kGroup + (s & 1) * kPK;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            bs[i] = make_uint4(pairs[4 * i], pairs[4 * i + 1], pairs[4 * i + 2], pairs[4 * i + 3]);
-        if (bpart == 0) Ss[buf][brow] = sreg;
+            areg[i] = *reinterpret_cast<const u32x4 *>(src + __mul24(arows[i], K) + 8 * ac);
+    };
+    auto store_a = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Asm[buf][a_lds + 512 * i] = areg[i];
+    };
+    // Quarter bq of real group g's codes (clamped to the last group): B
+    // dwords at per-wave offsets held in scalar registers.
+    int qoff[B];
+#pragma unroll
+    for (int e = 0; e < B; ++e) {
+        const int d = bq * B + e;
+        qoff[e] = __builtin_amdgcn_readfirstlane((d >> 2) * (WL::kTiled ? 1024 : 16) + (d & 3) * 4);
+    }
+    auto load_codes = [&](int g) __attribute__((always_inline)) {
+        const uint8_t *slot = bslot0 + (int64_t)min(g, G - 1) * bstep;
+#pragma unroll
+        for (int e = 0; e < B; ++e) creg[e] = *reinterpret_cast<const uint32_t *>(slot + qoff[e]);
+    };
+    // Chunk C (pairs 4C .. 4C+3, 8 codes) of the B operand (128 + c as bf16)
+    // from creg into B buffer buf.
+    auto fill_chunk = [&](int buf, auto cconst) __attribute__((always_inline)) {
+        constexpr int C = decltype(cconst)::value;
+        const u32x4 v{quarter_pair<B, 4 * C>(creg, mask, magic),
+                      quarter_pair<B, 4 * C + 1>(creg, mask, magic),
+                      quarter_pair<B, 4 * C + 2>(creg, mask, magic),
+                      quarter_pair<B, 4 * C + 3>(creg, mask, magic)};
+        Bsm[buf][swz16(brow, 4 * bq + C)] = v;
+    };
+    // Group g's scales into Ss[g&1] (the four quarter waves of a row store
+    // the same value: no branch).
+    auto store_scale = [&](int g) __attribute__((always_inline)) {
+        Ss[g & 1][brow] =
+            bf16_to_f32(*reinterpret_cast<const uint16_t *>(bscale0 + min(g, G - 1) * sstep));
+    };
+    auto fold_block = [&](int i, int j, const float(&sq)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[i][j][r] = fmaf(sq[j], P[i][j][r], tot[i][j][r]);
     };
 
-    f32x4_t tot[8][4], P[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
+    // One 64-k stage of the wave's 4 x 4 blocks: 8 steps (k-step kk, row
+    // block i) of 4 MFMAs.  After each MFMA, hook(step, j) issues a slice of
+    // the stage's other work (about one MFMA's worth of VALU), and the pair
+    // is fenced, so the order written here is the issue order: the matrix
+    // core always has queued work while the VALU slices issue.  Operands of
+    // step s+1 are read from LDS at the start of step s.  H = 0 opens a
+    // group: k-step 0 starts each block from zero.
+    auto mfma_stage = [&](int abuf, int gbuf, auto hconst, auto &&hook)
+        __attribute__((always_inline)) {
+        constexpr int H = decltype(hconst)::value;
+        const u32x4 *as = Asm[abuf];
+        const u32x4 *bs = Bsm[gbuf];
+        bf16x8_t bfr[2][4], af[2];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
+            bfr[0][j] = __builtin_bit_cast(bf16x8_t, bs[swz16(bmrow + 16 * j, 8 * H + q)]);
+        af[0] = __builtin_bit_cast(bf16x8_t, as[swz8(arow, q)]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) tot[i][j][r] = 0.0f;
-
-    fetch(0);
-    store(0, 0);
-    __syncthreads();
-
-    const int arow = wm * 128 + (lane & 15);
-    const int brow_w = wn * 64 + (lane & 15);
-    const int kq = 8 * (lane >> 4);
-
-    for (int s = 0; s < nstages; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nstages) fetch(s + 1);
-
-        const uint16_t *as = As[buf];
-        const uint16_t *bs = Bs[buf];
-        if ((s & 1) == 0)
-            compute_stage<true>(as, bs, arow, brow_w, kq, P);
-        else
-            compute_stage<false>(as, bs, arow, brow_w, kq, P);
-        if (s & 1) {  // group complete: total += s[n, g] * P
+        for (int step = 0; step < 8; ++step) {
+            const int kk = step >> 2, i = step & 3;
+            if (i < 3) {
+                af[(step + 1) & 1] =
+                    __builtin_bit_cast(bf16x8_t, as[swz8(arow + 16 * (i + 1), 4 * kk + q)]);
+            } else if (kk == 0) {
+                af[(step + 1) & 1] = __builtin_bit_cast(bf16x8_t, as[swz8(arow, 4 + q)]);
+            }
+            if (step == 2) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bfr[1][j] = __builtin_bit_cast(bf16x8_t,
+                                                   bs[swz16(bmrow + 16 * j, 8 * H + 4 + q)]);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float sc = Ss[buf][wn * 64 + 16 * j + (lane & 15)];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) tot[i][j][r] = fmaf(sc, P[i][j][r], tot[i][j][r]);
+                P[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    af[step & 1], bfr[kk][j],
+                    (H == 0 && kk == 0) ? f32x4_t{0.0f, 0.0f, 0.0f, 0.0f} : P[i][j], 0, 0, 0);
+                hook(step, j);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (s + 1 < nstages) store(s + 1, buf ^ 1);
-        __syncthreads();
+    };
+
+    // Folding group t (scales sq) runs one row block behind its last
+    // k-step: rows 0..2 during steps 5..7 of its closing stage, row 3
+    // during step 0 of the next group's opening stage (before step 3
+    // restarts P[3]).  P starts at zero, so the first such row-3 fold adds
+    // nothing.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) P[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float sq_prev[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    // ---- pseudo-groups (scale 1), not pipelined: A' from the pre-pass
+    // matrix, B' = s[n, k'/3] (zero beyond 3G) ----
+    {
+        const float one[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        for (int ps = 0; ps < NP; ++ps) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint16_t *src = Ap_blk + ps * kPseudoK + h * kPK;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    areg[i] = *reinterpret_cast<const u32x4 *>(src + __mul24(arows[i], Kp) + 8 * ac);
+                store_a(h);
+            }
+            const int k0 = ps * kPseudoK + 32 * bq;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t pr[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ka = k0 + 8 * u + 2 * e, kb = ka + 1;
+                    const uint32_t sa = *reinterpret_cast<const uint16_t *>(
+                        bscale0 + min(ka / 3, G - 1) * sstep);
+                    const uint32_t sb = *reinterpret_cast<const uint16_t *>(
+                        bscale0 + min(kb / 3, G - 1) * sstep);
+                    pr[e] = (ka < 3 * G ? sa : 0u) | ((kb < 3 * G ? sb : 0u) << 16);
+                }
+                Bsm[0][swz16(brow, 4 * bq + u)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+            }
+            lds_barrier();
+            mfma_stage(0, 0, std::integral_constant<int, 0>{}, [&](int step, int j) {
+                if (step == 0) fold_block(3, j, sq_prev);
+            });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sq_prev[j] = one[j];
+            mfma_stage(1, 0, std::integral_constant<int, 1>{}, [&](int step, int j) {
+                if (step >= 5) fold_block(step - 5, j, one);
+            });
+            lds_barrier();
+        }
+    }
+
+    // ---- real groups, software-pipelined ----
+    {
+        // Prologue: group 0's B and scales, A stage 0 in LDS, A stage 1 and
+        // the codes of group 1 in registers.
+        load_codes(0);
+        fill_chunk(0, std::integral_constant<int, 0>{});
+        fill_chunk(0, std::integral_constant<int, 1>{});
+        fill_chunk(0, std::integral_constant<int, 2>{});
+        fill_chunk(0, std::integral_constant<int, 3>{});
+        store_scale(0);
+        load_a(0);
+        store_a(0);
+        load_a(1);
+        load_codes(1);
+        lds_barrier();
+
+        for (int g = 0; g < G; ++g) {
+            const int gb = g & 1, nb = gb ^ 1;
+            float sq[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sq[j] = Ss[gb][wn * 64 + 16 * j + (lane & 15)];
+            // stage 2g (A buffer 0): finish folding the previous group; write
+            // A stage 2g+1, fetch A stage 2g+2; unpack group g+1 into the
+            // other B buffer (past the end: a harmless rewrite of a buffer
+            // nobody reads), one code pair per MFMA; fetch the codes of group
+            // g+2.
+            uint32_t pairs[16];
+            mfma_stage(0, gb, std::integral_constant<int, 0>{}, [&](int step, int j) {
+                if (step == 0) fold_block(3, j, sq_prev);
+                if (step == 1 && j == 0) store_a(1);
+                if (step == 2 && j == 0) load_a(2 * g + 2);
+                if (step >= 4) {
+                    const int pr = 4 * (step - 4) + j;
+                    pairs[pr] = quarter_pair_dyn<B>(pr, creg, mask, magic);
+                    if (j == 3)
+                        Bsm[nb][swz16(brow, 4 * bq + (step - 4))] =
+                            u32x4{pairs[pr - 3], pairs[pr - 2], pairs[pr - 1], pairs[pr]};
+                    if (step == 7 && j == 3) {
+                        store_scale(g + 1);
+                        load_codes(g + 2);
+                    }
+                }
+            });
+            lds_barrier();
+            // stage 2g+1 (A buffer 1): write A stage 2g+2, fetch A stage
+            // 2g+3; fold rows 0..2 of group g.
+            mfma_stage(1, gb, std::integral_constant<int, 1>{}, [&](int step, int j) {
+                if (step == 1 && j == 0) store_a(0);
+                if (step == 2 && j == 0) load_a(2 * g + 3);
+                if (step >= 5) fold_block(step - 5, j, sq);
+            });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sq_prev[j] = sq[j];
+            lds_barrier();
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fold_block(3, j, sq_prev);
     }
 
     // Output element r of block (i, j): row 4*(lane/16) + r, column lane%16.
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + wn * 64 + 16 * j + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * 128 + 16 * i + 4 * (lane >> 4) + r;
+                const int64_t m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
                 if (m < M && n < N) Y[m * N + n] = f32_to_bf16_rne(tot[i][j][r]);
             }
         }
@@ -366,11 +527,11 @@ static hipError_t prefill_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, 
     const dim3 grid((unsigned)(mtiles * ntiles));
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W), G, B};
-        hipLaunchKernelGGL((prefill_kernel<B, TiledW>), grid, dim3(256), 0, stream, A, Ap,
+        hipLaunchKernelGGL((prefill_kernel<B, TiledW>), grid, dim3(512), 0, stream, A, Ap,
                            (int)M, (int)N, (int)K, Kp, wl, Y, mtiles, ntiles);
     } else {
         DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
-        hipLaunchKernelGGL((prefill_kernel<B, DenseW>), grid, dim3(256), 0, stream, A, Ap,
+        hipLaunchKernelGGL((prefill_kernel<B, DenseW>), grid, dim3(512), 0, stream, A, Ap,
                            (int)M, (int)N, (int)K, Kp, wl, Y, mtiles, ntiles);
     }
     return hipGetLastError();
