@@ -35,82 +35,6 @@ constexpr int kPN = 128;          // workgroup cols (n)
 constexpr int kPK = 64;           // k per LDS stage
 constexpr int kPseudoK = 128;     // k' per pseudo-group
 
-// Codes 2P, 2P+1 of a 32-code quarter slot held in B words.
-template <int B, int P>
-struct QSel {
-    static constexpr int o0 = 2 * P * B;
-    static constexpr int o1 = o0 + B;
-    static constexpr int byte0 = o0 >> 3;
-    static constexpr int byte1 = o1 >> 3;
-    static constexpr int word = byte0 >> 2;
-    static constexpr int base = 4 * word;
-    static constexpr uint32_t sel = (uint32_t)(byte0 - base) |
-                                    ((uint32_t)(byte0 + 1 - base) << 8) |
-                                    ((uint32_t)(byte1 - base) << 16) |
-                                    ((uint32_t)(byte1 + 1 - base) << 24);
-    static constexpr int sh0 = o0 & 7;
-    static constexpr int sh1 = o1 & 7;
-    static constexpr bool has_hi = word + 1 < B;
-};
-
-template <int B, int P>
-__device__ __forceinline__ uint32_t quarter_pair(const uint32_t *w, uint32_t mask,
-                                                 uint32_t magic) {
-    if constexpr (B == 8) {
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const uint32_t x = w[P >> 1];
-        f32x2 f;
-        f.x = (float)((x >> (16 * (P & 1))) & 0xFFu);
-        f.y = (float)((x >> (16 * (P & 1) + 8)) & 0xFFu);
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-    } else {
-        using S = QSel<B, P>;
-        const uint32_t lo = w[S::word];
-        const uint32_t hi = S::has_hi ? w[S::word + 1] : 0u;
-        uint32_t x = __builtin_amdgcn_perm(hi, lo, S::sel);
-        if constexpr (S::sh0 != 0 || S::sh1 != 0) x = pk_shr16(x, S::sh0, S::sh1);
-        return and_or(x, mask, magic);
-    }
-}
-
-// quarter_pair<B, P> for a P that is a constant after unrolling.
-template <int B>
-__device__ __forceinline__ uint32_t quarter_pair_dyn(int p, const uint32_t *w, uint32_t mask,
-                                                     uint32_t magic) {
-    switch (p) {
-        case 0: return quarter_pair<B, 0>(w, mask, magic);
-        case 1: return quarter_pair<B, 1>(w, mask, magic);
-        case 2: return quarter_pair<B, 2>(w, mask, magic);
-        case 3: return quarter_pair<B, 3>(w, mask, magic);
-        case 4: return quarter_pair<B, 4>(w, mask, magic);
-        case 5: return quarter_pair<B, 5>(w, mask, magic);
-        case 6: return quarter_pair<B, 6>(w, mask, magic);
-        case 7: return quarter_pair<B, 7>(w, mask, magic);
-        case 8: return quarter_pair<B, 8>(w, mask, magic);
-        case 9: return quarter_pair<B, 9>(w, mask, magic);
-        case 10: return quarter_pair<B, 10>(w, mask, magic);
-        case 11: return quarter_pair<B, 11>(w, mask, magic);
-        case 12: return quarter_pair<B, 12>(w, mask, magic);
-        case 13: return quarter_pair<B, 13>(w, mask, magic);
-        case 14: return quarter_pair<B, 14>(w, mask, magic);
-        default: return quarter_pair<B, 15>(w, mask, magic);
-    }
-}
-
-template <int B, int P>
-struct QuarterPairs {
-    __device__ __forceinline__ static void run(const uint32_t *w, uint32_t mask, uint32_t magic,
-                                               uint32_t *out) {
-        out[P] = quarter_pair<B, P>(w, mask, magic);
-        QuarterPairs<B, P + 1>::run(w, mask, magic, out);
-    }
-};
-template <int B>
-struct QuarterPairs<B, 16> {
-    __device__ __forceinline__ static void run(const uint32_t *, uint32_t, uint32_t,
-                                               uint32_t *) {}
-};
-
 // Pre-pass: per (row m, group g) v = -off * sum_{k in g} a[m,k], written as
 // three bf16 terms at k' = 3g + {0,1,2} of a [M, Kp] bf16 matrix (zero beyond
 // 3G).  One workgroup of 256 threads per row; 16 threads per group, fixed
@@ -169,33 +93,6 @@ __device__ __forceinline__ int swz8(int row, int chunk) { return row * 8 + (chun
 __device__ __forceinline__ int swz16(int row, int chunk) {
     return row * 16 + (chunk ^ (row & 15));
 }
-
-// Dwords [Q*B, Q*B + B) of a slot (its quarter Q: codes 32Q .. 32Q+31) into
-// w[0..B), loaded as runs of consecutive dwords within one 16-byte chunk
-// (dword d sits at WL::dword_off(d); chunks are 16-byte aligned).
-template <class WL, int D, int END>
-struct QuarterLoad {
-    static constexpr int kRun = ((D | 3) + 1 < END ? (D | 3) + 1 : END) - D;
-    __device__ __forceinline__ static void run(const uint8_t *slot, uint32_t *w) {
-        const uint8_t *p = slot + WL::dword_off(D);
-        if constexpr (kRun == 4) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-        } else if constexpr (kRun == 2 && (D & 1) == 0) {
-            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
-            w[0] = v.x; w[1] = v.y;
-        } else {
-#pragma unroll
-            for (int e = 0; e < kRun; ++e) w[e] = reinterpret_cast<const uint32_t *>(p)[e];
-        }
-        QuarterLoad<WL, D + kRun, END>::run(slot, w + kRun);
-    }
-};
-template <class WL, int END>
-struct QuarterLoad<WL, END, END> {
-    __device__ __forceinline__ static void run(const uint8_t *, uint32_t *) {}
-};
 
 // Workgroup: 512 threads = 8 waves (two per SIMD) over a 256 (m) x 128 (n)
 // output tile; wave (wm, wn) owns rows 64 wm .. +64 and columns 64 wn .. +64
