@@ -15,6 +15,7 @@ Also reported on the same line:
                 average duration (HIP events on the launch stream), against the
                 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle (fp64, OpenMP) on the same decode layers;
+  decode_sweep  TB/s of wq_gemm at M = 4 and 16 on the same layer;
   prefill       TFLOP/s of wq_gemm at M = 4096 (up: K 5120 -> N 17408, down:
                 K 17408 -> N 5120, b = 6) against the 2.5 PFLOP/s bf16 peak;
   w4a8          TOP/s of wq_gemm_a8 at M = 2048 / 8192 (K 5120, N 17408) against
@@ -133,6 +134,38 @@ def bench_prefill(torch, wq, synth, reps: int):
         out[name] = {"M": w.M, "N": N, "K": K, "b": 6, "ms": t * 1e3, "TFLOP/s": tf,
                      "frac_of_peak": tf / BF16_PEAK_TFLOPS}
         del blob, A, Y
+    return out
+
+
+def bench_decode_sweep(torch, wq, synth, reps: int, copies: int):
+    """wq_gemm at M = 4 and 16 on the decode layer (K 5120 -> N 17408), b = 5,
+    6, 7, in TB/s of algorithmic bytes; rotating weight copies as in the
+    headline step."""
+    out = {}
+    for b in DECODE_BITS:
+        w = synth.decode(M=16, b=b, N=DECODE_N, K=DECODE_K)
+        packed = wq.wq_pack(w.codes, b)
+        packed_d = torch.from_numpy(packed.view(np.int32)).cuda()
+        scales_d = torch.from_numpy(w.scales.view(np.int16)).cuda().view(torch.bfloat16)
+        blob = wq.wq_repack(packed_d, scales_d, w.K, b)
+        blobs = [blob] + [blob.clone() for _ in range(copies - 1)]
+        del packed_d, scales_d
+        for M in (4, 16):
+            A = torch.from_numpy(np.ascontiguousarray(w.A[:M]).view(np.int16)).cuda().view(torch.bfloat16)
+            Y = torch.empty((M, w.N), dtype=torch.bfloat16, device="cuda")
+            nb = wq.wq_workspace_bytes(wq.WQ_OP_GEMM, M, w.N, w.K, b)
+            ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
+            n = 64
+
+            def fn():
+                for i in range(n):
+                    wq.wq_gemm(A, blobs[i % copies], wq.WQ_LAYOUT_TILED, None, w.N, b, Y=Y, ws=ws)
+
+            t = graph_time(torch, fn, reps, 1) / n
+            byts = algorithmic_bytes(M, w.N, w.K, b)
+            out["b%d_M%d" % (b, M)] = {"us": t * 1e6, "TB/s": byts / t / 1e12,
+                                      "frac_of_hbm_peak": byts / t / 1e9 / HBM_PEAK_GBS}
+        del blobs, blob
     return out
 
 
@@ -328,7 +361,8 @@ def main():
     achieved = l6.bytes / t6 / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                "kernel": "decode_kernel<6,1,TiledW>", "us_per_launch": t6 * 1e6,
+                "kernel": "decode_kernel<B=6, MT=1> (vector-ALU decode, tiled layout)",
+                "us_per_launch": t6 * 1e6,
                 "bytes_per_launch": l6.bytes}
     log("b=6 decode kernel: %.2f us/launch, %.0f GB/s" % (t6 * 1e6, achieved))
 
@@ -354,6 +388,9 @@ def main():
         "roofline": roofline,
     }
     if not args.no_secondary:
+        log("decode M=4/16")
+        result["decode_sweep"] = bench_decode_sweep(torch, wq, synth, 3, args.copies)
+        torch.cuda.empty_cache()
         log("prefill M=4096")
         result["prefill"] = bench_prefill(torch, wq, synth, reps=10)
         torch.cuda.empty_cache()
