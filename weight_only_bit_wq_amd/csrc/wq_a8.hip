@@ -6,7 +6,7 @@
 // scales as the weight-only path are used.  Here:
 //   1. quant_act_kernel: s_a[m] = max|a| / 127 (fp32, IEEE division),
 //      Aq = clamp(rint(a / s_a), -127, 127), zero row -> 0.
-//   2. gemm_a8_kernel: int8 MFMA (v_mfma_i32_32x32x32_i8) with exact int32
+//   2. gemm_a8_kernel: int8 MFMA (v_mfma_i32_16x16x64_i8) with exact int32
 //      sums per group of 128, folded in fp32 with the group scale, times s_a.
 //
 // Lossless widening with one AND per four codes: XOR-ing a nibble c with 8
@@ -23,7 +23,7 @@
 namespace wq {
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef int i32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // 8 activations (one uint4 of bf16) -> 8 int8 codes, as two dwords.
 // PERM: order (0,2,4,6 | 1,3,5,7) for the GEMM; else natural order.
@@ -90,8 +90,7 @@ hipError_t launch_quant_act(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq,
     return hipGetLastError();
 }
 
-constexpr int kABM = 128, kABN = 128;
-constexpr int kA8Row = 128 + 16;  // bytes per LDS row (pad)
+constexpr int kABM = 256, kABN = 128;
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
@@ -101,105 +100,179 @@ int64_t a8_ws_bytes(int64_t M, int64_t, int64_t K) {
     return kWsScratchOffset + align256(M * K) + align256(M * 4);
 }
 
+// LDS barrier that orders LDS only (global prefetches stay in flight).
+__device__ __forceinline__ void a8_lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// LDS rows of 128 bytes (8 chunks of 16 int8 = 16 k); chunk c of row r sits
+// at c ^ (r mod 8), so an operand read (16 rows, one chunk) and the loaders'
+// row-major writes are conflict free.
+__device__ __forceinline__ int a8_swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+// Workgroup: 512 threads = 8 waves (two per SIMD) over a 256 (m) x 128 (n)
+// tile; wave (wm, wn) owns 64 x 64 = 4 x 4 blocks of v_mfma_i32_16x16x64_i8.
+// Per group of 128 k: 2 k-steps x 16 MFMAs into exact int32 sums P, then
+// tot += (s/16) * float(P) (fp32).  A (int8, GEMM k-order) and the widened
+// B of a group sit in LDS (double-buffered, 32 + 16 KB per buffer); the next
+// group's A and codes are fetched into registers during the current one.
+// The fold runs one row block behind the group's last MFMAs (row 3 during
+// the next group's first k-step), one block per MFMA, so it issues in the
+// matrix core's shadow.
 template <class WL>
-__global__ __launch_bounds__(256) void gemm_a8_kernel(const int8_t *__restrict__ Aq,
+__global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__ Aq,
                                                       const float *__restrict__ sa, int M, int N,
                                                       int K, WL wl, void *__restrict__ Y,
-                                                      bool out_f32, int mtiles) {
-    __shared__ __attribute__((aligned(16))) uint8_t As[kABM * kA8Row];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[kABN * kA8Row];
-    __shared__ float scale_s[kABN];
+                                                      bool out_f32, int mtiles, int ntiles) {
+    __shared__ u32x4 Asm[2][kABM * 8];  // 2 x 32 KB
+    __shared__ u32x4 Bsm[2][kABN * 8];  // 2 x 16 KB
+    __shared__ float Ss[2][kABN];
 
     const int G = K / kGroup;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int bm = blockIdx.x % mtiles;
-    const int bn = blockIdx.x / mtiles;
+
+    // Block b runs on XCD b % 8: each XCD takes a contiguous run of logical
+    // tiles, n fastest, so the tiles it runs together share A rows.
+    const int total = mtiles * ntiles;
+    int logical = blockIdx.x;
+    if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    const int bm = logical / ntiles;
+    const int bn = logical - bm * ntiles;
     const int64_t m0 = (int64_t)bm * kABM;
     const int64_t n0 = (int64_t)bn * kABN;
 
-    float tot[2][2][16];
+    // A loader: rows ar + 64 i (i < 4), chunk ac; rows beyond M read row M-1.
+    const int ac = tid & 7;
+    const int ar = tid >> 3;
+    const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)kABM - 1);
+    int arows[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i) arows[i] = min(ar + 64 * i, mlim);
+    const int8_t *A_blk = Aq + m0 * K;
+    const int a_lds = a8_swz(ar, ac);  // + 512 i
+
+    // B loader: row brow, 16-byte chunk bj (wave-uniform) = codes 32 bj .. +32
+    // of the group; widened to int8 it fills LDS chunks 2 bj and 2 bj + 1.
+    const int brow = tid & (kABN - 1);
+    const int bj = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const int64_t bn_read = min(n0 + brow, (int64_t)N - 1);
+    const uint8_t *bslot0 = wl.slot0(bn_read);
+    const uint8_t *bscale0 = wl.scale0(bn_read);
+    const int bstep = (int)wl.slot_step();
+    const int sstep = (int)wl.scale_step();
+    const int bchunk_off = WL::dword_off(4 * bj);
+
+    // MFMA operand rows and k-chunk of this lane.
+    const int arow = wm * 64 + (lane & 15);
+    const int bmrow = wn * 64 + (lane & 15);
+    const int q = lane >> 4;
+
+    u32x4 areg[4], breg;
+    uint16_t sreg;
+    i32x4_t P[4][4];
+    f32x4_t tot[4][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.0f;
+        for (int j = 0; j < 4; ++j) {
+            tot[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            P[i][j] = i32x4_t{0, 0, 0, 0};
+        }
+
+    auto fetch = [&](int g) __attribute__((always_inline)) {  // clamped to the last group
+        g = min(g, G - 1);
+        const int8_t *src = A_blk + (int64_t)g * kGroup + 16 * ac;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            areg[i] = *reinterpret_cast<const u32x4 *>(src + (int64_t)arows[i] * K);
+        breg = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(bslot0 + (int64_t)g * bstep + bchunk_off));
+        sreg = *reinterpret_cast<const uint16_t *>(bscale0 + (int64_t)g * sstep);
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Asm[buf][a_lds + 512 * i] = areg[i];
+        const u32x4 x = breg ^ 0x88888888u;
+        Bsm[buf][a8_swz(brow, 2 * bj)] =
+            u32x4{(x.x << 4) & 0xF0F0F0F0u, x.x & 0xF0F0F0F0u, (x.y << 4) & 0xF0F0F0F0u,
+                  x.y & 0xF0F0F0F0u};
+        Bsm[buf][a8_swz(brow, 2 * bj + 1)] =
+            u32x4{(x.z << 4) & 0xF0F0F0F0u, x.z & 0xF0F0F0F0u, (x.w << 4) & 0xF0F0F0F0u,
+                  x.w & 0xF0F0F0F0u};
+        // The four chunk waves of a row store the same value: no branch.
+        Ss[buf][brow] = bf16_to_f32(sreg) * 0.0625f;
+    };
+    auto fold_block = [&](int i, int j, const float(&sq)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[i][j][r] = fmaf(sq[j], (float)P[i][j][r], tot[i][j][r]);
+    };
+
+    float sq_prev[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    fetch(0);
+    store(0);
+    fetch(1);
+    a8_lds_barrier();
 
     for (int g = 0; g < G; ++g) {
-        // A tile: 128 rows x 128 int8 (already in GEMM k-order), 4 uint4 per thread.
+        const int gb = g & 1;
+        float sq[4];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int idx = tid + 256 * it;
-            const int row = idx >> 3, c16 = idx & 7;
-            const int64_t m = m0 + row;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (m < M)
-                v = *reinterpret_cast<const uint4 *>(Aq + m * K + (int64_t)g * kGroup + c16 * 16);
-            *reinterpret_cast<uint4 *>(&As[row * kA8Row + c16 * 16]) = v;
-        }
-        if (tid < kABN) {
-            const int64_t n = n0 + tid;
-            const int64_t nr = n < N ? n : (int64_t)N - 1;
-            uint32_t w[16];
-            load_slot<4>(wl.chunks(nr, g), wl.chunk_stride(), w);
-            uint4 *dst = reinterpret_cast<uint4 *>(&Bs[tid * kA8Row]);
+        for (int j = 0; j < 4; ++j) sq[j] = Ss[gb][wn * 64 + 16 * j + (lane & 15)];
+        const u32x4 *as = Asm[gb];
+        const u32x4 *bs = Bsm[gb];
+        i32x4_t bfr[2][4], af[2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t x0 = w[2 * i] ^ 0x88888888u, x1 = w[2 * i + 1] ^ 0x88888888u;
-                dst[i] = make_uint4((x0 << 4) & 0xF0F0F0F0u, x0 & 0xF0F0F0F0u,
-                                    (x1 << 4) & 0xF0F0F0F0u, x1 & 0xF0F0F0F0u);
+        for (int j = 0; j < 4; ++j)
+            bfr[0][j] = __builtin_bit_cast(i32x4_t, bs[a8_swz(bmrow + 16 * j, q)]);
+        af[0] = __builtin_bit_cast(i32x4_t, as[a8_swz(arow, q)]);
+        __builtin_amdgcn_sched_barrier(0);
+        // 8 steps (k-step kk, row block i) of 4 MFMAs; each MFMA is followed
+        // by its slice of the other work, fenced so this is the issue order.
+#pragma unroll
+        for (int step = 0; step < 8; ++step) {
+            const int kk = step >> 2, i = step & 3;
+            if (i < 3)
+                af[(step + 1) & 1] =
+                    __builtin_bit_cast(i32x4_t, as[a8_swz(arow + 16 * (i + 1), 4 * kk + q)]);
+            else if (kk == 0)
+                af[(step + 1) & 1] = __builtin_bit_cast(i32x4_t, as[a8_swz(arow, 4 + q)]);
+            if (step == 2) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bfr[1][j] = __builtin_bit_cast(i32x4_t, bs[a8_swz(bmrow + 16 * j, 4 + q)]);
             }
-            scale_s[tid] = bf16_to_f32(wl.scale(nr, g)) * 0.0625f;
-        }
-        __syncthreads();
-
-        i32x16_t P[2][2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) P[i][j][r] = 0;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            i32x4_t af[2], bfr[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const i32x4_t *>(
-                    &As[(wm * 64 + i * 32 + (lane & 31)) * kA8Row + ks * 32 + (lane >> 5) * 16]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bfr[j] = *reinterpret_cast<const i32x4_t *>(
-                    &Bs[(wn * 64 + j * 32 + (lane & 31)) * kA8Row + ks * 32 + (lane >> 5) * 16]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    P[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bfr[j], P[i][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                P[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                    af[step & 1], bfr[kk][j], kk == 0 ? i32x4_t{0, 0, 0, 0} : P[i][j], 0, 0, 0);
+                if (step == 0) fold_block(3, j, sq_prev);  // previous group's row 3
+                if (step >= 5) fold_block(step - 5, j, sq);
+                if (step == 3 && j == 0) store(gb ^ 1);    // group g+1 into the other buffer
+                if (step == 4 && j == 0) fetch(g + 2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float s16 = scale_s[wn * 64 + j * 32 + (lane & 31)];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    tot[i][j][r] = fmaf(s16, (float)P[i][j][r], tot[i][j][r]);
-        }
-        __syncthreads();
+        for (int j = 0; j < 4; ++j) sq_prev[j] = sq[j];
+        a8_lds_barrier();
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fold_block(3, j, sq_prev);
 
+    // Output element r of block (i, j): row 4*(lane/16) + r, column lane%16.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + wn * 64 + 16 * j + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
                 if (m < M && n < N) {
                     const float y = sa[m] * tot[i][j][r];
                     if (out_f32)
@@ -227,12 +300,12 @@ hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, co
     const dim3 grid((unsigned)(mtiles * ntiles));
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W), G, 4};
-        hipLaunchKernelGGL((gemm_a8_kernel<TiledW>), grid, dim3(256), 0, stream, Aq, sa, (int)M,
-                           (int)N, (int)K, wl, Y, out_f32, mtiles);
+        hipLaunchKernelGGL((gemm_a8_kernel<TiledW>), grid, dim3(512), 0, stream, Aq, sa, (int)M,
+                           (int)N, (int)K, wl, Y, out_f32, mtiles, ntiles);
     } else {
         DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * 4 * G, G, 4};
-        hipLaunchKernelGGL((gemm_a8_kernel<DenseW>), grid, dim3(256), 0, stream, Aq, sa, (int)M,
-                           (int)N, (int)K, wl, Y, out_f32, mtiles);
+        hipLaunchKernelGGL((gemm_a8_kernel<DenseW>), grid, dim3(512), 0, stream, Aq, sa, (int)M,
+                           (int)N, (int)K, wl, Y, out_f32, mtiles, ntiles);
     }
     return hipGetLastError();
 }
