@@ -20,6 +20,7 @@
 // K runs in LDS stages of 64 for A and whole groups of 128 for B (unpacked
 // to bf16 in LDS once per workgroup), double-buffered, register-staged.
 // Workgroups an XCD runs together share an A row block.
+#include <algorithm>
 #include <type_traits>
 
 #include "wq_device.h"
@@ -120,7 +121,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
                                                       const uint16_t *__restrict__ Ap, int M,
                                                       int N, int K, int Kp, WL wl,
                                                       uint16_t *__restrict__ Y, int mtiles,
-                                                      int ntiles) {
+                                                      int ntiles, int splits,
+                                                      float *__restrict__ part, int64_t mnp) {
     __shared__ u32x4 Asm[2][kPM * 8];   // [stage buffer][256 rows x 8 chunks]
     __shared__ u32x4 Bsm[2][kPN * 16];  // [group buffer][128 rows x 16 chunks]
     __shared__ float Ss[2][kPN];
@@ -134,11 +136,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
 
     // Block b runs on XCD b % 8: give each XCD a contiguous run of logical
     // tiles, n fastest, so the tiles an XCD runs together share A rows.
-    const int total = mtiles * ntiles;
+    // With K split `splits` ways, logical = split * tiles + tile.
+    const int tiles = mtiles * ntiles;
+    const int total = tiles * splits;
     int logical = blockIdx.x;
     if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-    const int bm = logical / ntiles;
-    const int bn = logical - bm * ntiles;
+    const int sp = logical / tiles;
+    const int tile = logical - sp * tiles;
+    const int bm = tile / ntiles;
+    const int bn = tile - bm * ntiles;
+    // This workgroup's groups; the pseudo-groups go with split 0.
+    const int g_lo = (int)(((int64_t)G * sp) / splits);
+    const int g_hi = (int)(((int64_t)G * (sp + 1)) / splits);
     const int64_t m0 = (int64_t)bm * kPM;
     const int64_t n0 = (int64_t)bn * kPN;
 
@@ -179,9 +188,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int j = 0; j < 4; ++j) tot[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Real stage s (64 k of group s/2), clamped to the last one.
+    // Real stage s (64 k of group s/2), clamped to this split's last one.
     auto load_a = [&](int s) __attribute__((always_inline)) {
-        s = min(s, 2 * G - 1);
+        s = min(s, 2 * g_hi - 1);
         const uint16_t *src = A_blk + (s >> 1) * kGroup + (s & 1) * kPK;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -200,7 +209,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
         qoff[e] = __builtin_amdgcn_readfirstlane((d >> 2) * (WL::kTiled ? 1024 : 16) + (d & 3) * 4);
     }
     auto load_codes = [&](int g) __attribute__((always_inline)) {
-        const uint8_t *slot = bslot0 + (int64_t)min(g, G - 1) * bstep;
+        const uint8_t *slot = bslot0 + (int64_t)min(g, g_hi - 1) * bstep;
 #pragma unroll
         for (int e = 0; e < B; ++e) creg[e] = *reinterpret_cast<const uint32_t *>(slot + qoff[e]);
     };
@@ -214,11 +223,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
                       quarter_pair<B, 4 * C + 3>(creg, mask, magic)};
         Bsm[buf][swz16(brow, 4 * bq + C)] = v;
     };
-    // Group g's scales into Ss[g&1] (the four quarter waves of a row store
+    // Group g's scales into Ss[buf] (the four quarter waves of a row store
     // the same value: no branch).
-    auto store_scale = [&](int g) __attribute__((always_inline)) {
-        Ss[g & 1][brow] =
-            bf16_to_f32(*reinterpret_cast<const uint16_t *>(bscale0 + min(g, G - 1) * sstep));
+    auto store_scale = [&](int g, int buf) __attribute__((always_inline)) {
+        Ss[buf][brow] =
+            bf16_to_f32(*reinterpret_cast<const uint16_t *>(bscale0 + min(g, g_hi - 1) * sstep));
     };
     auto fold_block = [&](int i, int j, const float(&sq)[4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     // matrix, B' = s[n, k'/3] (zero beyond 3G) ----
     {
         const float one[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        for (int ps = 0; ps < NP; ++ps) {
+        for (int ps = 0; ps < (sp == 0 ? NP : 0); ++ps) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint16_t *src = Ap_blk + ps * kPseudoK + h * kPK;
@@ -325,20 +334,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     {
         // Prologue: group 0's B and scales, A stage 0 in LDS, A stage 1 and
         // the codes of group 1 in registers.
-        load_codes(0);
+        load_codes(g_lo);
         fill_chunk(0, std::integral_constant<int, 0>{});
         fill_chunk(0, std::integral_constant<int, 1>{});
         fill_chunk(0, std::integral_constant<int, 2>{});
         fill_chunk(0, std::integral_constant<int, 3>{});
-        store_scale(0);
-        load_a(0);
+        store_scale(g_lo, 0);
+        load_a(2 * g_lo);
         store_a(0);
-        load_a(1);
-        load_codes(1);
+        load_a(2 * g_lo + 1);
+        load_codes(g_lo + 1);
         lds_barrier();
 
-        for (int g = 0; g < G; ++g) {
-            const int gb = g & 1, nb = gb ^ 1;
+        for (int g = g_lo; g < g_hi; ++g) {
+            const int gb = (g - g_lo) & 1, nb = gb ^ 1;
             float sq[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) sq[j] = Ss[gb][wn * 64 + 16 * j + (lane & 15)];
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
                         Bsm[nb][swz16(brow, 4 * bq + (step - 4))] =
                             u32x4{pairs[pr - 3], pairs[pr - 2], pairs[pr - 1], pairs[pr]};
                     if (step == 7 && j == 3) {
-                        store_scale(g + 1);
+                        store_scale(g + 1, nb);
                         load_codes(g + 2);
                     }
                 }
@@ -389,9 +398,29 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
-                if (m < M && n < N) Y[m * N + n] = f32_to_bf16_rne(tot[i][j][r]);
+                if (m < M && n < N) {
+                    if (splits == 1)
+                        Y[m * N + n] = f32_to_bf16_rne(tot[i][j][r]);
+                    else
+                        part[(int64_t)sp * mnp + m * N + n] = tot[i][j][r];
+                }
             }
         }
+}
+
+// Y = bf16(sum over splits of part[s]) in split order (deterministic); four
+// consecutive outputs per thread.  Split s's partials start at s * mnp
+// (M * N rounded up to 64 floats, so the vector loads stay aligned).
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__restrict__ part,
+                                                             int splits, int64_t MN, int64_t mnp,
+                                                             uint16_t *__restrict__ Y) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= MN) return;
+    f32x4_t acc = *reinterpret_cast<const f32x4_t *>(part + e);
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f32x4_t *>(part + s * mnp + e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (e + i < MN) Y[e + i] = f32_to_bf16_rne(acc[i]);
 }
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
@@ -401,10 +430,27 @@ static int pseudo_kp(int64_t K) {
     return (3 * G + kPseudoK - 1) / kPseudoK * kPseudoK;
 }
 
+// K splits: when the tiles alone leave compute units idle, split K so that
+// tiles x splits is just under 256 (one workgroup per compute unit), at
+// least 8 groups per split.  (M = 512 on the 17408 -> 5120 layer: 80 tiles,
+// 3 splits.)
+static int prefill_splits(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
+    const int G = (int)(K / kGroup);
+    if (tiles >= 192) return 1;
+    int s = (int)std::max<int64_t>(1, 256 / tiles);
+    return std::max(1, std::min(s, G / 8));
+}
+
+static int64_t prefill_mnp(int64_t M, int64_t N) { return (M * N + 63) / 64 * 64; }
+
 // Workspace: the shared counter region (unused here), then the pre-pass
-// matrix [M, Kp] bf16.
-int64_t prefill_ws_bytes(int64_t M, int64_t, int64_t K, int) {
-    return kWsScratchOffset + align256(M * pseudo_kp(K) * 2);
+// matrix [M, Kp] bf16, then (K split) the fp32 partial outputs, split s at
+// s * mnp floats.
+int64_t prefill_ws_bytes(int64_t M, int64_t N, int64_t K, int) {
+    const int s = prefill_splits(M, N, K);
+    return kWsScratchOffset + align256(M * pseudo_kp(K) * 2) +
+           (s > 1 ? s * prefill_mnp(M, N) * 4 : 0);
 }
 
 template <int B>
@@ -414,6 +460,10 @@ static hipError_t prefill_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, 
     const int G = (int)(K / kGroup);
     const int Kp = pseudo_kp(K);
     uint16_t *Ap = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
+    const int splits = prefill_splits(M, N, K);
+    float *part = splits > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
+                                                         kWsScratchOffset + align256(M * Kp * 2))
+                             : nullptr;
     const float off = (B == 8) ? 128.0f : (float)(128 + (1 << (B - 1)));
     hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M), dim3(256), 0, stream, A, (int)K,
                        Kp, off, Ap);
@@ -421,16 +471,24 @@ static hipError_t prefill_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, 
     if (e != hipSuccess) return e;
     const int mtiles = (int)((M + kPM - 1) / kPM);
     const int ntiles = (int)((N + kPN - 1) / kPN);
-    const dim3 grid((unsigned)(mtiles * ntiles));
+    const dim3 grid((unsigned)(mtiles * ntiles * splits));
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W), G, B};
         hipLaunchKernelGGL((prefill_kernel<B, TiledW>), grid, dim3(512), 0, stream, A, Ap,
-                           (int)M, (int)N, (int)K, Kp, wl, Y, mtiles, ntiles);
+                           (int)M, (int)N, (int)K, Kp, wl, Y, mtiles, ntiles, splits, part,
+                           prefill_mnp(M, N));
     } else {
         DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
         hipLaunchKernelGGL((prefill_kernel<B, DenseW>), grid, dim3(512), 0, stream, A, Ap,
-                           (int)M, (int)N, (int)K, Kp, wl, Y, mtiles, ntiles);
+                           (int)M, (int)N, (int)K, Kp, wl, Y, mtiles, ntiles, splits, part,
+                           prefill_mnp(M, N));
     }
+    e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t MN = M * N;
+    const int64_t threads = (MN + 3) / 4;
+    hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, part, splits, MN, prefill_mnp(M, N), Y);
     return hipGetLastError();
 }
 
