@@ -21,6 +21,7 @@
 // to bf16 in LDS once per workgroup), double-buffered, register-staged.
 // Workgroups an XCD runs together share an A row block.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "wq_device.h"
@@ -432,12 +433,21 @@ static int pseudo_kp(int64_t K) {
 
 // K splits: when the tiles alone leave compute units idle, split K so that
 // tiles x splits is just under 256 (one workgroup per compute unit), at
-// least 8 groups per split.  (M = 512 on the 17408 -> 5120 layer: 80 tiles,
-// 3 splits.)
+// least 8 groups per split; between 192 and 383 tiles, 2 splits (the second
+// round of workgroups would otherwise run nearly empty).  Measured at M =
+// 512: 17408 -> 5120 (80 tiles) best at 3 splits, 174 vs 365 us unsplit;
+// 5120 -> 17408 (272 tiles) 219 us at 2 splits vs 240 us.
+// WQ_PREFILL_SPLITS forces a split count.
 static int prefill_splits(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
     const int G = (int)(K / kGroup);
-    if (tiles >= 192) return 1;
+    static const int forced = [] {
+        const char *e = std::getenv("WQ_PREFILL_SPLITS");
+        return e ? std::atoi(e) : 0;
+    }();
+    if (forced > 0) return std::max(1, std::min(forced, G));
+    if (tiles >= 384) return 1;
+    if (tiles >= 192) return G >= 16 ? 2 : 1;
     int s = (int)std::max<int64_t>(1, 256 / tiles);
     return std::max(1, std::min(s, G / 8));
 }
