@@ -209,8 +209,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     // Cross-workgroup reduction.  All shared data moves through device-scope
     // relaxed atomics (coherent across the XCDs' L2s without the L2
     // write-back/invalidate an agent-scope fence costs): partials are atomic
-    // stores, the barrier's s_waitcnt completes them before the ticket RMW,
-    // and the last workgroup reads them back with atomic loads.
+    // stores, each wave waits for their completion before the barrier that
+    // precedes the ticket RMW, and the last workgroup reads them back with
+    // atomic loads.
     for (int m = wave; m < MT; m += W) {
         float v = red[0][m][lane];
 #pragma unroll
@@ -218,6 +219,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         __hip_atomic_store(&part[((int64_t)s * MT + m) * Npad + n], v, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
+    wait_vm_stores();
     __syncthreads();  // every wave's partial stores have completed
     if (threadIdx.x == 0)
         ticket_sh = __hip_atomic_fetch_add(&counters[R], 1u, __ATOMIC_RELAXED,

@@ -222,6 +222,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t *__rest
         }
     }
     if (splits == 1) return;
+    wait_vm_stores();
     __syncthreads();  // every wave's partial stores have completed
     if (threadIdx.x == 0)
         ticket_sh = __hip_atomic_fetch_add(&counters[R], 1u, __ATOMIC_RELAXED,

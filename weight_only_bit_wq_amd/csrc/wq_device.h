@@ -185,6 +185,14 @@ __device__ __forceinline__ void load_slot(const uint4 *p, int64_t stride, uint32
     }
 }
 
+// Wait until this wave's vector-memory stores have completed.  Split-K
+// partials are device-scope atomic stores (written through to the
+// coherence point); a workgroup barrier does not wait for them, so a wave
+// must wait here before the barrier that precedes the split's ticket, or
+// the last split could read a partial that is still in flight.
+// (s_waitcnt vmcnt(0), other counters left unconstrained.)
+__device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------------------
 // bf16 helpers
 // ---------------------------------------------------------------------------
