@@ -116,6 +116,16 @@ def test_gemm_decode_sweep_full_shape(b, M):
     assert_wna16(Layer(w, wq.WQ_LAYOUT_TILED).gemm(), y_ref, mag, "decode sweep b=%d M=%d" % (b, M))
 
 
+@pytest.mark.parametrize("N,K,b", [(6437, 3840, 6), (4352, 5120, 5), (3200, 17408, 7),
+                                   (2560, 10240, 8)])
+def test_gemm_decode_m1_shapes(N, K, b):
+    # M = 1 at shapes between the parity and the full sweep sizes (ragged N,
+    # 30 to 136 groups, K split 1 to 5 ways); full outputs against the oracle.
+    w = _workload(1, N, K, b, seed=900 + b)
+    y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
+    assert_wna16(Layer(w, wq.WQ_LAYOUT_TILED).gemm(), y_ref, mag, "decode M=1 N=%d K=%d b=%d" % (N, K, b))
+
+
 @pytest.mark.parametrize("shape", [(5120, 17408), (17408, 5120)], ids=["up", "down"])
 def test_gemm_prefill_full_shape_sampled(shape):
     K, N = shape

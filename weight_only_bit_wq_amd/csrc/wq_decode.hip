@@ -53,7 +53,7 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b) {
     if (!(waves == 4 || (waves == 8 && p.mt <= 8) || (waves == 16 && p.mt <= 4)))
         waves = 4;
     if (p.rowblocks > kWsMaxCounters) splits = 1;
-    splits = std::min(splits, G);
+    splits = std::min(std::min(splits, G), kDecodeMaxSplits);
     p.waves = waves;
     p.gps = (G + splits - 1) / splits;
     p.splits = (G + p.gps - 1) / p.gps;

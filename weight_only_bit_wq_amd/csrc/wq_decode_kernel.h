@@ -226,12 +226,21 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
                                            __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket_sh != (unsigned)(splits - 1)) return;
+    // All of an output's partial loads are issued before its adds (they are
+    // independent; one at a time they would put `splits` round trips on the
+    // kernel's tail), then added in split order.
     for (int m = wave; m < MT; m += W) {
-        float v = 0.0f;
-        for (int t = 0; t < splits; ++t)
-            v += __hip_atomic_load(&part[((int64_t)t * MT + m) * Npad + n], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(v);
+        float v[kDecodeMaxSplits];
+#pragma unroll
+        for (int t = 0; t < kDecodeMaxSplits; ++t)
+            v[t] = t < splits ? __hip_atomic_load(&part[((int64_t)t * MT + m) * Npad + n],
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.0f;
+        float sum = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kDecodeMaxSplits; ++t)
+            if (t < splits) sum += v[t];
+        if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(sum);
     }
     if (threadIdx.x == 0)  // leave the counter region zero
         __hip_atomic_store(&counters[R], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

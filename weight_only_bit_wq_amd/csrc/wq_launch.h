@@ -22,6 +22,7 @@ constexpr int64_t kWsScratchOffset = kWsCounterBytes;
 
 // ---- decode path, M <= kDecodeMaxM (wq_decode.hip) ----
 constexpr int kDecodeMaxM = 16;
+constexpr int kDecodeMaxSplits = 16;  // K splits of the vector-ALU decode kernel
 
 struct DecodePlan {
     int mt;         // rows of A handled per kernel instance (template M tile)
