@@ -126,6 +126,18 @@ def test_gemm_decode_m1_shapes(N, K, b):
     assert_wna16(Layer(w, wq.WQ_LAYOUT_TILED).gemm(), y_ref, mag, "decode M=1 N=%d K=%d b=%d" % (N, K, b))
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("M,N,K,b", [(300, 700, 5120, 6), (130, 1000, 3072, 3)])
+def test_gemm_prefill_k_split(M, N, K, b, layout):
+    # Few output tiles: the prefill kernel splits K across workgroups (5 and
+    # 3 splits here) and a reduce pass adds the fp32 partials; full outputs.
+    w = _workload(M, N, K, b, seed=950 + b)
+    y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
+    Y = Layer(w, layout).gemm()
+    assert_wna16(Y, y_ref, mag, "prefill split M=%d b=%d" % (M, b))
+    np.testing.assert_array_equal(Layer(w, layout).gemm(), Y)
+
+
 @pytest.mark.parametrize("shape", [(5120, 17408), (17408, 5120)], ids=["up", "down"])
 def test_gemm_prefill_full_shape_sampled(shape):
     K, N = shape
