@@ -336,3 +336,4 @@ def test_split_k_handoff_repeated(b, M, K, N):
     assert_wna16(host_bf16_bits(Y0), y_ref, mag, "split-K b=%d M=%d" % (b, M))
     for Y in outs:
         assert torch.equal(Y.view(torch.int16), Y0.view(torch.int16))
+

@@ -18,8 +18,13 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwq.so")
 ARCH = "gfx950"
+# -amdgpu-atomic-optimizer-strategy=None: the kernels' atomics are single-lane
+# tickets and counters; the optimizer would rewrite each into a wave-wide
+# scan that reads the result at once, waiting out the round trip that the
+# split-K kernels issue early precisely to hide it.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-Wall"]
 
 

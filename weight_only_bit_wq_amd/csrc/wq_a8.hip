@@ -100,13 +100,6 @@ int64_t a8_ws_bytes(int64_t M, int64_t, int64_t K) {
     return kWsScratchOffset + align256(M * K) + align256(M * 4);
 }
 
-// LDS barrier that orders LDS only (global prefetches stay in flight).
-__device__ __forceinline__ void a8_lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // LDS rows of 128 bytes (8 chunks of 16 int8 = 16 k); chunk c of row r sits
 // at c ^ (r mod 8), so an operand read (16 rows, one chunk) and the loaders'
 // row-major writes are conflict free.
@@ -216,7 +209,7 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
     fetch(0);
     store(0);
     fetch(1);
-    a8_lds_barrier();
+    lds_barrier();
 
     for (int g = 0; g < G; ++g) {
         const int gb = g & 1;
@@ -259,7 +252,7 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) sq_prev[j] = sq[j];
-        a8_lds_barrier();
+        lds_barrier();
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) fold_block(3, j, sq_prev);

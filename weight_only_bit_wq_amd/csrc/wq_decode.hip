@@ -52,7 +52,8 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b) {
     if (const char *e = std::getenv("WQ_DECODE_SPLITS")) splits = std::max(1, std::atoi(e));
     if (!(waves == 4 || (waves == 8 && p.mt <= 8) || (waves == 16 && p.mt <= 4)))
         waves = 4;
-    if (p.rowblocks > kWsMaxCounters) splits = 1;
+    // One ticket per (row block, storing wave).
+    if ((int64_t)p.rowblocks * std::min(waves, p.mt) > kWsMaxCounters) splits = 1;
     splits = std::min(std::min(splits, G), kDecodeMaxSplits);
     p.waves = waves;
     p.gps = (G + splits - 1) / splits;

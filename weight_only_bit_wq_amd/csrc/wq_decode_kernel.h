@@ -13,12 +13,16 @@
 //   - All lanes of a wave work on the same group g, so the 128 activations
 //     of that group are wave-uniform: they are read with scalar loads and
 //     fed to v_dot2_f32_bf16 as its SGPR operand.
-//   - A workgroup (4 waves) covers 64 rows and `gps` consecutive groups, the
+//   - A workgroup (W waves) covers 64 rows and `gps` consecutive groups, the
 //     waves interleaving groups; `splits` workgroups share one 64-row block.
-//     Partial sums go to an fp32 workspace and the last workgroup of a block
-//     to finish (atomic ticket) adds them in split order (deterministic) and
-//     writes bf16.  The ticket counter (in the workspace's counter region) is
-//     reset to zero by that workgroup.
+//     Many small workgroups (rather than one per compute unit) let the
+//     dispatcher balance the stream: a compute unit whose loads come back
+//     early simply takes more workgroups.
+//   - Split K hands off through the workspace: after the waves' sums meet in
+//     LDS, only the waves that own output rows stay; each stores its fp32
+//     partials and takes a ticket per (block, wave); the last of the splits
+//     adds them in split order (deterministic), writes bf16 and resets the
+//     ticket (in the workspace's counter region) to zero.
 //
 // Arithmetic per pair of codes (b <= 7): v_perm_b32 + packed 16-bit shift
 // pull the two fields (straddling or not) into the two 16-bit halves,
@@ -124,6 +128,66 @@ __device__ __forceinline__ void dot_bytes(const uint32_t *w, const uint32_t *a,
     }
 }
 
+// Everything a lane reads from memory for one (row, group) slot: its b
+// chunks, its scale, and pair `lane` of the group's activations in each row m
+// (for the group's activation sum).  A slot is loaded whole before the
+// previous one is computed: the vector-memory counter retires in issue
+// order, so a load issued after the next slot's prefetch would make the
+// current slot wait for that prefetch.
+template <int B, int MT>
+struct SlotRegs {
+    uint32_t w[4 * B];
+    uint32_t al[MT];
+    uint16_t s;
+};
+template <int B, int MT, class WL>
+__device__ __forceinline__ void load_slot_regs(const WL &wl, int64_t nr, int g,
+                                               const uint32_t *A2, const int *row_off, int lane,
+                                               SlotRegs<B, MT> &r) {
+    load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), r.w);
+    r.s = wl.scale(nr, g);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) r.al[m] = A2[(int64_t)g * 64 + row_off[m] + lane];
+}
+
+// One (row, group) slot of lane's row against group g of every row m of A:
+//     x[m] = sum_k a[m,k] (128 + c_k) - (128 + 2^(b-1)) sum_k a[m,k]
+// (offset 128 for b = 8); the caller applies the group scale.  `a` points at
+// the group's first activation pair of row 0 (read with scalar loads);
+// `row_off[m]` is row m's offset in pairs; `alane` the slot's al[].
+template <int B, int MT>
+__device__ __forceinline__ void group_terms(const uint32_t *w, const uint32_t *a,
+                                            const int *row_off, const uint32_t *alane,
+                                            uint32_t mask, uint32_t magic, float *x) {
+    constexpr float kOff = (B == 8) ? 128.0f : (float)(128 + (1 << (B - 1)));
+    float d[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) d[m] = 0.0f;
+    if constexpr (B == 8) {
+        dot_bytes<MT>(w, a, row_off, d);
+    } else if constexpr (MT == 1) {
+        // One row: all 64 activation pairs of the group come in with four
+        // wide scalar loads issued together.
+        typedef typename UVec<16>::type vec16;
+        vec16 av[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) av[c] = *reinterpret_cast<const vec16 *>(a + 16 * c);
+        DotChunk<B, 1, 16, 0, 0>::run(w, &av[0], mask, magic, d);
+        DotChunk<B, 1, 16, 16, 0>::run(w, &av[1], mask, magic, d);
+        DotChunk<B, 1, 16, 32, 0>::run(w, &av[2], mask, magic, d);
+        DotChunk<B, 1, 16, 48, 0>::run(w, &av[3], mask, magic, d);
+    } else {
+        DotPairs<B, MT, 0>::run(w, a, row_off, mask, magic, d);
+    }
+    // Sum of this group's activations per row m: lane l adds pair l, then
+    // a DPP reduction across the wave (wave-uniform result).
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const float asum = wave_sum_uniform(dot2_bf16(alane[m], 0x3F803F80u, 0.0f));
+        x[m] = fmaf(-kOff, asum, d[m]);
+    }
+}
+
 template <int B, int MT, int W, class WL>
 __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restrict__ A, int M,
                                                         int N, int K, WL wl,
@@ -133,7 +197,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
                                                         int splits, int gps) {
     static_assert(W * MT <= 64, "LDS reduction table");
     __shared__ float red[W][MT][64];
-    __shared__ unsigned ticket_sh;
 
     const int G = K / kGroup;
     const int R = blockIdx.x / splits;
@@ -149,7 +212,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     // Dense rows beyond N do not exist: read row N-1 and drop the result.
     // Tiled blobs hold zero-padded rows, so nothing to clamp there.
     const int64_t nr = (WL::kTiled || n < N) ? n : (int64_t)N - 1;
-    constexpr float kOff = (B == 8) ? 128.0f : (float)(128 + (1 << (B - 1)));
 
     float acc[MT];
 #pragma unroll
@@ -163,87 +225,92 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
 
     // Each wave walks groups g_begin + wave, + W, ...; the next group's chunks
     // are loaded before the current one is computed.
-    uint32_t w[4 * B], wn[4 * B];
+    SlotRegs<B, MT> cur, nxt;
     int g = g_begin + wave;
-    if (g < g_end) load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), w);
+    if (g < g_end) load_slot_regs<B, MT>(wl, nr, g, A2, row_off, lane, cur);
     for (; g < g_end; g += W) {
         const int gn = g + W;
-        if (gn < g_end) load_slot<B>(wl.chunks(nr, gn), wl.chunk_stride(), wn);
-        const float sc = bf16_to_f32(wl.scale(nr, g));
-        // Wave-uniform activation pairs of this group for each row m.
-        const uint32_t *a = A2 + (int64_t)g * 64;
-        float d[MT];
+        if (gn < g_end) load_slot_regs<B, MT>(wl, nr, gn, A2, row_off, lane, nxt);
+        float x[MT];
+        group_terms<B, MT>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic, x);
+        const float sc = bf16_to_f32(cur.s);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) d[m] = 0.0f;
-        if constexpr (B == 8)
-            dot_bytes<MT>(w, a, row_off, d);
-        else
-            DotPairs<B, MT, 0>::run(w, a, row_off, mask, magic, d);
-        // Sum of this group's activations per row m: lane l adds pair l, then
-        // a DPP reduction across the wave (wave-uniform result).
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const float asum =
-                wave_sum_uniform(dot2_bf16(a[row_off[m] + lane], 0x3F803F80u, 0.0f));
-            acc[m] = fmaf(sc, fmaf(-kOff, asum, d[m]), acc[m]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4 * B; ++i) w[i] = wn[i];
+        for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
+        cur = nxt;
     }
 
 #pragma unroll
     for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
     __syncthreads();
 
-    const int Npad = (int)(gridDim.x / splits) * 64;
-    if (splits == 1) {
-        for (int m = wave; m < MT; m += W) {
-            float v = red[0][m][lane];
+    // Rows m of A are summed over the waves by wave m % W; the other waves
+    // are done and leave now, so that only the waves holding outputs stay
+    // through the split-K hand-off (their compute unit can take new
+    // workgroups meanwhile).
+    const int storing = min(W, MT);
+    if (wave >= storing) return;
+    float v[(MT + W - 1) / W];
 #pragma unroll
-            for (int w2 = 1; w2 < W; ++w2) v += red[w2][m][lane];
-            if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(v);
+    for (int i = 0; i < (MT + W - 1) / W; ++i) {
+        const int m = wave + i * W;
+        v[i] = 0.0f;
+        if (m < MT) {
+            v[i] = red[0][m][lane];
+#pragma unroll
+            for (int w2 = 1; w2 < W; ++w2) v[i] += red[w2][m][lane];
+        }
+    }
+    if (splits == 1) {
+#pragma unroll
+        for (int i = 0; i < (MT + W - 1) / W; ++i) {
+            const int m = wave + i * W;
+            if (m < MT && m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(v[i]);
         }
         return;
     }
 
-    // Cross-workgroup reduction.  All shared data moves through device-scope
-    // relaxed atomics (coherent across the XCDs' L2s without the L2
-    // write-back/invalidate an agent-scope fence costs): partials are atomic
-    // stores, each wave waits for their completion before the barrier that
-    // precedes the ticket RMW, and the last workgroup reads them back with
-    // atomic loads.
-    for (int m = wave; m < MT; m += W) {
-        float v = red[0][m][lane];
+    // Cross-workgroup reduction, per storing wave (rows m = wave + i W of
+    // this 64-row block).  Shared data moves through device-scope relaxed
+    // atomics (coherent across the XCDs' L2s without the L2
+    // write-back/invalidate an agent-scope fence costs): the partials are
+    // atomic stores, the wave waits for their completion before its ticket
+    // RMW, and the last of the `splits` waves with this (block, wave) reads
+    // them back with atomic loads, adds them in split order (deterministic)
+    // and resets the ticket.
+    const int Npad = (int)(gridDim.x / splits) * 64;
 #pragma unroll
-        for (int w2 = 1; w2 < W; ++w2) v += red[w2][m][lane];
-        __hip_atomic_store(&part[((int64_t)s * MT + m) * Npad + n], v, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < (MT + W - 1) / W; ++i) {
+        const int m = wave + i * W;
+        if (m < MT)
+            __hip_atomic_store(&part[((int64_t)s * MT + m) * Npad + n], v[i], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_vm_stores();
-    __syncthreads();  // every wave's partial stores have completed
-    if (threadIdx.x == 0)
-        ticket_sh = __hip_atomic_fetch_add(&counters[R], 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (ticket_sh != (unsigned)(splits - 1)) return;
+    unsigned *ticket = counters + (int64_t)R * storing + wave;
+    unsigned tk = 0;
+    if (lane == 0) tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(tk) != (unsigned)(splits - 1)) return;
     // All of an output's partial loads are issued before its adds (they are
     // independent; one at a time they would put `splits` round trips on the
-    // kernel's tail), then added in split order.
-    for (int m = wave; m < MT; m += W) {
-        float v[kDecodeMaxSplits];
+    // kernel's tail).
+#pragma unroll
+    for (int i = 0; i < (MT + W - 1) / W; ++i) {
+        const int m = wave + i * W;
+        if (m >= MT) continue;
+        float p[kDecodeMaxSplits];
 #pragma unroll
         for (int t = 0; t < kDecodeMaxSplits; ++t)
-            v[t] = t < splits ? __hip_atomic_load(&part[((int64_t)t * MT + m) * Npad + n],
+            p[t] = t < splits ? __hip_atomic_load(&part[((int64_t)t * MT + m) * Npad + n],
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                               : 0.0f;
         float sum = 0.0f;
 #pragma unroll
         for (int t = 0; t < kDecodeMaxSplits; ++t)
-            if (t < splits) sum += v[t];
+            if (t < splits) sum += p[t];
         if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(sum);
     }
-    if (threadIdx.x == 0)  // leave the counter region zero
-        __hip_atomic_store(&counters[R], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0)  // leave the counter region zero
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int B, int MT, int W>

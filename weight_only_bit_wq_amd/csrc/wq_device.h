@@ -193,6 +193,15 @@ __device__ __forceinline__ void load_slot(const uint4 *p, int64_t stride, uint32
 // (s_waitcnt vmcnt(0), other counters left unconstrained.)
 __device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
+// (lgkmcnt), not for its outstanding global loads, so prefetches stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // bf16 helpers
 // ---------------------------------------------------------------------------

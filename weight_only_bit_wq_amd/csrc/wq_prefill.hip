@@ -78,14 +78,6 @@ __global__ __launch_bounds__(256) void group_sum_split_kernel(const uint16_t *__
     }
 }
 
-// Workgroup barrier that orders LDS only: global prefetches in flight stay
-// in flight (a full __syncthreads would wait for them).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // LDS tiles are rows of 16-byte chunks (8 bf16 of k).  Chunk c of row r is
 // stored at position c ^ (r mod 8) (A: 8 chunks per row) or c ^ (r mod 16)
 // (B: 16 chunks per row), so the 16 rows one MFMA operand read touches sit on
