@@ -3,7 +3,7 @@
 // At large batch the layer is compute-bound ("vLLM Quantization", Key points
 // and Pitfalls: weight-only gains fade as batch grows), so codes are
 // dequantized once per workgroup tile into LDS and the product runs on the
-// matrix cores (v_mfma_f32_16x16x32_bf16), fp32 accumulation.
+// matrix cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation.
 //
 // Exactness.  The B operand holds 128 + c as bf16 (exact for c < 128; b = 8
 // uses byte conversion, offset 128), so the integer codes are never rounded.
@@ -16,9 +16,10 @@
 // multiplies that against s[n, k'/3] as extra "pseudo-groups" with scale 1.
 // No scale or code is ever rounded to bf16.
 //
-// Tiling.  Workgroup 256 (m) x 128 (n), 8 waves of 64 x 64 (two per SIMD).
-// K runs in LDS stages of 64 for A and whole groups of 128 for B (unpacked
-// to bf16 in LDS once per workgroup), double-buffered, register-staged.
+// Tiling.  Workgroup 256 (m) x 128 (n), 8 waves of 64 x 64 (two per SIMD),
+// each as 2 x 2 MFMA blocks of 32 x 32 run in two staggered halves.  K runs
+// in whole groups of 128 through LDS (A in two phase-shifted halves, B
+// unpacked to bf16 once per workgroup, double-buffered), register-staged.
 // Workgroups an XCD runs together share an A row block.
 #include <algorithm>
 #include <cstdlib>
@@ -34,7 +35,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPM = 256;          // workgroup rows (m)
 constexpr int kPN = 128;          // workgroup cols (n)
-constexpr int kPK = 64;           // k per LDS stage
 constexpr int kPseudoK = 128;     // k' per pseudo-group
 
 // Pre-pass: per (row m, group g) v = -off * sum_{k in g} a[m,k], written as
@@ -78,37 +78,54 @@ __global__ __launch_bounds__(256) void group_sum_split_kernel(const uint16_t *__
     }
 }
 
-// LDS tiles are rows of 16-byte chunks (8 bf16 of k).  Chunk c of row r is
-// stored at position c ^ (r mod 8) (A: 8 chunks per row) or c ^ (r mod 16)
-// (B: 16 chunks per row), so the 16 rows one MFMA operand read touches sit on
-// 16 distinct bank groups and the loaders' row-major writes stay conflict
-// free (no padding).
-__device__ __forceinline__ int swz8(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// LDS tiles are rows of 16-byte chunks (8 bf16 of k), 16 chunks (one group
+// of 128 k, 256 bytes) per row; chunk c of row r sits at r*16 + (c ^ (r &
+// 15)).  LDS serves a 128-bit read 16 lanes at a time over 64 banks, and
+// the 16 consecutive rows such a lane group reads (one chunk each) land on
+// 16 distinct 16-byte bank groups; the loaders' row-wise writes (16 chunks
+// of one row per 16 lanes) are conflict free too, with no padding.
 __device__ __forceinline__ int swz16(int row, int chunk) {
     return row * 16 + (chunk ^ (row & 15));
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 // Workgroup: 512 threads = 8 waves (two per SIMD) over a 256 (m) x 128 (n)
 // output tile; wave (wm, wn) owns rows 64 wm .. +64 and columns 64 wn .. +64
-// as 4 x 4 MFMA blocks of 16 x 16.  Per block two fp32 sets live in VGPRs:
-// P (the current group) and tot (the folded sum).
+// as 2 x 2 blocks (i, j) of 32 x 32 (v_mfma_f32_32x32x16_bf16: lane l holds
+// A row l%32 and B column l%32 at k-chunk l/32; result element r of lane l
+// is row 8(r/4) + 4(l/32) + r%4, column l%32).  Per block two fp32 sets live
+// in VGPRs: P (the current group) and tot (the folded sum).
 //
-// The NP pseudo-groups run first, unpipelined (A from the pre-pass matrix,
-// B = scales, scale 1).  The G real groups are software-pipelined.  LDS: A
-// per 64-k stage (two buffers, 32 KB each), B per 128-k group (two buffers,
-// 32 KB each), the group scales per group (two buffers).  Group g (stages
-// 2g, 2g+1):
-//   stage 2g:   MFMA (A buf 0, B buf g&1, k 0..63); fold row block 3 of
-//               group g-1; write A stage 2g+1 to A buf 1; fetch A stage
-//               2g+2; unpack group g+1 into B buf (g+1)&1 and its scales
-//               into Ss; fetch the codes of group g+2;            barrier
-//   stage 2g+1: MFMA (A buf 1, B buf g&1, k 64..127); fold row blocks 0..2
-//               of group g; write A stage 2g+2 to A buf 0; fetch A stage
-//               2g+3;                                              barrier
-// Each MFMA is followed by a small slice of the other work, in a fixed
-// order: an MFMA occupies the SIMD's issue port for about two VALU slots
-// and the matrix pipe for four, so about two VALU operations per MFMA issue
-// for free.
+// Staggered halves.  Folding a group (tot += s * P, one FMA per output
+// element) must read P after the group's last MFMA on it has completed and
+// before the next group's first MFMA overwrites it.  So each group runs in
+// two phases of 16 MFMA slots: phase 0 runs the 8 k-steps of blocks (0, *),
+// phase 1 those of blocks (1, *) (two accumulation chains each, alternating
+// j).  Phase 0 folds the (1, *) blocks of the previous group and phase 1 the
+// (0, *) blocks of this one, whose MFMAs finished a phase earlier: two FMAs
+// per slot, no wait on the matrix pipe.  The 32 x 32 x 16 MFMA holds the
+// matrix pipe about four times as long as the issue port, so the fold and
+// the code unpack (about 1.5 VALU per slot) issue beside it.
+//
+// LDS.  A is held one group at a time as two halves: half h has, for every
+// wave, its 32 rows of block row h (128 rows x 128 k, 32 KB); half 0 is read
+// in phase 0 and refilled with the next group during phase 1, half 1 the
+// other way round.  B (128 rows x 128 k, 32 KB) is double-buffered by group
+// and the group's scales sit beside it.  The NP pseudo-groups run first,
+// unpipelined (A from the pre-pass matrix, B = scales, scale 1); the G real
+// groups are software-pipelined:
+//   group g, phase 0: fold (1, *) of g-1; unpack codes of g+1 into the other
+//     B buffer (one pair every other slot, both phases); fetch the codes of
+//     g+2 (a second register set) at slot 1; write A half 1 of g (fetched in
+//     phase 1 of g-1) at slots 4-7, a 16-byte piece each; fetch A half 0 of
+//     g+1 at slot 8; barrier after slot 13, then read phase 1's first k-step;
+//   group g, phase 1: fold (0, *) of g; finish the unpack by slot 11 (with
+//     the scales of g+1); write A half 0 of g+1 at slots 4-7, fetch A half 1
+//     of g+1 at slot 8; barrier after slot 13, then read the first k-step of
+//     group g+1's phase 0; the codes of g+2 move to the first set.
+// Operands run one k-step ahead; the next phase's first k-step is read
+// right after the barrier, under the phase's last four MFMAs.
 template <int B, class WL>
 __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict__ A,
                                                       const uint16_t *__restrict__ Ap, int M,
@@ -116,7 +133,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
                                                       uint16_t *__restrict__ Y, int mtiles,
                                                       int ntiles, int splits,
                                                       float *__restrict__ part, int64_t mnp) {
-    __shared__ u32x4 Asm[2][kPM * 8];   // [stage buffer][256 rows x 8 chunks]
+    __shared__ u32x4 Ah[2][kPN * 16];   // [half][128 rows x 16 chunks]
     __shared__ u32x4 Bsm[2][kPN * 16];  // [group buffer][128 rows x 16 chunks]
     __shared__ float Ss[2][kPN];
 
@@ -147,17 +164,21 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     const uint32_t mask = __builtin_amdgcn_readfirstlane(pair_mask<B < 8 ? B : 7>());
     const uint32_t magic = in_vgpr(kBf16Magic128x2);
 
-    // A loader: rows ar + 64 i (i < 4), chunk ac.  Rows beyond M read row
-    // M-1 (their results are dropped).
-    const int ac = tid & 7;
-    const int ar = tid >> 3;
+    // A loader: chunk ac of half rows hr = ar + 32 u (u < 4), which are tile
+    // rows 64 u + 32 h + ar.  Rows beyond M read row M-1 (results dropped).
+    const int ac = tid & 15;
+    const int ar = tid >> 4;
     const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)kPM - 1);
-    int arows[4];
+    int arow_g[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) arows[i] = min(ar + 64 * i, mlim);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) arow_g[h][u] = min(64 * u + 32 * h + ar, mlim);
     const uint16_t *A_blk = A + m0 * K;
     const uint16_t *Ap_blk = Ap + m0 * Kp;
-    const int a_lds = swz8(ar, ac);  // + 512 i
+    int a_lds[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a_lds[u] = swz16(ar + 32 * u, ac);
 
     // B loader: row brow, quarter bq (wave-uniform) of each group.
     const int brow = tid & (kPN - 1);
@@ -168,30 +189,37 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     const int bstep = (int)wl.slot_step();
     const int sstep = (int)wl.scale_step();
 
-    // MFMA operand rows and k-chunk of this lane.
-    const int arow = wm * 64 + (lane & 15);
-    const int bmrow = wn * 64 + (lane & 15);
-    const int q = lane >> 4;
+    // MFMA operand rows (in an A half and in B) and k-chunk half of this lane.
+    const int arow = wm * 32 + (lane & 31);
+    const int bmrow = wn * 64 + (lane & 31);
+    const int khalf = lane >> 5;
 
     u32x4 areg[4];
-    uint32_t creg[B];
-    f32x4_t tot[4][4], P[4][4];
+    uint32_t creg[B], cnext[B];
+    f32x16_t tot[2][2], P[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) tot[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                tot[i][j][r] = 0.0f;
+                P[i][j][r] = 0.0f;
+            }
+        }
 
-    // Real stage s (64 k of group s/2), clamped to this split's last one.
-    auto load_a = [&](int s) __attribute__((always_inline)) {
-        s = min(s, 2 * g_hi - 1);
-        const uint16_t *src = A_blk + (s >> 1) * kGroup + (s & 1) * kPK;
+    // A half h of real group g (clamped to this split's last one) into areg
+    // / from areg into LDS.
+    auto load_a = [&](int g, int h) __attribute__((always_inline)) {
+        const uint16_t *src = A_blk + min(g, g_hi - 1) * kGroup + 8 * ac;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            areg[i] = *reinterpret_cast<const u32x4 *>(src + __mul24(arows[i], K) + 8 * ac);
+        for (int u = 0; u < 4; ++u)
+            areg[u] = *reinterpret_cast<const u32x4 *>(src + __mul24(arow_g[h][u], K));
     };
-    auto store_a = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Asm[buf][a_lds + 512 * i] = areg[i];
+    // One of the four 16-byte pieces (spread over four slots, so the LDS
+    // write queue never takes a whole phase's worth at once).
+    auto store_a = [&](int h, int u) __attribute__((always_inline)) {
+        Ah[h][a_lds[u]] = areg[u];
     };
     // Quarter bq of real group g's codes (clamped to the last group): B
     // dwords at per-wave offsets held in scalar registers.
@@ -201,10 +229,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
         const int d = bq * B + e;
         qoff[e] = __builtin_amdgcn_readfirstlane((d >> 2) * (WL::kTiled ? 1024 : 16) + (d & 3) * 4);
     }
-    auto load_codes = [&](int g) __attribute__((always_inline)) {
+    auto load_codes = [&](int g, uint32_t(&dst)[B]) __attribute__((always_inline)) {
         const uint8_t *slot = bslot0 + (int64_t)min(g, g_hi - 1) * bstep;
 #pragma unroll
-        for (int e = 0; e < B; ++e) creg[e] = *reinterpret_cast<const uint32_t *>(slot + qoff[e]);
+        for (int e = 0; e < B; ++e) dst[e] = *reinterpret_cast<const uint32_t *>(slot + qoff[e]);
     };
     // Chunk C (pairs 4C .. 4C+3, 8 codes) of the B operand (128 + c as bf16)
     // from creg into B buffer buf.
@@ -222,78 +250,77 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
         Ss[buf][brow] =
             bf16_to_f32(*reinterpret_cast<const uint16_t *>(bscale0 + min(g, g_hi - 1) * sstep));
     };
-    auto fold_block = [&](int i, int j, const float(&sq)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tot[i][j][r] = fmaf(sq[j], P[i][j][r], tot[i][j][r]);
+    // Slice q (of 16) of folding block row i with column scales sq: the
+    // slot's two FMAs.
+    auto fold_slice = [&](int i, int q, const float(&sq)[2]) __attribute__((always_inline)) {
+        const int j = q >> 3, r = 2 * (q & 7);
+        tot[i][j][r] = fmaf(sq[j], P[i][j][r], tot[i][j][r]);
+        tot[i][j][r + 1] = fmaf(sq[j], P[i][j][r + 1], tot[i][j][r + 1]);
     };
 
-    // One 64-k stage of the wave's 4 x 4 blocks: 8 steps (k-step kk, row
-    // block i) of 4 MFMAs.  After each MFMA, hook(step, j) issues a slice of
-    // the stage's other work (about one MFMA's worth of VALU), and the pair
-    // is fenced, so the order written here is the issue order: the matrix
-    // core always has queued work while the VALU slices issue.  Operands of
-    // step s+1 are read from LDS at the start of step s.  H = 0 opens a
-    // group: k-step 0 starts each block from zero.
-    auto mfma_stage = [&](int abuf, int gbuf, auto hconst, auto &&hook)
+    // Operands of one k-step (A half ah, B buffer gb): sets 0 and 1 hold
+    // k-steps of the running phase in turn, set 2 the next phase's k-step 0.
+    bf16x8_t af[3], bfr[3][2];
+    auto read_ops = [&](int ah, int gbuf, int kk, int e) __attribute__((always_inline)) {
+        af[e] = __builtin_bit_cast(bf16x8_t, Ah[ah][swz16(arow, 2 * kk + khalf)]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            bfr[e][j] = __builtin_bit_cast(bf16x8_t, Bsm[gbuf][swz16(bmrow + 32 * j, 2 * kk + khalf)]);
+    };
+
+    // One phase: the 8 k-steps of blocks (I, 0), (I, 1) from A half I and B
+    // buffer gbuf, starting from k-step 0's operands in set 2; k-step kk+1 is
+    // read into set (kk+1) & 1 at the start of k-step kk.  After each MFMA,
+    // hook(slot) issues a slice of the other work and the pair is fenced, so
+    // the order written here is the issue order.  With NEXT, the workgroup
+    // barrier follows slot 13: by then every operand read of this phase has
+    // been issued (the last one, k-step 7's, at the start of k-step 6), so
+    // no wave past the barrier can overwrite a buffer another wave still
+    // has to read; and every LDS write the next phase needs is issued in the
+    // hooks before it.  Then the next phase's k-step 0 (A half na, B buffer
+    // ngb) is read into set 2, under the phase's last two MFMAs.
+    auto phase = [&](auto iconst, int gbuf, auto nconst, int na, int ngb, auto &&hook)
         __attribute__((always_inline)) {
-        constexpr int H = decltype(hconst)::value;
-        const u32x4 *as = Asm[abuf];
-        const u32x4 *bs = Bsm[gbuf];
-        bf16x8_t bfr[2][4], af[2];
+        constexpr int I = decltype(iconst)::value;
+        constexpr bool NEXT = decltype(nconst)::value;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bfr[0][j] = __builtin_bit_cast(bf16x8_t, bs[swz16(bmrow + 16 * j, 8 * H + q)]);
-        af[0] = __builtin_bit_cast(bf16x8_t, as[swz8(arow, q)]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < 8; ++kk) {
+            if (kk + 1 < 8) read_ops(I, gbuf, kk + 1, (kk + 1) & 1);
+            const int e = kk == 0 ? 2 : (kk & 1);
 #pragma unroll
-        for (int step = 0; step < 8; ++step) {
-            const int kk = step >> 2, i = step & 3;
-            if (i < 3) {
-                af[(step + 1) & 1] =
-                    __builtin_bit_cast(bf16x8_t, as[swz8(arow + 16 * (i + 1), 4 * kk + q)]);
-            } else if (kk == 0) {
-                af[(step + 1) & 1] = __builtin_bit_cast(bf16x8_t, as[swz8(arow, 4 + q)]);
-            }
-            if (step == 2) {
+            for (int j = 0; j < 2; ++j) {
+                f32x16_t c = P[I][j];
+                if (kk == 0) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    bfr[1][j] = __builtin_bit_cast(bf16x8_t,
-                                                   bs[swz16(bmrow + 16 * j, 8 * H + 4 + q)]);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                P[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    af[step & 1], bfr[kk][j],
-                    (H == 0 && kk == 0) ? f32x4_t{0.0f, 0.0f, 0.0f, 0.0f} : P[i][j], 0, 0, 0);
-                hook(step, j);
+                    for (int r = 0; r < 16; ++r) c[r] = 0.0f;
+                }
+                P[I][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[e], bfr[e][j], c, 0, 0, 0);
+                const int slot = 2 * kk + j;
+                hook(slot);
+                if (NEXT && slot == 13) {
+                    lds_barrier();
+                    read_ops(na, ngb, 0, 2);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    // Folding group t (scales sq) runs one row block behind its last
-    // k-step: rows 0..2 during steps 5..7 of its closing stage, row 3
-    // during step 0 of the next group's opening stage (before step 3
-    // restarts P[3]).  P starts at zero, so the first such row-3 fold adds
-    // nothing.
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) P[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float sq_prev[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float sq_prev[2] = {0.0f, 0.0f};
 
     // ---- pseudo-groups (scale 1), not pipelined: A' from the pre-pass
     // matrix, B' = s[n, k'/3] (zero beyond 3G) ----
     {
-        const float one[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        const float one[2] = {1.0f, 1.0f};
         for (int ps = 0; ps < (sp == 0 ? NP : 0); ++ps) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const uint16_t *src = Ap_blk + ps * kPseudoK + h * kPK;
+                const uint16_t *src = Ap_blk + ps * kPseudoK + 8 * ac;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    areg[i] = *reinterpret_cast<const u32x4 *>(src + __mul24(arows[i], Kp) + 8 * ac);
-                store_a(h);
+                for (int u = 0; u < 4; ++u)
+                    areg[u] = *reinterpret_cast<const u32x4 *>(src + __mul24(arow_g[h][u], Kp));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) store_a(h, u);
             }
             const int k0 = ps * kPseudoK + 32 * bq;
 #pragma unroll
@@ -311,86 +338,98 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
                 Bsm[0][swz16(brow, 4 * bq + u)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
             }
             lds_barrier();
-            mfma_stage(0, 0, std::integral_constant<int, 0>{}, [&](int step, int j) {
-                if (step == 0) fold_block(3, j, sq_prev);
-            });
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sq_prev[j] = one[j];
-            mfma_stage(1, 0, std::integral_constant<int, 1>{}, [&](int step, int j) {
-                if (step >= 5) fold_block(step - 5, j, one);
-            });
+            read_ops(0, 0, 0, 2);
+            phase(std::integral_constant<int, 0>{}, 0, std::integral_constant<bool, false>{}, 0,
+                  0, [&](int slot) { fold_slice(1, slot, sq_prev); });
+            sq_prev[0] = one[0];
+            sq_prev[1] = one[1];
+            read_ops(1, 0, 0, 2);
+            phase(std::integral_constant<int, 1>{}, 0, std::integral_constant<bool, false>{}, 0,
+                  0, [&](int slot) { fold_slice(0, slot, one); });
             lds_barrier();
         }
     }
 
     // ---- real groups, software-pipelined ----
     {
-        // Prologue: group 0's B and scales, A stage 0 in LDS, A stage 1 and
-        // the codes of group 1 in registers.
-        load_codes(g_lo);
+        // Prologue: group g_lo's B, scales and both A halves in LDS; the
+        // codes of g_lo + 1 in registers.
+        load_codes(g_lo, creg);
         fill_chunk(0, std::integral_constant<int, 0>{});
         fill_chunk(0, std::integral_constant<int, 1>{});
         fill_chunk(0, std::integral_constant<int, 2>{});
         fill_chunk(0, std::integral_constant<int, 3>{});
         store_scale(g_lo, 0);
-        load_a(2 * g_lo);
-        store_a(0);
-        load_a(2 * g_lo + 1);
-        load_codes(g_lo + 1);
+        load_a(g_lo, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) store_a(0, u);
+        load_a(g_lo, 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) store_a(1, u);
+        load_codes(g_lo + 1, creg);
         lds_barrier();
+        read_ops(0, 0, 0, 2);
 
         for (int g = g_lo; g < g_hi; ++g) {
             const int gb = (g - g_lo) & 1, nb = gb ^ 1;
-            float sq[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sq[j] = Ss[gb][wn * 64 + 16 * j + (lane & 15)];
-            // stage 2g (A buffer 0): finish folding the previous group; write
-            // A stage 2g+1, fetch A stage 2g+2; unpack group g+1 into the
-            // other B buffer (past the end: a harmless rewrite of a buffer
-            // nobody reads), one code pair per MFMA; fetch the codes of group
-            // g+2.
+            const bool first = g == g_lo;
             uint32_t pairs[16];
-            mfma_stage(0, gb, std::integral_constant<int, 0>{}, [&](int step, int j) {
-                if (step == 0) fold_block(3, j, sq_prev);
-                if (step == 1 && j == 0) store_a(1);
-                if (step == 2 && j == 0) load_a(2 * g + 2);
-                if (step >= 4) {
-                    const int pr = 4 * (step - 4) + j;
-                    pairs[pr] = quarter_pair_dyn<B>(pr, creg, mask, magic);
-                    if (j == 3)
-                        Bsm[nb][swz16(brow, 4 * bq + (step - 4))] =
-                            u32x4{pairs[pr - 3], pairs[pr - 2], pairs[pr - 1], pairs[pr]};
-                    if (step == 7 && j == 3) {
-                        store_scale(g + 1, nb);
-                        load_codes(g + 2);
-                    }
-                }
-            });
-            lds_barrier();
-            // stage 2g+1 (A buffer 1): write A stage 2g+2, fetch A stage
-            // 2g+3; fold rows 0..2 of group g.
-            mfma_stage(1, gb, std::integral_constant<int, 1>{}, [&](int step, int j) {
-                if (step == 1 && j == 0) store_a(0);
-                if (step == 2 && j == 0) load_a(2 * g + 3);
-                if (step >= 5) fold_block(step - 5, j, sq);
-            });
+            // Unpack pair p of group g+1 at global slot 2p (p < 14), pairs
+            // 14 and 15 at slot 27; a 16-byte chunk goes to LDS every four.
+            auto unpack = [&](int sigma) __attribute__((always_inline)) {
+                int p0 = -1, p1 = -1;
+                if (sigma < 28 && (sigma & 1) == 0) p0 = sigma >> 1;
+                if (sigma == 27) { p0 = 14; p1 = 15; }
+                if (p0 >= 0) pairs[p0] = quarter_pair_dyn<B>(p0, creg, mask, magic);
+                if (p1 >= 0) pairs[p1] = quarter_pair_dyn<B>(p1, creg, mask, magic);
+                const int last = p1 >= 0 ? p1 : p0;
+                if (last >= 0 && (last & 3) == 3)
+                    Bsm[nb][swz16(brow, 4 * bq + (last >> 2))] =
+                        u32x4{pairs[last - 3], pairs[last - 2], pairs[last - 1], pairs[last]};
+            };
+            // Phase 0: blocks (0, *) of g; fold (1, *) of g-1.
+            phase(std::integral_constant<int, 0>{}, gb, std::integral_constant<bool, true>{}, 1,
+                  gb, [&](int slot) {
+                      fold_slice(1, slot, sq_prev);
+                      unpack(slot);
+                      if (slot == 1) load_codes(g + 2, cnext);
+                      if (slot >= 4 && slot <= 7 && !first) store_a(1, slot - 4);
+                      if (slot == 8) load_a(g + 1, 0);
+                  });
+            // Phase 1: blocks (1, *) of g; fold (0, *) of g.
+            float sq[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sq_prev[j] = sq[j];
-            lds_barrier();
+            for (int j = 0; j < 2; ++j) sq[j] = Ss[gb][wn * 64 + 32 * j + (lane & 31)];
+            phase(std::integral_constant<int, 1>{}, gb, std::integral_constant<bool, true>{}, 0,
+                  nb, [&](int slot) {
+                      fold_slice(0, slot, sq);
+                      unpack(16 + slot);
+                      if (slot == 11) store_scale(g + 1, nb);
+                      if (slot == 15) {
+#pragma unroll
+                          for (int e = 0; e < B; ++e) creg[e] = cnext[e];
+                      }
+                      if (slot >= 4 && slot <= 7) store_a(0, slot - 4);
+                      if (slot == 8) load_a(g + 1, 1);
+                  });
+            sq_prev[0] = sq[0];
+            sq_prev[1] = sq[1];
         }
+        // The last group's (1, *) blocks.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fold_block(3, j, sq_prev);
+        for (int q = 0; q < 16; ++q) fold_slice(1, q, sq_prev);
     }
 
-    // Output element r of block (i, j): row 4*(lane/16) + r, column lane%16.
+    // Output element r of block (i, j): row 8(r/4) + 4(lane/32) + r%4,
+    // column lane%32.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + wn * 64 + 16 * j + (lane & 15);
+        for (int j = 0; j < 2; ++j) {
+            const int64_t n = n0 + wn * 64 + 32 * j + (lane & 31);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * khalf + (r & 3);
                 if (m < M && n < N) {
                     if (splits == 1)
                         Y[m * N + n] = f32_to_bf16_rne(tot[i][j][r]);
