@@ -91,11 +91,8 @@ void parallel_rows(int64_t N, int64_t work_per_row, F f) {
 // 17408 and 17408 x 5120 layers); WQ_DECODE_MFMA_MIN_M overrides it (17
 // turns the matrix-core path off).
 int decode_mfma_min_m() {
-    static const int v = [] {
-        const char *e = std::getenv("WQ_DECODE_MFMA_MIN_M");
-        return e ? std::atoi(e) : 5;
-    }();
-    return v;
+    const char *e = std::getenv("WQ_DECODE_MFMA_MIN_M");  // read per call, like the plans' overrides
+    return e ? std::atoi(e) : 5;
 }
 
 int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int b) {
