@@ -144,13 +144,13 @@ __device__ __forceinline__ uint32_t code_pair(const uint32_t *w) {
     return code_pair_raw<B, P>(w) & pair_mask<B>();
 }
 
-// (x & m) | c in one v_and_or_b32.  gfx9 VOP3 encodings take no literal
-// constants and at most one scalar operand, so the mask comes in an SGPR and
-// the constant in a VGPR (the caller materialises both once).
+// (x & m) | c, selected as one v_and_or_b32: gfx9 VOP3 encodings take no
+// literal constants and at most one scalar operand, so the mask comes in an
+// SGPR (wave-uniform) and the constant in a VGPR the compiler cannot see
+// through (in_vgpr), which the caller materialises once.  Plain code rather
+// than inline assembly, so the hazard recognizer and scheduler see it.
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m_sgpr, uint32_t c_vgpr) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m_sgpr), "v"(c_vgpr));
-    return r;
+    return (x & m_sgpr) | c_vgpr;
 }
 
 // For B <= 7: the pair as two bf16 values (128 + c0, 128 + c1), exact.
