@@ -188,7 +188,10 @@ __device__ __forceinline__ void group_terms(const uint32_t *w, const uint32_t *a
     }
 }
 
-template <int B, int MT, int W, class WL>
+// ONE: every wave has at most one group (gps <= W, the plan for large
+// layers at small M): no prefetch register set, so more waves fit per SIMD
+// (used for row tiles of 2 and more, where that measured faster).
+template <int B, int MT, int W, class WL, bool ONE>
 __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restrict__ A, int M,
                                                         int N, int K, WL wl,
                                                         uint16_t *__restrict__ Y,
@@ -225,18 +228,31 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
 
     // Each wave walks groups g_begin + wave, + W, ...; the next group's chunks
     // are loaded before the current one is computed.
-    SlotRegs<B, MT> cur, nxt;
-    int g = g_begin + wave;
-    if (g < g_end) load_slot_regs<B, MT>(wl, nr, g, A2, row_off, lane, cur);
-    for (; g < g_end; g += W) {
-        const int gn = g + W;
-        if (gn < g_end) load_slot_regs<B, MT>(wl, nr, gn, A2, row_off, lane, nxt);
-        float x[MT];
-        group_terms<B, MT>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic, x);
-        const float sc = bf16_to_f32(cur.s);
+    if constexpr (ONE) {
+        const int g = g_begin + wave;
+        if (g < g_end) {
+            SlotRegs<B, MT> cur;
+            load_slot_regs<B, MT>(wl, nr, g, A2, row_off, lane, cur);
+            float x[MT];
+            group_terms<B, MT>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic, x);
+            const float sc = bf16_to_f32(cur.s);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
-        cur = nxt;
+            for (int m = 0; m < MT; ++m) acc[m] = sc * x[m];
+        }
+    } else {
+        SlotRegs<B, MT> cur, nxt;
+        int g = g_begin + wave;
+        if (g < g_end) load_slot_regs<B, MT>(wl, nr, g, A2, row_off, lane, cur);
+        for (; g < g_end; g += W) {
+            const int gn = g + W;
+            if (gn < g_end) load_slot_regs<B, MT>(wl, nr, gn, A2, row_off, lane, nxt);
+            float x[MT];
+            group_terms<B, MT>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic, x);
+            const float sc = bf16_to_f32(cur.s);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
+            cur = nxt;
+        }
     }
 
 #pragma unroll
@@ -325,14 +341,29 @@ hipError_t decode_bmw(const uint16_t *A, int64_t M, int64_t N, int64_t K, const 
         part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
     }
     const dim3 grid((unsigned)(p.rowblocks * p.splits));
+    // Measured (same box, alternating): the single-slot variant's extra
+    // occupancy gains 3.5% at M = 4 and loses 3.5% at M = 1.
+    const bool one = MT > 1 && p.gps <= W;
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W_), G, B};
-        hipLaunchKernelGGL((decode_kernel<B, MT, W, TiledW>), grid, dim3(64 * W), 0, stream, A,
-                           (int)M, (int)N, (int)K, wl, Y, part, counters, p.splits, p.gps);
+        if (one)
+            hipLaunchKernelGGL((decode_kernel<B, MT, W, TiledW, true>), grid, dim3(64 * W), 0,
+                               stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
+                               p.splits, p.gps);
+        else
+            hipLaunchKernelGGL((decode_kernel<B, MT, W, TiledW, false>), grid, dim3(64 * W), 0,
+                               stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
+                               p.splits, p.gps);
     } else {
         DenseW wl{static_cast<const uint8_t *>(W_), scales, (int64_t)16 * B * G, G, B};
-        hipLaunchKernelGGL((decode_kernel<B, MT, W, DenseW>), grid, dim3(64 * W), 0, stream, A,
-                           (int)M, (int)N, (int)K, wl, Y, part, counters, p.splits, p.gps);
+        if (one)
+            hipLaunchKernelGGL((decode_kernel<B, MT, W, DenseW, true>), grid, dim3(64 * W), 0,
+                               stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
+                               p.splits, p.gps);
+        else
+            hipLaunchKernelGGL((decode_kernel<B, MT, W, DenseW, false>), grid, dim3(64 * W), 0,
+                               stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
+                               p.splits, p.gps);
     }
     return hipGetLastError();
 }
