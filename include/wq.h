@@ -141,12 +141,13 @@ int wq_unpack_dev(const void *W_d, int layout, int64_t N, int64_t K, int b, int 
 
 /* Workspace bytes wq_gemm (op = WQ_OP_GEMM) or wq_gemm_a8 (WQ_OP_GEMM_A8)
  * needs for this problem (0 if none; -1 for invalid arguments).  Every
- * non-empty workspace begins with a 64 KiB region of counters that must be
- * zero before the first call that uses it; every call leaves that region
- * zero again, whatever the op or shape, so one workspace (sized for the
- * largest call) can serve any sequence of calls ordered on one stream.
- * The rest is scratch.  Calls that may run concurrently need separate
- * workspaces. */
+ * non-empty workspace begins with a region of WQ_WORKSPACE_ZERO_BYTES of
+ * split-K counters that must be zero before the first call that uses it;
+ * every call leaves that region zero again, whatever the op or shape, so one
+ * workspace (sized for the largest call) can serve any sequence of calls
+ * ordered on one stream.  The rest is scratch.  Calls that may run
+ * concurrently need separate workspaces. */
+#define WQ_WORKSPACE_ZERO_BYTES ((int64_t)1 << 16)
 int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int group);
 
 /* Device.  WNA16 layer: Y_d bf16 [M, N] = A_d bf16 [M, K] . dequant(W)^T.

@@ -3,6 +3,7 @@ every function include/wq.h declares, the host packer agrees with the oracle
 bit for bit, and every argument error is refused with its status before any
 device work (forced from the host with fake, never dereferenced pointers)."""
 import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -156,3 +157,13 @@ def test_repacked_sizes():
     assert tiled == N * 960 * 4 + N * (K // 128) * 2
     assert wq.wq_repacked_bytes(wq.WQ_LAYOUT_TILED, 65, K, b) == 2 * 40 * (6 * 1024 + 128)
     assert wq.wq_repacked_bytes(2, N, K, b) == -1
+
+
+def test_workspace_zero_region_constant():
+    # The binding's zero-region size is the one include/wq.h defines.
+    import re
+    with open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "include", "wq.h")) as f:
+        m = re.search(r"#define WQ_WORKSPACE_ZERO_BYTES \(\(int64_t\)(\d+) << (\d+)\)", f.read())
+    assert m, "WQ_WORKSPACE_ZERO_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == wq.WORKSPACE_ZERO_BYTES

@@ -318,7 +318,7 @@ def test_workspace_reused_across_shapes_and_ops():
         L4 = Layer(w4, wq.WQ_LAYOUT_TILED)
         wq.wq_gemm_a8(dev_bf16(w4.A), L4.W_d, L4.layout, None, 64, 4, ws=ws)
     torch.cuda.synchronize()
-    assert not ws[:65536].any()
+    assert not ws[:wq.WORKSPACE_ZERO_BYTES].any()
 
 
 @pytest.mark.parametrize("b,M,K,N", [(6, 1, 5120, 17408), (6, 4, 17408, 5120), (5, 16, 5120, 17408)])
@@ -365,4 +365,4 @@ def test_decode_split_k_forced(M, waves, monkeypatch):
     y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
     assert_wna16(host_bf16_bits(Y0), y_ref, mag, "forced split-K M=%d waves=%d" % (M, waves))
     assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
-    assert not ws[:65536].any()
+    assert not ws[:wq.WORKSPACE_ZERO_BYTES].any()

@@ -50,6 +50,8 @@ WQ_OP_GEMM_A8 = 1
 WQ_OUT_BF16 = 0
 WQ_OUT_F32 = 1
 GROUP = 128
+# Leading workspace bytes that must be zero before a call and are zero after it.
+WORKSPACE_ZERO_BYTES = 1 << 16
 
 
 class WQError(RuntimeError):

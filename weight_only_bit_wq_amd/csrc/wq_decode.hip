@@ -56,6 +56,12 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b) {
     if ((int64_t)p.rowblocks * std::min(waves, p.mt) > kWsMaxCounters) splits = 1;
     splits = std::min(std::min(splits, G), kDecodeMaxSplits);
     p.waves = waves;
+    // Tickets 32 counters (one 128-byte line) apart where the counter region
+    // allows: packed together, the tickets of neighbouring row blocks share a
+    // line and their device-scope atomics queue behind each other.
+    const int64_t tickets = (int64_t)p.rowblocks * std::min(waves, p.mt);
+    p.tstride = 1;
+    while (p.tstride < 32 && tickets * p.tstride * 2 <= kWsMaxCounters) p.tstride *= 2;
     p.gps = (G + splits - 1) / splits;
     p.splits = (G + p.gps - 1) / p.gps;
     if (p.splits > 1)

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
                                                         uint16_t *__restrict__ Y,
                                                         float *__restrict__ part,
                                                         unsigned *__restrict__ counters,
-                                                        int splits, int gps) {
+                                                        int splits, int gps, int tstride) {
     static_assert(W * MT <= 64, "LDS reduction table");
     __shared__ float red[W][MT][64];
 
@@ -294,6 +294,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     // them back with atomic loads, adds them in split order (deterministic)
     // and resets the ticket.
     const int Npad = (int)(gridDim.x / splits) * 64;
+    unsigned *ticket = counters + ((int64_t)R * storing + wave) * tstride;
 #pragma unroll
     for (int i = 0; i < (MT + W - 1) / W; ++i) {
         const int m = wave + i * W;
@@ -302,13 +303,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
                                __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_vm_stores();
-    unsigned *ticket = counters + (int64_t)R * storing + wave;
     unsigned tk = 0;
     if (lane == 0) tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (__builtin_amdgcn_readfirstlane(tk) != (unsigned)(splits - 1)) return;
-    // All of an output's partial loads are issued before its adds (they are
-    // independent; one at a time they would put `splits` round trips on the
-    // kernel's tail).
+    // All of an output's partial loads are issued before its adds, without
+    // branches (indices past the last split repeat it and are not added): one
+    // at a time, or behind a branch the compiler waits on, they would put
+    // extra round trips on the kernel's tail.
 #pragma unroll
     for (int i = 0; i < (MT + W - 1) / W; ++i) {
         const int m = wave + i * W;
@@ -316,12 +317,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         float p[kDecodeMaxSplits];
 #pragma unroll
         for (int t = 0; t < kDecodeMaxSplits; ++t)
-            p[t] = t < splits ? __hip_atomic_load(&part[((int64_t)t * MT + m) * Npad + n],
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                              : 0.0f;
-        float sum = 0.0f;
+            p[t] = __hip_atomic_load(&part[((int64_t)min(t, splits - 1) * MT + m) * Npad + n],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float sum = p[0];
 #pragma unroll
-        for (int t = 0; t < kDecodeMaxSplits; ++t)
+        for (int t = 1; t < kDecodeMaxSplits; ++t)
             if (t < splits) sum += p[t];
         if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16_rne(sum);
     }
@@ -349,21 +349,21 @@ hipError_t decode_bmw(const uint16_t *A, int64_t M, int64_t N, int64_t K, const 
         if (one)
             hipLaunchKernelGGL((decode_kernel<B, MT, W, TiledW, true>), grid, dim3(64 * W), 0,
                                stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
-                               p.splits, p.gps);
+                               p.splits, p.gps, p.tstride);
         else
             hipLaunchKernelGGL((decode_kernel<B, MT, W, TiledW, false>), grid, dim3(64 * W), 0,
                                stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
-                               p.splits, p.gps);
+                               p.splits, p.gps, p.tstride);
     } else {
         DenseW wl{static_cast<const uint8_t *>(W_), scales, (int64_t)16 * B * G, G, B};
         if (one)
             hipLaunchKernelGGL((decode_kernel<B, MT, W, DenseW, true>), grid, dim3(64 * W), 0,
                                stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
-                               p.splits, p.gps);
+                               p.splits, p.gps, p.tstride);
         else
             hipLaunchKernelGGL((decode_kernel<B, MT, W, DenseW, false>), grid, dim3(64 * W), 0,
                                stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
-                               p.splits, p.gps);
+                               p.splits, p.gps, p.tstride);
     }
     return hipGetLastError();
 }

@@ -30,6 +30,7 @@ struct DecodePlan {
     int gps;        // groups per split
     int waves;      // waves per workgroup (4, 8 or 16; 16 only for mt <= 4, 8 for mt <= 8)
     int rowblocks;  // ceil(N / 64)
+    int tstride;    // counters from one split-K ticket to the next (spreads them over cache lines)
     int64_t ws_bytes;
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b);
