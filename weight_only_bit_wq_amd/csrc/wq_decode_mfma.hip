@@ -291,21 +291,29 @@ hipError_t launch_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const vo
 
 }  // namespace
 
-// 64-row blocks (RB = 4: the activations loaded once per group serve 64
-// weight rows); K splits across workgroups for about 1024 workgroups (four
-// per compute unit) with at least 4 groups each; 2 waves per workgroup with
-// at least 2 groups each.  Measured on the 5120 x 17408 and 17408 x 5120
-// layers (b = 6, M = 2..16) against 2048 / 4096 workgroups and 4 waves.
-// WQ_DMFMA_TARGET_WGS and WQ_DMFMA_KS override the two targets.  Row blocks
-// beyond the counter region fall back to one split.
+// 32-row blocks (RB = 2: 109-120 VGPRs, four waves per SIMD; RB = 4 needs
+// 167-184, two per SIMD, and RB = 1 reloads the activations for every 16
+// rows); K splits across workgroups only up to about 512 workgroups (the
+// 5120 -> 17408 layer then runs unsplit, without a hand-off), with at least
+// 4 groups each; 4 waves per workgroup with at least 2 groups each.
+// Measured on the 5120 x 17408 and 17408 x 5120 layers (b = 6, M = 8 and
+// 16) against RB = 1 and 4, 768 to 4096 workgroups and 1, 2 or 8 waves:
+// 10-16% faster than 64-row blocks at 1024 workgroups of 2 waves.
+// WQ_DMFMA_RB, WQ_DMFMA_TARGET_WGS and WQ_DMFMA_KS override the three
+// choices.  Row blocks beyond the counter region fall back to one split.
 MfmaDecodePlan decode_mfma_plan(int64_t, int64_t N, int64_t K, int) {
     MfmaDecodePlan p;
-    p.rb = 4;
-    const int64_t rowblocks = (N + 63) / 64;
+    static const int rb_env = [] {
+        const char *e = std::getenv("WQ_DMFMA_RB");
+        const int v = e ? std::atoi(e) : 2;
+        return (v == 1 || v == 4) ? v : 2;
+    }();
+    p.rb = rb_env;
+    const int64_t rowblocks = (N + 16 * p.rb - 1) / (16 * p.rb);
     const int G = (int)(K / kGroup);
     static const int target = [] {
         const char *e = std::getenv("WQ_DMFMA_TARGET_WGS");
-        return e ? std::atoi(e) : 1024;
+        return e ? std::atoi(e) : 512;
     }();
     int64_t splits = (target + rowblocks - 1) / rowblocks;
     splits = std::min<int64_t>(splits, std::max(1, G / 4));
@@ -315,11 +323,11 @@ MfmaDecodePlan decode_mfma_plan(int64_t, int64_t N, int64_t K, int) {
     const int gps = (G + p.splits - 1) / p.splits;
     static const int ks_max = [] {
         const char *e = std::getenv("WQ_DMFMA_KS");
-        return e ? std::atoi(e) : 2;
+        return e ? std::atoi(e) : 4;
     }();
     p.ks = std::max(1, std::min(std::min(ks_max, 4), gps / 2));
     p.ws_bytes = kWsScratchOffset +
-                 (p.splits > 1 ? (int64_t)p.splits * 16 * rowblocks * 64 * 4 : 0);
+                 (p.splits > 1 ? (int64_t)p.splits * 16 * rowblocks * 16 * p.rb * 4 : 0);
     return p;
 }
 
