@@ -1,9 +1,9 @@
 // wq_prefill.hip -- WNA16 prefill path (M > 16): LDS-tiled bf16 MFMA GEMM.
 //
 // At large batch the layer is compute-bound ("vLLM Quantization", Key points
-// and Pitfalls: weight-only gains fade as batch grows), so codes are
-// dequantized once per workgroup tile into LDS and the product runs on the
-// matrix cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation.
+// and Pitfalls: weight-only gains fade as batch grows), so the product runs
+// on the matrix cores (v_mfma_f32_32x32x16_bf16) with fp32 accumulation and
+// the codes are dequantized straight into their operand registers.
 //
 // Exactness.  The B operand holds 128 + c as bf16 (exact for c < 128; b = 8
 // uses byte conversion, offset 128), so the integer codes are never rounded.
@@ -16,11 +16,12 @@
 // multiplies that against s[n, k'/3] as extra "pseudo-groups" with scale 1.
 // No scale or code is ever rounded to bf16.
 //
-// Tiling.  Workgroup 256 (m) x 128 (n), 8 waves of 64 x 64 (two per SIMD),
-// each as 2 x 2 MFMA blocks of 32 x 32 run in two staggered halves.  K runs
-// in whole groups of 128 through LDS (A in two phase-shifted halves, B
-// unpacked to bf16 once per workgroup, double-buffered), register-staged.
-// Workgroups an XCD runs together share an A row block.
+// Tiling.  Workgroup 256 (m) x 128 (n), 8 waves of 128 x 32 (two per SIMD),
+// each as four 32 x 32 MFMA blocks run in two staggered phases.  K runs in
+// whole groups of 128: A through LDS (double-buffered, filled by direct
+// global -> LDS loads), B from each lane's contiguous half-slot of codes
+// straight into operand registers.  Workgroups an XCD runs together share
+// an A row block.
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
@@ -82,50 +83,41 @@ __global__ __launch_bounds__(256) void group_sum_split_kernel(const uint16_t *__
 // of 128 k, 256 bytes) per row; chunk c of row r sits at r*16 + (c ^ (r &
 // 15)).  LDS serves a 128-bit read 16 lanes at a time over 64 banks, and
 // the 16 consecutive rows such a lane group reads (one chunk each) land on
-// 16 distinct 16-byte bank groups; the loaders' row-wise writes (16 chunks
-// of one row per 16 lanes) are conflict free too, with no padding.
+// 16 distinct 16-byte bank groups; the direct loads write 64 consecutive
+// 16-byte slots (four rows) per instruction, conflict free too, with no
+// padding.
 __device__ __forceinline__ int swz16(int row, int chunk) {
     return row * 16 + (chunk ^ (row & 15));
 }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Workgroup: 512 threads = 8 waves (two per SIMD) over a 256 (m) x 128 (n)
-// output tile; wave (wm, wn) owns rows 64 wm .. +64 and columns 64 wn .. +64
-// as 2 x 2 blocks (i, j) of 32 x 32 (v_mfma_f32_32x32x16_bf16: lane l holds
-// A row l%32 and B column l%32 at k-chunk l/32; result element r of lane l
-// is row 8(r/4) + 4(l/32) + r%4, column l%32).  Per block two fp32 sets live
-// in VGPRs: P (the current group) and tot (the folded sum).
+// B is unpacked straight into MFMA operand registers and A moved global ->
+// LDS by direct loads (global_load_lds_dwordx4): the LDS carries A alone,
+// written once per group by the loads and read by the waves.  (Unpacking B
+// into LDS for all waves to read, as well, put the LDS traffic at about the
+// matrix cores' time.)
 //
-// Staggered halves.  Folding a group (tot += s * P, one FMA per output
-// element) must read P after the group's last MFMA on it has completed and
-// before the next group's first MFMA overwrites it.  So each group runs in
-// two phases of 16 MFMA slots: phase 0 runs the 8 k-steps of blocks (0, *),
-// phase 1 those of blocks (1, *) (two accumulation chains each, alternating
-// j).  Phase 0 folds the (1, *) blocks of the previous group and phase 1 the
-// (0, *) blocks of this one, whose MFMAs finished a phase earlier: two FMAs
-// per slot, no wait on the matrix pipe.  The 32 x 32 x 16 MFMA holds the
-// matrix pipe about four times as long as the issue port, so the fold and
-// the code unpack (about 1.5 VALU per slot) issue beside it.
+// Workgroup 256 (m) x 128 (n), 8 waves as 2 (m) x 4 (n), wave (wm, wn) owns
+// rows 128 wm .. +128 and columns 32 wn .. +32 as four 32 x 32 blocks i
+// (block rows) in one block column.  K order inside a group: k-step j
+// (0..7) of v_mfma_f32_32x32x16_bf16 takes, in its lane half h (lanes 32 h
+// .. 32 h + 31), the 8 k of chunk 8 h + j; both operands use that order, so
+// lane (column n, half h) needs codes 64 h .. 64 h + 63 of row n's group:
+// dwords 2 h B .. 2 h B + 2 B - 1 of the slot, one contiguous half-slot,
+// loaded with 8-byte loads and unpacked to 128 + c pairs (exact) once per
+// group.  The A operand of the same k-step is chunk 8 h + j of its LDS row.
 //
-// LDS.  A is held one group at a time as two halves: half h has, for every
-// wave, its 32 rows of block row h (128 rows x 128 k, 32 KB); half 0 is read
-// in phase 0 and refilled with the next group during phase 1, half 1 the
-// other way round.  B (128 rows x 128 k, 32 KB) is double-buffered by group
-// and the group's scales sit beside it.  The NP pseudo-groups run first,
-// unpipelined (A from the pre-pass matrix, B = scales, scale 1); the G real
-// groups are software-pipelined:
-//   group g, phase 0: fold (1, *) of g-1; unpack codes of g+1 into the other
-//     B buffer (one pair every other slot, both phases); fetch the codes of
-//     g+2 (a second register set) at slot 1; write A half 1 of g (fetched in
-//     phase 1 of g-1) at slots 4-7, a 16-byte piece each; fetch A half 0 of
-//     g+1 at slot 8; barrier after slot 13, then read phase 1's first k-step;
-//   group g, phase 1: fold (0, *) of g; finish the unpack by slot 11 (with
-//     the scales of g+1); write A half 0 of g+1 at slots 4-7, fetch A half 1
-//     of g+1 at slot 8; barrier after slot 13, then read the first k-step of
-//     group g+1's phase 0; the codes of g+2 move to the first set.
-// Operands run one k-step ahead; the next phase's first k-step is read
-// right after the barrier, under the phase's last four MFMAs.
+// Each group runs in two phases of 16 MFMA slots: phase 0 the 8 k-steps of
+// block rows 0 and 1, phase 1 those of rows 2 and 3 (two accumulation
+// chains each), with the B operand of k-step j unpacked in phase 0 and kept
+// for phase 1.  Phase 0 folds rows 2, 3 of the previous group and phase 1
+// rows 0, 1 of this one (tot += s * P, two FMAs per slot), so no fold waits
+// on the matrix pipe.  A is double-buffered in two LDS objects (256 rows x
+// 128 k each); at the start of group g the waves pass a barrier (group g's
+// A has landed; nobody still reads the other buffer), issue the direct
+// loads of group g+1's A into the other buffer and the codes and scale of
+// g+1 into registers, and run g.
 template <int B, class WL>
 __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict__ A,
                                                       const uint16_t *__restrict__ Ap, int M,
@@ -133,20 +125,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
                                                       uint16_t *__restrict__ Y, int mtiles,
                                                       int ntiles, int splits,
                                                       float *__restrict__ part, int64_t mnp) {
-    __shared__ u32x4 Ah[2][kPN * 16];   // [half][128 rows x 16 chunks]
-    __shared__ u32x4 Bsm[2][kPN * 16];  // [group buffer][128 rows x 16 chunks]
-    __shared__ float Ss[2][kPN];
+    __shared__ u32x4 As0[kPM * 16];
+    __shared__ u32x4 As1[kPM * 16];
 
     const int G = K / kGroup;
     const int NP = Kp / kPseudoK;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int h = lane >> 5;
+    const int c32 = lane & 31;
 
-    // Block b runs on XCD b % 8: give each XCD a contiguous run of logical
+    // Block b runs on XCD b % 8: each XCD gets a contiguous run of logical
     // tiles, n fastest, so the tiles an XCD runs together share A rows.
-    // With K split `splits` ways, logical = split * tiles + tile.
     const int tiles = mtiles * ntiles;
     const int total = tiles * splits;
     int logical = blockIdx.x;
@@ -155,7 +147,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     const int tile = logical - sp * tiles;
     const int bm = tile / ntiles;
     const int bn = tile - bm * ntiles;
-    // This workgroup's groups; the pseudo-groups go with split 0.
     const int g_lo = (int)(((int64_t)G * sp) / splits);
     const int g_hi = (int)(((int64_t)G * (sp + 1)) / splits);
     const int64_t m0 = (int64_t)bm * kPM;
@@ -164,164 +155,167 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     const uint32_t mask = __builtin_amdgcn_readfirstlane(pair_mask<B < 8 ? B : 7>());
     const uint32_t magic = in_vgpr(kBf16Magic128x2);
 
-    // A loader: chunk ac of half rows hr = ar + 32 u (u < 4), which are tile
-    // rows 64 u + 32 h + ar.  Rows beyond M read row M-1 (results dropped).
-    const int ac = tid & 15;
-    const int ar = tid >> 4;
+    // Direct loads: wave w fills the 1 KB runs s = w + 8 u (u < 8); run s
+    // holds rows 4 s .. 4 s + 3, lane l at row 4 s + l / 16, physical chunk
+    // l % 16, which is logical chunk (l % 16) ^ (row % 16) (swz16; the row
+    // is 4 w + l / 16 modulo 16 for every u).  Rows beyond M read row M-1
+    // (their results are dropped).  Byte offsets from the block's column
+    // k0, per run, for A (row stride K) and the pre-pass matrix (Kp).
     const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)kPM - 1);
-    int arow_g[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) arow_g[h][u] = min(64 * u + 32 * h + ar, mlim);
+    const int dma_row0 = 4 * wave + (lane >> 4);
+    const int dma_chunk = (lane & 15) ^ (dma_row0 & 15);
     const uint16_t *A_blk = A + m0 * K;
     const uint16_t *Ap_blk = Ap + m0 * Kp;
-    int a_lds[4];
+    uint32_t doff[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a_lds[u] = swz16(ar + 32 * u, ac);
-
-    // B loader: row brow, quarter bq (wave-uniform) of each group.
-    const int brow = tid & (kPN - 1);
-    const int bq = __builtin_amdgcn_readfirstlane(tid >> 7);
-    const int64_t bn_read = min(n0 + brow, (int64_t)N - 1);
-    const uint8_t *bslot0 = wl.slot0(bn_read);
-    const uint8_t *bscale0 = wl.scale0(bn_read);
-    const int bstep = (int)wl.slot_step();
-    const int sstep = (int)wl.scale_step();
-
-    // MFMA operand rows (in an A half and in B) and k-chunk half of this lane.
-    const int arow = wm * 32 + (lane & 31);
-    const int bmrow = wn * 64 + (lane & 31);
-    const int khalf = lane >> 5;
-
-    u32x4 areg[4];
-    uint32_t creg[B], cnext[B];
-    f32x16_t tot[2][2], P[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                tot[i][j][r] = 0.0f;
-                P[i][j][r] = 0.0f;
-            }
-        }
-
-    // A half h of real group g (clamped to this split's last one) into areg
-    // / from areg into LDS.
-    auto load_a = [&](int g, int h) __attribute__((always_inline)) {
-        const uint16_t *src = A_blk + min(g, g_hi - 1) * kGroup + 8 * ac;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            areg[u] = *reinterpret_cast<const u32x4 *>(src + __mul24(arow_g[h][u], K));
-    };
-    // One of the four 16-byte pieces (spread over four slots, so the LDS
-    // write queue never takes a whole phase's worth at once).
-    auto store_a = [&](int h, int u) __attribute__((always_inline)) {
-        Ah[h][a_lds[u]] = areg[u];
-    };
-    // Quarter bq of real group g's codes (clamped to the last group): B
-    // dwords at per-wave offsets held in scalar registers.
-    int qoff[B];
-#pragma unroll
-    for (int e = 0; e < B; ++e) {
-        const int d = bq * B + e;
-        qoff[e] = __builtin_amdgcn_readfirstlane((d >> 2) * (WL::kTiled ? 1024 : 16) + (d & 3) * 4);
-    }
-    auto load_codes = [&](int g, uint32_t(&dst)[B]) __attribute__((always_inline)) {
-        const uint8_t *slot = bslot0 + (int64_t)min(g, g_hi - 1) * bstep;
-#pragma unroll
-        for (int e = 0; e < B; ++e) dst[e] = *reinterpret_cast<const uint32_t *>(slot + qoff[e]);
-    };
-    // Chunk C (pairs 4C .. 4C+3, 8 codes) of the B operand (128 + c as bf16)
-    // from creg into B buffer buf.
-    auto fill_chunk = [&](int buf, auto cconst) __attribute__((always_inline)) {
-        constexpr int C = decltype(cconst)::value;
-        const u32x4 v{quarter_pair<B, 4 * C>(creg, mask, magic),
-                      quarter_pair<B, 4 * C + 1>(creg, mask, magic),
-                      quarter_pair<B, 4 * C + 2>(creg, mask, magic),
-                      quarter_pair<B, 4 * C + 3>(creg, mask, magic)};
-        Bsm[buf][swz16(brow, 4 * bq + C)] = v;
-    };
-    // Group g's scales into Ss[buf] (the four quarter waves of a row store
-    // the same value: no branch).
-    auto store_scale = [&](int g, int buf) __attribute__((always_inline)) {
-        Ss[buf][brow] =
-            bf16_to_f32(*reinterpret_cast<const uint16_t *>(bscale0 + min(g, g_hi - 1) * sstep));
-    };
-    // Slice q (of 16) of folding block row i with column scales sq: the
-    // slot's two FMAs.
-    auto fold_slice = [&](int i, int q, const float(&sq)[2]) __attribute__((always_inline)) {
-        const int j = q >> 3, r = 2 * (q & 7);
-        tot[i][j][r] = fmaf(sq[j], P[i][j][r], tot[i][j][r]);
-        tot[i][j][r + 1] = fmaf(sq[j], P[i][j][r + 1], tot[i][j][r + 1]);
-    };
-
-    // Operands of one k-step (A half ah, B buffer gb): sets 0 and 1 hold
-    // k-steps of the running phase in turn, set 2 the next phase's k-step 0.
-    bf16x8_t af[3], bfr[3][2];
-    auto read_ops = [&](int ah, int gbuf, int kk, int e) __attribute__((always_inline)) {
-        af[e] = __builtin_bit_cast(bf16x8_t, Ah[ah][swz16(arow, 2 * kk + khalf)]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bfr[e][j] = __builtin_bit_cast(bf16x8_t, Bsm[gbuf][swz16(bmrow + 32 * j, 2 * kk + khalf)]);
-    };
-
-    // One phase: the 8 k-steps of blocks (I, 0), (I, 1) from A half I and B
-    // buffer gbuf, starting from k-step 0's operands in set 2; k-step kk+1 is
-    // read into set (kk+1) & 1 at the start of k-step kk.  After each MFMA,
-    // hook(slot) issues a slice of the other work and the pair is fenced, so
-    // the order written here is the issue order.  With NEXT, the workgroup
-    // barrier follows slot 13: by then every operand read of this phase has
-    // been issued (the last one, k-step 7's, at the start of k-step 6), so
-    // no wave past the barrier can overwrite a buffer another wave still
-    // has to read; and every LDS write the next phase needs is issued in the
-    // hooks before it.  Then the next phase's k-step 0 (A half na, B buffer
-    // ngb) is read into set 2, under the phase's last two MFMAs.
-    auto phase = [&](auto iconst, int gbuf, auto nconst, int na, int ngb, auto &&hook)
+    for (int u = 0; u < 8; ++u)
+        doff[u] = (uint32_t)((min(dma_row0 + 32 * u, mlim) * K + 8 * dma_chunk) * 2);
+    auto dma = [&](const uint16_t *base, int k0, const uint32_t(&off)[8], auto bconst)
         __attribute__((always_inline)) {
-        constexpr int I = decltype(iconst)::value;
-        constexpr bool NEXT = decltype(nconst)::value;
+        u32x4 *dst = decltype(bconst)::value == 0 ? As0 : As1;
+        const uint8_t *b8 = reinterpret_cast<const uint8_t *>(base + k0);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            if (kk + 1 < 8) read_ops(I, gbuf, kk + 1, (kk + 1) & 1);
-            const int e = kk == 0 ? 2 : (kk & 1);
+        for (int u = 0; u < 8; ++u)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(b8 + off[u]),
+                (__attribute__((address_space(3))) void *)&dst[64 * (wave + 8 * u)], 16, 0, 0);
+    };
+
+    // B: lane's column and half-slot.  Dword pair i of the half is slot
+    // dword d = 2 h B + 2 i (8-byte aligned, never across a 16-byte chunk).
+    const int64_t bcol = min(n0 + 32 * wn + c32, (int64_t)N - 1);
+    const uint8_t *bptr = wl.slot0(bcol);
+    const uint8_t *sptr = wl.scale0(bcol);
+    const int64_t bstep = wl.slot_step();
+    const int64_t sstep = wl.scale_step();
+    int boff[B];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                f32x16_t c = P[I][j];
-                if (kk == 0) {
+    for (int i = 0; i < B; ++i) {
+        const int d = 2 * h * B + 2 * i;
+        boff[i] = WL::kTiled ? (d >> 2) * 1024 + (d & 3) * 4 : 4 * d;
+    }
+    auto load_codes = [&](int g, uint32_t(&dst)[2 * B], uint32_t &sc) __attribute__((always_inline)) {
+        g = min(g, g_hi - 1);
+        const uint8_t *slot = bptr + g * bstep;
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(slot + boff[i]);
+            dst[2 * i] = v.x;
+            dst[2 * i + 1] = v.y;
+        }
+        sc = *reinterpret_cast<const uint16_t *>(sptr + g * sstep);
+    };
+    // A operand of k-step j: LDS row 128 wm + 64 PH + 32 t + c32 (the last
+    // three terms compile-time), chunk (8 h + j) ^ (c32 % 16).
+    int aoff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) aoff[j] = (128 * wm + c32) * 16 + ((8 * h + j) ^ (c32 & 15));
+
+    f32x16_t tot[4], P[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            tot[i][r] = 0.0f;
+            P[i][r] = 0.0f;
+        }
+    uint32_t creg[2 * B], cnext[2 * B];
+    uint32_t sreg = 0, snext = 0;
+    u32x4 bop[8];
+    bf16x8_t af[2][2];  // [set][row of the phase]
+
+    // B operand of k-step J: pairs 4 (J % 4) .. +3 of quarter J / 4 of the half.
+    auto unpack_pair = [&](auto jconst, auto iconst) __attribute__((always_inline)) {
+        constexpr int J = decltype(jconst)::value, I = decltype(iconst)::value;
+        bop[J][I] = quarter_pair<B, 4 * (J & 3) + I>(creg + (J >> 2) * B, mask, magic);
+    };
+    auto read_a = [&](auto bconst, int row0, int j, int set) __attribute__((always_inline)) {
+        const u32x4 *src = decltype(bconst)::value == 0 ? As0 : As1;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            af[set][t] = __builtin_bit_cast(bf16x8_t, src[aoff[j] + (row0 + 32 * t) * 16]);
+    };
+    auto fold_slice = [&](int i0, int q, float s) __attribute__((always_inline)) {
+        const int i = i0 + (q >> 3), r = 2 * (q & 7);
+        tot[i][r] = fmaf(s, P[i][r], tot[i][r]);
+        tot[i][r + 1] = fmaf(s, P[i][r + 1], tot[i][r + 1]);
+    };
+    // One phase: block rows 2 PH, 2 PH + 1, k-steps 0..7, operands one
+    // k-step ahead (k-step 0's already in set 0).  After each MFMA hook(slot)
+    // issues a slice of other work; the pair is fenced so the order written
+    // is the issue order.  The last k-step reads the next phase's k-step 0
+    // (phase 0 only: phase 1's successor follows a barrier).
+    auto phase = [&](auto phconst, auto bconst, auto &&hook) __attribute__((always_inline)) {
+        constexpr int PH = decltype(phconst)::value;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int set = j & 1;
+            if (j + 1 < 8) read_a(bconst, 64 * PH, j + 1, set ^ 1);
+            else if (PH == 0) read_a(bconst, 64, 0, set ^ 1);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f32x16_t c = P[2 * PH + t];
+                if (j == 0) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) c[r] = 0.0f;
                 }
-                P[I][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[e], bfr[e][j], c, 0, 0, 0);
-                const int slot = 2 * kk + j;
-                hook(slot);
-                if (NEXT && slot == 13) {
-                    lds_barrier();
-                    read_ops(na, ngb, 0, 2);
-                }
+                P[2 * PH + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    af[set][t], __builtin_bit_cast(bf16x8_t, bop[j]), c, 0, 0, 0);
+                hook(2 * j + t);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
+    // Phase 0's hook while unpacking: slots 2j, 2j+1 unpack pairs 0,1 and
+    // 2,3 of k-step j+1.
+    auto unpack_slot = [&](int slot) __attribute__((always_inline)) {
+        const int j = (slot >> 1) + 1;
+        if (j >= 8) return;
+        if ((slot & 1) == 0) {
+            switch (j) {
+                case 1: unpack_pair(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}); unpack_pair(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}); break;
+                case 2: unpack_pair(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{}); unpack_pair(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}); break;
+                case 3: unpack_pair(std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{}); unpack_pair(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{}); break;
+                case 4: unpack_pair(std::integral_constant<int, 4>{}, std::integral_constant<int, 0>{}); unpack_pair(std::integral_constant<int, 4>{}, std::integral_constant<int, 1>{}); break;
+                case 5: unpack_pair(std::integral_constant<int, 5>{}, std::integral_constant<int, 0>{}); unpack_pair(std::integral_constant<int, 5>{}, std::integral_constant<int, 1>{}); break;
+                case 6: unpack_pair(std::integral_constant<int, 6>{}, std::integral_constant<int, 0>{}); unpack_pair(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{}); break;
+                default: unpack_pair(std::integral_constant<int, 7>{}, std::integral_constant<int, 0>{}); unpack_pair(std::integral_constant<int, 7>{}, std::integral_constant<int, 1>{}); break;
+            }
+        } else {
+            switch (j) {
+                case 1: unpack_pair(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}); unpack_pair(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{}); break;
+                case 2: unpack_pair(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{}); unpack_pair(std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{}); break;
+                case 3: unpack_pair(std::integral_constant<int, 3>{}, std::integral_constant<int, 2>{}); unpack_pair(std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{}); break;
+                case 4: unpack_pair(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{}); unpack_pair(std::integral_constant<int, 4>{}, std::integral_constant<int, 3>{}); break;
+                case 5: unpack_pair(std::integral_constant<int, 5>{}, std::integral_constant<int, 2>{}); unpack_pair(std::integral_constant<int, 5>{}, std::integral_constant<int, 3>{}); break;
+                case 6: unpack_pair(std::integral_constant<int, 6>{}, std::integral_constant<int, 2>{}); unpack_pair(std::integral_constant<int, 6>{}, std::integral_constant<int, 3>{}); break;
+                default: unpack_pair(std::integral_constant<int, 7>{}, std::integral_constant<int, 2>{}); unpack_pair(std::integral_constant<int, 7>{}, std::integral_constant<int, 3>{}); break;
+            }
+        }
+    };
+    auto unpack_k0 = [&]() __attribute__((always_inline)) {
+        unpack_pair(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        unpack_pair(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+        unpack_pair(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
+        unpack_pair(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+    };
 
-    float sq_prev[2] = {0.0f, 0.0f};
+    float sq_prev = 0.0f;
 
     // ---- pseudo-groups (scale 1), not pipelined: A' from the pre-pass
-    // matrix, B' = s[n, k'/3] (zero beyond 3G) ----
-    {
-        const float one[2] = {1.0f, 1.0f};
-        for (int ps = 0; ps < (sp == 0 ? NP : 0); ++ps) {
+    // matrix into As0; B' = s[n, k'/3] (zero beyond 3G) built in As1 (free
+    // until the real groups) by thread (row tid % 128, quarter tid / 128),
+    // in the same swizzled row layout, and read back as the B operand. ----
+    if (sp == 0 && NP > 0) {
+        uint32_t poff[8];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint16_t *src = Ap_blk + ps * kPseudoK + 8 * ac;
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    areg[u] = *reinterpret_cast<const u32x4 *>(src + __mul24(arow_g[h][u], Kp));
-#pragma unroll
-                for (int u = 0; u < 4; ++u) store_a(h, u);
-            }
+        for (int u = 0; u < 8; ++u)
+            poff[u] = (uint32_t)((min(dma_row0 + 32 * u, mlim) * Kp + 8 * dma_chunk) * 2);
+        const int brow = tid & (kPN - 1);
+        const int bq = tid >> 7;
+        const uint8_t *sb0 = wl.scale0(min(n0 + brow, (int64_t)N - 1));
+        for (int ps = 0; ps < NP; ++ps) {
+            dma(Ap_blk, ps * kPseudoK, poff, std::integral_constant<int, 0>{});
             const int k0 = ps * kPseudoK + 32 * bq;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -329,115 +323,79 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int ka = k0 + 8 * u + 2 * e, kb = ka + 1;
-                    const uint32_t sa = *reinterpret_cast<const uint16_t *>(
-                        bscale0 + min(ka / 3, G - 1) * sstep);
-                    const uint32_t sb = *reinterpret_cast<const uint16_t *>(
-                        bscale0 + min(kb / 3, G - 1) * sstep);
+                    const uint32_t sa = *reinterpret_cast<const uint16_t *>(sb0 + min(ka / 3, G - 1) * sstep);
+                    const uint32_t sb = *reinterpret_cast<const uint16_t *>(sb0 + min(kb / 3, G - 1) * sstep);
                     pr[e] = (ka < 3 * G ? sa : 0u) | ((kb < 3 * G ? sb : 0u) << 16);
                 }
-                Bsm[0][swz16(brow, 4 * bq + u)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+                As1[swz16(brow, 4 * bq + u)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
             }
-            lds_barrier();
-            read_ops(0, 0, 0, 2);
-            phase(std::integral_constant<int, 0>{}, 0, std::integral_constant<bool, false>{}, 0,
-                  0, [&](int slot) { fold_slice(1, slot, sq_prev); });
-            sq_prev[0] = one[0];
-            sq_prev[1] = one[1];
-            read_ops(1, 0, 0, 2);
-            phase(std::integral_constant<int, 1>{}, 0, std::integral_constant<bool, false>{}, 0,
-                  0, [&](int slot) { fold_slice(0, slot, one); });
-            lds_barrier();
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads have landed
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bop[j] = As1[swz16(32 * wn + c32, 8 * h + j)];
+            read_a(std::integral_constant<int, 0>{}, 0, 0, 0);
+            phase(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+                  [&](int slot) { fold_slice(2, slot, sq_prev); });
+            sq_prev = 1.0f;
+            phase(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
+                  [&](int slot) { fold_slice(0, slot, 1.0f); });
+            __syncthreads();  // every wave is done with As0 and As1 before they are refilled
         }
     }
 
-    // ---- real groups, software-pipelined ----
-    {
-        // Prologue: group g_lo's B, scales and both A halves in LDS; the
-        // codes of g_lo + 1 in registers.
-        load_codes(g_lo, creg);
-        fill_chunk(0, std::integral_constant<int, 0>{});
-        fill_chunk(0, std::integral_constant<int, 1>{});
-        fill_chunk(0, std::integral_constant<int, 2>{});
-        fill_chunk(0, std::integral_constant<int, 3>{});
-        store_scale(g_lo, 0);
-        load_a(g_lo, 0);
+    // ---- real groups ----
+    // Group g's A in buffer (g - g_lo) & 1.  Prologue: group g_lo's A, codes
+    // and scale.
+    dma(A_blk, g_lo * kGroup, doff, std::integral_constant<int, 0>{});
+    load_codes(g_lo, creg, sreg);
+    auto group = [&](int g, auto bconst) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bconst)::value;
+        // Group g's A (and codes) have landed for this wave; after the
+        // barrier for every wave, and every wave is done with the other buffer.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        dma(A_blk, min(g + 1, g_hi - 1) * kGroup, doff, std::integral_constant<int, BUF ^ 1>{});
+        load_codes(g + 1, cnext, snext);
+        unpack_k0();
+        read_a(bconst, 0, 0, 0);
+        const float sg = bf16_to_f32((uint16_t)sreg);
+        phase(std::integral_constant<int, 0>{}, bconst, [&](int slot) {
+            fold_slice(2, slot, sq_prev);
+            unpack_slot(slot);
+        });
+        phase(std::integral_constant<int, 1>{}, bconst, [&](int slot) { fold_slice(0, slot, sg); });
+        sq_prev = sg;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) store_a(0, u);
-        load_a(g_lo, 1);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) store_a(1, u);
-        load_codes(g_lo + 1, creg);
-        lds_barrier();
-        read_ops(0, 0, 0, 2);
-
-        for (int g = g_lo; g < g_hi; ++g) {
-            const int gb = (g - g_lo) & 1, nb = gb ^ 1;
-            const bool first = g == g_lo;
-            uint32_t pairs[16];
-            // Unpack pair p of group g+1 at global slot 2p (p < 14), pairs
-            // 14 and 15 at slot 27; a 16-byte chunk goes to LDS every four.
-            auto unpack = [&](int sigma) __attribute__((always_inline)) {
-                int p0 = -1, p1 = -1;
-                if (sigma < 28 && (sigma & 1) == 0) p0 = sigma >> 1;
-                if (sigma == 27) { p0 = 14; p1 = 15; }
-                if (p0 >= 0) pairs[p0] = quarter_pair_dyn<B>(p0, creg, mask, magic);
-                if (p1 >= 0) pairs[p1] = quarter_pair_dyn<B>(p1, creg, mask, magic);
-                const int last = p1 >= 0 ? p1 : p0;
-                if (last >= 0 && (last & 3) == 3)
-                    Bsm[nb][swz16(brow, 4 * bq + (last >> 2))] =
-                        u32x4{pairs[last - 3], pairs[last - 2], pairs[last - 1], pairs[last]};
-            };
-            // Phase 0: blocks (0, *) of g; fold (1, *) of g-1.
-            phase(std::integral_constant<int, 0>{}, gb, std::integral_constant<bool, true>{}, 1,
-                  gb, [&](int slot) {
-                      fold_slice(1, slot, sq_prev);
-                      unpack(slot);
-                      if (slot == 1) load_codes(g + 2, cnext);
-                      if (slot >= 4 && slot <= 7 && !first) store_a(1, slot - 4);
-                      if (slot == 8) load_a(g + 1, 0);
-                  });
-            // Phase 1: blocks (1, *) of g; fold (0, *) of g.
-            float sq[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) sq[j] = Ss[gb][wn * 64 + 32 * j + (lane & 31)];
-            phase(std::integral_constant<int, 1>{}, gb, std::integral_constant<bool, true>{}, 0,
-                  nb, [&](int slot) {
-                      fold_slice(0, slot, sq);
-                      unpack(16 + slot);
-                      if (slot == 11) store_scale(g + 1, nb);
-                      if (slot == 15) {
-#pragma unroll
-                          for (int e = 0; e < B; ++e) creg[e] = cnext[e];
-                      }
-                      if (slot >= 4 && slot <= 7) store_a(0, slot - 4);
-                      if (slot == 8) load_a(g + 1, 1);
-                  });
-            sq_prev[0] = sq[0];
-            sq_prev[1] = sq[1];
-        }
-        // The last group's (1, *) blocks.
-#pragma unroll
-        for (int q = 0; q < 16; ++q) fold_slice(1, q, sq_prev);
+        for (int e = 0; e < 2 * B; ++e) creg[e] = cnext[e];
+        sreg = snext;
+    };
+    int g = g_lo;
+    for (; g + 1 < g_hi; g += 2) {
+        group(g, std::integral_constant<int, 0>{});
+        group(g + 1, std::integral_constant<int, 1>{});
     }
+    if (g < g_hi) group(g, std::integral_constant<int, 0>{});
+    // The last group's rows 2, 3.
+#pragma unroll
+    for (int q = 0; q < 16; ++q) fold_slice(2, q, sq_prev);
+    // Drain the (clamped, unused) prefetch of the group after the last.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
-    // Output element r of block (i, j): row 8(r/4) + 4(lane/32) + r%4,
-    // column lane%32.
+    // Output element r of block i: row 8(r/4) + 4h + r%4, column lane%32.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int64_t n = n0 + 32 * wn + c32;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t n = n0 + wn * 64 + 32 * j + (lane & 31);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * khalf + (r & 3);
-                if (m < M && n < N) {
-                    if (splits == 1)
-                        Y[m * N + n] = f32_to_bf16_rne(tot[i][j][r]);
-                    else
-                        part[(int64_t)sp * mnp + m * N + n] = tot[i][j][r];
-                }
+        for (int r = 0; r < 16; ++r) {
+            const int64_t m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (m < M && n < N) {
+                if (splits == 1)
+                    Y[m * N + n] = f32_to_bf16_rne(tot[i][r]);
+                else
+                    part[(int64_t)sp * mnp + m * N + n] = tot[i][r];
             }
         }
+    }
 }
 
 // Y = bf16(sum over splits of part[s]) in split order (deterministic); four
