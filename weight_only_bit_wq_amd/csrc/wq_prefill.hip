@@ -114,10 +114,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // for phase 1.  Phase 0 folds rows 2, 3 of the previous group and phase 1
 // rows 0, 1 of this one (tot += s * P, two FMAs per slot), so no fold waits
 // on the matrix pipe.  A is double-buffered in two LDS objects (256 rows x
-// 128 k each); at the start of group g the waves pass a barrier (group g's
-// A has landed; nobody still reads the other buffer), issue the direct
-// loads of group g+1's A into the other buffer and the codes and scale of
-// g+1 into registers, and run g.
+// 128 k each), the codes in a second double buffer; at the start of group
+// g the waves pass a barrier (group g's A and codes have landed; nobody
+// still reads the other buffers), read their half-slots, issue the direct
+// loads of group g+1's A and codes into the other buffers and its scale
+// into a register, and run g.
 template <int B, class WL>
 __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict__ A,
                                                       const uint16_t *__restrict__ Ap, int M,
@@ -127,6 +128,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
                                                       float *__restrict__ part, int64_t mnp) {
     __shared__ u32x4 As0[kPM * 16];
     __shared__ u32x4 As1[kPM * 16];
+    // Codes of the tile's 128 columns, double-buffered: [buffer][64-row
+    // block][plane][row].  (One object: its reads come right after the
+    // barrier, before any direct load into it is issued.)
+    __shared__ u32x4 Cs[2][2 * B * 64];
 
     const int G = K / kGroup;
     const int NP = Kp / kPseudoK;
@@ -181,29 +186,55 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
                 (__attribute__((address_space(3))) void *)&dst[64 * (wave + 8 * u)], 16, 0, 0);
     };
 
-    // B: lane's column and half-slot.  Dword pair i of the half is slot
-    // dword d = 2 h B + 2 i (8-byte aligned, never across a 16-byte chunk).
-    const int64_t bcol = min(n0 + 32 * wn + c32, (int64_t)N - 1);
-    const uint8_t *bptr = wl.slot0(bcol);
-    const uint8_t *sptr = wl.scale0(bcol);
-    const int64_t bstep = wl.slot_step();
-    const int64_t sstep = wl.scale_step();
-    int boff[B];
+    // Codes: each group's 128 columns x b planes of 16 bytes (2 b runs of
+    // 64 lanes, one 64-row block and plane each) go global -> LDS with the
+    // same direct loads; wave w issues runs w and w + 8.  Lane l of run r
+    // (block t = r / b, plane p = r % b) reads chunk p of row n0 + 64 t + l
+    // (rows beyond N read row N-1).  The lane's column (32 wn + c32, block
+    // t = wn / 2, row rho) and half h then read dword pair i of the half,
+    // slot dword d = 2 h B + 2 i, from LDS at coff[i].
+    const uint8_t *crow[2];
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-        const int d = 2 * h * B + 2 * i;
-        boff[i] = WL::kTiled ? (d >> 2) * 1024 + (d & 3) * 4 : 4 * d;
-    }
-    auto load_codes = [&](int g, uint32_t(&dst)[2 * B], uint32_t &sc) __attribute__((always_inline)) {
-        g = min(g, g_hi - 1);
-        const uint8_t *slot = bptr + g * bstep;
+    for (int t = 0; t < 2; ++t)
+        crow[t] = reinterpret_cast<const uint8_t *>(wl.chunks(min(n0 + 64 * t + lane, (int64_t)N - 1), 0));
+    const int64_t bstep = wl.slot_step();
+    const int cstride = (int)wl.chunk_stride() * 16;
+    auto dma_codes = [&](int g, auto bconst) __attribute__((always_inline)) {
+        u32x4 *dst = Cs[decltype(bconst)::value];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int r = wave + 8 * k;
+            if (r < 2 * B) {
+                const int t = r >= B ? 1 : 0, p = r - t * B;
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(crow[t] + g * bstep + p * cstride),
+                    (__attribute__((address_space(3))) void *)&dst[64 * r], 16, 0, 0);
+            }
+        }
+    };
+    int coff[B];
+    {
+        const int c = 32 * wn + c32, t = c >> 6, rho = c & 63;
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(slot + boff[i]);
+            const int d = 2 * h * B + 2 * i;
+            coff[i] = ((t * B + (d >> 2)) * 64 + rho) * 16 + (d & 3) * 4;
+        }
+    }
+    auto read_codes = [&](auto bconst, uint32_t(&dst)[2 * B]) __attribute__((always_inline)) {
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(Cs[decltype(bconst)::value]);
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(src + coff[i]);
             dst[2 * i] = v.x;
             dst[2 * i + 1] = v.y;
         }
-        sc = *reinterpret_cast<const uint16_t *>(sptr + g * sstep);
+    };
+    const int64_t bcol = min(n0 + 32 * wn + c32, (int64_t)N - 1);
+    const uint8_t *sptr = wl.scale0(bcol);
+    const int64_t sstep = wl.scale_step();
+    auto load_scale = [&](int g, uint32_t &sc) __attribute__((always_inline)) {
+        sc = *reinterpret_cast<const uint16_t *>(sptr + min(g, g_hi - 1) * sstep);
     };
     // A operand of k-step j: LDS row 128 wm + 64 PH + 32 t + c32 (the last
     // three terms compile-time), chunk (8 h + j) ^ (c32 % 16).
@@ -219,7 +250,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
             tot[i][r] = 0.0f;
             P[i][r] = 0.0f;
         }
-    uint32_t creg[2 * B], cnext[2 * B];
+    uint32_t creg[2 * B];
     uint32_t sreg = 0, snext = 0;
     u32x4 bop[8];
     bf16x8_t af[2][2];  // [set][row of the phase]
@@ -347,15 +378,19 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     // Group g's A in buffer (g - g_lo) & 1.  Prologue: group g_lo's A, codes
     // and scale.
     dma(A_blk, g_lo * kGroup, doff, std::integral_constant<int, 0>{});
-    load_codes(g_lo, creg, sreg);
+    dma_codes(g_lo, std::integral_constant<int, 0>{});
+    load_scale(g_lo, snext);
     auto group = [&](int g, auto bconst) __attribute__((always_inline)) {
         constexpr int BUF = decltype(bconst)::value;
-        // Group g's A (and codes) have landed for this wave; after the
-        // barrier for every wave, and every wave is done with the other buffer.
+        // Group g's A and codes have landed for this wave; after the barrier
+        // for every wave, and every wave is done with the other buffers.
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
+        sreg = snext;
+        read_codes(bconst, creg);
         dma(A_blk, min(g + 1, g_hi - 1) * kGroup, doff, std::integral_constant<int, BUF ^ 1>{});
-        load_codes(g + 1, cnext, snext);
+        dma_codes(min(g + 1, g_hi - 1), std::integral_constant<int, BUF ^ 1>{});
+        load_scale(g + 1, snext);
         unpack_k0();
         read_a(bconst, 0, 0, 0);
         const float sg = bf16_to_f32((uint16_t)sreg);
@@ -365,9 +400,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
         });
         phase(std::integral_constant<int, 1>{}, bconst, [&](int slot) { fold_slice(0, slot, sg); });
         sq_prev = sg;
-#pragma unroll
-        for (int e = 0; e < 2 * B; ++e) creg[e] = cnext[e];
-        sreg = snext;
     };
     int g = g_lo;
     for (; g + 1 < g_hi; g += 2) {
