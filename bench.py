@@ -258,6 +258,23 @@ def pmc_run(torch, wq, synth, copies: int):
         "of %d bytes; decode source hash %s" % (l6.bytes, CAL_BYTES, decode_source_hash()))
 
 
+def pmc_prefill_run(torch, wq, synth):
+    """Kernels for rocprofv3 --pmc activity counters of the prefill kernel:
+    three calls of the M = 4096, K 5120 -> N 17408, b = 6 layer (the first
+    one warms the caches)."""
+    K, N = 5120, 17408
+    w = synth.prefill(M=4096, N=N, K=K, b=6)
+    packed = wq.wq_pack(w.codes, 6)
+    blob = wq.wq_repack(torch.from_numpy(packed.view(np.int32)).cuda(),
+                        torch.from_numpy(w.scales.view(np.int16)).cuda().view(torch.bfloat16), K, 6)
+    A = torch.from_numpy(w.A.view(np.int16)).cuda().view(torch.bfloat16)
+    Y = torch.empty((w.M, N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        wq.wq_gemm(A, blob, wq.WQ_LAYOUT_TILED, None, N, 6, Y=Y)
+    torch.cuda.synchronize()
+    log("pmc prefill run done: M=4096 K=5120 N=17408 b=6 x3")
+
+
 def bench_stack(torch, wq, reps: int):
     """The 64-layer mixed-bit stack + 8-bit head: M = 1 (HBM-bound, TB/s of
     algorithmic bytes) and M = 512 (TFLOP/s).  One forward = 129 wq_gemm calls,
@@ -295,6 +312,9 @@ def main():
     ap.add_argument("--pmc-run", action="store_true",
                     help="no timing: 16 launches of the b=6 decode kernel, then a 64 MiB fill and "
                          "a 64 MiB sum (known-size references for rocprofv3 --pmc byte counters)")
+    ap.add_argument("--pmc-prefill", action="store_true",
+                    help="no timing: three calls of the M=4096, K=5120, N=17408, b=6 prefill "
+                         "layer (for rocprofv3 --pmc activity counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -313,6 +333,9 @@ def main():
 
     if args.pmc_run:
         pmc_run(torch, wq, synth, args.copies)
+        return
+    if args.pmc_prefill:
+        pmc_prefill_run(torch, wq, synth)
         return
 
     log("setting up decode layers (b=5,6,7; %d copies each)" % args.copies)

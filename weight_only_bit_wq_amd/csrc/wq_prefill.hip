@@ -221,13 +221,27 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
             coff[i] = ((t * B + (d >> 2)) * 64 + rho) * 16 + (d & 3) * 4;
         }
     }
+    // Even b: the half-slot starts on a 16-byte chunk, read as b / 2 16-byte
+    // reads (lanes 16 bytes apart: conflict free; 8-byte reads at that stride
+    // put two lanes on each bank).  Odd b: 8-byte reads.
     auto read_codes = [&](auto bconst, uint32_t(&dst)[2 * B]) __attribute__((always_inline)) {
         const uint8_t *src = reinterpret_cast<const uint8_t *>(Cs[decltype(bconst)::value]);
+        if constexpr ((B & 1) == 0) {
 #pragma unroll
-        for (int i = 0; i < B; ++i) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(src + coff[i]);
-            dst[2 * i] = v.x;
-            dst[2 * i + 1] = v.y;
+            for (int i = 0; i < B; i += 2) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(src + coff[i]);
+                dst[2 * i] = v.x;
+                dst[2 * i + 1] = v.y;
+                dst[2 * i + 2] = v.z;
+                dst[2 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(src + coff[i]);
+                dst[2 * i] = v.x;
+                dst[2 * i + 1] = v.y;
+            }
         }
     };
     const int64_t bcol = min(n0 + 32 * wn + c32, (int64_t)N - 1);
