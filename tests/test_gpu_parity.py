@@ -339,28 +339,29 @@ def test_split_k_handoff_repeated(b, M, K, N):
 
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
 @pytest.mark.parametrize("waves", [4, 8, 16])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 8, 13, 16])
-def test_decode_split_k_forced(M, waves, monkeypatch):
-    # The vector-ALU decode kernel's split-K hand-off (one ticket per row
+def test_decode_split_k_forced(M, waves, layout, monkeypatch):
+    # The lane-per-row decode kernel's split-K hand-off (one ticket per row
     # block and storing wave, the other waves leaving after the LDS sum) at
     # every row tile and wave count it supports, on a small ragged layer
     # with K forced into 4 splits of 3 groups (the default plan would not
     # split it): full outputs against the oracle, a bitwise repeat, and the
-    # counter region left zero.
-    mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8 if M <= 8 else 16
-    if (waves == 16 and mt > 4) or (waves == 8 and mt > 8):
+    # counter region left zero.  Row tiles above 1 take the 4x4x4 matrix-core
+    # form.
+    mt = 1 if M <= 1 else 4 if M <= 4 else 8 if M <= 8 else 16
+    if waves == 16 and mt > 4:
         pytest.skip("wave count not offered for this row tile")
-    monkeypatch.setenv("WQ_DECODE_MFMA_MIN_M", "17")  # keep M > 4 on the vector-ALU kernel
     monkeypatch.setenv("WQ_DECODE_WAVES", str(waves))
     monkeypatch.setenv("WQ_DECODE_SPLITS", "4")
     b, N, K = 6, 200, 1536
     w = _workload(M, N, K, b, seed=1600 + 17 * M + waves)
-    L = Layer(w, wq.WQ_LAYOUT_TILED)
+    L = Layer(w, layout)
     ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
     A = dev_bf16(w.A)
-    Y0 = wq.wq_gemm(A, L.W_d, L.layout, None, N, b, ws=ws)
-    Y1 = wq.wq_gemm(A, L.W_d, L.layout, None, N, b, ws=ws)
+    Y0 = wq.wq_gemm(A, L.W_d, L.layout, L.S_d, N, b, ws=ws)
+    Y1 = wq.wq_gemm(A, L.W_d, L.layout, L.S_d, N, b, ws=ws)
     torch.cuda.synchronize()
     y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
     assert_wna16(host_bf16_bits(Y0), y_ref, mag, "forced split-K M=%d waves=%d" % (M, waves))

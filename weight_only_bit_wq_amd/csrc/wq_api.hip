@@ -86,19 +86,8 @@ void parallel_rows(int64_t N, int64_t work_per_row, F f) {
     for (auto &t : th) t.join();
 }
 
-// Smallest batch that takes the matrix-core decode kernel (the vector-ALU
-// kernel below it: at M <= 4 it measured as fast or faster on the 5120 x
-// 17408 and 17408 x 5120 layers); WQ_DECODE_MFMA_MIN_M overrides it (17
-// turns the matrix-core path off).
-int decode_mfma_min_m() {
-    const char *e = std::getenv("WQ_DECODE_MFMA_MIN_M");  // read per call, like the plans' overrides
-    return e ? std::atoi(e) : 5;
-}
-
 int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int b) {
     if (M == 0) return 0;
-    if (M <= wq::kDecodeMaxM && M >= decode_mfma_min_m())
-        return wq::decode_mfma_plan(M, N, K, b).ws_bytes;
     if (M <= wq::kDecodeMaxM) return wq::decode_plan(M, N, K, b).ws_bytes;
     return wq::prefill_ws_bytes(M, N, K, b);
 }
@@ -256,11 +245,7 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
     if (int s = check_device()) return s;
     const bool tiled = layout == WQ_LAYOUT_TILED;
     hipError_t e;
-    if (M <= wq::kDecodeMaxM && M >= decode_mfma_min_m()) {
-        const wq::MfmaDecodePlan p = wq::decode_mfma_plan(M, N, K, b);
-        e = wq::launch_decode_mfma(A_d, M, N, K, W_d, tiled, scales_d, b, Y_d, ws_d, p,
-                                   (hipStream_t)stream);
-    } else if (M <= wq::kDecodeMaxM) {
+    if (M <= wq::kDecodeMaxM) {
         const wq::DecodePlan p = wq::decode_plan(M, N, K, b);
         e = wq::launch_decode(A_d, M, N, K, W_d, tiled, scales_d, b, Y_d, ws_d, p,
                               (hipStream_t)stream);

@@ -23,7 +23,6 @@ extern template hipError_t decode_b<8>(const uint16_t *, int64_t, int64_t, int64
 
 static int decode_mt(int64_t M) {
     if (M <= 1) return 1;
-    if (M <= 2) return 2;
     if (M <= 4) return 4;
     if (M <= 8) return 8;
     return 16;
@@ -35,22 +34,23 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b) {
     const int G = (int)(K / kGroupSize);
     p.mt = decode_mt(M);
     p.rowblocks = (int)((N + 63) / 64);
-    // Measured on MI355X at M = 1 (K 5120 -> N 17408 and K 17408 -> N 5120):
-    // with many 64-row blocks, 8 waves per workgroup and about one group per
-    // wave (K split in chunks of 8 groups); with fewer than 192 row blocks,
-    // 16 waves and K split so that ~240 workgroups are in flight.  Larger M
-    // tiles use fewer waves (LDS reduction table, register pressure).
+    // Measured on MI355X (K 5120 -> N 17408 and K 17408 -> N 5120): with
+    // many 64-row blocks, 8 waves per workgroup and one group per wave (K
+    // split in chunks of 8 groups); with fewer than 192 row blocks, K split
+    // so that ~240 workgroups are in flight, 16 waves for one row of A and 8
+    // for the matrix-core row tiles (a sweep of 4/8/16 waves and 2..16 splits
+    // at M = 4, 8, 16 found these plans best or within noise of it).
     int waves, splits;
     if (p.rowblocks >= 192) {
-        waves = p.mt <= 8 ? 8 : 4;
+        waves = 8;
         splits = (G + 7) / 8;
     } else {
-        waves = p.mt <= 4 ? 16 : (p.mt <= 8 ? 8 : 4);
+        waves = p.mt == 1 ? 16 : 8;
         splits = std::max(1, std::min(G / waves, (240 + p.rowblocks - 1) / p.rowblocks));
     }
     if (const char *e = std::getenv("WQ_DECODE_WAVES")) waves = std::atoi(e);
     if (const char *e = std::getenv("WQ_DECODE_SPLITS")) splits = std::max(1, std::atoi(e));
-    if (!(waves == 4 || (waves == 8 && p.mt <= 8) || (waves == 16 && p.mt <= 4)))
+    if (!(waves == 4 || waves == 8 || (waves == 16 && p.mt <= 4)))
         waves = 4;
     // One ticket per (row block, storing wave).
     if ((int64_t)p.rowblocks * std::min(waves, p.mt) > kWsMaxCounters) splits = 1;

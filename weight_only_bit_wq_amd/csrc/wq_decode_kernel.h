@@ -10,9 +10,12 @@
 //     b 16-byte chunks of a group (128 codes) are loaded into 4b VGPRs and
 //     unpacked in registers.  In the tiled layout the 64 lanes of a wave read
 //     one 1 KB plane per load instruction.
-//   - All lanes of a wave work on the same group g, so the 128 activations
-//     of that group are wave-uniform: they are read with scalar loads and
-//     fed to v_dot2_f32_bf16 as its SGPR operand.
+//   - All lanes of a wave work on the same group g.  With one row of A the
+//     128 activations of that group are wave-uniform: they are read with
+//     scalar loads and fed to v_dot2_f32_bf16 as its SGPR operand.  With 2..16
+//     rows (padded to a row tile MT of 4, 8 or 16) the products run on the
+//     matrix cores as 4x4x4 blocks that keep a lane on its row (see the
+//     matrix-core group terms below).
 //   - A workgroup (W waves) covers 64 rows and `gps` consecutive groups, the
 //     waves interleaving groups; `splits` workgroups share one 64-row block.
 //     Many small workgroups (rather than one per compute unit) let the
@@ -42,13 +45,6 @@
 namespace wq {
 
 
-// Activation pairs are read CP at a time per row (one wide scalar load each),
-// so at most 64 SGPRs of activations are live.
-template <int MT>
-struct ChunkPairs {
-    static constexpr int value = MT <= 4 ? 16 : 64 / MT;
-};
-
 template <int N_>
 struct UVec;
 template <>
@@ -58,7 +54,8 @@ struct UVec<8> { typedef unsigned type __attribute__((ext_vector_type(8))); };
 template <>
 struct UVec<16> { typedef unsigned type __attribute__((ext_vector_type(16))); };
 
-// Pairs P0 + I .. P0 + CP - 1 of the group, activations already in av[].
+// Pairs P0 + I .. P0 + CP - 1 of the group, activations already in av[]
+// (CP pairs of one row come in with one wide scalar load).
 template <int B, int MT, int CP, int P0, int I>
 struct DotChunk {
     typedef typename UVec<CP>::type vec;
@@ -77,26 +74,6 @@ struct DotChunk<B, MT, CP, P0, CP> {
                                                float *) {}
 };
 
-template <int B, int MT, int P0>
-struct DotPairs {
-    static constexpr int CP = ChunkPairs<MT>::value;
-    typedef typename UVec<CP>::type vec;
-    __device__ __forceinline__ static void run(const uint32_t *w, const uint32_t *a,
-                                               const int *row_off, uint32_t mask,
-                                               uint32_t magic, float *d) {
-        vec av[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) av[m] = *reinterpret_cast<const vec *>(a + row_off[m] + P0);
-        DotChunk<B, MT, CP, P0, 0>::run(w, av, mask, magic, d);
-        DotPairs<B, MT, P0 + CP>::run(w, a, row_off, mask, magic, d);
-    }
-};
-template <int B, int MT>
-struct DotPairs<B, MT, 64> {
-    __device__ __forceinline__ static void run(const uint32_t *, const uint32_t *, const int *,
-                                               uint32_t, uint32_t, float *) {}
-};
-
 // b = 8: codes are whole bytes.  Each byte goes through v_cvt_f32_ubyteN and
 // a pair is packed to bf16 with v_cvt_pk_bf16_f32 (values 0..255 are exact in
 // bf16), then the same dot2 path as narrower codes with offset 128.
@@ -111,7 +88,7 @@ __device__ __forceinline__ uint32_t bytes_to_bf16x2(uint32_t x, int lo_byte) {
 template <int MT>
 __device__ __forceinline__ void dot_bytes(const uint32_t *w, const uint32_t *a,
                                           const int *row_off, float *d) {
-    constexpr int CP = ChunkPairs<MT>::value;
+    constexpr int CP = 16;
     typedef typename UVec<CP>::type vec;
 #pragma unroll
     for (int p0 = 0; p0 < 64; p0 += CP) {
@@ -163,9 +140,10 @@ __device__ __forceinline__ void group_terms(const uint32_t *w, const uint32_t *a
     float d[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) d[m] = 0.0f;
+    static_assert(MT == 1, "row tiles above 1 take the matrix-core form");
     if constexpr (B == 8) {
         dot_bytes<MT>(w, a, row_off, d);
-    } else if constexpr (MT == 1) {
+    } else {
         // One row: all 64 activation pairs of the group come in with four
         // wide scalar loads issued together.
         typedef typename UVec<16>::type vec16;
@@ -176,8 +154,6 @@ __device__ __forceinline__ void group_terms(const uint32_t *w, const uint32_t *a
         DotChunk<B, 1, 16, 16, 0>::run(w, &av[1], mask, magic, d);
         DotChunk<B, 1, 16, 32, 0>::run(w, &av[2], mask, magic, d);
         DotChunk<B, 1, 16, 48, 0>::run(w, &av[3], mask, magic, d);
-    } else {
-        DotPairs<B, MT, 0>::run(w, a, row_off, mask, magic, d);
     }
     // Sum of this group's activations per row m: lane l adds pair l, then
     // a DPP reduction across the wave (wave-uniform result).
@@ -188,9 +164,129 @@ __device__ __forceinline__ void group_terms(const uint32_t *w, const uint32_t *a
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core group terms, for row tiles MT = 4, 8, 16.
+//
+// v_mfma_f32_4x4x4_16b_bf16 runs 16 independent 4x4x4 products, one per
+// block of 4 lanes: B column j of block i is lane 4i + j (4 consecutive k),
+// and that lane receives the column's 4 outputs (one per A row).  With the
+// broadcast control CBSZ = 4 all 16 blocks take their A operand (4 rows x 4
+// k) from block ABID.  So lanes stay weight rows, exactly as in the
+// vector-ALU form: a lane's unpacked code pairs 2j, 2j+1 are its B operand
+// for k-step j (k = 4j .. 4j+3), and it gets its row's dot products with 4
+// rows of A at once.  One 16-byte register per lane holds the activations of
+// 4 rows for the whole group: lane 4i + r holds row r's k = 8i .. 8i+7, so
+// k-step 2i + h is dwords 2h, 2h+1 of that register with ABID = i.  Rows of
+// A come in sets of 4 (MT / 4 sets, one MFMA chain each).
+// ---------------------------------------------------------------------------
+typedef short bf16x4_bits __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int B, int Q, int J>
+struct MfmaSteps {
+    __device__ __forceinline__ static void run(const uint32_t *w, const u32x4 *av, uint32_t mask,
+                                               uint32_t magic, f32x4_t *d) {
+        u32x2_t wp;
+        if constexpr (B == 8) {
+            wp.x = bytes_to_bf16x2(w[J], 0);
+            wp.y = bytes_to_bf16x2(w[J], 2);
+        } else {
+            wp.x = code_pair_bf16_plus128<B, 2 * J>(w, mask, magic);
+            wp.y = code_pair_bf16_plus128<B, 2 * J + 1>(w, mask, magic);
+        }
+        const bf16x4_bits bw = __builtin_bit_cast(bf16x4_bits, wp);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            u32x2_t a;
+            a.x = av[q][2 * (J & 1)];
+            a.y = av[q][2 * (J & 1) + 1];
+            d[q] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4_bits, a), bw,
+                                                          d[q], 4, J >> 1, 0);
+        }
+        MfmaSteps<B, Q, J + 1>::run(w, av, mask, magic, d);
+    }
+};
+template <int B, int Q>
+struct MfmaSteps<B, Q, 32> {
+    __device__ __forceinline__ static void run(const uint32_t *, const u32x4 *, uint32_t, uint32_t,
+                                               f32x4_t *) {}
+};
+
+// Sum over the 16 lanes 4i + r (i = 0..15) of a value, for each r; every
+// lane receives the sum for its own r.  Two row rotations add the 4 lanes of
+// a 16-lane row, the permlane swaps then add rows 2t and 2t+1, and the wave's
+// halves.  Fixed order, so deterministic.
+__device__ __forceinline__ float lane_class4_sum(float v) {
+    v = dpp_add<0x124, 0xF>(v);  // row_ror:4
+    v = dpp_add<0x128, 0xF>(v);  // row_ror:8
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                      false, false);
+    v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                      false, false);
+    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+// Value of lane 4 * (lane / 4) + R (quad_perm [R, R, R, R]).
+template <int R>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), R * 0x55, 0xF, 0xF, false));
+}
+
+// Everything a lane reads for one (row, group) slot on the matrix-core form:
+// its b chunks, its scale and its 16-byte activation register per set.
+template <int B, int MT>
+struct SlotRegsMf {
+    uint32_t w[4 * B];
+    u32x4 av[MT / 4];
+    uint16_t s;
+};
+template <int B, int MT, class WL>
+__device__ __forceinline__ void load_slot_regs_mf(const WL &wl, int64_t nr, int g,
+                                                  const uint32_t *A2, const int *arow_off,
+                                                  int lane, SlotRegsMf<B, MT> &r) {
+    load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), r.w);
+    r.s = wl.scale(nr, g);
+#pragma unroll
+    for (int q = 0; q < MT / 4; ++q)
+        r.av[q] = *reinterpret_cast<const u32x4 *>(A2 + (int64_t)g * 64 + arow_off[q] +
+                                                   4 * (lane >> 2));
+}
+
+// x[m] = sum_k a[m,k] (128 + c_k) - (128 + 2^(b-1)) sum_k a[m,k] for the
+// lane's row and rows m = 0 .. MT-1 of A (offset 128 for b = 8), as in
+// group_terms; the caller applies the group scale.
+template <int B, int MT>
+__device__ __forceinline__ void group_terms_mf(const uint32_t *w, const u32x4 *av, uint32_t mask,
+                                               uint32_t magic, float *x) {
+    constexpr int Q = MT / 4;
+    constexpr float kOff = (B == 8) ? 128.0f : (float)(128 + (1 << (B - 1)));
+    f32x4_t d[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) d[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    MfmaSteps<B, Q, 0>::run(w, av, mask, magic, d);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        // Row 4q + (lane & 3)'s group sum: the lane's 8 activations, then
+        // over the 16 lanes holding the same row.
+        float ps = dot2_bf16(av[q][0], 0x3F803F80u, 0.0f);
+        ps = dot2_bf16(av[q][1], 0x3F803F80u, ps);
+        ps = dot2_bf16(av[q][2], 0x3F803F80u, ps);
+        ps = dot2_bf16(av[q][3], 0x3F803F80u, ps);
+        const float as = lane_class4_sum(ps);
+        x[4 * q + 0] = fmaf(-kOff, quad_bcast<0>(as), d[q][0]);
+        x[4 * q + 1] = fmaf(-kOff, quad_bcast<1>(as), d[q][1]);
+        x[4 * q + 2] = fmaf(-kOff, quad_bcast<2>(as), d[q][2]);
+        x[4 * q + 3] = fmaf(-kOff, quad_bcast<3>(as), d[q][3]);
+    }
+}
+
 // ONE: every wave has at most one group (gps <= W, the plan for large
-// layers at small M): no prefetch register set, so more waves fit per SIMD
-// (used for row tiles of 2 and more, where that measured faster).
+// layers): no prefetch register set, so more waves fit per SIMD.  Used for
+// the matrix-core row tiles; with one row of A the prefetching form measured
+// 3.5% faster even then, so it keeps that one.
 template <int B, int MT, int W, class WL, bool ONE>
 __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restrict__ A, int M,
                                                         int N, int K, WL wl,
@@ -198,7 +294,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
                                                         float *__restrict__ part,
                                                         unsigned *__restrict__ counters,
                                                         int splits, int gps, int tstride) {
-    static_assert(W * MT <= 64, "LDS reduction table");
+    static_assert(W * MT <= 128, "LDS reduction table");
+    static_assert(MT == 1 || MT % 4 == 0, "row tiles above 1 take the matrix-core form");
+    constexpr bool MF = MT >= 4;
     __shared__ float red[W][MT][64];
 
     const int G = K / kGroup;
@@ -225,10 +323,40 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     int row_off[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) row_off[m] = min(m, M - 1) * Kp;
+    // Matrix-core form: lane 4i + r reads row 4q + r of set q (rows past M
+    // repeat row M-1; their outputs are dropped).
+    int arow_off[MF ? MT / 4 : 1];
+#pragma unroll
+    for (int q = 0; q < (MF ? MT / 4 : 1); ++q) arow_off[q] = min(4 * q + (lane & 3), M - 1) * Kp;
 
     // Each wave walks groups g_begin + wave, + W, ...; the next group's chunks
     // are loaded before the current one is computed.
-    if constexpr (ONE) {
+    if constexpr (MF && ONE) {
+        const int g = g_begin + wave;
+        if (g < g_end) {
+            SlotRegsMf<B, MT> cur;
+            load_slot_regs_mf<B, MT>(wl, nr, g, A2, arow_off, lane, cur);
+            float x[MT];
+            group_terms_mf<B, MT>(cur.w, cur.av, mask, magic, x);
+            const float sc = bf16_to_f32(cur.s);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = sc * x[m];
+        }
+    } else if constexpr (MF) {
+        SlotRegsMf<B, MT> cur, nxt;
+        int g = g_begin + wave;
+        if (g < g_end) load_slot_regs_mf<B, MT>(wl, nr, g, A2, arow_off, lane, cur);
+        for (; g < g_end; g += W) {
+            const int gn = g + W;
+            if (gn < g_end) load_slot_regs_mf<B, MT>(wl, nr, gn, A2, arow_off, lane, nxt);
+            float x[MT];
+            group_terms_mf<B, MT>(cur.w, cur.av, mask, magic, x);
+            const float sc = bf16_to_f32(cur.s);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
+            cur = nxt;
+        }
+    } else if constexpr (ONE) {
         const int g = g_begin + wave;
         if (g < g_end) {
             SlotRegs<B, MT> cur;
@@ -341,8 +469,6 @@ hipError_t decode_bmw(const uint16_t *A, int64_t M, int64_t N, int64_t K, const 
         part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
     }
     const dim3 grid((unsigned)(p.rowblocks * p.splits));
-    // Measured (same box, alternating): the single-slot variant's extra
-    // occupancy gains 3.5% at M = 4 and loses 3.5% at M = 1.
     const bool one = MT > 1 && p.gps <= W;
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W_), G, B};
@@ -376,7 +502,7 @@ hipError_t decode_bm(const uint16_t *A, int64_t M, int64_t N, int64_t K, const v
         if (p.waves == 16)
             return decode_bmw<B, MT, 16>(A, M, N, K, W_, tiled, scales, Y, ws, p, stream);
     }
-    if constexpr (MT <= 8) {
+    if constexpr (MT <= 16) {
         if (p.waves == 8)
             return decode_bmw<B, MT, 8>(A, M, N, K, W_, tiled, scales, Y, ws, p, stream);
     }
@@ -391,7 +517,6 @@ hipError_t decode_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const vo
                            const DecodePlan &p, hipStream_t stream) {
     switch (p.mt) {
         case 1: return decode_bm<B, 1>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
-        case 2: return decode_bm<B, 2>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
         case 4: return decode_bm<B, 4>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
         case 8: return decode_bm<B, 8>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
         case 16: return decode_bm<B, 16>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);

@@ -28,7 +28,7 @@ struct DecodePlan {
     int mt;         // rows of A handled per kernel instance (template M tile)
     int splits;     // K splits across workgroups
     int gps;        // groups per split
-    int waves;      // waves per workgroup (4, 8 or 16; 16 only for mt <= 4, 8 for mt <= 8)
+    int waves;      // waves per workgroup (4, 8 or 16; 16 only for mt <= 4)
     int rowblocks;  // ceil(N / 64)
     int tstride;    // counters from one split-K ticket to the next (spreads them over cache lines)
     int64_t ws_bytes;
@@ -38,18 +38,6 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b);
 hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
                          bool tiled, const uint16_t *scales, int b, uint16_t *Y, void *ws,
                          const DecodePlan &plan, hipStream_t stream);
-
-// ---- decode path on the matrix cores, 2 <= M <= kDecodeMaxM (wq_decode_mfma.hip) ----
-struct MfmaDecodePlan {
-    int rb;      // 16-row blocks per workgroup (1, 2 or 4)
-    int splits;  // K splits across workgroups (deterministic ticket hand-off)
-    int ks;      // waves per workgroup, splitting each split's groups
-    int64_t ws_bytes;
-};
-MfmaDecodePlan decode_mfma_plan(int64_t M, int64_t N, int64_t K, int b);
-hipError_t launch_decode_mfma(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                              bool tiled, const uint16_t *scales, int b, uint16_t *Y, void *ws,
-                              const MfmaDecodePlan &plan, hipStream_t stream);
 
 // ---- prefill path, M > kDecodeMaxM (wq_prefill.hip) ----
 int64_t prefill_ws_bytes(int64_t M, int64_t N, int64_t K, int b);
