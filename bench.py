@@ -258,12 +258,12 @@ def pmc_run(torch, wq, synth, copies: int):
         "of %d bytes; decode source hash %s" % (l6.bytes, CAL_BYTES, decode_source_hash()))
 
 
-def pmc_prefill_run(torch, wq, synth):
-    """Kernels for rocprofv3 --pmc activity counters of the prefill kernel:
-    three calls of the M = 4096, K 5120 -> N 17408, b = 6 layer (the first
-    one warms the caches)."""
+def pmc_layer_run(torch, wq, synth, M: int):
+    """Kernels for rocprofv3 --pmc activity counters: three calls of the
+    K 5120 -> N 17408, b = 6 layer at batch M (the first one warms the
+    caches)."""
     K, N = 5120, 17408
-    w = synth.prefill(M=4096, N=N, K=K, b=6)
+    w = synth.prefill(M=M, N=N, K=K, b=6) if M > 16 else synth.decode(M=M, b=6, N=N, K=K)
     packed = wq.wq_pack(w.codes, 6)
     blob = wq.wq_repack(torch.from_numpy(packed.view(np.int32)).cuda(),
                         torch.from_numpy(w.scales.view(np.int16)).cuda().view(torch.bfloat16), K, 6)
@@ -272,7 +272,7 @@ def pmc_prefill_run(torch, wq, synth):
     for _ in range(3):
         wq.wq_gemm(A, blob, wq.WQ_LAYOUT_TILED, None, N, 6, Y=Y)
     torch.cuda.synchronize()
-    log("pmc prefill run done: M=4096 K=5120 N=17408 b=6 x3")
+    log("pmc layer run done: M=%d K=5120 N=17408 b=6 x3" % M)
 
 
 def bench_stack(torch, wq, reps: int):
@@ -312,9 +312,9 @@ def main():
     ap.add_argument("--pmc-run", action="store_true",
                     help="no timing: 16 launches of the b=6 decode kernel, then a 64 MiB fill and "
                          "a 64 MiB sum (known-size references for rocprofv3 --pmc byte counters)")
-    ap.add_argument("--pmc-prefill", action="store_true",
-                    help="no timing: three calls of the M=4096, K=5120, N=17408, b=6 prefill "
-                         "layer (for rocprofv3 --pmc activity counters)")
+    ap.add_argument("--pmc-layer", type=int, default=0, metavar="M",
+                    help="no timing: three calls of the K=5120, N=17408, b=6 layer at batch M "
+                         "(for rocprofv3 --pmc activity counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -334,8 +334,8 @@ def main():
     if args.pmc_run:
         pmc_run(torch, wq, synth, args.copies)
         return
-    if args.pmc_prefill:
-        pmc_prefill_run(torch, wq, synth)
+    if args.pmc_layer > 0:
+        pmc_layer_run(torch, wq, synth, args.pmc_layer)
         return
 
     log("setting up decode layers (b=5,6,7; %d copies each)" % args.copies)

@@ -228,11 +228,11 @@ __device__ __forceinline__ float lane_class4_sum(float v) {
     return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
-// Value of lane 4 * (lane / 4) + R (quad_perm [R, R, R, R]).
+// Value of lane 4 * (lane / 4) + R (quad_perm [R, R, R, R]; every lane has
+// a source, so no old value is needed).
 template <int R>
 __device__ __forceinline__ float quad_bcast(float v) {
-    return __int_as_float(
-        __builtin_amdgcn_update_dpp(0, __float_as_int(v), R * 0x55, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), R * 0x55, 0xF, 0xF, false));
 }
 
 // Everything a lane reads for one (row, group) slot on the matrix-core form:
