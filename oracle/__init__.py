@@ -13,6 +13,8 @@ Functions mirror the C entry points:
   quant_act_i8(A)               fp32 per-token int8 quantization -> (Aq, s_a)
   w4a8(A, packed, scales)       fp64 W4A8 result and magnitude
   w4a8_points(Aq, sa, ...)      the same at chosen positions
+  bf16_rne(x)                   fp64 values -> nearest bf16 bit patterns (ties to even)
+  embed(packed, scales, K, b, ids)  quantized embedding gather -> bf16 bits [T, K]
 """
 from __future__ import annotations
 
@@ -57,8 +59,11 @@ def _load():
     lib.oracle_quant_act_i8.argtypes = [P, i64, i64, P, P]
     lib.oracle_w4a8.argtypes = [P, i64, i64, i64, P, P, ci, P, P, P, P]
     lib.oracle_w4a8_points.argtypes = [P, P, i64, i64, i64, P, P, ci, P, P, i64, P, P]
+    lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_embed.argtypes = [P, P, i64, i64, ci, ci, P, i64, P]
     for f in ("oracle_pack", "oracle_unpack", "oracle_wna16", "oracle_wna16_points",
-              "oracle_quant_act_i8", "oracle_w4a8", "oracle_w4a8_points",
+              "oracle_quant_act_i8", "oracle_w4a8", "oracle_w4a8_points", "oracle_embed",
               "oracle_num_threads", "oracle_abi", "oracle_little_endian"):
         getattr(lib, f).restype = ci
     _lib = lib
@@ -134,6 +139,28 @@ def wna16_points(A, packed, scales, b, m_idx, n_idx, group: int = 128):
     if r != 0:
         raise RuntimeError("oracle_wna16_points failed (%d)" % r)
     return y, mag
+
+
+def bf16_rne(x) -> np.ndarray:
+    """Nearest bf16 bit patterns (ties to even) of fp64 values."""
+    x = np.asarray(x, dtype=np.float64)
+    f = _load().oracle_bf16_rne
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def embed(packed: np.ndarray, scales: np.ndarray, K: int, b: int, ids, group: int = 128):
+    """Quantized embedding gather: bf16 bits [T, K] of rows ids of the dequantized table."""
+    packed = _c(packed, np.uint32)
+    scales = _c(scales, np.uint16)
+    ids = _c(ids, np.int64).ravel()
+    V = packed.shape[0]
+    assert packed.shape[1] == words_per_row(K, b) and scales.shape == (V, K // group)
+    out = np.empty((ids.size, K), dtype=np.uint16)
+    r = _load().oracle_embed(_ptr(packed), _ptr(scales), V, K, b, group, _ptr(ids), ids.size,
+                             _ptr(out))
+    if r != 0:
+        raise RuntimeError("oracle_embed failed (%d)" % r)
+    return out
 
 
 def quant_act_i8(A: np.ndarray):

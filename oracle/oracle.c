@@ -33,6 +33,15 @@
  *    y = A . dequant(W)^T with W of shape [out_features N, in_features K],
  *    no bias.  Here dequant is done in fp64 and the sum is exact-as-fp64.
  *
+ *  - Quantized embedding gather.  Same model card, Findings: an embedding
+ *    table in this dense layout needs a gather that reads the dense rows
+ *    (the one it names assumes codes never straddle a word); "vLLM Can Run
+ *    INT5-7", section 3: the vocabulary tables (248,320 x 5,120) are worth
+ *    quantizing.  Reading taken: row t of the result is row ids[t] of the
+ *    table dequantized as above and rounded once to bf16 (nearest, ties to
+ *    even); an id outside the table gives a row of zeros (the rows of a
+ *    vocabulary shard that belong to other shards).
+ *
  *  - W4A8.  club-3090 discussion #733, "Under the hood": activations are
  *    quantized per token to int8 at run time, int4 weights are widened to
  *    int8 without loss, the product runs on int8 units.  Reading taken
@@ -145,6 +154,49 @@ static void dequant_row(const uint32_t *packed, const uint16_t *scales, int64_t 
         const int q = (int)read_code(row, k, b) - zero;
         w[k] = bf16_to_double(scales[n * G + k / group]) * (double)q;
     }
+}
+
+/* Nearest bf16 to x, ties to even, as a bit pattern.  Written out from the
+ * definition: an 8-significant-bit value whose exponent is that of x (the
+ * smallest quantum is 2^-133, bf16's subnormal step), the integer multiple of
+ * the quantum chosen by nearbyint() in the default round-to-nearest-even
+ * mode, infinity past the largest finite bf16 (2 - 2^-7) * 2^127. */
+uint16_t oracle_bf16_rne(double x) {
+    if (isnan(x)) return 0x7FC0;
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    const double a = fabs(x);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e); /* a in [2^(e-1), 2^e) */
+    int q = e - 8;
+    if (q < -133) q = -133;
+    const double r = ldexp(nearbyint(ldexp(a, -q)), q);
+    if (r > ldexp(2.0 - ldexp(1.0, -7), 127)) return (uint16_t)(sign | 0x7F80);
+    const float f = (float)r; /* r is a bf16 value, so exact in fp32 */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | ((u >> 16) & 0x7FFF));
+}
+
+/* Quantized embedding gather: out[t, k] = bf16 of row ids[t] of the
+ * dequantized table (zeros for ids outside [0, V)).  packed is the dense
+ * [V, ceil(K*b/32)] table, scales bf16 [V, K/group], out bf16 bits [T, K]. */
+int oracle_embed(const uint32_t *packed, const uint16_t *scales, int64_t V, int64_t K, int b,
+                 int group, const int64_t *ids, int64_t T, uint16_t *out) {
+    if (!oracle_little_endian() || b < 2 || b > 8 || group <= 0 || K % group) return -1;
+    double *w = (double *)malloc((size_t)K * sizeof(double));
+    if (!w) return -2;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t id = ids[t];
+        if (id < 0 || id >= V) {
+            for (int64_t k = 0; k < K; ++k) out[t * K + k] = 0;
+            continue;
+        }
+        dequant_row(packed, scales, id, K, b, group, w);
+        for (int64_t k = 0; k < K; ++k) out[t * K + k] = oracle_bf16_rne(w[k]);
+    }
+    free(w);
+    return 0;
 }
 
 /* y[m,n] = sum_k A[m,k] * w[n,k] and mag[m,n] = sum_k |A[m,k] * w[n,k]|,

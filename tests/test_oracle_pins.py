@@ -412,3 +412,84 @@ def test_w4a8_within_activation_rounding_of_wna16():
     assert np.all(np.abs(y8 - y16) <= bound)
     # and the bound is not vacuous: the difference is well below |y16| scale
     assert np.median(np.abs(y8 - y16)) < 0.1 * np.median(np.abs(y16))
+
+
+# --- quantized embedding gather ([card] Findings; [int57] section 3) -------------
+
+def test_bf16_rne_closed_forms():
+    # Ties go to the even neighbour (bf16 keeps 7 fraction bits, so 2^-8 is
+    # half a step at 1.0); the sign of zero is kept; the subnormal step is
+    # 2^-133; past the largest finite value (2 - 2^-7) 2^127 the result is
+    # infinity once the rounding carries over.
+    cases = [(1.0, 0x3F80), (1 + 2.0 ** -8, 0x3F80), (1 + 3 * 2.0 ** -8, 0x3F82),
+             (-(1 + 2.0 ** -8 + 2.0 ** -30), 0xBF81), (-0.0, 0x8000), (0.0, 0x0000),
+             (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000), (3 * 2.0 ** -134, 0x0002),
+             ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F), ((2 - 2.0 ** -9) * 2.0 ** 127, 0x7F80),
+             (-96.0, 0xC2C0)]
+    got = oracle.bf16_rne([c[0] for c in cases])
+    assert [int(v) for v in got] == [c[1] for c in cases]
+
+
+def test_bf16_rne_matches_torch_on_fp32_values():
+    # torch's float32 -> bfloat16 conversion rounds to nearest even; on values
+    # that are exact in float32 (so no double rounding) the oracle must agree,
+    # ties included (constructed with the low 16 bits exactly 0x8000).
+    rng = np.random.default_rng(41)
+    x = (rng.normal(size=3000) * np.exp2(rng.integers(-30, 30, size=3000))).astype(np.float32)
+    ties = (x.view(np.uint32) & 0xFFFF0000) | 0x8000
+    x = np.concatenate([x, ties.astype(np.uint32).view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.bf16_rne(x.astype(np.float64)), ref)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 6, 7, 8])
+def test_embed_hand_computed_rows(b):
+    # The three weight rows of the hand-computed example, gathered in a mixed
+    # order with ids outside the table; closed forms: row 0 is q = 1 at scale
+    # 1 (1.0 everywhere), row 1 is q = (k mod 2^b) - 2^(b-1) at scale -1/2,
+    # row 2 is q = -2^(b-1) at scale 2^-7, ids -1 and 3 give zeros.
+    _, codes, scales = _hand_inputs(b)
+    K = 128
+    ids = np.array([2, 0, -1, 1, 3, 1])
+    out = oracle.embed(oracle.pack(codes, b), scales, K, b, ids)
+    k = np.arange(K)
+    row1 = -0.5 * ((k % (1 << b)) - (1 << (b - 1)))
+    expect = np.stack([np.full(K, -2.0 ** (b - 1 - 7)), np.ones(K), np.zeros(K), row1,
+                       np.zeros(K), row1])
+    got = synth.bf16_bits_to_f32(out).astype(np.float64)
+    np.testing.assert_array_equal(got, expect)
+    # -0.5 * 0 is -0: the product's sign is kept (row 1 where the code is 2^(b-1)).
+    assert np.all(out[3][(k % (1 << b)) == (1 << (b - 1))] == 0x8000)
+    assert np.all(out[2] == 0) and np.all(out[4] == 0)
+
+
+def test_embed_b8_unit_scale_is_integer():
+    # b = 8 with scale 1: the gathered row is the integer c - 128.
+    rng = np.random.default_rng(42)
+    V, K = 50, 384
+    codes = rng.integers(0, 256, size=(V, K), dtype=np.uint8)
+    scales = np.full((V, K // 128), BF16_ONE, dtype=np.uint16)
+    ids = rng.integers(0, V, size=20)
+    out = oracle.embed(oracle.pack(codes, 8), scales, K, 8, ids)
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(out),
+                                  (codes[ids].astype(np.float32) - 128))
+
+
+@pytest.mark.parametrize("b", [3, 5, 6, 7])
+def test_embed_equals_layer_on_one_hot_rows(b):
+    # Embedding row id, column k, is the layer's output for the one-hot
+    # activation row e_k at output id (y = A . dequant(W)^T with A = I):
+    # the gather must give the nearest bf16 of the layer's exact fp64 value.
+    # (The layer's sum starts from +0, so a weight of -0 comes out +0 there;
+    # zeros are compared without their sign, which the hand-computed rows pin.)
+    rng = np.random.default_rng(43 + b)
+    V, K = 40, 256
+    codes = rng.integers(0, 1 << b, size=(V, K), dtype=np.uint8)
+    scales = synth.draw_scales_halfnormal_signed(rng, V, K // 128)
+    packed = oracle.pack(codes, b)
+    eye = np.where(np.eye(K, dtype=bool), BF16_ONE, 0).astype(np.uint16)
+    y, _ = oracle.wna16(eye, packed, scales, b)          # y[k, n] = w[n, k]
+    ids = rng.integers(0, V, size=12)
+    out = oracle.embed(packed, scales, K, b, ids)
+    unsigned_zero = lambda bits: np.where(bits == 0x8000, 0, bits)
+    np.testing.assert_array_equal(unsigned_zero(out), unsigned_zero(oracle.bf16_rne(y[:, ids].T)))
