@@ -137,6 +137,37 @@ def bench_prefill(torch, wq, synth, reps: int):
     return out
 
 
+def bench_embed(torch, wq, synth, reps: int):
+    """Quantized embedding gather: 4096 token ids from the 248,320 x 5,120
+    table at b = 6 and 8 (dense layout).  The table is filled on the device
+    from a seeded generator (any words are a valid dense table; the values do
+    not change the gather's timing); 8 output buffers rotate so the written
+    rows (42 MB each) do not stay in the 256 MB Infinity Cache.  Algorithmic
+    bytes: per token the row's codes K*b/8 and scales 2K/128 read, the id
+    read, 2K written."""
+    V, K, T, copies = synth.EMBED_VOCAB, synth.EMBED_HIDDEN, 4096, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    ids = torch.from_numpy(synth.embed_ids(T, V)).cuda()
+    out = {}
+    for b in (6, 8):
+        words = torch.randint(-(1 << 31), 1 << 31, (V, K * b // 32), dtype=torch.int32,
+                              device="cuda", generator=gen)
+        scales = (torch.randn((V, K // 128), device="cuda", generator=gen) * 0.01).to(torch.bfloat16)
+        Ys = [torch.empty((T, K), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+
+        def fn():
+            for Y in Ys:
+                wq.wq_embed(ids, words, scales, K, b, Y=Y)
+
+        t = graph_time(torch, fn, reps, 2) / copies
+        byts = T * (K * b // 8 + 2 * K // 128 + 8 + 2 * K)
+        out["b%d" % b] = {"T": T, "V": V, "K": K, "us": t * 1e6, "bytes": byts,
+                          "GB/s": byts / t / 1e9, "frac_of_hbm_peak": byts / t / 1e9 / HBM_PEAK_GBS}
+        del words, scales, Ys
+    return out
+
+
 def bench_decode_sweep(torch, wq, synth, reps: int, copies: int):
     """wq_gemm at M = 4 and 16 on the decode layer (K 5120 -> N 17408), b = 5,
     6, 7, in TB/s of algorithmic bytes; rotating weight copies as in the
@@ -419,6 +450,9 @@ def main():
         torch.cuda.empty_cache()
         log("w4a8 M=2048/8192")
         result["w4a8"] = bench_w4a8(torch, wq, synth, reps=10)
+        torch.cuda.empty_cache()
+        log("embedding gather T=4096 from 248320 x 5120, b=6/8")
+        result["embed"] = bench_embed(torch, wq, synth, reps=20)
         torch.cuda.empty_cache()
         log("stack: 64 mixed-bit layers + 8-bit head, M=1 and 512")
         result["stack"] = bench_stack(torch, wq, reps=3)

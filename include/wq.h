@@ -168,6 +168,21 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
 int wq_quant_act_i8(const uint16_t *A_d, int64_t M, int64_t K, int8_t *Aq_d, float *sa_d,
                     void *stream);
 
+/* Device.  Quantized embedding gather on the dense layout (model card
+ * "Qwen3.8-27B-INT6-Mixed-AutoRound", Findings: a 5/6/7-bit embed_tokens
+ * needs a gather that reads the dense rows, codes straddling words; "vLLM
+ * Can Run INT5-7", section 3: the vocabulary tables, 248,320 x 5,120, are
+ * worth storing in INT8).  For t in [0, T), with id = ids_d[t]:
+ *   Y_d[t, k] = bf16_rne(s[id, k/128] * (c[id, k] - 2^(b-1)))   if 0 <= id < V
+ *   Y_d[t, k] = 0                                                otherwise
+ * (ids outside the table give zero rows, as the rows of a vocabulary shard
+ * that belong to other shards).  W_d: dense packed uint32 [V, ceil(K*b/32)]
+ * (what wq_pack writes), scales_d bf16 [V, K/128], ids_d int64 [T], Y_d bf16
+ * [T, K], all device memory owned by the caller.  The product is exact in
+ * fp32 and rounded once, so the result is bit-exact.  T = 0 is a no-op. */
+int wq_embed(const void *W_d, const uint16_t *scales_d, int64_t V, int64_t K, int b, int group,
+             const int64_t *ids_d, int64_t T, uint16_t *Y_d, void *stream);
+
 /* Device.  W4A8 layer (same page): activations quantized as wq_quant_act_i8
  * does, int4 codes widened to int8 without loss (c - 8 in [-8, 7]), int8
  * products summed exactly in int32 per group of 128, then

@@ -16,7 +16,7 @@ from weight_only_bit_wq_amd import synth
 def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(wq.lib_path)
     names = wq.declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert wq.wq_abi_version() == 1
@@ -147,6 +147,26 @@ def test_repack_and_unpack_dev_validation():
     assert lib.wq_unpack_dev(A, 3, 256, 512, 6, 128, A, None) == wq.WQ_ERR_BAD_LAYOUT
     assert lib.wq_unpack_dev(A, 0, 256, 512, 0, 128, A, None) == wq.WQ_ERR_UNSUPPORTED_BITS
     assert lib.wq_quant_act_i8(A, 4, 100, A, A, None) == wq.WQ_ERR_INVALID_ARG
+
+
+def test_embed_validation():
+    # Every refusal happens before the device check, so none of these touches a GPU.
+    lib = wq._load()
+    c = ctypes.c_void_p
+    A = c(ALIGNED)
+    V, K = 1000, 512
+    assert lib.wq_embed(A, A, V, K, 9, 128, A, 4, A, None) == wq.WQ_ERR_UNSUPPORTED_BITS
+    assert lib.wq_embed(A, A, V, K, 1, 128, A, 4, A, None) == wq.WQ_ERR_UNSUPPORTED_BITS
+    assert lib.wq_embed(A, A, V, 500, 6, 128, A, 4, A, None) == wq.WQ_ERR_BAD_GROUP
+    assert lib.wq_embed(A, A, V, K, 6, 64, A, 4, A, None) == wq.WQ_ERR_BAD_GROUP
+    assert lib.wq_embed(A, A, 0, K, 6, 128, A, 4, A, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_embed(A, A, V, K, 6, 128, A, -1, A, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_embed(A, A, V, K, 6, 128, A, 1 << 31, A, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_embed(A, A, V, K, 6, 128, None, 4, A, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_embed(A, A, V, K, 6, 128, c(MISALIGNED), 4, A, None) == wq.WQ_ERR_MISALIGNED
+    assert lib.wq_embed(A, A, V, K, 6, 128, A, 4, c(MISALIGNED), None) == wq.WQ_ERR_MISALIGNED
+    # an empty batch is a no-op, even without buffers
+    assert lib.wq_embed(None, None, V, K, 6, 128, None, 0, None, None) == wq.WQ_OK
 
 
 def test_repacked_sizes():

@@ -25,6 +25,7 @@ __all__ = [
     "wq_abi_version", "wq_status_str", "wq_last_hip_error", "wq_device_supported",
     "wq_packed_words_per_row", "wq_pack", "wq_unpack", "wq_repacked_bytes", "wq_repack",
     "wq_unpack_dev", "wq_workspace_bytes", "wq_gemm", "wq_quant_act_i8", "wq_gemm_a8",
+    "wq_embed",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +101,7 @@ def _load():
             "wq_gemm": ([P, L, L, L, P, I, P, I, I, P, P, L, P], I),
             "wq_quant_act_i8": ([P, L, L, P, P, P], I),
             "wq_gemm_a8": ([P, L, L, L, P, I, P, I, I, P, I, P, L, P], I),
+            "wq_embed": ([P, P, L, L, I, I, P, L, P, P], I),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -285,6 +287,24 @@ def wq_quant_act_i8(A_d, Aq=None, sa=None, stream=None):
     _check("wq_quant_act_i8", _load().wq_quant_act_i8(_ptr(A_d), M, K, _ptr(Aq), _ptr(sa),
                                                       _stream(stream)))
     return Aq, sa
+
+
+def wq_embed(ids_d, W_d, scales_d, K: int, b: int, group: int = GROUP, Y=None, stream=None):
+    """Device: quantized embedding gather from the dense layout -> bf16 [T, K]
+    (rows of ids outside [0, V) are zero)."""
+    import torch
+    _require_cuda("ids_d", ids_d, torch.int64)
+    V = W_d.shape[0]
+    _require_cuda("W_d", W_d, (torch.int32, torch.uint32), (V, wq_packed_words_per_row(K, b)))
+    _require_cuda("scales_d", scales_d, (torch.bfloat16, torch.int16), (V, K // group))
+    T = ids_d.numel()
+    if Y is None:
+        Y = torch.empty((T, K), dtype=torch.bfloat16, device=W_d.device)
+    else:
+        _require_cuda("Y", Y, torch.bfloat16, (T, K))
+    _check("wq_embed", _load().wq_embed(_ptr(W_d), _ptr(scales_d), V, K, b, group, _ptr(ids_d),
+                                        T, _ptr(Y), _stream(stream)))
+    return Y
 
 
 def wq_gemm_a8(A_d, W_d, layout: int, scales_d, N: int, b: int = 4, group: int = GROUP,

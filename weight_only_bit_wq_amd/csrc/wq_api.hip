@@ -217,6 +217,21 @@ int wq_unpack_dev(const void *W_d, int layout, int64_t N, int64_t K, int b, int 
     return e == hipSuccess ? WQ_OK : hip_fail(e);
 }
 
+int wq_embed(const void *W_d, const uint16_t *scales_d, int64_t V, int64_t K, int b, int group,
+             const int64_t *ids_d, int64_t T, uint16_t *Y_d, void *stream) {
+    if (!dims_ok(0, V, K) || T < 0 || T >= (1ll << 31)) return WQ_ERR_INVALID_ARG;
+    if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
+    if (int s = check_group(K, group)) return s;
+    if (T * ((K / 8 + 127) / 128) >= (1ll << 32)) return WQ_ERR_INVALID_ARG;  // grid size
+    if (T == 0) return WQ_OK;
+    if (!W_d || !scales_d || !ids_d || !Y_d) return WQ_ERR_INVALID_ARG;
+    if (!aligned16(W_d) || !aligned16(scales_d) || !aligned16(ids_d) || !aligned16(Y_d))
+        return WQ_ERR_MISALIGNED;
+    if (int s = check_device()) return s;
+    hipError_t e = wq::launch_embed(W_d, scales_d, V, K, b, ids_d, T, Y_d, (hipStream_t)stream);
+    return e == hipSuccess ? WQ_OK : hip_fail(e);
+}
+
 int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int group) {
     if (!dims_ok(M, N, K) || !valid_bits(b) || check_group(K, group) != WQ_OK) return -1;
     if (op == WQ_OP_GEMM) return gemm_ws_bytes(M, N, K, b);

@@ -45,6 +45,10 @@ hipError_t launch_prefill(const uint16_t *A, int64_t M, int64_t N, int64_t K, co
                           bool tiled, const uint16_t *scales, int b, uint16_t *Y, void *ws,
                           hipStream_t stream);
 
+// ---- quantized embedding gather (wq_embed.hip) ----
+hipError_t launch_embed(const void *W, const uint16_t *scales, int64_t V, int64_t K, int b,
+                        const int64_t *ids, int64_t T, uint16_t *Y, hipStream_t stream);
+
 // ---- W4A8 (wq_a8.hip) ----
 hipError_t launch_quant_act(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq, float *sa,
                             hipStream_t stream);

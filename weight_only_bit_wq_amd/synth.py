@@ -183,3 +183,26 @@ def stack_weights(b: int, kind: str, seed: int = 4, N: int | None = None,
 def stack_input(M: int, seed: int = 4, K: int = STACK_HIDDEN) -> np.ndarray:
     """Stack input activations ~N(0, 1), bf16 bits [M, K]."""
     return draw_act(np.random.default_rng([seed, 99, M]), M, K)
+
+
+EMBED_VOCAB = 248320
+EMBED_HIDDEN = 5120
+
+
+def embed_table(V: int = EMBED_VOCAB, K: int = EMBED_HIDDEN, b: int = 8, seed: int = 5):
+    """Quantized embedding table in the dense layout ("vLLM Can Run INT5-7",
+    section 3: vocabulary 248,320 x hidden 5,120).  With K*b a multiple of 32
+    a dense row has no padding bits, so every 32-bit pattern is a row of
+    uniform b-bit codes: the words themselves are drawn (no packing step).
+    Scales |N(0, 0.01)| with a random sign.  Returns (words uint32 [V, K*b/32],
+    scales bf16 bits [V, K/128])."""
+    assert (K * b) % 32 == 0 and K % GROUP == 0
+    rng = np.random.default_rng([seed, b, V, K])
+    words = rng.integers(0, 1 << 32, size=(V, K * b // 32), dtype=np.uint32)
+    scales = draw_scales_halfnormal_signed(rng, V, K // GROUP)
+    return words, scales
+
+
+def embed_ids(T: int, V: int = EMBED_VOCAB, seed: int = 5) -> np.ndarray:
+    """Token ids uniform in [0, V), int64 [T]."""
+    return np.random.default_rng([seed, 7, T]).integers(0, V, size=T, dtype=np.int64)
