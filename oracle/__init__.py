@@ -11,7 +11,7 @@ Functions mirror the C entry points:
   wna16(A, packed, scales, b)   fp64 y = A . dequant(W)^T and sum |a*w|
   wna16_points(...)             the same at chosen (m, n) positions
   quant_act_i8(A)               fp32 per-token int8 quantization -> (Aq, s_a)
-  w4a8(A, packed, scales)       fp64 W4A8 result and magnitude
+  w4a8(A, packed, scales, b=4)  fp64 int8-activation result and magnitude (b = 4: W4A8)
   w4a8_points(Aq, sa, ...)      the same at chosen positions
   bf16_rne(x)                   fp64 values -> nearest bf16 bit patterns (ties to even)
   embed(packed, scales, K, b, ids)  quantized embedding gather -> bf16 bits [T, K]
@@ -57,8 +57,8 @@ def _load():
     lib.oracle_wna16.argtypes = [P, i64, i64, i64, P, P, ci, ci, P, P]
     lib.oracle_wna16_points.argtypes = [P, i64, i64, i64, P, P, ci, ci, P, P, i64, P, P]
     lib.oracle_quant_act_i8.argtypes = [P, i64, i64, P, P]
-    lib.oracle_w4a8.argtypes = [P, i64, i64, i64, P, P, ci, P, P, P, P]
-    lib.oracle_w4a8_points.argtypes = [P, P, i64, i64, i64, P, P, ci, P, P, i64, P, P]
+    lib.oracle_w4a8.argtypes = [P, i64, i64, i64, P, P, ci, ci, P, P, P, P]
+    lib.oracle_w4a8_points.argtypes = [P, P, i64, i64, i64, P, P, ci, ci, P, P, i64, P, P]
     lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
     lib.oracle_bf16_rne.restype = ctypes.c_uint16
     lib.oracle_embed.argtypes = [P, P, i64, i64, ci, ci, P, i64, P]
@@ -173,26 +173,27 @@ def quant_act_i8(A: np.ndarray):
     return Aq, sa
 
 
-def w4a8(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, group: int = 128):
-    """Return (y, mag, Aq, s_a) for the int4-weight / int8-activation layer."""
+def w4a8(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, group: int = 128, b: int = 4):
+    """Return (y, mag, Aq, s_a) for the int8-activation layer on b-bit codes
+    (b = 4: W4A8)."""
     A = _c(A, np.uint16)
     packed = _c(packed, np.uint32)
     scales = _c(scales, np.uint16)
     M, K = A.shape
     N = packed.shape[0]
-    assert packed.shape[1] == words_per_row(K, 4) and scales.shape == (N, K // group)
+    assert packed.shape[1] == words_per_row(K, b) and scales.shape == (N, K // group)
     Aq = np.empty((M, K), dtype=np.int8)
     sa = np.empty(M, dtype=np.float32)
     y = np.empty((M, N), dtype=np.float64)
     mag = np.empty((M, N), dtype=np.float64)
-    r = _load().oracle_w4a8(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), group,
+    r = _load().oracle_w4a8(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), b, group,
                             _ptr(Aq), _ptr(sa), _ptr(y), _ptr(mag))
     if r != 0:
         raise RuntimeError("oracle_w4a8 failed (%d)" % r)
     return y, mag, Aq, sa
 
 
-def w4a8_points(Aq, sa, packed, scales, m_idx, n_idx, group: int = 128):
+def w4a8_points(Aq, sa, packed, scales, m_idx, n_idx, group: int = 128, b: int = 4):
     Aq = _c(Aq, np.int8)
     sa = _c(sa, np.float32)
     packed = _c(packed, np.uint32)
@@ -205,7 +206,7 @@ def w4a8_points(Aq, sa, packed, scales, m_idx, n_idx, group: int = 128):
     y = np.empty(P, dtype=np.float64)
     mag = np.empty(P, dtype=np.float64)
     r = _load().oracle_w4a8_points(_ptr(Aq), _ptr(sa), M, N, K, _ptr(packed), _ptr(scales),
-                                   group, _ptr(m_idx), _ptr(n_idx), P, _ptr(y), _ptr(mag))
+                                   b, group, _ptr(m_idx), _ptr(n_idx), P, _ptr(y), _ptr(mag))
     if r != 0:
         raise RuntimeError("oracle_w4a8_points failed (%d)" % r)
     return y, mag

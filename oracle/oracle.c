@@ -44,7 +44,10 @@
  *
  *  - W4A8.  club-3090 discussion #733, "Under the hood": activations are
  *    quantized per token to int8 at run time, int4 weights are widened to
- *    int8 without loss, the product runs on int8 units.  Reading taken
+ *    int8 without loss, the product runs on int8 units ("Which slugs": the
+ *    widening must be lossless, which rules out float formats; integer codes
+ *    of any b <= 8 widen losslessly as c - 2^(b-1) in [-128, 127], so the
+ *    same definition is kept for every b, b = 4 being W4A8).  Reading taken
  *    (the page gives no formula): s_a = amax_k |a| / 127 in fp32 with IEEE
  *    division, Aq = clamp(rint(a / s_a), -127, 127) with ties to even, a
  *    zero row gives s_a = 0 and Aq = 0; per group of 128 the int products
@@ -292,16 +295,17 @@ int oracle_quant_act_i8(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq, flo
     return 0;
 }
 
-/* One W4A8 output from an already quantized activation row:
- * y = s_a * sum_g s[n,g] * (sum_{k in g} Aq[k] * (c[n,k] - 8)),
+/* One int8-activation output from an already quantized activation row:
+ * y = s_a * sum_g s[n,g] * (sum_{k in g} Aq[k] * (c[n,k] - 2^(b-1))),
  * with the inner sums exact in int64 (they must fit int32) and the rest fp64. */
-static int w4a8_dot(const int8_t *aq_row, float sa, const uint8_t *codes_row,
+static int w4a8_dot(const int8_t *aq_row, float sa, const uint8_t *codes_row, int b,
                     const uint16_t *s_row, int64_t K, int group, double *y, double *mag) {
     double acc = 0.0, acc_abs = 0.0;
+    const int64_t zero = (int64_t)1 << (b - 1);
     for (int64_t g = 0; g < K / group; ++g) {
         int64_t ig = 0;
         for (int64_t k = g * group; k < (g + 1) * group; ++k)
-            ig += (int64_t)aq_row[k] * ((int64_t)codes_row[k] - 8);
+            ig += (int64_t)aq_row[k] * ((int64_t)codes_row[k] - zero);
         if (ig > INT32_MAX || ig < INT32_MIN) return -3;
         const double t = bf16_to_double(s_row[g]) * (double)ig;
         acc += t;
@@ -317,12 +321,12 @@ static void unpack_row(const uint32_t *packed, int64_t n, int64_t K, int b, uint
     for (int64_t k = 0; k < K; ++k) out[k] = (uint8_t)read_code(row, k, b);
 }
 
-/* Full W4A8 layer (b = 4).  Aq [M,K] and sa [M] are written too (caller
- * provides them).  y, mag: [M, N] fp64. */
+/* Full int8-activation layer on b-bit codes (b = 4: W4A8).  Aq [M,K] and
+ * sa [M] are written too (caller provides them).  y, mag: [M, N] fp64. */
 int oracle_w4a8(const uint16_t *A, int64_t M, int64_t N, int64_t K,
-                const uint32_t *packed, const uint16_t *scales, int group,
+                const uint32_t *packed, const uint16_t *scales, int b, int group,
                 int8_t *Aq, float *sa, double *y, double *mag) {
-    if (!oracle_little_endian() || group <= 0 || K % group) return -1;
+    if (!oracle_little_endian() || b < 2 || b > 8 || group <= 0 || K % group) return -1;
     oracle_quant_act_i8(A, M, K, Aq, sa);
     const int64_t G = K / group;
     int err = 0;
@@ -336,9 +340,9 @@ int oracle_w4a8(const uint16_t *A, int64_t M, int64_t N, int64_t K,
                 err = -2;
                 continue;
             }
-            unpack_row(packed, n, K, 4, c);
+            unpack_row(packed, n, K, b, c);
             for (int64_t m = 0; m < M; ++m) {
-                int r = w4a8_dot(Aq + m * K, sa[m], c, scales + n * G, K, group,
+                int r = w4a8_dot(Aq + m * K, sa[m], c, b, scales + n * G, K, group,
                                  &y[m * N + n], mag ? &mag[m * N + n] : NULL);
                 if (r) {
 #pragma omp atomic write
@@ -351,13 +355,13 @@ int oracle_w4a8(const uint16_t *A, int64_t M, int64_t N, int64_t K,
     return err;
 }
 
-/* W4A8 at P chosen output positions; Aq/sa must come from
- * oracle_quant_act_i8 on the same A. */
+/* The int8-activation layer at P chosen output positions; Aq/sa must come
+ * from oracle_quant_act_i8 on the same A. */
 int oracle_w4a8_points(const int8_t *Aq, const float *sa, int64_t M, int64_t N, int64_t K,
-                       const uint32_t *packed, const uint16_t *scales, int group,
+                       const uint32_t *packed, const uint16_t *scales, int b, int group,
                        const int64_t *m_idx, const int64_t *n_idx, int64_t P,
                        double *y, double *mag) {
-    if (!oracle_little_endian() || group <= 0 || K % group) return -1;
+    if (!oracle_little_endian() || b < 2 || b > 8 || group <= 0 || K % group) return -1;
     const int64_t G = K / group;
     int err = 0;
 #pragma omp parallel
@@ -371,8 +375,8 @@ int oracle_w4a8_points(const int8_t *Aq, const float *sa, int64_t M, int64_t N, 
                 err = -1;
                 continue;
             }
-            unpack_row(packed, n, K, 4, c);
-            int r = w4a8_dot(Aq + m * K, sa[m], c, scales + n * G, K, group,
+            unpack_row(packed, n, K, b, c);
+            int r = w4a8_dot(Aq + m * K, sa[m], c, b, scales + n * G, K, group,
                              &y[p], mag ? &mag[p] : NULL);
             if (r) {
 #pragma omp atomic write

@@ -317,29 +317,34 @@ def test_quant_act_matches_fp32_numpy_convention():
     np.testing.assert_array_equal(Aq, q)
 
 
-def test_w4a8_on_grid_integer_product():
-    rng = np.random.default_rng(8)
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 6, 7, 8])
+def test_w4a8_on_grid_integer_product(b):
+    # Activations already on the int8 grid (a 127 in every row, so s_a = 1)
+    # and unit scales: the layer is the integer product A . (c - 2^(b-1))^T.
+    rng = np.random.default_rng(8 + 100 * b)
     M, N, K = 6, 40, 512
-    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
     A_int = rng.integers(-127, 128, size=(M, K))
     A_int[:, 0] = 127
     scales = np.full((N, K // 128), BF16_ONE, dtype=np.uint16)
-    y, mag, Aq, sa = oracle.w4a8(_bf16(A_int.astype(np.float32)), oracle.pack(codes, 4), scales)
-    ref = A_int.astype(np.int64) @ (codes.astype(np.int64) - 8).T
+    y, mag, Aq, sa = oracle.w4a8(_bf16(A_int.astype(np.float32)), oracle.pack(codes, b), scales,
+                                 b=b)
+    ref = A_int.astype(np.int64) @ (codes.astype(np.int64) - (1 << (b - 1))).T
     np.testing.assert_array_equal(y, ref.astype(np.float64))
 
 
-def test_w4a8_equals_wna16_b4_for_on_grid_activations():
-    rng = np.random.default_rng(9)
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 6, 7, 8])
+def test_w4a8_equals_wna16_b4_for_on_grid_activations(b):
+    rng = np.random.default_rng(9 + 100 * b)
     M, N, K = 4, 24, 768
-    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
     A_int = rng.integers(-127, 128, size=(M, K))
     A_int[:, 5] = -127
     A = _bf16(A_int.astype(np.float32))
     scales = synth.draw_scales_halfnormal_signed(rng, N, K // 128)
-    packed = oracle.pack(codes, 4)
-    y8, mag8, _, _ = oracle.w4a8(A, packed, scales)
-    y16, mag16 = oracle.wna16(A, packed, scales, 4)
+    packed = oracle.pack(codes, b)
+    y8, mag8, _, _ = oracle.w4a8(A, packed, scales, b=b)
+    y16, mag16 = oracle.wna16(A, packed, scales, b)
     np.testing.assert_allclose(y8, y16, rtol=0, atol=1e-12 * mag16.max())
     np.testing.assert_allclose(mag8 >= np.abs(y8), True)
 
@@ -382,32 +387,35 @@ def test_workload_shapes_and_sign_mix():
     assert [synth.layer_bits(i) for i in (0, 9, 10, 11, 53, 54, 63)] == [7, 7, 5, 6, 6, 7, 7]
 
 
-def test_w4a8_power_of_two_activation_scale():
+@pytest.mark.parametrize("b", [4, 8])
+def test_w4a8_power_of_two_activation_scale(b):
     # On-grid activations times 2^-3: s_a = 2^-3 exactly, Aq = the integers,
-    # and the layer is 2^-3 * A_int . (c - 8)^T exactly.
-    rng = np.random.default_rng(13)
+    # and the layer is 2^-3 * A_int . (c - 2^(b-1))^T exactly.
+    rng = np.random.default_rng(13 + 100 * b)
     M, N, K = 5, 24, 512
-    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
     A_int = rng.integers(-127, 128, size=(M, K))
     A_int[:, 9] = 127
     A = _bf16((A_int * 2.0 ** -3).astype(np.float32))
     scales = np.full((N, K // 128), BF16_ONE, dtype=np.uint16)
-    y, _, Aq, sa = oracle.w4a8(A, oracle.pack(codes, 4), scales)
+    y, _, Aq, sa = oracle.w4a8(A, oracle.pack(codes, b), scales, b=b)
     np.testing.assert_array_equal(sa, np.full(M, 2.0 ** -3, dtype=np.float32))
     np.testing.assert_array_equal(Aq.astype(np.int64), A_int)
-    ref = (A_int.astype(np.int64) @ (codes.astype(np.int64) - 8).T) * 2.0 ** -3
+    ref = (A_int.astype(np.int64) @ (codes.astype(np.int64) - (1 << (b - 1))).T) * 2.0 ** -3
     np.testing.assert_array_equal(y, ref)
 
 
-def test_w4a8_within_activation_rounding_of_wna16():
+@pytest.mark.parametrize("b", [3, 4, 6, 8])
+def test_w4a8_within_activation_rounding_of_wna16(b):
     # For any activations the int8 layer differs from the bf16-activation
     # layer only by the activation rounding: |y8 - y16| <= (s_a / 2) * sum_k |w|.
     w = synth.w4a8(M=8, N=48, K=1024, seed=14)
-    packed = oracle.pack(w.codes, 4)
-    y8, _, Aq, sa = oracle.w4a8(w.A, packed, w.scales)
-    y16, _ = oracle.wna16(w.A, packed, w.scales, 4)
+    codes = synth.draw_codes(np.random.default_rng(15 + b), 48, 1024, b)
+    packed = oracle.pack(codes, b)
+    y8, _, Aq, sa = oracle.w4a8(w.A, packed, w.scales, b=b)
+    y16, _ = oracle.wna16(w.A, packed, w.scales, b)
     s = np.repeat(synth.bf16_bits_to_f32(w.scales).astype(np.float64), 128, axis=1)
-    wsum = np.abs(s * (w.codes.astype(np.float64) - 8)).sum(axis=1)
+    wsum = np.abs(s * (codes.astype(np.float64) - (1 << (b - 1)))).sum(axis=1)
     bound = 0.5 * sa.astype(np.float64)[:, None] * wsum[None, :] * (1 + 1e-6)
     assert np.all(np.abs(y8 - y16) <= bound)
     # and the bound is not vacuous: the difference is well below |y16| scale
