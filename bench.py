@@ -228,6 +228,26 @@ def bench_w4a8(torch, wq, synth, reps: int):
                           "frac_of_int8_peak": ops / t8 / 1e12 / INT8_PEAK_TOPS,
                           "wna16_b4_ms": t16 * 1e3, "speedup_vs_wna16_b4": t16 / t8}
         del A, Y, ws
+    # W8A8: 8-bit codes of the same shape, int8 activations, against WNA16 b = 8.
+    M = 2048
+    codes8 = synth.draw_codes(np.random.default_rng(8), w0.N, w0.K, 8)
+    blob8 = wq.wq_repack(torch.from_numpy(wq.wq_pack(codes8, 8).view(np.int32)).cuda(),
+                         torch.from_numpy(w0.scales.view(np.int16)).cuda().view(torch.bfloat16),
+                         w0.K, 8)
+    A = torch.from_numpy(synth.draw_act(rng, M, w0.K, outlier_frac=0.01).view(np.int16)).cuda() \
+        .view(torch.bfloat16)
+    Y = torch.empty((M, w0.N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, M, w0.N, w0.K, 8),
+                     dtype=torch.uint8, device="cuda")
+    t8 = graph_time(torch, lambda: wq.wq_gemm_a8(A, blob8, wq.WQ_LAYOUT_TILED, None, w0.N, 8,
+                                                 Y=Y, ws=ws), reps, 2)
+    t16 = graph_time(torch, lambda: wq.wq_gemm(A, blob8, wq.WQ_LAYOUT_TILED, None, w0.N, 8, Y=Y),
+                     reps, 2)
+    ops = 2.0 * M * w0.N * w0.K
+    out["W8A8_M%d" % M] = {"ms": t8 * 1e3, "TOP/s": ops / t8 / 1e12,
+                           "frac_of_int8_peak": ops / t8 / 1e12 / INT8_PEAK_TOPS,
+                           "wna16_b8_ms": t16 * 1e3, "speedup_vs_wna16_b8": t16 / t8}
+    del A, Y, ws, blob8
     return out
 
 

@@ -59,7 +59,7 @@ extern "C" {
 typedef enum wq_status {
     WQ_OK = 0,
     WQ_ERR_INVALID_ARG = 1,        /* null pointer, N or K <= 0, M < 0, bad enum */
-    WQ_ERR_UNSUPPORTED_BITS = 2,   /* b outside 2..8, or b != 4 for wq_gemm_a8 */
+    WQ_ERR_UNSUPPORTED_BITS = 2,   /* b outside 2..8 */
     WQ_ERR_BAD_GROUP = 3,          /* group != 128 or K % group != 0 */
     WQ_ERR_MISALIGNED = 4,         /* a device pointer is not 16-byte aligned */
     WQ_ERR_CODE_RANGE = 5,         /* wq_pack: a code is >= 2^b (never masked) */
@@ -183,13 +183,15 @@ int wq_quant_act_i8(const uint16_t *A_d, int64_t M, int64_t K, int8_t *Aq_d, flo
 int wq_embed(const void *W_d, const uint16_t *scales_d, int64_t V, int64_t K, int b, int group,
              const int64_t *ids_d, int64_t T, uint16_t *Y_d, void *stream);
 
-/* Device.  W4A8 layer (same page): activations quantized as wq_quant_act_i8
- * does, int4 codes widened to int8 without loss (c - 8 in [-8, 7]), int8
- * products summed exactly in int32 per group of 128, then
+/* Device.  Int8-activation layer (same page; b = 4 is its W4A8):
+ * activations quantized as wq_quant_act_i8 does, b-bit codes widened to
+ * int8 without loss (c - 2^(b-1) in [-128, 127]; the page's condition for
+ * the widening, met by integer codes of any b <= 8, so b = 8 gives W8A8),
+ * int8 products summed exactly in int32 per group of 128, then
  *   Y[m, n] = sa[m] * sum_g s[n, g] * acc_g[m, n]     (fp32)
  * written as bf16 (out_dtype WQ_OUT_BF16) or fp32 (WQ_OUT_F32).  The same
- * packed int4 weights and scales as wq_gemm with b = 4 are used; b != 4
- * returns WQ_ERR_UNSUPPORTED_BITS.  The workspace holds Aq and sa. */
+ * packed weights and scales as wq_gemm are used, any b in 2..8.  The
+ * workspace holds Aq and sa. */
 int wq_gemm_a8(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
                int layout, const uint16_t *scales_d, int b, int group, void *Y_d,
                int out_dtype, void *ws_d, int64_t ws_bytes, void *stream);

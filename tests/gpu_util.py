@@ -59,7 +59,7 @@ class Layer:
 
     def gemm_a8(self, out_dtype=wq.WQ_OUT_F32, A_bits: np.ndarray | None = None) -> np.ndarray:
         A = self.w.A if A_bits is None else A_bits
-        Y = wq.wq_gemm_a8(dev_bf16(A), self.W_d, self.layout, self.S_d, self.w.N, 4,
+        Y = wq.wq_gemm_a8(dev_bf16(A), self.W_d, self.layout, self.S_d, self.w.N, self.w.b,
                           out_dtype=out_dtype)
         torch.cuda.synchronize()
         if out_dtype == wq.WQ_OUT_F32:

@@ -119,16 +119,18 @@ def test_gemm_workspace_checks():
     assert _gemm(M=1, N=17408, K=5120, ws_bytes=need - 1) == wq.WQ_ERR_WORKSPACE
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 0, 17408, 5120, 6) == 0
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, 17408, 5120, 9) == -1
-    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 64, 17408, 5120, 6) == -1
-    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 64, 17408, 5120, 4) >= 64 * 5120 + 64 * 4
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 64, 17408, 5120, 9) == -1
+    for b in (2, 4, 6, 8):
+        assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 64, 17408, 5120, b) >= 64 * 5120 + 64 * 4
     assert wq.wq_workspace_bytes(7, 1, 256, 512, 6) == -1
 
 
-def test_gemm_a8_refuses_other_widths_and_bad_output():
+def test_gemm_a8_refuses_bad_widths_and_bad_output():
+    # Any b in 2..8 widens losslessly to int8 and is accepted; b outside is refused.
     lib = wq._load()
     c = ctypes.c_void_p
     A = c(ALIGNED)
-    for b in (2, 3, 5, 6, 7, 8):
+    for b in (0, 1, 9, 16):
         assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, b, 128, A, 0, A, 1 << 30, None) == \
             wq.WQ_ERR_UNSUPPORTED_BITS
     assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, 4, 128, A, 7, A, 1 << 30, None) == \

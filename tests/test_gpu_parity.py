@@ -271,6 +271,47 @@ def test_gemm_a8_fp32(M, N, K, layout):
     assert_a8(L.gemm_a8(wq.WQ_OUT_BF16), y_ref, mag, True, "a8 bf16 %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("M,N,K", [(37, 200, 640), (130, 96, 5120)])
+@pytest.mark.parametrize("b", [2, 3, 5, 6, 7, 8])
+def test_gemm_a8_other_widths(b, M, N, K, layout):
+    # Int8 activations on b-bit codes (b = 8: W8A8): the same activations as
+    # the W4A8 workload, codes of width b.
+    w4 = synth.w4a8(M=M, N=N, K=K, seed=1300 + M + b)
+    codes = synth.draw_codes(np.random.default_rng(1310 + b), N, K, b)
+    w = synth.Workload(w4.A, codes, w4.scales, b)
+    y_ref, mag, _, _ = oracle.w4a8(w.A, oracle.pack(codes, b), w.scales, b=b)
+    L = Layer(w, layout)
+    assert_a8(L.gemm_a8(wq.WQ_OUT_F32), y_ref, mag, False, "a8 b=%d f32 %dx%dx%d" % (b, M, N, K))
+    assert_a8(L.gemm_a8(wq.WQ_OUT_BF16), y_ref, mag, True, "a8 b=%d bf16 %dx%dx%d" % (b, M, N, K))
+
+
+@pytest.mark.parametrize("b", [2, 3, 5, 6, 7, 8])
+def test_gemm_a8_on_grid_integer_exact_other_widths(b):
+    rng = np.random.default_rng(1400 + b)
+    M, N, K = 40, 64, 512
+    codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
+    A_int = rng.integers(-127, 128, size=(M, K))
+    A_int[:, 3] = 127
+    w = synth.Workload(synth.f32_to_bf16_bits(A_int.astype(np.float32)), codes,
+                       np.full((N, K // 128), 0x3F80, dtype=np.uint16), b)
+    ref = (A_int @ (codes.astype(np.int64) - (1 << (b - 1))).T).astype(np.float64)
+    for layout in LAYOUTS:
+        np.testing.assert_array_equal(Layer(w, layout).gemm_a8(wq.WQ_OUT_F32), ref)
+
+
+def test_gemm_a8_w8a8_full_shape_sampled():
+    # W8A8 (8-bit codes, int8 activations) at the W4A8 prefill shape.
+    w4 = synth.w4a8(M=2048)
+    codes = synth.draw_codes(np.random.default_rng(1500), w4.N, w4.K, 8)
+    w = synth.Workload(w4.A, codes, w4.scales, 8)
+    Y = Layer(w, wq.WQ_LAYOUT_TILED).gemm_a8(wq.WQ_OUT_F32)
+    Aq, sa = oracle.quant_act_i8(w.A)
+    mi, ni = sample_points(w.M, w.N, 3000, seed=12)
+    y_ref, mag = oracle.w4a8_points(Aq, sa, oracle.pack(codes, 8), w.scales, mi, ni, b=8)
+    assert_a8(Y[mi, ni], y_ref, mag, False, "w8a8 full shape")
+
+
 def test_gemm_a8_on_grid_integer_exact():
     rng = np.random.default_rng(1100)
     M, N, K = 40, 64, 512

@@ -309,7 +309,7 @@ def wq_embed(ids_d, W_d, scales_d, K: int, b: int, group: int = GROUP, Y=None, s
 
 def wq_gemm_a8(A_d, W_d, layout: int, scales_d, N: int, b: int = 4, group: int = GROUP,
                out_dtype: int = WQ_OUT_BF16, Y=None, ws=None, stream=None):
-    """Device: W4A8 layer -> Y [M, N] (bf16 or float32)."""
+    """Device: int8-activation layer on b-bit weights (b = 4: W4A8) -> Y [M, N] (bf16 or float32)."""
     import torch
     _require_cuda("A_d", A_d, torch.bfloat16)
     _require_cuda("W_d", W_d)

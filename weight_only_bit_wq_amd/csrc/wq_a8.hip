@@ -1,9 +1,12 @@
-// wq_a8.hip -- W4A8: per-token int8 activations on int4 weights.
+// wq_a8.hip -- int8 activations on b-bit weights (b = 4: W4A8).
 //
 // club-3090 discussion #733, "Under the hood": activations are quantized per
 // token to int8 at run time, the int4 weights widen to int8 without loss and
 // the product runs on int8 matrix units; the same int4 checkpoint and group
-// scales as the weight-only path are used.  Here:
+// scales as the weight-only path are used.  ("Which slugs": the widening has
+// to be lossless, which is why a float format is refused there; integer
+// codes of any b <= 8 widen losslessly, so every b runs here, b = 8 being
+// W8A8.)  Here:
 //   1. quant_act_kernel: s_a[m] = max|a| / 127 (fp32, IEEE division),
 //      Aq = clamp(rint(a / s_a), -127, 127), zero row -> 0.
 //   2. gemm_a8_kernel: int8 MFMA (v_mfma_i32_16x16x64_i8) with exact int32
@@ -17,6 +20,15 @@
 // odd codes (x & 0xF0F0F0F0), so within every 8 consecutive k the B operand
 // is ordered (0,2,4,6,1,3,5,7); the activation bytes are written in the same
 // order, which leaves the contraction unchanged.
+//
+// Other widths, same idea: the b-bit field c ^ 2^(b-1) is the b-bit two's
+// complement of c - 2^(b-1); shifted to the top of its byte it reads as the
+// int8 value (c - 2^(b-1)) * 2^(8-b), and the group scale becomes
+// s / 2^(8-b) (exact).  Codes are pulled out in pairs with the unpacker's
+// byte-window selectors, four fields packed into a dword with one v_perm_b32,
+// then shifted and XOR-ed (b = 8: the code bytes XOR 0x80).  The k order is
+// the natural one for b != 4, and the activations are written in it.
+// Group sums stay exact: |Aq| <= 127, |w * 2^(8-b)| <= 128, 128 terms.
 #include "wq_device.h"
 #include "wq_launch.h"
 
@@ -50,6 +62,59 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s, bool zero) {
         out.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
     }
     return out;
+}
+
+// Codes 2P, 2P+1 of a 32-code quarter slot held in B words, as the low bits
+// of the two 16-bit halves (masked).
+template <int B, int P>
+__device__ __forceinline__ uint32_t quarter_fields(const uint32_t *w) {
+    using S = QSel<B, P>;
+    const uint32_t lo = w[S::word];
+    const uint32_t hi = S::has_hi ? w[S::word + 1] : 0u;
+    uint32_t x = __builtin_amdgcn_perm(hi, lo, S::sel);
+    if constexpr (S::sh0 != 0 || S::sh1 != 0) x = pk_shr16(x, S::sh0, S::sh1);
+    return x & pair_mask<B>();
+}
+
+// Codes 4I .. 4I+3 of a quarter as four int8 (c - 2^(b-1)) * 2^(8-b), in order.
+template <int B, int I>
+__device__ __forceinline__ uint32_t widen4(const uint32_t *w) {
+    if constexpr (B == 8) {
+        return w[I] ^ 0x80808080u;
+    } else {
+        const uint32_t x = __builtin_amdgcn_perm(quarter_fields<B, 2 * I + 1>(w),
+                                                 quarter_fields<B, 2 * I>(w), 0x06040200u);
+        return (x << (8 - B)) ^ 0x80808080u;
+    }
+}
+
+// Quarter q (dwords [B q, B q + B)) of the slot starting at `slot`, with q
+// wave-uniform: 16-byte loads when B % 4 == 0, 8-byte when B is even (a pair
+// never crosses a 16-byte chunk), else dwords.
+template <class WL, int B>
+__device__ __forceinline__ void load_quarter(const uint8_t *slot, int q, uint32_t *w) {
+    const int d0 = B * q;
+    if constexpr (B % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < B / 4; ++i) {
+            const u32x4 v = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(slot + WL::dword_off(d0 + 4 * i)));
+            w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    } else if constexpr (B % 2 == 0) {
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int i = 0; i < B / 2; ++i) {
+            const u32x2 v = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x2 *>(slot + WL::dword_off(d0 + 2 * i)));
+            w[2 * i] = v.x; w[2 * i + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < B; ++e)
+            w[e] = __builtin_nontemporal_load(
+                reinterpret_cast<const uint32_t *>(slot + WL::dword_off(d0 + e)));
+    }
 }
 
 // One workgroup (256 threads) per activation row.
@@ -114,7 +179,7 @@ __device__ __forceinline__ int a8_swz(int row, int chunk) { return row * 8 + (ch
 // The fold runs one row block behind the group's last MFMAs (row 3 during
 // the next group's first k-step), one block per MFMA, so it issues in the
 // matrix core's shadow.
-template <class WL>
+template <class WL, int B>
 __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__ Aq,
                                                       const float *__restrict__ sa, int M, int N,
                                                       int K, WL wl, void *__restrict__ Y,
@@ -149,8 +214,9 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
     const int8_t *A_blk = Aq + m0 * K;
     const int a_lds = a8_swz(ar, ac);  // + 512 i
 
-    // B loader: row brow, 16-byte chunk bj (wave-uniform) = codes 32 bj .. +32
-    // of the group; widened to int8 it fills LDS chunks 2 bj and 2 bj + 1.
+    // B loader: row brow, quarter bj (wave-uniform) = codes 32 bj .. +32 of
+    // the group (b = 4: 16-byte chunk bj); widened to int8 it fills LDS
+    // chunks 2 bj and 2 bj + 1.
     const int brow = tid & (kABN - 1);
     const int bj = __builtin_amdgcn_readfirstlane(tid >> 7);
     const int64_t bn_read = min(n0 + brow, (int64_t)N - 1);
@@ -158,14 +224,14 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
     const uint8_t *bscale0 = wl.scale0(bn_read);
     const int bstep = (int)wl.slot_step();
     const int sstep = (int)wl.scale_step();
-    const int bchunk_off = WL::dword_off(4 * bj);
 
     // MFMA operand rows and k-chunk of this lane.
     const int arow = wm * 64 + (lane & 15);
     const int bmrow = wn * 64 + (lane & 15);
     const int q = lane >> 4;
 
-    u32x4 areg[4], breg;
+    u32x4 areg[4];
+    uint32_t breg[B];
     uint16_t sreg;
     i32x4_t P[4][4];
     f32x4_t tot[4][4];
@@ -183,22 +249,28 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             areg[i] = *reinterpret_cast<const u32x4 *>(src + (int64_t)arows[i] * K);
-        breg = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4 *>(bslot0 + (int64_t)g * bstep + bchunk_off));
+        load_quarter<WL, B>(bslot0 + (int64_t)g * bstep, bj, breg);
         sreg = *reinterpret_cast<const uint16_t *>(bscale0 + (int64_t)g * sstep);
     };
     auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) Asm[buf][a_lds + 512 * i] = areg[i];
-        const u32x4 x = breg ^ 0x88888888u;
-        Bsm[buf][a8_swz(brow, 2 * bj)] =
-            u32x4{(x.x << 4) & 0xF0F0F0F0u, x.x & 0xF0F0F0F0u, (x.y << 4) & 0xF0F0F0F0u,
-                  x.y & 0xF0F0F0F0u};
-        Bsm[buf][a8_swz(brow, 2 * bj + 1)] =
-            u32x4{(x.z << 4) & 0xF0F0F0F0u, x.z & 0xF0F0F0F0u, (x.w << 4) & 0xF0F0F0F0u,
-                  x.w & 0xF0F0F0F0u};
+        if constexpr (B == 4) {
+            const u32x4 x = u32x4{breg[0], breg[1], breg[2], breg[3]} ^ 0x88888888u;
+            Bsm[buf][a8_swz(brow, 2 * bj)] =
+                u32x4{(x.x << 4) & 0xF0F0F0F0u, x.x & 0xF0F0F0F0u, (x.y << 4) & 0xF0F0F0F0u,
+                      x.y & 0xF0F0F0F0u};
+            Bsm[buf][a8_swz(brow, 2 * bj + 1)] =
+                u32x4{(x.z << 4) & 0xF0F0F0F0u, x.z & 0xF0F0F0F0u, (x.w << 4) & 0xF0F0F0F0u,
+                      x.w & 0xF0F0F0F0u};
+        } else {
+            Bsm[buf][a8_swz(brow, 2 * bj)] = u32x4{widen4<B, 0>(breg), widen4<B, 1>(breg),
+                                                   widen4<B, 2>(breg), widen4<B, 3>(breg)};
+            Bsm[buf][a8_swz(brow, 2 * bj + 1)] = u32x4{widen4<B, 4>(breg), widen4<B, 5>(breg),
+                                                       widen4<B, 6>(breg), widen4<B, 7>(breg)};
+        }
         // The four chunk waves of a row store the same value: no branch.
-        Ss[buf][brow] = bf16_to_f32(sreg) * 0.0625f;
+        Ss[buf][brow] = bf16_to_f32(sreg) * (1.0f / (float)(1 << (8 - B)));
     };
     auto fold_block = [&](int i, int j, const float(&sq)[4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -277,30 +349,51 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
         }
 }
 
-hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                          bool tiled, const uint16_t *scales, void *Y, bool out_f32, void *ws,
-                          hipStream_t stream) {
-    int8_t *Aq = reinterpret_cast<int8_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
-    float *sa = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset +
-                                          align256(M * K));
-    hipLaunchKernelGGL((quant_act_kernel<true>), dim3((unsigned)M), dim3(256), 0, stream, A,
-                       (int)K, Aq, sa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+template <int B>
+static hipError_t launch_gemm_a8_b(const int8_t *Aq, const float *sa, int64_t M, int64_t N,
+                                   int64_t K, const void *W, bool tiled, const uint16_t *scales,
+                                   void *Y, bool out_f32, hipStream_t stream) {
     const int G = (int)(K / kGroup);
     const int mtiles = (int)((M + kABM - 1) / kABM);
     const int ntiles = (int)((N + kABN - 1) / kABN);
     const dim3 grid((unsigned)(mtiles * ntiles));
     if (tiled) {
-        TiledW wl{static_cast<const uint8_t *>(W), G, 4};
-        hipLaunchKernelGGL((gemm_a8_kernel<TiledW>), grid, dim3(512), 0, stream, Aq, sa, (int)M,
-                           (int)N, (int)K, wl, Y, out_f32, mtiles, ntiles);
+        TiledW wl{static_cast<const uint8_t *>(W), G, B};
+        hipLaunchKernelGGL((gemm_a8_kernel<TiledW, B>), grid, dim3(512), 0, stream, Aq, sa,
+                           (int)M, (int)N, (int)K, wl, Y, out_f32, mtiles, ntiles);
     } else {
-        DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * 4 * G, G, 4};
-        hipLaunchKernelGGL((gemm_a8_kernel<DenseW>), grid, dim3(512), 0, stream, Aq, sa, (int)M,
-                           (int)N, (int)K, wl, Y, out_f32, mtiles, ntiles);
+        DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
+        hipLaunchKernelGGL((gemm_a8_kernel<DenseW, B>), grid, dim3(512), 0, stream, Aq, sa,
+                           (int)M, (int)N, (int)K, wl, Y, out_f32, mtiles, ntiles);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
+                          bool tiled, const uint16_t *scales, int b, void *Y, bool out_f32,
+                          void *ws, hipStream_t stream) {
+    int8_t *Aq = reinterpret_cast<int8_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
+    float *sa = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset +
+                                          align256(M * K));
+    // b = 4 takes the (0,2,4,6,1,3,5,7) k order of its widening; others the natural one.
+    if (b == 4)
+        hipLaunchKernelGGL((quant_act_kernel<true>), dim3((unsigned)M), dim3(256), 0, stream, A,
+                           (int)K, Aq, sa);
+    else
+        hipLaunchKernelGGL((quant_act_kernel<false>), dim3((unsigned)M), dim3(256), 0, stream, A,
+                           (int)K, Aq, sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (b) {
+        case 2: return launch_gemm_a8_b<2>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
+        case 3: return launch_gemm_a8_b<3>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
+        case 4: return launch_gemm_a8_b<4>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
+        case 5: return launch_gemm_a8_b<5>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
+        case 6: return launch_gemm_a8_b<6>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
+        case 7: return launch_gemm_a8_b<7>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
+        case 8: return launch_gemm_a8_b<8>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace wq

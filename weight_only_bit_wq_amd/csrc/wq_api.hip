@@ -102,7 +102,7 @@ const char *wq_status_str(int status) {
     switch (status) {
         case WQ_OK: return "ok";
         case WQ_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive N or K, negative M, or unknown enum value)";
-        case WQ_ERR_UNSUPPORTED_BITS: return "unsupported bit width: b must be in 2..8, and wq_gemm_a8 takes only b = 4 (int4 codes)";
+        case WQ_ERR_UNSUPPORTED_BITS: return "unsupported bit width: b must be in 2..8";
         case WQ_ERR_BAD_GROUP: return "group must be 128 and divide K";
         case WQ_ERR_MISALIGNED: return "device pointer is not 16-byte aligned";
         case WQ_ERR_CODE_RANGE: return "a code does not fit in b bits (codes are refused, never masked)";
@@ -235,10 +235,7 @@ int wq_embed(const void *W_d, const uint16_t *scales_d, int64_t V, int64_t K, in
 int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int group) {
     if (!dims_ok(M, N, K) || !valid_bits(b) || check_group(K, group) != WQ_OK) return -1;
     if (op == WQ_OP_GEMM) return gemm_ws_bytes(M, N, K, b);
-    if (op == WQ_OP_GEMM_A8) {
-        if (b != 4) return -1;
-        return wq::a8_ws_bytes(M, N, K);
-    }
+    if (op == WQ_OP_GEMM_A8) return wq::a8_ws_bytes(M, N, K);
     return -1;
 }
 
@@ -287,7 +284,7 @@ int wq_gemm_a8(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void 
                int layout, const uint16_t *scales_d, int b, int group, void *Y_d,
                int out_dtype, void *ws_d, int64_t ws_bytes, void *stream) {
     if (!dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
-    if (b != 4) return WQ_ERR_UNSUPPORTED_BITS;
+    if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
     if (int s = check_group(K, group)) return s;
     if (layout != WQ_LAYOUT_DENSE && layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
     if ((layout == WQ_LAYOUT_DENSE) != (scales_d != nullptr)) return WQ_ERR_BAD_LAYOUT;
@@ -300,8 +297,8 @@ int wq_gemm_a8(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void 
     const int64_t need = wq::a8_ws_bytes(M, N, K);
     if (!ws_d || ws_bytes < need) return WQ_ERR_WORKSPACE;
     if (int s = check_device()) return s;
-    hipError_t e = wq::launch_gemm_a8(A_d, M, N, K, W_d, layout == WQ_LAYOUT_TILED, scales_d, Y_d,
-                                      out_dtype == WQ_OUT_F32, ws_d, (hipStream_t)stream);
+    hipError_t e = wq::launch_gemm_a8(A_d, M, N, K, W_d, layout == WQ_LAYOUT_TILED, scales_d, b,
+                                      Y_d, out_dtype == WQ_OUT_F32, ws_d, (hipStream_t)stream);
     return e == hipSuccess ? WQ_OK : hip_fail(e);
 }
 

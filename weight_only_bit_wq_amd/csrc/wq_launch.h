@@ -54,7 +54,7 @@ hipError_t launch_quant_act(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq,
                             hipStream_t stream);
 int64_t a8_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                          bool tiled, const uint16_t *scales, void *Y, bool out_f32, void *ws,
-                          hipStream_t stream);
+                          bool tiled, const uint16_t *scales, int b, void *Y, bool out_f32,
+                          void *ws, hipStream_t stream);
 
 }  // namespace wq
