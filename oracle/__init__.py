@@ -54,14 +54,14 @@ def _load():
     lib.oracle_words_per_row.restype = i64
     lib.oracle_pack.argtypes = [P, i64, i64, ci, P]
     lib.oracle_unpack.argtypes = [P, i64, i64, ci, P]
-    lib.oracle_wna16.argtypes = [P, i64, i64, i64, P, P, ci, ci, P, P]
-    lib.oracle_wna16_points.argtypes = [P, i64, i64, i64, P, P, ci, ci, P, P, i64, P, P]
+    lib.oracle_wna16.argtypes = [P, i64, i64, i64, P, P, P, ci, ci, P, P]
+    lib.oracle_wna16_points.argtypes = [P, i64, i64, i64, P, P, P, ci, ci, P, P, i64, P, P]
     lib.oracle_quant_act_i8.argtypes = [P, i64, i64, P, P]
-    lib.oracle_w4a8.argtypes = [P, i64, i64, i64, P, P, ci, ci, P, P, P, P]
-    lib.oracle_w4a8_points.argtypes = [P, P, i64, i64, i64, P, P, ci, ci, P, P, i64, P, P]
+    lib.oracle_w4a8.argtypes = [P, i64, i64, i64, P, P, P, ci, ci, P, P, P, P]
+    lib.oracle_w4a8_points.argtypes = [P, P, i64, i64, i64, P, P, P, ci, ci, P, P, i64, P, P]
     lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
     lib.oracle_bf16_rne.restype = ctypes.c_uint16
-    lib.oracle_embed.argtypes = [P, P, i64, i64, ci, ci, P, i64, P]
+    lib.oracle_embed.argtypes = [P, P, P, i64, i64, ci, ci, P, i64, P]
     for f in ("oracle_pack", "oracle_unpack", "oracle_wna16", "oracle_wna16_points",
               "oracle_quant_act_i8", "oracle_w4a8", "oracle_w4a8_points", "oracle_embed",
               "oracle_num_threads", "oracle_abi", "oracle_little_endian"):
@@ -76,6 +76,15 @@ def _ptr(a: np.ndarray):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _zeros(zeros, N: int, G: int):
+    """Zero points uint8 [N, G] as (array, pointer), or (None, NULL) for symmetric groups."""
+    if zeros is None:
+        return None, None
+    z = _c(zeros, np.uint8)
+    assert z.shape == (N, G)
+    return z, _ptr(z)
 
 
 def num_threads() -> int:
@@ -105,24 +114,27 @@ def unpack(packed: np.ndarray, K: int, b: int) -> np.ndarray:
     return out
 
 
-def wna16(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, b: int, group: int = 128):
-    """Return (y, mag), fp64 [M, N]."""
+def wna16(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, b: int, group: int = 128,
+          zeros=None):
+    """Return (y, mag), fp64 [M, N].  zeros: uint8 [N, K/group] zero points, or None
+    for symmetric groups (z = 2^(b-1)); group = K is per-channel."""
     A = _c(A, np.uint16)
     packed = _c(packed, np.uint32)
     scales = _c(scales, np.uint16)
     M, K = A.shape
     N = packed.shape[0]
     assert packed.shape[1] == words_per_row(K, b) and scales.shape == (N, K // group)
+    z, zp = _zeros(zeros, N, K // group)
     y = np.empty((M, N), dtype=np.float64)
     mag = np.empty((M, N), dtype=np.float64)
-    r = _load().oracle_wna16(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), b, group,
+    r = _load().oracle_wna16(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), zp, b, group,
                              _ptr(y), _ptr(mag))
     if r != 0:
         raise RuntimeError("oracle_wna16 failed (%d)" % r)
     return y, mag
 
 
-def wna16_points(A, packed, scales, b, m_idx, n_idx, group: int = 128):
+def wna16_points(A, packed, scales, b, m_idx, n_idx, group: int = 128, zeros=None):
     A = _c(A, np.uint16)
     packed = _c(packed, np.uint32)
     scales = _c(scales, np.uint16)
@@ -132,9 +144,10 @@ def wna16_points(A, packed, scales, b, m_idx, n_idx, group: int = 128):
     N = packed.shape[0]
     assert packed.shape[1] == words_per_row(K, b) and scales.shape == (N, K // group)
     P = m_idx.size
+    z, zp = _zeros(zeros, N, K // group)
     y = np.empty(P, dtype=np.float64)
     mag = np.empty(P, dtype=np.float64)
-    r = _load().oracle_wna16_points(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), b, group,
+    r = _load().oracle_wna16_points(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), zp, b, group,
                                     _ptr(m_idx), _ptr(n_idx), P, _ptr(y), _ptr(mag))
     if r != 0:
         raise RuntimeError("oracle_wna16_points failed (%d)" % r)
@@ -148,15 +161,17 @@ def bf16_rne(x) -> np.ndarray:
     return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
 
 
-def embed(packed: np.ndarray, scales: np.ndarray, K: int, b: int, ids, group: int = 128):
+def embed(packed: np.ndarray, scales: np.ndarray, K: int, b: int, ids, group: int = 128,
+          zeros=None):
     """Quantized embedding gather: bf16 bits [T, K] of rows ids of the dequantized table."""
     packed = _c(packed, np.uint32)
     scales = _c(scales, np.uint16)
     ids = _c(ids, np.int64).ravel()
     V = packed.shape[0]
     assert packed.shape[1] == words_per_row(K, b) and scales.shape == (V, K // group)
+    z, zp = _zeros(zeros, V, K // group)
     out = np.empty((ids.size, K), dtype=np.uint16)
-    r = _load().oracle_embed(_ptr(packed), _ptr(scales), V, K, b, group, _ptr(ids), ids.size,
+    r = _load().oracle_embed(_ptr(packed), _ptr(scales), zp, V, K, b, group, _ptr(ids), ids.size,
                              _ptr(out))
     if r != 0:
         raise RuntimeError("oracle_embed failed (%d)" % r)
@@ -173,7 +188,8 @@ def quant_act_i8(A: np.ndarray):
     return Aq, sa
 
 
-def w4a8(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, group: int = 128, b: int = 4):
+def w4a8(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, group: int = 128, b: int = 4,
+         zeros=None):
     """Return (y, mag, Aq, s_a) for the int8-activation layer on b-bit codes
     (b = 4: W4A8)."""
     A = _c(A, np.uint16)
@@ -182,18 +198,19 @@ def w4a8(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, group: int = 128
     M, K = A.shape
     N = packed.shape[0]
     assert packed.shape[1] == words_per_row(K, b) and scales.shape == (N, K // group)
+    z, zp = _zeros(zeros, N, K // group)
     Aq = np.empty((M, K), dtype=np.int8)
     sa = np.empty(M, dtype=np.float32)
     y = np.empty((M, N), dtype=np.float64)
     mag = np.empty((M, N), dtype=np.float64)
-    r = _load().oracle_w4a8(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), b, group,
+    r = _load().oracle_w4a8(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), zp, b, group,
                             _ptr(Aq), _ptr(sa), _ptr(y), _ptr(mag))
     if r != 0:
         raise RuntimeError("oracle_w4a8 failed (%d)" % r)
     return y, mag, Aq, sa
 
 
-def w4a8_points(Aq, sa, packed, scales, m_idx, n_idx, group: int = 128, b: int = 4):
+def w4a8_points(Aq, sa, packed, scales, m_idx, n_idx, group: int = 128, b: int = 4, zeros=None):
     Aq = _c(Aq, np.int8)
     sa = _c(sa, np.float32)
     packed = _c(packed, np.uint32)
@@ -203,10 +220,11 @@ def w4a8_points(Aq, sa, packed, scales, m_idx, n_idx, group: int = 128, b: int =
     M, K = Aq.shape
     N = packed.shape[0]
     P = m_idx.size
+    z, zp = _zeros(zeros, N, K // group)
     y = np.empty(P, dtype=np.float64)
     mag = np.empty(P, dtype=np.float64)
     r = _load().oracle_w4a8_points(_ptr(Aq), _ptr(sa), M, N, K, _ptr(packed), _ptr(scales),
-                                   b, group, _ptr(m_idx), _ptr(n_idx), P, _ptr(y), _ptr(mag))
+                                   zp, b, group, _ptr(m_idx), _ptr(n_idx), P, _ptr(y), _ptr(mag))
     if r != 0:
         raise RuntimeError("oracle_w4a8_points failed (%d)" % r)
     return y, mag

@@ -33,6 +33,14 @@
  *    y = A . dequant(W)^T with W of shape [out_features N, in_features K],
  *    no bias.  Here dequant is done in fp64 and the sum is exact-as-fp64.
  *
+ *  - Zero points and per-channel scales.  Same model card, Findings: the
+ *    asymmetric (zero-point) form exists for 4 and 8 bits only; "vLLM
+ *    Quantization" (online shorthands) lists INT8 weights with one scale
+ *    per channel.  Reading taken: a zero point is an unsigned integer z per
+ *    (row, group) with the code's range, q = c - z replacing c - 2^(b-1)
+ *    (zeros == NULL is the symmetric case); a per-channel scale is the
+ *    group size K (one group per row).
+ *
  *  - Quantized embedding gather.  Same model card, Findings: an embedding
  *    table in this dense layout needs a gather that reads the dense rows
  *    (the one it names assumes codes never straddle a word); "vLLM Can Run
@@ -146,15 +154,19 @@ int oracle_unpack(const uint32_t *packed, int64_t N, int64_t K, int b, uint8_t *
     return 0;
 }
 
-/* Row n dequantized to fp64: w[k] = s[n, k/group] * (c[n,k] - 2^(b-1)). */
-static void dequant_row(const uint32_t *packed, const uint16_t *scales, int64_t n,
-                        int64_t K, int b, int group, double *w) {
+/* Zero point of (row n, group g): zeros[n, g], or 2^(b-1) when zeros is NULL. */
+static int zero_point(const uint8_t *zeros, int64_t n, int64_t G, int64_t g, int b) {
+    return zeros ? (int)zeros[n * G + g] : 1 << (b - 1);
+}
+
+/* Row n dequantized to fp64: w[k] = s[n, k/group] * (c[n,k] - z[n, k/group]). */
+static void dequant_row(const uint32_t *packed, const uint16_t *scales, const uint8_t *zeros,
+                        int64_t n, int64_t K, int b, int group, double *w) {
     const int64_t W = oracle_words_per_row(K, b);
     const int64_t G = K / group;
     const uint8_t *row = (const uint8_t *)(packed + n * W);
-    const int zero = 1 << (b - 1);
     for (int64_t k = 0; k < K; ++k) {
-        const int q = (int)read_code(row, k, b) - zero;
+        const int q = (int)read_code(row, k, b) - zero_point(zeros, n, G, k / group, b);
         w[k] = bf16_to_double(scales[n * G + k / group]) * (double)q;
     }
 }
@@ -184,8 +196,8 @@ uint16_t oracle_bf16_rne(double x) {
 /* Quantized embedding gather: out[t, k] = bf16 of row ids[t] of the
  * dequantized table (zeros for ids outside [0, V)).  packed is the dense
  * [V, ceil(K*b/32)] table, scales bf16 [V, K/group], out bf16 bits [T, K]. */
-int oracle_embed(const uint32_t *packed, const uint16_t *scales, int64_t V, int64_t K, int b,
-                 int group, const int64_t *ids, int64_t T, uint16_t *out) {
+int oracle_embed(const uint32_t *packed, const uint16_t *scales, const uint8_t *zeros, int64_t V,
+                 int64_t K, int b, int group, const int64_t *ids, int64_t T, uint16_t *out) {
     if (!oracle_little_endian() || b < 2 || b > 8 || group <= 0 || K % group) return -1;
     double *w = (double *)malloc((size_t)K * sizeof(double));
     if (!w) return -2;
@@ -195,7 +207,7 @@ int oracle_embed(const uint32_t *packed, const uint16_t *scales, int64_t V, int6
             for (int64_t k = 0; k < K; ++k) out[t * K + k] = 0;
             continue;
         }
-        dequant_row(packed, scales, id, K, b, group, w);
+        dequant_row(packed, scales, zeros, id, K, b, group, w);
         for (int64_t k = 0; k < K; ++k) out[t * K + k] = oracle_bf16_rne(w[k]);
     }
     free(w);
@@ -205,8 +217,8 @@ int oracle_embed(const uint32_t *packed, const uint16_t *scales, int64_t V, int6
 /* y[m,n] = sum_k A[m,k] * w[n,k] and mag[m,n] = sum_k |A[m,k] * w[n,k]|,
  * both fp64, outputs [M, N] row-major.  mag may be NULL. */
 int oracle_wna16(const uint16_t *A, int64_t M, int64_t N, int64_t K,
-                 const uint32_t *packed, const uint16_t *scales, int b, int group,
-                 double *y, double *mag) {
+                 const uint32_t *packed, const uint16_t *scales, const uint8_t *zeros, int b,
+                 int group, double *y, double *mag) {
     if (!oracle_little_endian() || b < 1 || b > 8 || group <= 0 || K % group) return -1;
     int err = 0;
 #pragma omp parallel
@@ -219,7 +231,7 @@ int oracle_wna16(const uint16_t *A, int64_t M, int64_t N, int64_t K,
 #pragma omp for schedule(dynamic, 16)
         for (int64_t n = 0; n < N; ++n) {
             if (!w) continue;
-            dequant_row(packed, scales, n, K, b, group, w);
+            dequant_row(packed, scales, zeros, n, K, b, group, w);
             for (int64_t m = 0; m < M; ++m) {
                 double acc = 0.0, acc_abs = 0.0;
                 for (int64_t k = 0; k < K; ++k) {
@@ -238,7 +250,8 @@ int oracle_wna16(const uint16_t *A, int64_t M, int64_t N, int64_t K,
 
 /* The same sums at P chosen output positions (m_idx[p], n_idx[p]). */
 int oracle_wna16_points(const uint16_t *A, int64_t M, int64_t N, int64_t K,
-                        const uint32_t *packed, const uint16_t *scales, int b, int group,
+                        const uint32_t *packed, const uint16_t *scales, const uint8_t *zeros,
+                        int b, int group,
                         const int64_t *m_idx, const int64_t *n_idx, int64_t P,
                         double *y, double *mag) {
     if (!oracle_little_endian() || b < 1 || b > 8 || group <= 0 || K % group) return -1;
@@ -254,7 +267,7 @@ int oracle_wna16_points(const uint16_t *A, int64_t M, int64_t N, int64_t K,
                 err = -1;
                 continue;
             }
-            dequant_row(packed, scales, n, K, b, group, w);
+            dequant_row(packed, scales, zeros, n, K, b, group, w);
             double acc = 0.0, acc_abs = 0.0;
             for (int64_t k = 0; k < K; ++k) {
                 const double t = bf16_to_double(A[m * K + k]) * w[k];
@@ -296,13 +309,15 @@ int oracle_quant_act_i8(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq, flo
 }
 
 /* One int8-activation output from an already quantized activation row:
- * y = s_a * sum_g s[n,g] * (sum_{k in g} Aq[k] * (c[n,k] - 2^(b-1))),
- * with the inner sums exact in int64 (they must fit int32) and the rest fp64. */
+ * y = s_a * sum_g s[n,g] * (sum_{k in g} Aq[k] * (c[n,k] - z[n,g])),
+ * with the inner sums exact in int64 (they must fit int32) and the rest fp64.
+ * z_row is row n of the zero points (NULL: 2^(b-1)). */
 static int w4a8_dot(const int8_t *aq_row, float sa, const uint8_t *codes_row, int b,
-                    const uint16_t *s_row, int64_t K, int group, double *y, double *mag) {
+                    const uint16_t *s_row, const uint8_t *z_row, int64_t K, int group,
+                    double *y, double *mag) {
     double acc = 0.0, acc_abs = 0.0;
-    const int64_t zero = (int64_t)1 << (b - 1);
     for (int64_t g = 0; g < K / group; ++g) {
+        const int64_t zero = z_row ? (int64_t)z_row[g] : (int64_t)1 << (b - 1);
         int64_t ig = 0;
         for (int64_t k = g * group; k < (g + 1) * group; ++k)
             ig += (int64_t)aq_row[k] * ((int64_t)codes_row[k] - zero);
@@ -324,7 +339,8 @@ static void unpack_row(const uint32_t *packed, int64_t n, int64_t K, int b, uint
 /* Full int8-activation layer on b-bit codes (b = 4: W4A8).  Aq [M,K] and
  * sa [M] are written too (caller provides them).  y, mag: [M, N] fp64. */
 int oracle_w4a8(const uint16_t *A, int64_t M, int64_t N, int64_t K,
-                const uint32_t *packed, const uint16_t *scales, int b, int group,
+                const uint32_t *packed, const uint16_t *scales, const uint8_t *zeros, int b,
+                int group,
                 int8_t *Aq, float *sa, double *y, double *mag) {
     if (!oracle_little_endian() || b < 2 || b > 8 || group <= 0 || K % group) return -1;
     oracle_quant_act_i8(A, M, K, Aq, sa);
@@ -342,7 +358,8 @@ int oracle_w4a8(const uint16_t *A, int64_t M, int64_t N, int64_t K,
             }
             unpack_row(packed, n, K, b, c);
             for (int64_t m = 0; m < M; ++m) {
-                int r = w4a8_dot(Aq + m * K, sa[m], c, b, scales + n * G, K, group,
+                int r = w4a8_dot(Aq + m * K, sa[m], c, b, scales + n * G,
+                                 zeros ? zeros + n * G : NULL, K, group,
                                  &y[m * N + n], mag ? &mag[m * N + n] : NULL);
                 if (r) {
 #pragma omp atomic write
@@ -358,7 +375,8 @@ int oracle_w4a8(const uint16_t *A, int64_t M, int64_t N, int64_t K,
 /* The int8-activation layer at P chosen output positions; Aq/sa must come
  * from oracle_quant_act_i8 on the same A. */
 int oracle_w4a8_points(const int8_t *Aq, const float *sa, int64_t M, int64_t N, int64_t K,
-                       const uint32_t *packed, const uint16_t *scales, int b, int group,
+                       const uint32_t *packed, const uint16_t *scales, const uint8_t *zeros,
+                       int b, int group,
                        const int64_t *m_idx, const int64_t *n_idx, int64_t P,
                        double *y, double *mag) {
     if (!oracle_little_endian() || b < 2 || b > 8 || group <= 0 || K % group) return -1;
@@ -376,8 +394,8 @@ int oracle_w4a8_points(const int8_t *Aq, const float *sa, int64_t M, int64_t N, 
                 continue;
             }
             unpack_row(packed, n, K, b, c);
-            int r = w4a8_dot(Aq + m * K, sa[m], c, b, scales + n * G, K, group,
-                             &y[p], mag ? &mag[p] : NULL);
+            int r = w4a8_dot(Aq + m * K, sa[m], c, b, scales + n * G,
+                             zeros ? zeros + n * G : NULL, K, group, &y[p], mag ? &mag[p] : NULL);
             if (r) {
 #pragma omp atomic write
                 err = r;

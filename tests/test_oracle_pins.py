@@ -501,3 +501,87 @@ def test_embed_equals_layer_on_one_hot_rows(b):
     out = oracle.embed(packed, scales, K, b, ids)
     unsigned_zero = lambda bits: np.where(bits == 0x8000, 0, bits)
     np.testing.assert_array_equal(unsigned_zero(out), unsigned_zero(oracle.bf16_rne(y[:, ids].T)))
+
+
+# --- zero points (b = 4, 8) and per-channel scales ([card] Findings; vLLM Quantization,
+#     online shorthands) ---------------------------------------------------------
+
+@pytest.mark.parametrize("b", [4, 8])
+def test_zero_points_integer_product(b):
+    # Integer activations, unit scales, zero points z[n, g]: the layer is the
+    # integer product sum_k a[m,k] (c[n,k] - z[n, k/128]).
+    rng = np.random.default_rng(60 + b)
+    M, N, K = 5, 33, 384
+    codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
+    zeros = rng.integers(0, 1 << b, size=(N, K // 128), dtype=np.uint8)
+    A_int = rng.integers(-16, 17, size=(M, K))
+    scales = np.full((N, K // 128), BF16_ONE, dtype=np.uint16)
+    y, _ = oracle.wna16(_bf16(A_int.astype(np.float32)), oracle.pack(codes, b), scales, b,
+                        zeros=zeros)
+    q = codes.astype(np.int64) - np.repeat(zeros.astype(np.int64), 128, axis=1)
+    np.testing.assert_array_equal(y, (A_int.astype(np.int64) @ q.T).astype(np.float64))
+
+
+@pytest.mark.parametrize("b", [4, 8])
+def test_midpoint_zero_points_are_the_symmetric_layer(b):
+    # z = 2^(b-1) everywhere is the symmetric form: identical fp64 results.
+    w = synth.decode(M=3, b=b, N=40, K=512)
+    packed = oracle.pack(w.codes, b)
+    zeros = np.full((40, 4), 1 << (b - 1), dtype=np.uint8)
+    y0, m0 = oracle.wna16(w.A, packed, w.scales, b)
+    y1, m1 = oracle.wna16(w.A, packed, w.scales, b, zeros=zeros)
+    np.testing.assert_array_equal(y1, y0)
+    np.testing.assert_array_equal(m1, m0)
+
+
+@pytest.mark.parametrize("b", [4, 6, 8])
+def test_per_channel_scale_is_the_replicated_group_scale(b):
+    # group = K (one scale per row) equals group 128 with that scale in every
+    # group: each dequantized weight is the same exact fp64 product.
+    rng = np.random.default_rng(70 + b)
+    M, N, K = 4, 24, 640
+    codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
+    s1 = synth.draw_scales_halfnormal_signed(rng, N, 1)
+    A = synth.draw_act(rng, M, K)
+    packed = oracle.pack(codes, b)
+    y_pc, mag_pc = oracle.wna16(A, packed, s1, b, group=K)
+    y_g, mag_g = oracle.wna16(A, packed, np.repeat(s1, K // 128, axis=1), b)
+    np.testing.assert_array_equal(y_pc, y_g)
+    np.testing.assert_array_equal(mag_pc, mag_g)
+
+
+def test_embed_zero_points_and_per_channel_closed_form():
+    # b = 4: row r has codes k mod 16, zero point r mod 16 in every group and
+    # scale 2^-(r mod 4): w = 2^-(r mod 4) * ((k mod 16) - (r mod 16)).
+    V, K, b = 20, 256, 4
+    k = np.arange(K)
+    codes = np.tile(k % 16, (V, 1)).astype(np.uint8)
+    r = np.arange(V)
+    zeros = np.repeat((r % 16)[:, None], K // 128, axis=1).astype(np.uint8)
+    s = _bf16(2.0 ** -(r % 4).astype(np.float32))[:, None]
+    ids = np.array([3, 17, 0, 19])
+    packed = oracle.pack(codes, b)
+    # group-128 scales (the row's scale in each group) with the zero points
+    out = oracle.embed(packed, np.repeat(s, K // 128, axis=1), K, b, ids, zeros=zeros)
+    expect = np.stack([2.0 ** -(i % 4) * ((k % 16) - (i % 16)) for i in ids])
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(out).astype(np.float64), expect)
+    # per-channel scales (group = K), symmetric: w = s * (c - 8)
+    out_pc = oracle.embed(packed, s, K, b, ids, group=K)
+    expect_sym = np.stack([2.0 ** -(i % 4) * ((k % 16) - 8) for i in ids])
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(out_pc).astype(np.float64), expect_sym)
+
+
+def test_w4a8_zero_points_integer_product():
+    # On-grid activations, unit scales, b = 4 with zero points: the int8 path
+    # is the integer product A . (c - z)^T.
+    rng = np.random.default_rng(80)
+    M, N, K = 6, 40, 512
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(N, K // 128), dtype=np.uint8)
+    A_int = rng.integers(-127, 128, size=(M, K))
+    A_int[:, 0] = 127
+    scales = np.full((N, K // 128), BF16_ONE, dtype=np.uint16)
+    y, _, _, _ = oracle.w4a8(_bf16(A_int.astype(np.float32)), oracle.pack(codes, 4), scales,
+                             zeros=zeros)
+    q = codes.astype(np.int64) - np.repeat(zeros.astype(np.int64), 128, axis=1)
+    np.testing.assert_array_equal(y, (A_int.astype(np.int64) @ q.T).astype(np.float64))
