@@ -19,6 +19,11 @@
  *     scale s[n, g] per group of 128 input features, no zero point; the
  *     signed weight is c - 2^(b-1).  Scales may be negative (club-3090
  *     discussion #733, "Under the hood").
+ *   - The asymmetric form exists for b = 4 and 8 only (same page,
+ *     Findings): an optional zero point z[n, g] (uint8 [N, K/128], zeros_d)
+ *     makes the signed weight c - z.  A per-channel scale ("vLLM
+ *     Quantization", online shorthands: INT8 with one scale per channel) is
+ *     group = K, scales [N, 1].
  *   - The result is the plain linear layer on the dequantized weights
  *     ("vLLM Can Run INT5-7", section 2), y = A . W^T, no bias.
  *
@@ -42,7 +47,10 @@
  *     (thread-local).
  *   - bf16 values travel as uint16_t bit patterns.
  *   - Device entry points require a gfx950 device (WQ_ERR_UNSUPPORTED_DEVICE
- *     otherwise) and group == 128 with K % 128 == 0 (WQ_ERR_BAD_GROUP).
+ *     otherwise), K % 128 == 0, and group == 128 or group == K
+ *     (WQ_ERR_BAD_GROUP).  Zero points are NULL (symmetric) or uint8
+ *     [N, K/128] with values below 2^b, and only for b = 4 or 8
+ *     (WQ_ERR_ZERO_POINTS).
  *   - Sizes are int64_t; M == 0 is a valid no-op; N, K must be > 0.
  */
 #ifndef WQ_H
@@ -54,19 +62,22 @@
 extern "C" {
 #endif
 
-#define WQ_ABI_VERSION 1
+#define WQ_ABI_VERSION 2
 
 typedef enum wq_status {
     WQ_OK = 0,
     WQ_ERR_INVALID_ARG = 1,        /* null pointer, N or K <= 0, M < 0, bad enum */
     WQ_ERR_UNSUPPORTED_BITS = 2,   /* b outside 2..8 */
-    WQ_ERR_BAD_GROUP = 3,          /* group != 128 or K % group != 0 */
+    WQ_ERR_BAD_GROUP = 3,          /* group not 128 or K, K % 128 != 0, or per-channel
+                                      scales (group K) on a GEMM's dense layout */
     WQ_ERR_MISALIGNED = 4,         /* a device pointer is not 16-byte aligned */
     WQ_ERR_CODE_RANGE = 5,         /* wq_pack: a code is >= 2^b (never masked) */
     WQ_ERR_WORKSPACE = 6,          /* workspace missing or smaller than required */
     WQ_ERR_BAD_LAYOUT = 7,         /* unknown layout, or scales given/missing wrongly */
     WQ_ERR_UNSUPPORTED_DEVICE = 8, /* current device is not gfx950 */
-    WQ_ERR_HIP = 9                 /* a HIP call or kernel launch failed */
+    WQ_ERR_HIP = 9,                /* a HIP call or kernel launch failed */
+    WQ_ERR_ZERO_POINTS = 10        /* zero points for a width without an asymmetric form
+                                      (b = 4 or 8; b = 4 on the int8-activation path) */
 } wq_status;
 
 /* Weight layouts accepted by the device entry points. */
@@ -128,8 +139,10 @@ int64_t wq_repacked_bytes(int layout, int64_t N, int64_t K, int b, int group);
 
 /* Device.  Repack (the "repack after load" step of "vLLM Quantization", How
  * it works): dense words packed_d uint32 [N, ceil(K*b/32)] and scales_d bf16
- * [N, K/128] -> out_d, wq_repacked_bytes(layout, ...) bytes, in `layout`
- * (only WQ_LAYOUT_TILED is a repack target).  Inputs are not modified. */
+ * [N, K/group] -> out_d, wq_repacked_bytes(layout, ...) bytes, in `layout`
+ * (only WQ_LAYOUT_TILED is a repack target).  With group = K (per-channel)
+ * the row's scale is written into every group of the blob.  Inputs are not
+ * modified. */
 int wq_repack(const uint32_t *packed_d, const uint16_t *scales_d, int64_t N, int64_t K,
               int b, int group, int layout, void *out_d, void *stream);
 
@@ -152,13 +165,16 @@ int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int g
 
 /* Device.  WNA16 layer: Y_d bf16 [M, N] = A_d bf16 [M, K] . dequant(W)^T.
  * W_d is in `layout`; scales_d bf16 [N, K/128] for WQ_LAYOUT_DENSE, NULL for
- * WQ_LAYOUT_TILED.  Accumulation is fp32 with the integer codes exact and
- * the group scale applied once per group; the output is rounded to bf16
- * (nearest even).  ws_d / ws_bytes: see wq_workspace_bytes.  Results are
- * deterministic (fixed reduction order). */
+ * WQ_LAYOUT_TILED (whose blob holds them; per-channel scales reach this
+ * layer through wq_repack with group = K, the dense layout takes group 128
+ * only).  zeros_d: NULL, or uint8 zero points [N, K/128] for b = 4 or 8.
+ * Accumulation is fp32 with the integer codes exact and the group scale
+ * applied once per group; the output is rounded to bf16 (nearest even).
+ * ws_d / ws_bytes: see wq_workspace_bytes.  Results are deterministic
+ * (fixed reduction order). */
 int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d, int layout,
-            const uint16_t *scales_d, int b, int group, uint16_t *Y_d, void *ws_d,
-            int64_t ws_bytes, void *stream);
+            const uint16_t *scales_d, const uint8_t *zeros_d, int b, int group, uint16_t *Y_d,
+            void *ws_d, int64_t ws_bytes, void *stream);
 
 /* Device.  Per-token dynamic int8 activation quantization (club-3090
  * discussion #733, "Under the hood"), fp32 throughout:
@@ -173,15 +189,18 @@ int wq_quant_act_i8(const uint16_t *A_d, int64_t M, int64_t K, int8_t *Aq_d, flo
  * needs a gather that reads the dense rows, codes straddling words; "vLLM
  * Can Run INT5-7", section 3: the vocabulary tables, 248,320 x 5,120, are
  * worth storing in INT8).  For t in [0, T), with id = ids_d[t]:
- *   Y_d[t, k] = bf16_rne(s[id, k/128] * (c[id, k] - 2^(b-1)))   if 0 <= id < V
- *   Y_d[t, k] = 0                                                otherwise
- * (ids outside the table give zero rows, as the rows of a vocabulary shard
- * that belong to other shards).  W_d: dense packed uint32 [V, ceil(K*b/32)]
- * (what wq_pack writes), scales_d bf16 [V, K/128], ids_d int64 [T], Y_d bf16
- * [T, K], all device memory owned by the caller.  The product is exact in
- * fp32 and rounded once, so the result is bit-exact.  T = 0 is a no-op. */
-int wq_embed(const void *W_d, const uint16_t *scales_d, int64_t V, int64_t K, int b, int group,
-             const int64_t *ids_d, int64_t T, uint16_t *Y_d, void *stream);
+ *   Y_d[t, k] = bf16_rne(s[id, k/group] * (c[id, k] - z[id, k/128]))   if 0 <= id < V
+ *   Y_d[t, k] = 0                                                       otherwise
+ * with z = 2^(b-1) when zeros_d is NULL (ids outside the table give zero
+ * rows, as the rows of a vocabulary shard that belong to other shards).
+ * W_d: dense packed uint32 [V, ceil(K*b/32)] (what wq_pack writes),
+ * scales_d bf16 [V, K/group] (group 128 or K), zeros_d NULL or uint8
+ * [V, K/128] (b = 4, 8), ids_d int64 [T], Y_d bf16 [T, K], all device memory
+ * owned by the caller.  The product is exact in fp32 and rounded once, so
+ * the result is bit-exact.  T = 0 is a no-op. */
+int wq_embed(const void *W_d, const uint16_t *scales_d, const uint8_t *zeros_d, int64_t V,
+             int64_t K, int b, int group, const int64_t *ids_d, int64_t T, uint16_t *Y_d,
+             void *stream);
 
 /* Device.  Int8-activation layer (same page; b = 4 is its W4A8):
  * activations quantized as wq_quant_act_i8 does, b-bit codes widened to
@@ -190,11 +209,12 @@ int wq_embed(const void *W_d, const uint16_t *scales_d, int64_t V, int64_t K, in
  * int8 products summed exactly in int32 per group of 128, then
  *   Y[m, n] = sa[m] * sum_g s[n, g] * acc_g[m, n]     (fp32)
  * written as bf16 (out_dtype WQ_OUT_BF16) or fp32 (WQ_OUT_F32).  The same
- * packed weights and scales as wq_gemm are used, any b in 2..8.  The
- * workspace holds Aq and sa. */
+ * packed weights and scales as wq_gemm are used, any b in 2..8.  Zero
+ * points (c - z) only for b = 4: at b = 8, c - z can leave the int8 range.
+ * The workspace holds Aq and sa. */
 int wq_gemm_a8(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
-               int layout, const uint16_t *scales_d, int b, int group, void *Y_d,
-               int out_dtype, void *ws_d, int64_t ws_bytes, void *stream);
+               int layout, const uint16_t *scales_d, const uint8_t *zeros_d, int b, int group,
+               void *Y_d, int out_dtype, void *ws_d, int64_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

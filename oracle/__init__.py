@@ -78,12 +78,12 @@ def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
 
 
-def _zeros(zeros, N: int, G: int):
-    """Zero points uint8 [N, G] as (array, pointer), or (None, NULL) for symmetric groups."""
+def _zeros(zeros, N: int, K: int):
+    """Zero points uint8 [N, K/128] as (array, pointer), or (None, NULL) for symmetric groups."""
     if zeros is None:
         return None, None
     z = _c(zeros, np.uint8)
-    assert z.shape == (N, G)
+    assert z.shape == (N, K // 128)
     return z, _ptr(z)
 
 
@@ -116,15 +116,15 @@ def unpack(packed: np.ndarray, K: int, b: int) -> np.ndarray:
 
 def wna16(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, b: int, group: int = 128,
           zeros=None):
-    """Return (y, mag), fp64 [M, N].  zeros: uint8 [N, K/group] zero points, or None
-    for symmetric groups (z = 2^(b-1)); group = K is per-channel."""
+    """Return (y, mag), fp64 [M, N].  zeros: uint8 [N, K/128] zero points, or None
+    for symmetric groups (z = 2^(b-1)); group = K is per-channel scales."""
     A = _c(A, np.uint16)
     packed = _c(packed, np.uint32)
     scales = _c(scales, np.uint16)
     M, K = A.shape
     N = packed.shape[0]
     assert packed.shape[1] == words_per_row(K, b) and scales.shape == (N, K // group)
-    z, zp = _zeros(zeros, N, K // group)
+    z, zp = _zeros(zeros, N, K)
     y = np.empty((M, N), dtype=np.float64)
     mag = np.empty((M, N), dtype=np.float64)
     r = _load().oracle_wna16(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), zp, b, group,
@@ -144,7 +144,7 @@ def wna16_points(A, packed, scales, b, m_idx, n_idx, group: int = 128, zeros=Non
     N = packed.shape[0]
     assert packed.shape[1] == words_per_row(K, b) and scales.shape == (N, K // group)
     P = m_idx.size
-    z, zp = _zeros(zeros, N, K // group)
+    z, zp = _zeros(zeros, N, K)
     y = np.empty(P, dtype=np.float64)
     mag = np.empty(P, dtype=np.float64)
     r = _load().oracle_wna16_points(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), zp, b, group,
@@ -169,7 +169,7 @@ def embed(packed: np.ndarray, scales: np.ndarray, K: int, b: int, ids, group: in
     ids = _c(ids, np.int64).ravel()
     V = packed.shape[0]
     assert packed.shape[1] == words_per_row(K, b) and scales.shape == (V, K // group)
-    z, zp = _zeros(zeros, V, K // group)
+    z, zp = _zeros(zeros, V, K)
     out = np.empty((ids.size, K), dtype=np.uint16)
     r = _load().oracle_embed(_ptr(packed), _ptr(scales), zp, V, K, b, group, _ptr(ids), ids.size,
                              _ptr(out))
@@ -198,7 +198,7 @@ def w4a8(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, group: int = 128
     M, K = A.shape
     N = packed.shape[0]
     assert packed.shape[1] == words_per_row(K, b) and scales.shape == (N, K // group)
-    z, zp = _zeros(zeros, N, K // group)
+    z, zp = _zeros(zeros, N, K)
     Aq = np.empty((M, K), dtype=np.int8)
     sa = np.empty(M, dtype=np.float32)
     y = np.empty((M, N), dtype=np.float64)
@@ -220,7 +220,7 @@ def w4a8_points(Aq, sa, packed, scales, m_idx, n_idx, group: int = 128, b: int =
     M, K = Aq.shape
     N = packed.shape[0]
     P = m_idx.size
-    z, zp = _zeros(zeros, N, K // group)
+    z, zp = _zeros(zeros, N, K)
     y = np.empty(P, dtype=np.float64)
     mag = np.empty(P, dtype=np.float64)
     r = _load().oracle_w4a8_points(_ptr(Aq), _ptr(sa), M, N, K, _ptr(packed), _ptr(scales),

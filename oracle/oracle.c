@@ -37,9 +37,9 @@
  *    asymmetric (zero-point) form exists for 4 and 8 bits only; "vLLM
  *    Quantization" (online shorthands) lists INT8 weights with one scale
  *    per channel.  Reading taken: a zero point is an unsigned integer z per
- *    (row, group) with the code's range, q = c - z replacing c - 2^(b-1)
- *    (zeros == NULL is the symmetric case); a per-channel scale is the
- *    group size K (one group per row).
+ *    (row, 128 codes) with the code's range, q = c - z replacing c - 2^(b-1)
+ *    (zeros == NULL is the symmetric case), whatever the scale grouping; a
+ *    per-channel scale is the group size K (one scale per row).
  *
  *  - Quantized embedding gather.  Same model card, Findings: an embedding
  *    table in this dense layout needs a gather that reads the dense rows
@@ -154,19 +154,20 @@ int oracle_unpack(const uint32_t *packed, int64_t N, int64_t K, int b, uint8_t *
     return 0;
 }
 
-/* Zero point of (row n, group g): zeros[n, g], or 2^(b-1) when zeros is NULL. */
-static int zero_point(const uint8_t *zeros, int64_t n, int64_t G, int64_t g, int b) {
-    return zeros ? (int)zeros[n * G + g] : 1 << (b - 1);
+/* Zero point of row n at code k: zeros[n, k/128] ([N, K/128]), or 2^(b-1)
+ * when zeros is NULL. */
+static int zero_point(const uint8_t *zeros, int64_t n, int64_t K, int64_t k, int b) {
+    return zeros ? (int)zeros[n * (K / 128) + k / 128] : 1 << (b - 1);
 }
 
-/* Row n dequantized to fp64: w[k] = s[n, k/group] * (c[n,k] - z[n, k/group]). */
+/* Row n dequantized to fp64: w[k] = s[n, k/group] * (c[n,k] - z[n, k/128]). */
 static void dequant_row(const uint32_t *packed, const uint16_t *scales, const uint8_t *zeros,
                         int64_t n, int64_t K, int b, int group, double *w) {
     const int64_t W = oracle_words_per_row(K, b);
     const int64_t G = K / group;
     const uint8_t *row = (const uint8_t *)(packed + n * W);
     for (int64_t k = 0; k < K; ++k) {
-        const int q = (int)read_code(row, k, b) - zero_point(zeros, n, G, k / group, b);
+        const int q = (int)read_code(row, k, b) - zero_point(zeros, n, K, k, b);
         w[k] = bf16_to_double(scales[n * G + k / group]) * (double)q;
     }
 }
@@ -309,18 +310,19 @@ int oracle_quant_act_i8(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq, flo
 }
 
 /* One int8-activation output from an already quantized activation row:
- * y = s_a * sum_g s[n,g] * (sum_{k in g} Aq[k] * (c[n,k] - z[n,g])),
+ * y = s_a * sum_g s[n,g] * (sum_{k in g} Aq[k] * (c[n,k] - z[n,k/128])),
  * with the inner sums exact in int64 (they must fit int32) and the rest fp64.
- * z_row is row n of the zero points (NULL: 2^(b-1)). */
+ * z_row is row n of the zero points, [K/128] (NULL: 2^(b-1)). */
 static int w4a8_dot(const int8_t *aq_row, float sa, const uint8_t *codes_row, int b,
                     const uint16_t *s_row, const uint8_t *z_row, int64_t K, int group,
                     double *y, double *mag) {
     double acc = 0.0, acc_abs = 0.0;
     for (int64_t g = 0; g < K / group; ++g) {
-        const int64_t zero = z_row ? (int64_t)z_row[g] : (int64_t)1 << (b - 1);
         int64_t ig = 0;
-        for (int64_t k = g * group; k < (g + 1) * group; ++k)
+        for (int64_t k = g * group; k < (g + 1) * group; ++k) {
+            const int64_t zero = z_row ? (int64_t)z_row[k / 128] : (int64_t)1 << (b - 1);
             ig += (int64_t)aq_row[k] * ((int64_t)codes_row[k] - zero);
+        }
         if (ig > INT32_MAX || ig < INT32_MIN) return -3;
         const double t = bf16_to_double(s_row[g]) * (double)ig;
         acc += t;
@@ -359,7 +361,7 @@ int oracle_w4a8(const uint16_t *A, int64_t M, int64_t N, int64_t K,
             unpack_row(packed, n, K, b, c);
             for (int64_t m = 0; m < M; ++m) {
                 int r = w4a8_dot(Aq + m * K, sa[m], c, b, scales + n * G,
-                                 zeros ? zeros + n * G : NULL, K, group,
+                                 zeros ? zeros + n * (K / 128) : NULL, K, group,
                                  &y[m * N + n], mag ? &mag[m * N + n] : NULL);
                 if (r) {
 #pragma omp atomic write
@@ -395,7 +397,7 @@ int oracle_w4a8_points(const int8_t *Aq, const float *sa, int64_t M, int64_t N, 
             }
             unpack_row(packed, n, K, b, c);
             int r = w4a8_dot(Aq + m * K, sa[m], c, b, scales + n * G,
-                             zeros ? zeros + n * G : NULL, K, group, &y[p], mag ? &mag[p] : NULL);
+                             zeros ? zeros + n * (K / 128) : NULL, K, group, &y[p], mag ? &mag[p] : NULL);
             if (r) {
 #pragma omp atomic write
                 err = r;

@@ -19,11 +19,11 @@ def test_library_exports_every_declared_function():
     assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
-    assert wq.wq_abi_version() == 1
+    assert wq.wq_abi_version() == 2
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(11):
         assert wq.wq_status_str(s) != "unknown status"
     assert wq.wq_status_str(99) == "unknown status"
     assert "2..8" in wq.wq_status_str(wq.WQ_ERR_UNSUPPORTED_BITS)
@@ -87,11 +87,11 @@ MISALIGNED = ALIGNED + 8
 
 
 def _gemm(A=ALIGNED, M=1, N=256, K=512, W=ALIGNED, layout=wq.WQ_LAYOUT_TILED, S=None, b=6,
-          group=128, Y=ALIGNED, ws=ALIGNED, ws_bytes=1 << 30):
+          group=128, Y=ALIGNED, ws=ALIGNED, ws_bytes=1 << 30, Z=None):
     lib = wq._load()
     c = ctypes.c_void_p
-    return lib.wq_gemm(c(A), M, N, K, c(W), layout, c(S) if S else None, b, group, c(Y),
-                       c(ws) if ws else None, ws_bytes, None)
+    return lib.wq_gemm(c(A), M, N, K, c(W), layout, c(S) if S else None, c(Z) if Z else None, b,
+                       group, c(Y), c(ws) if ws else None, ws_bytes, None)
 
 
 def test_gemm_validation_statuses():
@@ -110,6 +110,20 @@ def test_gemm_validation_statuses():
     assert _gemm(W=MISALIGNED) == wq.WQ_ERR_MISALIGNED
     assert _gemm(Y=MISALIGNED) == wq.WQ_ERR_MISALIGNED
     assert _gemm(M=0, A=0, W=0, Y=0) == wq.WQ_OK                             # empty batch: no-op
+
+
+def test_zero_point_and_per_channel_statuses():
+    # Zero points only for b = 4 and 8; per-channel scales (group = K) only
+    # through the tiled layout on the GEMM path.
+    for b in (2, 3, 5, 6, 7):
+        assert _gemm(b=b, Z=ALIGNED) == wq.WQ_ERR_ZERO_POINTS
+    assert _gemm(b=4, Z=MISALIGNED) == wq.WQ_ERR_MISALIGNED
+    assert _gemm(b=4, Z=ALIGNED, M=0, A=0, W=0, Y=0) == wq.WQ_OK
+    assert _gemm(group=512, K=512, layout=wq.WQ_LAYOUT_DENSE, S=ALIGNED) == wq.WQ_ERR_BAD_GROUP
+    assert _gemm(group=512, K=512, M=0, A=0, W=0, Y=0) == wq.WQ_OK           # tiled: accepted
+    assert _gemm(group=256, K=512) == wq.WQ_ERR_BAD_GROUP                    # neither 128 nor K
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, 17408, 5120, 6, 5120) > 0
+    assert "b = 4 or 8" in wq.wq_status_str(wq.WQ_ERR_ZERO_POINTS)
 
 
 def test_gemm_workspace_checks():
@@ -131,12 +145,15 @@ def test_gemm_a8_refuses_bad_widths_and_bad_output():
     c = ctypes.c_void_p
     A = c(ALIGNED)
     for b in (0, 1, 9, 16):
-        assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, b, 128, A, 0, A, 1 << 30, None) == \
+        assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, None, b, 128, A, 0, A, 1 << 30, None) == \
             wq.WQ_ERR_UNSUPPORTED_BITS
-    assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, 4, 128, A, 7, A, 1 << 30, None) == \
+    assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, None, 4, 128, A, 7, A, 1 << 30, None) == \
         wq.WQ_ERR_INVALID_ARG
-    assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, 4, 128, A, 0, None, 0, None) == \
+    assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, None, 4, 128, A, 0, None, 0, None) == \
         wq.WQ_ERR_WORKSPACE
+    # zero points on the int8 path: b = 4 only (c - z must fit int8)
+    assert lib.wq_gemm_a8(A, 8, 256, 512, A, 1, None, A, 8, 128, A, 0, A, 1 << 30, None) == \
+        wq.WQ_ERR_ZERO_POINTS
 
 
 def test_repack_and_unpack_dev_validation():
@@ -157,18 +174,20 @@ def test_embed_validation():
     c = ctypes.c_void_p
     A = c(ALIGNED)
     V, K = 1000, 512
-    assert lib.wq_embed(A, A, V, K, 9, 128, A, 4, A, None) == wq.WQ_ERR_UNSUPPORTED_BITS
-    assert lib.wq_embed(A, A, V, K, 1, 128, A, 4, A, None) == wq.WQ_ERR_UNSUPPORTED_BITS
-    assert lib.wq_embed(A, A, V, 500, 6, 128, A, 4, A, None) == wq.WQ_ERR_BAD_GROUP
-    assert lib.wq_embed(A, A, V, K, 6, 64, A, 4, A, None) == wq.WQ_ERR_BAD_GROUP
-    assert lib.wq_embed(A, A, 0, K, 6, 128, A, 4, A, None) == wq.WQ_ERR_INVALID_ARG
-    assert lib.wq_embed(A, A, V, K, 6, 128, A, -1, A, None) == wq.WQ_ERR_INVALID_ARG
-    assert lib.wq_embed(A, A, V, K, 6, 128, A, 1 << 31, A, None) == wq.WQ_ERR_INVALID_ARG
-    assert lib.wq_embed(A, A, V, K, 6, 128, None, 4, A, None) == wq.WQ_ERR_INVALID_ARG
-    assert lib.wq_embed(A, A, V, K, 6, 128, c(MISALIGNED), 4, A, None) == wq.WQ_ERR_MISALIGNED
-    assert lib.wq_embed(A, A, V, K, 6, 128, A, 4, c(MISALIGNED), None) == wq.WQ_ERR_MISALIGNED
+    assert lib.wq_embed(A, A, None, V, K, 9, 128, A, 4, A, None) == wq.WQ_ERR_UNSUPPORTED_BITS
+    assert lib.wq_embed(A, A, None, V, K, 1, 128, A, 4, A, None) == wq.WQ_ERR_UNSUPPORTED_BITS
+    assert lib.wq_embed(A, A, None, V, 500, 6, 128, A, 4, A, None) == wq.WQ_ERR_BAD_GROUP
+    assert lib.wq_embed(A, A, None, V, K, 6, 64, A, 4, A, None) == wq.WQ_ERR_BAD_GROUP
+    assert lib.wq_embed(A, A, None, 0, K, 6, 128, A, 4, A, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_embed(A, A, None, V, K, 6, 128, A, -1, A, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_embed(A, A, None, V, K, 6, 128, A, 1 << 31, A, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_embed(A, A, None, V, K, 6, 128, None, 4, A, None) == wq.WQ_ERR_INVALID_ARG
+    assert lib.wq_embed(A, A, None, V, K, 6, 128, c(MISALIGNED), 4, A, None) == wq.WQ_ERR_MISALIGNED
+    assert lib.wq_embed(A, A, None, V, K, 6, 128, A, 4, c(MISALIGNED), None) == wq.WQ_ERR_MISALIGNED
+    assert lib.wq_embed(A, A, A, V, K, 6, 128, A, 4, A, None) == wq.WQ_ERR_ZERO_POINTS
+    assert lib.wq_embed(A, A, None, V, K, 6, K, None, 4, A, None) == wq.WQ_ERR_INVALID_ARG
     # an empty batch is a no-op, even without buffers
-    assert lib.wq_embed(None, None, V, K, 6, 128, None, 0, None, None) == wq.WQ_OK
+    assert lib.wq_embed(None, None, None, V, K, 6, 128, None, 0, None, None) == wq.WQ_OK
 
 
 def test_repacked_sizes():

@@ -548,6 +548,11 @@ def test_per_channel_scale_is_the_replicated_group_scale(b):
     y_g, mag_g = oracle.wna16(A, packed, np.repeat(s1, K // 128, axis=1), b)
     np.testing.assert_array_equal(y_pc, y_g)
     np.testing.assert_array_equal(mag_pc, mag_g)
+    if b in (4, 8):  # zero points stay per 128 codes under a per-channel scale
+        z = rng.integers(0, 1 << b, size=(N, K // 128), dtype=np.uint8)
+        y_pc, _ = oracle.wna16(A, packed, s1, b, group=K, zeros=z)
+        y_g, _ = oracle.wna16(A, packed, np.repeat(s1, K // 128, axis=1), b, zeros=z)
+        np.testing.assert_array_equal(y_pc, y_g)
 
 
 def test_embed_zero_points_and_per_channel_closed_form():

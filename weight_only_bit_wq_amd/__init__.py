@@ -43,6 +43,7 @@ WQ_ERR_WORKSPACE = 6
 WQ_ERR_BAD_LAYOUT = 7
 WQ_ERR_UNSUPPORTED_DEVICE = 8
 WQ_ERR_HIP = 9
+WQ_ERR_ZERO_POINTS = 10
 
 WQ_LAYOUT_DENSE = 0
 WQ_LAYOUT_TILED = 1
@@ -98,10 +99,10 @@ def _load():
             "wq_repack": ([P, P, L, L, I, I, I, P, P], I),
             "wq_unpack_dev": ([P, I, L, L, I, I, P, P], I),
             "wq_workspace_bytes": ([I, L, L, L, I, I], L),
-            "wq_gemm": ([P, L, L, L, P, I, P, I, I, P, P, L, P], I),
+            "wq_gemm": ([P, L, L, L, P, I, P, P, I, I, P, P, L, P], I),
             "wq_quant_act_i8": ([P, L, L, P, P, P], I),
-            "wq_gemm_a8": ([P, L, L, L, P, I, P, I, I, P, I, P, L, P], I),
-            "wq_embed": ([P, P, L, L, I, I, P, L, P, P], I),
+            "wq_gemm_a8": ([P, L, L, L, P, I, P, P, I, I, P, I, P, L, P], I),
+            "wq_embed": ([P, P, P, L, L, I, I, P, L, P, P], I),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -199,7 +200,8 @@ def wq_repacked_bytes(layout: int, N: int, K: int, b: int, group: int = GROUP) -
 
 def wq_repack(packed_d, scales_d, K: int, b: int, group: int = GROUP,
               layout: int = WQ_LAYOUT_TILED, out=None, stream=None):
-    """Device: dense words (int32/uint32 [N, W]) + bf16 scales [N, K/128] -> blob (uint8)."""
+    """Device: dense words (int32/uint32 [N, W]) + bf16 scales [N, K/group] -> blob (uint8).
+    group = K (per-channel scales [N, 1]) writes the row's scale into every group."""
     import torch
     N = packed_d.shape[0]
     _require_cuda("packed_d", packed_d, (torch.int32, torch.uint32),
@@ -251,15 +253,23 @@ def _workspace(nbytes: int, device, stream):
     return buf, buf.numel()
 
 
+def _require_zeros(zeros_d, N: int, K: int):
+    if zeros_d is not None:
+        import torch
+        _require_cuda("zeros_d", zeros_d, torch.uint8, (N, K // GROUP))
+
+
 def wq_gemm(A_d, W_d, layout: int, scales_d, N: int, b: int, group: int = GROUP, Y=None,
-            ws=None, stream=None):
-    """Device: Y bf16 [M, N] = A_d bf16 [M, K] . dequant(W)^T."""
+            ws=None, stream=None, zeros=None):
+    """Device: Y bf16 [M, N] = A_d bf16 [M, K] . dequant(W)^T.  zeros: optional
+    uint8 zero points [N, K/128] (b = 4 or 8)."""
     import torch
     _require_cuda("A_d", A_d, torch.bfloat16)
     _require_cuda("W_d", W_d)
     M, K = A_d.shape
     if scales_d is not None:
         _require_cuda("scales_d", scales_d, (torch.bfloat16, torch.int16), (N, K // group))
+    _require_zeros(zeros, N, K)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=A_d.device)
     else:
@@ -270,8 +280,8 @@ def wq_gemm(A_d, W_d, layout: int, scales_d, N: int, b: int, group: int = GROUP,
         ws_buf, ws_bytes = _workspace(need, A_d.device, st)
     else:
         ws_buf, ws_bytes = ws, ws.numel() * ws.element_size()
-    _check("wq_gemm", _load().wq_gemm(_ptr(A_d), M, N, K, _ptr(W_d), layout, _ptr(scales_d), b,
-                                      group, _ptr(Y), _ptr(ws_buf), ws_bytes, st))
+    _check("wq_gemm", _load().wq_gemm(_ptr(A_d), M, N, K, _ptr(W_d), layout, _ptr(scales_d),
+                                      _ptr(zeros), b, group, _ptr(Y), _ptr(ws_buf), ws_bytes, st))
     return Y
 
 
@@ -289,33 +299,38 @@ def wq_quant_act_i8(A_d, Aq=None, sa=None, stream=None):
     return Aq, sa
 
 
-def wq_embed(ids_d, W_d, scales_d, K: int, b: int, group: int = GROUP, Y=None, stream=None):
+def wq_embed(ids_d, W_d, scales_d, K: int, b: int, group: int = GROUP, Y=None, stream=None,
+             zeros=None):
     """Device: quantized embedding gather from the dense layout -> bf16 [T, K]
-    (rows of ids outside [0, V) are zero)."""
+    (rows of ids outside [0, V) are zero).  group 128 or K (per-channel
+    scales); zeros: optional uint8 zero points [V, K/128] (b = 4 or 8)."""
     import torch
     _require_cuda("ids_d", ids_d, torch.int64)
     V = W_d.shape[0]
     _require_cuda("W_d", W_d, (torch.int32, torch.uint32), (V, wq_packed_words_per_row(K, b)))
     _require_cuda("scales_d", scales_d, (torch.bfloat16, torch.int16), (V, K // group))
+    _require_zeros(zeros, V, K)
     T = ids_d.numel()
     if Y is None:
         Y = torch.empty((T, K), dtype=torch.bfloat16, device=W_d.device)
     else:
         _require_cuda("Y", Y, torch.bfloat16, (T, K))
-    _check("wq_embed", _load().wq_embed(_ptr(W_d), _ptr(scales_d), V, K, b, group, _ptr(ids_d),
-                                        T, _ptr(Y), _stream(stream)))
+    _check("wq_embed", _load().wq_embed(_ptr(W_d), _ptr(scales_d), _ptr(zeros), V, K, b, group,
+                                        _ptr(ids_d), T, _ptr(Y), _stream(stream)))
     return Y
 
 
 def wq_gemm_a8(A_d, W_d, layout: int, scales_d, N: int, b: int = 4, group: int = GROUP,
-               out_dtype: int = WQ_OUT_BF16, Y=None, ws=None, stream=None):
-    """Device: int8-activation layer on b-bit weights (b = 4: W4A8) -> Y [M, N] (bf16 or float32)."""
+               out_dtype: int = WQ_OUT_BF16, Y=None, ws=None, stream=None, zeros=None):
+    """Device: int8-activation layer on b-bit weights (b = 4: W4A8) -> Y [M, N]
+    (bf16 or float32).  zeros: optional uint8 zero points [N, K/128] (b = 4)."""
     import torch
     _require_cuda("A_d", A_d, torch.bfloat16)
     _require_cuda("W_d", W_d)
     M, K = A_d.shape
     if scales_d is not None:
         _require_cuda("scales_d", scales_d, (torch.bfloat16, torch.int16), (N, K // group))
+    _require_zeros(zeros, N, K)
     ydt = torch.float32 if out_dtype == WQ_OUT_F32 else torch.bfloat16
     if Y is None:
         Y = torch.empty((M, N), dtype=ydt, device=A_d.device)
@@ -328,6 +343,6 @@ def wq_gemm_a8(A_d, W_d, layout: int, scales_d, N: int, b: int = 4, group: int =
     else:
         ws_buf, ws_bytes = ws, ws.numel() * ws.element_size()
     _check("wq_gemm_a8", _load().wq_gemm_a8(_ptr(A_d), M, N, K, _ptr(W_d), layout,
-                                            _ptr(scales_d), b, group, _ptr(Y), out_dtype,
-                                            _ptr(ws_buf), ws_bytes, st))
+                                            _ptr(scales_d), _ptr(zeros), b, group, _ptr(Y),
+                                            out_dtype, _ptr(ws_buf), ws_bytes, st))
     return Y

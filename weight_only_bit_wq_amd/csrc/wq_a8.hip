@@ -29,6 +29,12 @@
 // then shifted and XOR-ed (b = 8: the code bytes XOR 0x80).  The k order is
 // the natural one for b != 4, and the activations are written in it.
 // Group sums stay exact: |Aq| <= 127, |w * 2^(8-b)| <= 128, 128 terms.
+//
+// Zero points (b = 4 only: at b = 8, c - z can leave the int8 range): the
+// nibbles go to the low half of their bytes (even and odd codes apart, the
+// same k order), and ((c | 0x80) - z) ^ 0x80 per byte is the int8 c - z
+// (128 + c - z lies in 113..143, so no byte borrows from its neighbour); the
+// group scale is s itself.
 #include "wq_device.h"
 #include "wq_launch.h"
 
@@ -179,10 +185,12 @@ __device__ __forceinline__ int a8_swz(int row, int chunk) { return row * 8 + (ch
 // The fold runs one row block behind the group's last MFMAs (row 3 during
 // the next group's first k-step), one block per MFMA, so it issues in the
 // matrix core's shadow.
-template <class WL, int B>
+template <class WL, int B, bool ZP>
 __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__ Aq,
                                                       const float *__restrict__ sa, int M, int N,
-                                                      int K, WL wl, void *__restrict__ Y,
+                                                      int K, WL wl,
+                                                      const uint8_t *__restrict__ zeros,
+                                                      void *__restrict__ Y,
                                                       bool out_f32, int mtiles, int ntiles) {
     __shared__ u32x4 Asm[2][kABM * 8];  // 2 x 32 KB
     __shared__ u32x4 Bsm[2][kABN * 8];  // 2 x 16 KB
@@ -224,6 +232,7 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
     const uint8_t *bscale0 = wl.scale0(bn_read);
     const int bstep = (int)wl.slot_step();
     const int sstep = (int)wl.scale_step();
+    const uint8_t *zrow = ZP ? zeros + bn_read * G : nullptr;  // zero points [N, G]
 
     // MFMA operand rows and k-chunk of this lane.
     const int arow = wm * 64 + (lane & 15);
@@ -233,6 +242,7 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
     u32x4 areg[4];
     uint32_t breg[B];
     uint16_t sreg;
+    uint32_t zreg = 0;
     i32x4_t P[4][4];
     f32x4_t tot[4][4];
 #pragma unroll
@@ -251,11 +261,23 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
             areg[i] = *reinterpret_cast<const u32x4 *>(src + (int64_t)arows[i] * K);
         load_quarter<WL, B>(bslot0 + (int64_t)g * bstep, bj, breg);
         sreg = *reinterpret_cast<const uint16_t *>(bscale0 + (int64_t)g * sstep);
+        if constexpr (ZP) zreg = zrow[g];
     };
     auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) Asm[buf][a_lds + 512 * i] = areg[i];
-        if constexpr (B == 4) {
+        if constexpr (ZP) {  // b = 4: int8 c - z, codes ordered as below
+            const u32x4 x = u32x4{breg[0], breg[1], breg[2], breg[3]};
+            const uint32_t zb = zreg * 0x01010101u;
+            auto lo = [&](uint32_t v) {
+                return (((v & 0x0F0F0F0Fu) | 0x80808080u) - zb) ^ 0x80808080u;
+            };
+            auto hi = [&](uint32_t v) {
+                return ((((v >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zb) ^ 0x80808080u;
+            };
+            Bsm[buf][a8_swz(brow, 2 * bj)] = u32x4{lo(x.x), hi(x.x), lo(x.y), hi(x.y)};
+            Bsm[buf][a8_swz(brow, 2 * bj + 1)] = u32x4{lo(x.z), hi(x.z), lo(x.w), hi(x.w)};
+        } else if constexpr (B == 4) {
             const u32x4 x = u32x4{breg[0], breg[1], breg[2], breg[3]} ^ 0x88888888u;
             Bsm[buf][a8_swz(brow, 2 * bj)] =
                 u32x4{(x.x << 4) & 0xF0F0F0F0u, x.x & 0xF0F0F0F0u, (x.y << 4) & 0xF0F0F0F0u,
@@ -270,7 +292,7 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
                                                        widen4<B, 6>(breg), widen4<B, 7>(breg)};
         }
         // The four chunk waves of a row store the same value: no branch.
-        Ss[buf][brow] = bf16_to_f32(sreg) * (1.0f / (float)(1 << (8 - B)));
+        Ss[buf][brow] = bf16_to_f32(sreg) * (ZP ? 1.0f : 1.0f / (float)(1 << (8 - B)));
     };
     auto fold_block = [&](int i, int j, const float(&sq)[4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -349,29 +371,30 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
         }
 }
 
-template <int B>
+template <int B, bool ZP>
 static hipError_t launch_gemm_a8_b(const int8_t *Aq, const float *sa, int64_t M, int64_t N,
                                    int64_t K, const void *W, bool tiled, const uint16_t *scales,
-                                   void *Y, bool out_f32, hipStream_t stream) {
+                                   const uint8_t *zeros, void *Y, bool out_f32,
+                                   hipStream_t stream) {
     const int G = (int)(K / kGroup);
     const int mtiles = (int)((M + kABM - 1) / kABM);
     const int ntiles = (int)((N + kABN - 1) / kABN);
     const dim3 grid((unsigned)(mtiles * ntiles));
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W), G, B};
-        hipLaunchKernelGGL((gemm_a8_kernel<TiledW, B>), grid, dim3(512), 0, stream, Aq, sa,
-                           (int)M, (int)N, (int)K, wl, Y, out_f32, mtiles, ntiles);
+        hipLaunchKernelGGL((gemm_a8_kernel<TiledW, B, ZP>), grid, dim3(512), 0, stream, Aq, sa,
+                           (int)M, (int)N, (int)K, wl, zeros, Y, out_f32, mtiles, ntiles);
     } else {
         DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
-        hipLaunchKernelGGL((gemm_a8_kernel<DenseW, B>), grid, dim3(512), 0, stream, Aq, sa,
-                           (int)M, (int)N, (int)K, wl, Y, out_f32, mtiles, ntiles);
+        hipLaunchKernelGGL((gemm_a8_kernel<DenseW, B, ZP>), grid, dim3(512), 0, stream, Aq, sa,
+                           (int)M, (int)N, (int)K, wl, zeros, Y, out_f32, mtiles, ntiles);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                          bool tiled, const uint16_t *scales, int b, void *Y, bool out_f32,
-                          void *ws, hipStream_t stream) {
+                          bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
+                          void *Y, bool out_f32, void *ws, hipStream_t stream) {
     int8_t *Aq = reinterpret_cast<int8_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
     float *sa = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset +
                                           align256(M * K));
@@ -384,14 +407,33 @@ hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, co
                            (int)K, Aq, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (zeros) {  // b = 4 only (checked at the boundary)
+        if (b != 4) return hipErrorInvalidValue;
+        return launch_gemm_a8_b<4, true>(Aq, sa, M, N, K, W, tiled, scales, zeros, Y, out_f32,
+                                         stream);
+    }
     switch (b) {
-        case 2: return launch_gemm_a8_b<2>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
-        case 3: return launch_gemm_a8_b<3>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
-        case 4: return launch_gemm_a8_b<4>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
-        case 5: return launch_gemm_a8_b<5>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
-        case 6: return launch_gemm_a8_b<6>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
-        case 7: return launch_gemm_a8_b<7>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
-        case 8: return launch_gemm_a8_b<8>(Aq, sa, M, N, K, W, tiled, scales, Y, out_f32, stream);
+        case 2:
+            return launch_gemm_a8_b<2, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
+                                              out_f32, stream);
+        case 3:
+            return launch_gemm_a8_b<3, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
+                                              out_f32, stream);
+        case 4:
+            return launch_gemm_a8_b<4, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
+                                              out_f32, stream);
+        case 5:
+            return launch_gemm_a8_b<5, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
+                                              out_f32, stream);
+        case 6:
+            return launch_gemm_a8_b<6, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
+                                              out_f32, stream);
+        case 7:
+            return launch_gemm_a8_b<7, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
+                                              out_f32, stream);
+        case 8:
+            return launch_gemm_a8_b<8, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
+                                              out_f32, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -32,8 +32,19 @@ bool valid_bits(int b) { return b >= 2 && b <= 8; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Groups of 128 codes, or one group per row (per-channel scales, group = K).
 int check_group(int64_t K, int group) {
-    if (group != kGroup || K % kGroup != 0) return WQ_ERR_BAD_GROUP;
+    if (K % kGroup != 0 || (group != kGroup && group != K)) return WQ_ERR_BAD_GROUP;
+    return WQ_OK;
+}
+
+bool per_channel(int64_t K, int group) { return group == K && K != kGroup; }
+
+// Zero points exist for b = 4 and 8 (for b = 4 only on the int8-activation path).
+int check_zeros(const uint8_t *zeros, int b, bool a8) {
+    if (!zeros) return WQ_OK;
+    if (b != 4 && (b != 8 || a8)) return WQ_ERR_ZERO_POINTS;
+    if (!aligned16(zeros)) return WQ_ERR_MISALIGNED;
     return WQ_OK;
 }
 
@@ -103,13 +114,14 @@ const char *wq_status_str(int status) {
         case WQ_OK: return "ok";
         case WQ_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive N or K, negative M, or unknown enum value)";
         case WQ_ERR_UNSUPPORTED_BITS: return "unsupported bit width: b must be in 2..8";
-        case WQ_ERR_BAD_GROUP: return "group must be 128 and divide K";
+        case WQ_ERR_BAD_GROUP: return "group must be 128 or K, with K a multiple of 128; per-channel scales (group K) reach a GEMM through wq_repack (tiled layout)";
         case WQ_ERR_MISALIGNED: return "device pointer is not 16-byte aligned";
         case WQ_ERR_CODE_RANGE: return "a code does not fit in b bits (codes are refused, never masked)";
         case WQ_ERR_WORKSPACE: return "workspace missing or smaller than wq_workspace_bytes()";
         case WQ_ERR_BAD_LAYOUT: return "bad layout: unknown value, repack target not TILED, or scales_d given with TILED / missing with DENSE";
         case WQ_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950 (MI355X)";
         case WQ_ERR_HIP: return "HIP runtime or kernel launch error (see wq_last_hip_error)";
+        case WQ_ERR_ZERO_POINTS: return "zero points need b = 4 or 8 (b = 4 on the int8-activation path, where c - z must fit int8)";
     }
     return "unknown status";
 }
@@ -200,7 +212,8 @@ int wq_repack(const uint32_t *packed_d, const uint16_t *scales_d, int64_t N, int
     if (layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
     if (!aligned16(packed_d) || !aligned16(scales_d) || !aligned16(out_d)) return WQ_ERR_MISALIGNED;
     if (int s = check_device()) return s;
-    hipError_t e = wq::launch_repack_tiled(packed_d, scales_d, N, K, b, out_d, (hipStream_t)stream);
+    hipError_t e = wq::launch_repack_tiled(packed_d, scales_d, N, K, b, per_channel(K, group),
+                                           out_d, (hipStream_t)stream);
     return e == hipSuccess ? WQ_OK : hip_fail(e);
 }
 
@@ -217,18 +230,21 @@ int wq_unpack_dev(const void *W_d, int layout, int64_t N, int64_t K, int b, int 
     return e == hipSuccess ? WQ_OK : hip_fail(e);
 }
 
-int wq_embed(const void *W_d, const uint16_t *scales_d, int64_t V, int64_t K, int b, int group,
-             const int64_t *ids_d, int64_t T, uint16_t *Y_d, void *stream) {
+int wq_embed(const void *W_d, const uint16_t *scales_d, const uint8_t *zeros_d, int64_t V,
+             int64_t K, int b, int group, const int64_t *ids_d, int64_t T, uint16_t *Y_d,
+             void *stream) {
     if (!dims_ok(0, V, K) || T < 0 || T >= (1ll << 31)) return WQ_ERR_INVALID_ARG;
     if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
     if (int s = check_group(K, group)) return s;
+    if (int s = check_zeros(zeros_d, b, false)) return s;
     if (T * ((K / 8 + 127) / 128) >= (1ll << 32)) return WQ_ERR_INVALID_ARG;  // grid size
     if (T == 0) return WQ_OK;
     if (!W_d || !scales_d || !ids_d || !Y_d) return WQ_ERR_INVALID_ARG;
     if (!aligned16(W_d) || !aligned16(scales_d) || !aligned16(ids_d) || !aligned16(Y_d))
         return WQ_ERR_MISALIGNED;
     if (int s = check_device()) return s;
-    hipError_t e = wq::launch_embed(W_d, scales_d, V, K, b, ids_d, T, Y_d, (hipStream_t)stream);
+    hipError_t e = wq::launch_embed(W_d, scales_d, zeros_d, per_channel(K, group), V, K, b, ids_d,
+                                    T, Y_d, (hipStream_t)stream);
     return e == hipSuccess ? WQ_OK : hip_fail(e);
 }
 
@@ -240,13 +256,15 @@ int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int g
 }
 
 int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d, int layout,
-            const uint16_t *scales_d, int b, int group, uint16_t *Y_d, void *ws_d,
-            int64_t ws_bytes, void *stream) {
+            const uint16_t *scales_d, const uint8_t *zeros_d, int b, int group, uint16_t *Y_d,
+            void *ws_d, int64_t ws_bytes, void *stream) {
     if (!dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
     if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
     if (int s = check_group(K, group)) return s;
     if (layout != WQ_LAYOUT_DENSE && layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
     if ((layout == WQ_LAYOUT_DENSE) != (scales_d != nullptr)) return WQ_ERR_BAD_LAYOUT;
+    if (layout == WQ_LAYOUT_DENSE && per_channel(K, group)) return WQ_ERR_BAD_GROUP;
+    if (int s = check_zeros(zeros_d, b, false)) return s;
     if (M == 0) return WQ_OK;
     if (!A_d || !W_d || !Y_d) return WQ_ERR_INVALID_ARG;
     if (!aligned16(A_d) || !aligned16(W_d) || !aligned16(Y_d) ||
@@ -259,10 +277,10 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
     hipError_t e;
     if (M <= wq::kDecodeMaxM) {
         const wq::DecodePlan p = wq::decode_plan(M, N, K, b);
-        e = wq::launch_decode(A_d, M, N, K, W_d, tiled, scales_d, b, Y_d, ws_d, p,
+        e = wq::launch_decode(A_d, M, N, K, W_d, tiled, scales_d, zeros_d, b, Y_d, ws_d, p,
                               (hipStream_t)stream);
     } else {
-        e = wq::launch_prefill(A_d, M, N, K, W_d, tiled, scales_d, b, Y_d, ws_d,
+        e = wq::launch_prefill(A_d, M, N, K, W_d, tiled, scales_d, zeros_d, b, Y_d, ws_d,
                                (hipStream_t)stream);
     }
     return e == hipSuccess ? WQ_OK : hip_fail(e);
@@ -281,13 +299,15 @@ int wq_quant_act_i8(const uint16_t *A_d, int64_t M, int64_t K, int8_t *Aq_d, flo
 }
 
 int wq_gemm_a8(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
-               int layout, const uint16_t *scales_d, int b, int group, void *Y_d,
-               int out_dtype, void *ws_d, int64_t ws_bytes, void *stream) {
+               int layout, const uint16_t *scales_d, const uint8_t *zeros_d, int b, int group,
+               void *Y_d, int out_dtype, void *ws_d, int64_t ws_bytes, void *stream) {
     if (!dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
     if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
     if (int s = check_group(K, group)) return s;
     if (layout != WQ_LAYOUT_DENSE && layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
     if ((layout == WQ_LAYOUT_DENSE) != (scales_d != nullptr)) return WQ_ERR_BAD_LAYOUT;
+    if (layout == WQ_LAYOUT_DENSE && per_channel(K, group)) return WQ_ERR_BAD_GROUP;
+    if (int s = check_zeros(zeros_d, b, true)) return s;
     if (out_dtype != WQ_OUT_BF16 && out_dtype != WQ_OUT_F32) return WQ_ERR_INVALID_ARG;
     if (M == 0) return WQ_OK;
     if (!A_d || !W_d || !Y_d) return WQ_ERR_INVALID_ARG;
@@ -297,7 +317,8 @@ int wq_gemm_a8(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void 
     const int64_t need = wq::a8_ws_bytes(M, N, K);
     if (!ws_d || ws_bytes < need) return WQ_ERR_WORKSPACE;
     if (int s = check_device()) return s;
-    hipError_t e = wq::launch_gemm_a8(A_d, M, N, K, W_d, layout == WQ_LAYOUT_TILED, scales_d, b,
+    hipError_t e = wq::launch_gemm_a8(A_d, M, N, K, W_d, layout == WQ_LAYOUT_TILED, scales_d,
+                                      zeros_d, b,
                                       Y_d, out_dtype == WQ_OUT_F32, ws_d, (hipStream_t)stream);
     return e == hipSuccess ? WQ_OK : hip_fail(e);
 }

@@ -4,6 +4,6 @@
 
 namespace wq {
 template hipError_t decode_b<8>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool,
-                                const uint16_t *, uint16_t *, void *, const DecodePlan &,
-                                hipStream_t);
+                                const uint16_t *, const uint8_t *, uint16_t *, void *,
+                                const DecodePlan &, hipStream_t);
 }  // namespace wq

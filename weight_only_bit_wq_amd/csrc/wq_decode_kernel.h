@@ -35,6 +35,11 @@
 // removed and the group scale applied once in fp32:
 //     acc += s[n,g] * (sum_k a_k (128 + c_k) - (128 + 2^(b-1)) sum_k a_k)
 // which is sum_k a_k s (c_k - 2^(b-1)) with the integer codes exact.
+// Zero points (b = 4 and 8 only): for b = 4, (64 - z) is added to both
+// 16-bit halves after the exponent OR, so a pair becomes 192 + c - z exactly
+// (the mantissa 64 + c - z stays in 49..79), and the constant is 192; for
+// b = 8 the bytes convert to c - z (|c - z| <= 255, exact in bf16) and there
+// is no constant term.
 // For b = 8 codes are whole bytes: v_cvt_f32_ubyte{0..3} converts each one
 // and an fp32 FMA accumulates (offset 128).
 #pragma once
@@ -56,22 +61,23 @@ struct UVec<16> { typedef unsigned type __attribute__((ext_vector_type(16))); };
 
 // Pairs P0 + I .. P0 + CP - 1 of the group, activations already in av[]
 // (CP pairs of one row come in with one wide scalar load).
-template <int B, int MT, int CP, int P0, int I>
+template <int B, int MT, int CP, int P0, int I, bool ZP>
 struct DotChunk {
     typedef typename UVec<CP>::type vec;
     __device__ __forceinline__ static void run(const uint32_t *w, const vec *av, uint32_t mask,
-                                               uint32_t magic, float *d) {
-        const uint32_t wp = code_pair_bf16_plus128<B, P0 + I>(w, mask, magic);
+                                               uint32_t magic, uint32_t zv, float *d) {
+        uint32_t wp = code_pair_bf16_plus128<B, P0 + I>(w, mask, magic);
+        if constexpr (ZP) wp += zv;  // (64 - z) in both halves: 192 + c - z
 #pragma unroll
         for (int m = 0; m < MT; ++m) d[m] = dot2_bf16(av[m][I], wp, d[m]);
-        DotChunk<B, MT, CP, P0, I + 1>::run(w, av, mask, magic, d);
+        DotChunk<B, MT, CP, P0, I + 1, ZP>::run(w, av, mask, magic, zv, d);
     }
 };
-template <int B, int MT, int CP, int P0>
-struct DotChunk<B, MT, CP, P0, CP> {
+template <int B, int MT, int CP, int P0, bool ZP>
+struct DotChunk<B, MT, CP, P0, CP, ZP> {
     typedef typename UVec<CP>::type vec;
     __device__ __forceinline__ static void run(const uint32_t *, const vec *, uint32_t, uint32_t,
-                                               float *) {}
+                                               uint32_t, float *) {}
 };
 
 // b = 8: codes are whole bytes.  Each byte goes through v_cvt_f32_ubyteN and
@@ -85,9 +91,25 @@ __device__ __forceinline__ uint32_t bytes_to_bf16x2(uint32_t x, int lo_byte) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-template <int MT>
+// b = 8 with a zero point: (c0 - z, c1 - z) as bf16 (exact, |c - z| <= 255).
+__device__ __forceinline__ uint32_t bytes_minus_to_bf16x2(uint32_t x, int lo_byte, float z) {
+    f32x2_t f;
+    f.x = (float)((x >> (8 * lo_byte)) & 0xFFu) - z;
+    f.y = (float)((x >> (8 * lo_byte + 8)) & 0xFFu) - z;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// The per-slot zero-point operand: b = 8 the float z, else (64 - z) in both
+// 16-bit halves.
+template <int B>
+__device__ __forceinline__ uint32_t zero_operand(uint32_t z) {
+    if constexpr (B == 8) return __float_as_uint((float)z);
+    else return (64u - z) * 0x00010001u;
+}
+
+template <int MT, bool ZP>
 __device__ __forceinline__ void dot_bytes(const uint32_t *w, const uint32_t *a,
-                                          const int *row_off, float *d) {
+                                          const int *row_off, uint32_t zv, float *d) {
     constexpr int CP = 16;
     typedef typename UVec<CP>::type vec;
 #pragma unroll
@@ -98,7 +120,8 @@ __device__ __forceinline__ void dot_bytes(const uint32_t *w, const uint32_t *a,
 #pragma unroll
         for (int i = 0; i < CP; ++i) {
             const int p = p0 + i;
-            const uint32_t wp = bytes_to_bf16x2(w[p >> 1], 2 * (p & 1));
+            const uint32_t wp = ZP ? bytes_minus_to_bf16x2(w[p >> 1], 2 * (p & 1), __uint_as_float(zv))
+                                   : bytes_to_bf16x2(w[p >> 1], 2 * (p & 1));
 #pragma unroll
             for (int m = 0; m < MT; ++m) d[m] = dot2_bf16(av[m][i], wp, d[m]);
         }
@@ -116,13 +139,15 @@ struct SlotRegs {
     uint32_t w[4 * B];
     uint32_t al[MT];
     uint16_t s;
+    uint32_t z;  // zero point (only with zero points)
 };
-template <int B, int MT, class WL>
+template <int B, int MT, bool ZP, class WL>
 __device__ __forceinline__ void load_slot_regs(const WL &wl, int64_t nr, int g,
                                                const uint32_t *A2, const int *row_off, int lane,
-                                               SlotRegs<B, MT> &r) {
+                                               const uint8_t *zrow, SlotRegs<B, MT> &r) {
     load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), r.w);
     r.s = wl.scale(nr, g);
+    if constexpr (ZP) r.z = zrow[g];
 #pragma unroll
     for (int m = 0; m < MT; ++m) r.al[m] = A2[(int64_t)g * 64 + row_off[m] + lane];
 }
@@ -132,17 +157,23 @@ __device__ __forceinline__ void load_slot_regs(const WL &wl, int64_t nr, int g,
 // (offset 128 for b = 8); the caller applies the group scale.  `a` points at
 // the group's first activation pair of row 0 (read with scalar loads);
 // `row_off[m]` is row m's offset in pairs; `alane` the slot's al[].
-template <int B, int MT>
+template <int B>
+constexpr float decode_offset(bool zp) {
+    return zp ? (B == 8 ? 0.0f : 192.0f) : (B == 8 ? 128.0f : (float)(128 + (1 << (B - 1))));
+}
+
+template <int B, int MT, bool ZP>
 __device__ __forceinline__ void group_terms(const uint32_t *w, const uint32_t *a,
                                             const int *row_off, const uint32_t *alane,
-                                            uint32_t mask, uint32_t magic, float *x) {
-    constexpr float kOff = (B == 8) ? 128.0f : (float)(128 + (1 << (B - 1)));
+                                            uint32_t mask, uint32_t magic, uint32_t zv,
+                                            float *x) {
+    constexpr float kOff = decode_offset<B>(ZP);
     float d[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) d[m] = 0.0f;
     static_assert(MT == 1, "row tiles above 1 take the matrix-core form");
     if constexpr (B == 8) {
-        dot_bytes<MT>(w, a, row_off, d);
+        dot_bytes<MT, ZP>(w, a, row_off, zv, d);
     } else {
         // One row: all 64 activation pairs of the group come in with four
         // wide scalar loads issued together.
@@ -150,17 +181,21 @@ __device__ __forceinline__ void group_terms(const uint32_t *w, const uint32_t *a
         vec16 av[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) av[c] = *reinterpret_cast<const vec16 *>(a + 16 * c);
-        DotChunk<B, 1, 16, 0, 0>::run(w, &av[0], mask, magic, d);
-        DotChunk<B, 1, 16, 16, 0>::run(w, &av[1], mask, magic, d);
-        DotChunk<B, 1, 16, 32, 0>::run(w, &av[2], mask, magic, d);
-        DotChunk<B, 1, 16, 48, 0>::run(w, &av[3], mask, magic, d);
+        DotChunk<B, 1, 16, 0, 0, ZP>::run(w, &av[0], mask, magic, zv, d);
+        DotChunk<B, 1, 16, 16, 0, ZP>::run(w, &av[1], mask, magic, zv, d);
+        DotChunk<B, 1, 16, 32, 0, ZP>::run(w, &av[2], mask, magic, zv, d);
+        DotChunk<B, 1, 16, 48, 0, ZP>::run(w, &av[3], mask, magic, zv, d);
     }
     // Sum of this group's activations per row m: lane l adds pair l, then
     // a DPP reduction across the wave (wave-uniform result).
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        const float asum = wave_sum_uniform(dot2_bf16(alane[m], 0x3F803F80u, 0.0f));
-        x[m] = fmaf(-kOff, asum, d[m]);
+        if constexpr (kOff == 0.0f) {
+            x[m] = d[m];
+        } else {
+            const float asum = wave_sum_uniform(dot2_bf16(alane[m], 0x3F803F80u, 0.0f));
+            x[m] = fmaf(-kOff, asum, d[m]);
+        }
     }
 }
 
@@ -183,17 +218,24 @@ typedef short bf16x4_bits __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-template <int B, int Q, int J>
+template <int B, int Q, int J, bool ZP>
 struct MfmaSteps {
     __device__ __forceinline__ static void run(const uint32_t *w, const u32x4 *av, uint32_t mask,
-                                               uint32_t magic, f32x4_t *d) {
+                                               uint32_t magic, uint32_t zv, f32x4_t *d) {
         u32x2_t wp;
-        if constexpr (B == 8) {
+        if constexpr (B == 8 && ZP) {
+            wp.x = bytes_minus_to_bf16x2(w[J], 0, __uint_as_float(zv));
+            wp.y = bytes_minus_to_bf16x2(w[J], 2, __uint_as_float(zv));
+        } else if constexpr (B == 8) {
             wp.x = bytes_to_bf16x2(w[J], 0);
             wp.y = bytes_to_bf16x2(w[J], 2);
         } else {
             wp.x = code_pair_bf16_plus128<B, 2 * J>(w, mask, magic);
             wp.y = code_pair_bf16_plus128<B, 2 * J + 1>(w, mask, magic);
+            if constexpr (ZP) {
+                wp.x += zv;
+                wp.y += zv;
+            }
         }
         const bf16x4_bits bw = __builtin_bit_cast(bf16x4_bits, wp);
 #pragma unroll
@@ -204,13 +246,13 @@ struct MfmaSteps {
             d[q] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4_bits, a), bw,
                                                           d[q], 4, J >> 1, 0);
         }
-        MfmaSteps<B, Q, J + 1>::run(w, av, mask, magic, d);
+        MfmaSteps<B, Q, J + 1, ZP>::run(w, av, mask, magic, zv, d);
     }
 };
-template <int B, int Q>
-struct MfmaSteps<B, Q, 32> {
+template <int B, int Q, bool ZP>
+struct MfmaSteps<B, Q, 32, ZP> {
     __device__ __forceinline__ static void run(const uint32_t *, const u32x4 *, uint32_t, uint32_t,
-                                               f32x4_t *) {}
+                                               uint32_t, f32x4_t *) {}
 };
 
 // Sum over the 16 lanes 4i + r (i = 0..15) of a value, for each r; every
@@ -242,13 +284,16 @@ struct SlotRegsMf {
     uint32_t w[4 * B];
     u32x4 av[MT / 4];
     uint16_t s;
+    uint32_t z;  // zero point (only with zero points)
 };
-template <int B, int MT, class WL>
+template <int B, int MT, bool ZP, class WL>
 __device__ __forceinline__ void load_slot_regs_mf(const WL &wl, int64_t nr, int g,
                                                   const uint32_t *A2, const int *arow_off,
-                                                  int lane, SlotRegsMf<B, MT> &r) {
+                                                  int lane, const uint8_t *zrow,
+                                                  SlotRegsMf<B, MT> &r) {
     load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), r.w);
     r.s = wl.scale(nr, g);
+    if constexpr (ZP) r.z = zrow[g];
 #pragma unroll
     for (int q = 0; q < MT / 4; ++q)
         r.av[q] = *reinterpret_cast<const u32x4 *>(A2 + (int64_t)g * 64 + arow_off[q] +
@@ -258,17 +303,24 @@ __device__ __forceinline__ void load_slot_regs_mf(const WL &wl, int64_t nr, int 
 // x[m] = sum_k a[m,k] (128 + c_k) - (128 + 2^(b-1)) sum_k a[m,k] for the
 // lane's row and rows m = 0 .. MT-1 of A (offset 128 for b = 8), as in
 // group_terms; the caller applies the group scale.
-template <int B, int MT>
+template <int B, int MT, bool ZP>
 __device__ __forceinline__ void group_terms_mf(const uint32_t *w, const u32x4 *av, uint32_t mask,
-                                               uint32_t magic, float *x) {
+                                               uint32_t magic, uint32_t zv, float *x) {
     constexpr int Q = MT / 4;
-    constexpr float kOff = (B == 8) ? 128.0f : (float)(128 + (1 << (B - 1)));
+    constexpr float kOff = decode_offset<B>(ZP);
     f32x4_t d[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) d[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    MfmaSteps<B, Q, 0>::run(w, av, mask, magic, d);
+    MfmaSteps<B, Q, 0, ZP>::run(w, av, mask, magic, zv, d);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
+        if constexpr (kOff == 0.0f) {
+            x[4 * q + 0] = d[q][0];
+            x[4 * q + 1] = d[q][1];
+            x[4 * q + 2] = d[q][2];
+            x[4 * q + 3] = d[q][3];
+            continue;
+        }
         // Row 4q + (lane & 3)'s group sum: the lane's 8 activations, then
         // over the 16 lanes holding the same row.
         float ps = dot2_bf16(av[q][0], 0x3F803F80u, 0.0f);
@@ -287,9 +339,10 @@ __device__ __forceinline__ void group_terms_mf(const uint32_t *w, const u32x4 *a
 // layers): no prefetch register set, so more waves fit per SIMD.  Used for
 // the matrix-core row tiles; with one row of A the prefetching form measured
 // 3.5% faster even then, so it keeps that one.
-template <int B, int MT, int W, class WL, bool ONE>
+template <int B, int MT, int W, class WL, bool ONE, bool ZP>
 __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restrict__ A, int M,
                                                         int N, int K, WL wl,
+                                                        const uint8_t *__restrict__ zeros,
                                                         uint16_t *__restrict__ Y,
                                                         float *__restrict__ part,
                                                         unsigned *__restrict__ counters,
@@ -313,6 +366,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     // Dense rows beyond N do not exist: read row N-1 and drop the result.
     // Tiled blobs hold zero-padded rows, so nothing to clamp there.
     const int64_t nr = (WL::kTiled || n < N) ? n : (int64_t)N - 1;
+    // Zero points are [N, G] in either layout: padded tile rows read row N-1.
+    const uint8_t *zrow = ZP ? zeros + (n < N ? n : (int64_t)N - 1) * G : nullptr;
 
     float acc[MT];
 #pragma unroll
@@ -335,9 +390,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         const int g = g_begin + wave;
         if (g < g_end) {
             SlotRegsMf<B, MT> cur;
-            load_slot_regs_mf<B, MT>(wl, nr, g, A2, arow_off, lane, cur);
+            load_slot_regs_mf<B, MT, ZP>(wl, nr, g, A2, arow_off, lane, zrow, cur);
             float x[MT];
-            group_terms_mf<B, MT>(cur.w, cur.av, mask, magic, x);
+            group_terms_mf<B, MT, ZP>(cur.w, cur.av, mask, magic, zero_operand<B>(cur.z), x);
             const float sc = bf16_to_f32(cur.s);
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m] = sc * x[m];
@@ -345,12 +400,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     } else if constexpr (MF) {
         SlotRegsMf<B, MT> cur, nxt;
         int g = g_begin + wave;
-        if (g < g_end) load_slot_regs_mf<B, MT>(wl, nr, g, A2, arow_off, lane, cur);
+        if (g < g_end) load_slot_regs_mf<B, MT, ZP>(wl, nr, g, A2, arow_off, lane, zrow, cur);
         for (; g < g_end; g += W) {
             const int gn = g + W;
-            if (gn < g_end) load_slot_regs_mf<B, MT>(wl, nr, gn, A2, arow_off, lane, nxt);
+            if (gn < g_end)
+                load_slot_regs_mf<B, MT, ZP>(wl, nr, gn, A2, arow_off, lane, zrow, nxt);
             float x[MT];
-            group_terms_mf<B, MT>(cur.w, cur.av, mask, magic, x);
+            group_terms_mf<B, MT, ZP>(cur.w, cur.av, mask, magic, zero_operand<B>(cur.z), x);
             const float sc = bf16_to_f32(cur.s);
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
@@ -360,9 +416,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         const int g = g_begin + wave;
         if (g < g_end) {
             SlotRegs<B, MT> cur;
-            load_slot_regs<B, MT>(wl, nr, g, A2, row_off, lane, cur);
+            load_slot_regs<B, MT, ZP>(wl, nr, g, A2, row_off, lane, zrow, cur);
             float x[MT];
-            group_terms<B, MT>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic, x);
+            group_terms<B, MT, ZP>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic,
+                                   zero_operand<B>(cur.z), x);
             const float sc = bf16_to_f32(cur.s);
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m] = sc * x[m];
@@ -370,12 +427,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     } else {
         SlotRegs<B, MT> cur, nxt;
         int g = g_begin + wave;
-        if (g < g_end) load_slot_regs<B, MT>(wl, nr, g, A2, row_off, lane, cur);
+        if (g < g_end) load_slot_regs<B, MT, ZP>(wl, nr, g, A2, row_off, lane, zrow, cur);
         for (; g < g_end; g += W) {
             const int gn = g + W;
-            if (gn < g_end) load_slot_regs<B, MT>(wl, nr, gn, A2, row_off, lane, nxt);
+            if (gn < g_end) load_slot_regs<B, MT, ZP>(wl, nr, gn, A2, row_off, lane, zrow, nxt);
             float x[MT];
-            group_terms<B, MT>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic, x);
+            group_terms<B, MT, ZP>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic,
+                                   zero_operand<B>(cur.z), x);
             const float sc = bf16_to_f32(cur.s);
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
@@ -457,10 +515,41 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int B, int MT, int W, class WL, bool ZP>
+static void launch_decode_kernel(bool one, const uint16_t *A, int64_t M, int64_t N, int64_t K,
+                                 const WL &wl, const uint8_t *zeros, uint16_t *Y, float *part,
+                                 unsigned *counters, const DecodePlan &p, hipStream_t stream) {
+    const dim3 grid((unsigned)(p.rowblocks * p.splits));
+    if (one)
+        hipLaunchKernelGGL((decode_kernel<B, MT, W, WL, true, ZP>), grid, dim3(64 * W), 0, stream,
+                           A, (int)M, (int)N, (int)K, wl, zeros, Y, part, counters, p.splits,
+                           p.gps, p.tstride);
+    else
+        hipLaunchKernelGGL((decode_kernel<B, MT, W, WL, false, ZP>), grid, dim3(64 * W), 0,
+                           stream, A, (int)M, (int)N, (int)K, wl, zeros, Y, part, counters,
+                           p.splits, p.gps, p.tstride);
+}
+
+template <int B, int MT, int W, class WL>
+static hipError_t launch_decode_zp(bool one, const uint16_t *A, int64_t M, int64_t N, int64_t K,
+                                   const WL &wl, const uint8_t *zeros, uint16_t *Y, float *part,
+                                   unsigned *counters, const DecodePlan &p, hipStream_t stream) {
+    if (!zeros) {
+        launch_decode_kernel<B, MT, W, WL, false>(one, A, M, N, K, wl, nullptr, Y, part,
+                                                  counters, p, stream);
+    } else if constexpr (B == 4 || B == 8) {  // the widths with an asymmetric form
+        launch_decode_kernel<B, MT, W, WL, true>(one, A, M, N, K, wl, zeros, Y, part, counters,
+                                                 p, stream);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int B, int MT, int W>
 hipError_t decode_bmw(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W_,
-                      bool tiled, const uint16_t *scales, uint16_t *Y, void *ws,
-                      const DecodePlan &p, hipStream_t stream) {
+                      bool tiled, const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
+                      void *ws, const DecodePlan &p, hipStream_t stream) {
     const int G = (int)(K / kGroup);
     float *part = nullptr;
     unsigned *counters = nullptr;
@@ -468,58 +557,40 @@ hipError_t decode_bmw(const uint16_t *A, int64_t M, int64_t N, int64_t K, const 
         counters = static_cast<unsigned *>(ws);
         part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
     }
-    const dim3 grid((unsigned)(p.rowblocks * p.splits));
     const bool one = MT > 1 && p.gps <= W;
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W_), G, B};
-        if (one)
-            hipLaunchKernelGGL((decode_kernel<B, MT, W, TiledW, true>), grid, dim3(64 * W), 0,
-                               stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
-                               p.splits, p.gps, p.tstride);
-        else
-            hipLaunchKernelGGL((decode_kernel<B, MT, W, TiledW, false>), grid, dim3(64 * W), 0,
-                               stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
-                               p.splits, p.gps, p.tstride);
-    } else {
-        DenseW wl{static_cast<const uint8_t *>(W_), scales, (int64_t)16 * B * G, G, B};
-        if (one)
-            hipLaunchKernelGGL((decode_kernel<B, MT, W, DenseW, true>), grid, dim3(64 * W), 0,
-                               stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
-                               p.splits, p.gps, p.tstride);
-        else
-            hipLaunchKernelGGL((decode_kernel<B, MT, W, DenseW, false>), grid, dim3(64 * W), 0,
-                               stream, A, (int)M, (int)N, (int)K, wl, Y, part, counters,
-                               p.splits, p.gps, p.tstride);
+        return launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p,
+                                          stream);
     }
-    return hipGetLastError();
+    DenseW wl{static_cast<const uint8_t *>(W_), scales, (int64_t)16 * B * G, G, B};
+    return launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p, stream);
 }
 
 template <int B, int MT>
 hipError_t decode_bm(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W_,
-                     bool tiled, const uint16_t *scales, uint16_t *Y, void *ws,
-                     const DecodePlan &p, hipStream_t stream) {
+                     bool tiled, const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
+                     void *ws, const DecodePlan &p, hipStream_t stream) {
     if constexpr (MT <= 4) {
         if (p.waves == 16)
-            return decode_bmw<B, MT, 16>(A, M, N, K, W_, tiled, scales, Y, ws, p, stream);
+            return decode_bmw<B, MT, 16>(A, M, N, K, W_, tiled, scales, zeros, Y, ws, p, stream);
     }
-    if constexpr (MT <= 16) {
-        if (p.waves == 8)
-            return decode_bmw<B, MT, 8>(A, M, N, K, W_, tiled, scales, Y, ws, p, stream);
-    }
+    if (p.waves == 8)
+        return decode_bmw<B, MT, 8>(A, M, N, K, W_, tiled, scales, zeros, Y, ws, p, stream);
     if (p.waves == 4)
-        return decode_bmw<B, MT, 4>(A, M, N, K, W_, tiled, scales, Y, ws, p, stream);
+        return decode_bmw<B, MT, 4>(A, M, N, K, W_, tiled, scales, zeros, Y, ws, p, stream);
     return hipErrorInvalidValue;
 }
 
 template <int B>
 hipError_t decode_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                           bool tiled, const uint16_t *scales, uint16_t *Y, void *ws,
-                           const DecodePlan &p, hipStream_t stream) {
+                    bool tiled, const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
+                    void *ws, const DecodePlan &p, hipStream_t stream) {
     switch (p.mt) {
-        case 1: return decode_bm<B, 1>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
-        case 4: return decode_bm<B, 4>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
-        case 8: return decode_bm<B, 8>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
-        case 16: return decode_bm<B, 16>(A, M, N, K, W, tiled, scales, Y, ws, p, stream);
+        case 1: return decode_bm<B, 1>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
+        case 4: return decode_bm<B, 4>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
+        case 8: return decode_bm<B, 8>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
+        case 16: return decode_bm<B, 16>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
     }
     return hipErrorInvalidValue;
 }

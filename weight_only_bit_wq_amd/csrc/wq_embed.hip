@@ -17,11 +17,13 @@
 // b = 7 at some offsets; addresses clamped to the row so none leaves it),
 // shifts them by 8 * (b*j mod 4) bits so code i sits at bit b*i of a 64-bit
 // window, extracts the 8 codes at those compile-time offsets and writes
-//     Y[t, 8j + i] = bf16_rne(s[id, j/16] * (c_i - 2^(b-1)))      (id = ids[t])
-// c - 2^(b-1) is formed exactly in fp32 and then multiplied by the scale (a
-// product, so a zero code under a negative scale gives -0 as the exact
-// product does); the product has at most 16 significant bits, so it is exact
-// in fp32 and the one rounding is the bf16 conversion.  Ids outside [0, V)
+//     Y[t, 8j + i] = bf16_rne(s[id, j/16] * (c_i - z[id, j/16]))      (id = ids[t])
+// with z = 2^(b-1) for symmetric groups (the zero points exist for b = 4 and
+// 8; a per-channel scale is s[id] for every group).  c - z is formed exactly
+// in fp32 and then multiplied by the scale (a product, so a zero code under
+// a negative scale gives -0 as the exact product does); the product has at
+// most 16 significant bits, so it is exact in fp32 and the one rounding is
+// the bf16 conversion.  Ids outside [0, V)
 // give rows of zeros: the rows of a vocabulary shard that belong to other
 // shards.
 #include "wq_device.h"
@@ -46,6 +48,8 @@ constexpr int kEmbedBlock = 128;  // chunks (threads) per block
 template <int B>
 __global__ __launch_bounds__(kEmbedBlock) void embed_kernel(const uint32_t *__restrict__ W,
                                                     const uint16_t *__restrict__ scales,
+                                                    const uint8_t *__restrict__ zeros,
+                                                    int sG, int sg,
                                                     int64_t V, int K, int bpt,
                                                     const int64_t *__restrict__ ids,
                                                     uint16_t *__restrict__ Y) {
@@ -75,8 +79,9 @@ __global__ __launch_bounds__(kEmbedBlock) void embed_kernel(const uint32_t *__re
     } else {  // (byte0 & 3) + B <= 8: two dwords hold the chunk
         hi = sh ? (w1 >> sh) : w1;
     }
-    const float s = bf16_to_f32(scales[id * (K / kGroup) + (j >> 4)]);
-    constexpr float kOff = (float)(1 << (B - 1));
+    const int G = K / kGroup;
+    const float s = bf16_to_f32(scales[id * sG + (j >> 4) * sg]);
+    const float kOff = zeros ? (float)zeros[id * G + (j >> 4)] : (float)(1 << (B - 1));
     uint32_t c[8];
     c[0] = window_code<B, 0>(lo, hi);
     c[1] = window_code<B, 1>(lo, hi);
@@ -97,20 +102,43 @@ __global__ __launch_bounds__(kEmbedBlock) void embed_kernel(const uint32_t *__re
     *dst = u32x4{o[0], o[1], o[2], o[3]};
 }
 
-hipError_t launch_embed(const void *W, const uint16_t *scales, int64_t V, int64_t K, int b,
-                        const int64_t *ids, int64_t T, uint16_t *Y, hipStream_t stream) {
+hipError_t launch_embed(const void *W, const uint16_t *scales, const uint8_t *zeros,
+                        bool per_channel, int64_t V, int64_t K, int b, const int64_t *ids,
+                        int64_t T, uint16_t *Y, hipStream_t stream) {
+    const int sG = per_channel ? 1 : (int)(K / kGroup), sg = per_channel ? 0 : 1;
     const int bpt = (int)((K / 8 + kEmbedBlock - 1) / kEmbedBlock);
     const dim3 grid((unsigned)(T * bpt)), block(kEmbedBlock);
     const uint32_t *w = static_cast<const uint32_t *>(W);
     const int k = (int)K;
     switch (b) {
-        case 2: hipLaunchKernelGGL(embed_kernel<2>, grid, block, 0, stream, w, scales, V, k, bpt, ids, Y); break;
-        case 3: hipLaunchKernelGGL(embed_kernel<3>, grid, block, 0, stream, w, scales, V, k, bpt, ids, Y); break;
-        case 4: hipLaunchKernelGGL(embed_kernel<4>, grid, block, 0, stream, w, scales, V, k, bpt, ids, Y); break;
-        case 5: hipLaunchKernelGGL(embed_kernel<5>, grid, block, 0, stream, w, scales, V, k, bpt, ids, Y); break;
-        case 6: hipLaunchKernelGGL(embed_kernel<6>, grid, block, 0, stream, w, scales, V, k, bpt, ids, Y); break;
-        case 7: hipLaunchKernelGGL(embed_kernel<7>, grid, block, 0, stream, w, scales, V, k, bpt, ids, Y); break;
-        case 8: hipLaunchKernelGGL(embed_kernel<8>, grid, block, 0, stream, w, scales, V, k, bpt, ids, Y); break;
+        case 2:
+            hipLaunchKernelGGL(embed_kernel<2>, grid, block, 0, stream, w, scales, zeros, sG, sg, V,
+                               k, bpt, ids, Y);
+            break;
+        case 3:
+            hipLaunchKernelGGL(embed_kernel<3>, grid, block, 0, stream, w, scales, zeros, sG, sg, V,
+                               k, bpt, ids, Y);
+            break;
+        case 4:
+            hipLaunchKernelGGL(embed_kernel<4>, grid, block, 0, stream, w, scales, zeros, sG, sg, V,
+                               k, bpt, ids, Y);
+            break;
+        case 5:
+            hipLaunchKernelGGL(embed_kernel<5>, grid, block, 0, stream, w, scales, zeros, sG, sg, V,
+                               k, bpt, ids, Y);
+            break;
+        case 6:
+            hipLaunchKernelGGL(embed_kernel<6>, grid, block, 0, stream, w, scales, zeros, sG, sg, V,
+                               k, bpt, ids, Y);
+            break;
+        case 7:
+            hipLaunchKernelGGL(embed_kernel<7>, grid, block, 0, stream, w, scales, zeros, sG, sg, V,
+                               k, bpt, ids, Y);
+            break;
+        case 8:
+            hipLaunchKernelGGL(embed_kernel<8>, grid, block, 0, stream, w, scales, zeros, sG, sg, V,
+                               k, bpt, ids, Y);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

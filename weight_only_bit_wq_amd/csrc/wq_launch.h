@@ -8,7 +8,7 @@ namespace wq {
 
 // ---- repack / unpack (wq_unpack.hip) ----
 hipError_t launch_repack_tiled(const uint32_t *packed, const uint16_t *scales, int64_t N,
-                               int64_t K, int b, void *out, hipStream_t stream);
+                               int64_t K, int b, bool per_channel, void *out, hipStream_t stream);
 hipError_t launch_unpack(const void *W, bool tiled, const uint16_t *scales_unused, int64_t N,
                          int64_t K, int b, uint8_t *codes, hipStream_t stream);
 
@@ -36,25 +36,26 @@ struct DecodePlan {
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b);
 
 hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                         bool tiled, const uint16_t *scales, int b, uint16_t *Y, void *ws,
-                         const DecodePlan &plan, hipStream_t stream);
+                         bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
+                         uint16_t *Y, void *ws, const DecodePlan &plan, hipStream_t stream);
 
 // ---- prefill path, M > kDecodeMaxM (wq_prefill.hip) ----
 int64_t prefill_ws_bytes(int64_t M, int64_t N, int64_t K, int b);
 hipError_t launch_prefill(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                          bool tiled, const uint16_t *scales, int b, uint16_t *Y, void *ws,
-                          hipStream_t stream);
+                          bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
+                          uint16_t *Y, void *ws, hipStream_t stream);
 
 // ---- quantized embedding gather (wq_embed.hip) ----
-hipError_t launch_embed(const void *W, const uint16_t *scales, int64_t V, int64_t K, int b,
-                        const int64_t *ids, int64_t T, uint16_t *Y, hipStream_t stream);
+hipError_t launch_embed(const void *W, const uint16_t *scales, const uint8_t *zeros,
+                        bool per_channel, int64_t V, int64_t K, int b, const int64_t *ids,
+                        int64_t T, uint16_t *Y, hipStream_t stream);
 
 // ---- W4A8 (wq_a8.hip) ----
 hipError_t launch_quant_act(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq, float *sa,
                             hipStream_t stream);
 int64_t a8_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                          bool tiled, const uint16_t *scales, int b, void *Y, bool out_f32,
-                          void *ws, hipStream_t stream);
+                          bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
+                          void *Y, bool out_f32, void *ws, hipStream_t stream);
 
 }  // namespace wq

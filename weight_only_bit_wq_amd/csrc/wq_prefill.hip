@@ -16,6 +16,11 @@
 // multiplies that against s[n, k'/3] as extra "pseudo-groups" with scale 1.
 // No scale or code is ever rounded to bf16.
 //
+// Zero points (b = 4 and 8): b = 4 adds (64 - z) to both 16-bit halves of a
+// pair after the exponent OR, so B holds 192 + c - z exactly and the
+// pre-pass constant is 192; b = 8 converts bytes to c - z (exact in bf16)
+// and has no constant term, so it runs without the pre-pass.
+//
 // Tiling.  Workgroup 256 (m) x 128 (n), 8 waves of 128 x 32 (two per SIMD),
 // each as four 32 x 32 MFMA blocks run in two staggered phases.  K runs in
 // whole groups of 128: A through LDS (double-buffered, filled by direct
@@ -119,10 +124,30 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // still reads the other buffers), read their half-slots, issue the direct
 // loads of group g+1's A and codes into the other buffers and its scale
 // into a register, and run g.
-template <int B, class WL>
+// Pair P of a 32-code quarter as bf16 with a zero point: b = 4 gives
+// 192 + c - z (zv = (64 - z) in both halves), b = 8 gives c - z (zv = the
+// float z).
+template <int B, int P>
+__device__ __forceinline__ uint32_t quarter_pair_zp(const uint32_t *w, uint32_t mask,
+                                                    uint32_t magic, uint32_t zv) {
+    if constexpr (B == 8) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const uint32_t x = w[P >> 1];
+        const float z = __uint_as_float(zv);
+        f32x2 f;
+        f.x = (float)((x >> (16 * (P & 1))) & 0xFFu) - z;
+        f.y = (float)((x >> (16 * (P & 1) + 8)) & 0xFFu) - z;
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+    } else {
+        return quarter_pair<B, P>(w, mask, magic) + zv;
+    }
+}
+
+template <int B, class WL, bool ZP>
 __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict__ A,
                                                       const uint16_t *__restrict__ Ap, int M,
                                                       int N, int K, int Kp, WL wl,
+                                                      const uint8_t *__restrict__ zeros,
                                                       uint16_t *__restrict__ Y, int mtiles,
                                                       int ntiles, int splits,
                                                       float *__restrict__ part, int64_t mnp) {
@@ -247,8 +272,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     const int64_t bcol = min(n0 + 32 * wn + c32, (int64_t)N - 1);
     const uint8_t *sptr = wl.scale0(bcol);
     const int64_t sstep = wl.scale_step();
+    // Zero points [N, G]: the lane's column, one group ahead like the scale.
+    const uint8_t *zrow = ZP ? zeros + bcol * G : nullptr;
+    uint32_t zop = 0, znext = 0;
     auto load_scale = [&](int g, uint32_t &sc) __attribute__((always_inline)) {
         sc = *reinterpret_cast<const uint16_t *>(sptr + min(g, g_hi - 1) * sstep);
+        if constexpr (ZP) {
+            const uint32_t z = zrow[min(g, g_hi - 1)];
+            znext = B == 8 ? __float_as_uint((float)z) : (64u - z) * 0x00010001u;
+        }
     };
     // A operand of k-step j: LDS row 128 wm + 64 PH + 32 t + c32 (the last
     // three terms compile-time), chunk (8 h + j) ^ (c32 % 16).
@@ -272,7 +304,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     // B operand of k-step J: pairs 4 (J % 4) .. +3 of quarter J / 4 of the half.
     auto unpack_pair = [&](auto jconst, auto iconst) __attribute__((always_inline)) {
         constexpr int J = decltype(jconst)::value, I = decltype(iconst)::value;
-        bop[J][I] = quarter_pair<B, 4 * (J & 3) + I>(creg + (J >> 2) * B, mask, magic);
+        if constexpr (ZP)
+            bop[J][I] = quarter_pair_zp<B, 4 * (J & 3) + I>(creg + (J >> 2) * B, mask, magic, zop);
+        else
+            bop[J][I] = quarter_pair<B, 4 * (J & 3) + I>(creg + (J >> 2) * B, mask, magic);
     };
     auto read_a = [&](auto bconst, int row0, int j, int set) __attribute__((always_inline)) {
         const u32x4 *src = decltype(bconst)::value == 0 ? As0 : As1;
@@ -408,6 +443,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         sreg = snext;
+        zop = znext;
         read_codes(bconst, creg);
         dma(A_blk, min(g + 1, g_hi - 1) * kGroup, doff, std::integral_constant<int, BUF ^ 1>{});
         dma_codes(min(g + 1, g_hi - 1), std::integral_constant<int, BUF ^ 1>{});
@@ -510,34 +546,40 @@ int64_t prefill_ws_bytes(int64_t M, int64_t N, int64_t K, int) {
            (s > 1 ? s * prefill_mnp(M, N) * 4 : 0);
 }
 
-template <int B>
-static hipError_t prefill_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                            bool tiled, const uint16_t *scales, uint16_t *Y, void *ws,
-                            hipStream_t stream) {
+template <int B, bool ZP>
+static hipError_t prefill_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
+                             bool tiled, const uint16_t *scales, const uint8_t *zeros,
+                             uint16_t *Y, void *ws, hipStream_t stream) {
     const int G = (int)(K / kGroup);
-    const int Kp = pseudo_kp(K);
+    // The constant term: (128 + 2^(b-1)) symmetric, 192 with b = 4 zero
+    // points, none (no pre-pass, no pseudo-groups) with b = 8 zero points.
+    const float off = ZP ? (B == 8 ? 0.0f : 192.0f)
+                         : (B == 8 ? 128.0f : (float)(128 + (1 << (B - 1))));
+    const int Kp = off != 0.0f ? pseudo_kp(K) : 0;
     uint16_t *Ap = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
     const int splits = prefill_splits(M, N, K);
     float *part = splits > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
                                                          kWsScratchOffset + align256(M * Kp * 2))
                              : nullptr;
-    const float off = (B == 8) ? 128.0f : (float)(128 + (1 << (B - 1)));
-    hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M), dim3(256), 0, stream, A, (int)K,
-                       Kp, off, Ap);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (Kp > 0) {
+        hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M), dim3(256), 0, stream, A,
+                           (int)K, Kp, off, Ap);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int mtiles = (int)((M + kPM - 1) / kPM);
     const int ntiles = (int)((N + kPN - 1) / kPN);
     const dim3 grid((unsigned)(mtiles * ntiles * splits));
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W), G, B};
-        hipLaunchKernelGGL((prefill_kernel<B, TiledW>), grid, dim3(512), 0, stream, A, Ap,
-                           (int)M, (int)N, (int)K, Kp, wl, Y, mtiles, ntiles, splits, part,
+        hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP>), grid, dim3(512), 0, stream, A, Ap,
+                           (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles, splits, part,
                            prefill_mnp(M, N));
     } else {
         DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
-        hipLaunchKernelGGL((prefill_kernel<B, DenseW>), grid, dim3(512), 0, stream, A, Ap,
-                           (int)M, (int)N, (int)K, Kp, wl, Y, mtiles, ntiles, splits, part,
+        hipLaunchKernelGGL((prefill_kernel<B, DenseW, ZP>), grid, dim3(512), 0, stream, A, Ap,
+                           (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles, splits, part,
                            prefill_mnp(M, N));
     }
     e = hipGetLastError();
@@ -549,17 +591,27 @@ static hipError_t prefill_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, 
     return hipGetLastError();
 }
 
+template <int B>
+static hipError_t prefill_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
+                            bool tiled, const uint16_t *scales, const uint8_t *zeros,
+                            uint16_t *Y, void *ws, hipStream_t stream) {
+    if (!zeros) return prefill_bz<B, false>(A, M, N, K, W, tiled, scales, nullptr, Y, ws, stream);
+    if constexpr (B == 4 || B == 8)  // the widths with an asymmetric form
+        return prefill_bz<B, true>(A, M, N, K, W, tiled, scales, zeros, Y, ws, stream);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_prefill(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
-                          bool tiled, const uint16_t *scales, int b, uint16_t *Y, void *ws,
-                          hipStream_t stream) {
+                          bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
+                          uint16_t *Y, void *ws, hipStream_t stream) {
     switch (b) {
-        case 2: return prefill_b<2>(A, M, N, K, W, tiled, scales, Y, ws, stream);
-        case 3: return prefill_b<3>(A, M, N, K, W, tiled, scales, Y, ws, stream);
-        case 4: return prefill_b<4>(A, M, N, K, W, tiled, scales, Y, ws, stream);
-        case 5: return prefill_b<5>(A, M, N, K, W, tiled, scales, Y, ws, stream);
-        case 6: return prefill_b<6>(A, M, N, K, W, tiled, scales, Y, ws, stream);
-        case 7: return prefill_b<7>(A, M, N, K, W, tiled, scales, Y, ws, stream);
-        case 8: return prefill_b<8>(A, M, N, K, W, tiled, scales, Y, ws, stream);
+        case 2: return prefill_b<2>(A, M, N, K, W, tiled, scales, zeros, Y, ws, stream);
+        case 3: return prefill_b<3>(A, M, N, K, W, tiled, scales, zeros, Y, ws, stream);
+        case 4: return prefill_b<4>(A, M, N, K, W, tiled, scales, zeros, Y, ws, stream);
+        case 5: return prefill_b<5>(A, M, N, K, W, tiled, scales, zeros, Y, ws, stream);
+        case 6: return prefill_b<6>(A, M, N, K, W, tiled, scales, zeros, Y, ws, stream);
+        case 7: return prefill_b<7>(A, M, N, K, W, tiled, scales, zeros, Y, ws, stream);
+        case 8: return prefill_b<8>(A, M, N, K, W, tiled, scales, zeros, Y, ws, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -9,11 +9,14 @@ namespace wq {
 // One thread per (64-row block R, group g, row r in block): copies the b
 // 16-byte chunks of that slot into plane j of the tile (lanes = rows, so each
 // plane store is 1 KB contiguous per wave) and the scale after the planes.
-// Rows >= N are written as zero codes and zero scales.
+// Rows >= N are written as zero codes and zero scales.  Scales are read at
+// n * sG + g * sg: (G, 1) for group scales, (1, 0) for one scale per row
+// (per-channel), which every group of the row then carries.
 template <int B>
 __global__ __launch_bounds__(256) void repack_tiled_kernel(const uint32_t *__restrict__ packed,
                                                           const uint16_t *__restrict__ scales,
-                                                          int64_t N, int G, int rowblocks,
+                                                          int64_t N, int G, int sG, int sg,
+                                                          int rowblocks,
                                                           uint8_t *__restrict__ out) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t slots = (int64_t)rowblocks * G * 64;
@@ -31,7 +34,7 @@ __global__ __launch_bounds__(256) void repack_tiled_kernel(const uint32_t *__res
             (int64_t)g * 16 * B);
 #pragma unroll
         for (int j = 0; j < B; ++j) dst[j * 64] = src[j];
-        reinterpret_cast<uint16_t *>(tile + tile_code_bytes(B))[r] = scales[n * G + g];
+        reinterpret_cast<uint16_t *>(tile + tile_code_bytes(B))[r] = scales[n * sG + g * sg];
     } else {
         const uint4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -85,26 +88,27 @@ __global__ __launch_bounds__(256) void unpack_kernel(WL wl, int64_t N, int G, bo
 
 template <int B>
 static hipError_t repack_b(const uint32_t *packed, const uint16_t *scales, int64_t N, int G,
-                           void *out, hipStream_t stream) {
+                           bool per_channel, void *out, hipStream_t stream) {
     const int rowblocks = (int)((N + 63) / 64);
     const int64_t slots = (int64_t)rowblocks * G * 64;
     const int64_t blocks = (slots + 255) / 256;
     hipLaunchKernelGGL(repack_tiled_kernel<B>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       packed, scales, N, G, rowblocks, static_cast<uint8_t *>(out));
+                       packed, scales, N, G, per_channel ? 1 : G, per_channel ? 0 : 1, rowblocks,
+                       static_cast<uint8_t *>(out));
     return hipGetLastError();
 }
 
 hipError_t launch_repack_tiled(const uint32_t *packed, const uint16_t *scales, int64_t N,
-                               int64_t K, int b, void *out, hipStream_t stream) {
+                               int64_t K, int b, bool per_channel, void *out, hipStream_t stream) {
     const int G = (int)(K / kGroup);
     switch (b) {
-        case 2: return repack_b<2>(packed, scales, N, G, out, stream);
-        case 3: return repack_b<3>(packed, scales, N, G, out, stream);
-        case 4: return repack_b<4>(packed, scales, N, G, out, stream);
-        case 5: return repack_b<5>(packed, scales, N, G, out, stream);
-        case 6: return repack_b<6>(packed, scales, N, G, out, stream);
-        case 7: return repack_b<7>(packed, scales, N, G, out, stream);
-        case 8: return repack_b<8>(packed, scales, N, G, out, stream);
+        case 2: return repack_b<2>(packed, scales, N, G, per_channel, out, stream);
+        case 3: return repack_b<3>(packed, scales, N, G, per_channel, out, stream);
+        case 4: return repack_b<4>(packed, scales, N, G, per_channel, out, stream);
+        case 5: return repack_b<5>(packed, scales, N, G, per_channel, out, stream);
+        case 6: return repack_b<6>(packed, scales, N, G, per_channel, out, stream);
+        case 7: return repack_b<7>(packed, scales, N, G, per_channel, out, stream);
+        case 8: return repack_b<8>(packed, scales, N, G, per_channel, out, stream);
     }
     return hipErrorInvalidValue;
 }
