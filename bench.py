@@ -168,6 +168,48 @@ def bench_embed(torch, wq, synth, reps: int):
     return out
 
 
+def bench_zero_points(torch, wq, synth, reps: int, copies: int):
+    """Zero points (b = 4, 8) and per-channel scales against the symmetric
+    kernels on the same layer (K 5120 -> N 17408, tiled): decode M = 1 with
+    rotating weight copies, prefill M = 4096."""
+    K, N = 5120, 17408
+    rng = np.random.default_rng(9)
+    out = {}
+    for b in (4, 8):
+        codes = synth.draw_codes(rng, N, K, b)
+        scales = synth.draw_scales_halfnormal_signed(rng, N, K // 128)
+        z = torch.from_numpy(rng.integers(0, 1 << b, size=(N, K // 128), dtype=np.uint8)).cuda()
+        words = torch.from_numpy(wq.wq_pack(codes, b).view(np.int32)).cuda()
+        s_d = torch.from_numpy(scales.view(np.int16)).cuda().view(torch.bfloat16)
+        blobs = [wq.wq_repack(words, s_d, K, b) for _ in range(copies)]
+        s1 = s_d[:, :1].contiguous()
+        blobs_pc = [wq.wq_repack(words, s1, K, b, group=K) for _ in range(copies)]
+        byts = algorithmic_bytes(1, N, K, b)
+        A1 = torch.from_numpy(synth.draw_act(rng, 1, K).view(np.int16)).cuda().view(torch.bfloat16)
+        Y1 = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+        res = {}
+        for name, bl, kw in (("symmetric", blobs, {}), ("zero_points", blobs, {"zeros": z}),
+                             ("per_channel", blobs_pc, {"group": K})):
+            it = [0]
+
+            def f(bl=bl, kw=kw):
+                wq.wq_gemm(A1, bl[it[0] % copies], wq.WQ_LAYOUT_TILED, None, N, b, Y=Y1, **kw)
+                it[0] += 1
+
+            t = graph_time(torch, lambda: [f() for _ in range(copies)], reps, 2) / copies
+            res["decode_M1_" + name] = {"us": t * 1e6, "TB/s": byts / t / 1e12}
+        A = torch.from_numpy(synth.draw_act(rng, 4096, K).view(np.int16)).cuda().view(torch.bfloat16)
+        Y = torch.empty((4096, N), dtype=torch.bfloat16, device="cuda")
+        for name, kw in (("symmetric", {}), ("zero_points", {"zeros": z})):
+            t = graph_time(torch, lambda: wq.wq_gemm(A, blobs[0], wq.WQ_LAYOUT_TILED, None, N, b,
+                                                     Y=Y, **kw), max(2, reps // 4), 1)
+            res["prefill_M4096_" + name] = {"ms": t * 1e3,
+                                            "TFLOP/s": 2.0 * 4096 * N * K / t / 1e12}
+        out["b%d" % b] = res
+        del blobs, blobs_pc, A, Y
+    return out
+
+
 def bench_decode_sweep(torch, wq, synth, reps: int, copies: int):
     """wq_gemm at M = 4 and 16 on the decode layer (K 5120 -> N 17408), b = 5,
     6, 7, in TB/s of algorithmic bytes; rotating weight copies as in the
@@ -470,6 +512,9 @@ def main():
         torch.cuda.empty_cache()
         log("w4a8 M=2048/8192")
         result["w4a8"] = bench_w4a8(torch, wq, synth, reps=10)
+        torch.cuda.empty_cache()
+        log("zero points / per-channel scales, b=4/8")
+        result["zero_points"] = bench_zero_points(torch, wq, synth, 10, args.copies)
         torch.cuda.empty_cache()
         log("embedding gather T=4096 from 248320 x 5120, b=6/8")
         result["embed"] = bench_embed(torch, wq, synth, reps=20)
