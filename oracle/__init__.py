@@ -13,6 +13,7 @@ Functions mirror the C entry points:
   quant_act_i8(A)               fp32 per-token int8 quantization -> (Aq, s_a)
   w4a8(A, packed, scales, b=4)  fp64 int8-activation result and magnitude (b = 4: W4A8)
   w4a8_points(Aq, sa, ...)      the same at chosen positions
+  wna16_grouped(A, packed, scales, b, offsets)  grouped (mixture-of-experts) layer
   bf16_rne(x)                   fp64 values -> nearest bf16 bit patterns (ties to even)
   embed(packed, scales, K, b, ids)  quantized embedding gather -> bf16 bits [T, K]
 """
@@ -59,11 +60,13 @@ def _load():
     lib.oracle_quant_act_i8.argtypes = [P, i64, i64, P, P]
     lib.oracle_w4a8.argtypes = [P, i64, i64, i64, P, P, P, ci, ci, P, P, P, P]
     lib.oracle_w4a8_points.argtypes = [P, P, i64, i64, i64, P, P, P, ci, ci, P, P, i64, P, P]
+    lib.oracle_wna16_grouped.argtypes = [P, i64, i64, i64, P, P, P, ci, ci, P, i64, P, P]
     lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
     lib.oracle_bf16_rne.restype = ctypes.c_uint16
     lib.oracle_embed.argtypes = [P, P, P, i64, i64, ci, ci, P, i64, P]
     for f in ("oracle_pack", "oracle_unpack", "oracle_wna16", "oracle_wna16_points",
               "oracle_quant_act_i8", "oracle_w4a8", "oracle_w4a8_points", "oracle_embed",
+              "oracle_wna16_grouped",
               "oracle_num_threads", "oracle_abi", "oracle_little_endian"):
         getattr(lib, f).restype = ci
     _lib = lib
@@ -151,6 +154,28 @@ def wna16_points(A, packed, scales, b, m_idx, n_idx, group: int = 128, zeros=Non
                                     _ptr(m_idx), _ptr(n_idx), P, _ptr(y), _ptr(mag))
     if r != 0:
         raise RuntimeError("oracle_wna16_points failed (%d)" % r)
+    return y, mag
+
+
+def wna16_grouped(A, packed, scales, b, offsets, group: int = 128, zeros=None):
+    """Grouped layer: packed [E*N, W], scales [E*N, K/group], zero points
+    [E*N, K/128] or None; rows [offsets[e], offsets[e+1]) of A through expert e.
+    Return (y, mag) fp64 [M, N]."""
+    A = _c(A, np.uint16)
+    packed = _c(packed, np.uint32)
+    scales = _c(scales, np.uint16)
+    off = _c(offsets, np.int64)
+    M, K = A.shape
+    E = off.size - 1
+    N = packed.shape[0] // E
+    assert packed.shape == (E * N, words_per_row(K, b)) and scales.shape == (E * N, K // group)
+    z, zp = _zeros(zeros, E * N, K)
+    y = np.zeros((M, N), dtype=np.float64)
+    mag = np.zeros((M, N), dtype=np.float64)
+    r = _load().oracle_wna16_grouped(_ptr(A), M, N, K, _ptr(packed), _ptr(scales), zp, b, group,
+                                     _ptr(off), E, _ptr(y), _ptr(mag))
+    if r != 0:
+        raise RuntimeError("oracle_wna16_grouped failed (%d)" % r)
     return y, mag
 
 

@@ -41,6 +41,13 @@
  *    (zeros == NULL is the symmetric case), whatever the scale grouping; a
  *    per-channel scale is the group size K (one scale per row).
  *
+ *  - Grouped (mixture-of-experts) layer.  Same model card, Findings: the
+ *    native checkpoint format has a fused MoE path and the dense layout
+ *    does not.  Reading taken: E experts, each a layer of the shape above
+ *    with its own codes, scales (and zero points); the rows of A are sorted
+ *    by expert, expert e owning rows [off[e], off[e+1]); each row goes
+ *    through its expert's layer.
+ *
  *  - Quantized embedding gather.  Same model card, Findings: an embedding
  *    table in this dense layout needs a gather that reads the dense rows
  *    (the one it names assumes codes never straddle a word); "vLLM Can Run
@@ -406,4 +413,26 @@ int oracle_w4a8_points(const int8_t *Aq, const float *sa, int64_t M, int64_t N, 
         free(c);
     }
     return err;
+}
+
+/* Grouped layer: for expert e, rows [off[e], off[e+1]) of A through expert
+ * e's layer (packed rows e*N .. e*N+N-1 of the stacked [E*N, W] codes, its
+ * scales [E*N, K/group] and zero points [E*N, K/128] rows likewise).
+ * off[0] = 0, off[E] = M, nondecreasing.  y, mag: [M, N]. */
+int oracle_wna16_grouped(const uint16_t *A, int64_t M, int64_t N, int64_t K,
+                         const uint32_t *packed, const uint16_t *scales, const uint8_t *zeros,
+                         int b, int group, const int64_t *off, int64_t E, double *y, double *mag) {
+    if (off[0] != 0 || off[E] != M || group <= 0 || K % group) return -1;
+    const int64_t W = oracle_words_per_row(K, b);
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t m0 = off[e], me = off[e + 1] - off[e];
+        if (me < 0) return -1;
+        if (me == 0) continue;
+        const int r = oracle_wna16(A + m0 * K, me, N, K, packed + e * N * W,
+                                   scales + e * N * (K / group),
+                                   zeros ? zeros + e * N * (K / 128) : NULL, b, group,
+                                   y + m0 * N, mag ? mag + m0 * N : NULL);
+        if (r) return r;
+    }
+    return 0;
 }

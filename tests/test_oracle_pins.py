@@ -590,3 +590,40 @@ def test_w4a8_zero_points_integer_product():
                              zeros=zeros)
     q = codes.astype(np.int64) - np.repeat(zeros.astype(np.int64), 128, axis=1)
     np.testing.assert_array_equal(y, (A_int.astype(np.int64) @ q.T).astype(np.float64))
+
+
+# --- grouped (mixture-of-experts) layer ([card] Findings) ------------------------
+
+@pytest.mark.parametrize("b", [4, 6])
+def test_grouped_constant_experts_closed_form(b):
+    # Expert e has every weight q = e + 1 at scale 1 (codes 2^(b-1) + e + 1):
+    # a row of expert e gives (e + 1) * sum_k a[m,k] in every column.
+    E, N, K = 3, 16, 256
+    off = np.array([0, 2, 2, 7])  # expert 1 has no rows
+    rng = np.random.default_rng(90 + b)
+    A_int = rng.integers(-8, 9, size=(7, K))
+    codes = np.concatenate([np.full((N, K), (1 << (b - 1)) + e + 1) for e in range(E)]).astype(np.uint8)
+    scales = np.full((E * N, K // 128), BF16_ONE, dtype=np.uint16)
+    y, mag = oracle.wna16_grouped(_bf16(A_int.astype(np.float32)), oracle.pack(codes, b), scales,
+                                  b, off)
+    expert = np.repeat(np.arange(E), np.diff(off))
+    expect = ((expert + 1) * A_int.sum(axis=1))[:, None] * np.ones((1, N))
+    np.testing.assert_array_equal(y, expect)
+
+
+def test_grouped_is_invariant_under_expert_order():
+    # Reordering the experts, and their row blocks with them, permutes the
+    # output rows the same way.
+    E, N, K, b = 4, 24, 384, 5
+    rng = np.random.default_rng(95)
+    off = np.array([0, 3, 3, 9, 10])
+    A = synth.draw_act(rng, 10, K)
+    codes = synth.draw_codes(rng, E * N, K, b)
+    scales = synth.draw_scales_halfnormal_signed(rng, E * N, K // 128)
+    y, _ = oracle.wna16_grouped(A, oracle.pack(codes, b), scales, b, off)
+    perm = [2, 0, 3, 1]
+    rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in perm])
+    off2 = np.concatenate([[0], np.cumsum([off[e + 1] - off[e] for e in perm])])
+    wrows = np.concatenate([np.arange(e * N, (e + 1) * N) for e in perm])
+    y2, _ = oracle.wna16_grouped(A[rows], oracle.pack(codes[wrows], b), scales[wrows], b, off2)
+    np.testing.assert_array_equal(y2, y[rows])
