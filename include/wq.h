@@ -176,6 +176,22 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
             const uint16_t *scales_d, const uint8_t *zeros_d, int b, int group, uint16_t *Y_d,
             void *ws_d, int64_t ws_bytes, void *stream);
 
+/* Device.  Grouped (mixture-of-experts) WNA16 layer (model card
+ * "Qwen3.8-27B-INT6-Mixed-AutoRound", Findings: the dense format has no
+ * fused MoE path).  E experts, each a tiled blob (wq_repack output for
+ * N x K at b) at W_d + e * expert_bytes (expert_bytes >= that blob's size,
+ * a multiple of 16); the rows of A_d bf16 [M, K] are sorted by expert:
+ * expert e owns rows [offsets[e], offsets[e+1]) (a host array of E + 1
+ * values, offsets[0] = 0, offsets[E] = M, nondecreasing), and Y_d bf16
+ * [M, N] row m is row m of A through its expert's layer.  zeros_d: NULL or
+ * uint8 [E * N, K/128] (b = 4, 8).  ws_d / ws_bytes: at least the largest
+ * wq_workspace_bytes(WQ_OP_GEMM, rows of one expert, N, K, b, group).
+ * Experts without rows read nothing. */
+int wq_gemm_grouped(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
+                    int64_t expert_bytes, const uint8_t *zeros_d, const int64_t *offsets,
+                    int64_t E, int b, int group, uint16_t *Y_d, void *ws_d, int64_t ws_bytes,
+                    void *stream);
+
 /* Device.  Per-token dynamic int8 activation quantization (club-3090
  * discussion #733, "Under the hood"), fp32 throughout:
  *   sa_d[m] = max_k |A[m,k]| / 127   (IEEE division)

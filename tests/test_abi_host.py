@@ -16,7 +16,7 @@ from weight_only_bit_wq_amd import synth
 def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(wq.lib_path)
     names = wq.declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert wq.wq_abi_version() == 2
@@ -208,3 +208,29 @@ def test_workspace_zero_region_constant():
         m = re.search(r"#define WQ_WORKSPACE_ZERO_BYTES \(\(int64_t\)(\d+) << (\d+)\)", f.read())
     assert m, "WQ_WORKSPACE_ZERO_BYTES not found"
     assert int(m.group(1)) << int(m.group(2)) == wq.WORKSPACE_ZERO_BYTES
+
+
+def test_grouped_validation():
+    # Offsets are a host array, checked before any device work.
+    lib = wq._load()
+    c = ctypes.c_void_p
+    A = c(ALIGNED)
+    N, K, b = 256, 512, 6
+    eb = wq.wq_repacked_bytes(wq.WQ_LAYOUT_TILED, N, K, b)
+
+    def call(off, M, E=None, expert_bytes=eb, bits=b, Z=None, ws_bytes=1 << 30):
+        off = np.asarray(off, dtype=np.int64)
+        E = off.size - 1 if E is None else E
+        return lib.wq_gemm_grouped(A, M, N, K, A, expert_bytes, Z, wq._ptr(off), E, bits, 128,
+                                   A, A, ws_bytes, None)
+
+    assert call([1, 3, 5], 5) == wq.WQ_ERR_INVALID_ARG        # offsets[0] != 0
+    assert call([0, 3, 4], 5) == wq.WQ_ERR_INVALID_ARG        # offsets[E] != M
+    assert call([0, 4, 3, 5], 5) == wq.WQ_ERR_INVALID_ARG     # decreasing
+    assert call([0, 5], 5, expert_bytes=eb - 16) == wq.WQ_ERR_INVALID_ARG
+    assert call([0, 5], 5, expert_bytes=eb + 8) == wq.WQ_ERR_INVALID_ARG   # not a multiple of 16
+    assert call([0, 5], 5, bits=9) == wq.WQ_ERR_UNSUPPORTED_BITS
+    assert call([0, 5], 5, Z=A) == wq.WQ_ERR_ZERO_POINTS      # b = 6 has no zero points
+    assert call([0, 5], 5, E=0) == wq.WQ_ERR_INVALID_ARG
+    assert call([0, 20, 20], 20, ws_bytes=0) == wq.WQ_ERR_WORKSPACE
+    assert call([0, 0, 0], 0) == wq.WQ_OK                     # no rows: no-op

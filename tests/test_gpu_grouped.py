@@ -1,0 +1,64 @@
+"""GPU parity of the grouped (mixture-of-experts) WNA16 layer (wq_gemm_grouped,
+through the C ABI) against the CPU oracle: experts with no rows, decode-sized
+and prefill-sized row blocks in one call, with and without zero points.
+Page: model card "Qwen3.8-27B-INT6-Mixed-AutoRound", Findings (the dense
+format has no fused MoE path)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_bit_wq_amd as wq
+from weight_only_bit_wq_amd import synth
+from gpu_util import assert_wna16, dev_bf16, dev_words, host_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _experts(E, N, K, b, seed, zp=False):
+    rng = np.random.default_rng(seed)
+    codes = synth.draw_codes(rng, E * N, K, b)
+    scales = synth.draw_scales_halfnormal_signed(rng, E * N, K // 128)
+    zeros = rng.integers(0, 1 << b, size=(E * N, K // 128), dtype=np.uint8) if zp else None
+    packed = wq.wq_pack(codes, b)
+    eb = wq.wq_repacked_bytes(wq.WQ_LAYOUT_TILED, N, K, b)
+    W = torch.empty(E * eb, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        wq.wq_repack(dev_words(packed[e * N:(e + 1) * N]), dev_bf16(scales[e * N:(e + 1) * N]),
+                     K, b, out=W[e * eb:(e + 1) * eb])
+    return packed, scales, zeros, W, eb
+
+
+@pytest.mark.parametrize("b,zp", [(4, False), (4, True), (6, False), (8, True)])
+def test_grouped_mixed_sizes(b, zp):
+    E, N, K = 7, 200, 1024
+    sizes = [3, 0, 1, 40, 16, 0, 17]   # empty, decode row tiles, prefill
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    packed, scales, zeros, W, eb = _experts(E, N, K, b, 3000 + b + 10 * zp, zp)
+    A = synth.draw_act(np.random.default_rng(3001 + b), int(off[-1]), K)
+    print("grouped b=%d zp=%d rows=%s" % (b, zp, sizes), flush=True)
+    Z = torch.from_numpy(zeros).cuda() if zp else None
+    Y = wq.wq_gemm_grouped(dev_bf16(A), W, eb, off, N, b, zeros=Z)
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.wna16_grouped(A, packed, scales, b, off, zeros=zeros)
+    assert_wna16(host_bf16_bits(Y), y_ref, mag, "grouped b=%d zp=%d" % (b, zp))
+
+
+def test_grouped_decode_routing():
+    # One token routed to 4 of 16 experts (rows sorted by expert), b = 4.
+    E, N, K, b = 16, 512, 2048, 4
+    packed, scales, _, W, eb = _experts(E, N, K, b, 3100)
+    active = [2, 5, 11, 14]
+    sizes = [1 if e in active else 0 for e in range(E)]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    A = np.repeat(synth.draw_act(np.random.default_rng(3101), 1, K), 4, axis=0)
+    Y = wq.wq_gemm_grouped(dev_bf16(A), W, eb, off, N, b)
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.wna16_grouped(A, packed, scales, b, off)
+    assert_wna16(host_bf16_bits(Y), y_ref, mag, "grouped decode routing")
+    # each output row is that expert's dense layer on the token
+    for i, e in enumerate(active):
+        blob = W[e * eb:(e + 1) * eb]
+        Ye = wq.wq_gemm(dev_bf16(A[i:i + 1]), blob, wq.WQ_LAYOUT_TILED, None, N, b)
+        torch.cuda.synchronize()
+        assert torch.equal(Ye.view(torch.int16), Y[i:i + 1].view(torch.int16))

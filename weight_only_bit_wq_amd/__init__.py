@@ -25,7 +25,7 @@ __all__ = [
     "wq_abi_version", "wq_status_str", "wq_last_hip_error", "wq_device_supported",
     "wq_packed_words_per_row", "wq_pack", "wq_unpack", "wq_repacked_bytes", "wq_repack",
     "wq_unpack_dev", "wq_workspace_bytes", "wq_gemm", "wq_quant_act_i8", "wq_gemm_a8",
-    "wq_embed",
+    "wq_embed", "wq_gemm_grouped",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +103,7 @@ def _load():
             "wq_quant_act_i8": ([P, L, L, P, P, P], I),
             "wq_gemm_a8": ([P, L, L, L, P, I, P, P, I, I, P, I, P, L, P], I),
             "wq_embed": ([P, P, P, L, L, I, I, P, L, P, P], I),
+            "wq_gemm_grouped": ([P, L, L, L, P, L, P, P, L, I, I, P, P, L, P], I),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -282,6 +283,36 @@ def wq_gemm(A_d, W_d, layout: int, scales_d, N: int, b: int, group: int = GROUP,
         ws_buf, ws_bytes = ws, ws.numel() * ws.element_size()
     _check("wq_gemm", _load().wq_gemm(_ptr(A_d), M, N, K, _ptr(W_d), layout, _ptr(scales_d),
                                       _ptr(zeros), b, group, _ptr(Y), _ptr(ws_buf), ws_bytes, st))
+    return Y
+
+
+def wq_gemm_grouped(A_d, W_d, expert_bytes: int, offsets, N: int, b: int, group: int = GROUP,
+                    Y=None, ws=None, stream=None, zeros=None):
+    """Device: grouped (mixture-of-experts) layer.  W_d: E tiled blobs at
+    expert_bytes apart (uint8); offsets: host int64 [E + 1], rows of A_d sorted
+    by expert.  Returns Y bf16 [M, N]."""
+    import torch
+    _require_cuda("A_d", A_d, torch.bfloat16)
+    _require_cuda("W_d", W_d)
+    M, K = A_d.shape
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    E = off.size - 1
+    if zeros is not None:
+        _require_cuda("zeros_d", zeros, torch.uint8, (E * N, K // GROUP))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=A_d.device)
+    else:
+        _require_cuda("Y", Y, torch.bfloat16, (M, N))
+    st = _stream(stream)
+    need = max([0] + [wq_workspace_bytes(WQ_OP_GEMM, int(off[e + 1] - off[e]), N, K, b, group)
+                      for e in range(E)])
+    if ws is None:
+        ws_buf, ws_bytes = _workspace(need, A_d.device, st)
+    else:
+        ws_buf, ws_bytes = ws, ws.numel() * ws.element_size()
+    _check("wq_gemm_grouped", _load().wq_gemm_grouped(
+        _ptr(A_d), M, N, K, _ptr(W_d), expert_bytes, _ptr(zeros), _ptr(off), E, b, group,
+        _ptr(Y), _ptr(ws_buf), ws_bytes, st))
     return Y
 
 

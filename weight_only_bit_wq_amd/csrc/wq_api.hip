@@ -97,6 +97,17 @@ void parallel_rows(int64_t N, int64_t work_per_row, F f) {
     for (auto &t : th) t.join();
 }
 
+// The WNA16 layer on one weight set: the decode kernel up to kDecodeMaxM
+// rows, the prefill kernel above.
+hipError_t gemm_dispatch(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
+                         bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
+                         uint16_t *Y, void *ws, hipStream_t stream) {
+    if (M <= wq::kDecodeMaxM)
+        return wq::launch_decode(A, M, N, K, W, tiled, scales, zeros, b, Y, ws,
+                                 wq::decode_plan(M, N, K, b), stream);
+    return wq::launch_prefill(A, M, N, K, W, tiled, scales, zeros, b, Y, ws, stream);
+}
+
 int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int b) {
     if (M == 0) return 0;
     if (M <= wq::kDecodeMaxM) return wq::decode_plan(M, N, K, b).ws_bytes;
@@ -273,17 +284,46 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
     const int64_t need = gemm_ws_bytes(M, N, K, b);
     if (need > 0 && (!ws_d || ws_bytes < need)) return WQ_ERR_WORKSPACE;
     if (int s = check_device()) return s;
-    const bool tiled = layout == WQ_LAYOUT_TILED;
-    hipError_t e;
-    if (M <= wq::kDecodeMaxM) {
-        const wq::DecodePlan p = wq::decode_plan(M, N, K, b);
-        e = wq::launch_decode(A_d, M, N, K, W_d, tiled, scales_d, zeros_d, b, Y_d, ws_d, p,
-                              (hipStream_t)stream);
-    } else {
-        e = wq::launch_prefill(A_d, M, N, K, W_d, tiled, scales_d, zeros_d, b, Y_d, ws_d,
-                               (hipStream_t)stream);
-    }
+    const hipError_t e = gemm_dispatch(A_d, M, N, K, W_d, layout == WQ_LAYOUT_TILED, scales_d,
+                                       zeros_d, b, Y_d, ws_d, (hipStream_t)stream);
     return e == hipSuccess ? WQ_OK : hip_fail(e);
+}
+
+int wq_gemm_grouped(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
+                    int64_t expert_bytes, const uint8_t *zeros_d, const int64_t *offsets,
+                    int64_t E, int b, int group, uint16_t *Y_d, void *ws_d, int64_t ws_bytes,
+                    void *stream) {
+    if (!dims_ok(M, N, K) || E <= 0 || !offsets) return WQ_ERR_INVALID_ARG;
+    if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
+    if (int s = check_group(K, group)) return s;
+    if (int s = check_zeros(zeros_d, b, false)) return s;
+    if (expert_bytes < wq_repacked_bytes(WQ_LAYOUT_TILED, N, K, b, kGroup) || expert_bytes % 16)
+        return WQ_ERR_INVALID_ARG;
+    if (offsets[0] != 0 || offsets[E] != M) return WQ_ERR_INVALID_ARG;
+    int64_t need = 0;
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t me = offsets[e + 1] - offsets[e];
+        if (me < 0) return WQ_ERR_INVALID_ARG;
+        need = std::max(need, gemm_ws_bytes(me, N, K, b));
+    }
+    if (M == 0) return WQ_OK;
+    if (!A_d || !W_d || !Y_d) return WQ_ERR_INVALID_ARG;
+    if (!aligned16(A_d) || !aligned16(W_d) || !aligned16(Y_d) || (ws_d && !aligned16(ws_d)))
+        return WQ_ERR_MISALIGNED;
+    if (need > 0 && (!ws_d || ws_bytes < need)) return WQ_ERR_WORKSPACE;
+    if (int s = check_device()) return s;
+    // One launch sequence per expert with rows, in order on the stream; the
+    // workspace is reused (each call leaves its counter region zero).
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t m0 = offsets[e], me = offsets[e + 1] - m0;
+        if (me == 0) continue;
+        const hipError_t err = gemm_dispatch(
+            A_d + m0 * K, me, N, K, static_cast<const uint8_t *>(W_d) + e * expert_bytes, true,
+            nullptr, zeros_d ? zeros_d + e * N * (K / kGroup) : nullptr, b, Y_d + m0 * N, ws_d,
+            (hipStream_t)stream);
+        if (err != hipSuccess) return hip_fail(err);
+    }
+    return WQ_OK;
 }
 
 int wq_quant_act_i8(const uint16_t *A_d, int64_t M, int64_t K, int8_t *Aq_d, float *sa_d,
