@@ -210,6 +210,48 @@ def bench_zero_points(torch, wq, synth, reps: int, copies: int):
     return out
 
 
+def bench_grouped(torch, wq, synth, reps: int):
+    """Grouped (mixture-of-experts) layer, synthetic: 64 experts of
+    K 5120 -> N 2048 at b = 6, top-4 routing.  Decode: one token (4 experts,
+    one row each; algorithmic bytes = the 4 experts' weights), 16 calls with
+    different routings per timed replay so the experts read (~500 MB) do
+    not stay in the Infinity Cache; prefill: 1024 tokens (4096 rows, uniform
+    random routing; 2 * rows * N * K flops)."""
+    E, N, K, b, topk = 64, 2048, 5120, 6, 4
+    rng = np.random.default_rng(10)
+    eb = wq.wq_repacked_bytes(wq.WQ_LAYOUT_TILED, N, K, b)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(10)
+    words = torch.randint(-(1 << 31), 1 << 31, (N, K * b // 32), dtype=torch.int32, device="cuda",
+                          generator=gen)
+    W = torch.empty(E * eb, dtype=torch.uint8, device="cuda")
+    for e in range(E):  # distinct scales per expert, codes shared (values do not change timing)
+        s = (torch.randn((N, K // 128), device="cuda", generator=gen) * 0.01).to(torch.bfloat16)
+        wq.wq_repack(words, s, K, b, out=W[e * eb:(e + 1) * eb])
+    out = {}
+    for name, T, calls in (("decode_T1", 1, 16), ("prefill_T1024", 1024, 1)):
+        offs = []
+        for _ in range(calls):
+            experts = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(T)])
+            sizes = np.bincount(experts.ravel(), minlength=E)
+            offs.append(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64))
+        rows = T * topk
+        A = torch.from_numpy(synth.draw_act(rng, rows, K).view(np.int16)).cuda().view(torch.bfloat16)
+        Y = torch.empty((rows, N), dtype=torch.bfloat16, device="cuda")
+
+        def fn():
+            for off in offs:
+                wq.wq_gemm_grouped(A, W, eb, off, N, b, Y=Y)
+
+        t = graph_time(torch, fn, reps, 2) / calls
+        active = float(np.mean([(np.diff(off) > 0).sum() for off in offs]))
+        byts = active * algorithmic_bytes(0, N, K, b) + rows * K * 2 + rows * N * 2
+        out[name] = {"experts": E, "active": active, "rows": rows, "us": t * 1e6,
+                     "TB/s": byts / t / 1e12, "TFLOP/s": 2.0 * rows * N * K / t / 1e12}
+    del W
+    return out
+
+
 def bench_decode_sweep(torch, wq, synth, reps: int, copies: int):
     """wq_gemm at M = 4 and 16 on the decode layer (K 5120 -> N 17408), b = 5,
     6, 7, in TB/s of algorithmic bytes; rotating weight copies as in the
@@ -515,6 +557,9 @@ def main():
         torch.cuda.empty_cache()
         log("zero points / per-channel scales, b=4/8")
         result["zero_points"] = bench_zero_points(torch, wq, synth, 10, args.copies)
+        torch.cuda.empty_cache()
+        log("grouped layer: 64 experts 5120 -> 2048, b=6, top-4")
+        result["grouped"] = bench_grouped(torch, wq, synth, 10)
         torch.cuda.empty_cache()
         log("embedding gather T=4096 from 248320 x 5120, b=6/8")
         result["embed"] = bench_embed(torch, wq, synth, reps=20)

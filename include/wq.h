@@ -184,9 +184,13 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
  * expert e owns rows [offsets[e], offsets[e+1]) (a host array of E + 1
  * values, offsets[0] = 0, offsets[E] = M, nondecreasing), and Y_d bf16
  * [M, N] row m is row m of A through its expert's layer.  zeros_d: NULL or
- * uint8 [E * N, K/128] (b = 4, 8).  ws_d / ws_bytes: at least the largest
- * wq_workspace_bytes(WQ_OP_GEMM, rows of one expert, N, K, b, group).
- * Experts without rows read nothing. */
+ * uint8 [E * N, K/128] (b = 4, 8).  ws_d / ws_bytes: at least
+ * wq_grouped_workspace_bytes (the same counter-region rule as wq_gemm).
+ * Experts with at most 16 rows run in one decode launch (one table entry per
+ * expert, passed as a kernel argument), the others in one prefill launch
+ * over their 256-row tiles; experts without rows read nothing. */
+int64_t wq_grouped_workspace_bytes(const int64_t *offsets, int64_t E, int64_t N, int64_t K,
+                                   int b, int group);
 int wq_gemm_grouped(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
                     int64_t expert_bytes, const uint8_t *zeros_d, const int64_t *offsets,
                     int64_t E, int b, int group, uint16_t *Y_d, void *ws_d, int64_t ws_bytes,

@@ -16,7 +16,7 @@ from weight_only_bit_wq_amd import synth
 def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(wq.lib_path)
     names = wq.declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert wq.wq_abi_version() == 2

@@ -62,3 +62,26 @@ def test_grouped_decode_routing():
         Ye = wq.wq_gemm(dev_bf16(A[i:i + 1]), blob, wq.WQ_LAYOUT_TILED, None, N, b)
         torch.cuda.synchronize()
         assert torch.equal(Ye.view(torch.int16), Y[i:i + 1].view(torch.int16))
+
+
+@pytest.mark.parametrize("b", [4, 6])
+def test_grouped_many_experts_ragged(b):
+    # 40 experts with a ragged N (not a multiple of 64), most with decode-
+    # sized row blocks, a few with prefill-sized ones (two 256-row tiles).
+    E, N, K = 40, 200, 640
+    rng = np.random.default_rng(3200 + b)
+    sizes = rng.integers(0, 6, size=E)
+    sizes[[3, 17]] = [300, 20]
+    sizes[[5, 6, 30]] = 0
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    packed, scales, _, W, eb = _experts(E, N, K, b, 3210 + b)
+    A = synth.draw_act(rng, int(off[-1]), K)
+    ws = torch.zeros(wq.wq_grouped_workspace_bytes(off, N, K, b) + 256, dtype=torch.uint8,
+                     device="cuda")
+    Y0 = wq.wq_gemm_grouped(dev_bf16(A), W, eb, off, N, b, ws=ws)
+    Y1 = wq.wq_gemm_grouped(dev_bf16(A), W, eb, off, N, b, ws=ws)
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.wna16_grouped(A, packed, scales, b, off)
+    assert_wna16(host_bf16_bits(Y0), y_ref, mag, "grouped many b=%d" % b)
+    assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
+    assert not ws[:wq.WORKSPACE_ZERO_BYTES].any()

@@ -25,7 +25,7 @@ __all__ = [
     "wq_abi_version", "wq_status_str", "wq_last_hip_error", "wq_device_supported",
     "wq_packed_words_per_row", "wq_pack", "wq_unpack", "wq_repacked_bytes", "wq_repack",
     "wq_unpack_dev", "wq_workspace_bytes", "wq_gemm", "wq_quant_act_i8", "wq_gemm_a8",
-    "wq_embed", "wq_gemm_grouped",
+    "wq_embed", "wq_gemm_grouped", "wq_grouped_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -104,6 +104,7 @@ def _load():
             "wq_gemm_a8": ([P, L, L, L, P, I, P, P, I, I, P, I, P, L, P], I),
             "wq_embed": ([P, P, P, L, L, I, I, P, L, P, P], I),
             "wq_gemm_grouped": ([P, L, L, L, P, L, P, P, L, I, I, P, P, L, P], I),
+            "wq_grouped_workspace_bytes": ([P, L, L, L, I, I], L),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -286,6 +287,12 @@ def wq_gemm(A_d, W_d, layout: int, scales_d, N: int, b: int, group: int = GROUP,
     return Y
 
 
+def wq_grouped_workspace_bytes(offsets, N: int, K: int, b: int, group: int = GROUP) -> int:
+    """Workspace bytes of a grouped call with these host offsets (-1: invalid)."""
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    return int(_load().wq_grouped_workspace_bytes(_ptr(off), off.size - 1, N, K, b, group))
+
+
 def wq_gemm_grouped(A_d, W_d, expert_bytes: int, offsets, N: int, b: int, group: int = GROUP,
                     Y=None, ws=None, stream=None, zeros=None):
     """Device: grouped (mixture-of-experts) layer.  W_d: E tiled blobs at
@@ -304,8 +311,9 @@ def wq_gemm_grouped(A_d, W_d, expert_bytes: int, offsets, N: int, b: int, group:
     else:
         _require_cuda("Y", Y, torch.bfloat16, (M, N))
     st = _stream(stream)
-    need = max([0] + [wq_workspace_bytes(WQ_OP_GEMM, int(off[e + 1] - off[e]), N, K, b, group)
-                      for e in range(E)])
+    need = int(_load().wq_grouped_workspace_bytes(_ptr(off), E, N, K, b, group))
+    if need < 0:
+        raise WQError("wq_grouped_workspace_bytes", WQ_ERR_INVALID_ARG)
     if ws is None:
         ws_buf, ws_bytes = _workspace(need, A_d.device, st)
     else:

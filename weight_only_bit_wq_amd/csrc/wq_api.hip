@@ -114,6 +114,70 @@ int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int b) {
     return wq::prefill_ws_bytes(M, N, K, b);
 }
 
+// The launches of a grouped call: experts with at most kDecodeMaxM rows go
+// into decode tables (one entry per expert), the others into prefill tables
+// (one entry per 256-row tile); a table is emitted when full or at the end.
+// emit(is_decode, table, max rows of its entries).
+template <class F>
+void grouped_tables(const int64_t *off, int64_t E, int64_t N, int64_t expert_bytes, F emit) {
+    wq::GroupTable dec{}, pre{};
+    int dec_max = 0;
+    dec.per = (int)((N + 63) / 64);
+    dec.expert_bytes = pre.expert_bytes = expert_bytes;
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t m0 = off[e], me = off[e + 1] - off[e];
+        if (me == 0) continue;
+        if (me <= wq::kDecodeMaxM) {
+            dec.e[dec.n] = (int)e;
+            dec.m0[dec.n] = (int)m0;
+            dec.me[dec.n] = (int)me;
+            dec_max = std::max(dec_max, (int)me);
+            if (++dec.n == wq::kMaxGroups) {
+                emit(true, dec, dec_max);
+                dec.n = 0;
+                dec_max = 0;
+            }
+            continue;
+        }
+        for (int64_t r = 0; r < me; r += wq::kPrefillTileM) {
+            pre.e[pre.n] = (int)e;
+            pre.m0[pre.n] = (int)(m0 + r);
+            pre.me[pre.n] = (int)std::min<int64_t>(wq::kPrefillTileM, me - r);
+            if (++pre.n == wq::kMaxGroups) {
+                emit(false, pre, wq::kPrefillTileM);
+                pre.n = 0;
+            }
+        }
+    }
+    if (dec.n) emit(true, dec, dec_max);
+    if (pre.n) emit(false, pre, wq::kPrefillTileM);
+}
+
+// Decode plan of a grouped decode table: the plan for its largest row count
+// over the grid's columns, entries * ceil(N/64) blocks of 64, so its row
+// blocks (tickets, partial sums, workspace) are exactly the grid's.
+wq::DecodePlan grouped_decode_plan(const wq::GroupTable &t, int max_me, int64_t N, int64_t K,
+                                   int b) {
+    (void)N;
+    return wq::decode_plan(max_me, (int64_t)t.n * t.per * 64, K, b);
+}
+
+int64_t grouped_ws_bytes(const int64_t *off, int64_t E, int64_t M, int64_t N, int64_t K, int b) {
+    int64_t need = 0;
+    grouped_tables(off, E, N, 0, [&](bool is_dec, const wq::GroupTable &t, int max_me) {
+        need = std::max(need, is_dec ? grouped_decode_plan(t, max_me, N, K, b).ws_bytes
+                                     : wq::prefill_grouped_ws_bytes(M, K));
+    });
+    return need;
+}
+
+int check_offsets(const int64_t *off, int64_t E, int64_t M) {
+    if (!off || E <= 0 || off[0] != 0 || off[E] != M) return WQ_ERR_INVALID_ARG;
+    for (int64_t e = 0; e < E; ++e)
+        if (off[e + 1] < off[e]) return WQ_ERR_INVALID_ARG;
+    return WQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,41 +353,52 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
     return e == hipSuccess ? WQ_OK : hip_fail(e);
 }
 
+int64_t wq_grouped_workspace_bytes(const int64_t *offsets, int64_t E, int64_t N, int64_t K,
+                                   int b, int group) {
+    if (!dims_ok(0, N, K) || !valid_bits(b) || check_group(K, group) != WQ_OK || !offsets ||
+        E <= 0)
+        return -1;
+    const int64_t M = offsets[E];
+    if (check_offsets(offsets, E, M) != WQ_OK || M >= (1ll << 31)) return -1;
+    return grouped_ws_bytes(offsets, E, M, N, K, b);
+}
+
 int wq_gemm_grouped(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
                     int64_t expert_bytes, const uint8_t *zeros_d, const int64_t *offsets,
                     int64_t E, int b, int group, uint16_t *Y_d, void *ws_d, int64_t ws_bytes,
                     void *stream) {
-    if (!dims_ok(M, N, K) || E <= 0 || !offsets) return WQ_ERR_INVALID_ARG;
+    if (!dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
+    if (int s = check_offsets(offsets, E, M)) return s;
     if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
     if (int s = check_group(K, group)) return s;
     if (int s = check_zeros(zeros_d, b, false)) return s;
     if (expert_bytes < wq_repacked_bytes(WQ_LAYOUT_TILED, N, K, b, kGroup) || expert_bytes % 16)
         return WQ_ERR_INVALID_ARG;
-    if (offsets[0] != 0 || offsets[E] != M) return WQ_ERR_INVALID_ARG;
-    int64_t need = 0;
-    for (int64_t e = 0; e < E; ++e) {
-        const int64_t me = offsets[e + 1] - offsets[e];
-        if (me < 0) return WQ_ERR_INVALID_ARG;
-        need = std::max(need, gemm_ws_bytes(me, N, K, b));
-    }
     if (M == 0) return WQ_OK;
     if (!A_d || !W_d || !Y_d) return WQ_ERR_INVALID_ARG;
     if (!aligned16(A_d) || !aligned16(W_d) || !aligned16(Y_d) || (ws_d && !aligned16(ws_d)))
         return WQ_ERR_MISALIGNED;
+    const int64_t need = grouped_ws_bytes(offsets, E, M, N, K, b);
     if (need > 0 && (!ws_d || ws_bytes < need)) return WQ_ERR_WORKSPACE;
     if (int s = check_device()) return s;
-    // One launch sequence per expert with rows, in order on the stream; the
-    // workspace is reused (each call leaves its counter region zero).
-    for (int64_t e = 0; e < E; ++e) {
-        const int64_t m0 = offsets[e], me = offsets[e + 1] - m0;
-        if (me == 0) continue;
-        const hipError_t err = gemm_dispatch(
-            A_d + m0 * K, me, N, K, static_cast<const uint8_t *>(W_d) + e * expert_bytes, true,
-            nullptr, zeros_d ? zeros_d + e * N * (K / kGroup) : nullptr, b, Y_d + m0 * N, ws_d,
-            (hipStream_t)stream);
-        if (err != hipSuccess) return hip_fail(err);
-    }
-    return WQ_OK;
+    // One launch per table, in order on the stream (one workspace: each
+    // leaves the counter region zero; the pre-pass matrix is computed once).
+    hipError_t err = hipSuccess;
+    bool prepass = true;
+    grouped_tables(offsets, E, N, expert_bytes,
+                   [&](bool is_dec, const wq::GroupTable &t, int max_me) {
+        if (err != hipSuccess) return;
+        if (is_dec) {
+            err = wq::launch_decode_grouped(A_d, N, K, W_d, zeros_d, b, Y_d, ws_d,
+                                            grouped_decode_plan(t, max_me, N, K, b), t,
+                                            (hipStream_t)stream);
+        } else {
+            err = wq::launch_prefill_grouped(A_d, M, N, K, W_d, zeros_d, b, Y_d, ws_d, t,
+                                             prepass, (hipStream_t)stream);
+            prepass = false;
+        }
+    });
+    return err == hipSuccess ? WQ_OK : hip_fail(err);
 }
 
 int wq_quant_act_i8(const uint16_t *A_d, int64_t M, int64_t K, int8_t *Aq_d, float *sa_d,

@@ -9,17 +9,24 @@ namespace wq {
 
 constexpr int kGroupSize = 128;
 
-template <int B>
+template <int B, class GT>
 hipError_t decode_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
                     bool tiled, const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
-                    void *ws, const DecodePlan &p, hipStream_t stream);
-extern template hipError_t decode_b<2>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, hipStream_t);
-extern template hipError_t decode_b<3>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, hipStream_t);
-extern template hipError_t decode_b<4>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, hipStream_t);
-extern template hipError_t decode_b<5>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, hipStream_t);
-extern template hipError_t decode_b<6>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, hipStream_t);
-extern template hipError_t decode_b<7>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, hipStream_t);
-extern template hipError_t decode_b<8>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, hipStream_t);
+                    void *ws, const DecodePlan &p, const GT &gt, hipStream_t stream);
+extern template hipError_t decode_b<2, NoGroups>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const NoGroups &, hipStream_t);
+extern template hipError_t decode_b<2, GroupTable>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const GroupTable &, hipStream_t);
+extern template hipError_t decode_b<3, NoGroups>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const NoGroups &, hipStream_t);
+extern template hipError_t decode_b<3, GroupTable>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const GroupTable &, hipStream_t);
+extern template hipError_t decode_b<4, NoGroups>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const NoGroups &, hipStream_t);
+extern template hipError_t decode_b<4, GroupTable>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const GroupTable &, hipStream_t);
+extern template hipError_t decode_b<5, NoGroups>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const NoGroups &, hipStream_t);
+extern template hipError_t decode_b<5, GroupTable>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const GroupTable &, hipStream_t);
+extern template hipError_t decode_b<6, NoGroups>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const NoGroups &, hipStream_t);
+extern template hipError_t decode_b<6, GroupTable>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const GroupTable &, hipStream_t);
+extern template hipError_t decode_b<7, NoGroups>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const NoGroups &, hipStream_t);
+extern template hipError_t decode_b<7, GroupTable>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const GroupTable &, hipStream_t);
+extern template hipError_t decode_b<8, NoGroups>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const NoGroups &, hipStream_t);
+extern template hipError_t decode_b<8, GroupTable>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool, const uint16_t *, const uint8_t *, uint16_t *, void *, const DecodePlan &, const GroupTable &, hipStream_t);
 
 static int decode_mt(int64_t M) {
     if (M <= 1) return 1;
@@ -75,13 +82,28 @@ hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, con
                          bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
                          uint16_t *Y, void *ws, const DecodePlan &p, hipStream_t stream) {
     switch (b) {
-        case 2: return decode_b<2>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
-        case 3: return decode_b<3>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
-        case 4: return decode_b<4>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
-        case 5: return decode_b<5>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
-        case 6: return decode_b<6>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
-        case 7: return decode_b<7>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
-        case 8: return decode_b<8>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
+        case 2: return decode_b<2>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, NoGroups{}, stream);
+        case 3: return decode_b<3>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, NoGroups{}, stream);
+        case 4: return decode_b<4>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, NoGroups{}, stream);
+        case 5: return decode_b<5>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, NoGroups{}, stream);
+        case 6: return decode_b<6>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, NoGroups{}, stream);
+        case 7: return decode_b<7>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, NoGroups{}, stream);
+        case 8: return decode_b<8>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, NoGroups{}, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_grouped(const uint16_t *A, int64_t N, int64_t K, const void *W,
+                                 const uint8_t *zeros, int b, uint16_t *Y, void *ws,
+                                 const DecodePlan &p, const GroupTable &gt, hipStream_t stream) {
+    switch (b) {
+        case 2: return decode_b<2>(A, 0, N, K, W, true, nullptr, zeros, Y, ws, p, gt, stream);
+        case 3: return decode_b<3>(A, 0, N, K, W, true, nullptr, zeros, Y, ws, p, gt, stream);
+        case 4: return decode_b<4>(A, 0, N, K, W, true, nullptr, zeros, Y, ws, p, gt, stream);
+        case 5: return decode_b<5>(A, 0, N, K, W, true, nullptr, zeros, Y, ws, p, gt, stream);
+        case 6: return decode_b<6>(A, 0, N, K, W, true, nullptr, zeros, Y, ws, p, gt, stream);
+        case 7: return decode_b<7>(A, 0, N, K, W, true, nullptr, zeros, Y, ws, p, gt, stream);
+        case 8: return decode_b<8>(A, 0, N, K, W, true, nullptr, zeros, Y, ws, p, gt, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -3,7 +3,12 @@
 #include "wq_decode_kernel.h"
 
 namespace wq {
-template hipError_t decode_b<4>(const uint16_t *, int64_t, int64_t, int64_t, const void *, bool,
-                                const uint16_t *, const uint8_t *, uint16_t *, void *,
-                                const DecodePlan &, hipStream_t);
+template hipError_t decode_b<4, NoGroups>(const uint16_t *, int64_t, int64_t, int64_t,
+                                          const void *, bool, const uint16_t *, const uint8_t *,
+                                          uint16_t *, void *, const DecodePlan &,
+                                          const NoGroups &, hipStream_t);
+template hipError_t decode_b<4, GroupTable>(const uint16_t *, int64_t, int64_t, int64_t,
+                                            const void *, bool, const uint16_t *,
+                                            const uint8_t *, uint16_t *, void *,
+                                            const DecodePlan &, const GroupTable &, hipStream_t);
 }  // namespace wq

@@ -339,22 +339,37 @@ __device__ __forceinline__ void group_terms_mf(const uint32_t *w, const u32x4 *a
 // layers): no prefetch register set, so more waves fit per SIMD.  Used for
 // the matrix-core row tiles; with one row of A the prefetching form measured
 // 3.5% faster even then, so it keeps that one.
-template <int B, int MT, int W, class WL, bool ONE, bool ZP>
+// GT: NoGroups, or a GroupTable (one entry per expert; the grid's 64-row
+// blocks run entry by entry, and each workgroup rebases A, Y, the weights
+// and the zero points to its expert).
+template <int B, int MT, int W, class WL, bool ONE, bool ZP, class GT>
 __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restrict__ A, int M,
                                                         int N, int K, WL wl,
                                                         const uint8_t *__restrict__ zeros,
                                                         uint16_t *__restrict__ Y,
                                                         float *__restrict__ part,
                                                         unsigned *__restrict__ counters,
-                                                        int splits, int gps, int tstride) {
+                                                        int splits, int gps, int tstride,
+                                                        const GT gt) {
     static_assert(W * MT <= 128, "LDS reduction table");
     static_assert(MT == 1 || MT % 4 == 0, "row tiles above 1 take the matrix-core form");
     constexpr bool MF = MT >= 4;
     __shared__ float red[W][MT][64];
 
     const int G = K / kGroup;
-    const int R = blockIdx.x / splits;
-    const int s = blockIdx.x - R * splits;
+    const int RB = blockIdx.x / splits;  // 64-row block of the grid (tickets, partials)
+    const int s = blockIdx.x - RB * splits;
+    int R = RB;  // 64-row block within the weights
+    if constexpr (GT::kGrouped) {
+        const int gi = RB / gt.per;
+        R = RB - gi * gt.per;
+        const int e = gt.e[gi];
+        A += (int64_t)gt.m0[gi] * K;
+        Y += (int64_t)gt.m0[gi] * N;
+        M = gt.me[gi];
+        wl.w += (int64_t)e * gt.expert_bytes;
+        if constexpr (ZP) zeros += (int64_t)e * N * G;
+    }
     const int g_begin = s * gps;
     const int g_end = min(G, g_begin + gps);
     const int lane = threadIdx.x & 63;
@@ -480,12 +495,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     // them back with atomic loads, adds them in split order (deterministic)
     // and resets the ticket.
     const int Npad = (int)(gridDim.x / splits) * 64;
-    unsigned *ticket = counters + ((int64_t)R * storing + wave) * tstride;
+    unsigned *ticket = counters + ((int64_t)RB * storing + wave) * tstride;
+    const int64_t np = (int64_t)RB * 64 + lane;  // partial-sum column
 #pragma unroll
     for (int i = 0; i < (MT + W - 1) / W; ++i) {
         const int m = wave + i * W;
         if (m < MT)
-            __hip_atomic_store(&part[((int64_t)s * MT + m) * Npad + n], v[i], __ATOMIC_RELAXED,
+            __hip_atomic_store(&part[((int64_t)s * MT + m) * Npad + np], v[i], __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_vm_stores();
@@ -503,7 +519,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         float p[kDecodeMaxSplits];
 #pragma unroll
         for (int t = 0; t < kDecodeMaxSplits; ++t)
-            p[t] = __hip_atomic_load(&part[((int64_t)min(t, splits - 1) * MT + m) * Npad + n],
+            p[t] = __hip_atomic_load(&part[((int64_t)min(t, splits - 1) * MT + m) * Npad + np],
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         float sum = p[0];
 #pragma unroll
@@ -515,41 +531,43 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int B, int MT, int W, class WL, bool ZP>
+template <int B, int MT, int W, class WL, bool ZP, class GT>
 static void launch_decode_kernel(bool one, const uint16_t *A, int64_t M, int64_t N, int64_t K,
                                  const WL &wl, const uint8_t *zeros, uint16_t *Y, float *part,
-                                 unsigned *counters, const DecodePlan &p, hipStream_t stream) {
+                                 unsigned *counters, const DecodePlan &p, const GT &gt,
+                                 hipStream_t stream) {
     const dim3 grid((unsigned)(p.rowblocks * p.splits));
     if (one)
-        hipLaunchKernelGGL((decode_kernel<B, MT, W, WL, true, ZP>), grid, dim3(64 * W), 0, stream,
-                           A, (int)M, (int)N, (int)K, wl, zeros, Y, part, counters, p.splits,
-                           p.gps, p.tstride);
-    else
-        hipLaunchKernelGGL((decode_kernel<B, MT, W, WL, false, ZP>), grid, dim3(64 * W), 0,
+        hipLaunchKernelGGL((decode_kernel<B, MT, W, WL, true, ZP, GT>), grid, dim3(64 * W), 0,
                            stream, A, (int)M, (int)N, (int)K, wl, zeros, Y, part, counters,
-                           p.splits, p.gps, p.tstride);
+                           p.splits, p.gps, p.tstride, gt);
+    else
+        hipLaunchKernelGGL((decode_kernel<B, MT, W, WL, false, ZP, GT>), grid, dim3(64 * W), 0,
+                           stream, A, (int)M, (int)N, (int)K, wl, zeros, Y, part, counters,
+                           p.splits, p.gps, p.tstride, gt);
 }
 
-template <int B, int MT, int W, class WL>
+template <int B, int MT, int W, class WL, class GT>
 static hipError_t launch_decode_zp(bool one, const uint16_t *A, int64_t M, int64_t N, int64_t K,
                                    const WL &wl, const uint8_t *zeros, uint16_t *Y, float *part,
-                                   unsigned *counters, const DecodePlan &p, hipStream_t stream) {
+                                   unsigned *counters, const DecodePlan &p, const GT &gt,
+                                   hipStream_t stream) {
     if (!zeros) {
         launch_decode_kernel<B, MT, W, WL, false>(one, A, M, N, K, wl, nullptr, Y, part,
-                                                  counters, p, stream);
+                                                  counters, p, gt, stream);
     } else if constexpr (B == 4 || B == 8) {  // the widths with an asymmetric form
         launch_decode_kernel<B, MT, W, WL, true>(one, A, M, N, K, wl, zeros, Y, part, counters,
-                                                 p, stream);
+                                                 p, gt, stream);
     } else {
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <int B, int MT, int W>
+template <int B, int MT, int W, class GT>
 hipError_t decode_bmw(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W_,
                       bool tiled, const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
-                      void *ws, const DecodePlan &p, hipStream_t stream) {
+                      void *ws, const DecodePlan &p, const GT &gt, hipStream_t stream) {
     const int G = (int)(K / kGroup);
     float *part = nullptr;
     unsigned *counters = nullptr;
@@ -560,37 +578,44 @@ hipError_t decode_bmw(const uint16_t *A, int64_t M, int64_t N, int64_t K, const 
     const bool one = MT > 1 && p.gps <= W;
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W_), G, B};
-        return launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p,
+        return launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p, gt,
                                           stream);
     }
-    DenseW wl{static_cast<const uint8_t *>(W_), scales, (int64_t)16 * B * G, G, B};
-    return launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p, stream);
+    if constexpr (GT::kGrouped) {
+        return hipErrorInvalidValue;  // grouped launches take the tiled layout
+    } else {
+        DenseW wl{static_cast<const uint8_t *>(W_), scales, (int64_t)16 * B * G, G, B};
+        return launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p, gt,
+                                          stream);
+    }
 }
 
-template <int B, int MT>
+template <int B, int MT, class GT>
 hipError_t decode_bm(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W_,
                      bool tiled, const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
-                     void *ws, const DecodePlan &p, hipStream_t stream) {
+                     void *ws, const DecodePlan &p, const GT &gt, hipStream_t stream) {
     if constexpr (MT <= 4) {
         if (p.waves == 16)
-            return decode_bmw<B, MT, 16>(A, M, N, K, W_, tiled, scales, zeros, Y, ws, p, stream);
+            return decode_bmw<B, MT, 16>(A, M, N, K, W_, tiled, scales, zeros, Y, ws, p, gt,
+                                         stream);
     }
     if (p.waves == 8)
-        return decode_bmw<B, MT, 8>(A, M, N, K, W_, tiled, scales, zeros, Y, ws, p, stream);
+        return decode_bmw<B, MT, 8>(A, M, N, K, W_, tiled, scales, zeros, Y, ws, p, gt, stream);
     if (p.waves == 4)
-        return decode_bmw<B, MT, 4>(A, M, N, K, W_, tiled, scales, zeros, Y, ws, p, stream);
+        return decode_bmw<B, MT, 4>(A, M, N, K, W_, tiled, scales, zeros, Y, ws, p, gt, stream);
     return hipErrorInvalidValue;
 }
 
-template <int B>
+template <int B, class GT>
 hipError_t decode_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
                     bool tiled, const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
-                    void *ws, const DecodePlan &p, hipStream_t stream) {
+                    void *ws, const DecodePlan &p, const GT &gt, hipStream_t stream) {
     switch (p.mt) {
-        case 1: return decode_bm<B, 1>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
-        case 4: return decode_bm<B, 4>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
-        case 8: return decode_bm<B, 8>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
-        case 16: return decode_bm<B, 16>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, stream);
+        case 1: return decode_bm<B, 1>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, gt, stream);
+        case 4: return decode_bm<B, 4>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, gt, stream);
+        case 8: return decode_bm<B, 8>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, gt, stream);
+        case 16:
+            return decode_bm<B, 16>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, gt, stream);
     }
     return hipErrorInvalidValue;
 }

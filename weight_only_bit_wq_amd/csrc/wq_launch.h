@@ -20,6 +20,26 @@ constexpr int64_t kWsCounterBytes = 65536;
 constexpr int kWsMaxCounters = (int)(kWsCounterBytes / 4);
 constexpr int64_t kWsScratchOffset = kWsCounterBytes;
 
+// ---- grouped (mixture-of-experts) launches ----
+// One launch covers several experts: entry i is expert e[i] with rows
+// [m0[i], m0[i] + me[i]) of A and Y.  Passed by value as a kernel argument
+// (the host knows the offsets), so nothing is allocated or copied.  The
+// decode kernel takes one entry per expert with rows; the prefill kernel
+// one entry per 256-row tile.
+constexpr int kMaxGroups = 240;
+struct NoGroups {
+    static constexpr bool kGrouped = false;
+};
+struct GroupTable {
+    static constexpr bool kGrouped = true;
+    int n;                 // entries
+    int per;               // decode: 64-row blocks per expert (grid blocks per entry)
+    int64_t expert_bytes;  // stride of the expert blobs
+    int e[kMaxGroups];
+    int m0[kMaxGroups];
+    int me[kMaxGroups];
+};
+
 // ---- decode path, M <= kDecodeMaxM (wq_decode.hip) ----
 constexpr int kDecodeMaxM = 16;
 constexpr int kDecodeMaxSplits = 16;  // K splits of the vector-ALU decode kernel
@@ -38,6 +58,13 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b);
 hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
                          bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
                          uint16_t *Y, void *ws, const DecodePlan &plan, hipStream_t stream);
+// Grouped decode: every entry of gt has at most kDecodeMaxM rows; the plan
+// is decode_plan(max rows, entries * N, K, b) with rowblocks = entries *
+// ceil(N / 64).  Tiled layout.
+hipError_t launch_decode_grouped(const uint16_t *A, int64_t N, int64_t K, const void *W,
+                                 const uint8_t *zeros, int b, uint16_t *Y, void *ws,
+                                 const DecodePlan &plan, const GroupTable &gt,
+                                 hipStream_t stream);
 
 // ---- prefill path, M > kDecodeMaxM (wq_prefill.hip) ----
 int64_t prefill_ws_bytes(int64_t M, int64_t N, int64_t K, int b);
@@ -49,6 +76,16 @@ hipError_t launch_prefill(const uint16_t *A, int64_t M, int64_t N, int64_t K, co
 hipError_t launch_embed(const void *W, const uint16_t *scales, const uint8_t *zeros,
                         bool per_channel, int64_t V, int64_t K, int b, const int64_t *ids,
                         int64_t T, uint16_t *Y, hipStream_t stream);
+
+// Grouped prefill: one entry of gt per 256-row tile; the workspace holds
+// the pre-pass matrix for all M rows (prefill_grouped_ws_bytes), computed
+// when `prepass` (once per call: later launches of the call reuse it).
+constexpr int kPrefillTileM = 256;
+int64_t prefill_grouped_ws_bytes(int64_t M, int64_t K);
+hipError_t launch_prefill_grouped(const uint16_t *A, int64_t M, int64_t N, int64_t K,
+                                  const void *W, const uint8_t *zeros, int b, uint16_t *Y,
+                                  void *ws, const GroupTable &gt, bool prepass,
+                                  hipStream_t stream);
 
 // ---- W4A8 (wq_a8.hip) ----
 hipError_t launch_quant_act(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq, float *sa,

@@ -143,14 +143,18 @@ __device__ __forceinline__ uint32_t quarter_pair_zp(const uint32_t *w, uint32_t 
     }
 }
 
-template <int B, class WL, bool ZP>
+// GT: NoGroups, or a GroupTable with one entry per 256-row tile (expert
+// e[i], rows [m0[i], m0[i] + me[i]) of A and Y); the grid's m-tiles run the
+// entries, each rebasing its rows, weights and zero points.
+template <int B, class WL, bool ZP, class GT>
 __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict__ A,
                                                       const uint16_t *__restrict__ Ap, int M,
                                                       int N, int K, int Kp, WL wl,
                                                       const uint8_t *__restrict__ zeros,
                                                       uint16_t *__restrict__ Y, int mtiles,
                                                       int ntiles, int splits,
-                                                      float *__restrict__ part, int64_t mnp) {
+                                                      float *__restrict__ part, int64_t mnp,
+                                                      const GT gt) {
     __shared__ u32x4 As0[kPM * 16];
     __shared__ u32x4 As1[kPM * 16];
     // Codes of the tile's 128 columns, double-buffered: [buffer][64-row
@@ -179,7 +183,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     const int bn = tile - bm * ntiles;
     const int g_lo = (int)(((int64_t)G * sp) / splits);
     const int g_hi = (int)(((int64_t)G * (sp + 1)) / splits);
-    const int64_t m0 = (int64_t)bm * kPM;
+    int64_t m0 = (int64_t)bm * kPM;
+    if constexpr (GT::kGrouped) {
+        m0 = gt.m0[bm];
+        M = (int)(m0 + gt.me[bm]);
+        wl.w += (int64_t)gt.e[bm] * gt.expert_bytes;
+        if constexpr (ZP) zeros += (int64_t)gt.e[bm] * N * G;
+    }
     const int64_t n0 = (int64_t)bn * kPN;
 
     const uint32_t mask = __builtin_amdgcn_readfirstlane(pair_mask<B < 8 ? B : 7>());
@@ -573,14 +583,14 @@ static hipError_t prefill_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K,
     const dim3 grid((unsigned)(mtiles * ntiles * splits));
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W), G, B};
-        hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP>), grid, dim3(512), 0, stream, A, Ap,
-                           (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles, splits, part,
-                           prefill_mnp(M, N));
+        hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, NoGroups>), grid, dim3(512), 0, stream,
+                           A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles,
+                           splits, part, prefill_mnp(M, N), NoGroups{});
     } else {
         DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
-        hipLaunchKernelGGL((prefill_kernel<B, DenseW, ZP>), grid, dim3(512), 0, stream, A, Ap,
-                           (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles, splits, part,
-                           prefill_mnp(M, N));
+        hipLaunchKernelGGL((prefill_kernel<B, DenseW, ZP, NoGroups>), grid, dim3(512), 0, stream,
+                           A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles,
+                           splits, part, prefill_mnp(M, N), NoGroups{});
     }
     e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
@@ -598,6 +608,56 @@ static hipError_t prefill_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, 
     if (!zeros) return prefill_bz<B, false>(A, M, N, K, W, tiled, scales, nullptr, Y, ws, stream);
     if constexpr (B == 4 || B == 8)  // the widths with an asymmetric form
         return prefill_bz<B, true>(A, M, N, K, W, tiled, scales, zeros, Y, ws, stream);
+    return hipErrorInvalidValue;
+}
+
+// Grouped prefill: the pre-pass over all M rows of A, then one launch over
+// (table entry, n-tile), tiled layout, no K split.
+int64_t prefill_grouped_ws_bytes(int64_t M, int64_t K) {
+    return kWsScratchOffset + align256(M * pseudo_kp(K) * 2);
+}
+
+template <int B, bool ZP>
+static hipError_t prefill_grouped_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K,
+                                     const void *W, const uint8_t *zeros, uint16_t *Y, void *ws,
+                                     const GroupTable &gt, bool prepass, hipStream_t stream) {
+    const int G = (int)(K / kGroup);
+    const float off = ZP ? (B == 8 ? 0.0f : 192.0f)
+                         : (B == 8 ? 128.0f : (float)(128 + (1 << (B - 1))));
+    const int Kp = off != 0.0f ? pseudo_kp(K) : 0;
+    uint16_t *Ap = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
+    if (Kp > 0 && prepass) {
+        hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M), dim3(256), 0, stream, A,
+                           (int)K, Kp, off, Ap);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int ntiles = (int)((N + kPN - 1) / kPN);
+    TiledW wl{static_cast<const uint8_t *>(W), G, B};
+    hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, GroupTable>), dim3((unsigned)(gt.n * ntiles)),
+                       dim3(512), 0, stream, A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y,
+                       gt.n, ntiles, 1, (float *)nullptr, (int64_t)0, gt);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_grouped(const uint16_t *A, int64_t M, int64_t N, int64_t K,
+                                  const void *W, const uint8_t *zeros, int b, uint16_t *Y,
+                                  void *ws, const GroupTable &gt, bool prepass,
+                                  hipStream_t stream) {
+    if (zeros) {
+        if (b == 4) return prefill_grouped_bz<4, true>(A, M, N, K, W, zeros, Y, ws, gt, prepass, stream);
+        if (b == 8) return prefill_grouped_bz<8, true>(A, M, N, K, W, zeros, Y, ws, gt, prepass, stream);
+        return hipErrorInvalidValue;
+    }
+    switch (b) {
+        case 2: return prefill_grouped_bz<2, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
+        case 3: return prefill_grouped_bz<3, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
+        case 4: return prefill_grouped_bz<4, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
+        case 5: return prefill_grouped_bz<5, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
+        case 6: return prefill_grouped_bz<6, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
+        case 7: return prefill_grouped_bz<7, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
+        case 8: return prefill_grouped_bz<8, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
+    }
     return hipErrorInvalidValue;
 }
 
