@@ -202,6 +202,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     // (their results are dropped).  Byte offsets from the block's column
     // k0, per run, for A (row stride K) and the pre-pass matrix (Kp).
     const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)kPM - 1);
+    // A wave whose 128 rows all lie past the tile's last row (a short last
+    // tile, or a small expert's tile) computes nothing: it runs its own loop
+    // that only takes its part in the workgroup's loads and barriers.
+    const bool idle = 128 * wm > mlim;
     const int dma_row0 = 4 * wave + (lane >> 4);
     const int dma_chunk = (lane & 15) ^ (dma_row0 & 15);
     const uint16_t *A_blk = A + m0 * K;
@@ -474,6 +478,22 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
         sq_prev = sg;
     };
     int g = g_lo;
+    if (idle) {
+        auto idle_group = [&](int gi, auto bconst) __attribute__((always_inline)) {
+            constexpr int BUF = decltype(bconst)::value;
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            dma(A_blk, min(gi + 1, g_hi - 1) * kGroup, doff,
+                std::integral_constant<int, BUF ^ 1>{});
+            dma_codes(min(gi + 1, g_hi - 1), std::integral_constant<int, BUF ^ 1>{});
+        };
+        for (; g + 1 < g_hi; g += 2) {
+            idle_group(g, std::integral_constant<int, 0>{});
+            idle_group(g + 1, std::integral_constant<int, 1>{});
+        }
+        if (g < g_hi) idle_group(g, std::integral_constant<int, 0>{});
+        g = g_hi;
+    }
     for (; g + 1 < g_hi; g += 2) {
         group(g, std::integral_constant<int, 0>{});
         group(g + 1, std::integral_constant<int, 1>{});
