@@ -206,6 +206,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     // tile, or a small expert's tile) computes nothing: it runs its own loop
     // that only takes its part in the workgroup's loads and barriers.
     const bool idle = 128 * wm > mlim;
+    // A wave whose last 64 rows (phase 1) are all past the tile's end runs
+    // phase 0 only.
+    const bool half = !idle && 128 * wm + 64 > mlim;
     const int dma_row0 = 4 * wave + (lane >> 4);
     const int dma_chunk = (lane & 15) ^ (dma_row0 & 15);
     const uint16_t *A_blk = A + m0 * K;
@@ -492,6 +495,34 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
             idle_group(g + 1, std::integral_constant<int, 1>{});
         }
         if (g < g_hi) idle_group(g, std::integral_constant<int, 0>{});
+        g = g_hi;
+    }
+    if (half) {
+        // As group(), without phase 1: rows 0, 1 are folded after phase 0,
+        // rows 2, 3 are empty.
+        auto half_group = [&](int gi, auto bconst) __attribute__((always_inline)) {
+            constexpr int BUF = decltype(bconst)::value;
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            sreg = snext;
+            zop = znext;
+            read_codes(bconst, creg);
+            dma(A_blk, min(gi + 1, g_hi - 1) * kGroup, doff,
+                std::integral_constant<int, BUF ^ 1>{});
+            dma_codes(min(gi + 1, g_hi - 1), std::integral_constant<int, BUF ^ 1>{});
+            load_scale(gi + 1, snext);
+            unpack_k0();
+            read_a(bconst, 0, 0, 0);
+            const float sg = bf16_to_f32((uint16_t)sreg);
+            phase(std::integral_constant<int, 0>{}, bconst, [&](int slot) { unpack_slot(slot); });
+#pragma unroll
+            for (int q = 0; q < 16; ++q) fold_slice(0, q, sg);
+        };
+        for (; g + 1 < g_hi; g += 2) {
+            half_group(g, std::integral_constant<int, 0>{});
+            half_group(g + 1, std::integral_constant<int, 1>{});
+        }
+        if (g < g_hi) half_group(g, std::integral_constant<int, 0>{});
         g = g_hi;
     }
     for (; g + 1 < g_hi; g += 2) {
