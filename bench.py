@@ -252,6 +252,48 @@ def bench_grouped(torch, wq, synth, reps: int):
     return out
 
 
+def ceilings_run(torch):
+    """Practical ceilings next to the spec peaks, with torch's own kernels,
+    timed eagerly with events: the HBM read rate (torch.sum over a 4 GiB
+    buffer) and copy rate (2 GiB to 2 GiB, read + write bytes), both far
+    past the 256 MB Infinity Cache; and torch's bf16 GEMM (hipBLASLt) at
+    the prefill shapes with the weight stored [N, K] as the library's is
+    (Y = A @ W^T)."""
+    def eager(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / 1e3 / reps
+
+    out = {}
+    big = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    t = eager(lambda: big.sum(), 20)
+    out["hbm_read"] = {"bytes": big.numel() * 4, "us": t * 1e6,
+                       "TB/s": big.numel() * 4 / t / 1e12,
+                       "frac_of_hbm_peak": big.numel() * 4 / t / 1e9 / HBM_PEAK_GBS}
+    half = big.view(2, -1)
+    t = eager(lambda: half[1].copy_(half[0]), 20)
+    out["hbm_copy"] = {"bytes": big.numel() * 4, "us": t * 1e6,
+                       "TB/s": big.numel() * 4 / t / 1e12,
+                       "frac_of_hbm_peak": big.numel() * 4 / t / 1e9 / HBM_PEAK_GBS}
+    del big, half
+    for name, (K, N) in (("gemm_bf16_up", (5120, 17408)), ("gemm_bf16_down", (17408, 5120))):
+        A = torch.randn((4096, K), device="cuda").to(torch.bfloat16)
+        W = torch.randn((N, K), device="cuda").to(torch.bfloat16)
+        t = eager(lambda: torch.matmul(A, W.t()), 20)
+        tf = 2.0 * 4096 * N * K / t / 1e12
+        out[name] = {"M": 4096, "N": N, "K": K, "us": t * 1e6, "TFLOP/s": tf,
+                     "frac_of_peak": tf / BF16_PEAK_TFLOPS}
+        del A, W
+    return out
+
+
 def bench_decode_sweep(torch, wq, synth, reps: int, copies: int):
     """wq_gemm at M = 4 and 16 on the decode layer (K 5120 -> N 17408), b = 5,
     6, 7, in TB/s of algorithmic bytes; rotating weight copies as in the
@@ -447,6 +489,9 @@ def main():
     ap.add_argument("--pmc-run", action="store_true",
                     help="no timing: 16 launches of the b=6 decode kernel, then a 64 MiB fill and "
                          "a 64 MiB sum (known-size references for rocprofv3 --pmc byte counters)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="no library timing: practical ceilings (streaming read of the decode "
+                         "layer's bytes, torch bf16 GEMM at the prefill shapes), one JSON line")
     ap.add_argument("--pmc-layer", type=int, default=0, metavar="M",
                     help="no timing: three calls of the K=5120, N=17408, b=6 layer at batch M "
                          "(for rocprofv3 --pmc activity counters)")
@@ -468,6 +513,9 @@ def main():
 
     if args.pmc_run:
         pmc_run(torch, wq, synth, args.copies)
+        return
+    if args.ceilings:
+        print(json.dumps(ceilings_run(torch)), flush=True)
         return
     if args.pmc_layer > 0:
         pmc_layer_run(torch, wq, synth, args.pmc_layer)
