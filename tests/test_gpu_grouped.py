@@ -44,6 +44,25 @@ def test_grouped_mixed_sizes(b, zp):
     assert_wna16(host_bf16_bits(Y), y_ref, mag, "grouped b=%d zp=%d" % (b, zp))
 
 
+@pytest.mark.parametrize("b,zp", [(3, False), (6, False), (4, True), (8, True)])
+def test_grouped_tile_boundaries(b, zp):
+    # Expert sizes on both sides of every tile boundary: 64-row tiles below
+    # 192 remaining rows (64, 65, 191, 17, 128), 256-row tiles from 192 (192,
+    # 257 = 256 + a 1-row small tile, 449 = 256 + 193); K = 6144 (two
+    # pseudo-groups of the pre-pass constant), N = 136 (a ragged n-tile).
+    E, N, K = 10, 136, 6144
+    sizes = [64, 65, 191, 192, 257, 449, 17, 128, 0, 5]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    packed, scales, zeros, W, eb = _experts(E, N, K, b, 3050 + b + 10 * zp, zp)
+    A = synth.draw_act(np.random.default_rng(3051 + b), int(off[-1]), K)
+    print("grouped tiles b=%d zp=%d rows=%s" % (b, zp, sizes), flush=True)
+    Z = torch.from_numpy(zeros).cuda() if zp else None
+    Y = wq.wq_gemm_grouped(dev_bf16(A), W, eb, off, N, b, zeros=Z)
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.wna16_grouped(A, packed, scales, b, off, zeros=zeros)
+    assert_wna16(host_bf16_bits(Y), y_ref, mag, "grouped tiles b=%d zp=%d" % (b, zp))
+
+
 def test_grouped_decode_routing():
     # One token routed to 4 of 16 experts (rows sorted by expert), b = 4.
     E, N, K, b = 16, 512, 2048, 4
@@ -67,7 +86,8 @@ def test_grouped_decode_routing():
 @pytest.mark.parametrize("b", [4, 6])
 def test_grouped_many_experts_ragged(b):
     # 40 experts with a ragged N (not a multiple of 64), most with decode-
-    # sized row blocks, a few with prefill-sized ones (two 256-row tiles).
+    # sized row blocks, a few with prefill-sized ones (300 rows: a 256-row
+    # and a 64-row tile; 20 rows: a 64-row tile).
     E, N, K = 40, 200, 640
     rng = np.random.default_rng(3200 + b)
     sizes = rng.integers(0, 6, size=E)
@@ -85,3 +105,19 @@ def test_grouped_many_experts_ragged(b):
     assert_wna16(host_bf16_bits(Y0), y_ref, mag, "grouped many b=%d" % b)
     assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
     assert not ws[:wq.WORKSPACE_ZERO_BYTES].any()
+
+
+def test_grouped_table_overflow():
+    # 260 experts of 17..40 rows: more 64-row tiles than one launch's table
+    # holds (240 entries), so the call spans two prefill launches.
+    E, N, K, b = 260, 64, 256, 5
+    rng = np.random.default_rng(3300)
+    sizes = rng.integers(17, 41, size=E)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    packed, scales, _, W, eb = _experts(E, N, K, b, 3301)
+    A = synth.draw_act(rng, int(off[-1]), K)
+    print("grouped overflow E=%d rows=%d" % (E, off[-1]), flush=True)
+    Y = wq.wq_gemm_grouped(dev_bf16(A), W, eb, off, N, b)
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.wna16_grouped(A, packed, scales, b, off)
+    assert_wna16(host_bf16_bits(Y), y_ref, mag, "grouped overflow")

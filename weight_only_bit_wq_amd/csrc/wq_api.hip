@@ -116,14 +116,15 @@ int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int b) {
 
 // The launches of a grouped call: experts with at most kDecodeMaxM rows go
 // into decode tables (one entry per expert), the others into prefill tables
-// (one entry per 256-row tile); a table is emitted when full or at the end.
-// emit(is_decode, table, max rows of its entries).
+// of 256-row or of 64-row m-tiles (one entry per tile); a table is emitted
+// when full or at the end.  emit(is_decode, table, m): for a decode table
+// the most rows of its entries, for a prefill table its tile size.
 template <class F>
 void grouped_tables(const int64_t *off, int64_t E, int64_t N, int64_t expert_bytes, F emit) {
-    wq::GroupTable dec{}, pre{};
+    wq::GroupTable dec{}, pre{}, small{};
     int dec_max = 0;
     dec.per = (int)((N + 63) / 64);
-    dec.expert_bytes = pre.expert_bytes = expert_bytes;
+    dec.expert_bytes = pre.expert_bytes = small.expert_bytes = expert_bytes;
     for (int64_t e = 0; e < E; ++e) {
         const int64_t m0 = off[e], me = off[e + 1] - off[e];
         if (me == 0) continue;
@@ -139,18 +140,25 @@ void grouped_tables(const int64_t *off, int64_t E, int64_t N, int64_t expert_byt
             }
             continue;
         }
-        for (int64_t r = 0; r < me; r += wq::kPrefillTileM) {
-            pre.e[pre.n] = (int)e;
-            pre.m0[pre.n] = (int)(m0 + r);
-            pre.me[pre.n] = (int)std::min<int64_t>(wq::kPrefillTileM, me - r);
-            if (++pre.n == wq::kMaxGroups) {
-                emit(false, pre, wq::kPrefillTileM);
-                pre.n = 0;
+        // 256-row tiles while at least 192 rows remain, then 64-row tiles
+        // (a few dozen rows in a 256-row tile leave most of its waves idle).
+        for (int64_t r = 0; r < me;) {
+            const bool big = me - r >= 192;
+            wq::GroupTable &t = big ? pre : small;
+            const int tm = big ? wq::kPrefillTileM : wq::kPrefillSmallTileM;
+            t.e[t.n] = (int)e;
+            t.m0[t.n] = (int)(m0 + r);
+            t.me[t.n] = (int)std::min<int64_t>(tm, me - r);
+            r += t.me[t.n];
+            if (++t.n == wq::kMaxGroups) {
+                emit(false, t, tm);
+                t.n = 0;
             }
         }
     }
     if (dec.n) emit(true, dec, dec_max);
     if (pre.n) emit(false, pre, wq::kPrefillTileM);
+    if (small.n) emit(false, small, wq::kPrefillSmallTileM);
 }
 
 // Decode plan of a grouped decode table: the plan for its largest row count
@@ -394,7 +402,7 @@ int wq_gemm_grouped(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const 
                                             (hipStream_t)stream);
         } else {
             err = wq::launch_prefill_grouped(A_d, M, N, K, W_d, zeros_d, b, Y_d, ws_d, t,
-                                             prepass, (hipStream_t)stream);
+                                             max_me, prepass, (hipStream_t)stream);
             prepass = false;
         }
     });

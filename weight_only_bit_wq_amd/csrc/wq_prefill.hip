@@ -143,11 +143,17 @@ __device__ __forceinline__ uint32_t quarter_pair_zp(const uint32_t *w, uint32_t 
     }
 }
 
-// GT: NoGroups, or a GroupTable with one entry per 256-row tile (expert
-// e[i], rows [m0[i], m0[i] + me[i]) of A and Y); the grid's m-tiles run the
+// GT: NoGroups, or a GroupTable with one entry per m-tile (expert e[i],
+// rows [m0[i], m0[i] + me[i]) of A and Y); the grid's m-tiles run the
 // entries, each rebasing its rows, weights and zero points.
-template <int B, class WL, bool ZP, class GT>
-__global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict__ A,
+//
+// TM: workgroup rows, 256 (8 waves as above) or 64 for the small m-tiles of
+// grouped launches (experts of a few dozen rows): 4 waves of 64 x 32, one
+// per SIMD, each running phase 0 only, with a 32 KB A double buffer, so
+// that LDS (56 KB at b = 6) leaves room for two workgroups per compute unit
+// and their loads overlap each other's matrix work.
+template <int B, class WL, bool ZP, class GT, int TM = kPM>
+__global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const uint16_t *__restrict__ A,
                                                       const uint16_t *__restrict__ Ap, int M,
                                                       int N, int K, int Kp, WL wl,
                                                       const uint8_t *__restrict__ zeros,
@@ -155,8 +161,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
                                                       int ntiles, int splits,
                                                       float *__restrict__ part, int64_t mnp,
                                                       const GT gt) {
-    __shared__ u32x4 As0[kPM * 16];
-    __shared__ u32x4 As1[kPM * 16];
+    static_assert(TM == kPM || TM == 64, "m-tile of 256 or 64 rows");
+    constexpr int NW = TM == kPM ? 8 : 4;  // waves
+    constexpr bool kSmall = TM != kPM;
+    __shared__ u32x4 As0[TM * 16];
+    __shared__ u32x4 As1[TM * 16];
     // Codes of the tile's 128 columns, double-buffered: [buffer][64-row
     // block][plane][row].  (One object: its reads come right after the
     // barrier, before any direct load into it is issued.)
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = kSmall ? 0 : wave >> 2, wn = wave & 3;
     const int h = lane >> 5;
     const int c32 = lane & 31;
 
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     const int bn = tile - bm * ntiles;
     const int g_lo = (int)(((int64_t)G * sp) / splits);
     const int g_hi = (int)(((int64_t)G * (sp + 1)) / splits);
-    int64_t m0 = (int64_t)bm * kPM;
+    int64_t m0 = (int64_t)bm * TM;
     if constexpr (GT::kGrouped) {
         m0 = gt.m0[bm];
         M = (int)(m0 + gt.me[bm]);
@@ -195,42 +204,43 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     const uint32_t mask = __builtin_amdgcn_readfirstlane(pair_mask<B < 8 ? B : 7>());
     const uint32_t magic = in_vgpr(kBf16Magic128x2);
 
-    // Direct loads: wave w fills the 1 KB runs s = w + 8 u (u < 8); run s
-    // holds rows 4 s .. 4 s + 3, lane l at row 4 s + l / 16, physical chunk
-    // l % 16, which is logical chunk (l % 16) ^ (row % 16) (swz16; the row
-    // is 4 w + l / 16 modulo 16 for every u).  Rows beyond M read row M-1
+    // Direct loads: wave w fills the 1 KB runs s = w + NW u (u < TM / 4 NW);
+    // run s holds rows 4 s .. 4 s + 3, lane l at row 4 s + l / 16, physical
+    // chunk l % 16, which is logical chunk (l % 16) ^ (row % 16) (swz16; the
+    // row is 4 w + l / 16 modulo 16 for every u).  Rows beyond M read row M-1
     // (their results are dropped).  Byte offsets from the block's column
     // k0, per run, for A (row stride K) and the pre-pass matrix (Kp).
-    const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)kPM - 1);
+    const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)TM - 1);
     // A wave whose 128 rows all lie past the tile's last row (a short last
     // tile, or a small expert's tile) computes nothing: it runs its own loop
     // that only takes its part in the workgroup's loads and barriers.
-    const bool idle = 128 * wm > mlim;
+    const bool idle = !kSmall && 128 * wm > mlim;
     // A wave whose last 64 rows (phase 1) are all past the tile's end runs
-    // phase 0 only.
-    const bool half = !idle && 128 * wm + 64 > mlim;
+    // phase 0 only (every wave of a 64-row tile).
+    const bool half = kSmall || (!idle && 128 * wm + 64 > mlim);
     const int dma_row0 = 4 * wave + (lane >> 4);
     const int dma_chunk = (lane & 15) ^ (dma_row0 & 15);
     const uint16_t *A_blk = A + m0 * K;
     const uint16_t *Ap_blk = Ap + m0 * Kp;
-    uint32_t doff[8];
+    constexpr int RU = TM / (4 * NW);  // runs per wave
+    uint32_t doff[RU];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-        doff[u] = (uint32_t)((min(dma_row0 + 32 * u, mlim) * K + 8 * dma_chunk) * 2);
-    auto dma = [&](const uint16_t *base, int k0, const uint32_t(&off)[8], auto bconst)
+    for (int u = 0; u < RU; ++u)
+        doff[u] = (uint32_t)((min(dma_row0 + 4 * NW * u, mlim) * K + 8 * dma_chunk) * 2);
+    auto dma = [&](const uint16_t *base, int k0, const uint32_t(&off)[RU], auto bconst)
         __attribute__((always_inline)) {
         u32x4 *dst = decltype(bconst)::value == 0 ? As0 : As1;
         const uint8_t *b8 = reinterpret_cast<const uint8_t *>(base + k0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < RU; ++u)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void *)(b8 + off[u]),
-                (__attribute__((address_space(3))) void *)&dst[64 * (wave + 8 * u)], 16, 0, 0);
+                (__attribute__((address_space(3))) void *)&dst[64 * (wave + NW * u)], 16, 0, 0);
     };
 
     // Codes: each group's 128 columns x b planes of 16 bytes (2 b runs of
     // 64 lanes, one 64-row block and plane each) go global -> LDS with the
-    // same direct loads; wave w issues runs w and w + 8.  Lane l of run r
+    // same direct loads; wave w issues runs w, w + NW, ...  Lane l of run r
     // (block t = r / b, plane p = r % b) reads chunk p of row n0 + 64 t + l
     // (rows beyond N read row N-1).  The lane's column (32 wn + c32, block
     // t = wn / 2, row rho) and half h then read dword pair i of the half,
@@ -244,8 +254,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     auto dma_codes = [&](int g, auto bconst) __attribute__((always_inline)) {
         u32x4 *dst = Cs[decltype(bconst)::value];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int r = wave + 8 * k;
+        for (int k = 0; k < (2 * B + NW - 1) / NW; ++k) {
+            const int r = wave + NW * k;
             if (r < 2 * B) {
                 const int t = r >= B ? 1 : 0, p = r - t * B;
                 __builtin_amdgcn_global_load_lds(
@@ -355,7 +365,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
         for (int j = 0; j < 8; ++j) {
             const int set = j & 1;
             if (j + 1 < 8) read_a(bconst, 64 * PH, j + 1, set ^ 1);
-            else if (PH == 0) read_a(bconst, 64, 0, set ^ 1);
+            else if (PH == 0 && !kSmall) read_a(bconst, 64, 0, set ^ 1);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 f32x16_t c = P[2 * PH + t];
@@ -410,11 +420,39 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
     // matrix into As0; B' = s[n, k'/3] (zero beyond 3G) built in As1 (free
     // until the real groups) by thread (row tid % 128, quarter tid / 128),
     // in the same swizzled row layout, and read back as the B operand. ----
-    if (sp == 0 && NP > 0) {
-        uint32_t poff[8];
+    if (sp == 0 && NP > 0 && kSmall) {
+        // 64-row tile: the B' operand is built in registers, each lane
+        // reading its column's scales (As1 holds 64 rows, not 128); phase 0
+        // only, rows 0, 1 folded with scale 1.
+        uint32_t poff[RU];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            poff[u] = (uint32_t)((min(dma_row0 + 32 * u, mlim) * Kp + 8 * dma_chunk) * 2);
+        for (int u = 0; u < RU; ++u)
+            poff[u] = (uint32_t)((min(dma_row0 + 4 * NW * u, mlim) * Kp + 8 * dma_chunk) * 2);
+        for (int ps = 0; ps < NP; ++ps) {
+            dma(Ap_blk, ps * kPseudoK, poff, std::integral_constant<int, 0>{});
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ka = ps * kPseudoK + 64 * h + 8 * j + 2 * e, kb = ka + 1;
+                    const uint32_t sa = *reinterpret_cast<const uint16_t *>(sptr + min(ka / 3, G - 1) * sstep);
+                    const uint32_t sb = *reinterpret_cast<const uint16_t *>(sptr + min(kb / 3, G - 1) * sstep);
+                    bop[j][e] = (ka < 3 * G ? sa : 0u) | ((kb < 3 * G ? sb : 0u) << 16);
+                }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads have landed
+            __syncthreads();
+            read_a(std::integral_constant<int, 0>{}, 0, 0, 0);
+            phase(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, [&](int) {});
+#pragma unroll
+            for (int q = 0; q < 16; ++q) fold_slice(0, q, 1.0f);
+            __syncthreads();  // every wave is done with As0 before it is refilled
+        }
+    }
+    if (sp == 0 && NP > 0 && !kSmall) {
+        uint32_t poff[RU];
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+            poff[u] = (uint32_t)((min(dma_row0 + 4 * NW * u, mlim) * Kp + 8 * dma_chunk) * 2);
         const int brow = tid & (kPN - 1);
         const int bq = tid >> 7;
         const uint8_t *sb0 = wl.scale0(min(n0 + brow, (int64_t)N - 1));
@@ -481,7 +519,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
         sq_prev = sg;
     };
     int g = g_lo;
-    if (idle) {
+    if (!kSmall && idle) {
         auto idle_group = [&](int gi, auto bconst) __attribute__((always_inline)) {
             constexpr int BUF = decltype(bconst)::value;
             __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -525,20 +563,22 @@ __global__ __launch_bounds__(512) void prefill_kernel(const uint16_t *__restrict
         if (g < g_hi) half_group(g, std::integral_constant<int, 0>{});
         g = g_hi;
     }
-    for (; g + 1 < g_hi; g += 2) {
-        group(g, std::integral_constant<int, 0>{});
-        group(g + 1, std::integral_constant<int, 1>{});
-    }
-    if (g < g_hi) group(g, std::integral_constant<int, 0>{});
-    // The last group's rows 2, 3.
+    if constexpr (!kSmall) {
+        for (; g + 1 < g_hi; g += 2) {
+            group(g, std::integral_constant<int, 0>{});
+            group(g + 1, std::integral_constant<int, 1>{});
+        }
+        if (g < g_hi) group(g, std::integral_constant<int, 0>{});
+        // The last group's rows 2, 3.
 #pragma unroll
-    for (int q = 0; q < 16; ++q) fold_slice(2, q, sq_prev);
+        for (int q = 0; q < 16; ++q) fold_slice(2, q, sq_prev);
+    }
     // Drain the (clamped, unused) prefetch of the group after the last.
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // Output element r of block i: row 8(r/4) + 4h + r%4, column lane%32.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < (kSmall ? 2 : 4); ++i) {
         const int64_t n = n0 + 32 * wn + c32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -671,7 +711,8 @@ int64_t prefill_grouped_ws_bytes(int64_t M, int64_t K) {
 template <int B, bool ZP>
 static hipError_t prefill_grouped_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K,
                                      const void *W, const uint8_t *zeros, uint16_t *Y, void *ws,
-                                     const GroupTable &gt, bool prepass, hipStream_t stream) {
+                                     const GroupTable &gt, int tile_m, bool prepass,
+                                     hipStream_t stream) {
     const int G = (int)(K / kGroup);
     const float off = ZP ? (B == 8 ? 0.0f : 192.0f)
                          : (B == 8 ? 128.0f : (float)(128 + (1 << (B - 1))));
@@ -685,29 +726,37 @@ static hipError_t prefill_grouped_bz(const uint16_t *A, int64_t M, int64_t N, in
     }
     const int ntiles = (int)((N + kPN - 1) / kPN);
     TiledW wl{static_cast<const uint8_t *>(W), G, B};
-    hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, GroupTable>), dim3((unsigned)(gt.n * ntiles)),
-                       dim3(512), 0, stream, A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y,
-                       gt.n, ntiles, 1, (float *)nullptr, (int64_t)0, gt);
+    if (tile_m == kPrefillSmallTileM)
+        hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, GroupTable, kPrefillSmallTileM>),
+                           dim3((unsigned)(gt.n * ntiles)), dim3(256), 0, stream, A, Ap, (int)M,
+                           (int)N, (int)K, Kp, wl, zeros, Y, gt.n, ntiles, 1, (float *)nullptr,
+                           (int64_t)0, gt);
+    else if (tile_m == kPrefillTileM)
+        hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, GroupTable>), dim3((unsigned)(gt.n * ntiles)),
+                           dim3(512), 0, stream, A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y,
+                           gt.n, ntiles, 1, (float *)nullptr, (int64_t)0, gt);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_grouped(const uint16_t *A, int64_t M, int64_t N, int64_t K,
                                   const void *W, const uint8_t *zeros, int b, uint16_t *Y,
-                                  void *ws, const GroupTable &gt, bool prepass,
+                                  void *ws, const GroupTable &gt, int tile_m, bool prepass,
                                   hipStream_t stream) {
     if (zeros) {
-        if (b == 4) return prefill_grouped_bz<4, true>(A, M, N, K, W, zeros, Y, ws, gt, prepass, stream);
-        if (b == 8) return prefill_grouped_bz<8, true>(A, M, N, K, W, zeros, Y, ws, gt, prepass, stream);
+        if (b == 4) return prefill_grouped_bz<4, true>(A, M, N, K, W, zeros, Y, ws, gt, tile_m, prepass, stream);
+        if (b == 8) return prefill_grouped_bz<8, true>(A, M, N, K, W, zeros, Y, ws, gt, tile_m, prepass, stream);
         return hipErrorInvalidValue;
     }
     switch (b) {
-        case 2: return prefill_grouped_bz<2, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
-        case 3: return prefill_grouped_bz<3, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
-        case 4: return prefill_grouped_bz<4, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
-        case 5: return prefill_grouped_bz<5, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
-        case 6: return prefill_grouped_bz<6, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
-        case 7: return prefill_grouped_bz<7, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
-        case 8: return prefill_grouped_bz<8, false>(A, M, N, K, W, nullptr, Y, ws, gt, prepass, stream);
+        case 2: return prefill_grouped_bz<2, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
+        case 3: return prefill_grouped_bz<3, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
+        case 4: return prefill_grouped_bz<4, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
+        case 5: return prefill_grouped_bz<5, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
+        case 6: return prefill_grouped_bz<6, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
+        case 7: return prefill_grouped_bz<7, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
+        case 8: return prefill_grouped_bz<8, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
     }
     return hipErrorInvalidValue;
 }
