@@ -100,9 +100,10 @@ def test_gemm_decode_path(b, M, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
-@pytest.mark.parametrize("M", [17, 130, 257])
+@pytest.mark.parametrize("M", [17, 100, 128, 130, 257])
 @pytest.mark.parametrize("b", BITS)
 def test_gemm_prefill_path(b, M, layout):
+    # 64-row m-tiles up to M = 128 (100: a ragged second tile), 256-row above.
     w = _workload(M, 200, 640, b, seed=500 + 10 * b + M)
     y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
     assert_wna16(Layer(w, layout).gemm(), y_ref, mag, "prefill b=%d M=%d" % (b, M))
@@ -127,10 +128,13 @@ def test_gemm_decode_m1_shapes(N, K, b):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
-@pytest.mark.parametrize("M,N,K,b", [(300, 700, 5120, 6), (130, 1000, 3072, 3)])
+@pytest.mark.parametrize("M,N,K,b", [(300, 700, 5120, 6), (130, 1000, 3072, 3),
+                                     (100, 700, 6144, 6), (40, 1000, 17408, 4)])
 def test_gemm_prefill_k_split(M, N, K, b, layout):
-    # Few output tiles: the prefill kernel splits K across workgroups (5 and
-    # 3 splits here) and a reduce pass adds the fp32 partials; full outputs.
+    # Few output tiles: the prefill kernel splits K across workgroups (5, 3,
+    # 6 and 17 splits here; the last two on 64-row tiles, with 2 and 4
+    # pseudo-groups of the constant term) and a reduce pass adds the fp32
+    # partials; full outputs.
     w = _workload(M, N, K, b, seed=950 + b)
     y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
     Y = Layer(w, layout).gemm()

@@ -91,7 +91,7 @@ def test_gemm_zero_points_integer_exact(b):
                                       synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(ref)))
 
 
-@pytest.mark.parametrize("M", [1, 4, 16, 300])
+@pytest.mark.parametrize("M", [1, 4, 16, 40, 300])
 @pytest.mark.parametrize("b", [4, 6, 8])
 def test_gemm_per_channel_scales(b, M):
     # One scale per row (group = K), expanded into the tiled blob by wq_repack.

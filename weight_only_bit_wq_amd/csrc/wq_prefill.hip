@@ -615,24 +615,42 @@ static int pseudo_kp(int64_t K) {
     return (3 * G + kPseudoK - 1) / kPseudoK * kPseudoK;
 }
 
+// m-tile rows of a plain (not grouped) launch: 64 up to kSmallTileMaxM
+// rows, else 256.  Measured, b = 6, 5120 -> 17408 / 17408 -> 5120: M = 17..64
+// 32-35 / 44-48 us with 64-row tiles vs 57-58 / 53-56 with 256; M = 96, 128
+// 58-60 vs 61-63 both ways; M = 192 81 / 77 vs 75.  WQ_PREFILL_TILE_M (64 or
+// 256) forces one.
+constexpr int64_t kSmallTileMaxM = 128;
+static int prefill_tile_m(int64_t M) {
+    static const int forced = [] {
+        const char *e = std::getenv("WQ_PREFILL_TILE_M");
+        return e ? std::atoi(e) : 0;
+    }();
+    if (forced == kPM || forced == kPrefillSmallTileM) return forced;
+    return M <= kSmallTileMaxM ? kPrefillSmallTileM : kPM;
+}
+
 // K splits: when the tiles alone leave compute units idle, split K so that
-// tiles x splits is just under 256 (one workgroup per compute unit), at
-// least 8 groups per split; between 192 and 383 tiles, 2 splits (the second
-// round of workgroups would otherwise run nearly empty).  Measured at M =
-// 512: 17408 -> 5120 (80 tiles) best at 3 splits, 174 vs 365 us unsplit;
+// tiles x splits is just under the workgroup slots (256 for 256-row tiles,
+// one per compute unit; 512 for 64-row tiles, two), at least 8 groups per
+// split; between 3/4 and 3/2 of the slots, 2 splits (the second round of
+// workgroups would otherwise run nearly empty).  Measured at M = 512:
+// 17408 -> 5120 (80 tiles) best at 3 splits, 174 vs 365 us unsplit;
 // 5120 -> 17408 (272 tiles) 219 us at 2 splits vs 240 us.
 // WQ_PREFILL_SPLITS forces a split count.
 static int prefill_splits(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = ((M + kPM - 1) / kPM) * ((N + kPN - 1) / kPN);
+    const int tm = prefill_tile_m(M);
+    const int64_t slots = tm == kPM ? 256 : 512;
+    const int64_t tiles = ((M + tm - 1) / tm) * ((N + kPN - 1) / kPN);
     const int G = (int)(K / kGroup);
     static const int forced = [] {
         const char *e = std::getenv("WQ_PREFILL_SPLITS");
         return e ? std::atoi(e) : 0;
     }();
     if (forced > 0) return std::max(1, std::min(forced, G));
-    if (tiles >= 384) return 1;
-    if (tiles >= 192) return G >= 16 ? 2 : 1;
-    int s = (int)std::max<int64_t>(1, 256 / tiles);
+    if (tiles >= slots * 3 / 2) return 1;
+    if (tiles >= slots * 3 / 4) return G >= 16 ? 2 : 1;
+    int s = (int)std::max<int64_t>(1, slots / tiles);
     return std::max(1, std::min(s, G / 8));
 }
 
@@ -669,20 +687,25 @@ static hipError_t prefill_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K,
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int mtiles = (int)((M + kPM - 1) / kPM);
+    const int tm = prefill_tile_m(M);
+    const int mtiles = (int)((M + tm - 1) / tm);
     const int ntiles = (int)((N + kPN - 1) / kPN);
     const dim3 grid((unsigned)(mtiles * ntiles * splits));
-    if (tiled) {
-        TiledW wl{static_cast<const uint8_t *>(W), G, B};
-        hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, NoGroups>), grid, dim3(512), 0, stream,
-                           A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles,
-                           splits, part, prefill_mnp(M, N), NoGroups{});
-    } else {
-        DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
-        hipLaunchKernelGGL((prefill_kernel<B, DenseW, ZP, NoGroups>), grid, dim3(512), 0, stream,
-                           A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles,
-                           splits, part, prefill_mnp(M, N), NoGroups{});
-    }
+    auto run = [&](auto wl) {
+        typedef decltype(wl) WL;
+        if (tm == kPM)
+            hipLaunchKernelGGL((prefill_kernel<B, WL, ZP, NoGroups>), grid, dim3(512), 0, stream,
+                               A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles,
+                               splits, part, prefill_mnp(M, N), NoGroups{});
+        else
+            hipLaunchKernelGGL((prefill_kernel<B, WL, ZP, NoGroups, kPrefillSmallTileM>), grid,
+                               dim3(256), 0, stream, A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros,
+                               Y, mtiles, ntiles, splits, part, prefill_mnp(M, N), NoGroups{});
+    };
+    if (tiled)
+        run(TiledW{static_cast<const uint8_t *>(W), G, B});
+    else
+        run(DenseW{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B});
     e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int64_t MN = M * N;
