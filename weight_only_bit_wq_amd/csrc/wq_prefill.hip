@@ -166,10 +166,11 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     constexpr bool kSmall = TM != kPM;
     __shared__ u32x4 As0[TM * 16];
     __shared__ u32x4 As1[TM * 16];
+    __shared__ u32x4 As2[kSmall ? TM * 16 : 1];  // third A buffer of the 64-row ring
     // Codes of the tile's 128 columns, double-buffered: [buffer][64-row
     // block][plane][row].  (One object: its reads come right after the
     // barrier, before any direct load into it is issued.)
-    __shared__ u32x4 Cs[2][2 * B * 64];
+    __shared__ u32x4 Cs[2][kSmall ? 1 : 2 * B * 64];
 
     const int G = K / kGroup;
     const int NP = Kp / kPseudoK;
@@ -229,7 +230,8 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
         doff[u] = (uint32_t)((min(dma_row0 + 4 * NW * u, mlim) * K + 8 * dma_chunk) * 2);
     auto dma = [&](const uint16_t *base, int k0, const uint32_t(&off)[RU], auto bconst)
         __attribute__((always_inline)) {
-        u32x4 *dst = decltype(bconst)::value == 0 ? As0 : As1;
+        constexpr int BUF = decltype(bconst)::value;
+        u32x4 *dst = BUF == 0 ? As0 : BUF == 1 ? As1 : As2;
         const uint8_t *b8 = reinterpret_cast<const uint8_t *>(base + k0);
 #pragma unroll
         for (int u = 0; u < RU; ++u)
@@ -337,7 +339,8 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
             bop[J][I] = quarter_pair<B, 4 * (J & 3) + I>(creg + (J >> 2) * B, mask, magic);
     };
     auto read_a = [&](auto bconst, int row0, int j, int set) __attribute__((always_inline)) {
-        const u32x4 *src = decltype(bconst)::value == 0 ? As0 : As1;
+        constexpr int BUF = decltype(bconst)::value;
+        const u32x4 *src = BUF == 0 ? As0 : BUF == 1 ? As1 : As2;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
             af[set][t] = __builtin_bit_cast(bf16x8_t, src[aoff[j] + (row0 + 32 * t) * 16]);
@@ -488,9 +491,11 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     // ---- real groups ----
     // Group g's A in buffer (g - g_lo) & 1.  Prologue: group g_lo's A, codes
     // and scale.
-    dma(A_blk, g_lo * kGroup, doff, std::integral_constant<int, 0>{});
-    dma_codes(g_lo, std::integral_constant<int, 0>{});
-    load_scale(g_lo, snext);
+    if constexpr (!kSmall) {
+        dma(A_blk, g_lo * kGroup, doff, std::integral_constant<int, 0>{});
+        dma_codes(g_lo, std::integral_constant<int, 0>{});
+        load_scale(g_lo, snext);
+    }
     auto group = [&](int g, auto bconst) __attribute__((always_inline)) {
         constexpr int BUF = decltype(bconst)::value;
         // Group g's A and codes have landed for this wave; after the barrier
@@ -519,7 +524,78 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
         sq_prev = sg;
     };
     int g = g_lo;
-    if (!kSmall && idle) {
+    if constexpr (kSmall) {
+        // 64-row tile, a three-stage ring: group g's A in LDS buffer
+        // (g - g_lo) % 3 and its codes (the lane's half-slot, loaded per lane),
+        // scale and zero point in register stage (g - g_lo) % 3, all issued two
+        // groups ahead.  The wait before group g leaves the L vector loads each
+        // wave issued for group g + 1 in flight (vector loads complete in
+        // issue order); the barrier after it also means every wave is done
+        // with the buffer group g + 2 then fills (read in group g - 1).
+        constexpr int NC = (B & 1) ? B : B / 2;           // code loads per lane
+        constexpr int L = RU + NC + 1 + (ZP ? 1 : 0);     // vector loads per group
+        static_assert(L < 16, "vmcnt field");
+        const uint8_t *cslot = reinterpret_cast<const uint8_t *>(wl.slot0(bcol));
+        int goff[NC];
+#pragma unroll
+        for (int q = 0; q < NC; ++q)
+            goff[q] = WL::dword_off(2 * h * B + ((B & 1) ? 2 * q : 4 * q));
+        uint32_t cr[3][2 * B];
+        uint32_t sr[3], zr[3];
+        auto issue = [&](int gi, auto sconst) __attribute__((always_inline)) {
+            constexpr int S = decltype(sconst)::value;
+            gi = min(gi, g_hi - 1);
+            dma(A_blk, gi * kGroup, doff, sconst);
+            const uint8_t *src = cslot + gi * bstep;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                if constexpr ((B & 1) == 0) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + goff[q]);
+                    cr[S][4 * q] = v.x;
+                    cr[S][4 * q + 1] = v.y;
+                    cr[S][4 * q + 2] = v.z;
+                    cr[S][4 * q + 3] = v.w;
+                } else {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(src + goff[q]);
+                    cr[S][2 * q] = v.x;
+                    cr[S][2 * q + 1] = v.y;
+                }
+            }
+            sr[S] = *reinterpret_cast<const uint16_t *>(sptr + gi * sstep);
+            if constexpr (ZP) zr[S] = zrow[gi];
+        };
+        auto ring_group = [&](int gi, auto sconst) __attribute__((always_inline)) {
+            constexpr int S = decltype(sconst)::value;
+            __builtin_amdgcn_s_waitcnt(0x0F70 | L);  // vmcnt(L)
+            // A bare barrier (the memory clobber keeps the compiler from
+            // moving LDS accesses across it): __syncthreads()' release fence
+            // would wait for every direct load, the next group's too.
+            asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < 2 * B; ++i) creg[i] = cr[S][i];
+            sreg = sr[S];
+            if constexpr (ZP)
+                zop = B == 8 ? __float_as_uint((float)zr[S]) : (64u - zr[S]) * 0x00010001u;
+            issue(gi + 2, std::integral_constant<int, (S + 2) % 3>{});
+            unpack_k0();
+            read_a(sconst, 0, 0, 0);
+            const float sg = bf16_to_f32((uint16_t)sreg);
+            phase(std::integral_constant<int, 0>{}, sconst, [&](int slot) { unpack_slot(slot); });
+#pragma unroll
+            for (int q = 0; q < 16; ++q) fold_slice(0, q, sg);
+        };
+        issue(g_lo, std::integral_constant<int, 0>{});
+        issue(g_lo + 1, std::integral_constant<int, 1>{});
+        for (; g + 2 < g_hi; g += 3) {
+            ring_group(g, std::integral_constant<int, 0>{});
+            ring_group(g + 1, std::integral_constant<int, 1>{});
+            ring_group(g + 2, std::integral_constant<int, 2>{});
+        }
+        if (g < g_hi) ring_group(g, std::integral_constant<int, 0>{});
+        if (g + 1 < g_hi) ring_group(g + 1, std::integral_constant<int, 1>{});
+        g = g_hi;
+    }
+    if constexpr (!kSmall) if (idle) {
         auto idle_group = [&](int gi, auto bconst) __attribute__((always_inline)) {
             constexpr int BUF = decltype(bconst)::value;
             __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -535,7 +611,7 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
         if (g < g_hi) idle_group(g, std::integral_constant<int, 0>{});
         g = g_hi;
     }
-    if (half) {
+    if constexpr (!kSmall) if (half) {
         // As group(), without phase 1: rows 0, 1 are folded after phase 0,
         // rows 2, 3 are empty.
         auto half_group = [&](int gi, auto bconst) __attribute__((always_inline)) {
