@@ -694,8 +694,8 @@ static int pseudo_kp(int64_t K) {
 // m-tile rows of a plain (not grouped) launch: 64 up to kSmallTileMaxM
 // rows, else 256.  Measured, b = 6, 5120 -> 17408 / 17408 -> 5120: M = 17..64
 // 32-35 / 44-48 us with 64-row tiles vs 57-58 / 53-56 with 256; M = 96, 128
-// 58-60 vs 61-63 both ways; M = 192 81 / 77 vs 75.  WQ_PREFILL_TILE_M (64 or
-// 256) forces one.
+// 58-61 vs 61-64 both ways; M = 160, 192 within 3% either way; M = 224, 256
+// 88-92 vs 85-89.  WQ_PREFILL_TILE_M (64 or 256) forces one.
 constexpr int64_t kSmallTileMaxM = 128;
 static int prefill_tile_m(int64_t M) {
     static const int forced = [] {
