@@ -45,8 +45,10 @@ constexpr int kPseudoK = 128;     // k' per pseudo-group
 
 // Pre-pass: per (row m, group g) v = -off * sum_{k in g} a[m,k], written as
 // three bf16 terms at k' = 3g + {0,1,2} of a [M, Kp] bf16 matrix (zero beyond
-// 3G).  One workgroup of 256 threads per row; 16 threads per group, fixed
-// reduction order.
+// 3G).  Workgroups of 256 threads, gridDim.y per row, each taking every
+// gridDim.y-th run of 2048 k: 16 threads per group, fixed reduction order;
+// the row's first workgroup clears the tail.
+constexpr int kSumChunk = 256 * 8;
 __global__ __launch_bounds__(256) void group_sum_split_kernel(const uint16_t *__restrict__ A,
                                                               int K, int Kp, float off,
                                                               uint16_t *__restrict__ Ap) {
@@ -54,8 +56,9 @@ __global__ __launch_bounds__(256) void group_sum_split_kernel(const uint16_t *__
     const int G = K / kGroup;
     const int t = threadIdx.x;
     uint16_t *out = Ap + m * Kp;
-    for (int k = 3 * G + t; k < Kp; k += 256) out[k] = 0;
-    for (int base = 0; base < K; base += 256 * 8) {
+    if (blockIdx.y == 0)
+        for (int k = 3 * G + t; k < Kp; k += 256) out[k] = 0;
+    for (int base = (int)blockIdx.y * kSumChunk; base < K; base += (int)gridDim.y * kSumChunk) {
         const int k0 = base + 8 * t;
         float s = 0.0f;
         if (k0 < K) {
@@ -686,6 +689,13 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__rest
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// Pre-pass workgroups per row: one per 2048 k for a few rows (a row's
+// serial walk over K is then the whole pass: M = 32, K = 17408 took 4.5 us),
+// one per row once the rows alone fill the chip.
+static unsigned sum_chunks(int64_t M, int64_t K) {
+    return M >= 1024 ? 1u : (unsigned)((K + kSumChunk - 1) / kSumChunk);
+}
+
 static int pseudo_kp(int64_t K) {
     const int G = (int)(K / kGroup);
     return (3 * G + kPseudoK - 1) / kPseudoK * kPseudoK;
@@ -758,7 +768,7 @@ static hipError_t prefill_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K,
                              : nullptr;
     hipError_t e = hipSuccess;
     if (Kp > 0) {
-        hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M), dim3(256), 0, stream, A,
+        hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M, sum_chunks(M, K)), dim3(256), 0, stream, A,
                            (int)K, Kp, off, Ap);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -818,7 +828,7 @@ static hipError_t prefill_grouped_bz(const uint16_t *A, int64_t M, int64_t N, in
     const int Kp = off != 0.0f ? pseudo_kp(K) : 0;
     uint16_t *Ap = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
     if (Kp > 0 && prepass) {
-        hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M), dim3(256), 0, stream, A,
+        hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M, sum_chunks(M, K)), dim3(256), 0, stream, A,
                            (int)K, Kp, off, Ap);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
