@@ -349,6 +349,48 @@ def test_w4a8_equals_wna16_b4_for_on_grid_activations(b):
     np.testing.assert_allclose(mag8 >= np.abs(y8), True)
 
 
+@pytest.mark.parametrize("b", [4, 6])
+def test_w4a8_exact_rational_brute_force(b):
+    # y and its tolerance denominator mag = |s_a| * sum_g |s_g * acc_g| in
+    # exact rational arithmetic, from codes read off the big-integer stream
+    # and activation codes from the fp32 numpy convention (not the oracle's
+    # own unpacker or quantizer).  The absolute value sits outside each
+    # group's integer sum [w4a8 Under the hood: group scales applied to the
+    # int products]; moving it inside (a looser bound) must fail here, so
+    # the case is checked to tell the two apart.
+    rng = np.random.default_rng(70 + b)
+    M, N, K = 2, 3, 384
+    codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
+    scales = synth.draw_scales_halfnormal_signed(rng, N, K // 128)
+    A = _bf16(rng.normal(size=(M, K)).astype(np.float32))
+    packed = oracle.pack(codes, b)
+    y, mag, Aq, sa = oracle.w4a8(A, packed, scales, b=b)
+    a = synth.bf16_bits_to_f32(A)
+    s_a = (np.abs(a).max(axis=1) / np.float32(127)).astype(np.float32)
+    q_a = np.clip(np.rint(a / s_a[:, None]), -127, 127).astype(np.int64)
+    np.testing.assert_array_equal(sa, s_a)
+    np.testing.assert_array_equal(Aq, q_a)
+    s = synth.bf16_bits_to_f32(scales)
+    for n in range(N):
+        stream = 0
+        for j, wd in enumerate(packed[n]):
+            stream |= int(wd) << (32 * j)
+        qw = [((stream >> (k * b)) & ((1 << b) - 1)) - (1 << (b - 1)) for k in range(K)]
+        for m in range(M):
+            acc = [sum(int(q_a[m, k]) * qw[k] for k in range(g * 128, (g + 1) * 128))
+                   for g in range(K // 128)]
+            exact = Fraction(float(s_a[m])) * sum(Fraction(float(s[n, g])) * acc[g]
+                                                  for g in range(K // 128))
+            exact_mag = abs(Fraction(float(s_a[m]))) * sum(abs(Fraction(float(s[n, g])) * acc[g])
+                                                           for g in range(K // 128))
+            loose = abs(Fraction(float(s_a[m]))) * sum(
+                abs(Fraction(float(s[n, k // 128])) * int(q_a[m, k]) * qw[k]) for k in range(K))
+            assert loose > exact_mag * Fraction(11, 10)  # the case separates the two readings
+            bound = 8 * 2.0 ** -52 * float(exact_mag)
+            assert abs(y[m, n] - float(exact)) <= bound
+            assert abs(mag[m, n] - float(exact_mag)) <= bound
+
+
 def test_w4a8_negative_scales_negate_output():
     w = synth.w4a8(M=8, N=32, K=512, seed=11)
     packed = oracle.pack(w.codes, 4)
