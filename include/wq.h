@@ -52,6 +52,8 @@
  *     [N, K/128] with values below 2^b, and only for b = 4 or 8
  *     (WQ_ERR_ZERO_POINTS).
  *   - Sizes are int64_t; M == 0 is a valid no-op; N, K must be > 0.
+ *     wq_gemm and wq_gemm_grouped take K <= 2^22 (WQ_ERR_INVALID_ARG above:
+ *     their tile offsets are 32-bit).
  */
 #ifndef WQ_H
 #define WQ_H
@@ -109,13 +111,22 @@ typedef enum wq_out_dtype {
 /* WQ_ABI_VERSION of the loaded library. */
 int wq_abi_version(void);
 
-/* Static text describing a wq_status value ("unknown status" otherwise). */
+/* Static text describing a wq_status value ("unknown status" otherwise):
+ * the reason a request was refused, in words (club-3090 discussion #733,
+ * "Which slugs": an invalid combination is refused and the reason given;
+ * model card "Qwen3.8-27B-INT6-Mixed-AutoRound", Findings: an unsupported
+ * width raises instead of computing something else). */
 const char *wq_status_str(int status);
 
 /* hipError_t of the last WQ_ERR_HIP returned on this thread (0 if none). */
 int wq_last_hip_error(void);
 
-/* 1 if HIP device `device` is a gfx950 the kernels were built for, else 0. */
+/* 1 if HIP device `device` is a gfx950 the kernels were built for, else 0:
+ * the capability gate (model card "Qwen3.8-27B-INT6-Mixed-AutoRound", How
+ * to use: the WNA16 kernel declares a minimum device capability and runs
+ * only on hardware that meets it; here that is the one architecture the
+ * library is built for).  Device entry points run
+ * the same check on the current device (WQ_ERR_UNSUPPORTED_DEVICE). */
 int wq_device_supported(int device);
 
 /* Packed row length of the dense layout: ceil(K * b / 32) 32-bit words
@@ -168,8 +179,11 @@ int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int g
  * WQ_LAYOUT_TILED (whose blob holds them; per-channel scales reach this
  * layer through wq_repack with group = K, the dense layout takes group 128
  * only).  zeros_d: NULL, or uint8 zero points [N, K/128] for b = 4 or 8.
- * Accumulation is fp32 with the integer codes exact and the group scale
- * applied once per group; the output is rounded to bf16 (nearest even).
+ * Every product multiplies an activation by the exact signed code
+ * (c - 2^(b-1), or c - z) as bf16, accumulation is fp32 and the group scale
+ * is applied once per group in fp32, so the rounding error of an output is
+ * bounded by the sum of |a * w| of its own terms (a row of midpoint codes
+ * gives exactly 0); the output is rounded to bf16 (nearest even).
  * ws_d / ws_bytes: see wq_workspace_bytes.  Results are deterministic
  * (fixed reduction order). */
 int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d, int layout,

@@ -112,6 +112,26 @@ def test_gemm_validation_statuses():
     assert _gemm(M=0, A=0, W=0, Y=0) == wq.WQ_OK                             # empty batch: no-op
 
 
+def test_gemm_refuses_k_beyond_32bit_tile_offsets():
+    # The prefill kernel's activation offsets within a 256-row tile are
+    # 32-bit (row * K * 2 bytes): K above 2^22 is refused before any device
+    # work, for every batch size and for the grouped layer.
+    big = (1 << 22) + 128
+    for M in (1, 16, 17, 4096):
+        assert _gemm(M=M, K=big, N=64) == wq.WQ_ERR_INVALID_ARG
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 4096, 64, big, 6) == -1
+    assert wq.wq_grouped_workspace_bytes([0, 20], 64, big, 6) == -1
+    lib = wq._load()
+    off = np.asarray([0, 20], dtype=np.int64)
+    assert lib.wq_gemm_grouped(ctypes.c_void_p(ALIGNED), 20, 64, big, ctypes.c_void_p(ALIGNED),
+                               1 << 30, None, wq._ptr(off), 1, 6, 128, ctypes.c_void_p(ALIGNED),
+                               None, 0, None) == wq.WQ_ERR_INVALID_ARG
+    # K = 2^22 passes the size checks (host-only query: never a launch on
+    # these fake pointers).
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 4096, 64, 1 << 22, 6) >= 0
+    assert wq.wq_grouped_workspace_bytes([0, 20], 64, 1 << 22, 6) >= 0
+
+
 def test_zero_point_and_per_channel_statuses():
     # Zero points only for b = 4 and 8; per-channel scales (group = K) only
     # through the tiled layout on the GEMM path.
@@ -232,5 +252,14 @@ def test_grouped_validation():
     assert call([0, 5], 5, bits=9) == wq.WQ_ERR_UNSUPPORTED_BITS
     assert call([0, 5], 5, Z=A) == wq.WQ_ERR_ZERO_POINTS      # b = 6 has no zero points
     assert call([0, 5], 5, E=0) == wq.WQ_ERR_INVALID_ARG
-    assert call([0, 20, 20], 20, ws_bytes=0) == wq.WQ_ERR_WORKSPACE
     assert call([0, 0, 0], 0) == wq.WQ_OK                     # no rows: no-op
+    # Prefill-sized experts need no workspace (no K split, no pre-pass);
+    # a decode table whose K is split does.
+    assert wq.wq_grouped_workspace_bytes([0, 20, 20], N, K, b) == 0
+    K2 = 5120
+    need = wq.wq_grouped_workspace_bytes([0, 3, 3], N, K2, b)
+    assert need > wq.WORKSPACE_ZERO_BYTES
+    off = np.asarray([0, 3, 3], dtype=np.int64)
+    eb2 = wq.wq_repacked_bytes(wq.WQ_LAYOUT_TILED, N, K2, b)
+    assert lib.wq_gemm_grouped(A, 3, N, K2, A, eb2, None, wq._ptr(off), 2, b, 128, A, A,
+                               need - 1, None) == wq.WQ_ERR_WORKSPACE

@@ -48,8 +48,8 @@ def test_grouped_mixed_sizes(b, zp):
 def test_grouped_tile_boundaries(b, zp):
     # Expert sizes on both sides of every tile boundary: 64-row tiles below
     # 192 remaining rows (64, 65, 191, 17, 128), 256-row tiles from 192 (192,
-    # 257 = 256 + a 1-row small tile, 449 = 256 + 193); K = 6144 (two
-    # pseudo-groups of the pre-pass constant), N = 136 (a ragged n-tile).
+    # 257 = 256 + a 1-row small tile, 449 = 256 + 193); K = 6144 (48
+    # groups), N = 136 (a ragged n-tile).
     E, N, K = 10, 136, 6144
     sizes = [64, 65, 191, 192, 257, 449, 17, 128, 0, 5]
     off = np.concatenate([[0], np.cumsum(sizes)])

@@ -1,7 +1,7 @@
 """GPU parity with zero points (b = 4 and 8) and per-channel scales (group = K)
 against the CPU oracle, through the C ABI: the WNA16 layer on every kernel
-(decode row tiles 1/4/8/16, the split-K hand-off, prefill with and without
-its pre-pass) in both layouts, the int8-activation path (b = 4) and the
+(decode row tiles 1/4/8/16, the split-K hand-off, prefill on both tile
+sizes) in both layouts, the int8-activation path (b = 4) and the
 embedding gather (bit-exact).  Pages: model card
 "Qwen3.8-27B-INT6-Mixed-AutoRound", Findings (the asymmetric form exists for
 4 and 8 bits); "vLLM Quantization", online shorthands (INT8, one scale per

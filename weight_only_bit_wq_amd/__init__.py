@@ -135,10 +135,14 @@ def _ptr(x):
     return ctypes.c_void_p(x.data_ptr())
 
 
-def _stream(stream=None):
+def _torch_stream(stream=None):
+    """The torch stream a call runs on: `stream`, else torch's current one."""
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
+def _stream(stream=None):
+    return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
 
 
 def _require_cuda(name: str, t, dtype=None, shape=None):
@@ -212,12 +216,13 @@ def wq_repack(packed_d, scales_d, K: int, b: int, group: int = GROUP,
     nbytes = wq_repacked_bytes(layout, N, K, b, group)
     if nbytes < 0:
         raise WQError("wq_repacked_bytes", WQ_ERR_INVALID_ARG)
+    ts = _torch_stream(stream)
     if out is None:
-        out = torch.empty(nbytes, dtype=torch.uint8, device=packed_d.device)
+        out = _empty_on(ts, nbytes, torch.uint8, packed_d.device)
     else:
         _require_cuda("out", out, torch.uint8, (nbytes,))
     _check("wq_repack", _load().wq_repack(_ptr(packed_d), _ptr(scales_d), N, K, b, group, layout,
-                                          _ptr(out), _stream(stream)))
+                                          _ptr(out), _stream(ts)))
     return out
 
 
@@ -226,12 +231,13 @@ def wq_unpack_dev(W_d, layout: int, N: int, K: int, b: int, group: int = GROUP, 
     """Device: codes of a weight buffer in `layout` -> uint8 [N, K]."""
     import torch
     _require_cuda("W_d", W_d)
+    ts = _torch_stream(stream)
     if out is None:
-        out = torch.empty((N, K), dtype=torch.uint8, device=W_d.device)
+        out = _empty_on(ts, (N, K), torch.uint8, W_d.device)
     else:
         _require_cuda("out", out, torch.uint8, (N, K))
     _check("wq_unpack_dev", _load().wq_unpack_dev(_ptr(W_d), layout, N, K, b, group, _ptr(out),
-                                                  _stream(stream)))
+                                                  _stream(ts)))
     return out
 
 
@@ -240,19 +246,31 @@ def wq_workspace_bytes(op: int, M: int, N: int, K: int, b: int, group: int = GRO
 
 
 # One zero-filled workspace per (device, stream); the library leaves it zeroed.
+# It is allocated and zeroed on the stream whose calls use it (inside
+# torch.cuda.stream(s)), so its zero fill is ordered before those calls and
+# torch's caching allocator ties the memory to that stream: a buffer
+# replaced by a larger one is only reused by later work on the same stream.
 _ws_cache: dict = {}
 
 
-def _workspace(nbytes: int, device, stream):
+def _workspace(nbytes: int, device, ts):
     import torch
     if nbytes <= 0:
         return None, 0
-    key = (str(device), int(stream.value or 0))
+    key = (str(device), int(ts.cuda_stream))
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(ts):
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf, buf.numel()
+
+
+def _empty_on(ts, shape, dtype, device):
+    """An output allocated on the stream that writes it (see _workspace)."""
+    import torch
+    with torch.cuda.stream(ts):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _require_zeros(zeros_d, N: int, K: int):
@@ -272,14 +290,15 @@ def wq_gemm(A_d, W_d, layout: int, scales_d, N: int, b: int, group: int = GROUP,
     if scales_d is not None:
         _require_cuda("scales_d", scales_d, (torch.bfloat16, torch.int16), (N, K // group))
     _require_zeros(zeros, N, K)
+    ts = _torch_stream(stream)
     if Y is None:
-        Y = torch.empty((M, N), dtype=torch.bfloat16, device=A_d.device)
+        Y = _empty_on(ts, (M, N), torch.bfloat16, A_d.device)
     else:
         _require_cuda("Y", Y, torch.bfloat16, (M, N))
-    st = _stream(stream)
+    st = _stream(ts)
     need = wq_workspace_bytes(WQ_OP_GEMM, M, N, K, b, group)
     if ws is None:
-        ws_buf, ws_bytes = _workspace(need, A_d.device, st)
+        ws_buf, ws_bytes = _workspace(need, A_d.device, ts)
     else:
         ws_buf, ws_bytes = ws, ws.numel() * ws.element_size()
     _check("wq_gemm", _load().wq_gemm(_ptr(A_d), M, N, K, _ptr(W_d), layout, _ptr(scales_d),
@@ -306,16 +325,17 @@ def wq_gemm_grouped(A_d, W_d, expert_bytes: int, offsets, N: int, b: int, group:
     E = off.size - 1
     if zeros is not None:
         _require_cuda("zeros_d", zeros, torch.uint8, (E * N, K // GROUP))
+    ts = _torch_stream(stream)
     if Y is None:
-        Y = torch.empty((M, N), dtype=torch.bfloat16, device=A_d.device)
+        Y = _empty_on(ts, (M, N), torch.bfloat16, A_d.device)
     else:
         _require_cuda("Y", Y, torch.bfloat16, (M, N))
-    st = _stream(stream)
+    st = _stream(ts)
     need = int(_load().wq_grouped_workspace_bytes(_ptr(off), E, N, K, b, group))
     if need < 0:
         raise WQError("wq_grouped_workspace_bytes", WQ_ERR_INVALID_ARG)
     if ws is None:
-        ws_buf, ws_bytes = _workspace(need, A_d.device, st)
+        ws_buf, ws_bytes = _workspace(need, A_d.device, ts)
     else:
         ws_buf, ws_bytes = ws, ws.numel() * ws.element_size()
     _check("wq_gemm_grouped", _load().wq_gemm_grouped(
@@ -329,12 +349,13 @@ def wq_quant_act_i8(A_d, Aq=None, sa=None, stream=None):
     import torch
     _require_cuda("A_d", A_d, torch.bfloat16)
     M, K = A_d.shape
+    ts = _torch_stream(stream)
     if Aq is None:
-        Aq = torch.empty((M, K), dtype=torch.int8, device=A_d.device)
+        Aq = _empty_on(ts, (M, K), torch.int8, A_d.device)
     if sa is None:
-        sa = torch.empty((M,), dtype=torch.float32, device=A_d.device)
+        sa = _empty_on(ts, (M,), torch.float32, A_d.device)
     _check("wq_quant_act_i8", _load().wq_quant_act_i8(_ptr(A_d), M, K, _ptr(Aq), _ptr(sa),
-                                                      _stream(stream)))
+                                                      _stream(ts)))
     return Aq, sa
 
 
@@ -350,12 +371,13 @@ def wq_embed(ids_d, W_d, scales_d, K: int, b: int, group: int = GROUP, Y=None, s
     _require_cuda("scales_d", scales_d, (torch.bfloat16, torch.int16), (V, K // group))
     _require_zeros(zeros, V, K)
     T = ids_d.numel()
+    ts = _torch_stream(stream)
     if Y is None:
-        Y = torch.empty((T, K), dtype=torch.bfloat16, device=W_d.device)
+        Y = _empty_on(ts, (T, K), torch.bfloat16, W_d.device)
     else:
         _require_cuda("Y", Y, torch.bfloat16, (T, K))
     _check("wq_embed", _load().wq_embed(_ptr(W_d), _ptr(scales_d), _ptr(zeros), V, K, b, group,
-                                        _ptr(ids_d), T, _ptr(Y), _stream(stream)))
+                                        _ptr(ids_d), T, _ptr(Y), _stream(ts)))
     return Y
 
 
@@ -371,14 +393,15 @@ def wq_gemm_a8(A_d, W_d, layout: int, scales_d, N: int, b: int = 4, group: int =
         _require_cuda("scales_d", scales_d, (torch.bfloat16, torch.int16), (N, K // group))
     _require_zeros(zeros, N, K)
     ydt = torch.float32 if out_dtype == WQ_OUT_F32 else torch.bfloat16
+    ts = _torch_stream(stream)
     if Y is None:
-        Y = torch.empty((M, N), dtype=ydt, device=A_d.device)
+        Y = _empty_on(ts, (M, N), ydt, A_d.device)
     else:
         _require_cuda("Y", Y, ydt, (M, N))
-    st = _stream(stream)
+    st = _stream(ts)
     need = wq_workspace_bytes(WQ_OP_GEMM_A8, M, N, K, b, group)
     if ws is None:
-        ws_buf, ws_bytes = _workspace(need, A_d.device, st)
+        ws_buf, ws_bytes = _workspace(need, A_d.device, ts)
     else:
         ws_buf, ws_bytes = ws, ws.numel() * ws.element_size()
     _check("wq_gemm_a8", _load().wq_gemm_a8(_ptr(A_d), M, N, K, _ptr(W_d), layout,

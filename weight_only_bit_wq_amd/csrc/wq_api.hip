@@ -53,6 +53,11 @@ bool dims_ok(int64_t M, int64_t N, int64_t K) {
     return M >= 0 && N > 0 && K > 0 && M < (1ll << 31) && N < (1ll << 31) && K < (1ll << 31);
 }
 
+// The WNA16 prefill kernel addresses a tile's activation rows with 32-bit
+// byte offsets (row * K * 2 with row < 256), which hold for K <= 2^22.
+constexpr int64_t kMaxGemmK = 1ll << 22;
+bool gemm_dims_ok(int64_t M, int64_t N, int64_t K) { return dims_ok(M, N, K) && K <= kMaxGemmK; }
+
 int query_device(int dev) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 2;
@@ -170,11 +175,11 @@ wq::DecodePlan grouped_decode_plan(const wq::GroupTable &t, int max_me, int64_t 
     return wq::decode_plan(max_me, (int64_t)t.n * t.per * 64, K, b);
 }
 
-int64_t grouped_ws_bytes(const int64_t *off, int64_t E, int64_t M, int64_t N, int64_t K, int b) {
+int64_t grouped_ws_bytes(const int64_t *off, int64_t E, int64_t N, int64_t K, int b) {
     int64_t need = 0;
     grouped_tables(off, E, N, 0, [&](bool is_dec, const wq::GroupTable &t, int max_me) {
-        need = std::max(need, is_dec ? grouped_decode_plan(t, max_me, N, K, b).ws_bytes
-                                     : wq::prefill_grouped_ws_bytes(M, K));
+        // Prefill tables need no workspace (no K split).
+        if (is_dec) need = std::max(need, grouped_decode_plan(t, max_me, N, K, b).ws_bytes);
     });
     return need;
 }
@@ -333,7 +338,7 @@ int wq_embed(const void *W_d, const uint16_t *scales_d, const uint8_t *zeros_d, 
 
 int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int group) {
     if (!dims_ok(M, N, K) || !valid_bits(b) || check_group(K, group) != WQ_OK) return -1;
-    if (op == WQ_OP_GEMM) return gemm_ws_bytes(M, N, K, b);
+    if (op == WQ_OP_GEMM) return K <= kMaxGemmK ? gemm_ws_bytes(M, N, K, b) : -1;
     if (op == WQ_OP_GEMM_A8) return wq::a8_ws_bytes(M, N, K);
     return -1;
 }
@@ -341,7 +346,7 @@ int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int g
 int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d, int layout,
             const uint16_t *scales_d, const uint8_t *zeros_d, int b, int group, uint16_t *Y_d,
             void *ws_d, int64_t ws_bytes, void *stream) {
-    if (!dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
+    if (!gemm_dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
     if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
     if (int s = check_group(K, group)) return s;
     if (layout != WQ_LAYOUT_DENSE && layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
@@ -363,19 +368,19 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
 
 int64_t wq_grouped_workspace_bytes(const int64_t *offsets, int64_t E, int64_t N, int64_t K,
                                    int b, int group) {
-    if (!dims_ok(0, N, K) || !valid_bits(b) || check_group(K, group) != WQ_OK || !offsets ||
+    if (!gemm_dims_ok(0, N, K) || !valid_bits(b) || check_group(K, group) != WQ_OK || !offsets ||
         E <= 0)
         return -1;
     const int64_t M = offsets[E];
     if (check_offsets(offsets, E, M) != WQ_OK || M >= (1ll << 31)) return -1;
-    return grouped_ws_bytes(offsets, E, M, N, K, b);
+    return grouped_ws_bytes(offsets, E, N, K, b);
 }
 
 int wq_gemm_grouped(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
                     int64_t expert_bytes, const uint8_t *zeros_d, const int64_t *offsets,
                     int64_t E, int b, int group, uint16_t *Y_d, void *ws_d, int64_t ws_bytes,
                     void *stream) {
-    if (!dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
+    if (!gemm_dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
     if (int s = check_offsets(offsets, E, M)) return s;
     if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
     if (int s = check_group(K, group)) return s;
@@ -386,13 +391,12 @@ int wq_gemm_grouped(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const 
     if (!A_d || !W_d || !Y_d) return WQ_ERR_INVALID_ARG;
     if (!aligned16(A_d) || !aligned16(W_d) || !aligned16(Y_d) || (ws_d && !aligned16(ws_d)))
         return WQ_ERR_MISALIGNED;
-    const int64_t need = grouped_ws_bytes(offsets, E, M, N, K, b);
+    const int64_t need = grouped_ws_bytes(offsets, E, N, K, b);
     if (need > 0 && (!ws_d || ws_bytes < need)) return WQ_ERR_WORKSPACE;
     if (int s = check_device()) return s;
-    // One launch per table, in order on the stream (one workspace: each
-    // leaves the counter region zero; the pre-pass matrix is computed once).
+    // One launch per table, in order on the stream (one workspace, used by
+    // the decode tables only: each leaves the counter region zero).
     hipError_t err = hipSuccess;
-    bool prepass = true;
     grouped_tables(offsets, E, N, expert_bytes,
                    [&](bool is_dec, const wq::GroupTable &t, int max_me) {
         if (err != hipSuccess) return;
@@ -401,9 +405,8 @@ int wq_gemm_grouped(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const 
                                             grouped_decode_plan(t, max_me, N, K, b), t,
                                             (hipStream_t)stream);
         } else {
-            err = wq::launch_prefill_grouped(A_d, M, N, K, W_d, zeros_d, b, Y_d, ws_d, t,
-                                             max_me, prepass, (hipStream_t)stream);
-            prepass = false;
+            err = wq::launch_prefill_grouped(A_d, M, N, K, W_d, zeros_d, b, Y_d, t, max_me,
+                                             (hipStream_t)stream);
         }
     });
     return err == hipSuccess ? WQ_OK : hip_fail(err);

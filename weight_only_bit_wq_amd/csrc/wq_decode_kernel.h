@@ -27,21 +27,17 @@
 //     adds them in split order (deterministic), writes bf16 and resets the
 //     ticket (in the workspace's counter region) to zero.
 //
-// Arithmetic per pair of codes (b <= 7): v_perm_b32 + packed 16-bit shift
-// pull the two fields (straddling or not) into the two 16-bit halves,
-// v_and_or_b32 masks them and sets the bf16 exponent of 128, giving exactly
-// (128 + c0, 128 + c1); v_dot2_f32_bf16 multiplies by the activation pair and
-// accumulates in fp32.  Per group the constant (128 + 2^(b-1)) * sum(a) is
-// removed and the group scale applied once in fp32:
-//     acc += s[n,g] * (sum_k a_k (128 + c_k) - (128 + 2^(b-1)) sum_k a_k)
-// which is sum_k a_k s (c_k - 2^(b-1)) with the integer codes exact.
-// Zero points (b = 4 and 8 only): for b = 4, (64 - z) is added to both
-// 16-bit halves after the exponent OR, so a pair becomes 192 + c - z exactly
-// (the mantissa 64 + c - z stays in 49..79), and the constant is 192; for
-// b = 8 the bytes convert to c - z (|c - z| <= 255, exact in bf16) and there
-// is no constant term.
-// For b = 8 codes are whole bytes: v_cvt_f32_ubyte{0..3} converts each one
-// and an fp32 FMA accumulates (offset 128).
+// Arithmetic: the codes of a slot are turned into exact signed values
+// q = c - 2^(b-1) (bf16 pairs, see wq_device.h: one XOR per word, a
+// sign-extending extract and an int -> float conversion per code, one pack
+// per pair), multiplied by the activations with fp32 accumulation
+// (v_dot2_f32_bf16 at one row, 4x4x4 matrix-core blocks at 2..16 rows), and
+// the group scale applied once per group in fp32:
+//     acc += s[n,g] * sum_{k in g} a_k * q_k
+// Every product is exact, so the rounding error is bounded by the sum of
+// |a * w| of the row's own terms (a row of midpoint codes gives exactly 0).
+// Zero points (b = 4 and 8 only) replace 2^(b-1) by z: q = c - z, exact too
+// (|c - z| <= 255).
 #pragma once
 
 #include "wq_device.h"
@@ -59,144 +55,63 @@ struct UVec<8> { typedef unsigned type __attribute__((ext_vector_type(8))); };
 template <>
 struct UVec<16> { typedef unsigned type __attribute__((ext_vector_type(16))); };
 
-// Pairs P0 + I .. P0 + CP - 1 of the group, activations already in av[]
-// (CP pairs of one row come in with one wide scalar load).
-template <int B, int MT, int CP, int P0, int I, bool ZP>
+// Pairs P0 + I .. P0 + CP - 1 of the slot against the activation pairs in
+// av (CP pairs of the one row come in with one wide scalar load).  Pair p
+// of the slot is pair p % 16 of its 32-code quarter p / 16.
+template <int B, int CP, int P0, int I, bool ZP>
 struct DotChunk {
     typedef typename UVec<CP>::type vec;
-    __device__ __forceinline__ static void run(const uint32_t *w, const vec *av, uint32_t mask,
-                                               uint32_t magic, uint32_t zv, float *d) {
-        uint32_t wp = code_pair_bf16_plus128<B, P0 + I>(w, mask, magic);
-        if constexpr (ZP) wp += zv;  // (64 - z) in both halves: 192 + c - z
-#pragma unroll
-        for (int m = 0; m < MT; ++m) d[m] = dot2_bf16(av[m][I], wp, d[m]);
-        DotChunk<B, MT, CP, P0, I + 1, ZP>::run(w, av, mask, magic, zv, d);
+    __device__ __forceinline__ static void run(const uint32_t *w, const vec &av, int z, float &d) {
+        constexpr int P = P0 + I;
+        d = dot2_bf16(av[I], wpair<B, P % 16, ZP>(w + (P / 16) * B, z), d);
+        DotChunk<B, CP, P0, I + 1, ZP>::run(w, av, z, d);
     }
 };
-template <int B, int MT, int CP, int P0, bool ZP>
-struct DotChunk<B, MT, CP, P0, CP, ZP> {
+template <int B, int CP, int P0, bool ZP>
+struct DotChunk<B, CP, P0, CP, ZP> {
     typedef typename UVec<CP>::type vec;
-    __device__ __forceinline__ static void run(const uint32_t *, const vec *, uint32_t, uint32_t,
-                                               uint32_t, float *) {}
+    __device__ __forceinline__ static void run(const uint32_t *, const vec &, int, float &) {}
 };
-
-// b = 8: codes are whole bytes.  Each byte goes through v_cvt_f32_ubyteN and
-// a pair is packed to bf16 with v_cvt_pk_bf16_f32 (values 0..255 are exact in
-// bf16), then the same dot2 path as narrower codes with offset 128.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t bytes_to_bf16x2(uint32_t x, int lo_byte) {
-    f32x2_t f;
-    f.x = (float)((x >> (8 * lo_byte)) & 0xFFu);
-    f.y = (float)((x >> (8 * lo_byte + 8)) & 0xFFu);
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-// b = 8 with a zero point: (c0 - z, c1 - z) as bf16 (exact, |c - z| <= 255).
-__device__ __forceinline__ uint32_t bytes_minus_to_bf16x2(uint32_t x, int lo_byte, float z) {
-    f32x2_t f;
-    f.x = (float)((x >> (8 * lo_byte)) & 0xFFu) - z;
-    f.y = (float)((x >> (8 * lo_byte + 8)) & 0xFFu) - z;
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-// The per-slot zero-point operand: b = 8 the float z, else (64 - z) in both
-// 16-bit halves.
-template <int B>
-__device__ __forceinline__ uint32_t zero_operand(uint32_t z) {
-    if constexpr (B == 8) return __float_as_uint((float)z);
-    else return (64u - z) * 0x00010001u;
-}
-
-template <int MT, bool ZP>
-__device__ __forceinline__ void dot_bytes(const uint32_t *w, const uint32_t *a,
-                                          const int *row_off, uint32_t zv, float *d) {
-    constexpr int CP = 16;
-    typedef typename UVec<CP>::type vec;
-#pragma unroll
-    for (int p0 = 0; p0 < 64; p0 += CP) {
-        vec av[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) av[m] = *reinterpret_cast<const vec *>(a + row_off[m] + p0);
-#pragma unroll
-        for (int i = 0; i < CP; ++i) {
-            const int p = p0 + i;
-            const uint32_t wp = ZP ? bytes_minus_to_bf16x2(w[p >> 1], 2 * (p & 1), __uint_as_float(zv))
-                                   : bytes_to_bf16x2(w[p >> 1], 2 * (p & 1));
-#pragma unroll
-            for (int m = 0; m < MT; ++m) d[m] = dot2_bf16(av[m][i], wp, d[m]);
-        }
-    }
-}
 
 // Everything a lane reads from memory for one (row, group) slot: its b
-// chunks, its scale, and pair `lane` of the group's activations in each row m
-// (for the group's activation sum).  A slot is loaded whole before the
-// previous one is computed: the vector-memory counter retires in issue
-// order, so a load issued after the next slot's prefetch would make the
-// current slot wait for that prefetch.
+// chunks, its scale and (with zero points) its zero point.  A slot is
+// loaded whole before the previous one is computed: the vector-memory
+// counter retires in issue order, so a load issued after the next slot's
+// prefetch would make the current slot wait for that prefetch.
 template <int B, int MT>
 struct SlotRegs {
     uint32_t w[4 * B];
-    uint32_t al[MT];
     uint16_t s;
     uint32_t z;  // zero point (only with zero points)
 };
 template <int B, int MT, bool ZP, class WL>
 __device__ __forceinline__ void load_slot_regs(const WL &wl, int64_t nr, int g,
-                                               const uint32_t *A2, const int *row_off, int lane,
                                                const uint8_t *zrow, SlotRegs<B, MT> &r) {
     load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), r.w);
     r.s = wl.scale(nr, g);
     if constexpr (ZP) r.z = zrow[g];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) r.al[m] = A2[(int64_t)g * 64 + row_off[m] + lane];
 }
 
-// One (row, group) slot of lane's row against group g of every row m of A:
-//     x[m] = sum_k a[m,k] (128 + c_k) - (128 + 2^(b-1)) sum_k a[m,k]
-// (offset 128 for b = 8); the caller applies the group scale.  `a` points at
-// the group's first activation pair of row 0 (read with scalar loads);
-// `row_off[m]` is row m's offset in pairs; `alane` the slot's al[].
-template <int B>
-constexpr float decode_offset(bool zp) {
-    return zp ? (B == 8 ? 0.0f : 192.0f) : (B == 8 ? 128.0f : (float)(128 + (1 << (B - 1))));
-}
-
-template <int B, int MT, bool ZP>
-__device__ __forceinline__ void group_terms(const uint32_t *w, const uint32_t *a,
-                                            const int *row_off, const uint32_t *alane,
-                                            uint32_t mask, uint32_t magic, uint32_t zv,
-                                            float *x) {
-    constexpr float kOff = decode_offset<B>(ZP);
-    float d[MT];
+// One (row, group) slot of lane's row against group g of the one row of A:
+//     x = sum_k a[k] q_k
+// (the caller applies the group scale).  `a` points at the group's first
+// activation pair (read with scalar loads: wave-uniform).  The slot's
+// words are sign-flipped in place.
+template <int B, bool ZP>
+__device__ __forceinline__ float group_terms(uint32_t *w, const uint32_t *a, int z) {
+    if constexpr (!ZP) flip_signs<B, 4 * B>(w);
+    // All 64 activation pairs of the group come in with four wide scalar
+    // loads issued together.
+    typedef typename UVec<16>::type vec16;
+    vec16 av[4];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) d[m] = 0.0f;
-    static_assert(MT == 1, "row tiles above 1 take the matrix-core form");
-    if constexpr (B == 8) {
-        dot_bytes<MT, ZP>(w, a, row_off, zv, d);
-    } else {
-        // One row: all 64 activation pairs of the group come in with four
-        // wide scalar loads issued together.
-        typedef typename UVec<16>::type vec16;
-        vec16 av[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) av[c] = *reinterpret_cast<const vec16 *>(a + 16 * c);
-        DotChunk<B, 1, 16, 0, 0, ZP>::run(w, &av[0], mask, magic, zv, d);
-        DotChunk<B, 1, 16, 16, 0, ZP>::run(w, &av[1], mask, magic, zv, d);
-        DotChunk<B, 1, 16, 32, 0, ZP>::run(w, &av[2], mask, magic, zv, d);
-        DotChunk<B, 1, 16, 48, 0, ZP>::run(w, &av[3], mask, magic, zv, d);
-    }
-    // Sum of this group's activations per row m: lane l adds pair l, then
-    // a DPP reduction across the wave (wave-uniform result).
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if constexpr (kOff == 0.0f) {
-            x[m] = d[m];
-        } else {
-            const float asum = wave_sum_uniform(dot2_bf16(alane[m], 0x3F803F80u, 0.0f));
-            x[m] = fmaf(-kOff, asum, d[m]);
-        }
-    }
+    for (int c = 0; c < 4; ++c) av[c] = *reinterpret_cast<const vec16 *>(a + 16 * c);
+    float d = 0.0f;
+    DotChunk<B, 16, 0, 0, ZP>::run(w, av[0], z, d);
+    DotChunk<B, 16, 16, 0, ZP>::run(w, av[1], z, d);
+    DotChunk<B, 16, 32, 0, ZP>::run(w, av[2], z, d);
+    DotChunk<B, 16, 48, 0, ZP>::run(w, av[3], z, d);
+    return d;
 }
 
 // ---------------------------------------------------------------------------
@@ -220,23 +135,14 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 template <int B, int Q, int J, bool ZP>
 struct MfmaSteps {
-    __device__ __forceinline__ static void run(const uint32_t *w, const u32x4 *av, uint32_t mask,
-                                               uint32_t magic, uint32_t zv, f32x4_t *d) {
+    __device__ __forceinline__ static void run(const uint32_t *w, const u32x4 *av, int z,
+                                               f32x4_t *d) {
+        // k-step J: codes 4J .. 4J+3, pairs 2J and 2J+1 of the slot (pair p
+        // is pair p % 16 of quarter p / 16).
+        constexpr int P0 = 2 * J, P1 = 2 * J + 1;
         u32x2_t wp;
-        if constexpr (B == 8 && ZP) {
-            wp.x = bytes_minus_to_bf16x2(w[J], 0, __uint_as_float(zv));
-            wp.y = bytes_minus_to_bf16x2(w[J], 2, __uint_as_float(zv));
-        } else if constexpr (B == 8) {
-            wp.x = bytes_to_bf16x2(w[J], 0);
-            wp.y = bytes_to_bf16x2(w[J], 2);
-        } else {
-            wp.x = code_pair_bf16_plus128<B, 2 * J>(w, mask, magic);
-            wp.y = code_pair_bf16_plus128<B, 2 * J + 1>(w, mask, magic);
-            if constexpr (ZP) {
-                wp.x += zv;
-                wp.y += zv;
-            }
-        }
+        wp.x = wpair<B, P0 % 16, ZP>(w + (P0 / 16) * B, z);
+        wp.y = wpair<B, P1 % 16, ZP>(w + (P1 / 16) * B, z);
         const bf16x4_bits bw = __builtin_bit_cast(bf16x4_bits, wp);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -246,36 +152,13 @@ struct MfmaSteps {
             d[q] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4_bits, a), bw,
                                                           d[q], 4, J >> 1, 0);
         }
-        MfmaSteps<B, Q, J + 1, ZP>::run(w, av, mask, magic, zv, d);
+        MfmaSteps<B, Q, J + 1, ZP>::run(w, av, z, d);
     }
 };
 template <int B, int Q, bool ZP>
 struct MfmaSteps<B, Q, 32, ZP> {
-    __device__ __forceinline__ static void run(const uint32_t *, const u32x4 *, uint32_t, uint32_t,
-                                               uint32_t, f32x4_t *) {}
+    __device__ __forceinline__ static void run(const uint32_t *, const u32x4 *, int, f32x4_t *) {}
 };
-
-// Sum over the 16 lanes 4i + r (i = 0..15) of a value, for each r; every
-// lane receives the sum for its own r.  Two row rotations add the 4 lanes of
-// a 16-lane row, the permlane swaps then add rows 2t and 2t+1, and the wave's
-// halves.  Fixed order, so deterministic.
-__device__ __forceinline__ float lane_class4_sum(float v) {
-    v = dpp_add<0x124, 0xF>(v);  // row_ror:4
-    v = dpp_add<0x128, 0xF>(v);  // row_ror:8
-    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
-                                                      false, false);
-    v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
-                                                      false, false);
-    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-}
-
-// Value of lane 4 * (lane / 4) + R (quad_perm [R, R, R, R]; every lane has
-// a source, so no old value is needed).
-template <int R>
-__device__ __forceinline__ float quad_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), R * 0x55, 0xF, 0xF, false));
-}
 
 // Everything a lane reads for one (row, group) slot on the matrix-core form:
 // its b chunks, its scale and its 16-byte activation register per set.
@@ -300,38 +183,22 @@ __device__ __forceinline__ void load_slot_regs_mf(const WL &wl, int64_t nr, int 
                                                    4 * (lane >> 2));
 }
 
-// x[m] = sum_k a[m,k] (128 + c_k) - (128 + 2^(b-1)) sum_k a[m,k] for the
-// lane's row and rows m = 0 .. MT-1 of A (offset 128 for b = 8), as in
-// group_terms; the caller applies the group scale.
+// x[m] = sum_k a[m,k] q_k for the lane's row and rows m = 0 .. MT-1 of A,
+// as in group_terms; the caller applies the group scale.
 template <int B, int MT, bool ZP>
-__device__ __forceinline__ void group_terms_mf(const uint32_t *w, const u32x4 *av, uint32_t mask,
-                                               uint32_t magic, uint32_t zv, float *x) {
+__device__ __forceinline__ void group_terms_mf(uint32_t *w, const u32x4 *av, int z, float *x) {
     constexpr int Q = MT / 4;
-    constexpr float kOff = decode_offset<B>(ZP);
+    if constexpr (!ZP) flip_signs<B, 4 * B>(w);
     f32x4_t d[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) d[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    MfmaSteps<B, Q, 0, ZP>::run(w, av, mask, magic, zv, d);
+    MfmaSteps<B, Q, 0, ZP>::run(w, av, z, d);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        if constexpr (kOff == 0.0f) {
-            x[4 * q + 0] = d[q][0];
-            x[4 * q + 1] = d[q][1];
-            x[4 * q + 2] = d[q][2];
-            x[4 * q + 3] = d[q][3];
-            continue;
-        }
-        // Row 4q + (lane & 3)'s group sum: the lane's 8 activations, then
-        // over the 16 lanes holding the same row.
-        float ps = dot2_bf16(av[q][0], 0x3F803F80u, 0.0f);
-        ps = dot2_bf16(av[q][1], 0x3F803F80u, ps);
-        ps = dot2_bf16(av[q][2], 0x3F803F80u, ps);
-        ps = dot2_bf16(av[q][3], 0x3F803F80u, ps);
-        const float as = lane_class4_sum(ps);
-        x[4 * q + 0] = fmaf(-kOff, quad_bcast<0>(as), d[q][0]);
-        x[4 * q + 1] = fmaf(-kOff, quad_bcast<1>(as), d[q][1]);
-        x[4 * q + 2] = fmaf(-kOff, quad_bcast<2>(as), d[q][2]);
-        x[4 * q + 3] = fmaf(-kOff, quad_bcast<3>(as), d[q][3]);
+        x[4 * q + 0] = d[q][0];
+        x[4 * q + 1] = d[q][1];
+        x[4 * q + 2] = d[q][2];
+        x[4 * q + 3] = d[q][3];
     }
 }
 
@@ -387,12 +254,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-    const uint32_t mask = __builtin_amdgcn_readfirstlane(pair_mask<B < 8 ? B : 7>());
-    const uint32_t magic = in_vgpr(kBf16Magic128x2);
-
-    int row_off[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) row_off[m] = min(m, M - 1) * Kp;
     // Matrix-core form: lane 4i + r reads row 4q + r of set q (rows past M
     // repeat row M-1; their outputs are dropped).
     int arow_off[MF ? MT / 4 : 1];
@@ -407,7 +268,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
             SlotRegsMf<B, MT> cur;
             load_slot_regs_mf<B, MT, ZP>(wl, nr, g, A2, arow_off, lane, zrow, cur);
             float x[MT];
-            group_terms_mf<B, MT, ZP>(cur.w, cur.av, mask, magic, zero_operand<B>(cur.z), x);
+            group_terms_mf<B, MT, ZP>(cur.w, cur.av, (int)cur.z, x);
             const float sc = bf16_to_f32(cur.s);
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m] = sc * x[m];
@@ -421,7 +282,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
             if (gn < g_end)
                 load_slot_regs_mf<B, MT, ZP>(wl, nr, gn, A2, arow_off, lane, zrow, nxt);
             float x[MT];
-            group_terms_mf<B, MT, ZP>(cur.w, cur.av, mask, magic, zero_operand<B>(cur.z), x);
+            group_terms_mf<B, MT, ZP>(cur.w, cur.av, (int)cur.z, x);
             const float sc = bf16_to_f32(cur.s);
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
@@ -431,27 +292,18 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         const int g = g_begin + wave;
         if (g < g_end) {
             SlotRegs<B, MT> cur;
-            load_slot_regs<B, MT, ZP>(wl, nr, g, A2, row_off, lane, zrow, cur);
-            float x[MT];
-            group_terms<B, MT, ZP>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic,
-                                   zero_operand<B>(cur.z), x);
-            const float sc = bf16_to_f32(cur.s);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m] = sc * x[m];
+            load_slot_regs<B, MT, ZP>(wl, nr, g, zrow, cur);
+            acc[0] = bf16_to_f32(cur.s) * group_terms<B, ZP>(cur.w, A2 + (int64_t)g * 64, (int)cur.z);
         }
     } else {
         SlotRegs<B, MT> cur, nxt;
         int g = g_begin + wave;
-        if (g < g_end) load_slot_regs<B, MT, ZP>(wl, nr, g, A2, row_off, lane, zrow, cur);
+        if (g < g_end) load_slot_regs<B, MT, ZP>(wl, nr, g, zrow, cur);
         for (; g < g_end; g += W) {
             const int gn = g + W;
-            if (gn < g_end) load_slot_regs<B, MT, ZP>(wl, nr, gn, A2, row_off, lane, zrow, nxt);
-            float x[MT];
-            group_terms<B, MT, ZP>(cur.w, A2 + (int64_t)g * 64, row_off, cur.al, mask, magic,
-                                   zero_operand<B>(cur.z), x);
-            const float sc = bf16_to_f32(cur.s);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
+            if (gn < g_end) load_slot_regs<B, MT, ZP>(wl, nr, gn, zrow, nxt);
+            const float x = group_terms<B, ZP>(cur.w, A2 + (int64_t)g * 64, (int)cur.z);
+            acc[0] = fmaf(bf16_to_f32(cur.s), x, acc[0]);
             cur = nxt;
         }
     }

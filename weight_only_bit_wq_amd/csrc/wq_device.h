@@ -144,32 +144,94 @@ __device__ __forceinline__ uint32_t code_pair(const uint32_t *w) {
     return code_pair_raw<B, P>(w) & pair_mask<B>();
 }
 
-// (x & m) | c, selected as one v_and_or_b32: gfx9 VOP3 encodings take no
-// literal constants and at most one scalar operand, so the mask comes in an
-// SGPR (wave-uniform) and the constant in a VGPR the compiler cannot see
-// through (in_vgpr), which the caller materialises once.  Plain code rather
-// than inline assembly, so the hazard recognizer and scheduler see it.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m_sgpr, uint32_t c_vgpr) {
-    return (x & m_sgpr) | c_vgpr;
+// ---------------------------------------------------------------------------
+// Exact signed codes.
+//
+// The GEMM kernels multiply activations by the signed code q = c - 2^(b-1)
+// itself, as an exact bf16 (|q| <= 128 has at most 8 significant bits), and
+// apply the group scale once per group in fp32.  So every product a * q is
+// exact and the rounding error of a dot product is bounded by the sum of
+// |a * w| of its own terms: a row of midpoint codes (zero weights) gives
+// exactly zero whatever the activations.  (An operand with a constant offset
+// such as 128 + c, removed afterwards, would instead carry rounding error
+// proportional to that offset times sum |a|.)
+//
+// For a b-bit code c, c XOR 2^(b-1) is the b-bit two's complement of q.  A
+// run of 32 codes is exactly b 32-bit words, so one XOR per word with the
+// pattern of every code's top bit, then one sign-extending bit-field
+// extract per code (v_bfe_i32; a code that straddles two words first goes
+// through v_alignbit_b32), gives q as an int32; v_cvt_f32_i32 converts it
+// exactly and v_cvt_pk_bf16_f32 packs two of them (exact: |q| <= 128).
+// For b = 8 the extracts are whole bytes and the compiler folds them into
+// the conversions (SDWA byte selects).
+// ---------------------------------------------------------------------------
+
+// Top bits of the codes whose top bit lies in word d of a 32-code run.
+template <int B>
+__host__ __device__ constexpr uint32_t sign_bits(int d) {
+    uint32_t p = 0;
+    for (int k = 0; k < 32; ++k) {
+        const int t = k * B + B - 1 - 32 * d;
+        if (t >= 0 && t < 32) p |= 1u << t;
+    }
+    return p;
 }
 
-// For B <= 7: the pair as two bf16 values (128 + c0, 128 + c1), exact.
-// bf16 0x4300 is 128.0 with a zero 7-bit mantissa, so OR-ing a code c < 128
-// into the mantissa gives exactly 128 + c.  `mask` must hold pair_mask<B>()
-// and `magic` kBf16Magic128x2.
-constexpr uint32_t kBf16Magic128x2 = 0x43004300u;
+// XOR the n words of a slot or part of one (starting at word d0 of a
+// 32-code run) with the code top bits, in place.
+template <int B, int NW>
+__device__ __forceinline__ void flip_signs(uint32_t *w, int d0 = 0) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] ^= sign_bits<B>((d0 + i) % B);
+}
+
+// Code K (0..31) of a 32-code run held in B sign-flipped words: q as float.
+template <int B, int K>
+__device__ __forceinline__ float qcode_f32(const uint32_t *wx) {
+    constexpr int o = K * B, d = o >> 5, sh = o & 31;
+    int v;
+    if constexpr (sh + B <= 32)
+        v = __builtin_amdgcn_sbfe((int)wx[d], sh, B);
+    else
+        v = __builtin_amdgcn_sbfe((int)__builtin_amdgcn_alignbit(wx[d + 1], wx[d], sh), 0, B);
+    return (float)v;
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats that hold small integers as a bf16 pair (lo, hi); exact.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2_t f;
+    f.x = lo;
+    f.y = hi;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// Codes 2P, 2P+1 (P = 0..15) of a 32-code run as the bf16 pair (q0, q1).
 template <int B, int P>
-__device__ __forceinline__ uint32_t code_pair_bf16_plus128(const uint32_t *w, uint32_t mask,
-                                                           uint32_t magic) {
-    static_assert(B <= 7, "magic-exponent conversion needs codes < 128");
-    return and_or(code_pair_raw<B, P>(w), mask, magic);
+__device__ __forceinline__ uint32_t qpair(const uint32_t *wx) {
+    return pack_bf16x2(qcode_f32<B, 2 * P>(wx), qcode_f32<B, 2 * P + 1>(wx));
 }
 
-// Materialise a constant in a VGPR (opaque to constant folding).
-__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
-    uint32_t r;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
-    return r;
+// With a zero point z (b = 4, 8; words not sign-flipped): (c - z) as float,
+// |c - z| <= 255, exact in fp32 and in bf16.
+template <int B, int K>
+__device__ __forceinline__ float zcode_f32(const uint32_t *w, int z) {
+    static_assert(B == 4 || B == 8, "zero points exist for 4 and 8 bits");
+    constexpr int o = K * B, d = o >> 5, sh = o & 31;
+    return (float)((int)__builtin_amdgcn_ubfe(w[d], sh, B) - z);
+}
+template <int B, int P>
+__device__ __forceinline__ uint32_t zpair(const uint32_t *w, int z) {
+    return pack_bf16x2(zcode_f32<B, 2 * P>(w, z), zcode_f32<B, 2 * P + 1>(w, z));
+}
+
+// Pair P of a run: the symmetric or the zero-point form (w sign-flipped
+// only in the symmetric form).
+template <int B, int P, bool ZP>
+__device__ __forceinline__ uint32_t wpair(const uint32_t *w, int z) {
+    if constexpr (ZP) return zpair<B, P>(w, z);
+    else return qpair<B, P>(w);
 }
 
 // Load the 4*B words of one slot (B 16-byte chunks, `stride` uint4 apart).
@@ -252,8 +314,8 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
 // ---------------------------------------------------------------------------
 // Quarter slots.  A group's 128 codes split into 4 quarters of 32 codes; a
 // quarter is exactly B 32-bit words (32 * B bits), so dwords [Q*B, Q*B+B) of
-// a slot hold quarter Q.  The matrix-core kernels give one lane one quarter
-// of a row and unpack it straight into bf16 operand pairs.
+// a slot hold quarter Q.  The int8-activation kernel gives a lane a quarter
+// of a row and widens it straight into int8 operand registers.
 // ---------------------------------------------------------------------------
 
 // Codes 2P, 2P+1 of a 32-code quarter slot held in B words.
@@ -272,64 +334,6 @@ struct QSel {
     static constexpr int sh0 = o0 & 7;
     static constexpr int sh1 = o1 & 7;
     static constexpr bool has_hi = word + 1 < B;
-};
-
-template <int B, int P>
-__device__ __forceinline__ uint32_t quarter_pair(const uint32_t *w, uint32_t mask,
-                                                 uint32_t magic) {
-    if constexpr (B == 8) {
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const uint32_t x = w[P >> 1];
-        f32x2 f;
-        f.x = (float)((x >> (16 * (P & 1))) & 0xFFu);
-        f.y = (float)((x >> (16 * (P & 1) + 8)) & 0xFFu);
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-    } else {
-        using S = QSel<B, P>;
-        const uint32_t lo = w[S::word];
-        const uint32_t hi = S::has_hi ? w[S::word + 1] : 0u;
-        uint32_t x = __builtin_amdgcn_perm(hi, lo, S::sel);
-        if constexpr (S::sh0 != 0 || S::sh1 != 0) x = pk_shr16(x, S::sh0, S::sh1);
-        return and_or(x, mask, magic);
-    }
-}
-
-// quarter_pair<B, P> for a P that is a constant after unrolling.
-template <int B>
-__device__ __forceinline__ uint32_t quarter_pair_dyn(int p, const uint32_t *w, uint32_t mask,
-                                                     uint32_t magic) {
-    switch (p) {
-        case 0: return quarter_pair<B, 0>(w, mask, magic);
-        case 1: return quarter_pair<B, 1>(w, mask, magic);
-        case 2: return quarter_pair<B, 2>(w, mask, magic);
-        case 3: return quarter_pair<B, 3>(w, mask, magic);
-        case 4: return quarter_pair<B, 4>(w, mask, magic);
-        case 5: return quarter_pair<B, 5>(w, mask, magic);
-        case 6: return quarter_pair<B, 6>(w, mask, magic);
-        case 7: return quarter_pair<B, 7>(w, mask, magic);
-        case 8: return quarter_pair<B, 8>(w, mask, magic);
-        case 9: return quarter_pair<B, 9>(w, mask, magic);
-        case 10: return quarter_pair<B, 10>(w, mask, magic);
-        case 11: return quarter_pair<B, 11>(w, mask, magic);
-        case 12: return quarter_pair<B, 12>(w, mask, magic);
-        case 13: return quarter_pair<B, 13>(w, mask, magic);
-        case 14: return quarter_pair<B, 14>(w, mask, magic);
-        default: return quarter_pair<B, 15>(w, mask, magic);
-    }
-}
-
-template <int B, int P>
-struct QuarterPairs {
-    __device__ __forceinline__ static void run(const uint32_t *w, uint32_t mask, uint32_t magic,
-                                               uint32_t *out) {
-        out[P] = quarter_pair<B, P>(w, mask, magic);
-        QuarterPairs<B, P + 1>::run(w, mask, magic, out);
-    }
-};
-template <int B>
-struct QuarterPairs<B, 16> {
-    __device__ __forceinline__ static void run(const uint32_t *, uint32_t, uint32_t,
-                                               uint32_t *) {}
 };
 
 // Dwords [Q*B, Q*B + B) of a slot (its quarter Q: codes 32Q .. 32Q+31) into

@@ -78,16 +78,13 @@ hipError_t launch_embed(const void *W, const uint16_t *scales, const uint8_t *ze
                         int64_t T, uint16_t *Y, hipStream_t stream);
 
 // Grouped prefill: one entry of gt per m-tile of tile_m rows
-// (kPrefillTileM or kPrefillSmallTileM, one size per launch); the workspace
-// holds the pre-pass matrix for all M rows (prefill_grouped_ws_bytes),
-// computed when `prepass` (once per call: later launches reuse it).
+// (kPrefillTileM or kPrefillSmallTileM, one size per launch); no K split,
+// no workspace.
 constexpr int kPrefillTileM = 256;
 constexpr int kPrefillSmallTileM = 64;
-int64_t prefill_grouped_ws_bytes(int64_t M, int64_t K);
 hipError_t launch_prefill_grouped(const uint16_t *A, int64_t M, int64_t N, int64_t K,
                                   const void *W, const uint8_t *zeros, int b, uint16_t *Y,
-                                  void *ws, const GroupTable &gt, int tile_m, bool prepass,
-                                  hipStream_t stream);
+                                  const GroupTable &gt, int tile_m, hipStream_t stream);
 
 // ---- W4A8 (wq_a8.hip) ----
 hipError_t launch_quant_act(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq, float *sa,

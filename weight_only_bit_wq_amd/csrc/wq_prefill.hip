@@ -5,21 +5,15 @@
 // on the matrix cores (v_mfma_f32_32x32x16_bf16) with fp32 accumulation and
 // the codes are dequantized straight into their operand registers.
 //
-// Exactness.  The B operand holds 128 + c as bf16 (exact for c < 128; b = 8
-// uses byte conversion, offset 128), so the integer codes are never rounded.
-// Each group of 128 k is accumulated into its own fp32 block P_g and folded
-// as  total += s[n,g] * P_g  in fp32.  The constant part
-//     -(128 + 2^(b-1)) * sum_g s[n,g] * sum_{k in g} a[m,k]
-// is a small product over groups: a pre-pass writes, per (row m, group g),
-// v = -(128 + 2^(b-1)) * sum_{k in g} a[m,k] split exactly into three bf16
-// terms (hi + mid + lo, error ~2^-24 |v|) at k' = 3g + t, and the main loop
-// multiplies that against s[n, k'/3] as extra "pseudo-groups" with scale 1.
-// No scale or code is ever rounded to bf16.
+// Exactness.  The B operand holds the signed code q = c - 2^(b-1) itself
+// as an exact bf16 (wq_device.h), so the integer codes are never rounded
+// and no constant offset is carried through the accumulation.  Each group
+// of 128 k is accumulated into its own fp32 block P_g and folded as
+// total += s[n,g] * P_g in fp32.  No scale or code is ever rounded to bf16,
+// and the rounding error of an output is bounded by the sum of |a * w| of
+// its own terms.
 //
-// Zero points (b = 4 and 8): b = 4 adds (64 - z) to both 16-bit halves of a
-// pair after the exponent OR, so B holds 192 + c - z exactly and the
-// pre-pass constant is 192; b = 8 converts bytes to c - z (exact in bf16)
-// and has no constant term, so it runs without the pre-pass.
+// Zero points (b = 4 and 8): q = c - z, exact as well (|c - z| <= 255).
 //
 // Tiling.  Workgroup 256 (m) x 128 (n), 8 waves of 128 x 32 (two per SIMD),
 // each as four 32 x 32 MFMA blocks run in two staggered phases.  K runs in
@@ -41,51 +35,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPM = 256;          // workgroup rows (m)
 constexpr int kPN = 128;          // workgroup cols (n)
-constexpr int kPseudoK = 128;     // k' per pseudo-group
-
-// Pre-pass: per (row m, group g) v = -off * sum_{k in g} a[m,k], written as
-// three bf16 terms at k' = 3g + {0,1,2} of a [M, Kp] bf16 matrix (zero beyond
-// 3G).  Workgroups of 256 threads, gridDim.y per row, each taking every
-// gridDim.y-th run of 2048 k: 16 threads per group, fixed reduction order;
-// the row's first workgroup clears the tail.
-constexpr int kSumChunk = 256 * 8;
-__global__ __launch_bounds__(256) void group_sum_split_kernel(const uint16_t *__restrict__ A,
-                                                              int K, int Kp, float off,
-                                                              uint16_t *__restrict__ Ap) {
-    const int64_t m = blockIdx.x;
-    const int G = K / kGroup;
-    const int t = threadIdx.x;
-    uint16_t *out = Ap + m * Kp;
-    if (blockIdx.y == 0)
-        for (int k = 3 * G + t; k < Kp; k += 256) out[k] = 0;
-    for (int base = (int)blockIdx.y * kSumChunk; base < K; base += (int)gridDim.y * kSumChunk) {
-        const int k0 = base + 8 * t;
-        float s = 0.0f;
-        if (k0 < K) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(A + m * K + k0);
-            s = dot2_bf16(v.x, 0x3F803F80u, s);
-            s = dot2_bf16(v.y, 0x3F803F80u, s);
-            s = dot2_bf16(v.z, 0x3F803F80u, s);
-            s = dot2_bf16(v.w, 0x3F803F80u, s);
-        }
-        // 16 consecutive threads hold one group (16 x 8 = 128 k).
-        s += __shfl_xor(s, 1, 16);
-        s += __shfl_xor(s, 2, 16);
-        s += __shfl_xor(s, 4, 16);
-        s += __shfl_xor(s, 8, 16);
-        if ((t & 15) == 0 && k0 < K) {
-            const int g = k0 / kGroup;
-            const float v = -off * s;
-            const uint16_t hi = f32_to_bf16_rne(v);
-            const float r1 = v - bf16_to_f32(hi);
-            const uint16_t mid = f32_to_bf16_rne(r1);
-            const float r2 = r1 - bf16_to_f32(mid);
-            out[3 * g + 0] = hi;
-            out[3 * g + 1] = mid;
-            out[3 * g + 2] = f32_to_bf16_rne(r2);
-        }
-    }
-}
 
 // LDS tiles are rows of 16-byte chunks (8 bf16 of k), 16 chunks (one group
 // of 128 k, 256 bytes) per row; chunk c of row r sits at r*16 + (c ^ (r &
@@ -113,7 +62,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // .. 32 h + 31), the 8 k of chunk 8 h + j; both operands use that order, so
 // lane (column n, half h) needs codes 64 h .. 64 h + 63 of row n's group:
 // dwords 2 h B .. 2 h B + 2 B - 1 of the slot, one contiguous half-slot,
-// loaded with 8-byte loads and unpacked to 128 + c pairs (exact) once per
+// loaded with 8-byte loads and unpacked to exact signed bf16 pairs once per
 // group.  The A operand of the same k-step is chunk 8 h + j of its LDS row.
 //
 // Each group runs in two phases of 16 MFMA slots: phase 0 the 8 k-steps of
@@ -127,25 +76,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // still reads the other buffers), read their half-slots, issue the direct
 // loads of group g+1's A and codes into the other buffers and its scale
 // into a register, and run g.
-// Pair P of a 32-code quarter as bf16 with a zero point: b = 4 gives
-// 192 + c - z (zv = (64 - z) in both halves), b = 8 gives c - z (zv = the
-// float z).
-template <int B, int P>
-__device__ __forceinline__ uint32_t quarter_pair_zp(const uint32_t *w, uint32_t mask,
-                                                    uint32_t magic, uint32_t zv) {
-    if constexpr (B == 8) {
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const uint32_t x = w[P >> 1];
-        const float z = __uint_as_float(zv);
-        f32x2 f;
-        f.x = (float)((x >> (16 * (P & 1))) & 0xFFu) - z;
-        f.y = (float)((x >> (16 * (P & 1) + 8)) & 0xFFu) - z;
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-    } else {
-        return quarter_pair<B, P>(w, mask, magic) + zv;
-    }
-}
-
 // GT: NoGroups, or a GroupTable with one entry per m-tile (expert e[i],
 // rows [m0[i], m0[i] + me[i]) of A and Y); the grid's m-tiles run the
 // entries, each rebasing its rows, weights and zero points.
@@ -156,9 +86,8 @@ __device__ __forceinline__ uint32_t quarter_pair_zp(const uint32_t *w, uint32_t 
 // that LDS (56 KB at b = 6) leaves room for two workgroups per compute unit
 // and their loads overlap each other's matrix work.
 template <int B, class WL, bool ZP, class GT, int TM = kPM>
-__global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const uint16_t *__restrict__ A,
-                                                      const uint16_t *__restrict__ Ap, int M,
-                                                      int N, int K, int Kp, WL wl,
+__global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const uint16_t *__restrict__ A, int M,
+                                                      int N, int K, WL wl,
                                                       const uint8_t *__restrict__ zeros,
                                                       uint16_t *__restrict__ Y, int mtiles,
                                                       int ntiles, int splits,
@@ -176,7 +105,6 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     __shared__ u32x4 Cs[2][kSmall ? 1 : 2 * B * 64];
 
     const int G = K / kGroup;
-    const int NP = Kp / kPseudoK;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,15 +133,12 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     }
     const int64_t n0 = (int64_t)bn * kPN;
 
-    const uint32_t mask = __builtin_amdgcn_readfirstlane(pair_mask<B < 8 ? B : 7>());
-    const uint32_t magic = in_vgpr(kBf16Magic128x2);
-
     // Direct loads: wave w fills the 1 KB runs s = w + NW u (u < TM / 4 NW);
     // run s holds rows 4 s .. 4 s + 3, lane l at row 4 s + l / 16, physical
     // chunk l % 16, which is logical chunk (l % 16) ^ (row % 16) (swz16; the
     // row is 4 w + l / 16 modulo 16 for every u).  Rows beyond M read row M-1
     // (their results are dropped).  Byte offsets from the block's column
-    // k0, per run, for A (row stride K) and the pre-pass matrix (Kp).
+    // k0, per run, for A (row stride K).
     const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)TM - 1);
     // A wave whose 128 rows all lie past the tile's last row (a short last
     // tile, or a small expert's tile) computes nothing: it runs its own loop
@@ -225,7 +150,6 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     const int dma_row0 = 4 * wave + (lane >> 4);
     const int dma_chunk = (lane & 15) ^ (dma_row0 & 15);
     const uint16_t *A_blk = A + m0 * K;
-    const uint16_t *Ap_blk = Ap + m0 * Kp;
     constexpr int RU = TM / (4 * NW);  // runs per wave
     uint32_t doff[RU];
 #pragma unroll
@@ -306,13 +230,15 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     const int64_t sstep = wl.scale_step();
     // Zero points [N, G]: the lane's column, one group ahead like the scale.
     const uint8_t *zrow = ZP ? zeros + bcol * G : nullptr;
-    uint32_t zop = 0, znext = 0;
+    int zop = 0, znext = 0;
     auto load_scale = [&](int g, uint32_t &sc) __attribute__((always_inline)) {
         sc = *reinterpret_cast<const uint16_t *>(sptr + min(g, g_hi - 1) * sstep);
-        if constexpr (ZP) {
-            const uint32_t z = zrow[min(g, g_hi - 1)];
-            znext = B == 8 ? __float_as_uint((float)z) : (64u - z) * 0x00010001u;
-        }
+        if constexpr (ZP) znext = zrow[min(g, g_hi - 1)];
+    };
+    // The lane's half-slot of codes as read, sign-flipped in place for the
+    // symmetric form (its 2B words are whole 32-code quarters).
+    auto flip = [&](uint32_t(&c)[2 * B]) __attribute__((always_inline)) {
+        if constexpr (!ZP) flip_signs<B, 2 * B>(c);
     };
     // A operand of k-step j: LDS row 128 wm + 64 PH + 32 t + c32 (the last
     // three terms compile-time), chunk (8 h + j) ^ (c32 % 16).
@@ -336,10 +262,7 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     // B operand of k-step J: pairs 4 (J % 4) .. +3 of quarter J / 4 of the half.
     auto unpack_pair = [&](auto jconst, auto iconst) __attribute__((always_inline)) {
         constexpr int J = decltype(jconst)::value, I = decltype(iconst)::value;
-        if constexpr (ZP)
-            bop[J][I] = quarter_pair_zp<B, 4 * (J & 3) + I>(creg + (J >> 2) * B, mask, magic, zop);
-        else
-            bop[J][I] = quarter_pair<B, 4 * (J & 3) + I>(creg + (J >> 2) * B, mask, magic);
+        bop[J][I] = wpair<B, 4 * (J & 3) + I, ZP>(creg + (J >> 2) * B, zop);
     };
     auto read_a = [&](auto bconst, int row0, int j, int set) __attribute__((always_inline)) {
         constexpr int BUF = decltype(bconst)::value;
@@ -422,75 +345,6 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
 
     float sq_prev = 0.0f;
 
-    // ---- pseudo-groups (scale 1), not pipelined: A' from the pre-pass
-    // matrix into As0; B' = s[n, k'/3] (zero beyond 3G) built in As1 (free
-    // until the real groups) by thread (row tid % 128, quarter tid / 128),
-    // in the same swizzled row layout, and read back as the B operand. ----
-    if (sp == 0 && NP > 0 && kSmall) {
-        // 64-row tile: the B' operand is built in registers, each lane
-        // reading its column's scales (As1 holds 64 rows, not 128); phase 0
-        // only, rows 0, 1 folded with scale 1.
-        uint32_t poff[RU];
-#pragma unroll
-        for (int u = 0; u < RU; ++u)
-            poff[u] = (uint32_t)((min(dma_row0 + 4 * NW * u, mlim) * Kp + 8 * dma_chunk) * 2);
-        for (int ps = 0; ps < NP; ++ps) {
-            dma(Ap_blk, ps * kPseudoK, poff, std::integral_constant<int, 0>{});
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int ka = ps * kPseudoK + 64 * h + 8 * j + 2 * e, kb = ka + 1;
-                    const uint32_t sa = *reinterpret_cast<const uint16_t *>(sptr + min(ka / 3, G - 1) * sstep);
-                    const uint32_t sb = *reinterpret_cast<const uint16_t *>(sptr + min(kb / 3, G - 1) * sstep);
-                    bop[j][e] = (ka < 3 * G ? sa : 0u) | ((kb < 3 * G ? sb : 0u) << 16);
-                }
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads have landed
-            __syncthreads();
-            read_a(std::integral_constant<int, 0>{}, 0, 0, 0);
-            phase(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, [&](int) {});
-#pragma unroll
-            for (int q = 0; q < 16; ++q) fold_slice(0, q, 1.0f);
-            __syncthreads();  // every wave is done with As0 before it is refilled
-        }
-    }
-    if (sp == 0 && NP > 0 && !kSmall) {
-        uint32_t poff[RU];
-#pragma unroll
-        for (int u = 0; u < RU; ++u)
-            poff[u] = (uint32_t)((min(dma_row0 + 4 * NW * u, mlim) * Kp + 8 * dma_chunk) * 2);
-        const int brow = tid & (kPN - 1);
-        const int bq = tid >> 7;
-        const uint8_t *sb0 = wl.scale0(min(n0 + brow, (int64_t)N - 1));
-        for (int ps = 0; ps < NP; ++ps) {
-            dma(Ap_blk, ps * kPseudoK, poff, std::integral_constant<int, 0>{});
-            const int k0 = ps * kPseudoK + 32 * bq;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                uint32_t pr[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int ka = k0 + 8 * u + 2 * e, kb = ka + 1;
-                    const uint32_t sa = *reinterpret_cast<const uint16_t *>(sb0 + min(ka / 3, G - 1) * sstep);
-                    const uint32_t sb = *reinterpret_cast<const uint16_t *>(sb0 + min(kb / 3, G - 1) * sstep);
-                    pr[e] = (ka < 3 * G ? sa : 0u) | ((kb < 3 * G ? sb : 0u) << 16);
-                }
-                As1[swz16(brow, 4 * bq + u)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
-            }
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads have landed
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bop[j] = As1[swz16(32 * wn + c32, 8 * h + j)];
-            read_a(std::integral_constant<int, 0>{}, 0, 0, 0);
-            phase(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
-                  [&](int slot) { fold_slice(2, slot, sq_prev); });
-            sq_prev = 1.0f;
-            phase(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
-                  [&](int slot) { fold_slice(0, slot, 1.0f); });
-            __syncthreads();  // every wave is done with As0 and As1 before they are refilled
-        }
-    }
-
     // ---- real groups ----
     // Group g's A in buffer (g - g_lo) & 1.  Prologue: group g_lo's A, codes
     // and scale.
@@ -508,6 +362,7 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
         sreg = snext;
         zop = znext;
         read_codes(bconst, creg);
+        flip(creg);
         dma(A_blk, min(g + 1, g_hi - 1) * kGroup, doff, std::integral_constant<int, BUF ^ 1>{});
         dma_codes(min(g + 1, g_hi - 1), std::integral_constant<int, BUF ^ 1>{});
         load_scale(g + 1, snext);
@@ -576,9 +431,9 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
             asm volatile("s_barrier" ::: "memory");
 #pragma unroll
             for (int i = 0; i < 2 * B; ++i) creg[i] = cr[S][i];
+            flip(creg);
             sreg = sr[S];
-            if constexpr (ZP)
-                zop = B == 8 ? __float_as_uint((float)zr[S]) : (64u - zr[S]) * 0x00010001u;
+            if constexpr (ZP) zop = (int)zr[S];
             issue(gi + 2, std::integral_constant<int, (S + 2) % 3>{});
             unpack_k0();
             read_a(sconst, 0, 0, 0);
@@ -624,6 +479,7 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
             sreg = snext;
             zop = znext;
             read_codes(bconst, creg);
+            flip(creg);
             dma(A_blk, min(gi + 1, g_hi - 1) * kGroup, doff,
                 std::integral_constant<int, BUF ^ 1>{});
             dma_codes(min(gi + 1, g_hi - 1), std::integral_constant<int, BUF ^ 1>{});
@@ -687,20 +543,6 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__rest
         if (e + i < MN) Y[e + i] = f32_to_bf16_rne(acc[i]);
 }
 
-static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
-
-// Pre-pass workgroups per row: one per 2048 k for a few rows (a row's
-// serial walk over K is then the whole pass: M = 32, K = 17408 took 4.5 us),
-// one per row once the rows alone fill the chip.
-static unsigned sum_chunks(int64_t M, int64_t K) {
-    return M >= 1024 ? 1u : (unsigned)((K + kSumChunk - 1) / kSumChunk);
-}
-
-static int pseudo_kp(int64_t K) {
-    const int G = (int)(K / kGroup);
-    return (3 * G + kPseudoK - 1) / kPseudoK * kPseudoK;
-}
-
 // m-tile rows of a plain (not grouped) launch: 64 up to kSmallTileMaxM
 // rows, else 256.  Measured, b = 6, 5120 -> 17408 / 17408 -> 5120: M = 17..64
 // 32-35 / 44-48 us with 64-row tiles vs 57-58 / 53-56 with 256; M = 96, 128
@@ -742,13 +584,11 @@ static int prefill_splits(int64_t M, int64_t N, int64_t K) {
 
 static int64_t prefill_mnp(int64_t M, int64_t N) { return (M * N + 63) / 64 * 64; }
 
-// Workspace: the shared counter region (unused here), then the pre-pass
-// matrix [M, Kp] bf16, then (K split) the fp32 partial outputs, split s at
-// s * mnp floats.
+// Workspace: the shared counter region (unused here), then (K split) the
+// fp32 partial outputs, split s at s * mnp floats; nothing without a split.
 int64_t prefill_ws_bytes(int64_t M, int64_t N, int64_t K, int) {
     const int s = prefill_splits(M, N, K);
-    return kWsScratchOffset + align256(M * pseudo_kp(K) * 2) +
-           (s > 1 ? s * prefill_mnp(M, N) * 4 : 0);
+    return s > 1 ? kWsScratchOffset + s * prefill_mnp(M, N) * 4 : 0;
 }
 
 template <int B, bool ZP>
@@ -756,23 +596,11 @@ static hipError_t prefill_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K,
                              bool tiled, const uint16_t *scales, const uint8_t *zeros,
                              uint16_t *Y, void *ws, hipStream_t stream) {
     const int G = (int)(K / kGroup);
-    // The constant term: (128 + 2^(b-1)) symmetric, 192 with b = 4 zero
-    // points, none (no pre-pass, no pseudo-groups) with b = 8 zero points.
-    const float off = ZP ? (B == 8 ? 0.0f : 192.0f)
-                         : (B == 8 ? 128.0f : (float)(128 + (1 << (B - 1))));
-    const int Kp = off != 0.0f ? pseudo_kp(K) : 0;
-    uint16_t *Ap = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
     const int splits = prefill_splits(M, N, K);
     float *part = splits > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
-                                                         kWsScratchOffset + align256(M * Kp * 2))
+                                                         kWsScratchOffset)
                              : nullptr;
     hipError_t e = hipSuccess;
-    if (Kp > 0) {
-        hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M, sum_chunks(M, K)), dim3(256), 0, stream, A,
-                           (int)K, Kp, off, Ap);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     const int tm = prefill_tile_m(M);
     const int mtiles = (int)((M + tm - 1) / tm);
     const int ntiles = (int)((N + kPN - 1) / kPN);
@@ -781,11 +609,11 @@ static hipError_t prefill_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K,
         typedef decltype(wl) WL;
         if (tm == kPM)
             hipLaunchKernelGGL((prefill_kernel<B, WL, ZP, NoGroups>), grid, dim3(512), 0, stream,
-                               A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y, mtiles, ntiles,
+                               A, (int)M, (int)N, (int)K, wl, zeros, Y, mtiles, ntiles,
                                splits, part, prefill_mnp(M, N), NoGroups{});
         else
             hipLaunchKernelGGL((prefill_kernel<B, WL, ZP, NoGroups, kPrefillSmallTileM>), grid,
-                               dim3(256), 0, stream, A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros,
+                               dim3(256), 0, stream, A, (int)M, (int)N, (int)K, wl, zeros,
                                Y, mtiles, ntiles, splits, part, prefill_mnp(M, N), NoGroups{});
     };
     if (tiled)
@@ -811,38 +639,23 @@ static hipError_t prefill_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, 
     return hipErrorInvalidValue;
 }
 
-// Grouped prefill: the pre-pass over all M rows of A, then one launch over
-// (table entry, n-tile), tiled layout, no K split.
-int64_t prefill_grouped_ws_bytes(int64_t M, int64_t K) {
-    return kWsScratchOffset + align256(M * pseudo_kp(K) * 2);
-}
-
+// Grouped prefill: one launch over (table entry, n-tile), tiled layout, no
+// K split; no workspace.
 template <int B, bool ZP>
 static hipError_t prefill_grouped_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K,
-                                     const void *W, const uint8_t *zeros, uint16_t *Y, void *ws,
-                                     const GroupTable &gt, int tile_m, bool prepass,
-                                     hipStream_t stream) {
+                                     const void *W, const uint8_t *zeros, uint16_t *Y,
+                                     const GroupTable &gt, int tile_m, hipStream_t stream) {
     const int G = (int)(K / kGroup);
-    const float off = ZP ? (B == 8 ? 0.0f : 192.0f)
-                         : (B == 8 ? 128.0f : (float)(128 + (1 << (B - 1))));
-    const int Kp = off != 0.0f ? pseudo_kp(K) : 0;
-    uint16_t *Ap = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
-    if (Kp > 0 && prepass) {
-        hipLaunchKernelGGL(group_sum_split_kernel, dim3((unsigned)M, sum_chunks(M, K)), dim3(256), 0, stream, A,
-                           (int)K, Kp, off, Ap);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     const int ntiles = (int)((N + kPN - 1) / kPN);
     TiledW wl{static_cast<const uint8_t *>(W), G, B};
     if (tile_m == kPrefillSmallTileM)
         hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, GroupTable, kPrefillSmallTileM>),
-                           dim3((unsigned)(gt.n * ntiles)), dim3(256), 0, stream, A, Ap, (int)M,
-                           (int)N, (int)K, Kp, wl, zeros, Y, gt.n, ntiles, 1, (float *)nullptr,
+                           dim3((unsigned)(gt.n * ntiles)), dim3(256), 0, stream, A, (int)M,
+                           (int)N, (int)K, wl, zeros, Y, gt.n, ntiles, 1, (float *)nullptr,
                            (int64_t)0, gt);
     else if (tile_m == kPrefillTileM)
         hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, GroupTable>), dim3((unsigned)(gt.n * ntiles)),
-                           dim3(512), 0, stream, A, Ap, (int)M, (int)N, (int)K, Kp, wl, zeros, Y,
+                           dim3(512), 0, stream, A, (int)M, (int)N, (int)K, wl, zeros, Y,
                            gt.n, ntiles, 1, (float *)nullptr, (int64_t)0, gt);
     else
         return hipErrorInvalidValue;
@@ -851,21 +664,20 @@ static hipError_t prefill_grouped_bz(const uint16_t *A, int64_t M, int64_t N, in
 
 hipError_t launch_prefill_grouped(const uint16_t *A, int64_t M, int64_t N, int64_t K,
                                   const void *W, const uint8_t *zeros, int b, uint16_t *Y,
-                                  void *ws, const GroupTable &gt, int tile_m, bool prepass,
-                                  hipStream_t stream) {
+                                  const GroupTable &gt, int tile_m, hipStream_t stream) {
     if (zeros) {
-        if (b == 4) return prefill_grouped_bz<4, true>(A, M, N, K, W, zeros, Y, ws, gt, tile_m, prepass, stream);
-        if (b == 8) return prefill_grouped_bz<8, true>(A, M, N, K, W, zeros, Y, ws, gt, tile_m, prepass, stream);
+        if (b == 4) return prefill_grouped_bz<4, true>(A, M, N, K, W, zeros, Y, gt, tile_m, stream);
+        if (b == 8) return prefill_grouped_bz<8, true>(A, M, N, K, W, zeros, Y, gt, tile_m, stream);
         return hipErrorInvalidValue;
     }
     switch (b) {
-        case 2: return prefill_grouped_bz<2, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
-        case 3: return prefill_grouped_bz<3, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
-        case 4: return prefill_grouped_bz<4, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
-        case 5: return prefill_grouped_bz<5, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
-        case 6: return prefill_grouped_bz<6, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
-        case 7: return prefill_grouped_bz<7, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
-        case 8: return prefill_grouped_bz<8, false>(A, M, N, K, W, nullptr, Y, ws, gt, tile_m, prepass, stream);
+        case 2: return prefill_grouped_bz<2, false>(A, M, N, K, W, nullptr, Y, gt, tile_m, stream);
+        case 3: return prefill_grouped_bz<3, false>(A, M, N, K, W, nullptr, Y, gt, tile_m, stream);
+        case 4: return prefill_grouped_bz<4, false>(A, M, N, K, W, nullptr, Y, gt, tile_m, stream);
+        case 5: return prefill_grouped_bz<5, false>(A, M, N, K, W, nullptr, Y, gt, tile_m, stream);
+        case 6: return prefill_grouped_bz<6, false>(A, M, N, K, W, nullptr, Y, gt, tile_m, stream);
+        case 7: return prefill_grouped_bz<7, false>(A, M, N, K, W, nullptr, Y, gt, tile_m, stream);
+        case 8: return prefill_grouped_bz<8, false>(A, M, N, K, W, nullptr, Y, gt, tile_m, stream);
     }
     return hipErrorInvalidValue;
 }
