@@ -252,13 +252,86 @@ def bench_grouped(torch, wq, synth, reps: int):
     return out
 
 
+def hip_ceilings(torch, quick: bool):
+    """Practical ceilings measured with the committed measurement kernels of
+    libwq_ceilings.so (csrc_ceilings/ceilings.hip):
+      stream_read  a plain 128-bit streaming read over the b = 6 decode
+                   layer's algorithmic byte count, rotating 8 buffers (past
+                   the 256 MB Infinity Cache), the best of a sweep over
+                   workgroup counts and loads in flight per lane;
+      mfma_bf16    back-to-back v_mfma_f32_32x32x16_bf16, 2 waves per SIMD;
+      mfma_i8      the same with v_mfma_i32_16x16x64_i8."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_bit_wq_amd", "libwq_ceilings.so"))
+    P, L, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.wqc_stream_read.argtypes = [P, L, I, I, P, P]
+    lib.wqc_mfma_loop.argtypes = [I, I, I, I, P, P]
+    for f in (lib.wqc_stream_read, lib.wqc_mfma_loop):
+        f.restype = I
+
+    def st():
+        return P(torch.cuda.current_stream().cuda_stream)
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError("%s failed: hipError %d" % (what, rc))
+
+    out = {}
+    nbytes = algorithmic_bytes(1, DECODE_N, DECODE_K, 6) // 16 * 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(8)]
+    for bb in bufs:
+        bb.fill_(1)
+    sweep = ((1024, 4), (2048, 4)) if quick else \
+        tuple((w, u) for w in (256, 512, 1024, 2048, 4096, 8192) for u in (1, 2, 4, 8))
+    sink = torch.empty(max(w for w, _ in sweep) * 256, dtype=torch.int32, device="cuda")
+    table, best = [], None
+    for wgs, unroll in sweep:
+        def fn(wgs=wgs, unroll=unroll):
+            for i in range(32):
+                check(lib.wqc_stream_read(P(bufs[i % 8].data_ptr()), nbytes, wgs, unroll,
+                                          P(sink.data_ptr()), st()), "wqc_stream_read")
+        t = graph_time(torch, fn, 3, 1) / 32
+        row = {"workgroups": wgs, "loads_in_flight": unroll, "us": t * 1e6,
+               "TB/s": nbytes / t / 1e12}
+        table.append(row)
+        if best is None or row["TB/s"] > best["TB/s"]:
+            best = row
+    out["stream_read"] = dict(best, bytes=nbytes, frac_of_hbm_peak=best["TB/s"] * 1e3 / HBM_PEAK_GBS)
+    if not quick:
+        out["stream_read"]["sweep"] = table
+    del bufs
+    # MFMA-only loops: 2 or 4 waves per SIMD (512 or 1024 workgroups of 4
+    # waves), 4 or 8 accumulator chains per wave; the best of each
+    # instruction is the ceiling.
+    instrs = ((0, "v_mfma_f32_32x32x16_bf16", 32 * 32 * 16, "bf16"),
+              (1, "v_mfma_f32_16x16x32_bf16", 16 * 16 * 32, "bf16"),
+              (2, "v_mfma_i32_16x16x64_i8", 16 * 16 * 64, "i8"),
+              (3, "v_mfma_i32_32x32x32_i8", 32 * 32 * 32, "i8"))
+    configs = ((512, 4),) if quick else ((512, 4), (512, 8), (1024, 4), (1024, 8))
+    fs = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    for op, name, mnk, kind in instrs:
+        best = None
+        for wgs, chains in configs:
+            iters = 1000
+            t = graph_time(torch, lambda: check(lib.wqc_mfma_loop(op, chains, wgs, iters,
+                                                                  P(fs.data_ptr()), st()),
+                                                "wqc_mfma_loop"), 5, 1)
+            rate = wgs * 4 * iters * chains * 2 * mnk / t / 1e12
+            peak = BF16_PEAK_TFLOPS if kind == "bf16" else INT8_PEAK_TOPS
+            row = {"instr": name, "workgroups": wgs, "chains": chains, "us": t * 1e6,
+                   ("TFLOP/s" if kind == "bf16" else "TOP/s"): rate, "frac_of_peak": rate / peak}
+            if best is None or row["frac_of_peak"] > best["frac_of_peak"]:
+                best = row
+        out["mfma_" + name.split("_", 2)[2]] = best
+    return out
+
+
 def ceilings_run(torch):
-    """Practical ceilings next to the spec peaks, with torch's own kernels,
-    timed eagerly with events: the HBM read rate (torch.sum over a 4 GiB
-    buffer) and copy rate (2 GiB to 2 GiB, read + write bytes), both far
-    past the 256 MB Infinity Cache; and torch's bf16 GEMM (hipBLASLt) at
-    the prefill shapes with the weight stored [N, K] as the library's is
-    (Y = A @ W^T)."""
+    """The committed ceiling kernels with their full streaming-read sweep,
+    plus torch's own kernels for comparison, timed eagerly with events: an
+    HBM read (torch.sum over a 4 GiB buffer) and copy (2 GiB to 2 GiB, read
+    + write bytes), and torch's bf16 GEMM (hipBLASLt) at the prefill shapes
+    with the weight stored [N, K] as the library's is (Y = A @ W^T)."""
     def eager(fn, reps):
         fn()
         torch.cuda.synchronize()
@@ -271,19 +344,20 @@ def ceilings_run(torch):
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / 1e3 / reps
 
-    out = {}
+    out = hip_ceilings(torch, quick=False)
     big = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
     t = eager(lambda: big.sum(), 20)
-    out["hbm_read"] = {"bytes": big.numel() * 4, "us": t * 1e6,
-                       "TB/s": big.numel() * 4 / t / 1e12,
-                       "frac_of_hbm_peak": big.numel() * 4 / t / 1e9 / HBM_PEAK_GBS}
+    out["torch_hbm_read"] = {"bytes": big.numel() * 4, "us": t * 1e6,
+                             "TB/s": big.numel() * 4 / t / 1e12,
+                             "frac_of_hbm_peak": big.numel() * 4 / t / 1e9 / HBM_PEAK_GBS}
     half = big.view(2, -1)
     t = eager(lambda: half[1].copy_(half[0]), 20)
-    out["hbm_copy"] = {"bytes": big.numel() * 4, "us": t * 1e6,
-                       "TB/s": big.numel() * 4 / t / 1e12,
-                       "frac_of_hbm_peak": big.numel() * 4 / t / 1e9 / HBM_PEAK_GBS}
+    out["torch_hbm_copy"] = {"bytes": big.numel() * 4, "us": t * 1e6,
+                             "TB/s": big.numel() * 4 / t / 1e12,
+                             "frac_of_hbm_peak": big.numel() * 4 / t / 1e9 / HBM_PEAK_GBS}
     del big, half
-    for name, (K, N) in (("gemm_bf16_up", (5120, 17408)), ("gemm_bf16_down", (17408, 5120))):
+    for name, (K, N) in (("torch_gemm_bf16_up", (5120, 17408)),
+                         ("torch_gemm_bf16_down", (17408, 5120))):
         A = torch.randn((4096, K), device="cuda").to(torch.bfloat16)
         W = torch.randn((N, K), device="cuda").to(torch.bfloat16)
         t = eager(lambda: torch.matmul(A, W.t()), 20)

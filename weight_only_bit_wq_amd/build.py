@@ -3,6 +3,10 @@
 Each .hip translation unit is compiled to an object in parallel, then linked
 into weight_only_bit_wq_amd/libwq.so.  Flags: -O3, C++17, gfx950 only,
 packed-fp32 instructions disabled (-packed-fp32-ops), no fast-math.
+
+The measurement kernels of csrc_ceilings/ (streaming read, MFMA-only loops;
+not part of the library) go into libwq_ceilings.so, which only bench.py
+loads.
 """
 from __future__ import annotations
 
@@ -17,6 +21,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwq.so")
+CEIL_SRC = os.path.join(HERE, "csrc_ceilings")
+CEIL_LIB = os.path.join(HERE, "libwq_ceilings.so")
 ARCH = "gfx950"
 # -amdgpu-atomic-optimizer-strategy=None: the kernels' atomics are single-lane
 # tickets and counters; the optimizer would rewrite each into a wave-wide
@@ -48,16 +54,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _link(objs: list, lib: str):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-o", tmp] + objs
+    subprocess.check_call(cmd)
+    os.replace(tmp, lib)
+
+
 def build(jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    ceil_srcs = sorted(glob.glob(os.path.join(CEIL_SRC, "*.hip")))
     jobs = jobs or min(16, os.cpu_count() or 4)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-o", tmp] + objs
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+        objs = list(ex.map(_compile, srcs + ceil_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], CEIL_LIB)
     return LIB
 
 
