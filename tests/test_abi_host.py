@@ -142,15 +142,18 @@ def test_zero_point_and_per_channel_statuses():
     assert _gemm(group=512, K=512, layout=wq.WQ_LAYOUT_DENSE, S=ALIGNED) == wq.WQ_ERR_BAD_GROUP
     assert _gemm(group=512, K=512, M=0, A=0, W=0, Y=0) == wq.WQ_OK           # tiled: accepted
     assert _gemm(group=256, K=512) == wq.WQ_ERR_BAD_GROUP                    # neither 128 nor K
-    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, 17408, 5120, 6, 5120) > 0
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 4, 17408, 5120, 6, 5120) > 0
     assert "b = 4 or 8" in wq.wq_status_str(wq.WQ_ERR_ZERO_POINTS)
 
 
 def test_gemm_workspace_checks():
-    need = wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, 17408, 5120, 6)
+    # One row of A on a large layer runs without a K split (no workspace);
+    # 2..16 rows split K across workgroups and need one.
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, 17408, 5120, 6) == 0
+    need = wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 4, 17408, 5120, 6)
     assert need > 0
-    assert _gemm(M=1, N=17408, K=5120, ws=None, ws_bytes=0) == wq.WQ_ERR_WORKSPACE
-    assert _gemm(M=1, N=17408, K=5120, ws_bytes=need - 1) == wq.WQ_ERR_WORKSPACE
+    assert _gemm(M=4, N=17408, K=5120, ws=None, ws_bytes=0) == wq.WQ_ERR_WORKSPACE
+    assert _gemm(M=4, N=17408, K=5120, ws_bytes=need - 1) == wq.WQ_ERR_WORKSPACE
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 0, 17408, 5120, 6) == 0
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, 17408, 5120, 9) == -1
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 64, 17408, 5120, 9) == -1

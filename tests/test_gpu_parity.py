@@ -397,3 +397,27 @@ def test_decode_split_k_forced(M, waves, layout, monkeypatch):
     assert_wna16(host_bf16_bits(Y0), y_ref, mag, "forced split-K M=%d waves=%d" % (M, waves))
     assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
     assert not ws[:wq.WORKSPACE_ZERO_BYTES].any()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("share", [1, 2, 4])
+@pytest.mark.parametrize("rows", [4, 8])
+@pytest.mark.parametrize("N,K", [(300, 128), (777, 640), (200, 5120), (130, 17408)])
+@pytest.mark.parametrize("b", BITS)
+def test_decode_row_kernel_forced(b, N, K, rows, share, layout, monkeypatch):
+    # The one-row kernel without a cross-workgroup K split (a wave owns 8 or
+    # 4 rows, 8 or 16 lanes per row take every 8th or 16th group, 1, 2 or 4
+    # waves of a workgroup share a row set's groups; the lanes' sums meet by
+    # DPP, the waves' in LDS), forced onto small ragged layers: 1 to 136
+    # groups, groups per lane not a whole number, waves with no group at
+    # all, rows past N in the last wave; full outputs against the oracle and
+    # a bitwise repeat.
+    monkeypatch.setenv("WQ_DECODE_ROWS", str(rows))
+    monkeypatch.setenv("WQ_DECODE_ROW_WAVES", str(share))
+    w = _workload(1, N, K, b, seed=3000 + 7 * b + N + K)
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, N, K, b) == 0
+    L = Layer(w, layout)
+    y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
+    Y = L.gemm()
+    assert_wna16(Y, y_ref, mag, "row kernel b=%d N=%d K=%d rows=%d" % (b, N, K, rows))
+    np.testing.assert_array_equal(L.gemm(), Y)

@@ -72,6 +72,16 @@ def test_decode_zero_weights(b, M, act):
     _check(w, Layer(w, wq.WQ_LAYOUT_TILED).gemm(), "decode b=%d M=%d %s" % (b, M, act))
 
 
+@pytest.mark.parametrize("rows", [4, 8])
+@pytest.mark.parametrize("b", [2, 6, 7, 8])
+def test_decode_row_kernel_zero_weights(b, rows, monkeypatch):
+    # The one-row kernel without a K split (the default for large layers),
+    # forced onto the edge-case layer.
+    monkeypatch.setenv("WQ_DECODE_ROWS", str(rows))
+    w = _edge_workload(1, 256, 17408, b, seed=2050 + 10 * b + rows, act="half50")
+    _check(w, Layer(w, wq.WQ_LAYOUT_TILED).gemm(), "row kernel b=%d rows=%d" % (b, rows))
+
+
 @pytest.mark.parametrize("M,N,K", [(40, 256, 5120), (100, 256, 5120), (300, 256, 5120),
                                    (600, 2048, 1024)])
 @pytest.mark.parametrize("b", [2, 6, 8])
@@ -130,10 +140,12 @@ def test_grouped_decode_split_after_many_prefill_tiles():
         assert_wna16(Y[r0:r1], y_ref, mag, "grouped expert %d" % e)
 
 
-def test_non_default_stream_split_k():
+def test_non_default_stream_split_k(monkeypatch):
     # The binding allocates the output and the zeroed workspace on the
-    # stream the call runs on; a one-row decode with its K split runs on a
-    # fresh stream, twice, against the oracle and bit for bit.
+    # stream the call runs on; a one-row decode with its K split (the
+    # split-K kernel forced) runs on a fresh stream, twice, against the
+    # oracle and bit for bit.
+    monkeypatch.setenv("WQ_DECODE_ROWS", "0")
     w = synth.decode(M=1, b=6, N=4096, K=5120)
     L = Layer(w, wq.WQ_LAYOUT_TILED)
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, w.N, w.K, 6) > 0

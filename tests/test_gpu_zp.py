@@ -172,3 +172,18 @@ def test_zero_points_refused_for_other_widths():
         wq.wq_gemm(dev_bf16(A), W_d, wq.WQ_LAYOUT_TILED, None, 64, 6,
                    zeros=torch.zeros((64, 2), dtype=torch.uint8, device="cuda"))
     assert e.value.status == wq.WQ_ERR_ZERO_POINTS
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("rows", [4, 8])
+@pytest.mark.parametrize("b", [4, 8])
+def test_gemm_zero_points_row_kernel(b, rows, layout, monkeypatch):
+    # The one-row kernel without a K split, forced, with zero points.
+    monkeypatch.setenv("WQ_DECODE_ROWS", str(rows))
+    N, K = 333, 1920
+    A, codes, scales, zeros = _zp_workload(1, N, K, b, 2500 + 10 * rows + b)
+    W_d, S_d, packed = _weights(codes, scales, b, layout)
+    Y = wq.wq_gemm(dev_bf16(A), W_d, layout, S_d, N, b, zeros=torch.from_numpy(zeros).cuda())
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.wna16(A, packed, scales, b, zeros=zeros)
+    assert_wna16(host_bf16_bits(Y), y_ref, mag, "zp row kernel b=%d rows=%d" % (b, rows))

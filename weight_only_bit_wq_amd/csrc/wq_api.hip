@@ -172,7 +172,7 @@ void grouped_tables(const int64_t *off, int64_t E, int64_t N, int64_t expert_byt
 wq::DecodePlan grouped_decode_plan(const wq::GroupTable &t, int max_me, int64_t N, int64_t K,
                                    int b) {
     (void)N;
-    return wq::decode_plan(max_me, (int64_t)t.n * t.per * 64, K, b);
+    return wq::decode_plan(max_me, (int64_t)t.n * t.per * 64, K, b, false);
 }
 
 int64_t grouped_ws_bytes(const int64_t *off, int64_t E, int64_t N, int64_t K, int b) {

@@ -8,6 +8,7 @@
 namespace wq {
 
 constexpr int kGroupSize = 128;
+constexpr int kRowWaves = 4;  // waves per workgroup of the row kernel
 
 template <int B, class GT>
 hipError_t decode_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
@@ -35,12 +36,50 @@ static int decode_mt(int64_t M) {
     return 16;
 }
 
-DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b) {
+// The one-row kernel's shape: rows per wave (8, or 4; 0 takes the split-K
+// kernel) and the waves of a workgroup that share those rows' groups (1, 2
+// or 4).  8 rows per wave, and the fewest sharing waves that give at least
+// 3072 waves (three per SIMD: each wave then walks a few slots); 4 rows per
+// wave if 8 leave fewer than 8 groups per lane class; the split-K kernel
+// for small layers (under 1024 waves of 4 rows) and K beyond what the row
+// kernel stages.  WQ_DECODE_ROWS (0, 4 or 8) and WQ_DECODE_ROW_WAVES (1, 2,
+// 4) force a choice.
+static void decode_rows_shape(int64_t M, int64_t N, int64_t K, int &rw, int &s) {
+    rw = 0;
+    s = 1;
+    if (M != 1 || K > kRowKernelMaxK) return;
+    const int G = (int)(K / kGroupSize);
+    rw = (N + 3) / 4 >= 1024 ? (G >= 8 ? 8 : 4) : 0;
+    if (const char *e = std::getenv("WQ_DECODE_ROWS")) {
+        const int f = std::atoi(e);
+        rw = f == 4 || f == 8 ? f : 0;
+    }
+    if (!rw) return;
+    const int C = 64 / rw;
+    const int64_t sets = (N + rw - 1) / rw;
+    while (s < 4 && sets * s < 3072 && G >= C * s * 2) s *= 2;
+    if (const char *e = std::getenv("WQ_DECODE_ROW_WAVES")) {
+        const int f = std::atoi(e);
+        if (f == 1 || f == 2 || f == 4) s = f;
+    }
+}
+
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b, bool rows_ok) {
     (void)b;
     DecodePlan p{};
     const int G = (int)(K / kGroupSize);
     p.mt = decode_mt(M);
     p.rowblocks = (int)((N + 63) / 64);
+    int rs = 1;
+    if (rows_ok) decode_rows_shape(M, N, K, p.rw, rs);
+    if (p.rw) {
+        p.splits = rs;  // waves of a workgroup sharing a row set's groups
+        p.gps = G;
+        p.waves = kRowWaves;
+        p.tstride = 1;
+        p.ws_bytes = 0;
+        return p;
+    }
     // Measured on MI355X (K 5120 -> N 17408 and K 17408 -> N 5120): with
     // many 64-row blocks, 8 waves per workgroup and one group per wave (K
     // split in chunks of 8 groups); with fewer than 192 row blocks, K split

@@ -383,6 +383,198 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// One-row decode without a cross-workgroup K split (the row kernel).
+//
+// A wave owns RW rows of the weights (8, or 4) and a share of K: lane l
+// works on row l % RW, and on groups g = j + C (S t + s), t = 0, 1, ...,
+// with C = 64 / RW lane classes, j = l / RW and s the wave's share
+// among the S waves of its workgroup that hold the same rows.  Each lane
+// loads whole slots (b 16-byte chunks; in the tiled layout the RW rows of
+// one class are 16 * RW consecutive bytes of a plane, whole cache lines),
+// turns the codes into exact bf16 pairs and multiplies them with the
+// group's activations on the matrix cores (4x4x4 blocks, see RowChunks;
+// the vector ALU only converts), which the workgroup stages once in LDS
+// (groups 272 bytes apart, so 16 consecutive groups start on distinct
+// 16-byte bank groups and the C classes' reads do not conflict).  The group
+// scale is applied once per group in fp32.  The C partial sums of a row are
+// added with DPP and the S waves' sums in LDS, in a fixed order, and one
+// lane writes the bf16 output: no cross-workgroup hand-off and no
+// workspace.  The next slot is in flight while one is computed; the many
+// short waves (a few slots each) keep the memory system busy.
+// ---------------------------------------------------------------------------
+constexpr int kRowActStride = 272;  // LDS bytes per group of staged activations
+constexpr int kRowWaves = 4;        // waves per workgroup
+
+// Sum of v over the C lanes of a row (lanes r, r + RW, r + 2 RW, ...;
+// RW = 8 or 4); every such lane receives it.  Fixed order: deterministic.
+template <int RW>
+__device__ __forceinline__ float class_sum(float v) {
+    if constexpr (RW == 4) v = dpp_add<0x124, 0xF>(v);  // row_ror:4
+    v = dpp_add<0x128, 0xF>(v);                         // row_ror:8
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                      false, false);
+    v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                      false, false);
+    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+// Activation chunk I of the group (8 k, staged in LDS at ab) against codes
+// 8I .. 8I+7 of the slot: two k-steps of v_mfma_f32_4x4x4_16b_bf16, one per
+// accumulator chain.  The 4 lanes of an MFMA block are 4 rows of one lane
+// class, so they hold the same activations: block i's A operand has that
+// chunk's 4 k in all four of its rows, its B column j is lane 4i + j's 4
+// exact codes, and every row of its output column j is the lane's dot
+// product.  Chunk I+1 is read ahead; the fence keeps the compiler from
+// hoisting every read and conversion of the slot.
+template <int B, bool ZP, int I>
+struct RowChunks {
+    // One k-step: pairs Q, Q+1 of the slot against activation dwords E, E+1.
+    template <int Q, int E>
+    __device__ __forceinline__ static void step(const uint32_t *w, u32x4 av, int z,
+                                                f32x4_t &d) {
+        u32x2_t wp, a;
+        wp.x = wpair<B, Q % 16, ZP>(w + (Q / 16) * B, z);
+        wp.y = wpair<B, (Q + 1) % 16, ZP>(w + ((Q + 1) / 16) * B, z);
+        a.x = av[E];
+        a.y = av[E + 1];
+        d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4_bits, a),
+                                                   __builtin_bit_cast(bf16x4_bits, wp), d, 0, 0,
+                                                   0);
+    }
+    __device__ __forceinline__ static void run(const uint32_t *w, const uint8_t *ab, int z,
+                                               u32x4 av, f32x4_t *d) {
+        u32x4 nx = av;
+        if constexpr (I + 1 < 16) nx = *reinterpret_cast<const u32x4 *>(ab + 16 * (I + 1));
+        constexpr int P = 4 * I;
+        step<P, 0>(w, av, z, d[0]);
+        step<P + 2, 2>(w, av, z, d[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        RowChunks<B, ZP, I + 1>::run(w, ab, z, nx, d);
+    }
+};
+template <int B, bool ZP>
+struct RowChunks<B, ZP, 16> {
+    __device__ __forceinline__ static void run(const uint32_t *, const uint8_t *, int, u32x4,
+                                               f32x4_t *) {}
+};
+
+template <int B, int RW, int S, class WL, bool ZP>
+__global__ __launch_bounds__(64 * kRowWaves, (B == 7 || (B == 8 && ZP)) ? 4 : 5) void decode_rows_kernel(
+        const uint16_t *__restrict__ A, int N, int K, WL wl, const uint8_t *__restrict__ zeros,
+        uint16_t *__restrict__ Y) {
+    constexpr int C = 64 / RW;
+    constexpr int RO = kRowWaves / S;  // row sets per workgroup
+    extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];
+    __shared__ float red[S > 1 ? RO : 1][S][RW];
+    const int G = K / kGroup;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ro = wave / S, sw = wave % S;
+    // Lane l: row l % RW of the wave's row set, class j = l / RW (so each
+    // 4-lane MFMA block is 4 rows of one class).
+    const int j = lane / RW;
+    const int rr = lane % RW;
+    const int64_t n = ((int64_t)blockIdx.x * RO + ro) * RW + rr;
+    // Dense rows beyond N do not exist: read row N-1 and drop the result.
+    // Tiled blobs hold zero-padded rows (RW divides 64), so nothing to clamp.
+    const int64_t nr = (WL::kTiled || n < N) ? n : (int64_t)N - 1;
+    const uint8_t *zrow = ZP ? zeros + (n < N ? n : (int64_t)N - 1) * G : nullptr;
+    // Slots of this wave's lanes: groups j + C (S t + sw) below G.
+    const int T = (G - C * sw + C * S - 1) / (C * S);
+
+    // Activations straight into LDS: one direct load per group, each lane
+    // 4 bytes, so one instruction writes exactly the group's 256 bytes at
+    // its padded place (no registers held).
+    for (int g = wave; g < G; g += kRowWaves)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(A + (int64_t)g * kGroup + 2 * lane),
+            (__attribute__((address_space(3))) void *)(act_lds + g * kRowActStride), 4, 0, 0);
+
+    auto load = [&](int t, SlotRegs<B, 1> &r) __attribute__((always_inline)) {
+        const int g = min(j + C * (S * t + sw), G - 1);
+        load_slot<B>(wl.chunks(nr, g), wl.chunk_stride(), r.w);
+        r.s = wl.scale(nr, g);
+        if constexpr (ZP) r.z = zrow[g];
+    };
+    float acc = 0.0f;
+    auto compute = [&](int t, SlotRegs<B, 1> &r) __attribute__((always_inline)) {
+        const int g = j + C * (S * t + sw);
+        const int gc = min(g, G - 1);
+        if constexpr (!ZP) flip_signs<B, 4 * B>(r.w);
+        f32x4_t d[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+        const uint8_t *ab = act_lds + gc * kRowActStride;
+        RowChunks<B, ZP, 0>::run(r.w, ab, (int)r.z, *reinterpret_cast<const u32x4 *>(ab), d);
+        const float v = fmaf(bf16_to_f32(r.s), d[0][0] + d[1][0], acc);
+        acc = g < G ? v : acc;
+    };
+
+    SlotRegs<B, 1> cur, nxt;
+    if (T > 0) load(0, cur);
+    // The activations (and the first slot, issued with them) have landed
+    // for this wave; after the barrier, for every wave.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    // Slot t + 1 is loaded before slot t is computed (loads retire in issue
+    // order, so slot t's wait leaves t + 1 in flight).
+    for (int t = 0; t < T; ++t) {
+        if (t + 1 < T) load(t + 1, nxt);
+        compute(t, cur);
+        cur = nxt;
+    }
+    const float y = class_sum<RW>(acc);
+    if constexpr (S == 1) {
+        if (j == 0 && n < N) Y[n] = f32_to_bf16_rne(y);
+    } else {
+        if (j == 0) red[ro][sw][rr] = y;
+        __syncthreads();
+        if (sw == 0 && j == 0 && n < N) {
+            float v = red[ro][0][rr];
+#pragma unroll
+            for (int i = 1; i < S; ++i) v += red[ro][i][rr];
+            Y[n] = f32_to_bf16_rne(v);
+        }
+    }
+}
+
+template <int B, int RW, int S, class WL, bool ZP>
+static void launch_rows_kernel(const uint16_t *A, int64_t N, int64_t K, const WL &wl,
+                               const uint8_t *zeros, uint16_t *Y, hipStream_t stream) {
+    constexpr int RO = kRowWaves / S;
+    const int64_t sets = (N + RW - 1) / RW;
+    const dim3 grid((unsigned)((sets + RO - 1) / RO));
+    const size_t lds = (size_t)(K / kGroup) * kRowActStride;
+    hipLaunchKernelGGL((decode_rows_kernel<B, RW, S, WL, ZP>), grid, dim3(64 * kRowWaves), lds,
+                       stream, A, (int)N, (int)K, wl, zeros, Y);
+}
+
+template <int B, int RW, class WL, bool ZP>
+static void launch_rows_s(const uint16_t *A, int64_t N, int64_t K, const WL &wl,
+                          const uint8_t *zeros, uint16_t *Y, int s, hipStream_t stream) {
+    if (s == 4) launch_rows_kernel<B, RW, 4, WL, ZP>(A, N, K, wl, zeros, Y, stream);
+    else if (s == 2) launch_rows_kernel<B, RW, 2, WL, ZP>(A, N, K, wl, zeros, Y, stream);
+    else launch_rows_kernel<B, RW, 1, WL, ZP>(A, N, K, wl, zeros, Y, stream);
+}
+
+template <int B, class WL>
+static hipError_t launch_rows(const uint16_t *A, int64_t N, int64_t K, const WL &wl,
+                              const uint8_t *zeros, uint16_t *Y, int rw, int s,
+                              hipStream_t stream) {
+    if (zeros) {
+        if constexpr (B == 4 || B == 8) {
+            if (rw == 8) launch_rows_s<B, 8, WL, true>(A, N, K, wl, zeros, Y, s, stream);
+            else launch_rows_s<B, 4, WL, true>(A, N, K, wl, zeros, Y, s, stream);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else {
+        if (rw == 8) launch_rows_s<B, 8, WL, false>(A, N, K, wl, nullptr, Y, s, stream);
+        else launch_rows_s<B, 4, WL, false>(A, N, K, wl, nullptr, Y, s, stream);
+    }
+    return hipGetLastError();
+}
+
 template <int B, int MT, int W, class WL, bool ZP, class GT>
 static void launch_decode_kernel(bool one, const uint16_t *A, int64_t M, int64_t N, int64_t K,
                                  const WL &wl, const uint8_t *zeros, uint16_t *Y, float *part,
@@ -462,6 +654,18 @@ template <int B, class GT>
 hipError_t decode_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
                     bool tiled, const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
                     void *ws, const DecodePlan &p, const GT &gt, hipStream_t stream) {
+    if constexpr (!GT::kGrouped) {
+        if (p.rw) {
+            const int G = (int)(K / kGroup);
+            if (tiled)
+                return launch_rows<B>(A, N, K, TiledW{static_cast<const uint8_t *>(W), G, B},
+                                      zeros, Y, p.rw, p.splits, stream);
+            return launch_rows<B>(A, N, K,
+                                  DenseW{static_cast<const uint8_t *>(W), scales,
+                                         (int64_t)16 * B * G, G, B},
+                                  zeros, Y, p.rw, p.splits, stream);
+        }
+    }
     switch (p.mt) {
         case 1: return decode_bm<B, 1>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, gt, stream);
         case 4: return decode_bm<B, 4>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, gt, stream);

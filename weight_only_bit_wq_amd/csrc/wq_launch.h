@@ -46,14 +46,19 @@ constexpr int kDecodeMaxSplits = 16;  // K splits of the vector-ALU decode kerne
 
 struct DecodePlan {
     int mt;         // rows of A handled per kernel instance (template M tile)
-    int splits;     // K splits across workgroups
+    int splits;     // K splits across workgroups (row kernel: waves sharing a row set)
     int gps;        // groups per split
     int waves;      // waves per workgroup (4, 8 or 16; 16 only for mt <= 4)
     int rowblocks;  // ceil(N / 64)
     int tstride;    // counters from one split-K ticket to the next (spreads them over cache lines)
+    int rw;         // one row of A without a K split: rows per wave of the row kernel (8 or 4); 0 = split-K kernel
     int64_t ws_bytes;
 };
-DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b);
+// The row kernel stages a row of A in LDS, 272 bytes per group of 128:
+// K <= 24576 keeps that within 52 KB.
+constexpr int64_t kRowKernelMaxK = 24576;
+// rows_ok: the one-row kernel may be chosen (not for grouped launches).
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b, bool rows_ok = true);
 
 hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
                          bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
