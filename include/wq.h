@@ -94,7 +94,20 @@ typedef enum wq_layout {
      * j holds, for row r of the block, bytes [16j, 16j + 16) of that row's
      * group-g stream (b*16 bytes, 128 codes) at offset 16r, followed by the
      * 64 bf16 scales s[row, g].  Tiles are ordered block-major, then g.
-     * Scales live inside the blob, so scales_d must be NULL. */
+     * Scales live inside the blob, so scales_d must be NULL.
+     * For b = 2, 3, 4, 8 the group stream is the dense one.  For b = 5, 6, 7
+     * it is rearranged so that it decodes to int8 with masks and shifts:
+     * with v_i = c_i XOR 2^(b-1) (the b-bit two's complement of the signed
+     * weight c_i - 2^(b-1)), the 16b bytes are 4 runs of 4b bytes, run q
+     * holding u_k = v_(32q+k), k < 32.  Byte k < 4b of a run holds u_k in its
+     * top b bits; its low 8 - b bits carry u_(4b) .. u_31 (e = 0..3):
+     *   b = 7: bit 0 of byte 4i + e is bit i of u_(28+e), i = 0..6;
+     *   b = 6: bits 1:0 of bytes 12s + e, 12s + 4 + e, 12s + 8 + e are bits
+     *          5:4, 3:2, 1:0 of u_(24+4s+e), s = 0, 1;
+     *   b = 5: bits 2:0 of byte 4s + e are bits 4:2 and bits 1:0 of byte
+     *          12 + 4s + e are bits 1:0 of u_(20+4s+e), s = 0, 1; bits 2:0
+     *          of byte 8 + e are bits 4:2 of u_(28+e), bit 2 of byte 12 + e
+     *          its bit 1 and bit 2 of byte 16 + e its bit 0. */
     WQ_LAYOUT_TILED = 1
 } wq_layout;
 

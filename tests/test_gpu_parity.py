@@ -59,6 +59,42 @@ def test_unpack_dev_decode_shape(b):
     np.testing.assert_array_equal(codes, w.codes)
 
 
+def _arranged_group_stream(c, b):
+    """The 16b bytes of one row's group stream for b = 5, 6, 7 in the tiled
+    layout, built from the 128 codes c by the rule wq.h states: v = c XOR
+    2^(b-1), 4 runs of 32 values; byte k < 4b of a run holds u_k in its top b
+    bits, the low 8 - b bits hold the bits of u_(4b) .. u_31 as listed."""
+    out = np.zeros(16 * b, dtype=np.uint8)
+    v = [int(x) ^ (1 << (b - 1)) for x in c]
+    for q in range(4):
+        u = v[32 * q:32 * q + 32]
+        run = [(u[k] << (8 - b)) & 0xFF for k in range(4 * b)]
+
+        def put(byte, bit, val):
+            run[byte] |= val << bit
+        for e in range(4):
+            if b == 7:
+                for i in range(7):
+                    put(4 * i + e, 0, (u[28 + e] >> i) & 1)
+            elif b == 6:
+                for s in range(2):
+                    x = u[24 + 4 * s + e]
+                    put(12 * s + e, 0, (x >> 4) & 3)
+                    put(12 * s + 4 + e, 0, (x >> 2) & 3)
+                    put(12 * s + 8 + e, 0, x & 3)
+            else:
+                for s in range(2):
+                    x = u[20 + 4 * s + e]
+                    put(4 * s + e, 0, (x >> 2) & 7)
+                    put(12 + 4 * s + e, 0, x & 3)
+                x = u[28 + e]
+                put(8 + e, 0, (x >> 2) & 7)
+                put(12 + e, 2, (x >> 1) & 1)
+                put(16 + e, 2, x & 1)
+        out[4 * b * q:4 * b * (q + 1)] = run
+    return out
+
+
 @pytest.mark.parametrize("b", BITS)
 def test_repack_matches_documented_tile_layout(b):
     w = _workload(1, 130, 256, b, seed=300 + b)
@@ -70,10 +106,14 @@ def test_repack_matches_documented_tile_layout(b):
     dense = L.packed.view(np.uint8).reshape(w.N, -1)
     for n in (0, 63, 64, 129):
         for g in range(G):
+            if b in (5, 6, 7):
+                stream = _arranged_group_stream(w.codes[n, 128 * g:128 * (g + 1)], b)
+            else:
+                stream = dense[n, g * 16 * b:(g + 1) * 16 * b]
             tile = blob[((n // 64) * G + g) * tb:((n // 64) * G + g + 1) * tb]
             for j in range(b):
                 got = tile[j * 1024 + (n % 64) * 16:j * 1024 + (n % 64) * 16 + 16]
-                np.testing.assert_array_equal(got, dense[n, g * 16 * b + 16 * j:g * 16 * b + 16 * j + 16])
+                np.testing.assert_array_equal(got, stream[16 * j:16 * j + 16])
             s = tile[b * 1024:].view(np.uint16)
             assert s[n % 64] == w.scales[n, g]
     # padded rows 130..191 are zero

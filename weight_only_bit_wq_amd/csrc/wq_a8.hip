@@ -26,8 +26,11 @@
 // int8 value (c - 2^(b-1)) * 2^(8-b), and the group scale becomes
 // s / 2^(8-b) (exact).  Codes are pulled out in pairs with the unpacker's
 // byte-window selectors, four fields packed into a dword with one v_perm_b32,
-// then shifted and XOR-ed (b = 8: the code bytes XOR 0x80).  The k order is
-// the natural one for b != 4, and the activations are written in it.
+// then shifted and XOR-ed (b = 8: the code bytes XOR 0x80); in the tiled
+// layout the runs of b = 5, 6, 7 are stored arranged (wq_device.h) and
+// decode to those int8 values with a few masks and bit-field inserts.  The
+// k order is the natural one for b != 4, and the activations are written in
+// it.
 // Group sums stay exact: |Aq| <= 127, |w * 2^(8-b)| <= 128, 128 terms.
 //
 // Zero points (b = 4 only: at b = 8, c - z can leave the int8 range): the
@@ -285,6 +288,13 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
             Bsm[buf][a8_swz(brow, 2 * bj + 1)] =
                 u32x4{(x.z << 4) & 0xF0F0F0F0u, x.z & 0xF0F0F0F0u, (x.w << 4) & 0xF0F0F0F0u,
                       x.w & 0xF0F0F0F0u};
+        } else if constexpr (WL::kTiled && int8_ready<B>()) {
+            // The tiled layout's arranged run decodes straight to the int8
+            // values q * 2^(8-b), natural order.
+            uint32_t o[8];
+            run_int8<B>(breg, o);
+            Bsm[buf][a8_swz(brow, 2 * bj)] = u32x4{o[0], o[1], o[2], o[3]};
+            Bsm[buf][a8_swz(brow, 2 * bj + 1)] = u32x4{o[4], o[5], o[6], o[7]};
         } else {
             Bsm[buf][a8_swz(brow, 2 * bj)] = u32x4{widen4<B, 0>(breg), widen4<B, 1>(breg),
                                                    widen4<B, 2>(breg), widen4<B, 3>(breg)};

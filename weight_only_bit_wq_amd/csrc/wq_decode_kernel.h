@@ -58,19 +58,21 @@ struct UVec<16> { typedef unsigned type __attribute__((ext_vector_type(16))); };
 // Pairs P0 + I .. P0 + CP - 1 of the slot against the activation pairs in
 // av (CP pairs of the one row come in with one wide scalar load).  Pair p
 // of the slot is pair p % 16 of its 32-code quarter p / 16.
-template <int B, int CP, int P0, int I, bool ZP>
+template <int B, int CP, int P0, int I, bool ZP, bool I8>
 struct DotChunk {
     typedef typename UVec<CP>::type vec;
-    __device__ __forceinline__ static void run(const uint32_t *w, const vec &av, int z, float &d) {
+    __device__ __forceinline__ static void run(const uint32_t *w, const uint32_t *o,
+                                               const vec &av, int z, float &d) {
         constexpr int P = P0 + I;
-        d = dot2_bf16(av[I], wpair<B, P % 16, ZP>(w + (P / 16) * B, z), d);
-        DotChunk<B, CP, P0, I + 1, ZP>::run(w, av, z, d);
+        d = dot2_bf16(av[I], slot_pair<B, P, ZP, I8>(w, o, z), d);
+        DotChunk<B, CP, P0, I + 1, ZP, I8>::run(w, o, av, z, d);
     }
 };
-template <int B, int CP, int P0, bool ZP>
-struct DotChunk<B, CP, P0, CP, ZP> {
+template <int B, int CP, int P0, bool ZP, bool I8>
+struct DotChunk<B, CP, P0, CP, ZP, I8> {
     typedef typename UVec<CP>::type vec;
-    __device__ __forceinline__ static void run(const uint32_t *, const vec &, int, float &) {}
+    __device__ __forceinline__ static void run(const uint32_t *, const uint32_t *, const vec &,
+                                               int, float &) {}
 };
 
 // Everything a lane reads from memory for one (row, group) slot: its b
@@ -93,13 +95,14 @@ __device__ __forceinline__ void load_slot_regs(const WL &wl, int64_t nr, int g,
 }
 
 // One (row, group) slot of lane's row against group g of the one row of A:
-//     x = sum_k a[k] q_k
+//     x = sum_k a[k] q_k   (times 2^(8-b) for arranged runs, I8)
 // (the caller applies the group scale).  `a` points at the group's first
 // activation pair (read with scalar loads: wave-uniform).  The slot's
-// words are sign-flipped in place.
-template <int B, bool ZP>
+// words are prepared in place (prep_runs).
+template <int B, bool ZP, bool I8>
 __device__ __forceinline__ float group_terms(uint32_t *w, const uint32_t *a, int z) {
-    if constexpr (!ZP) flip_signs<B, 4 * B>(w);
+    uint32_t o[I8 ? 32 : 1];
+    prep_runs<B, ZP, I8, 4>(w, o);
     // All 64 activation pairs of the group come in with four wide scalar
     // loads issued together.
     typedef typename UVec<16>::type vec16;
@@ -107,10 +110,10 @@ __device__ __forceinline__ float group_terms(uint32_t *w, const uint32_t *a, int
 #pragma unroll
     for (int c = 0; c < 4; ++c) av[c] = *reinterpret_cast<const vec16 *>(a + 16 * c);
     float d = 0.0f;
-    DotChunk<B, 16, 0, 0, ZP>::run(w, av[0], z, d);
-    DotChunk<B, 16, 16, 0, ZP>::run(w, av[1], z, d);
-    DotChunk<B, 16, 32, 0, ZP>::run(w, av[2], z, d);
-    DotChunk<B, 16, 48, 0, ZP>::run(w, av[3], z, d);
+    DotChunk<B, 16, 0, 0, ZP, I8>::run(w, o, av[0], z, d);
+    DotChunk<B, 16, 16, 0, ZP, I8>::run(w, o, av[1], z, d);
+    DotChunk<B, 16, 32, 0, ZP, I8>::run(w, o, av[2], z, d);
+    DotChunk<B, 16, 48, 0, ZP, I8>::run(w, o, av[3], z, d);
     return d;
 }
 
@@ -133,16 +136,16 @@ typedef short bf16x4_bits __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-template <int B, int Q, int J, bool ZP>
+template <int B, int Q, int J, bool ZP, bool I8>
 struct MfmaSteps {
-    __device__ __forceinline__ static void run(const uint32_t *w, const u32x4 *av, int z,
-                                               f32x4_t *d) {
+    __device__ __forceinline__ static void run(const uint32_t *w, const uint32_t *o,
+                                               const u32x4 *av, int z, f32x4_t *d) {
         // k-step J: codes 4J .. 4J+3, pairs 2J and 2J+1 of the slot (pair p
         // is pair p % 16 of quarter p / 16).
         constexpr int P0 = 2 * J, P1 = 2 * J + 1;
         u32x2_t wp;
-        wp.x = wpair<B, P0 % 16, ZP>(w + (P0 / 16) * B, z);
-        wp.y = wpair<B, P1 % 16, ZP>(w + (P1 / 16) * B, z);
+        wp.x = slot_pair<B, P0, ZP, I8>(w, o, z);
+        wp.y = slot_pair<B, P1, ZP, I8>(w, o, z);
         const bf16x4_bits bw = __builtin_bit_cast(bf16x4_bits, wp);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -152,12 +155,13 @@ struct MfmaSteps {
             d[q] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4_bits, a), bw,
                                                           d[q], 4, J >> 1, 0);
         }
-        MfmaSteps<B, Q, J + 1, ZP>::run(w, av, z, d);
+        MfmaSteps<B, Q, J + 1, ZP, I8>::run(w, o, av, z, d);
     }
 };
-template <int B, int Q, bool ZP>
-struct MfmaSteps<B, Q, 32, ZP> {
-    __device__ __forceinline__ static void run(const uint32_t *, const u32x4 *, int, f32x4_t *) {}
+template <int B, int Q, bool ZP, bool I8>
+struct MfmaSteps<B, Q, 32, ZP, I8> {
+    __device__ __forceinline__ static void run(const uint32_t *, const uint32_t *, const u32x4 *,
+                                               int, f32x4_t *) {}
 };
 
 // Everything a lane reads for one (row, group) slot on the matrix-core form:
@@ -185,14 +189,15 @@ __device__ __forceinline__ void load_slot_regs_mf(const WL &wl, int64_t nr, int 
 
 // x[m] = sum_k a[m,k] q_k for the lane's row and rows m = 0 .. MT-1 of A,
 // as in group_terms; the caller applies the group scale.
-template <int B, int MT, bool ZP>
+template <int B, int MT, bool ZP, bool I8>
 __device__ __forceinline__ void group_terms_mf(uint32_t *w, const u32x4 *av, int z, float *x) {
     constexpr int Q = MT / 4;
-    if constexpr (!ZP) flip_signs<B, 4 * B>(w);
+    uint32_t o[I8 ? 32 : 1];
+    prep_runs<B, ZP, I8, 4>(w, o);
     f32x4_t d[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) d[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    MfmaSteps<B, Q, 0, ZP>::run(w, av, z, d);
+    MfmaSteps<B, Q, 0, ZP, I8>::run(w, o, av, z, d);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         x[4 * q + 0] = d[q][0];
@@ -221,6 +226,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     static_assert(W * MT <= 128, "LDS reduction table");
     static_assert(MT == 1 || MT % 4 == 0, "row tiles above 1 take the matrix-core form");
     constexpr bool MF = MT >= 4;
+    constexpr bool I8 = WL::kTiled && int8_ready<B>() && !ZP;  // arranged runs
+    constexpr float kSInv = operand_scale_inv<B, I8>();
     __shared__ float red[W][MT][64];
 
     const int G = K / kGroup;
@@ -268,8 +275,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
             SlotRegsMf<B, MT> cur;
             load_slot_regs_mf<B, MT, ZP>(wl, nr, g, A2, arow_off, lane, zrow, cur);
             float x[MT];
-            group_terms_mf<B, MT, ZP>(cur.w, cur.av, (int)cur.z, x);
-            const float sc = bf16_to_f32(cur.s);
+            group_terms_mf<B, MT, ZP, I8>(cur.w, cur.av, (int)cur.z, x);
+            const float sc = bf16_to_f32(cur.s) * kSInv;
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m] = sc * x[m];
         }
@@ -282,8 +289,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
             if (gn < g_end)
                 load_slot_regs_mf<B, MT, ZP>(wl, nr, gn, A2, arow_off, lane, zrow, nxt);
             float x[MT];
-            group_terms_mf<B, MT, ZP>(cur.w, cur.av, (int)cur.z, x);
-            const float sc = bf16_to_f32(cur.s);
+            group_terms_mf<B, MT, ZP, I8>(cur.w, cur.av, (int)cur.z, x);
+            const float sc = bf16_to_f32(cur.s) * kSInv;
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
             cur = nxt;
@@ -293,7 +300,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         if (g < g_end) {
             SlotRegs<B, MT> cur;
             load_slot_regs<B, MT, ZP>(wl, nr, g, zrow, cur);
-            acc[0] = bf16_to_f32(cur.s) * group_terms<B, ZP>(cur.w, A2 + (int64_t)g * 64, (int)cur.z);
+            acc[0] = bf16_to_f32(cur.s) * kSInv *
+                     group_terms<B, ZP, I8>(cur.w, A2 + (int64_t)g * 64, (int)cur.z);
         }
     } else {
         SlotRegs<B, MT> cur, nxt;
@@ -302,8 +310,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         for (; g < g_end; g += W) {
             const int gn = g + W;
             if (gn < g_end) load_slot_regs<B, MT, ZP>(wl, nr, gn, zrow, nxt);
-            const float x = group_terms<B, ZP>(cur.w, A2 + (int64_t)g * 64, (int)cur.z);
-            acc[0] = fmaf(bf16_to_f32(cur.s), x, acc[0]);
+            const float x = group_terms<B, ZP, I8>(cur.w, A2 + (int64_t)g * 64, (int)cur.z);
+            acc[0] = fmaf(bf16_to_f32(cur.s) * kSInv, x, acc[0]);
             cur = nxt;
         }
     }
@@ -428,44 +436,46 @@ __device__ __forceinline__ float class_sum(float v) {
 // exact codes, and every row of its output column j is the lane's dot
 // product.  Chunk I+1 is read ahead; the fence keeps the compiler from
 // hoisting every read and conversion of the slot.
-template <int B, bool ZP, int I>
+template <int B, bool ZP, bool I8, int I>
 struct RowChunks {
     // One k-step: pairs Q, Q+1 of the slot against activation dwords E, E+1.
     template <int Q, int E>
-    __device__ __forceinline__ static void step(const uint32_t *w, u32x4 av, int z,
-                                                f32x4_t &d) {
+    __device__ __forceinline__ static void step(const uint32_t *w, const uint32_t *o, u32x4 av,
+                                                int z, f32x4_t &d) {
         u32x2_t wp, a;
-        wp.x = wpair<B, Q % 16, ZP>(w + (Q / 16) * B, z);
-        wp.y = wpair<B, (Q + 1) % 16, ZP>(w + ((Q + 1) / 16) * B, z);
+        wp.x = slot_pair<B, Q, ZP, I8>(w, o, z);
+        wp.y = slot_pair<B, Q + 1, ZP, I8>(w, o, z);
         a.x = av[E];
         a.y = av[E + 1];
         d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4_bits, a),
                                                    __builtin_bit_cast(bf16x4_bits, wp), d, 0, 0,
                                                    0);
     }
-    __device__ __forceinline__ static void run(const uint32_t *w, const uint8_t *ab, int z,
-                                               u32x4 av, f32x4_t *d) {
+    __device__ __forceinline__ static void run(const uint32_t *w, const uint32_t *o,
+                                               const uint8_t *ab, int z, u32x4 av, f32x4_t *d) {
         u32x4 nx = av;
         if constexpr (I + 1 < 16) nx = *reinterpret_cast<const u32x4 *>(ab + 16 * (I + 1));
         constexpr int P = 4 * I;
-        step<P, 0>(w, av, z, d[0]);
-        step<P + 2, 2>(w, av, z, d[1]);
+        step<P, 0>(w, o, av, z, d[0]);
+        step<P + 2, 2>(w, o, av, z, d[1]);
         __builtin_amdgcn_sched_barrier(0);
-        RowChunks<B, ZP, I + 1>::run(w, ab, z, nx, d);
+        RowChunks<B, ZP, I8, I + 1>::run(w, o, ab, z, nx, d);
     }
 };
-template <int B, bool ZP>
-struct RowChunks<B, ZP, 16> {
-    __device__ __forceinline__ static void run(const uint32_t *, const uint8_t *, int, u32x4,
-                                               f32x4_t *) {}
+template <int B, bool ZP, bool I8>
+struct RowChunks<B, ZP, I8, 16> {
+    __device__ __forceinline__ static void run(const uint32_t *, const uint32_t *,
+                                               const uint8_t *, int, u32x4, f32x4_t *) {}
 };
 
 template <int B, int RW, int S, class WL, bool ZP>
-__global__ __launch_bounds__(64 * kRowWaves, (B == 7 || (B == 8 && ZP)) ? 4 : 5) void decode_rows_kernel(
+__global__ __launch_bounds__(64 * kRowWaves, ((B == 7 && !WL::kTiled) || (B == 8 && ZP)) ? 4 : 5) void decode_rows_kernel(
         const uint16_t *__restrict__ A, int N, int K, WL wl, const uint8_t *__restrict__ zeros,
         uint16_t *__restrict__ Y) {
     constexpr int C = 64 / RW;
     constexpr int RO = kRowWaves / S;  // row sets per workgroup
+    constexpr bool I8 = WL::kTiled && int8_ready<B>() && !ZP;  // arranged runs
+    constexpr float kSInv = operand_scale_inv<B, I8>();
     extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];
     __shared__ float red[S > 1 ? RO : 1][S][RW];
     const int G = K / kGroup;
@@ -502,26 +512,51 @@ __global__ __launch_bounds__(64 * kRowWaves, (B == 7 || (B == 8 && ZP)) ? 4 : 5)
     auto compute = [&](int t, SlotRegs<B, 1> &r) __attribute__((always_inline)) {
         const int g = j + C * (S * t + sw);
         const int gc = min(g, G - 1);
-        if constexpr (!ZP) flip_signs<B, 4 * B>(r.w);
+        uint32_t o[I8 ? 32 : 1];
+        prep_runs<B, ZP, I8, 4>(r.w, o);
         f32x4_t d[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
         const uint8_t *ab = act_lds + gc * kRowActStride;
-        RowChunks<B, ZP, 0>::run(r.w, ab, (int)r.z, *reinterpret_cast<const u32x4 *>(ab), d);
-        const float v = fmaf(bf16_to_f32(r.s), d[0][0] + d[1][0], acc);
+        RowChunks<B, ZP, I8, 0>::run(r.w, o, ab, (int)r.z, *reinterpret_cast<const u32x4 *>(ab),
+                                     d);
+        const float v = fmaf(bf16_to_f32(r.s) * kSInv, d[0][0] + d[1][0], acc);
         acc = g < G ? v : acc;
     };
 
-    SlotRegs<B, 1> cur, nxt;
-    if (T > 0) load(0, cur);
-    // The activations (and the first slot, issued with them) have landed
-    // for this wave; after the barrier, for every wave.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    // Slot t + 1 is loaded before slot t is computed (loads retire in issue
-    // order, so slot t's wait leaves t + 1 in flight).
-    for (int t = 0; t < T; ++t) {
-        if (t + 1 < T) load(t + 1, nxt);
-        compute(t, cur);
-        cur = nxt;
+    if constexpr (I8) {
+        // One slot buffer: slot t is decoded to its int8 words first, which
+        // frees the buffer for slot t + 1's loads before slot t's products.
+        SlotRegs<B, 1> r;
+        if (T > 0) load(0, r);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): activations and first slot
+        __syncthreads();
+        for (int t = 0; t < T; ++t) {
+            const int g = j + C * (S * t + sw);
+            const int gc = min(g, G - 1);
+            uint32_t o[32];
+            prep_runs<B, ZP, true, 4>(r.w, o);
+            const float sc = bf16_to_f32(r.s) * kSInv;
+            if (t + 1 < T) load(t + 1, r);
+            f32x4_t d[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+            const uint8_t *ab = act_lds + gc * kRowActStride;
+            RowChunks<B, ZP, true, 0>::run(nullptr, o, ab, 0, *reinterpret_cast<const u32x4 *>(ab),
+                                           d);
+            const float v = fmaf(sc, d[0][0] + d[1][0], acc);
+            acc = g < G ? v : acc;
+        }
+    } else {
+        SlotRegs<B, 1> cur, nxt;
+        if (T > 0) load(0, cur);
+        // The activations (and the first slot, issued with them) have landed
+        // for this wave; after the barrier, for every wave.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        // Slot t + 1 is loaded before slot t is computed (loads retire in
+        // issue order, so slot t's wait leaves t + 1 in flight).
+        for (int t = 0; t < T; ++t) {
+            if (t + 1 < T) load(t + 1, nxt);
+            compute(t, cur);
+            cur = nxt;
+        }
     }
     const float y = class_sum<RW>(acc);
     if constexpr (S == 1) {

@@ -234,6 +234,137 @@ __device__ __forceinline__ uint32_t wpair(const uint32_t *w, int z) {
     else return qpair<B, P>(w);
 }
 
+// ---------------------------------------------------------------------------
+// The int8-ready arrangement of the tiled layout (b = 5, 6, 7).
+//
+// The repack may store a 32-code run (b words) in any order of its bits, so
+// for these widths it stores the signed values v = c XOR 2^(b-1) (b-bit two's
+// complement of q = c - 2^(b-1)) such that most codes sit in the top b bits
+// of a byte of their own:
+//   - codes 0 .. 4b-1: byte k of the run, bits 7 .. 8-b, is v_k; one AND per
+//     word then leaves the int8 value q * 2^(8-b) in every byte;
+//   - the other 4 (8 - b) codes fill the 8 - b spare low bits of the bytes:
+//       b = 6: codes 24 + 4s + e: v bits 5..4, 3..2, 1..0 in bits 1..0 of
+//              byte e of words 3s, 3s + 1, 3s + 2;
+//       b = 5: codes 20 + 4s + e (s = 0, 1): v bits 4..2 in bits 2..0 of
+//              byte e of word s, v bits 1..0 in bits 1..0 of byte e of word
+//              3 + s; s = 2: v bits 4..2 in bits 2..0 of byte e of word 2,
+//              v bit 1 in bit 2 of byte e of word 3, v bit 0 in bit 2 of
+//              byte e of word 4;
+//       b = 7: codes 28 + e: v bit i in bit 0 of byte e of word i;
+//     a few shifts and bit-field inserts per 4 codes put them at the top of
+//     bytes too.
+// So a run decodes to 8 words of int8 values q * 2^(8-b), code k in byte
+// k % 4 of word k / 4, each converted to fp32 by one v_cvt_f32_i32 with a
+// sign-extended byte select: about 2 VALU ops per code instead of about
+// 2.8 for the dense stream.  The factor 2^(8-b) is exact and is taken out of
+// the group scale (fp32 keeps denormals, so s * 2^-(8-b) is exact too).
+// ---------------------------------------------------------------------------
+template <int B>
+__host__ __device__ constexpr bool int8_ready() { return B >= 5 && B <= 7; }
+
+// (x & m) | (y & ~m): one v_bfi_b32.
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t x, uint32_t y) {
+    return (x & m) | (y & ~m);
+}
+
+// The B words of an arranged run -> 8 words of int8 q * 2^(8-B).
+template <int B>
+__device__ __forceinline__ void run_int8(const uint32_t *d, uint32_t *o) {
+    static_assert(int8_ready<B>(), "arranged runs exist for b = 5, 6, 7");
+    constexpr uint32_t top = ((0xFFu << (8 - B)) & 0xFFu) * 0x01010101u;
+#pragma unroll
+    for (int i = 0; i < B; ++i) o[i] = d[i] & top;
+    if constexpr (B == 6) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            o[6 + s] = bfi(0xC0C0C0C0u, d[3 * s] << 6,
+                           bfi(0x30303030u, d[3 * s + 1] << 4, d[3 * s + 2] << 2)) & top;
+    } else if constexpr (B == 5) {
+        o[5] = bfi(0xE0E0E0E0u, d[0] << 5, d[3] << 3) & top;
+        o[6] = bfi(0xE0E0E0E0u, d[1] << 5, d[4] << 3) & top;
+        o[7] = bfi(0xE0E0E0E0u, d[2] << 5, bfi(0x10101010u, d[3] << 2, d[4] << 1)) & top;
+    } else {
+        uint32_t r = d[6] & 0x01010101u;
+#pragma unroll
+        for (int i = 5; i >= 0; --i) r = bfi(0x01010101u, d[i], r << 1);
+        o[7] = r << 1;
+    }
+}
+
+// Arranges 32 signed b-bit values v[k] (low b bits used) into B words, the
+// inverse of run_int8 (used by the repack).
+template <int B>
+__host__ __device__ inline void arrange_run(const uint32_t *v, uint32_t *d) {
+    static_assert(int8_ready<B>(), "arranged runs exist for b = 5, 6, 7");
+    constexpr uint32_t mask = (1u << B) - 1u;
+    for (int i = 0; i < B; ++i) d[i] = 0;
+    for (int k = 0; k < 4 * B; ++k) d[k >> 2] |= ((v[k] & mask) << (8 - B)) << (8 * (k & 3));
+    for (int e = 0; e < 4; ++e) {
+        auto put = [&](int word, int bit, uint32_t bits) { d[word] |= bits << (8 * e + bit); };
+        if constexpr (B == 6) {
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t x = v[24 + 4 * s + e] & mask;
+                put(3 * s, 0, (x >> 4) & 3u);
+                put(3 * s + 1, 0, (x >> 2) & 3u);
+                put(3 * s + 2, 0, x & 3u);
+            }
+        } else if constexpr (B == 5) {
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t x = v[20 + 4 * s + e] & mask;
+                put(s, 0, (x >> 2) & 7u);
+                put(3 + s, 0, x & 3u);
+            }
+            const uint32_t x = v[28 + e] & mask;
+            put(2, 0, (x >> 2) & 7u);
+            put(3, 2, (x >> 1) & 1u);
+            put(4, 2, x & 1u);
+        } else {
+            const uint32_t x = v[28 + e] & mask;
+            for (int i = 0; i < 7; ++i) put(i, 0, (x >> i) & 1u);
+        }
+    }
+}
+
+// Code K of a decoded run o[] as float: q * 2^(8-B), exact (one
+// v_cvt_f32_i32 with a sign-extended byte select).
+template <int K>
+__device__ __forceinline__ float i8code_f32(const uint32_t *o) {
+    return (float)(int)(int8_t)(uint8_t)(o[K >> 2] >> (8 * (K & 3)));
+}
+template <int P>
+__device__ __forceinline__ uint32_t i8pair(const uint32_t *o) {
+    return pack_bf16x2(i8code_f32<2 * P>(o), i8code_f32<2 * P + 1>(o));
+}
+
+// The factor by which a run's operands exceed q: 2^(8-B) for an arranged
+// run (I8), else 1; the group scale is multiplied by its inverse.
+template <int B, bool I8>
+__host__ __device__ constexpr float operand_scale_inv() {
+    return I8 ? 1.0f / (float)(1 << (8 - B)) : 1.0f;
+}
+
+// Prepares the 4 * NQ words of NQ runs (w) for slot_pair: sign flips for
+// the dense stream (symmetric), nothing for zero points, or the 8 * NQ
+// int8 words of arranged runs into o.
+template <int B, bool ZP, bool I8, int NQ>
+__device__ __forceinline__ void prep_runs(uint32_t *w, uint32_t *o) {
+    if constexpr (I8) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) run_int8<B>(w + q * B, o + q * 8);
+    } else if constexpr (!ZP) {
+        flip_signs<B, NQ * B>(w);
+    }
+}
+
+// Pair P of the prepared runs (pair P % 16 of run P / 16): from the words
+// (w, generic) or from the int8 words (o, arranged).
+template <int B, int P, bool ZP, bool I8>
+__device__ __forceinline__ uint32_t slot_pair(const uint32_t *w, const uint32_t *o, int z) {
+    if constexpr (I8) return i8pair<P % 16>(o + (P / 16) * 8);
+    else return wpair<B, P % 16, ZP>(w + (P / 16) * B, z);
+}
+
 // Load the 4*B words of one slot (B 16-byte chunks, `stride` uint4 apart).
 template <int B>
 __device__ __forceinline__ void load_slot(const uint4 *p, int64_t stride, uint32_t *w) {

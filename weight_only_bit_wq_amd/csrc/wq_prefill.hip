@@ -235,10 +235,15 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
         sc = *reinterpret_cast<const uint16_t *>(sptr + min(g, g_hi - 1) * sstep);
         if constexpr (ZP) znext = zrow[min(g, g_hi - 1)];
     };
-    // The lane's half-slot of codes as read, sign-flipped in place for the
-    // symmetric form (its 2B words are whole 32-code quarters).
+    // The lane's half-slot of codes as read (its 2B words are whole 32-code
+    // runs), prepared for slot_pair: sign-flipped in place (dense stream,
+    // symmetric), as is (zero points), or decoded to int8 words (tiled
+    // layout, arranged runs of b = 5, 6, 7).
+    constexpr bool I8 = WL::kTiled && int8_ready<B>() && !ZP;
+    constexpr float kSInv = operand_scale_inv<B, I8>();
+    uint32_t cint[I8 ? 16 : 1];
     auto flip = [&](uint32_t(&c)[2 * B]) __attribute__((always_inline)) {
-        if constexpr (!ZP) flip_signs<B, 2 * B>(c);
+        prep_runs<B, ZP, I8, 2>(c, cint);
     };
     // A operand of k-step j: LDS row 128 wm + 64 PH + 32 t + c32 (the last
     // three terms compile-time), chunk (8 h + j) ^ (c32 % 16).
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     // B operand of k-step J: pairs 4 (J % 4) .. +3 of quarter J / 4 of the half.
     auto unpack_pair = [&](auto jconst, auto iconst) __attribute__((always_inline)) {
         constexpr int J = decltype(jconst)::value, I = decltype(iconst)::value;
-        bop[J][I] = wpair<B, 4 * (J & 3) + I, ZP>(creg + (J >> 2) * B, zop);
+        bop[J][I] = slot_pair<B, 16 * (J >> 2) + 4 * (J & 3) + I, ZP, I8>(creg, cint, zop);
     };
     auto read_a = [&](auto bconst, int row0, int j, int set) __attribute__((always_inline)) {
         constexpr int BUF = decltype(bconst)::value;
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
         load_scale(g + 1, snext);
         unpack_k0();
         read_a(bconst, 0, 0, 0);
-        const float sg = bf16_to_f32((uint16_t)sreg);
+        const float sg = bf16_to_f32((uint16_t)sreg) * kSInv;
         phase(std::integral_constant<int, 0>{}, bconst, [&](int slot) {
             fold_slice(2, slot, sq_prev);
             unpack_slot(slot);
@@ -437,7 +442,7 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
             issue(gi + 2, std::integral_constant<int, (S + 2) % 3>{});
             unpack_k0();
             read_a(sconst, 0, 0, 0);
-            const float sg = bf16_to_f32((uint16_t)sreg);
+            const float sg = bf16_to_f32((uint16_t)sreg) * kSInv;
             phase(std::integral_constant<int, 0>{}, sconst, [&](int slot) { unpack_slot(slot); });
 #pragma unroll
             for (int q = 0; q < 16; ++q) fold_slice(0, q, sg);
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
             load_scale(gi + 1, snext);
             unpack_k0();
             read_a(bconst, 0, 0, 0);
-            const float sg = bf16_to_f32((uint16_t)sreg);
+            const float sg = bf16_to_f32((uint16_t)sreg) * kSInv;
             phase(std::integral_constant<int, 0>{}, bconst, [&](int slot) { unpack_slot(slot); });
 #pragma unroll
             for (int q = 0; q < 16; ++q) fold_slice(0, q, sg);

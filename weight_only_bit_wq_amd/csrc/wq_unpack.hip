@@ -9,9 +9,12 @@ namespace wq {
 // One thread per (64-row block R, group g, row r in block): copies the b
 // 16-byte chunks of that slot into plane j of the tile (lanes = rows, so each
 // plane store is 1 KB contiguous per wave) and the scale after the planes.
-// Rows >= N are written as zero codes and zero scales.  Scales are read at
-// n * sG + g * sg: (G, 1) for group scales, (1, 0) for one scale per row
-// (per-channel), which every group of the row then carries.
+// For b = 5, 6, 7 each 32-code run of the slot is first rewritten in the
+// int8-ready arrangement (signed values, see wq_device.h); other widths keep
+// the dense stream's bits.  Rows >= N are written as zero words and zero
+// scales.  Scales are read at n * sG + g * sg: (G, 1) for group scales,
+// (1, 0) for one scale per row (per-channel), which every group of the row
+// then carries.
 template <int B>
 __global__ __launch_bounds__(256) void repack_tiled_kernel(const uint32_t *__restrict__ packed,
                                                           const uint16_t *__restrict__ scales,
@@ -32,8 +35,35 @@ __global__ __launch_bounds__(256) void repack_tiled_kernel(const uint32_t *__res
         const uint4 *src = reinterpret_cast<const uint4 *>(
             reinterpret_cast<const uint8_t *>(packed) + n * (int64_t)(16 * B * G) +
             (int64_t)g * 16 * B);
+        if constexpr (int8_ready<B>()) {
+            uint32_t w[4 * B];
 #pragma unroll
-        for (int j = 0; j < B; ++j) dst[j * 64] = src[j];
+            for (int j = 0; j < B; ++j) {
+                const uint4 c = src[j];
+                w[4 * j] = c.x; w[4 * j + 1] = c.y; w[4 * j + 2] = c.z; w[4 * j + 3] = c.w;
+            }
+            constexpr uint32_t mask = (1u << B) - 1u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t v[32], d[B];
+#pragma unroll
+                for (int k = 0; k < 32; ++k) {
+                    const int o = k * B, i = o >> 5, sh = o & 31;
+                    const uint64_t win = (uint64_t)w[q * B + i] |
+                                         ((i + 1 < B) ? (uint64_t)w[q * B + i + 1] << 32 : 0ull);
+                    v[k] = ((uint32_t)(win >> sh) & mask) ^ (1u << (B - 1));
+                }
+                arrange_run<B>(v, d);
+#pragma unroll
+                for (int i = 0; i < B; ++i) w[q * B + i] = d[i];
+            }
+#pragma unroll
+            for (int j = 0; j < B; ++j)
+                dst[j * 64] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < B; ++j) dst[j * 64] = src[j];
+        }
         reinterpret_cast<uint16_t *>(tile + tile_code_bytes(B))[r] = scales[n * sG + g * sg];
     } else {
         const uint4 z = {0u, 0u, 0u, 0u};
@@ -79,7 +109,28 @@ __global__ __launch_bounds__(256) void unpack_kernel(WL wl, int64_t N, int G, bo
     uint32_t w[4 * B];
     load_slot<B>(wl.chunks(n, g), wl.chunk_stride(), w);
     uint32_t out[32];
-    UnpackStep<B, 0>::run(w, out);
+    if constexpr (int8_ready<B>()) {
+        if (tiled) {
+            // Arranged runs: int8 q * 2^(8-b) per byte -> c = q + 2^(b-1).
+            uint32_t o[32];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) run_int8<B>(w + q * B, o + q * 8);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int qv = (int)(int8_t)(uint8_t)(o[i] >> (8 * e)) >> (8 - B);
+                    x |= (uint32_t)(qv + (1 << (B - 1))) << (8 * e);
+                }
+                out[i] = x;
+            }
+        } else {
+            UnpackStep<B, 0>::run(w, out);
+        }
+    } else {
+        UnpackStep<B, 0>::run(w, out);
+    }
     uint4 *dst = reinterpret_cast<uint4 *>(codes + n * (int64_t)G * kGroup + (int64_t)g * kGroup);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
