@@ -641,7 +641,7 @@ def main():
     achieved = l6.bytes / t6 / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                "kernel": "decode_kernel<B=6, MT=1> (vector-ALU decode, tiled layout)",
+                "kernel": "decode_rows_kernel<B=6, RW=8, S=2> (one-row decode, tiled layout)",
                 "us_per_launch": t6 * 1e6,
                 "bytes_per_launch": l6.bytes}
     log("b=6 decode kernel: %.2f us/launch, %.0f GB/s" % (t6 * 1e6, achieved))
