@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define WQ_ABI_VERSION 2
+#define WQ_ABI_VERSION 3
 
 typedef enum wq_status {
     WQ_OK = 0,
@@ -78,8 +78,10 @@ typedef enum wq_status {
     WQ_ERR_BAD_LAYOUT = 7,         /* unknown layout, or scales given/missing wrongly */
     WQ_ERR_UNSUPPORTED_DEVICE = 8, /* current device is not gfx950 */
     WQ_ERR_HIP = 9,                /* a HIP call or kernel launch failed */
-    WQ_ERR_ZERO_POINTS = 10        /* zero points for a width without an asymmetric form
+    WQ_ERR_ZERO_POINTS = 10,       /* zero points for a width without an asymmetric form
                                       (b = 4 or 8; b = 4 on the int8-activation path) */
+    WQ_ERR_SCRATCH_LIMIT = 11      /* wq_gemm_noalloc: the problem's scratch exceeds
+                                      WQ_NOALLOC_SCRATCH_BYTES */
 } wq_status;
 
 /* Weight layouts accepted by the device entry points. */
@@ -202,6 +204,23 @@ int64_t wq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int b, int g
 int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d, int layout,
             const uint16_t *scales_d, const uint8_t *zeros_d, int b, int group, uint16_t *Y_d,
             void *ws_d, int64_t ws_bytes, void *stream);
+
+/* Device.  wq_gemm without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments,
+ * results and rounding are those of wq_gemm (the same kernels and plans);
+ * the split-K scratch is a static array of WQ_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends.  A problem
+ * whose wq_workspace_bytes(WQ_OP_GEMM, ...) exceeds that size is refused
+ * with WQ_ERR_SCRATCH_LIMIT before anything is launched.  All calls on one
+ * GPU share its array: calls that may overlap in time on one GPU (different
+ * streams, or host threads without ordering) race and must not be issued;
+ * calls ordered on one stream are safe.  The first call on a device that
+ * needs scratch also enqueues a small kernel that clears its counters. */
+#define WQ_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+int wq_gemm_noalloc(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
+                    int layout, const uint16_t *scales_d, const uint8_t *zeros_d, int b,
+                    int group, uint16_t *Y_d, void *stream);
 
 /* Device.  Grouped (mixture-of-experts) WNA16 layer (model card
  * "Qwen3.8-27B-INT6-Mixed-AutoRound", Findings: the dense format has no

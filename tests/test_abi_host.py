@@ -3,6 +3,7 @@ every function include/wq.h declares, the host packer agrees with the oracle
 bit for bit, and every argument error is refused with its status before any
 device work (forced from the host with fake, never dereferenced pointers)."""
 import ctypes
+import re
 import os
 
 import numpy as np
@@ -16,14 +17,14 @@ from weight_only_bit_wq_amd import synth
 def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(wq.lib_path)
     names = wq.declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
-    assert wq.wq_abi_version() == 2
+    assert wq.wq_abi_version() == 3
 
 
 def test_status_strings():
-    for s in range(11):
+    for s in range(12):
         assert wq.wq_status_str(s) != "unknown status"
     assert wq.wq_status_str(99) == "unknown status"
     assert "2..8" in wq.wq_status_str(wq.WQ_ERR_UNSUPPORTED_BITS)
@@ -130,6 +131,29 @@ def test_gemm_refuses_k_beyond_32bit_tile_offsets():
     # these fake pointers).
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 4096, 64, 1 << 22, 6) >= 0
     assert wq.wq_grouped_workspace_bytes([0, 20], 64, 1 << 22, 6) >= 0
+
+
+def test_noalloc_refuses_beyond_static_scratch():
+    # wq_gemm_noalloc refuses, before any device work, a problem whose
+    # split-K scratch exceeds the static per-GPU array (32 MiB, as the header
+    # states); its argument checks are those of wq_gemm.
+    with open(wq.header_path) as f:
+        m = re.search(r"#define WQ_NOALLOC_SCRATCH_BYTES \(\(int64_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == wq.WQ_NOALLOC_SCRATCH_BYTES
+    N, K = 131072, 5120
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 16, N, K, 6) > wq.WQ_NOALLOC_SCRATCH_BYTES
+    lib = wq._load()
+    p = ctypes.c_void_p(ALIGNED)
+
+    def call(A=p, M=16, b=6, layout=wq.WQ_LAYOUT_TILED, S=None):
+        return lib.wq_gemm_noalloc(A, M, N, K, p, layout, S, None, b, 128, p, None)
+    assert call() == wq.WQ_ERR_SCRATCH_LIMIT
+    assert "WQ_NOALLOC_SCRATCH_BYTES" in wq.wq_status_str(wq.WQ_ERR_SCRATCH_LIMIT)
+    assert call(b=9) == wq.WQ_ERR_UNSUPPORTED_BITS
+    assert call(A=ctypes.c_void_p(MISALIGNED)) == wq.WQ_ERR_MISALIGNED
+    assert call(layout=wq.WQ_LAYOUT_DENSE) == wq.WQ_ERR_BAD_LAYOUT
+    assert call(M=-1) == wq.WQ_ERR_INVALID_ARG
+    assert call(M=0) == wq.WQ_OK
 
 
 def test_zero_point_and_per_channel_statuses():

@@ -24,7 +24,8 @@ __all__ = [
     "WQ_OUT_BF16", "WQ_OUT_F32",
     "wq_abi_version", "wq_status_str", "wq_last_hip_error", "wq_device_supported",
     "wq_packed_words_per_row", "wq_pack", "wq_unpack", "wq_repacked_bytes", "wq_repack",
-    "wq_unpack_dev", "wq_workspace_bytes", "wq_gemm", "wq_quant_act_i8", "wq_gemm_a8",
+    "wq_unpack_dev", "wq_workspace_bytes", "wq_gemm", "wq_gemm_noalloc", "wq_quant_act_i8",
+    "wq_gemm_a8",
     "wq_embed", "wq_gemm_grouped", "wq_grouped_workspace_bytes",
 ]
 
@@ -44,6 +45,8 @@ WQ_ERR_BAD_LAYOUT = 7
 WQ_ERR_UNSUPPORTED_DEVICE = 8
 WQ_ERR_HIP = 9
 WQ_ERR_ZERO_POINTS = 10
+WQ_ERR_SCRATCH_LIMIT = 11
+WQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 WQ_LAYOUT_DENSE = 0
 WQ_LAYOUT_TILED = 1
@@ -100,6 +103,7 @@ def _load():
             "wq_unpack_dev": ([P, I, L, L, I, I, P, P], I),
             "wq_workspace_bytes": ([I, L, L, L, I, I], L),
             "wq_gemm": ([P, L, L, L, P, I, P, P, I, I, P, P, L, P], I),
+            "wq_gemm_noalloc": ([P, L, L, L, P, I, P, P, I, I, P, P], I),
             "wq_quant_act_i8": ([P, L, L, P, P, P], I),
             "wq_gemm_a8": ([P, L, L, L, P, I, P, P, I, I, P, I, P, L, P], I),
             "wq_embed": ([P, P, P, L, L, I, I, P, L, P, P], I),
@@ -303,6 +307,29 @@ def wq_gemm(A_d, W_d, layout: int, scales_d, N: int, b: int, group: int = GROUP,
         ws_buf, ws_bytes = ws, ws.numel() * ws.element_size()
     _check("wq_gemm", _load().wq_gemm(_ptr(A_d), M, N, K, _ptr(W_d), layout, _ptr(scales_d),
                                       _ptr(zeros), b, group, _ptr(Y), _ptr(ws_buf), ws_bytes, st))
+    return Y
+
+
+def wq_gemm_noalloc(A_d, W_d, layout: int, scales_d, N: int, b: int, group: int = GROUP,
+                    Y=None, stream=None, zeros=None):
+    """Device: wq_gemm with the library's static per-GPU scratch instead of a
+    workspace.  Y must be given by a caller that cannot allocate (else a new
+    tensor is returned); calls that overlap on one GPU race."""
+    import torch
+    _require_cuda("A_d", A_d, torch.bfloat16)
+    _require_cuda("W_d", W_d)
+    M, K = A_d.shape
+    if scales_d is not None:
+        _require_cuda("scales_d", scales_d, (torch.bfloat16, torch.int16), (N, K // group))
+    _require_zeros(zeros, N, K)
+    ts = _torch_stream(stream)
+    if Y is None:
+        Y = _empty_on(ts, (M, N), torch.bfloat16, A_d.device)
+    else:
+        _require_cuda("Y", Y, torch.bfloat16, (M, N))
+    _check("wq_gemm_noalloc", _load().wq_gemm_noalloc(_ptr(A_d), M, N, K, _ptr(W_d), layout,
+                                                      _ptr(scales_d), _ptr(zeros), b, group,
+                                                      _ptr(Y), _stream(ts)))
     return Y
 
 

@@ -12,6 +12,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -191,6 +192,47 @@ int check_offsets(const int64_t *off, int64_t E, int64_t M) {
     return WQ_OK;
 }
 
+// The no-allocation entry point's scratch: one array per GPU, owned by the
+// library until the process ends.  Its host-side name is not a device
+// address; kernels and copies use the address hipGetSymbolAddress gives on
+// each device (g_scratch[dev]).  The first WQ_WORKSPACE_ZERO_BYTES are the
+// split-K counters, zero at rest: they start zero (static storage), are
+// cleared again by a small kernel before the first call on each device and
+// after any call whose launch failed, and every completed call leaves them
+// zero.
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[WQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+    std::atomic<bool> clean{false};
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *__restrict__ p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The device address of the current device's scratch array (set up once per
+// device, with that device current), or an error.
+hipError_t scratch_for(int dev, void **ptr) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    ScratchSlot &sl = g_scratch[dev];
+    std::call_once(sl.once, [&] {
+        void *p = nullptr;
+        sl.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (sl.err == hipSuccess) sl.ptr = p;
+    });
+    *ptr = sl.ptr;
+    return sl.err;
+}
+
 }  // namespace
 
 extern "C" {
@@ -210,6 +252,7 @@ const char *wq_status_str(int status) {
         case WQ_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950 (MI355X)";
         case WQ_ERR_HIP: return "HIP runtime or kernel launch error (see wq_last_hip_error)";
         case WQ_ERR_ZERO_POINTS: return "zero points need b = 4 or 8 (b = 4 on the int8-activation path, where c - z must fit int8)";
+        case WQ_ERR_SCRATCH_LIMIT: return "the problem needs more scratch than the static per-GPU array of wq_gemm_noalloc holds (WQ_NOALLOC_SCRATCH_BYTES); call wq_gemm with a workspace";
     }
     return "unknown status";
 }
@@ -363,6 +406,52 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
     if (int s = check_device()) return s;
     const hipError_t e = gemm_dispatch(A_d, M, N, K, W_d, layout == WQ_LAYOUT_TILED, scales_d,
                                        zeros_d, b, Y_d, ws_d, (hipStream_t)stream);
+    return e == hipSuccess ? WQ_OK : hip_fail(e);
+}
+
+int wq_gemm_noalloc(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
+                    int layout, const uint16_t *scales_d, const uint8_t *zeros_d, int b,
+                    int group, uint16_t *Y_d, void *stream) {
+    if (!gemm_dims_ok(M, N, K)) return WQ_ERR_INVALID_ARG;
+    if (!valid_bits(b)) return WQ_ERR_UNSUPPORTED_BITS;
+    if (int s = check_group(K, group)) return s;
+    if (layout != WQ_LAYOUT_DENSE && layout != WQ_LAYOUT_TILED) return WQ_ERR_BAD_LAYOUT;
+    if ((layout == WQ_LAYOUT_DENSE) != (scales_d != nullptr)) return WQ_ERR_BAD_LAYOUT;
+    if (layout == WQ_LAYOUT_DENSE && per_channel(K, group)) return WQ_ERR_BAD_GROUP;
+    if (int s = check_zeros(zeros_d, b, false)) return s;
+    if (M == 0) return WQ_OK;
+    if (!A_d || !W_d || !Y_d) return WQ_ERR_INVALID_ARG;
+    if (!aligned16(A_d) || !aligned16(W_d) || !aligned16(Y_d) ||
+        (scales_d && !aligned16(scales_d)))
+        return WQ_ERR_MISALIGNED;
+    const int64_t need = gemm_ws_bytes(M, N, K, b);
+    if (need > WQ_NOALLOC_SCRATCH_BYTES) return WQ_ERR_SCRATCH_LIMIT;
+    if (int s = check_device()) return s;
+    void *ws = nullptr;
+    if (need > 0) {
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = scratch_for(dev, &ws);
+        if (e != hipSuccess) return hip_fail(e);
+        ScratchSlot &sl = g_scratch[dev];
+        if (!sl.clean.load(std::memory_order_acquire)) {
+            constexpr int words = (int)(WQ_WORKSPACE_ZERO_BYTES / 4);
+            hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0,
+                               (hipStream_t)stream, static_cast<uint32_t *>(ws), words);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail(e);
+            sl.clean.store(true, std::memory_order_release);
+        }
+        e = gemm_dispatch(A_d, M, N, K, W_d, layout == WQ_LAYOUT_TILED, scales_d, zeros_d, b,
+                          Y_d, ws, (hipStream_t)stream);
+        if (e != hipSuccess) {
+            sl.clean.store(false, std::memory_order_release);
+            return hip_fail(e);
+        }
+        return WQ_OK;
+    }
+    const hipError_t e = gemm_dispatch(A_d, M, N, K, W_d, layout == WQ_LAYOUT_TILED, scales_d,
+                                       zeros_d, b, Y_d, nullptr, (hipStream_t)stream);
     return e == hipSuccess ? WQ_OK : hip_fail(e);
 }
 
