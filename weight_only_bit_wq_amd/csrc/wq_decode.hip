@@ -39,11 +39,14 @@ static int decode_mt(int64_t M) {
 // The one-row kernel's shape: rows per wave (8, or 4; 0 takes the split-K
 // kernel) and the waves of a workgroup that share those rows' groups (1, 2
 // or 4).  8 rows per wave, and the fewest sharing waves that give at least
-// 3072 waves (three per SIMD: each wave then walks a few slots); 4 rows per
-// wave if 8 leave fewer than 8 groups per lane class; the split-K kernel
-// for small layers (under 1024 waves of 4 rows) and K beyond what the row
-// kernel stages.  WQ_DECODE_ROWS (0, 4 or 8) and WQ_DECODE_ROW_WAVES (1, 2,
-// 4) force a choice.
+// 3072 waves (three per SIMD: each wave then walks a few slots) and at most
+// two slots per lane where 4 waves allow it (measured on MI355X at K 5120 ->
+// N 17408: loading both slots at the start beat a slot-ahead ring by 2-5%);
+// 4 rows per wave if 8 leave fewer than 8 groups per lane class; the
+// split-K kernel for small layers (under 1024 waves of 4 rows) and K beyond
+// what the row kernel stages.  WQ_DECODE_ROWS (0, 4 or 8),
+// WQ_DECODE_ROW_WAVES (1, 2, 4) and WQ_DECODE_ROW_TMAX (0, 2, 3: slots per
+// lane loaded at the start) force a choice.
 static void decode_rows_shape(int64_t M, int64_t N, int64_t K, int &rw, int &s) {
     rw = 0;
     s = 1;
@@ -58,6 +61,9 @@ static void decode_rows_shape(int64_t M, int64_t N, int64_t K, int &rw, int &s) 
     const int C = 64 / rw;
     const int64_t sets = (N + rw - 1) / rw;
     while (s < 4 && sets * s < 3072 && G >= C * s * 2) s *= 2;
+    // More sharing waves while a lane would have over two slots: with at
+    // most two, every slot is loaded at the start.
+    while (s < 4 && G > 2 * C * s) s *= 2;
     if (const char *e = std::getenv("WQ_DECODE_ROW_WAVES")) {
         const int f = std::atoi(e);
         if (f == 1 || f == 2 || f == 4) s = f;
@@ -73,6 +79,8 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b, bool rows_ok) {
     int rs = 1;
     if (rows_ok) decode_rows_shape(M, N, K, p.rw, rs);
     if (p.rw) {
+        p.tmax = 3;
+        if (const char *e = std::getenv("WQ_DECODE_ROW_TMAX")) p.tmax = std::atoi(e);
         p.splits = rs;  // waves of a workgroup sharing a row set's groups
         p.gps = G;
         p.waves = kRowWaves;

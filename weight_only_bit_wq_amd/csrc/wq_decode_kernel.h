@@ -408,8 +408,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
 // scale is applied once per group in fp32.  The C partial sums of a row are
 // added with DPP and the S waves' sums in LDS, in a fixed order, and one
 // lane writes the bf16 output: no cross-workgroup hand-off and no
-// workspace.  The next slot is in flight while one is computed; the many
-// short waves (a few slots each) keep the memory system busy.
+// workspace.  A wave's time is about one memory round trip per slot it
+// waits on, so lanes with few slots (two, or three up to b = 6) load them
+// all at the start and the whole layer is requested at once; otherwise the
+// next slot is in flight while one is computed.
 // ---------------------------------------------------------------------------
 constexpr int kRowActStride = 272;  // LDS bytes per group of staged activations
 constexpr int kRowWaves = 4;        // waves per workgroup
@@ -468,8 +470,11 @@ struct RowChunks<B, ZP, I8, 16> {
                                                const uint8_t *, int, u32x4, f32x4_t *) {}
 };
 
-template <int B, int RW, int S, class WL, bool ZP>
-__global__ __launch_bounds__(64 * kRowWaves, ((B == 7 && !WL::kTiled) || (B == 8 && ZP)) ? 4 : 5) void decode_rows_kernel(
+// TMAX > 0: every lane has at most TMAX slots, all loaded at the start (the
+// whole layer is requested at once and each slot is computed as it lands);
+// 0: any number of slots, the next one loaded while one is computed.
+template <int B, int RW, int S, class WL, bool ZP, int TMAX>
+__global__ __launch_bounds__(64 * kRowWaves, (TMAX > 0 || (B == 7 && !WL::kTiled) || (B == 8 && ZP)) ? 4 : 5) void decode_rows_kernel(
         const uint16_t *__restrict__ A, int N, int K, WL wl, const uint8_t *__restrict__ zeros,
         uint16_t *__restrict__ Y) {
     constexpr int C = 64 / RW;
@@ -522,7 +527,25 @@ __global__ __launch_bounds__(64 * kRowWaves, ((B == 7 && !WL::kTiled) || (B == 8
         acc = g < G ? v : acc;
     };
 
-    if constexpr (I8) {
+    if constexpr (TMAX > 0) {
+        // All slots at once, after the activations (fenced so the counts
+        // hold): each load() is B chunk loads, the scale and the zero point.
+        // Every lane issues TMAX of them (group indices clamped), so waiting
+        // until at most TMAX * L are outstanding leaves only the activations
+        // landed; each slot's own wait then comes in issue order.
+        constexpr int L = B + 1 + (ZP ? 1 : 0);
+        static_assert(TMAX * L <= 63, "vmcnt field");
+        __builtin_amdgcn_sched_barrier(0);
+        SlotRegs<B, 1> r[TMAX];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) load(t, r[t]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(TMAX * L));
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t)
+            if (t < T) compute(t, r[t]);
+    } else if constexpr (I8) {
         // One slot buffer: slot t is decoded to its int8 words first, which
         // frees the buffer for slot t + 1's loads before slot t's products.
         SlotRegs<B, 1> r;
@@ -575,37 +598,55 @@ __global__ __launch_bounds__(64 * kRowWaves, ((B == 7 && !WL::kTiled) || (B == 8
 
 template <int B, int RW, int S, class WL, bool ZP>
 static void launch_rows_kernel(const uint16_t *A, int64_t N, int64_t K, const WL &wl,
-                               const uint8_t *zeros, uint16_t *Y, hipStream_t stream) {
+                               const uint8_t *zeros, uint16_t *Y, int tmax, hipStream_t stream) {
     constexpr int RO = kRowWaves / S;
+    constexpr int C = 64 / RW;
     const int64_t sets = (N + RW - 1) / RW;
     const dim3 grid((unsigned)((sets + RO - 1) / RO));
-    const size_t lds = (size_t)(K / kGroup) * kRowActStride;
-    hipLaunchKernelGGL((decode_rows_kernel<B, RW, S, WL, ZP>), grid, dim3(64 * kRowWaves), lds,
+    const int G = (int)(K / kGroup);
+    const size_t lds = (size_t)G * kRowActStride;
+    const int T = (G + C * S - 1) / (C * S);  // most slots of any lane
+    // Three slots in registers fit up to b = 6 (b = 7, 8 would spill).
+    if (tmax >= 2 && T <= 2) {
+        hipLaunchKernelGGL((decode_rows_kernel<B, RW, S, WL, ZP, 2>), grid, dim3(64 * kRowWaves),
+                           lds, stream, A, (int)N, (int)K, wl, zeros, Y);
+        return;
+    }
+    if constexpr (B <= 6) {
+        if (tmax >= 3 && T <= 3) {
+            hipLaunchKernelGGL((decode_rows_kernel<B, RW, S, WL, ZP, 3>), grid,
+                               dim3(64 * kRowWaves), lds, stream, A, (int)N, (int)K, wl, zeros,
+                               Y);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((decode_rows_kernel<B, RW, S, WL, ZP, 0>), grid, dim3(64 * kRowWaves), lds,
                        stream, A, (int)N, (int)K, wl, zeros, Y);
 }
 
 template <int B, int RW, class WL, bool ZP>
 static void launch_rows_s(const uint16_t *A, int64_t N, int64_t K, const WL &wl,
-                          const uint8_t *zeros, uint16_t *Y, int s, hipStream_t stream) {
-    if (s == 4) launch_rows_kernel<B, RW, 4, WL, ZP>(A, N, K, wl, zeros, Y, stream);
-    else if (s == 2) launch_rows_kernel<B, RW, 2, WL, ZP>(A, N, K, wl, zeros, Y, stream);
-    else launch_rows_kernel<B, RW, 1, WL, ZP>(A, N, K, wl, zeros, Y, stream);
+                          const uint8_t *zeros, uint16_t *Y, int s, int tmax,
+                          hipStream_t stream) {
+    if (s == 4) launch_rows_kernel<B, RW, 4, WL, ZP>(A, N, K, wl, zeros, Y, tmax, stream);
+    else if (s == 2) launch_rows_kernel<B, RW, 2, WL, ZP>(A, N, K, wl, zeros, Y, tmax, stream);
+    else launch_rows_kernel<B, RW, 1, WL, ZP>(A, N, K, wl, zeros, Y, tmax, stream);
 }
 
 template <int B, class WL>
 static hipError_t launch_rows(const uint16_t *A, int64_t N, int64_t K, const WL &wl,
-                              const uint8_t *zeros, uint16_t *Y, int rw, int s,
+                              const uint8_t *zeros, uint16_t *Y, int rw, int s, int tmax,
                               hipStream_t stream) {
     if (zeros) {
         if constexpr (B == 4 || B == 8) {
-            if (rw == 8) launch_rows_s<B, 8, WL, true>(A, N, K, wl, zeros, Y, s, stream);
-            else launch_rows_s<B, 4, WL, true>(A, N, K, wl, zeros, Y, s, stream);
+            if (rw == 8) launch_rows_s<B, 8, WL, true>(A, N, K, wl, zeros, Y, s, tmax, stream);
+            else launch_rows_s<B, 4, WL, true>(A, N, K, wl, zeros, Y, s, tmax, stream);
         } else {
             return hipErrorInvalidValue;
         }
     } else {
-        if (rw == 8) launch_rows_s<B, 8, WL, false>(A, N, K, wl, nullptr, Y, s, stream);
-        else launch_rows_s<B, 4, WL, false>(A, N, K, wl, nullptr, Y, s, stream);
+        if (rw == 8) launch_rows_s<B, 8, WL, false>(A, N, K, wl, nullptr, Y, s, tmax, stream);
+        else launch_rows_s<B, 4, WL, false>(A, N, K, wl, nullptr, Y, s, tmax, stream);
     }
     return hipGetLastError();
 }
@@ -694,11 +735,11 @@ hipError_t decode_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const vo
             const int G = (int)(K / kGroup);
             if (tiled)
                 return launch_rows<B>(A, N, K, TiledW{static_cast<const uint8_t *>(W), G, B},
-                                      zeros, Y, p.rw, p.splits, stream);
+                                      zeros, Y, p.rw, p.splits, p.tmax, stream);
             return launch_rows<B>(A, N, K,
                                   DenseW{static_cast<const uint8_t *>(W), scales,
                                          (int64_t)16 * B * G, G, B},
-                                  zeros, Y, p.rw, p.splits, stream);
+                                  zeros, Y, p.rw, p.splits, p.tmax, stream);
         }
     }
     switch (p.mt) {

@@ -386,6 +386,11 @@ __device__ __forceinline__ void load_slot(const uint4 *p, int64_t stride, uint32
 // (s_waitcnt vmcnt(0), other counters left unconstrained.)
 __device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt immediate that waits until at most n of this wave's vector-memory
+// operations are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at "no wait").
+__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
 // (lgkmcnt), not for its outstanding global loads, so prefetches stay in
 // flight across it.

@@ -52,6 +52,7 @@ struct DecodePlan {
     int rowblocks;  // ceil(N / 64)
     int tstride;    // counters from one split-K ticket to the next (spreads them over cache lines)
     int rw;         // one row of A without a K split: rows per wave of the row kernel (8 or 4); 0 = split-K kernel
+    int tmax;       // row kernel: load every slot at the start when a lane has at most tmax (2 or 3; 0 never)
     int64_t ws_bytes;
 };
 // The row kernel stages a row of A in LDS, 272 bytes per group of 128:
