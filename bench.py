@@ -93,9 +93,24 @@ def graph_time(torch, fn, reps: int, warmup: int) -> float:
     return start.elapsed_time(stop) / 1e3 / reps
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(oracle, synth, target_s: float):
     """The oracle on the same decode step (b = 5, 6, 7 at M = 1), repeated
-    until target_s seconds of CPU time have passed."""
+    until target_s seconds of CPU time have passed; then, once each, a
+    64-row slice of the prefill layer (M = 64 of the M = 4096 up shape, K
+    5120 -> N 17408, b = 6) and of the W4A8 layer (M = 64, K 5120 -> N 17408,
+    b = 4), whose per-row rates stand for the full layers (the oracle's cost is
+    linear in M)."""
     layers = []
     for b in DECODE_BITS:
         w = synth.decode(M=1, b=b, N=DECODE_N, K=DECODE_K)
@@ -109,10 +124,29 @@ def cpu_baseline(oracle, synth, target_s: float):
         if el >= target_s:
             break
     total = sum(algorithmic_bytes(1, w.N, w.K, w.b) for w, _ in layers)
-    return {"value": total * steps / el / 1e12, "unit": "TB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "%d full decode steps (M=1, K=5120, N=17408, b=5/6/7) in %.1f s, fp64"
-                      % (steps, el)}
+    out = {"value": total * steps / el / 1e12, "unit": "TB/s", "cores": oracle.num_threads(),
+           "cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+           "kind": "oracle",
+           "sample": "%d full decode steps (M=1, K=5120, N=17408, b=5/6/7) in %.1f s, fp64"
+                     % (steps, el)}
+    w = synth.prefill(M=64, N=DECODE_N, K=DECODE_K, b=6)
+    p = oracle.pack(w.codes, 6)
+    t0 = time.perf_counter()
+    oracle.wna16(w.A, p, w.scales, 6)
+    el = time.perf_counter() - t0
+    out["prefill_slice"] = {"TFLOP/s": 2.0 * 64 * w.N * w.K / el / 1e12, "s": el,
+                            "sample": "64 rows of the M=4096 prefill layer (K=5120, N=17408, "
+                                      "b=6), fp64; the rate stands for all 4096 rows"}
+    w = synth.w4a8(M=64)
+    p = oracle.pack(w.codes, 4)
+    t0 = time.perf_counter()
+    oracle.w4a8(w.A, p, w.scales)
+    el = time.perf_counter() - t0
+    out["w4a8_slice"] = {"TOP/s": 2.0 * 64 * w.N * w.K / el / 1e12, "s": el,
+                         "sample": "64 rows of the W4A8 layer (K=%d, N=%d, b=4): int8 "
+                                   "activation quantization and integer group sums; the rate "
+                                   "stands for M=2048 and 8192" % (w.K, w.N)}
+    return out
 
 
 def bench_prefill(torch, wq, synth, reps: int):
@@ -668,14 +702,31 @@ def main():
         "roofline": roofline,
     }
     if not args.no_secondary:
+        log("practical ceilings (quick)")
+        ceil = hip_ceilings(torch, quick=True)
+        result["ceilings"] = ceil
+        sr = ceil["stream_read"]["TB/s"] * 1e3
+        roofline["ceiling"] = {"kind": "stream_read", "GB/s": sr}
+        roofline["frac_of_ceiling"] = roofline["achieved"] / sr
+        for v in per_b.values():
+            v["frac_of_ceiling"] = v["TB/s"] * 1e3 / sr
+        torch.cuda.empty_cache()
         log("decode M=4/16")
         result["decode_sweep"] = bench_decode_sweep(torch, wq, synth, 3, args.copies)
         torch.cuda.empty_cache()
+        for v in result["decode_sweep"].values():
+            v["frac_of_ceiling"] = v["TB/s"] * 1e3 / sr
         log("prefill M=4096")
         result["prefill"] = bench_prefill(torch, wq, synth, reps=10)
+        bf = ceil["mfma_f32_32x32x16_bf16"]["TFLOP/s"]
+        for v in result["prefill"].values():
+            v["frac_of_ceiling"] = v["TFLOP/s"] / bf
         torch.cuda.empty_cache()
         log("w4a8 M=2048/8192")
         result["w4a8"] = bench_w4a8(torch, wq, synth, reps=10)
+        i8 = max(ceil["mfma_i32_16x16x64_i8"]["TOP/s"], ceil["mfma_i32_32x32x32_i8"]["TOP/s"])
+        for v in result["w4a8"].values():
+            v["frac_of_ceiling"] = v["TOP/s"] / i8
         torch.cuda.empty_cache()
         log("zero points / per-channel scales, b=4/8")
         result["zero_points"] = bench_zero_points(torch, wq, synth, 10, args.copies)

@@ -368,6 +368,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     unsigned tk = 0;
     if (lane == 0) tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (__builtin_amdgcn_readfirstlane(tk) != (unsigned)(splits - 1)) return;
+    // The partial loads below follow the ticket (a compiler barrier: the
+    // hardware has already returned the ticket, whose value chose this path).
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     // All of an output's partial loads are issued before its adds, without
     // branches (indices past the last split repeat it and are not added): one
     // at a time, or behind a branch the compiler waits on, they would put

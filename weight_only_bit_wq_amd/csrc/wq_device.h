@@ -380,11 +380,13 @@ __device__ __forceinline__ void load_slot(const uint4 *p, int64_t stride, uint32
 
 // Wait until this wave's vector-memory stores have completed.  Split-K
 // partials are device-scope atomic stores (written through to the
-// coherence point); a workgroup barrier does not wait for them, so a wave
-// must wait here before the barrier that precedes the split's ticket, or
-// the last split could read a partial that is still in flight.
-// (s_waitcnt vmcnt(0), other counters left unconstrained.)
-__device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// coherence point); the wave must see them acknowledged before it takes
+// its ticket, or the last split could read a partial still in flight.  On
+// this architecture vmcnt also counts stores, and a store is counted until
+// the coherence point has it.  The "memory" clobber makes the wait a
+// compiler barrier as well: relaxed atomics to different addresses may
+// otherwise be moved across it.
+__device__ __forceinline__ void wait_vm_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // s_waitcnt immediate that waits until at most n of this wave's vector-memory
 // operations are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
