@@ -560,6 +560,25 @@ def pmc_layer_run(torch, wq, synth, M: int):
     log("pmc layer run done: M=%d K=5120 N=17408 b=6 x3" % M)
 
 
+def pmc_a8_run(torch, wq, synth, M: int):
+    """Kernels for rocprofv3 --pmc activity counters: three calls of the W4A8
+    layer (K 5120 -> N 17408, b = 4) at batch M (the first one warms the
+    caches)."""
+    w = synth.w4a8(M=M)
+    packed = wq.wq_pack(w.codes, 4)
+    blob = wq.wq_repack(torch.from_numpy(packed.view(np.int32)).cuda(),
+                        torch.from_numpy(w.scales.view(np.int16)).cuda().view(torch.bfloat16),
+                        w.K, 4)
+    A = torch.from_numpy(w.A.view(np.int16)).cuda().view(torch.bfloat16)
+    Y = torch.empty((M, w.N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, M, w.N, w.K, 4), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(3):
+        wq.wq_gemm_a8(A, blob, wq.WQ_LAYOUT_TILED, None, w.N, 4, Y=Y, ws=ws)
+    torch.cuda.synchronize()
+    log("pmc a8 run done: M=%d K=%d N=%d b=4 x3" % (M, w.K, w.N))
+
+
 def bench_stack(torch, wq, reps: int):
     """The 64-layer mixed-bit stack + 8-bit head: M = 1 (HBM-bound, TB/s of
     algorithmic bytes) and M = 512 (TFLOP/s).  One forward = 129 wq_gemm calls,
@@ -603,6 +622,9 @@ def main():
     ap.add_argument("--pmc-layer", type=int, default=0, metavar="M",
                     help="no timing: three calls of the K=5120, N=17408, b=6 layer at batch M "
                          "(for rocprofv3 --pmc activity counters)")
+    ap.add_argument("--pmc-a8", type=int, default=0, metavar="M",
+                    help="no timing: three calls of the W4A8 layer (K=5120, N=17408, b=4) at "
+                         "batch M (for rocprofv3 --pmc activity counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -627,6 +649,9 @@ def main():
         return
     if args.pmc_layer > 0:
         pmc_layer_run(torch, wq, synth, args.pmc_layer)
+        return
+    if args.pmc_a8 > 0:
+        pmc_a8_run(torch, wq, synth, args.pmc_a8)
         return
 
     log("setting up decode layers (b=5,6,7; %d copies each)" % args.copies)

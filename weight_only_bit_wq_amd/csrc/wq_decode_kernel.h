@@ -418,6 +418,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
 // ---------------------------------------------------------------------------
 constexpr int kRowActStride = 272;  // LDS bytes per group of staged activations
 constexpr int kRowWaves = 4;        // waves per workgroup
+constexpr int kRowActRegs = 16;     // activation dwords a lane stages up front
+constexpr int kRowUpfrontMaxG = kRowWaves * kRowActRegs;  // groups the up-front form takes
 
 // Sum of v over the C lanes of a row (lanes r, r + RW, r + 2 RW, ...;
 // RW = 8 or 4); every such lane receives it.  Fixed order: deterministic.
@@ -494,7 +496,12 @@ __global__ __launch_bounds__(64 * kRowWaves, (TMAX > 0 || (B == 7 && !WL::kTiled
     // 4-lane MFMA block is 4 rows of one class).
     const int j = lane / RW;
     const int rr = lane % RW;
-    const int64_t n = ((int64_t)blockIdx.x * RO + ro) * RW + rr;
+    // Workgroup b runs on XCD b % 8; the row sets of one 64-row block share
+    // its tiles' scale lines, so consecutive row sets go to one XCD (one L2
+    // fetch per line): XCD x takes a contiguous run of the grid.
+    int blk = blockIdx.x;
+    if ((gridDim.x & 7) == 0) blk = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int64_t n = ((int64_t)blk * RO + ro) * RW + rr;
     // Dense rows beyond N do not exist: read row N-1 and drop the result.
     // Tiled blobs hold zero-padded rows (RW divides 64), so nothing to clamp.
     const int64_t nr = (WL::kTiled || n < N) ? n : (int64_t)N - 1;
@@ -502,13 +509,26 @@ __global__ __launch_bounds__(64 * kRowWaves, (TMAX > 0 || (B == 7 && !WL::kTiled
     // Slots of this wave's lanes: groups j + C (S t + sw) below G.
     const int T = (G - C * sw + C * S - 1) / (C * S);
 
-    // Activations straight into LDS: one direct load per group, each lane
-    // 4 bytes, so one instruction writes exactly the group's 256 bytes at
-    // its padded place (no registers held).
-    for (int g = wave; g < G; g += kRowWaves)
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void *)(A + (int64_t)g * kGroup + 2 * lane),
-            (__attribute__((address_space(3))) void *)(act_lds + g * kRowActStride), 4, 0, 0);
+    // Activations into LDS, one group (256 bytes) per wave-wide step, each
+    // lane 4 bytes at the group's padded place.  The rolled form loads
+    // them straight into LDS (no registers held); the all-slots-up-front
+    // form (launched for at most kRowUpfrontMaxG groups, so at most
+    // kRowActRegs per wave) goes through registers, so that the compiler's
+    // waits see which loads the LDS writes depend on and the slot loads
+    // stay in flight past them.
+    constexpr int kActRegs = kRowActRegs;
+    uint32_t areg[TMAX > 0 ? kActRegs : 1];
+    if constexpr (TMAX > 0) {
+        const uint32_t *A32 = reinterpret_cast<const uint32_t *>(A);
+#pragma unroll
+        for (int i = 0; i < kActRegs; ++i)
+            areg[i] = A32[(int64_t)min(wave + kRowWaves * i, G - 1) * (kGroup / 2) + lane];
+    } else {
+        for (int g = wave; g < G; g += kRowWaves)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(A + (int64_t)g * kGroup + 2 * lane),
+                (__attribute__((address_space(3))) void *)(act_lds + g * kRowActStride), 4, 0, 0);
+    }
 
     auto load = [&](int t, SlotRegs<B, 1> &r) __attribute__((always_inline)) {
         const int g = min(j + C * (S * t + sw), G - 1);
@@ -531,20 +551,29 @@ __global__ __launch_bounds__(64 * kRowWaves, (TMAX > 0 || (B == 7 && !WL::kTiled
     };
 
     if constexpr (TMAX > 0) {
-        // All slots at once, after the activations (fenced so the counts
-        // hold): each load() is B chunk loads, the scale and the zero point.
-        // Every lane issues TMAX of them (group indices clamped), so waiting
-        // until at most TMAX * L are outstanding leaves only the activations
-        // landed; each slot's own wait then comes in issue order.
-        constexpr int L = B + 1 + (ZP ? 1 : 0);
-        static_assert(TMAX * L <= 63, "vmcnt field");
-        __builtin_amdgcn_sched_barrier(0);
+        // All slots at once, after the activations' loads: each slot is B
+        // chunk loads, the scale and the zero point, TMAX slots for every
+        // wave.  A slot past the lane's last group (the wave has fewer than
+        // TMAX, or G is not a multiple of the C classes) reads row 0's first
+        // slot instead: one line that all such loads share, so no slot is
+        // fetched twice.
         SlotRegs<B, 1> r[TMAX];
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) load(t, r[t]);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(TMAX * L));
-        __syncthreads();
+        for (int t = 0; t < TMAX; ++t) {
+            const int g = j + C * (S * t + sw);
+            const bool real = g < G;
+            load_slot<B>(real ? wl.chunks(nr, g) : wl.chunks(0, 0), wl.chunk_stride(), r[t].w);
+            r[t].s = real ? wl.scale(nr, g) : wl.scale(0, 0);
+            if constexpr (ZP) r[t].z = real ? zrow[g] : zeros[0];
+        }
+        // The activations' LDS writes wait for their own loads only; the
+        // barrier then orders LDS (the slot loads stay in flight).
+#pragma unroll
+        for (int i = 0; i < kActRegs; ++i) {
+            const int g = wave + kRowWaves * i;
+            if (g < G) *reinterpret_cast<uint32_t *>(act_lds + g * kRowActStride + 4 * lane) = areg[i];
+        }
+        lds_barrier();
 #pragma unroll
         for (int t = 0; t < TMAX; ++t)
             if (t < T) compute(t, r[t]);
@@ -609,7 +638,9 @@ static void launch_rows_kernel(const uint16_t *A, int64_t N, int64_t K, const WL
     const int G = (int)(K / kGroup);
     const size_t lds = (size_t)G * kRowActStride;
     const int T = (G + C * S - 1) / (C * S);  // most slots of any lane
-    // Three slots in registers fit up to b = 6 (b = 7, 8 would spill).
+    // Three slots in registers fit up to b = 6 (b = 7, 8 would spill); the
+    // up-front form stages at most kRowUpfrontMaxG groups of activations.
+    if (G > kRowUpfrontMaxG) tmax = 0;
     if (tmax >= 2 && T <= 2) {
         hipLaunchKernelGGL((decode_rows_kernel<B, RW, S, WL, ZP, 2>), grid, dim3(64 * kRowWaves),
                            lds, stream, A, (int)N, (int)K, wl, zeros, Y);
