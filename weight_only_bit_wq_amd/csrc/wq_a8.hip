@@ -9,7 +9,7 @@
 // W8A8.)  Here:
 //   1. quant_act_kernel: s_a[m] = max|a| / 127 (fp32, IEEE division),
 //      Aq = clamp(rint(a / s_a), -127, 127), zero row -> 0.
-//   2. gemm_a8_kernel: int8 MFMA (v_mfma_i32_16x16x64_i8) with exact int32
+//   2. gemm_a8_kernel: int8 MFMA (v_mfma_i32_32x32x32_i8) with exact int32
 //      sums per group of 128, folded in fp32 with the group scale, times s_a.
 //
 // Lossless widening with one AND per four codes: XOR-ing a nibble c with 8
@@ -38,6 +38,8 @@
 // same k order), and ((c | 0x80) - z) ^ 0x80 per byte is the int8 c - z
 // (128 + c - z lies in 113..143, so no byte borrows from its neighbour); the
 // group scale is s itself.
+#include <type_traits>
+
 #include "wq_device.h"
 #include "wq_launch.h"
 
@@ -180,14 +182,26 @@ int64_t a8_ws_bytes(int64_t M, int64_t, int64_t K) {
 __device__ __forceinline__ int a8_swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
 // Workgroup: 512 threads = 8 waves (two per SIMD) over a 256 (m) x 128 (n)
-// tile; wave (wm, wn) owns 64 x 64 = 4 x 4 blocks of v_mfma_i32_16x16x64_i8.
-// Per group of 128 k: 2 k-steps x 16 MFMAs into exact int32 sums P, then
-// tot += (s/16) * float(P) (fp32).  A (int8, GEMM k-order) and the widened
-// B of a group sit in LDS (double-buffered, 32 + 16 KB per buffer); the next
-// group's A and codes are fetched into registers during the current one.
-// The fold runs one row block behind the group's last MFMAs (row 3 during
-// the next group's first k-step), one block per MFMA, so it issues in the
-// matrix core's shadow.
+// tile; wave (wm, wn) owns 64 x 64 = 2 x 2 blocks of v_mfma_i32_32x32x32_i8
+// (lane l: row / column l % 32 of a block's operands, k-half l / 32 of the
+// k-step; result column l % 32, rows 8 (r / 4) + 4 (l / 32) + r % 4 in
+// register r).  Per group of 128 k: 4 k-steps x 4 MFMAs into exact int32
+// sums P, then tot += (s/16) * float(P) (fp32): 64 conversions and FMAs per
+// lane, as much vector-ALU time as the MFMAs take on the matrix cores.  The
+// two waves of a SIMD (wm and wm + 2) take the group in opposite orders: the
+// early one runs its MFMAs and then folds them, the late one folds the
+// previous group's sums and then runs its MFMAs, so each wave's fold issues
+// while its partner's MFMAs run.
+// Data: A (int8, GEMM k-order) goes global -> LDS by direct loads, the codes
+// through registers (widened to int8 on their way into LDS), both double-
+// buffered in separate LDS objects (so the compiler sees that the reads of
+// one buffer do not wait for loads into the other).  At the start of group
+// g a wave stores group g + 1's widened codes (fetched during g - 1), then
+// issues group g + 2's code fetch and group g + 1's A loads: everything has
+// a whole group to land before the wait and barrier that open group g + 1.
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 template <class WL, int B, bool ZP>
 __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__ Aq,
                                                       const float *__restrict__ sa, int M, int N,
@@ -195,8 +209,10 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
                                                       const uint8_t *__restrict__ zeros,
                                                       void *__restrict__ Y,
                                                       bool out_f32, int mtiles, int ntiles) {
-    __shared__ u32x4 Asm[2][kABM * 8];  // 2 x 32 KB
-    __shared__ u32x4 Bsm[2][kABN * 8];  // 2 x 16 KB
+    __shared__ u32x4 As0[kABM * 8];  // 32 KB each
+    __shared__ u32x4 As1[kABM * 8];
+    __shared__ u32x4 Bs0[kABN * 8];  // 16 KB each
+    __shared__ u32x4 Bs1[kABN * 8];
     __shared__ float Ss[2][kABN];
 
     const int G = K / kGroup;
@@ -215,15 +231,28 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
     const int64_t m0 = (int64_t)bm * kABM;
     const int64_t n0 = (int64_t)bn * kABN;
 
-    // A loader: rows ar + 64 i (i < 4), chunk ac; rows beyond M read row M-1.
-    const int ac = tid & 7;
-    const int ar = tid >> 3;
+    // A direct loads: instruction u of wave w fills LDS slots 64 (w + 8u) ..
+    // +63, rows 8 (w + 8u) .. +7; lane l writes slot l of them: row
+    // 8 (w + 8u) + l / 8, physical chunk l % 8, which holds logical chunk
+    // (l % 8) ^ (row % 8) (a8_swz).  Rows beyond M read row M-1.
     const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)kABM - 1);
-    int arows[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) arows[i] = min(ar + 64 * i, mlim);
     const int8_t *A_blk = Aq + m0 * K;
-    const int a_lds = a8_swz(ar, ac);  // + 512 i
+    uint32_t aoff[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int row = 8 * (wave + 8 * u) + (lane >> 3);
+        const int chunk = (lane & 7) ^ (row & 7);
+        aoff[u] = (uint32_t)(min(row, mlim) * K + 16 * chunk);
+    }
+    auto dma_a = [&](int g, u32x4 *dst) __attribute__((always_inline)) {
+        g = min(g, G - 1);
+        const int8_t *src = A_blk + (int64_t)g * kGroup;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + aoff[u]),
+                (__attribute__((address_space(3))) void *)&dst[64 * (wave + 8 * u)], 16, 0, 0);
+    };
 
     // B loader: row brow, quarter bj (wave-uniform) = codes 32 bj .. +32 of
     // the group (b = 4: 16-byte chunk bj); widened to int8 it fills LDS
@@ -237,38 +266,34 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
     const int sstep = (int)wl.scale_step();
     const uint8_t *zrow = ZP ? zeros + bn_read * G : nullptr;  // zero points [N, G]
 
-    // MFMA operand rows and k-chunk of this lane.
-    const int arow = wm * 64 + (lane & 15);
-    const int bmrow = wn * 64 + (lane & 15);
-    const int q = lane >> 4;
+    // MFMA operand rows and k-half of this lane.
+    const int r32 = lane & 31, hh = lane >> 5;
+    const int arow = wm * 64 + r32;
+    const int bmrow = wn * 64 + r32;
 
-    u32x4 areg[4];
     uint32_t breg[B];
     uint16_t sreg;
     uint32_t zreg = 0;
-    i32x4_t P[4][4];
-    f32x4_t tot[4][4];
+    i32x16_t P[2][2];  // [block row][block column]
+    f32x16_t tot[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            tot[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            P[i][j] = i32x4_t{0, 0, 0, 0};
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                tot[i][j][r] = 0.0f;
+                P[i][j][r] = 0;
+            }
+    const bool late = wm >= 2;  // the second wave of its SIMD
 
-    auto fetch = [&](int g) __attribute__((always_inline)) {  // clamped to the last group
+    auto fetch_b = [&](int g) __attribute__((always_inline)) {  // clamped to the last group
         g = min(g, G - 1);
-        const int8_t *src = A_blk + (int64_t)g * kGroup + 16 * ac;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            areg[i] = *reinterpret_cast<const u32x4 *>(src + (int64_t)arows[i] * K);
         load_quarter<WL, B>(bslot0 + (int64_t)g * bstep, bj, breg);
         sreg = *reinterpret_cast<const uint16_t *>(bscale0 + (int64_t)g * sstep);
         if constexpr (ZP) zreg = zrow[g];
     };
-    auto store = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Asm[buf][a_lds + 512 * i] = areg[i];
+    auto store_b = [&](u32x4 *Bsm, float *Sr) __attribute__((always_inline)) {
         if constexpr (ZP) {  // b = 4: int8 c - z, codes ordered as below
             const u32x4 x = u32x4{breg[0], breg[1], breg[2], breg[3]};
             const uint32_t zb = zreg * 0x01010101u;
@@ -278,14 +303,14 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
             auto hi = [&](uint32_t v) {
                 return ((((v >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zb) ^ 0x80808080u;
             };
-            Bsm[buf][a8_swz(brow, 2 * bj)] = u32x4{lo(x.x), hi(x.x), lo(x.y), hi(x.y)};
-            Bsm[buf][a8_swz(brow, 2 * bj + 1)] = u32x4{lo(x.z), hi(x.z), lo(x.w), hi(x.w)};
+            Bsm[a8_swz(brow, 2 * bj)] = u32x4{lo(x.x), hi(x.x), lo(x.y), hi(x.y)};
+            Bsm[a8_swz(brow, 2 * bj + 1)] = u32x4{lo(x.z), hi(x.z), lo(x.w), hi(x.w)};
         } else if constexpr (B == 4) {
             const u32x4 x = u32x4{breg[0], breg[1], breg[2], breg[3]} ^ 0x88888888u;
-            Bsm[buf][a8_swz(brow, 2 * bj)] =
+            Bsm[a8_swz(brow, 2 * bj)] =
                 u32x4{(x.x << 4) & 0xF0F0F0F0u, x.x & 0xF0F0F0F0u, (x.y << 4) & 0xF0F0F0F0u,
                       x.y & 0xF0F0F0F0u};
-            Bsm[buf][a8_swz(brow, 2 * bj + 1)] =
+            Bsm[a8_swz(brow, 2 * bj + 1)] =
                 u32x4{(x.z << 4) & 0xF0F0F0F0u, x.z & 0xF0F0F0F0u, (x.w << 4) & 0xF0F0F0F0u,
                       x.w & 0xF0F0F0F0u};
         } else if constexpr (WL::kTiled && int8_ready<B>()) {
@@ -293,83 +318,114 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
             // values q * 2^(8-b), natural order.
             uint32_t o[8];
             run_int8<B>(breg, o);
-            Bsm[buf][a8_swz(brow, 2 * bj)] = u32x4{o[0], o[1], o[2], o[3]};
-            Bsm[buf][a8_swz(brow, 2 * bj + 1)] = u32x4{o[4], o[5], o[6], o[7]};
+            Bsm[a8_swz(brow, 2 * bj)] = u32x4{o[0], o[1], o[2], o[3]};
+            Bsm[a8_swz(brow, 2 * bj + 1)] = u32x4{o[4], o[5], o[6], o[7]};
         } else {
-            Bsm[buf][a8_swz(brow, 2 * bj)] = u32x4{widen4<B, 0>(breg), widen4<B, 1>(breg),
-                                                   widen4<B, 2>(breg), widen4<B, 3>(breg)};
-            Bsm[buf][a8_swz(brow, 2 * bj + 1)] = u32x4{widen4<B, 4>(breg), widen4<B, 5>(breg),
-                                                       widen4<B, 6>(breg), widen4<B, 7>(breg)};
+            Bsm[a8_swz(brow, 2 * bj)] = u32x4{widen4<B, 0>(breg), widen4<B, 1>(breg),
+                                              widen4<B, 2>(breg), widen4<B, 3>(breg)};
+            Bsm[a8_swz(brow, 2 * bj + 1)] = u32x4{widen4<B, 4>(breg), widen4<B, 5>(breg),
+                                                  widen4<B, 6>(breg), widen4<B, 7>(breg)};
         }
         // The four chunk waves of a row store the same value: no branch.
-        Ss[buf][brow] = bf16_to_f32(sreg) * (ZP ? 1.0f : 1.0f / (float)(1 << (8 - B)));
+        Sr[brow] = bf16_to_f32(sreg) * (ZP ? 1.0f : 1.0f / (float)(1 << (8 - B)));
     };
-    auto fold_block = [&](int i, int j, const float(&sq)[4]) __attribute__((always_inline)) {
+    auto fold_all = [&](const float(&sq)[2]) __attribute__((always_inline)) {
+        // tot += s * P for the lane's 64 sums
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tot[i][j][r] = fmaf(sq[j], (float)P[i][j][r], tot[i][j][r]);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    tot[i][j][r] = fmaf(sq[j], (float)P[i][j][r], tot[i][j][r]);
     };
 
-    float sq_prev[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    fetch(0);
-    store(0);
-    fetch(1);
-    lds_barrier();
+    // Prologue: group 0's A and codes in buffer 0, group 1's codes in
+    // registers.
+    dma_a(0, As0);
+    fetch_b(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    store_b(Bs0, Ss[0]);
+    fetch_b(1);
 
-    for (int g = 0; g < G; ++g) {
-        const int gb = g & 1;
-        float sq[4];
+    // LATE: fold the previous group's sums before the MFMAs (the first time
+    // they are zero), else fold this group's after them.  Each role runs its
+    // own loop, so no register moves at merges.
+    auto run = [&](auto latec) __attribute__((always_inline)) {
+        constexpr bool LATE = decltype(latec)::value;
+        float sq_prev[2] = {0.0f, 0.0f};
+        auto group = [&](int g, auto bufc) __attribute__((always_inline)) {
+            constexpr int BUF = decltype(bufc)::value;
+            const u32x4 *as = BUF ? As1 : As0;
+            const u32x4 *bs = BUF ? Bs1 : Bs0;
+            // Group g's A (loaded during g - 1) and codes (stored at the
+            // start of g - 1) are in buffer BUF for every wave, and every
+            // wave is done with the other buffer.  Fenced: the scheduler
+            // would otherwise move the previous group's MFMAs and fold past
+            // this wait, which then stalls on loads issued just before.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            store_b(BUF ? Bs0 : Bs1, Ss[BUF ^ 1]);  // group g + 1's codes
+            fetch_b(g + 2);
+            dma_a(g + 1, BUF ? As0 : As1);
+            __builtin_amdgcn_sched_barrier(0);  // the loads go out now
+            float sq[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sq[j] = Ss[gb][wn * 64 + 16 * j + (lane & 15)];
-        const u32x4 *as = Asm[gb];
-        const u32x4 *bs = Bsm[gb];
-        i32x4_t bfr[2][4], af[2];
+            for (int j = 0; j < 2; ++j) sq[j] = Ss[BUF][wn * 64 + 32 * j + r32];
+            i32x4_t af[2][2], bf[2][2];  // [k-step parity][block]
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bfr[0][j] = __builtin_bit_cast(i32x4_t, bs[a8_swz(bmrow + 16 * j, q)]);
-        af[0] = __builtin_bit_cast(i32x4_t, as[a8_swz(arow, q)]);
-        __builtin_amdgcn_sched_barrier(0);
-        // 8 steps (k-step kk, row block i) of 4 MFMAs; each MFMA is followed
-        // by its slice of the other work, fenced so this is the issue order.
-#pragma unroll
-        for (int step = 0; step < 8; ++step) {
-            const int kk = step >> 2, i = step & 3;
-            if (i < 3)
-                af[(step + 1) & 1] =
-                    __builtin_bit_cast(i32x4_t, as[a8_swz(arow + 16 * (i + 1), 4 * kk + q)]);
-            else if (kk == 0)
-                af[(step + 1) & 1] = __builtin_bit_cast(i32x4_t, as[a8_swz(arow, 4 + q)]);
-            if (step == 2) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    bfr[1][j] = __builtin_bit_cast(i32x4_t, bs[a8_swz(bmrow + 16 * j, 4 + q)]);
+            for (int i = 0; i < 2; ++i) {
+                af[0][i] = __builtin_bit_cast(i32x4_t, as[a8_swz(arow + 32 * i, hh)]);
+                bf[0][i] = __builtin_bit_cast(i32x4_t, bs[a8_swz(bmrow + 32 * i, hh)]);
             }
+            if constexpr (LATE) fold_all(sq_prev);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                P[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                    af[step & 1], bfr[kk][j], kk == 0 ? i32x4_t{0, 0, 0, 0} : P[i][j], 0, 0, 0);
-                if (step == 0) fold_block(3, j, sq_prev);  // previous group's row 3
-                if (step >= 5) fold_block(step - 5, j, sq);
-                if (step == 3 && j == 0) store(gb ^ 1);    // group g+1 into the other buffer
-                if (step == 4 && j == 0) fetch(g + 2);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int kk = 0; kk < 4; ++kk) {
+                const int c = kk & 1;
+                if (kk + 1 < 4) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        af[c ^ 1][i] = __builtin_bit_cast(
+                            i32x4_t, as[a8_swz(arow + 32 * i, 2 * (kk + 1) + hh)]);
+                        bf[c ^ 1][i] = __builtin_bit_cast(
+                            i32x4_t, bs[a8_swz(bmrow + 32 * i, 2 * (kk + 1) + hh)]);
+                    }
+                }
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk) {
+                    const int i = blk >> 1, j = blk & 1;
+                    const i32x16_t zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                    P[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        af[c][i], bf[c][j], kk == 0 ? zero : P[i][j], 0, 0, 0);
+                }
             }
+            if constexpr (!LATE) fold_all(sq);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sq_prev[j] = sq[j];
+        };
+        int g = 0;
+        for (; g + 1 < G; g += 2) {
+            group(g, std::integral_constant<int, 0>{});
+            group(g + 1, std::integral_constant<int, 1>{});
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sq_prev[j] = sq[j];
-        lds_barrier();
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fold_block(3, j, sq_prev);
+        if (g < G) group(g, std::integral_constant<int, 0>{});
+        if constexpr (LATE) fold_all(sq_prev);
+    };
+    if (late) run(std::true_type{});
+    else run(std::false_type{});
 
-    // Output element r of block (i, j): row 4*(lane/16) + r, column lane%16.
+    // Output register r of block (i, j): row 8 (r / 4) + 4 (lane / 32) + r % 4,
+    // column lane % 32.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + wn * 64 + 16 * j + (lane & 15);
+        for (int j = 0; j < 2; ++j) {
+            const int64_t n = n0 + wn * 64 + 32 * j + r32;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
                 if (m < M && n < N) {
                     const float y = sa[m] * tot[i][j][r];
                     if (out_f32)
