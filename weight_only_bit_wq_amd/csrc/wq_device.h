@@ -388,6 +388,11 @@ __device__ __forceinline__ void load_slot(const uint4 *p, int64_t stride, uint32
 // otherwise be moved across it.
 __device__ __forceinline__ void wait_vm_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Word 3 of a raw buffer resource on this architecture (gfx9 family): 32-bit
+// data format, no swizzle or stride; accesses are range-checked against the
+// resource's num_records (out of range reads return zero).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 // s_waitcnt immediate that waits until at most n of this wave's vector-memory
 // operations are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
 // left at "no wait").

@@ -155,16 +155,20 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
 #pragma unroll
     for (int u = 0; u < RU; ++u)
         doff[u] = (uint32_t)((min(dma_row0 + 4 * NW * u, mlim) * K + 8 * dma_chunk) * 2);
-    auto dma = [&](const uint16_t *base, int k0, const uint32_t(&off)[RU], auto bconst)
+    // Direct loads through a buffer resource on the tile's rows: the lane's
+    // offset (under 2^31 bytes: row < 256, K <= 2^22) in a VGPR, the group's
+    // column offset in an SGPR, so no per-load 64-bit address arithmetic.
+    const __amdgpu_buffer_rsrc_t a_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)A_blk, (short)0, 0x7FFFFFFF, kBufferRsrcWord3);
+    auto dma = [&](const uint16_t *, int k0, const uint32_t(&off)[RU], auto bconst)
         __attribute__((always_inline)) {
         constexpr int BUF = decltype(bconst)::value;
         u32x4 *dst = BUF == 0 ? As0 : BUF == 1 ? As1 : As2;
-        const uint8_t *b8 = reinterpret_cast<const uint8_t *>(base + k0);
 #pragma unroll
         for (int u = 0; u < RU; ++u)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(b8 + off[u]),
-                (__attribute__((address_space(3))) void *)&dst[64 * (wave + NW * u)], 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                a_rsrc, (__attribute__((address_space(3))) void *)&dst[64 * (wave + NW * u)], 16,
+                (int)off[u], 2 * k0, 0, 0);
     };
 
     // Codes: each group's 128 columns x b planes of 16 bytes (2 b runs of
@@ -174,10 +178,18 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     // (rows beyond N read row N-1).  The lane's column (32 wn + c32, block
     // t = wn / 2, row rho) and half h then read dword pair i of the half,
     // slot dword d = 2 h B + 2 i, from LDS at coff[i].
-    const uint8_t *crow[2];
+    // Codes through a buffer resource based at the tile's first row: every
+    // offset is under 2^31 bytes (two 64-row blocks of tiles, or 128 dense
+    // rows of at most 4 MB).
+    const uint8_t *cbase = reinterpret_cast<const uint8_t *>(wl.chunks(min(n0, (int64_t)N - 1), 0));
+    const __amdgpu_buffer_rsrc_t c_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)cbase, (short)0, 0x7FFFFFFF, kBufferRsrcWord3);
+    int crow[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-        crow[t] = reinterpret_cast<const uint8_t *>(wl.chunks(min(n0 + 64 * t + lane, (int64_t)N - 1), 0));
+        crow[t] = (int)(reinterpret_cast<const uint8_t *>(
+                            wl.chunks(min(n0 + 64 * t + lane, (int64_t)N - 1), 0)) -
+                        cbase);
     const int64_t bstep = wl.slot_step();
     const int cstride = (int)wl.chunk_stride() * 16;
     auto dma_codes = [&](int g, auto bconst) __attribute__((always_inline)) {
@@ -187,9 +199,9 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
             const int r = wave + NW * k;
             if (r < 2 * B) {
                 const int t = r >= B ? 1 : 0, p = r - t * B;
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(crow[t] + g * bstep + p * cstride),
-                    (__attribute__((address_space(3))) void *)&dst[64 * r], 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    c_rsrc, (__attribute__((address_space(3))) void *)&dst[64 * r], 16, crow[t],
+                    (int)(g * bstep) + p * cstride, 0, 0);
             }
         }
     };
