@@ -166,7 +166,9 @@ hipError_t launch_quant_act(const uint16_t *A, int64_t M, int64_t K, int8_t *Aq,
     return hipGetLastError();
 }
 
-constexpr int kABM = 256, kABN = 128;
+constexpr int kABM = 256, kABN = 128;  // workgroup tile (m x n)
+constexpr int kAW = kABM / 32;          // waves: (kABM / 64) x 2 of 64 x 64
+constexpr int kAQ = 4 * kABN / (64 * kAW);  // 32-code quarters each thread stages per group
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
@@ -177,9 +179,10 @@ int64_t a8_ws_bytes(int64_t M, int64_t, int64_t K) {
 }
 
 // LDS rows of 128 bytes (8 chunks of 16 int8 = 16 k); chunk c of row r sits
-// at c ^ (r mod 8), so an operand read (16 rows, one chunk) and the loaders'
-// row-major writes are conflict free.
-__device__ __forceinline__ int a8_swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// at c ^ ((r / 2) mod 8): the 16 consecutive rows of one chunk that an
+// operand read or a code store touches land in 16 distinct 16-byte bank
+// groups (row parity picks the half of the 256 bytes, r / 2 the slot).
+__device__ __forceinline__ int a8_swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 // Workgroup: 512 threads = 8 waves (two per SIMD) over a 256 (m) x 128 (n)
 // tile; wave (wm, wn) owns 64 x 64 = 2 x 2 blocks of v_mfma_i32_32x32x32_i8
@@ -203,13 +206,13 @@ typedef int i32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <class WL, int B, bool ZP>
-__global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__ Aq,
+__global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restrict__ Aq,
                                                       const float *__restrict__ sa, int M, int N,
                                                       int K, WL wl,
                                                       const uint8_t *__restrict__ zeros,
                                                       void *__restrict__ Y,
                                                       bool out_f32, int mtiles, int ntiles) {
-    __shared__ u32x4 As0[kABM * 8];  // 32 KB each
+    __shared__ u32x4 As0[kABM * 8];  // 128 bytes per row: 32 KB each
     __shared__ u32x4 As1[kABM * 8];
     __shared__ u32x4 Bs0[kABN * 8];  // 16 KB each
     __shared__ u32x4 Bs1[kABN * 8];
@@ -231,34 +234,36 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
     const int64_t m0 = (int64_t)bm * kABM;
     const int64_t n0 = (int64_t)bn * kABN;
 
-    // A direct loads: instruction u of wave w fills LDS slots 64 (w + 8u) ..
-    // +63, rows 8 (w + 8u) .. +7; lane l writes slot l of them: row
-    // 8 (w + 8u) + l / 8, physical chunk l % 8, which holds logical chunk
-    // (l % 8) ^ (row % 8) (a8_swz).  Rows beyond M read row M-1.
+    // A direct loads: instruction u of wave w fills LDS slots 64 (w + W u)
+    // .. +63 (W waves), rows 8 (w + W u) .. +7; lane l writes slot l of them:
+    // row 8 (w + W u) + l / 8, physical chunk l % 8, which holds logical
+    // chunk (l % 8) ^ ((row / 2) % 8) (a8_swz).  Rows beyond M read row M-1.
+    constexpr int AU = kABM / (8 * kAW);  // direct loads per wave per group
     const int mlim = (int)min((int64_t)M - 1 - m0, (int64_t)kABM - 1);
     const int8_t *A_blk = Aq + m0 * K;
-    uint32_t aoff[4];
+    uint32_t aoff[AU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int row = 8 * (wave + 8 * u) + (lane >> 3);
-        const int chunk = (lane & 7) ^ (row & 7);
+    for (int u = 0; u < AU; ++u) {
+        const int row = 8 * (wave + kAW * u) + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
         aoff[u] = (uint32_t)(min(row, mlim) * K + 16 * chunk);
     }
     auto dma_a = [&](int g, u32x4 *dst) __attribute__((always_inline)) {
         g = min(g, G - 1);
         const int8_t *src = A_blk + (int64_t)g * kGroup;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < AU; ++u)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void *)(src + aoff[u]),
-                (__attribute__((address_space(3))) void *)&dst[64 * (wave + 8 * u)], 16, 0, 0);
+                (__attribute__((address_space(3))) void *)&dst[64 * (wave + kAW * u)], 16, 0, 0);
     };
 
-    // B loader: row brow, quarter bj (wave-uniform) = codes 32 bj .. +32 of
-    // the group (b = 4: 16-byte chunk bj); widened to int8 it fills LDS
-    // chunks 2 bj and 2 bj + 1.
+    // B loader: row brow, quarters bj + (64 kAW / kABN) i (i < kAQ, wave-
+    // uniform) = codes 32 q .. +32 of the group (b = 4: 16-byte chunk q);
+    // widened to int8 quarter q fills LDS chunks 2 q and 2 q + 1.
     const int brow = tid & (kABN - 1);
     const int bj = __builtin_amdgcn_readfirstlane(tid >> 7);
+    constexpr int kQStep = 64 * kAW / kABN;
     const int64_t bn_read = min(n0 + brow, (int64_t)N - 1);
     const uint8_t *bslot0 = wl.slot0(bn_read);
     const uint8_t *bscale0 = wl.scale0(bn_read);
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
     const int arow = wm * 64 + r32;
     const int bmrow = wn * 64 + r32;
 
-    uint32_t breg[B];
+    uint32_t breg[kAQ][B];
     uint16_t sreg;
     uint32_t zreg = 0;
     i32x16_t P[2][2];  // [block row][block column]
@@ -285,17 +290,26 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
                 tot[i][j][r] = 0.0f;
                 P[i][j][r] = 0;
             }
-    const bool late = wm >= 2;  // the second wave of its SIMD
+    // With two waves of one workgroup on a SIMD (256-row tiles) they take
+    // the group in opposite orders; with one (128-row tiles, measured
+    // slower) every wave runs MFMAs, then the fold.
+    const bool late = kAW == 8 && wm >= 2;
 
     auto fetch_b = [&](int g) __attribute__((always_inline)) {  // clamped to the last group
         g = min(g, G - 1);
-        load_quarter<WL, B>(bslot0 + (int64_t)g * bstep, bj, breg);
+#pragma unroll
+        for (int i = 0; i < kAQ; ++i)
+            load_quarter<WL, B>(bslot0 + (int64_t)g * bstep, bj + kQStep * i, breg[i]);
         sreg = *reinterpret_cast<const uint16_t *>(bscale0 + (int64_t)g * sstep);
         if constexpr (ZP) zreg = zrow[g];
     };
     auto store_b = [&](u32x4 *Bsm, float *Sr) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qi = 0; qi < kAQ; ++qi) {
+        const int bq = bj + kQStep * qi;
+        const uint32_t *breg_q = breg[qi];
         if constexpr (ZP) {  // b = 4: int8 c - z, codes ordered as below
-            const u32x4 x = u32x4{breg[0], breg[1], breg[2], breg[3]};
+            const u32x4 x = u32x4{breg_q[0], breg_q[1], breg_q[2], breg_q[3]};
             const uint32_t zb = zreg * 0x01010101u;
             auto lo = [&](uint32_t v) {
                 return (((v & 0x0F0F0F0Fu) | 0x80808080u) - zb) ^ 0x80808080u;
@@ -303,30 +317,31 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(const int8_t *__restrict__
             auto hi = [&](uint32_t v) {
                 return ((((v >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zb) ^ 0x80808080u;
             };
-            Bsm[a8_swz(brow, 2 * bj)] = u32x4{lo(x.x), hi(x.x), lo(x.y), hi(x.y)};
-            Bsm[a8_swz(brow, 2 * bj + 1)] = u32x4{lo(x.z), hi(x.z), lo(x.w), hi(x.w)};
+            Bsm[a8_swz(brow, 2 * bq)] = u32x4{lo(x.x), hi(x.x), lo(x.y), hi(x.y)};
+            Bsm[a8_swz(brow, 2 * bq + 1)] = u32x4{lo(x.z), hi(x.z), lo(x.w), hi(x.w)};
         } else if constexpr (B == 4) {
-            const u32x4 x = u32x4{breg[0], breg[1], breg[2], breg[3]} ^ 0x88888888u;
-            Bsm[a8_swz(brow, 2 * bj)] =
+            const u32x4 x = u32x4{breg_q[0], breg_q[1], breg_q[2], breg_q[3]} ^ 0x88888888u;
+            Bsm[a8_swz(brow, 2 * bq)] =
                 u32x4{(x.x << 4) & 0xF0F0F0F0u, x.x & 0xF0F0F0F0u, (x.y << 4) & 0xF0F0F0F0u,
                       x.y & 0xF0F0F0F0u};
-            Bsm[a8_swz(brow, 2 * bj + 1)] =
+            Bsm[a8_swz(brow, 2 * bq + 1)] =
                 u32x4{(x.z << 4) & 0xF0F0F0F0u, x.z & 0xF0F0F0F0u, (x.w << 4) & 0xF0F0F0F0u,
                       x.w & 0xF0F0F0F0u};
         } else if constexpr (WL::kTiled && int8_ready<B>()) {
             // The tiled layout's arranged run decodes straight to the int8
             // values q * 2^(8-b), natural order.
             uint32_t o[8];
-            run_int8<B>(breg, o);
-            Bsm[a8_swz(brow, 2 * bj)] = u32x4{o[0], o[1], o[2], o[3]};
-            Bsm[a8_swz(brow, 2 * bj + 1)] = u32x4{o[4], o[5], o[6], o[7]};
+            run_int8<B>(breg_q, o);
+            Bsm[a8_swz(brow, 2 * bq)] = u32x4{o[0], o[1], o[2], o[3]};
+            Bsm[a8_swz(brow, 2 * bq + 1)] = u32x4{o[4], o[5], o[6], o[7]};
         } else {
-            Bsm[a8_swz(brow, 2 * bj)] = u32x4{widen4<B, 0>(breg), widen4<B, 1>(breg),
-                                              widen4<B, 2>(breg), widen4<B, 3>(breg)};
-            Bsm[a8_swz(brow, 2 * bj + 1)] = u32x4{widen4<B, 4>(breg), widen4<B, 5>(breg),
-                                                  widen4<B, 6>(breg), widen4<B, 7>(breg)};
+            Bsm[a8_swz(brow, 2 * bq)] = u32x4{widen4<B, 0>(breg_q), widen4<B, 1>(breg_q),
+                                              widen4<B, 2>(breg_q), widen4<B, 3>(breg_q)};
+            Bsm[a8_swz(brow, 2 * bq + 1)] = u32x4{widen4<B, 4>(breg_q), widen4<B, 5>(breg_q),
+                                                  widen4<B, 6>(breg_q), widen4<B, 7>(breg_q)};
         }
-        // The four chunk waves of a row store the same value: no branch.
+      }
+        // The waves holding a row's quarters store the same value: no branch.
         Sr[brow] = bf16_to_f32(sreg) * (ZP ? 1.0f : 1.0f / (float)(1 << (8 - B)));
     };
     auto fold_all = [&](const float(&sq)[2]) __attribute__((always_inline)) {
@@ -448,11 +463,11 @@ static hipError_t launch_gemm_a8_b(const int8_t *Aq, const float *sa, int64_t M,
     const dim3 grid((unsigned)(mtiles * ntiles));
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W), G, B};
-        hipLaunchKernelGGL((gemm_a8_kernel<TiledW, B, ZP>), grid, dim3(512), 0, stream, Aq, sa,
+        hipLaunchKernelGGL((gemm_a8_kernel<TiledW, B, ZP>), grid, dim3(64 * kAW), 0, stream, Aq, sa,
                            (int)M, (int)N, (int)K, wl, zeros, Y, out_f32, mtiles, ntiles);
     } else {
         DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
-        hipLaunchKernelGGL((gemm_a8_kernel<DenseW, B, ZP>), grid, dim3(512), 0, stream, Aq, sa,
+        hipLaunchKernelGGL((gemm_a8_kernel<DenseW, B, ZP>), grid, dim3(64 * kAW), 0, stream, Aq, sa,
                            (int)M, (int)N, (int)K, wl, zeros, Y, out_f32, mtiles, ntiles);
     }
     return hipGetLastError();
