@@ -121,3 +121,23 @@ def test_grouped_table_overflow():
     torch.cuda.synchronize()
     y_ref, mag = oracle.wna16_grouped(A, packed, scales, b, off)
     assert_wna16(host_bf16_bits(Y), y_ref, mag, "grouped overflow")
+
+
+def test_grouped_overflow_with_split_decode_expert():
+    # A 300-row expert first, then 239 prefill-sized experts (more 64-row
+    # tiles than one table holds, so prefill launches come before and after
+    # the decode table) and a 3-row expert whose decode table splits K: its
+    # partials live in the workspace while prefill tiles of the first
+    # expert are still pending.  Every prefill launch must be unaffected.
+    E, N, K, b = 241, 64, 2048, 5
+    sizes = [300] + [20] * 239 + [3]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    need = wq.wq_grouped_workspace_bytes(off, N, K, b)
+    assert need > wq.WORKSPACE_ZERO_BYTES  # the decode table is split
+    packed, scales, _, W, eb = _experts(E, N, K, b, 3400)
+    A = synth.draw_act(np.random.default_rng(3401), int(off[-1]), K)
+    print("grouped overflow + split decode rows=%d ws=%d" % (off[-1], need), flush=True)
+    Y = wq.wq_gemm_grouped(dev_bf16(A), W, eb, off, N, b)
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.wna16_grouped(A, packed, scales, b, off)
+    assert_wna16(host_bf16_bits(Y), y_ref, mag, "grouped overflow + split decode")
