@@ -415,6 +415,10 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
                     P[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                         af[c][i], bf[c][j], kk == 0 ? zero : P[i][j], 0, 0, 0);
                 }
+                // Keep the k-step order: the scheduler would otherwise run
+                // each block's four MFMAs back to back (each waiting on the
+                // one before) to start that block's fold sooner.
+                __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (!LATE) fold_all(sq);
 #pragma unroll
