@@ -294,13 +294,18 @@ def hip_ceilings(torch, quick: bool):
                    the 256 MB Infinity Cache), the best of a sweep over
                    workgroup counts and loads in flight per lane;
       mfma_bf16    back-to-back v_mfma_f32_32x32x16_bf16, 2 waves per SIMD;
-      mfma_i8      the same with v_mfma_i32_16x16x64_i8."""
+      mfma_i8      the same with v_mfma_i32_16x16x64_i8;
+      mfma_fold    v_mfma_f32_32x32x16_bf16 / v_mfma_i32_32x32x32_i8 with NV
+                   vector-ALU fold operations after each MFMA (2 waves per
+                   SIMD, two chains): what a GEMM that folds per-group sums
+                   into fp32 keeps of the matrix-core rate."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_bit_wq_amd", "libwq_ceilings.so"))
     P, L, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.wqc_stream_read.argtypes = [P, L, I, I, P, P]
     lib.wqc_mfma_loop.argtypes = [I, I, I, I, P, P]
-    for f in (lib.wqc_stream_read, lib.wqc_mfma_loop):
+    lib.wqc_mfma_fold.argtypes = [I, I, I, I, P, P]
+    for f in (lib.wqc_stream_read, lib.wqc_mfma_loop, lib.wqc_mfma_fold):
         f.restype = I
 
     def st():
@@ -358,6 +363,20 @@ def hip_ceilings(torch, quick: bool):
             if best is None or row["frac_of_peak"] > best["frac_of_peak"]:
                 best = row
         out["mfma_" + name.split("_", 2)[2]] = best
+    # MFMA with per-MFMA vector-ALU folds, 512 workgroups of 4 waves.
+    fold = []
+    for op, name, mnk, kind in ((0, "v_mfma_f32_32x32x16_bf16", 32 * 32 * 16, "bf16"),
+                                (1, "v_mfma_i32_32x32x32_i8", 32 * 32 * 32, "i8")):
+        for nv in ((0, 4, 8) if quick else (0, 2, 4, 6, 8, 10, 12)):
+            wgs, iters = 512, 500
+            t = graph_time(torch, lambda: check(lib.wqc_mfma_fold(op, nv, wgs, iters,
+                                                                  P(fs.data_ptr()), st()),
+                                                "wqc_mfma_fold"), 5, 1)
+            rate = wgs * 4 * iters * 16 * 2 * mnk / t / 1e12
+            peak = BF16_PEAK_TFLOPS if kind == "bf16" else INT8_PEAK_TOPS
+            fold.append({"instr": name, "valu_per_mfma": nv, "us": t * 1e6,
+                         "frac_of_peak": rate / peak})
+    out["mfma_fold"] = fold
     return out
 
 
