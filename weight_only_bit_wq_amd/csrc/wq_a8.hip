@@ -191,17 +191,15 @@ __device__ __forceinline__ int a8_swz(int row, int chunk) { return row * 8 + (ch
 // register r).  Per group of 128 k: 4 k-steps x 4 MFMAs into exact int32
 // sums P, then tot += (s/16) * float(P) (fp32): 64 conversions and FMAs per
 // lane, as much vector-ALU time as the MFMAs take on the matrix cores.  The
-// two waves of a SIMD (wm and wm + 2) take the group in opposite orders: the
-// early one runs its MFMAs and then folds them, the late one folds the
-// previous group's sums and then runs its MFMAs, so each wave's fold issues
-// while its partner's MFMAs run.
+// fold is spread evenly over the MFMA slots: each group runs block row 0,
+// then block row 1, each over the four k-steps, and every MFMA slot folds 4
+// sums of the block row the matrix core is not writing (see group below).
 // Data: A (int8, GEMM k-order) goes global -> LDS by direct loads, the codes
 // through registers (widened to int8 on their way into LDS), both double-
 // buffered in separate LDS objects (so the compiler sees that the reads of
 // one buffer do not wait for loads into the other).  At the start of group
 // g a wave stores group g + 1's widened codes (fetched during g - 1), then
-// issues group g + 2's code fetch and group g + 1's A loads: everything has
-// a whole group to land before the wait and barrier that open group g + 1.
+// issues group g + 2's code fetch and group g + 1's A loads.
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -290,10 +288,6 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
                 tot[i][j][r] = 0.0f;
                 P[i][j][r] = 0;
             }
-    // With two waves of one workgroup on a SIMD (256-row tiles) they take
-    // the group in opposite orders; with one (128-row tiles, measured
-    // slower) every wave runs MFMAs, then the fold.
-    const bool late = kAW == 8 && wm >= 2;
 
     auto fetch_b = [&](int g) __attribute__((always_inline)) {  // clamped to the last group
         g = min(g, G - 1);
@@ -344,15 +338,16 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
         // The waves holding a row's quarters store the same value: no branch.
         Sr[brow] = bf16_to_f32(sreg) * (ZP ? 1.0f : 1.0f / (float)(1 << (8 - B)));
     };
-    auto fold_all = [&](const float(&sq)[2]) __attribute__((always_inline)) {
-        // tot += s * P for the lane's 64 sums
+    // tot += s * P for elements 4 q .. 4 q + 3 of block (i, j): four
+    // conversions and four FMAs, pinned in their MFMA slot by an empty asm.
+    auto fold4 = [&](int i, int j, int q, float sc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    tot[i][j][r] = fmaf(sq[j], (float)P[i][j][r], tot[i][j][r]);
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q + e;
+            float t = fmaf(sc, (float)P[i][j][r], tot[i][j][r]);
+            asm volatile("" : "+v"(t));
+            tot[i][j][r] = t;
+        }
     };
 
     // Prologue: group 0's A and codes in buffer 0, group 1's codes in
@@ -363,77 +358,79 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
     store_b(Bs0, Ss[0]);
     fetch_b(1);
 
-    // LATE: fold the previous group's sums before the MFMAs (the first time
-    // they are zero), else fold this group's after them.  Each role runs its
-    // own loop, so no register moves at merges.
-    auto run = [&](auto latec) __attribute__((always_inline)) {
-        constexpr bool LATE = decltype(latec)::value;
-        float sq_prev[2] = {0.0f, 0.0f};
-        auto group = [&](int g, auto bufc) __attribute__((always_inline)) {
-            constexpr int BUF = decltype(bufc)::value;
-            const u32x4 *as = BUF ? As1 : As0;
-            const u32x4 *bs = BUF ? Bs1 : Bs0;
-            // Group g's A (loaded during g - 1) and codes (stored at the
-            // start of g - 1) are in buffer BUF for every wave, and every
-            // wave is done with the other buffer.  Fenced: the scheduler
-            // would otherwise move the previous group's MFMAs and fold past
-            // this wait, which then stalls on loads issued just before.
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-            __syncthreads();
-            __builtin_amdgcn_sched_barrier(0);
-            store_b(BUF ? Bs0 : Bs1, Ss[BUF ^ 1]);  // group g + 1's codes
-            fetch_b(g + 2);
-            dma_a(g + 1, BUF ? As0 : As1);
-            __builtin_amdgcn_sched_barrier(0);  // the loads go out now
-            float sq[2];
+    // Each group runs in two phases of 8 MFMA slots: phase 0 runs block row
+    // 0 (blocks (0, 0), (0, 1)) over the group's four k-steps and folds
+    // block row 1 of the previous group; phase 1 runs block row 1 and folds
+    // block row 0 of this group (block (0, 0) from phase 1's first slot, two
+    // MFMAs after its last one; block (0, 1) from its fifth).  Every MFMA
+    // slot carries the same fold work (4 conversions, 4 FMAs) in both waves
+    // of a SIMD, so neither runs a long stretch of vector-ALU work with the
+    // matrix core idle.  The B operands of the group's four k-steps are read
+    // during phase 0 and kept for phase 1; the A operand one k-step ahead.
+    float sq_prev[2] = {0.0f, 0.0f};
+    auto group = [&](int g, auto bufc) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        const u32x4 *as = BUF ? As1 : As0;
+        const u32x4 *bs = BUF ? Bs1 : Bs0;
+        // Group g's A (loaded during g - 1) and codes (stored at the start
+        // of g - 1) are in buffer BUF for every wave, and every wave is done
+        // with the other buffer.  Fenced: the scheduler would otherwise move
+        // the previous group's MFMAs and folds past this wait, which then
+        // stalls on loads issued just before.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        store_b(BUF ? Bs0 : Bs1, Ss[BUF ^ 1]);  // group g + 1's codes
+        fetch_b(g + 2);
+        dma_a(g + 1, BUF ? As0 : As1);
+        __builtin_amdgcn_sched_barrier(0);  // the loads go out now
+        float sq[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) sq[j] = Ss[BUF][wn * 64 + 32 * j + r32];
-            i32x4_t af[2][2], bf[2][2];  // [k-step parity][block]
+        for (int j = 0; j < 2; ++j) sq[j] = Ss[BUF][wn * 64 + 32 * j + r32];
+        i32x4_t bf[4][2], af[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[0][i] = __builtin_bit_cast(i32x4_t, as[a8_swz(arow + 32 * i, hh)]);
-                bf[0][i] = __builtin_bit_cast(i32x4_t, bs[a8_swz(bmrow + 32 * i, hh)]);
-            }
-            if constexpr (LATE) fold_all(sq_prev);
+        for (int j = 0; j < 2; ++j)
+            bf[0][j] = __builtin_bit_cast(i32x4_t, bs[a8_swz(bmrow + 32 * j, hh)]);
+        af[0] = __builtin_bit_cast(i32x4_t, as[a8_swz(arow, hh)]);
+        static_for<0, 16>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int S = decltype(sc)::value;
+            constexpr int PH = S >> 3, kk = (S & 7) >> 1, j = S & 1;
+            if constexpr (j == 0) {
+                if constexpr (kk + 1 < 4) {
+                    af[(kk + 1) & 1] = __builtin_bit_cast(
+                        i32x4_t, as[a8_swz(arow + 32 * PH, 2 * (kk + 1) + hh)]);
+                    if constexpr (PH == 0) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int c = kk & 1;
-                if (kk + 1 < 4) {
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        af[c ^ 1][i] = __builtin_bit_cast(
-                            i32x4_t, as[a8_swz(arow + 32 * i, 2 * (kk + 1) + hh)]);
-                        bf[c ^ 1][i] = __builtin_bit_cast(
-                            i32x4_t, bs[a8_swz(bmrow + 32 * i, 2 * (kk + 1) + hh)]);
+                        for (int jj = 0; jj < 2; ++jj)
+                            bf[kk + 1][jj] = __builtin_bit_cast(
+                                i32x4_t, bs[a8_swz(bmrow + 32 * jj, 2 * (kk + 1) + hh)]);
                     }
+                } else if constexpr (PH == 0) {
+                    af[0] = __builtin_bit_cast(i32x4_t, as[a8_swz(arow + 32, hh)]);
                 }
-#pragma unroll
-                for (int blk = 0; blk < 4; ++blk) {
-                    const int i = blk >> 1, j = blk & 1;
-                    const i32x16_t zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-                    P[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        af[c][i], bf[c][j], kk == 0 ? zero : P[i][j], 0, 0, 0);
-                }
-                // Keep the k-step order: the scheduler would otherwise run
-                // each block's four MFMAs back to back (each waiting on the
-                // one before) to start that block's fold sooner.
-                __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (!LATE) fold_all(sq);
+            const i32x16_t zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            P[PH][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kk & 1], bf[kk][j],
+                                                            kk == 0 ? zero : P[PH][j], 0, 0, 0);
+            if constexpr (PH == 0) fold4(1, S >> 2, S & 3, sq_prev[S >> 2]);
+            else fold4(0, (S - 8) >> 2, S & 3, sq[(S - 8) >> 2]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
 #pragma unroll
-            for (int j = 0; j < 2; ++j) sq_prev[j] = sq[j];
-        };
-        int g = 0;
-        for (; g + 1 < G; g += 2) {
-            group(g, std::integral_constant<int, 0>{});
-            group(g + 1, std::integral_constant<int, 1>{});
-        }
-        if (g < G) group(g, std::integral_constant<int, 0>{});
-        if constexpr (LATE) fold_all(sq_prev);
+        for (int j = 0; j < 2; ++j) sq_prev[j] = sq[j];
     };
-    if (late) run(std::true_type{});
-    else run(std::false_type{});
+    int g = 0;
+    for (; g + 1 < G; g += 2) {
+        group(g, std::integral_constant<int, 0>{});
+        group(g + 1, std::integral_constant<int, 1>{});
+    }
+    if (g < G) group(g, std::integral_constant<int, 0>{});
+    // The last group's block row 1.
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) fold4(1, j, q, sq_prev[j]);
 
     // Output register r of block (i, j): row 8 (r / 4) + 4 (lane / 32) + r % 4,
     // column lane % 32.

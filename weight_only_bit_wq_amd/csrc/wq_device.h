@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace wq {
 
 constexpr int kGroup = 128;     // codes per scale group
@@ -363,6 +365,15 @@ template <int B, int P, bool ZP, bool I8>
 __device__ __forceinline__ uint32_t slot_pair(const uint32_t *w, const uint32_t *o, int z) {
     if constexpr (I8) return i8pair<P % 16>(o + (P / 16) * 8);
     else return wpair<B, P % 16, ZP>(w + (P / 16) * B, z);
+}
+
+// f(std::integral_constant<int, I>{}) for I = I0 .. N - 1, unrolled.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
 }
 
 // Load the 4*B words of one slot (B 16-byte chunks, `stride` uint4 apart).
