@@ -409,22 +409,26 @@ def test_split_k_handoff_repeated(b, M, K, N):
 
 
 
+@pytest.mark.parametrize("reduce", [0, 1], ids=["handoff", "reduce"])
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
 @pytest.mark.parametrize("waves", [4, 8, 16])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 8, 13, 16])
-def test_decode_split_k_forced(M, waves, layout, monkeypatch):
-    # The lane-per-row decode kernel's split-K hand-off (one ticket per row
-    # block and storing wave, the other waves leaving after the LDS sum) at
-    # every row tile and wave count it supports, on a small ragged layer
-    # with K forced into 4 splits of 3 groups (the default plan would not
-    # split it): full outputs against the oracle, a bitwise repeat, and the
-    # counter region left zero.  Row tiles above 1 take the 4x4x4 matrix-core
-    # form.
+def test_decode_split_k_forced(M, waves, layout, reduce, monkeypatch):
+    # The lane-per-row decode kernel's split-K sum at every row tile and
+    # wave count it supports, either handed off inside the kernel (one
+    # ticket per row block and storing wave, the other waves leaving after
+    # the LDS sum) or by the second kernel that adds the stored partials, on
+    # a small ragged layer with K forced into 4 splits of 3 groups (the
+    # default plan would not split it): full outputs against the oracle, a
+    # bitwise repeat, the counter region left zero, and (second kernel) the
+    # same bits as the hand-off, which adds in the same order.  Row tiles
+    # above 1 take the 4x4x4 matrix-core form.
     mt = 1 if M <= 1 else 4 if M <= 4 else 8 if M <= 8 else 16
     if waves == 16 and mt > 4:
         pytest.skip("wave count not offered for this row tile")
     monkeypatch.setenv("WQ_DECODE_WAVES", str(waves))
     monkeypatch.setenv("WQ_DECODE_SPLITS", "4")
+    monkeypatch.setenv("WQ_DECODE_REDUCE", str(reduce))
     b, N, K = 6, 200, 1536
     w = _workload(M, N, K, b, seed=1600 + 17 * M + waves)
     L = Layer(w, layout)
@@ -434,9 +438,16 @@ def test_decode_split_k_forced(M, waves, layout, monkeypatch):
     Y1 = wq.wq_gemm(A, L.W_d, L.layout, L.S_d, N, b, ws=ws)
     torch.cuda.synchronize()
     y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, b), w.scales, b)
-    assert_wna16(host_bf16_bits(Y0), y_ref, mag, "forced split-K M=%d waves=%d" % (M, waves))
+    assert_wna16(host_bf16_bits(Y0), y_ref, mag,
+                 "forced split-K M=%d waves=%d reduce=%d" % (M, waves, reduce))
     assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
     assert not ws[:wq.WORKSPACE_ZERO_BYTES].any()
+    if reduce:
+        monkeypatch.setenv("WQ_DECODE_REDUCE", "0")
+        Yh = wq.wq_gemm(A, L.W_d, L.layout, L.S_d, N, b, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(Y0.view(torch.int16), Yh.view(torch.int16))
+        assert not ws[:wq.WORKSPACE_ZERO_BYTES].any()
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])

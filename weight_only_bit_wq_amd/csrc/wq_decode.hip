@@ -1,6 +1,7 @@
 // wq_decode.hip -- decode-path planning and dispatch over b (the kernels are
 // instantiated one bit width per translation unit, wq_decode_b<b>.hip).
 #include "wq_launch.h"
+#include "wq_device.h"
 
 #include <algorithm>
 #include <cstdlib>
@@ -118,6 +119,17 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b, bool rows_ok) {
     while (p.tstride < 32 && tickets * p.tstride * 2 <= kWsMaxCounters) p.tstride *= 2;
     p.gps = (G + splits - 1) / splits;
     p.splits = (G + p.gps - 1) / p.gps;
+    // Row tiles of 8 and 16 with a K split store their partials and leave;
+    // a second kernel adds them.  Measured on MI355X at K 5120 -> N 17408,
+    // b = 5, 6, 7: 1.2-2.6 us faster per call at M = 16 than the in-kernel
+    // hand-off (whose last workgroup per row block waits out a store, a
+    // ticket and a load round trip), and up to 1.5 us slower at M = 4,
+    // where the second launch costs more than the hand-off it saves.
+    // Grouped launches (rows_ok false) keep the hand-off.  WQ_DECODE_REDUCE
+    // (0 or 1) forces the choice for non-grouped launches.
+    p.reduce = rows_ok && p.splits > 1 && p.mt >= 8;
+    if (const char *e = std::getenv("WQ_DECODE_REDUCE"))
+        p.reduce = rows_ok && p.splits > 1 && std::atoi(e) != 0;
     if (p.splits > 1)
         p.ws_bytes = kWsScratchOffset + (int64_t)p.splits * p.mt * p.rowblocks * 64 * 4;
     else
@@ -138,6 +150,43 @@ hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, con
         case 8: return decode_b<8>(A, M, N, K, W, tiled, scales, zeros, Y, ws, p, NoGroups{}, stream);
     }
     return hipErrorInvalidValue;
+}
+
+// One thread per 4 consecutive columns of one row: the splits' float4s
+// added in split order (the order and rounding of the in-kernel hand-off),
+// rounded to bf16 once.
+__global__ __launch_bounds__(256) void decode_reduce_kernel(const float *__restrict__ part,
+                                                            int splits, int mt, int M, int N,
+                                                            int npad, uint16_t *__restrict__ Y) {
+    const int64_t q = npad / 4;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int m = (int)(t / q);
+    const int64_t n = (t - (int64_t)m * q) * 4;
+    if (m >= M || n >= N) return;
+    const float4 *p = reinterpret_cast<const float4 *>(part + (int64_t)m * npad + n);
+    const int64_t step = (int64_t)mt * q;  // float4s from one split to the next
+    float4 acc = p[0];
+    for (int s = 1; s < splits; ++s) {
+        const float4 v = p[s * step];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    uint16_t *y = Y + (int64_t)m * N + n;
+    y[0] = f32_to_bf16_rne(acc.x);
+    if (n + 1 < N) y[1] = f32_to_bf16_rne(acc.y);
+    if (n + 2 < N) y[2] = f32_to_bf16_rne(acc.z);
+    if (n + 3 < N) y[3] = f32_to_bf16_rne(acc.w);
+}
+
+hipError_t launch_decode_reduce(const float *part, int splits, int mt, int64_t M, int64_t N,
+                                int rowblocks, uint16_t *Y, hipStream_t stream) {
+    const int npad = rowblocks * 64;
+    const int64_t threads = M * (npad / 4);
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       0, stream, part, splits, mt, (int)M, (int)N, npad, Y);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_grouped(const uint16_t *A, int64_t N, int64_t K, const void *W,

@@ -25,7 +25,10 @@
 //     LDS, only the waves that own output rows stay; each stores its fp32
 //     partials and takes a ticket per (block, wave); the last of the splits
 //     adds them in split order (deterministic), writes bf16 and resets the
-//     ticket (in the workspace's counter region) to zero.
+//     ticket (in the workspace's counter region) to zero.  Row tiles of 8
+//     and 16 (plan.reduce) only store their partials, and a second kernel
+//     adds them in the same order: no ticket, and no workgroup waits out
+//     the store, ticket and load round trips at the end.
 //
 // Arithmetic: the codes of a slot are turned into exact signed values
 // q = c - 2^(b-1) (bf16 pairs, see wq_device.h: one XOR per word, a
@@ -346,6 +349,19 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         return;
     }
 
+    const int Npad = (int)(gridDim.x / splits) * 64;
+    const int64_t np = (int64_t)RB * 64 + lane;  // partial-sum column
+    // No counters: a second kernel adds the partials (stream order makes
+    // these stores visible to it).
+    if (counters == nullptr) {
+#pragma unroll
+        for (int i = 0; i < (MT + W - 1) / W; ++i) {
+            const int m = wave + i * W;
+            if (m < MT) part[((int64_t)s * MT + m) * Npad + np] = v[i];
+        }
+        return;
+    }
+
     // Cross-workgroup reduction, per storing wave (rows m = wave + i W of
     // this 64-row block).  Shared data moves through device-scope relaxed
     // atomics (coherent across the XCDs' L2s without the L2
@@ -354,9 +370,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     // RMW, and the last of the `splits` waves with this (block, wave) reads
     // them back with atomic loads, adds them in split order (deterministic)
     // and resets the ticket.
-    const int Npad = (int)(gridDim.x / splits) * 64;
     unsigned *ticket = counters + ((int64_t)RB * storing + wave) * tstride;
-    const int64_t np = (int64_t)RB * 64 + lane;  // partial-sum column
 #pragma unroll
     for (int i = 0; i < (MT + W - 1) / W; ++i) {
         const int m = wave + i * W;
@@ -726,22 +740,25 @@ hipError_t decode_bmw(const uint16_t *A, int64_t M, int64_t N, int64_t K, const 
     float *part = nullptr;
     unsigned *counters = nullptr;
     if (p.splits > 1) {
-        counters = static_cast<unsigned *>(ws);
+        if (!p.reduce) counters = static_cast<unsigned *>(ws);
         part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
     }
     const bool one = MT > 1 && p.gps <= W;
+    hipError_t e;
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W_), G, B};
-        return launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p, gt,
-                                          stream);
-    }
-    if constexpr (GT::kGrouped) {
+        e = launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p, gt,
+                                       stream);
+    } else if constexpr (GT::kGrouped) {
         return hipErrorInvalidValue;  // grouped launches take the tiled layout
     } else {
         DenseW wl{static_cast<const uint8_t *>(W_), scales, (int64_t)16 * B * G, G, B};
-        return launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p, gt,
-                                          stream);
+        e = launch_decode_zp<B, MT, W>(one, A, M, N, K, wl, zeros, Y, part, counters, p, gt,
+                                       stream);
     }
+    if (e != hipSuccess || p.splits == 1 || !p.reduce) return e;
+    if constexpr (GT::kGrouped) return hipErrorInvalidValue;  // grouped plans keep the hand-off
+    return launch_decode_reduce(part, p.splits, MT, M, N, p.rowblocks, Y, stream);
 }
 
 template <int B, int MT, class GT>

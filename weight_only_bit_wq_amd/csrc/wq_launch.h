@@ -53,6 +53,7 @@ struct DecodePlan {
     int tstride;    // counters from one split-K ticket to the next (spreads them over cache lines)
     int rw;         // one row of A without a K split: rows per wave of the row kernel (8 or 4); 0 = split-K kernel
     int tmax;       // row kernel: load every slot at the start when a lane has at most tmax (2 or 3; 0 never)
+    int reduce;     // K split summed by a second kernel (no tickets): 1, or 0 for the in-kernel hand-off
     int64_t ws_bytes;
 };
 // The row kernel stages a row of A in LDS, 272 bytes per group of 128:
@@ -64,6 +65,11 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int b, bool rows_ok = tr
 hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
                          bool tiled, const uint16_t *scales, const uint8_t *zeros, int b,
                          uint16_t *Y, void *ws, const DecodePlan &plan, hipStream_t stream);
+// Sum of the split-K partials that the decode kernel stored at `part`
+// (split s, row m, column n at (s * mt + m) * 64 * rowblocks + n), in split
+// order, written to Y [M, N] as bf16.
+hipError_t launch_decode_reduce(const float *part, int splits, int mt, int64_t M, int64_t N,
+                                int rowblocks, uint16_t *Y, hipStream_t stream);
 // Grouped decode: every entry of gt has at most kDecodeMaxM rows; the plan
 // is decode_plan(max rows, entries * N, K, b) with rowblocks = entries *
 // ceil(N / 64).  Tiled layout.
