@@ -186,8 +186,7 @@ __device__ __forceinline__ void load_slot_regs_mf(const WL &wl, int64_t nr, int 
     if constexpr (ZP) r.z = zrow[g];
 #pragma unroll
     for (int q = 0; q < MT / 4; ++q)
-        r.av[q] = *reinterpret_cast<const u32x4 *>(A2 + (int64_t)g * 64 + arow_off[q] +
-                                                   4 * (lane >> 2));
+        r.av[q] = *reinterpret_cast<const u32x4 *>(A2 + (int64_t)g * 64 + arow_off[q]);
 }
 
 // x[m] = sum_k a[m,k] q_k for the lane's row and rows m = 0 .. MT-1 of A,
@@ -210,6 +209,90 @@ __device__ __forceinline__ void group_terms_mf(uint32_t *w, const u32x4 *av, int
     }
 }
 
+// ---------------------------------------------------------------------------
+// Row tile 16 on v_mfma_f32_16x16x32_bf16: a quarter of the matrix-core time
+// of four 4x4x4 chains (measured: the 4x4x4 chains took ~3 us of a 24 us
+// call at K 5120 -> N 17408).  The 16x16x32 block takes 16 weight rows,
+// each spread over 4 lanes (k-quarters), while the loads leave every lane
+// with its own row's whole slot; so each lane's exact code pairs move by 4x4
+// transposes of the wave's 16-lane quarters (below).  For row block cb (rows
+// 16 cb .. 16 cb + 15 of the wave's 64) and k-step t, lane (c, q) = (l % 16,
+// l / 16) supplies pairs 16 t + 4 q .. + 3 (codes 32 t + 8 q .. + 7) of row
+// 16 cb + c as its B operand, and the same 8 k of row c of A as its A
+// operand, and receives rows 4 q .. 4 q + 3 of A against weight row
+// 16 cb + c.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+
+// x_r <- quarter r of (x0, x1, x2, x3) taken across: afterwards quarter q of
+// x_r holds what quarter r of x_q held (two v_permlane32_swap, then two
+// v_permlane16_swap).
+__device__ __forceinline__ void transpose_quarters(uint32_t &x0, uint32_t &x1, uint32_t &x2,
+                                                   uint32_t &x3) {
+    // Upper halves of x0, x1 <-> lower halves of x2, x3.
+    const auto a = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
+    // Odd quarters of the first <-> even quarters of the second.
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    x0 = c[0];
+    x1 = c[1];
+    x2 = d[0];
+    x3 = d[1];
+}
+
+// x[4 cb + r] = sum_k a[4 q + r, k] q_k of weight row 16 cb + c (lane (c, q)),
+// unscaled; av[t] holds the lane's 8 activations of k-step t.
+template <int B, bool ZP, bool I8>
+__device__ __forceinline__ void group_terms_mf16(uint32_t *w, const u32x4 *av, int z, float *x) {
+    uint32_t o[I8 ? 32 : 1];
+    prep_runs<B, ZP, I8, 4>(w, o);
+    f32x4_t d[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) d[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    static_for<0, 4>([&](auto tc) __attribute__((always_inline)) {
+        constexpr int T = decltype(tc)::value;
+        uint32_t y[4][4];  // [pair i of the 8 codes][row block]
+        static_for<0, 4>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int I = decltype(ic)::value;
+            uint32_t x0 = slot_pair<B, 16 * T + 0 + I, ZP, I8>(w, o, z);
+            uint32_t x1 = slot_pair<B, 16 * T + 4 + I, ZP, I8>(w, o, z);
+            uint32_t x2 = slot_pair<B, 16 * T + 8 + I, ZP, I8>(w, o, z);
+            uint32_t x3 = slot_pair<B, 16 * T + 12 + I, ZP, I8>(w, o, z);
+            transpose_quarters(x0, x1, x2, x3);
+            y[I][0] = x0;
+            y[I][1] = x1;
+            y[I][2] = x2;
+            y[I][3] = x3;
+        });
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            u32x4 bv;
+            bv.x = y[0][cb];
+            bv.y = y[1][cb];
+            bv.z = y[2][cb];
+            bv.w = y[3][cb];
+            d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, av[T]),
+                                                            __builtin_bit_cast(bf16x8_v, bv),
+                                                            d[cb], 0, 0, 0);
+        }
+    });
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[4 * cb + r] = d[cb][r];
+}
+
+// The lane's own row scale as seen by lane (c, q) for rows 16 cb + c.
+__device__ __forceinline__ void row_block_scales(float sc, float *out) {
+    uint32_t x0 = __float_as_uint(sc), x1 = x0, x2 = x0, x3 = x0;
+    transpose_quarters(x0, x1, x2, x3);
+    out[0] = __uint_as_float(x0);
+    out[1] = __uint_as_float(x1);
+    out[2] = __uint_as_float(x2);
+    out[3] = __uint_as_float(x3);
+}
+
 // ONE: every wave has at most one group (gps <= W, the plan for large
 // layers): no prefetch register set, so more waves fit per SIMD.  Used for
 // the matrix-core row tiles; with one row of A the prefetching form measured
@@ -229,6 +312,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     static_assert(W * MT <= 128, "LDS reduction table");
     static_assert(MT == 1 || MT % 4 == 0, "row tiles above 1 take the matrix-core form");
     constexpr bool MF = MT >= 4;
+    constexpr bool MF16 = MT == 16;  // 16x16x32 blocks (4x4x4 below)
     constexpr bool I8 = WL::kTiled && int8_ready<B>() && !ZP;  // arranged runs
     constexpr float kSInv = operand_scale_inv<B, I8>();
     __shared__ float red[W][MT][64];
@@ -264,11 +348,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-    // Matrix-core form: lane 4i + r reads row 4q + r of set q (rows past M
-    // repeat row M-1; their outputs are dropped).
+    // Matrix-core form, activation dwords of a group: 4x4x4, lane 4i + r
+    // reads row 4q + r of set q, k = 8i .. 8i + 7; 16x16x32, lane (c, q)
+    // reads row c, k = 32 t + 8 q .. + 7 for k-step t.  Rows past M repeat
+    // row M-1; their outputs are dropped.
     int arow_off[MF ? MT / 4 : 1];
 #pragma unroll
-    for (int q = 0; q < (MF ? MT / 4 : 1); ++q) arow_off[q] = min(4 * q + (lane & 3), M - 1) * Kp;
+    for (int q = 0; q < (MF ? MT / 4 : 1); ++q)
+        arow_off[q] = MF16 ? min(lane & 15, M - 1) * Kp + 16 * q + 4 * (lane >> 4)
+                           : min(4 * q + (lane & 3), M - 1) * Kp + 4 * (lane >> 2);
 
     // Each wave walks groups g_begin + wave, + W, ...; the next group's chunks
     // are loaded before the current one is computed.
@@ -278,10 +366,18 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
             SlotRegsMf<B, MT> cur;
             load_slot_regs_mf<B, MT, ZP>(wl, nr, g, A2, arow_off, lane, zrow, cur);
             float x[MT];
-            group_terms_mf<B, MT, ZP, I8>(cur.w, cur.av, (int)cur.z, x);
             const float sc = bf16_to_f32(cur.s) * kSInv;
+            if constexpr (MF16) {
+                group_terms_mf16<B, ZP, I8>(cur.w, cur.av, (int)cur.z, x);
+                float sb[4];
+                row_block_scales(sc, sb);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m] = sc * x[m];
+                for (int m = 0; m < MT; ++m) acc[m] = sb[m >> 2] * x[m];
+            } else {
+                group_terms_mf<B, MT, ZP, I8>(cur.w, cur.av, (int)cur.z, x);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] = sc * x[m];
+            }
         }
     } else if constexpr (MF) {
         SlotRegsMf<B, MT> cur, nxt;
@@ -292,10 +388,18 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
             if (gn < g_end)
                 load_slot_regs_mf<B, MT, ZP>(wl, nr, gn, A2, arow_off, lane, zrow, nxt);
             float x[MT];
-            group_terms_mf<B, MT, ZP, I8>(cur.w, cur.av, (int)cur.z, x);
             const float sc = bf16_to_f32(cur.s) * kSInv;
+            if constexpr (MF16) {
+                group_terms_mf16<B, ZP, I8>(cur.w, cur.av, (int)cur.z, x);
+                float sb[4];
+                row_block_scales(sc, sb);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
+                for (int m = 0; m < MT; ++m) acc[m] = fmaf(sb[m >> 2], x[m], acc[m]);
+            } else {
+                group_terms_mf<B, MT, ZP, I8>(cur.w, cur.av, (int)cur.z, x);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc, x[m], acc[m]);
+            }
             cur = nxt;
         }
     } else if constexpr (ONE) {
@@ -319,8 +423,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
         }
     }
 
+    // 16x16x32: acc[4 cb + r] is row 4 q + r of A against weight row 16 cb + c.
 #pragma unroll
-    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    for (int m = 0; m < MT; ++m) {
+        if constexpr (MF16) red[wave][4 * (lane >> 4) + (m & 3)][16 * (m >> 2) + (lane & 15)] = acc[m];
+        else red[wave][m][lane] = acc[m];
+    }
     __syncthreads();
 
     // Rows m of A are summed over the waves by wave m % W; the other waves
