@@ -247,6 +247,32 @@ def test_repacked_sizes():
     assert wq.wq_repacked_bytes(2, N, K, b) == -1
 
 
+def test_a8_workspace_holds_the_tail_parts():
+    # The int8-activation layer splits the tiles of a last round at most half
+    # full (256 tiles of 256 x 128 per round) into up to 4 K parts of at
+    # least 4 groups; the workspace holds their fp32 partials after Aq, s_a.
+    def base(M, K):
+        a = lambda x: (x + 255) // 256 * 256
+        return wq.WORKSPACE_ZERO_BYTES + a(M * K) + a(M * 4)
+    tile = 256 * 128 * 4
+    # 1088 tiles: 4 rounds and 64 tiles, split in 4.
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 2048, 17408, 5120, 4) == \
+        base(2048, 5120) + 64 * 4 * tile
+    # 258 tiles (both edges ragged): 2 tiles, 4 parts of 4 groups.
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 300, 16500, 2048, 6) == \
+        base(300, 2048) + 2 * 4 * tile
+    # 8 groups only: 2 parts.
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 300, 16500, 1024, 4) == \
+        base(300, 1024) + 2 * 2 * tile
+    # Whole rounds (4352 tiles), a last round over half full (1224 tiles:
+    # 200 in the last), fewer tiles than a round (136), or too few groups
+    # to split: no parts.
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 8192, 17408, 5120, 4) == base(8192, 5120)
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 2304, 17408, 5120, 4) == base(2304, 5120)
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 256, 17408, 5120, 4) == base(256, 5120)
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 300, 16500, 512, 4) == base(300, 512)
+
+
 def test_workspace_zero_region_constant():
     # The binding's zero-region size is the one include/wq.h defines.
     import re

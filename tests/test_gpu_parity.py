@@ -364,6 +364,31 @@ def test_gemm_a8_full_shape_sampled(M):
     assert_a8(Y[mi, ni], y_ref, mag, False, "a8 full shape")
 
 
+@pytest.mark.parametrize("b,layout", [(4, wq.WQ_LAYOUT_TILED), (4, wq.WQ_LAYOUT_DENSE),
+                                      (6, wq.WQ_LAYOUT_TILED)], ids=["b4-tiled", "b4-dense", "b6-tiled"])
+def test_gemm_a8_tail_split(b, layout):
+    # 258 tiles of 256 x 128 (M 300 and N 16500: both edges ragged), K 2048:
+    # the last round's 2 tiles (row tile 1, column tiles 127 and 128) run as
+    # 4 K parts of 4 groups each, added by the second kernel.  Every output
+    # of those tiles, and a sample of the others, against the oracle, in
+    # both output types.
+    M, N, K = 300, 16500, 2048
+    w4 = synth.w4a8(M=M, N=N, K=K, seed=1500 + b)
+    codes = w4.codes if b == 4 else synth.draw_codes(np.random.default_rng(1510 + b), N, K, b)
+    w = synth.Workload(w4.A, codes, w4.scales, b)
+    L = Layer(w, layout)
+    Aq, sa = oracle.quant_act_i8(w.A)
+    tm, tn = np.meshgrid(np.arange(256, M), np.arange(127 * 128, N), indexing="ij")
+    si, sj = sample_points(M, N, 2000, seed=15 + b)
+    mi = np.concatenate([tm.ravel(), si])
+    ni = np.concatenate([tn.ravel(), sj])
+    y_ref, mag = oracle.w4a8_points(Aq, sa, oracle.pack(codes, b), w.scales, mi, ni, b=b)
+    Y = L.gemm_a8(wq.WQ_OUT_F32)
+    assert_a8(Y[mi, ni], y_ref, mag, False, "a8 tail split b=%d f32" % b)
+    Yb = L.gemm_a8(wq.WQ_OUT_BF16)
+    assert_a8(Yb[mi, ni], y_ref, mag, True, "a8 tail split b=%d bf16" % b)
+
+
 def test_gemm_a8_negated_scales():
     w = synth.w4a8(M=64, N=128, K=1024, seed=1200)
     Y1 = Layer(w, wq.WQ_LAYOUT_TILED).gemm_a8(wq.WQ_OUT_F32)

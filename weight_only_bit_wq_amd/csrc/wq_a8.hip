@@ -172,10 +172,46 @@ constexpr int kAQ = 4 * kABN / (64 * kAW);  // 32-code quarters each thread stag
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// Tail balance.  One workgroup per compute unit (the tile's LDS buffers
+// take 97 KB) and 256 compute units, so the tiles run in rounds of 256.
+// When the last round would be at most half full (M = 2048 at N = 17408:
+// 1088 tiles, 4 rounds and 64 tiles), its tiles are split along K into up
+// to 4 parts (at least 4 groups each), which fill the last round with
+// shorter workgroups; they store fp32 partials and a second kernel adds
+// them in split order.  (Measured on MI355X at K 5120 -> N 17408: M = 2048
+// took 98% of the time of M = 2304, 12.5% more work.)  The split tiles are
+// the last in logical order and run last.
+constexpr int kA8Slots = 256;
+struct A8Plan {
+    int tiles;   // all tiles
+    int full;    // tiles run whole (the first `full` in logical order)
+    int splits;  // K parts of each remaining tile (1: none)
+};
+static A8Plan a8_plan(int64_t M, int64_t N, int64_t K) {
+    A8Plan p;
+    p.tiles = (int)(((M + kABM - 1) / kABM) * ((N + kABN - 1) / kABN));
+    p.full = p.tiles;
+    p.splits = 1;
+    const int G = (int)(K / kGroup);
+    const int r = p.tiles % kA8Slots;
+    if (p.tiles >= kA8Slots && r > 0 && 2 * r <= kA8Slots) {
+        const int s = std::min(std::min(kA8Slots / r, 4), G / 4);
+        if (s >= 2) {
+            p.full = p.tiles - r;
+            p.splits = s;
+        }
+    }
+    return p;
+}
+static int64_t a8_part_bytes(const A8Plan &p) {
+    return (int64_t)(p.tiles - p.full) * p.splits * kABM * kABN * 4;
+}
+
 // Workspace: the shared counter region (unused here, left zero), then Aq
-// (GEMM k-order) and s_a.
-int64_t a8_ws_bytes(int64_t M, int64_t, int64_t K) {
-    return kWsScratchOffset + align256(M * K) + align256(M * 4);
+// (GEMM k-order), s_a and the tail tiles' partials.
+int64_t a8_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    return kWsScratchOffset + align256(M * K) + align256(M * 4) +
+           align256(a8_part_bytes(a8_plan(M, N, K)));
 }
 
 // LDS rows of 128 bytes (8 chunks of 16 int8 = 16 k); chunk c of row r sits
@@ -209,7 +245,9 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
                                                       int K, WL wl,
                                                       const uint8_t *__restrict__ zeros,
                                                       void *__restrict__ Y,
-                                                      bool out_f32, int mtiles, int ntiles) {
+                                                      bool out_f32, int mtiles, int ntiles,
+                                                      int nfull, int tsplits,
+                                                      float *__restrict__ part) {
     __shared__ u32x4 As0[kABM * 8];  // 128 bytes per row: 32 KB each
     __shared__ u32x4 As1[kABM * 8];
     __shared__ u32x4 Bs0[kABN * 8];  // 16 KB each
@@ -222,11 +260,21 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    // Block b runs on XCD b % 8: each XCD takes a contiguous run of logical
-    // tiles, n fastest, so the tiles it runs together share A rows.
-    const int total = mtiles * ntiles;
-    int logical = blockIdx.x;
-    if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    // Block b < nfull runs whole tile b, remapped: block b runs on XCD
+    // b % 8, and each XCD takes a contiguous run of logical tiles, n fastest,
+    // so the tiles it runs together share A rows.  Blocks past nfull run
+    // part sp of the K split of tile nfull + (b - nfull) / tsplits.
+    const int b = blockIdx.x;
+    int logical = b, sp = 0, g_lo = 0, g_hi = G;
+    if (b < nfull) {
+        if ((nfull & 7) == 0) logical = (b & 7) * (nfull >> 3) + (b >> 3);
+    } else {
+        const int j = b - nfull;
+        logical = nfull + j / tsplits;
+        sp = j - (j / tsplits) * tsplits;
+        g_lo = (int)((int64_t)G * sp / tsplits);
+        g_hi = (int)((int64_t)G * (sp + 1) / tsplits);
+    }
     const int bm = logical / ntiles;
     const int bn = logical - bm * ntiles;
     const int64_t m0 = (int64_t)bm * kABM;
@@ -247,7 +295,7 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
         aoff[u] = (uint32_t)(min(row, mlim) * K + 16 * chunk);
     }
     auto dma_a = [&](int g, u32x4 *dst) __attribute__((always_inline)) {
-        g = min(g, G - 1);
+        g = min(g, g_hi - 1);
         const int8_t *src = A_blk + (int64_t)g * kGroup;
 #pragma unroll
         for (int u = 0; u < AU; ++u)
@@ -290,7 +338,7 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
             }
 
     auto fetch_b = [&](int g) __attribute__((always_inline)) {  // clamped to the last group
-        g = min(g, G - 1);
+        g = min(g, g_hi - 1);
 #pragma unroll
         for (int i = 0; i < kAQ; ++i)
             load_quarter<WL, B>(bslot0 + (int64_t)g * bstep, bj + kQStep * i, breg[i]);
@@ -350,13 +398,13 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
         }
     };
 
-    // Prologue: group 0's A and codes in buffer 0, group 1's codes in
-    // registers.
-    dma_a(0, As0);
-    fetch_b(0);
+    // Prologue: group g_lo's A and codes in buffer 0, group g_lo + 1's codes
+    // in registers.
+    dma_a(g_lo, As0);
+    fetch_b(g_lo);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     store_b(Bs0, Ss[0]);
-    fetch_b(1);
+    fetch_b(g_lo + 1);
 
     // Each group runs in two phases of 8 MFMA slots: phase 0 runs block row
     // 0 (blocks (0, 0), (0, 1)) over the group's four k-steps and folds
@@ -420,12 +468,12 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
 #pragma unroll
         for (int j = 0; j < 2; ++j) sq_prev[j] = sq[j];
     };
-    int g = 0;
-    for (; g + 1 < G; g += 2) {
+    int g = g_lo;
+    for (; g + 1 < g_hi; g += 2) {
         group(g, std::integral_constant<int, 0>{});
         group(g + 1, std::integral_constant<int, 1>{});
     }
-    if (g < G) group(g, std::integral_constant<int, 0>{});
+    if (g < g_hi) group(g, std::integral_constant<int, 0>{});
     // The last group's block row 1.
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -433,7 +481,11 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
         for (int q = 0; q < 4; ++q) fold4(1, j, q, sq_prev[j]);
 
     // Output register r of block (i, j): row 8 (r / 4) + 4 (lane / 32) + r % 4,
-    // column lane % 32.
+    // column lane % 32.  A part of a split tile stores its fp32 sums (before
+    // the s_a factor) at [part][split tile][row of the tile][column].
+    float *pt = nullptr;
+    if (b >= nfull)
+        pt = part + ((int64_t)sp * (mtiles * ntiles - nfull) + (logical - nfull)) * (kABM * kABN);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -443,6 +495,10 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
                 if (m < M && n < N) {
+                    if (pt) {
+                        pt[(m - m0) * kABN + (n - n0)] = tot[i][j][r];
+                        continue;
+                    }
                     const float y = sa[m] * tot[i][j][r];
                     if (out_f32)
                         static_cast<float *>(Y)[m * N + n] = y;
@@ -453,24 +509,71 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
         }
 }
 
+// The split tiles' outputs: thread t takes 4 consecutive columns of one row
+// of split tile t / (kABM kABN / 4), adds the parts' sums in part order and
+// applies s_a, as the whole-tile epilogue does.
+__global__ __launch_bounds__(256) void a8_tail_reduce_kernel(const float *__restrict__ part,
+                                                             const float *__restrict__ sa,
+                                                             int splits, int nfull, int nsplit,
+                                                             int ntiles, int M, int N,
+                                                             void *__restrict__ Y, bool out_f32) {
+    constexpr int kQuads = kABM * kABN / 4;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int ts = (int)(t / kQuads);
+    if (ts >= nsplit) return;
+    const int e = (int)(t - (int64_t)ts * kQuads) * 4;
+    const int tile = nfull + ts;
+    const int bm = tile / ntiles, bn = tile - (tile / ntiles) * ntiles;
+    const int64_t m = (int64_t)bm * kABM + e / kABN;
+    const int64_t n = (int64_t)bn * kABN + e % kABN;
+    if (m >= M || n >= N) return;
+    const int64_t stride = (int64_t)nsplit * (kABM * kABN);  // floats from one part to the next
+    const float *p = part + (int64_t)ts * (kABM * kABN) + e;
+    float acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = p[c];
+    for (int s = 1; s < splits; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += p[s * stride + c];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (n + c >= N) break;
+        const float y = sa[m] * acc[c];
+        if (out_f32)
+            static_cast<float *>(Y)[m * N + n + c] = y;
+        else
+            static_cast<uint16_t *>(Y)[m * N + n + c] = f32_to_bf16_rne(y);
+    }
+}
+
 template <int B, bool ZP>
 static hipError_t launch_gemm_a8_b(const int8_t *Aq, const float *sa, int64_t M, int64_t N,
                                    int64_t K, const void *W, bool tiled, const uint16_t *scales,
-                                   const uint8_t *zeros, void *Y, bool out_f32,
+                                   const uint8_t *zeros, void *Y, bool out_f32, float *part,
                                    hipStream_t stream) {
     const int G = (int)(K / kGroup);
     const int mtiles = (int)((M + kABM - 1) / kABM);
     const int ntiles = (int)((N + kABN - 1) / kABN);
-    const dim3 grid((unsigned)(mtiles * ntiles));
+    const A8Plan p = a8_plan(M, N, K);
+    const int nsplit = p.tiles - p.full;
+    const dim3 grid((unsigned)(p.full + nsplit * p.splits));
     if (tiled) {
         TiledW wl{static_cast<const uint8_t *>(W), G, B};
         hipLaunchKernelGGL((gemm_a8_kernel<TiledW, B, ZP>), grid, dim3(64 * kAW), 0, stream, Aq, sa,
-                           (int)M, (int)N, (int)K, wl, zeros, Y, out_f32, mtiles, ntiles);
+                           (int)M, (int)N, (int)K, wl, zeros, Y, out_f32, mtiles, ntiles,
+                           p.full, p.splits, part);
     } else {
         DenseW wl{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B};
         hipLaunchKernelGGL((gemm_a8_kernel<DenseW, B, ZP>), grid, dim3(64 * kAW), 0, stream, Aq, sa,
-                           (int)M, (int)N, (int)K, wl, zeros, Y, out_f32, mtiles, ntiles);
+                           (int)M, (int)N, (int)K, wl, zeros, Y, out_f32, mtiles, ntiles,
+                           p.full, p.splits, part);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit == 0) return e;
+    const int64_t threads = (int64_t)nsplit * (kABM * kABN / 4);
+    hipLaunchKernelGGL(a8_tail_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       0, stream, part, sa, p.splits, p.full, nsplit, ntiles, (int)M, (int)N, Y,
+                       out_f32);
     return hipGetLastError();
 }
 
@@ -480,6 +583,8 @@ hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, co
     int8_t *Aq = reinterpret_cast<int8_t *>(static_cast<uint8_t *>(ws) + kWsScratchOffset);
     float *sa = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset +
                                           align256(M * K));
+    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kWsScratchOffset +
+                                            align256(M * K) + align256(M * 4));
     // b = 4 takes the (0,2,4,6,1,3,5,7) k order of its widening; others the natural one.
     if (b == 4)
         hipLaunchKernelGGL((quant_act_kernel<true>), dim3((unsigned)M), dim3(256), 0, stream, A,
@@ -492,30 +597,30 @@ hipError_t launch_gemm_a8(const uint16_t *A, int64_t M, int64_t N, int64_t K, co
     if (zeros) {  // b = 4 only (checked at the boundary)
         if (b != 4) return hipErrorInvalidValue;
         return launch_gemm_a8_b<4, true>(Aq, sa, M, N, K, W, tiled, scales, zeros, Y, out_f32,
-                                         stream);
+                                         part, stream);
     }
     switch (b) {
         case 2:
             return launch_gemm_a8_b<2, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
-                                              out_f32, stream);
+                                              out_f32, part, stream);
         case 3:
             return launch_gemm_a8_b<3, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
-                                              out_f32, stream);
+                                              out_f32, part, stream);
         case 4:
             return launch_gemm_a8_b<4, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
-                                              out_f32, stream);
+                                              out_f32, part, stream);
         case 5:
             return launch_gemm_a8_b<5, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
-                                              out_f32, stream);
+                                              out_f32, part, stream);
         case 6:
             return launch_gemm_a8_b<6, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
-                                              out_f32, stream);
+                                              out_f32, part, stream);
         case 7:
             return launch_gemm_a8_b<7, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
-                                              out_f32, stream);
+                                              out_f32, part, stream);
         case 8:
             return launch_gemm_a8_b<8, false>(Aq, sa, M, N, K, W, tiled, scales, nullptr, Y,
-                                              out_f32, stream);
+                                              out_f32, part, stream);
     }
     return hipErrorInvalidValue;
 }
