@@ -217,7 +217,7 @@ int wq_gemm(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_
  * streams, or host threads without ordering) race and must not be issued;
  * calls ordered on one stream are safe.  The first call on a device that
  * needs scratch also enqueues a small kernel that clears its counters. */
-#define WQ_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+#define WQ_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
 int wq_gemm_noalloc(const uint16_t *A_d, int64_t M, int64_t N, int64_t K, const void *W_d,
                     int layout, const uint16_t *scales_d, const uint8_t *zeros_d, int b,
                     int group, uint16_t *Y_d, void *stream);

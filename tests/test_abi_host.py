@@ -135,12 +135,12 @@ def test_gemm_refuses_k_beyond_32bit_tile_offsets():
 
 def test_noalloc_refuses_beyond_static_scratch():
     # wq_gemm_noalloc refuses, before any device work, a problem whose
-    # split-K scratch exceeds the static per-GPU array (32 MiB, as the header
+    # split-K scratch exceeds the static per-GPU array (64 MiB, as the header
     # states); its argument checks are those of wq_gemm.
     with open(wq.header_path) as f:
         m = re.search(r"#define WQ_NOALLOC_SCRATCH_BYTES \(\(int64_t\)(\d+) << (\d+)\)", f.read())
     assert m and int(m.group(1)) << int(m.group(2)) == wq.WQ_NOALLOC_SCRATCH_BYTES
-    N, K = 131072, 5120
+    N, K = 131072, 65536  # 16 K splits of 16 rows over 131072 columns: 134 MB
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 16, N, K, 6) > wq.WQ_NOALLOC_SCRATCH_BYTES
     lib = wq._load()
     p = ctypes.c_void_p(ALIGNED)
@@ -271,6 +271,35 @@ def test_a8_workspace_holds_the_tail_parts():
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 2304, 17408, 5120, 4) == base(2304, 5120)
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 256, 17408, 5120, 4) == base(256, 5120)
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, 300, 16500, 512, 4) == base(300, 512)
+
+
+def test_prefill_workspace_holds_the_tail_parts():
+    # The prefill layer splits the tiles of a last round at most a quarter
+    # full, or at most half full with 64 groups or more (256 tiles of
+    # 256 x 128 per round, 512 of 64 x 128), into up to 4 K parts of at least
+    # 8 groups; their fp32 partials follow the counter region.  At most one
+    # round of parts, so always within the static array of the
+    # no-allocation entry point.
+    tile = 256 * 128 * 4
+    Z = wq.WORKSPACE_ZERO_BYTES
+    # M = 4096, 17408 -> 5120: 640 tiles, 128 of 136 groups in the last
+    # round, 2 parts; 5120 -> 17408: 2176 tiles, 128 of 40 groups, none.
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 4096, 5120, 17408, 6) == Z + 128 * 2 * tile
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 4096, 17408, 5120, 6) == 0
+    # Both edges ragged: 520 tiles (8 in the last round) at 32 groups, 4
+    # parts; 384 tiles (128: the whole last row of tiles) at 64 groups, 2.
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 800, 16590, 4096, 3) == Z + 8 * 4 * tile
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 556, 16334, 8192, 6) == Z + 128 * 2 * tile
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 556, 16334, 2048, 6) == 0
+    # Whole rounds, a last round over half full, too few groups, or fewer
+    # tiles than 1.5 rounds (the uniform split's domain): no tail parts.
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 8192, 4096, 5120, 6) == 0      # 1024 tiles
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 6144, 17408, 5120, 6) == 0     # 3264: 192 last
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 800, 16590, 1024, 6) == 0      # 8 groups
+    two = 2 * ((300 * 16590 + 63) // 64 * 64) * 4  # 260 tiles: a uniform 2-way split
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 300, 16590, 2048, 6) == Z + two
+    for M, N, K in ((4096, 5120, 17408), (800, 16590, 4096), (556, 16334, 8192)):
+        assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, M, N, K, 6) <= wq.WQ_NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_zero_region_constant():

@@ -181,6 +181,32 @@ def test_gemm_prefill_k_split(M, N, K, b, layout):
     np.testing.assert_array_equal(Layer(w, layout).gemm(), Y)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("M,N,K,b,bn0", [(800, 16590, 4096, 3, 122), (556, 16334, 8192, 6, 0)],
+                         ids=["4parts", "2parts"])
+def test_gemm_prefill_tail_split(M, N, K, b, bn0, layout):
+    # Tiles of 256 x 128 with both edges ragged: 4 x 130 = 520 tiles, whose
+    # last round of 8 (row tile 3, column tiles 122 .. 129) runs as 4 K parts
+    # of 8 groups, or 3 x 128 = 384 tiles, whose last round is the whole last
+    # row of tiles, as 2 parts of 32 groups.  Every output of the split tiles
+    # (of the first and last three of that row), and a sample of the others,
+    # against the oracle; a bitwise repeat.
+    w = _workload(M, N, K, b, seed=980 + b)
+    packed = oracle.pack(w.codes, b)
+    m0 = (M - 1) // 256 * 256
+    cols = np.arange(bn0 * 128, N)
+    if len(cols) > 2048:  # the first three and the last three column tiles
+        cols = np.concatenate([cols[:384], cols[-(N - (N - 1) // 128 * 128) - 256:]])
+    tm, tn = np.meshgrid(np.arange(m0, M), cols, indexing="ij")
+    si, sj = sample_points(M, N, 2000, seed=17 + b)
+    mi = np.concatenate([tm.ravel(), si])
+    ni = np.concatenate([tn.ravel(), sj])
+    y_ref, mag = oracle.wna16_points(w.A, packed, w.scales, b, mi, ni)
+    Y = Layer(w, layout).gemm()
+    assert_wna16(Y[mi, ni], y_ref, mag, "prefill tail split M=%d b=%d" % (M, b))
+    np.testing.assert_array_equal(Layer(w, layout).gemm(), Y)
+
+
 @pytest.mark.parametrize("shape", [(5120, 17408), (17408, 5120)], ids=["up", "down"])
 def test_gemm_prefill_full_shape_sampled(shape):
     K, N = shape

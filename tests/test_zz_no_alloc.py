@@ -6,7 +6,8 @@ for bit; each is also held to the oracle's bound
 Every case makes two calls in a row, the second on a smaller input, so the
 second call runs on the scratch the first one left behind: a K split across
 workgroups at decode batch sizes (tickets and partials in the scratch), a K
-split in prefill (partials), and the one-row decode kernel (no scratch)."""
+split in prefill (partials), the prefill split of a last round's tiles
+(partials), and the one-row decode kernel (no scratch)."""
 import numpy as np
 import pytest
 import torch
@@ -47,6 +48,7 @@ CASES = {
     "decode_split_k": [((4, 4096, 5120), (2, 1024, 2560)), 6],
     "decode_split_k_m16": [((16, 2048, 17408), (9, 512, 5120)), 5],
     "prefill_split_k": [((300, 256, 5120), (100, 256, 2560)), 6],
+    "prefill_tail_split": [((800, 16590, 4096), (790, 16420, 4096)), 6],
     "one_row": [((1, 4352, 5120), (1, 640, 1280)), 7],
 }
 

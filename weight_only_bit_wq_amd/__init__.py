@@ -46,7 +46,7 @@ WQ_ERR_UNSUPPORTED_DEVICE = 8
 WQ_ERR_HIP = 9
 WQ_ERR_ZERO_POINTS = 10
 WQ_ERR_SCRATCH_LIMIT = 11
-WQ_NOALLOC_SCRATCH_BYTES = 32 << 20
+WQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 WQ_LAYOUT_DENSE = 0
 WQ_LAYOUT_TILED = 1

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
                                                       uint16_t *__restrict__ Y, int mtiles,
                                                       int ntiles, int splits,
                                                       float *__restrict__ part, int64_t mnp,
-                                                      const GT gt) {
+                                                      int nfull, int tsplits, const GT gt) {
     static_assert(TM == kPM || TM == 64, "m-tile of 256 or 64 rows");
     constexpr int NW = TM == kPM ? 8 : 4;  // waves
     constexpr bool kSmall = TM != kPM;
@@ -116,16 +116,30 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
 
     // Block b runs on XCD b % 8: each XCD gets a contiguous run of logical
     // tiles, n fastest, so the tiles an XCD runs together share A rows.
+    // With a uniform K split (splits > 1) the logical index is split-major.
+    // With a tail split (tsplits > 1) blocks past nfull run part sp of the K
+    // split of tile nfull + (b - nfull) / tsplits, and only the first nfull
+    // blocks are remapped.
     const int tiles = mtiles * ntiles;
-    const int total = tiles * splits;
-    int logical = blockIdx.x;
-    if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-    const int sp = logical / tiles;
-    const int tile = logical - sp * tiles;
+    const bool tail = tsplits > 1 && (int)blockIdx.x >= nfull;
+    int sp, tile, g_lo, g_hi;
+    if (tail) {
+        const int j = (int)blockIdx.x - nfull;
+        tile = nfull + j / tsplits;
+        sp = j - (j / tsplits) * tsplits;
+        g_lo = (int)(((int64_t)G * sp) / tsplits);
+        g_hi = (int)(((int64_t)G * (sp + 1)) / tsplits);
+    } else {
+        const int total = tsplits > 1 ? nfull : tiles * splits;
+        int logical = blockIdx.x;
+        if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+        sp = logical / tiles;
+        tile = logical - sp * tiles;
+        g_lo = (int)(((int64_t)G * sp) / splits);
+        g_hi = (int)(((int64_t)G * (sp + 1)) / splits);
+    }
     const int bm = tile / ntiles;
     const int bn = tile - bm * ntiles;
-    const int g_lo = (int)(((int64_t)G * sp) / splits);
-    const int g_hi = (int)(((int64_t)G * (sp + 1)) / splits);
     int64_t m0 = (int64_t)bm * TM;
     if constexpr (GT::kGrouped) {
         m0 = gt.m0[bm];
@@ -542,6 +556,10 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // Output element r of block i: row 8(r/4) + 4h + r%4, column lane%32.
+    // A tail part stores its fp32 sums at [part][tail tile][row of the
+    // tile][column].
+    float *pt = nullptr;
+    if (tail) pt = part + ((int64_t)sp * (tiles - nfull) + (tile - nfull)) * (TM * kPN);
 #pragma unroll
     for (int i = 0; i < (kSmall ? 2 : 4); ++i) {
         const int64_t n = n0 + 32 * wn + c32;
@@ -549,13 +567,39 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
         for (int r = 0; r < 16; ++r) {
             const int64_t m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
             if (m < M && n < N) {
-                if (splits == 1)
+                if (pt)
+                    pt[(m - m0) * kPN + (n - n0)] = tot[i][r];
+                else if (splits == 1)
                     Y[m * N + n] = f32_to_bf16_rne(tot[i][r]);
                 else
                     part[(int64_t)sp * mnp + m * N + n] = tot[i][r];
             }
         }
     }
+}
+
+// The tail tiles' outputs: thread t takes 4 consecutive columns of one row of
+// tail tile t / (TM kPN / 4) and adds the parts' sums in part order.
+__global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
+        const float *__restrict__ part, int tsplits, int nfull, int ntail, int ntiles, int tm,
+        int M, int N, uint16_t *__restrict__ Y) {
+    const int quads = tm * kPN / 4;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int ts = (int)(t / quads);
+    if (ts >= ntail) return;
+    const int e = (int)(t - (int64_t)ts * quads) * 4;
+    const int tile = nfull + ts;
+    const int bm = tile / ntiles, bn = tile - (tile / ntiles) * ntiles;
+    const int64_t m = (int64_t)bm * tm + e / kPN;
+    const int64_t n = (int64_t)bn * kPN + e % kPN;
+    if (m >= M || n >= N) return;
+    const int64_t stride = (int64_t)ntail * tm * kPN;  // floats from one part to the next
+    const float *p = part + (int64_t)ts * tm * kPN + e;
+    f32x4_t acc = *reinterpret_cast<const f32x4_t *>(p);
+    for (int s = 1; s < tsplits; ++s) acc += *reinterpret_cast<const f32x4_t *>(p + s * stride);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (n + c < N) Y[m * N + n + c] = f32_to_bf16_rne(acc[c]);
 }
 
 // Y = bf16(sum over splits of part[s]) in split order (deterministic); four
@@ -614,11 +658,60 @@ static int prefill_splits(int64_t M, int64_t N, int64_t K) {
 
 static int64_t prefill_mnp(int64_t M, int64_t N) { return (M * N + 63) / 64 * 64; }
 
-// Workspace: the shared counter region (unused here), then (K split) the
-// fp32 partial outputs, split s at s * mnp floats; nothing without a split.
+// Tail balance.  With whole rounds of workgroups and a last round at most a
+// quarter full, or at most half full with long tiles (64 groups or more;
+// M = 4096 at 17408 -> 5120 is 640 tiles, 2 rounds and 128 tiles of 136
+// groups), the last round's tiles are split along K into up to 4 parts of
+// at least 8 groups, which fill that round with shorter workgroups; the
+// parts store fp32 sums and a second kernel adds them in part order.
+// Measured on MI355X, b = 6, 17408 -> 5120: M = 3584 / 4096 / 5120 0.75 /
+// 0.76 / 0.97 ms -> 0.67-0.68 / 0.71 / 0.86-0.87; 5120 -> 17408 at M = 4096
+// (2176 tiles, 128 of 40 groups in the last round) was no faster split, so
+// it is not.  The parts of one round hold at most 256 tiles' outputs (32 MiB
+// in fp32).  Never with a forced uniform split; WQ_PREFILL_TAIL=0 turns it
+// off.
+struct PrefillPlan {
+    int tm;       // m-tile rows
+    int tiles;    // m-tiles x n-tiles
+    int splits;   // uniform K split (1: none)
+    int full;     // tiles run whole; the others run as tsplits K parts
+    int tsplits;  // K parts of a tail tile (1: no tail split)
+    int64_t ws_bytes;
+};
+static PrefillPlan prefill_plan(int64_t M, int64_t N, int64_t K) {
+    PrefillPlan p;
+    p.tm = prefill_tile_m(M);
+    p.tiles = (int)(((M + p.tm - 1) / p.tm) * ((N + kPN - 1) / kPN));
+    p.splits = prefill_splits(M, N, K);
+    p.full = p.tiles;
+    p.tsplits = 1;
+    p.ws_bytes = p.splits > 1 ? kWsScratchOffset + p.splits * prefill_mnp(M, N) * 4 : 0;
+    static const bool tail_off = [] {
+        const char *e = std::getenv("WQ_PREFILL_TAIL");
+        return e && std::atoi(e) == 0;
+    }();
+    static const bool forced = std::getenv("WQ_PREFILL_SPLITS") != nullptr;
+    const int slots = p.tm == kPM ? 256 : 512;
+    const int G = (int)(K / kGroup);
+    const int r = p.tiles % slots;
+    const bool sparse = 4 * r <= slots || (2 * r <= slots && G >= 64);
+    if (!tail_off && !forced && p.splits == 1 && p.tiles >= slots && r > 0 && sparse) {
+        const int s = std::min(std::min(slots / r, 4), G / 8);
+        const int64_t bytes = kWsScratchOffset + (int64_t)r * s * p.tm * kPN * 4;
+        if (s >= 2) {
+            p.full = p.tiles - r;
+            p.tsplits = s;
+            p.ws_bytes = bytes;
+        }
+    }
+    return p;
+}
+
+// Workspace: the shared counter region (unused here), then the fp32 partial
+// outputs: uniform K split, split s at s * mnp floats; tail split, part s of
+// tail tile t at (s * tail tiles + t) * tm * 128 floats; nothing otherwise.
 int64_t prefill_ws_bytes(int64_t M, int64_t N, int64_t K, int) {
-    const int s = prefill_splits(M, N, K);
-    return s > 1 ? kWsScratchOffset + s * prefill_mnp(M, N) * 4 : 0;
+    return prefill_plan(M, N, K).ws_bytes;
 }
 
 template <int B, bool ZP>
@@ -626,32 +719,43 @@ static hipError_t prefill_bz(const uint16_t *A, int64_t M, int64_t N, int64_t K,
                              bool tiled, const uint16_t *scales, const uint8_t *zeros,
                              uint16_t *Y, void *ws, hipStream_t stream) {
     const int G = (int)(K / kGroup);
-    const int splits = prefill_splits(M, N, K);
-    float *part = splits > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
-                                                         kWsScratchOffset)
-                             : nullptr;
+    const PrefillPlan pl = prefill_plan(M, N, K);
+    const int splits = pl.splits;
+    float *part = pl.ws_bytes > 0 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
+                                                              kWsScratchOffset)
+                                  : nullptr;
     hipError_t e = hipSuccess;
-    const int tm = prefill_tile_m(M);
+    const int tm = pl.tm;
     const int mtiles = (int)((M + tm - 1) / tm);
     const int ntiles = (int)((N + kPN - 1) / kPN);
-    const dim3 grid((unsigned)(mtiles * ntiles * splits));
+    const int ntail = pl.tiles - pl.full;
+    const dim3 grid((unsigned)(pl.full * splits + ntail * pl.tsplits));
     auto run = [&](auto wl) {
         typedef decltype(wl) WL;
         if (tm == kPM)
             hipLaunchKernelGGL((prefill_kernel<B, WL, ZP, NoGroups>), grid, dim3(512), 0, stream,
                                A, (int)M, (int)N, (int)K, wl, zeros, Y, mtiles, ntiles,
-                               splits, part, prefill_mnp(M, N), NoGroups{});
+                               splits, part, prefill_mnp(M, N), pl.full, pl.tsplits, NoGroups{});
         else
             hipLaunchKernelGGL((prefill_kernel<B, WL, ZP, NoGroups, kPrefillSmallTileM>), grid,
                                dim3(256), 0, stream, A, (int)M, (int)N, (int)K, wl, zeros,
-                               Y, mtiles, ntiles, splits, part, prefill_mnp(M, N), NoGroups{});
+                               Y, mtiles, ntiles, splits, part, prefill_mnp(M, N), pl.full,
+                               pl.tsplits, NoGroups{});
     };
     if (tiled)
         run(TiledW{static_cast<const uint8_t *>(W), G, B});
     else
         run(DenseW{static_cast<const uint8_t *>(W), scales, (int64_t)16 * B * G, G, B});
     e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
+    if (e != hipSuccess) return e;
+    if (ntail > 0) {
+        const int64_t threads = (int64_t)ntail * tm * kPN / 4;
+        hipLaunchKernelGGL(prefill_tail_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
+                           dim3(256), 0, stream, part, pl.tsplits, pl.full, ntail, ntiles, tm,
+                           (int)M, (int)N, Y);
+        return hipGetLastError();
+    }
+    if (splits == 1) return e;
     const int64_t MN = M * N;
     const int64_t threads = (MN + 3) / 4;
     hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
@@ -682,11 +786,11 @@ static hipError_t prefill_grouped_bz(const uint16_t *A, int64_t M, int64_t N, in
         hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, GroupTable, kPrefillSmallTileM>),
                            dim3((unsigned)(gt.n * ntiles)), dim3(256), 0, stream, A, (int)M,
                            (int)N, (int)K, wl, zeros, Y, gt.n, ntiles, 1, (float *)nullptr,
-                           (int64_t)0, gt);
+                           (int64_t)0, gt.n * ntiles, 1, gt);
     else if (tile_m == kPrefillTileM)
         hipLaunchKernelGGL((prefill_kernel<B, TiledW, ZP, GroupTable>), dim3((unsigned)(gt.n * ntiles)),
                            dim3(512), 0, stream, A, (int)M, (int)N, (int)K, wl, zeros, Y,
-                           gt.n, ntiles, 1, (float *)nullptr, (int64_t)0, gt);
+                           gt.n, ntiles, 1, (float *)nullptr, (int64_t)0, gt.n * ntiles, 1, gt);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
