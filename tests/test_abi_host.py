@@ -291,13 +291,17 @@ def test_prefill_workspace_holds_the_tail_parts():
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 800, 16590, 4096, 3) == Z + 8 * 4 * tile
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 556, 16334, 8192, 6) == Z + 128 * 2 * tile
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 556, 16334, 2048, 6) == 0
-    # Whole rounds, a last round over half full, too few groups, or fewer
-    # tiles than 1.5 rounds (the uniform split's domain): no tail parts.
+    # Whole rounds, a last round over half full, or too few groups: no tail
+    # parts.
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 8192, 4096, 5120, 6) == 0      # 1024 tiles
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 6144, 17408, 5120, 6) == 0     # 3264: 192 last
     assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 800, 16590, 1024, 6) == 0      # 8 groups
-    two = 2 * ((300 * 16590 + 63) // 64 * 64) * 4  # 260 tiles: a uniform 2-way split
-    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 300, 16590, 2048, 6) == Z + two
+    # Between one and 1.5 rounds the tail split replaces the uniform 2-way
+    # split of the whole output: 260 tiles, 4 in 2 parts.
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 300, 16590, 2048, 6) == Z + 4 * 2 * tile
+    # Fewer tiles than a round: the uniform split (2 parts of the whole output).
+    two = 2 * ((300 * 12800 + 63) // 64 * 64) * 4  # 200 tiles
+    assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 300, 12800, 2048, 6) == Z + two
     for M, N, K in ((4096, 5120, 17408), (800, 16590, 4096), (556, 16334, 8192)):
         assert wq.wq_workspace_bytes(wq.WQ_OP_GEMM, M, N, K, 6) <= wq.WQ_NOALLOC_SCRATCH_BYTES
 

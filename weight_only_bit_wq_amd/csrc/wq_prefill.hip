@@ -638,7 +638,8 @@ static int prefill_tile_m(int64_t M) {
 // split; between 3/4 and 3/2 of the slots, 2 splits (the second round of
 // workgroups would otherwise run nearly empty).  Measured at M = 512:
 // 17408 -> 5120 (80 tiles) best at 3 splits, 174 vs 365 us unsplit;
-// 5120 -> 17408 (272 tiles) 219 us at 2 splits vs 240 us.
+// 5120 -> 17408 (272 tiles) 219 us at 2 splits vs 240 us (from one round
+// up, the tail split below replaces this one).
 // WQ_PREFILL_SPLITS forces a split count.
 static int prefill_splits(int64_t M, int64_t N, int64_t K) {
     const int tm = prefill_tile_m(M);
@@ -667,7 +668,9 @@ static int64_t prefill_mnp(int64_t M, int64_t N) { return (M * N + 63) / 64 * 64
 // Measured on MI355X, b = 6, 17408 -> 5120: M = 3584 / 4096 / 5120 0.75 /
 // 0.76 / 0.97 ms -> 0.67-0.68 / 0.71 / 0.86-0.87; 5120 -> 17408 at M = 4096
 // (2176 tiles, 128 of 40 groups in the last round) was no faster split, so
-// it is not.  The parts of one round hold at most 256 tiles' outputs (32 MiB
+// it is not.  Between one and 1.5 rounds it replaces the uniform 2-way
+// split: 5120 -> 17408 at M = 300 and 512 (272 tiles) 134 / 148 -> 106 /
+// 117 us, 17408 -> 5120 at M = 1792 (280 tiles) 399 -> 340 us.  The parts of one round hold at most 256 tiles' outputs (32 MiB
 // in fp32).  Never with a forced uniform split; WQ_PREFILL_TAIL=0 turns it
 // off.
 struct PrefillPlan {
@@ -694,11 +697,15 @@ static PrefillPlan prefill_plan(int64_t M, int64_t N, int64_t K) {
     const int slots = p.tm == kPM ? 256 : 512;
     const int G = (int)(K / kGroup);
     const int r = p.tiles % slots;
+    // Between one and 1.5 rounds the tail split replaces the uniform one
+    // (whose partials cover the whole output).
     const bool sparse = 4 * r <= slots || (2 * r <= slots && G >= 64);
-    if (!tail_off && !forced && p.splits == 1 && p.tiles >= slots && r > 0 && sparse) {
+    const bool band = p.splits > 1 && 2 * p.tiles < 3 * slots;
+    if (!tail_off && !forced && p.tiles >= slots && r > 0 && (band || (p.splits == 1 && sparse))) {
         const int s = std::min(std::min(slots / r, 4), G / 8);
         const int64_t bytes = kWsScratchOffset + (int64_t)r * s * p.tm * kPN * 4;
         if (s >= 2) {
+            p.splits = 1;
             p.full = p.tiles - r;
             p.tsplits = s;
             p.ws_bytes = bytes;
