@@ -529,12 +529,21 @@ __global__ __launch_bounds__(256) void a8_tail_reduce_kernel(const float *__rest
     if (m >= M || n >= N) return;
     const int64_t stride = (int64_t)nsplit * (kABM * kABN);  // floats from one part to the next
     const float *p = part + (int64_t)ts * (kABM * kABN) + e;
-    float acc[4];
+    // All (at most 4) loads before the first add; indices past the last part
+    // repeat it and are not added.
+    float4 v[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = p[c];
-    for (int s = 1; s < splits; ++s)
+    for (int s = 0; s < 4; ++s) v[s] = *reinterpret_cast<const float4 *>(p + min(s, splits - 1) * stride);
+    float acc[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] += p[s * stride + c];
+    for (int s = 1; s < 4; ++s) {
+        if (s < splits) {
+            acc[0] += v[s].x;
+            acc[1] += v[s].y;
+            acc[2] += v[s].z;
+            acc[3] += v[s].w;
+        }
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         if (n + c >= N) break;

@@ -154,7 +154,9 @@ hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, con
 
 // One thread per 4 consecutive columns of one row: the splits' float4s
 // added in split order (the order and rounding of the in-kernel hand-off),
-// rounded to bf16 once.
+// rounded to bf16 once.  All loads go out before the first add (indices
+// past the last split repeat it and are not added): a loop of dependent
+// load-add steps took ~4 us at 5 splits, one memory round trip each.
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float *__restrict__ part,
                                                             int splits, int mt, int M, int N,
                                                             int npad, uint16_t *__restrict__ Y) {
@@ -165,13 +167,18 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float *__restr
     if (m >= M || n >= N) return;
     const float4 *p = reinterpret_cast<const float4 *>(part + (int64_t)m * npad + n);
     const int64_t step = (int64_t)mt * q;  // float4s from one split to the next
-    float4 acc = p[0];
-    for (int s = 1; s < splits; ++s) {
-        const float4 v = p[s * step];
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+    float4 v[kDecodeMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kDecodeMaxSplits; ++s) v[s] = p[min(s, splits - 1) * step];
+    float4 acc = v[0];
+#pragma unroll
+    for (int s = 1; s < kDecodeMaxSplits; ++s) {
+        if (s < splits) {
+            acc.x += v[s].x;
+            acc.y += v[s].y;
+            acc.z += v[s].z;
+            acc.w += v[s].w;
+        }
     }
     uint16_t *y = Y + (int64_t)m * N + n;
     y[0] = f32_to_bf16_rne(acc.x);

@@ -595,8 +595,16 @@ __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
     if (m >= M || n >= N) return;
     const int64_t stride = (int64_t)ntail * tm * kPN;  // floats from one part to the next
     const float *p = part + (int64_t)ts * tm * kPN + e;
-    f32x4_t acc = *reinterpret_cast<const f32x4_t *>(p);
-    for (int s = 1; s < tsplits; ++s) acc += *reinterpret_cast<const f32x4_t *>(p + s * stride);
+    // All (at most 4) loads before the first add; indices past the last part
+    // repeat it and are not added.
+    f32x4_t v[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        v[s] = *reinterpret_cast<const f32x4_t *>(p + min(s, tsplits - 1) * stride);
+    f32x4_t acc = v[0];
+#pragma unroll
+    for (int s = 1; s < 4; ++s)
+        if (s < tsplits) acc += v[s];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
         if (n + c < N) Y[m * N + n + c] = f32_to_bf16_rne(acc[c]);
@@ -610,8 +618,18 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__rest
                                                              uint16_t *__restrict__ Y) {
     const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= MN) return;
+    // Loads in batches of 8 issued before their adds (a loop of dependent
+    // load-add steps waits one memory round trip per split).
     f32x4_t acc = *reinterpret_cast<const f32x4_t *>(part + e);
-    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f32x4_t *>(part + s * mnp + e);
+    for (int s0 = 1; s0 < splits; s0 += 8) {
+        f32x4_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = *reinterpret_cast<const f32x4_t *>(part + min(s0 + i, splits - 1) * mnp + e);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (s0 + i < splits) acc += v[i];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         if (e + i < MN) Y[e + i] = f32_to_bf16_rne(acc[i]);
