@@ -155,8 +155,9 @@ hipError_t launch_decode(const uint16_t *A, int64_t M, int64_t N, int64_t K, con
 // One thread per 4 consecutive columns of one row: the splits' float4s
 // added in split order (the order and rounding of the in-kernel hand-off),
 // rounded to bf16 once.  All loads go out before the first add (indices
-// past the last split repeat it and are not added): a loop of dependent
-// load-add steps took ~4 us at 5 splits, one memory round trip each.
+// past the last split repeat it and are not added).  At M = 16 on the
+// 5120 -> 17408 layer the kernel takes ~4 us (5.6 MB read by one workgroup
+// per compute unit: about one launch and one memory round trip).
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float *__restrict__ part,
                                                             int splits, int mt, int M, int N,
                                                             int npad, uint16_t *__restrict__ Y) {

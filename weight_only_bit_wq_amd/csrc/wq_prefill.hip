@@ -618,8 +618,7 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__rest
                                                              uint16_t *__restrict__ Y) {
     const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= MN) return;
-    // Loads in batches of 8 issued before their adds (a loop of dependent
-    // load-add steps waits one memory round trip per split).
+    // Loads in batches of 8 issued before their adds.
     f32x4_t acc = *reinterpret_cast<const f32x4_t *>(part + e);
     for (int s0 = 1; s0 < splits; s0 += 8) {
         f32x4_t v[8];
