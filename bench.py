@@ -73,8 +73,13 @@ class DecodeLayer:
                    self.b, Y=self.Y, ws=self.ws)
 
 
-def graph_time(torch, fn, reps: int, warmup: int) -> float:
-    """Capture fn() once, replay warmup + reps times; seconds per replay."""
+def graph_time(torch, fn, reps: int, warmup: int, warm_s: float = 0.0) -> float:
+    """Capture fn() once, replay warmup + reps times; seconds per replay.
+    warm_s > 0: after the warmup replays, keep replaying (untimed) for about
+    warm_s seconds first.  A GEMM of ~1 ms measured right after the light
+    decode benches ran up to 20% slower over its first ten replays than
+    later in the same process (the shader clock rises under sustained
+    matrix load)."""
     fn()  # first call outside capture (device checks, lazy init)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -83,6 +88,14 @@ def graph_time(torch, fn, reps: int, warmup: int) -> float:
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
+    if warm_s > 0:
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        one = max(time.perf_counter() - t0, 1e-6)
+        for _ in range(int(warm_s / one) + 1):
+            g.replay()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
@@ -163,7 +176,7 @@ def bench_prefill(torch, wq, synth, reps: int):
         def fn():
             wq.wq_gemm(A, blob, wq.WQ_LAYOUT_TILED, None, N, 6, Y=Y)
 
-        t = graph_time(torch, fn, reps, 2)
+        t = graph_time(torch, fn, reps, 2, warm_s=0.05)
         tf = 2.0 * w.M * N * K / t / 1e12
         out[name] = {"M": w.M, "N": N, "K": K, "b": 6, "ms": t * 1e3, "TFLOP/s": tf,
                      "frac_of_peak": tf / BF16_PEAK_TFLOPS}
@@ -236,7 +249,7 @@ def bench_zero_points(torch, wq, synth, reps: int, copies: int):
         Y = torch.empty((4096, N), dtype=torch.bfloat16, device="cuda")
         for name, kw in (("symmetric", {}), ("zero_points", {"zeros": z})):
             t = graph_time(torch, lambda: wq.wq_gemm(A, blobs[0], wq.WQ_LAYOUT_TILED, None, N, b,
-                                                     Y=Y, **kw), max(2, reps // 4), 1)
+                                                     Y=Y, **kw), max(2, reps // 4), 1, warm_s=0.05)
             res["prefill_M4096_" + name] = {"ms": t * 1e3,
                                             "TFLOP/s": 2.0 * 4096 * N * K / t / 1e12}
         out["b%d" % b] = res
@@ -277,7 +290,7 @@ def bench_grouped(torch, wq, synth, reps: int):
             for off in offs:
                 wq.wq_gemm_grouped(A, W, eb, off, N, b, Y=Y)
 
-        t = graph_time(torch, fn, reps, 2) / calls
+        t = graph_time(torch, fn, reps, 2, warm_s=0.05) / calls
         active = float(np.mean([(np.diff(off) > 0).sum() for off in offs]))
         byts = active * algorithmic_bytes(0, N, K, b) + rows * K * 2 + rows * N * 2
         out[name] = {"experts": E, "active": active, "rows": rows, "us": t * 1e6,
@@ -475,8 +488,8 @@ def bench_w4a8(torch, wq, synth, reps: int):
         def f16():
             wq.wq_gemm(A, blob, wq.WQ_LAYOUT_TILED, None, w0.N, 4, Y=Y)
 
-        t8 = graph_time(torch, f8, reps, 2)
-        t16 = graph_time(torch, f16, reps, 2)
+        t8 = graph_time(torch, f8, reps, 2, warm_s=0.05)
+        t16 = graph_time(torch, f16, reps, 2, warm_s=0.05)
         ops = 2.0 * M * w0.N * w0.K
         out["M%d" % M] = {"ms": t8 * 1e3, "TOP/s": ops / t8 / 1e12,
                           "frac_of_int8_peak": ops / t8 / 1e12 / INT8_PEAK_TOPS,
@@ -494,9 +507,9 @@ def bench_w4a8(torch, wq, synth, reps: int):
     ws = torch.zeros(wq.wq_workspace_bytes(wq.WQ_OP_GEMM_A8, M, w0.N, w0.K, 8),
                      dtype=torch.uint8, device="cuda")
     t8 = graph_time(torch, lambda: wq.wq_gemm_a8(A, blob8, wq.WQ_LAYOUT_TILED, None, w0.N, 8,
-                                                 Y=Y, ws=ws), reps, 2)
+                                                 Y=Y, ws=ws), reps, 2, warm_s=0.05)
     t16 = graph_time(torch, lambda: wq.wq_gemm(A, blob8, wq.WQ_LAYOUT_TILED, None, w0.N, 8, Y=Y),
-                     reps, 2)
+                     reps, 2, warm_s=0.05)
     ops = 2.0 * M * w0.N * w0.K
     out["W8A8_M%d" % M] = {"ms": t8 * 1e3, "TOP/s": ops / t8 / 1e12,
                            "frac_of_int8_peak": ops / t8 / 1e12 / INT8_PEAK_TOPS,
@@ -610,7 +623,7 @@ def bench_stack(torch, wq, reps: int):
     for M in (1, 512):
         x = torch.from_numpy(synth.stack_input(M).view(np.int16)).cuda().view(torch.bfloat16)
         bufs = st.buffers(M)
-        t = graph_time(torch, lambda: st.forward(x, bufs), reps, 1)
+        t = graph_time(torch, lambda: st.forward(x, bufs), reps, 1, warm_s=0.05)
         if M == 1:
             bps = st.bytes(1) / t
             out["M1"] = {"ms": t * 1e3, "TB/s": bps / 1e12, "frac_of_hbm_peak": bps / 1e9 / HBM_PEAK_GBS}
