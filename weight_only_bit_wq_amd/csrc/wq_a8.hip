@@ -483,9 +483,56 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
     // Output register r of block (i, j): row 8 (r / 4) + 4 (lane / 32) + r % 4,
     // column lane % 32.  A part of a split tile stores its fp32 sums (before
     // the s_a factor) at [part][split tile][row of the tile][column].
-    float *pt = nullptr;
-    if (b >= nfull)
-        pt = part + ((int64_t)sp * (mtiles * ntiles - nfull) + (logical - nfull)) * (kABM * kABN);
+    const int64_t mw = m0 + wm * 64 + 4 * hh;  // row of register 0, block row 0
+    if (b >= nfull) {
+        float *pt = part + ((int64_t)sp * (mtiles * ntiles - nfull) + (logical - nfull)) *
+                                   (kABM * kABN);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t n = n0 + wn * 64 + 32 * j + r32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = mw + 32 * i + 8 * (r >> 2) + (r & 3);
+                    if (m < M && n < N) pt[(m - m0) * kABN + (n - n0)] = tot[i][j][r];
+                }
+            }
+        return;
+    }
+    // The s_a factors of the lane's 32 rows, all loaded before the first is
+    // used (rows 4 q .. 4 q + 3 of a block row are consecutive: one 16-byte
+    // load; past row M - 1 the loads read row M - 1).
+    float sv[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t m = mw + 32 * i + 8 * q;
+            if (m + 3 < M) {
+                const f32x4_t v = *reinterpret_cast<const f32x4_t *>(sa + m);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[i][4 * q + e] = v[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[i][4 * q + e] = sa[min(m + e, (int64_t)M - 1)];
+            }
+        }
+    if (!out_f32 && m0 + kABM <= M && n0 + kABN <= N) {
+        // A whole tile in bf16: each register's 64 values go to two 64-byte
+        // row runs; the row offset is wave-uniform, the lane's offset fixed.
+        uint16_t *Yw = static_cast<uint16_t *>(Y) + (m0 + wm * 64) * N + n0 + wn * 64;
+        const uint32_t lo = (uint32_t)(4 * hh) * (uint32_t)N + (uint32_t)r32;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    (Yw + (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * N + 32 * j)[lo] =
+                            f32_to_bf16_rne(sv[i][r] * tot[i][j][r]);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -493,13 +540,9 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
             const int64_t n = n0 + wn * 64 + 32 * j + r32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const int64_t m = mw + 32 * i + 8 * (r >> 2) + (r & 3);
                 if (m < M && n < N) {
-                    if (pt) {
-                        pt[(m - m0) * kABN + (n - n0)] = tot[i][j][r];
-                        continue;
-                    }
-                    const float y = sa[m] * tot[i][j][r];
+                    const float y = sv[i][r] * tot[i][j][r];
                     if (out_f32)
                         static_cast<float *>(Y)[m * N + n] = y;
                     else

@@ -560,6 +560,19 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     // tile][column].
     float *pt = nullptr;
     if (tail) pt = part + ((int64_t)sp * (tiles - nfull) + (tile - nfull)) * (TM * kPN);
+    if (!tail && splits == 1 && m0 + TM <= M && n0 + kPN <= N) {
+        // A whole tile: each register's 64 values go to two 64-byte row
+        // runs; the row offset is wave-uniform, the lane's offset fixed.
+        uint16_t *Yw = Y + (m0 + 128 * wm) * N + n0 + 32 * wn;
+        const uint32_t lo = (uint32_t)(4 * h) * (uint32_t)N + (uint32_t)c32;
+#pragma unroll
+        for (int i = 0; i < (kSmall ? 2 : 4); ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                (Yw + (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * N)[lo] =
+                        f32_to_bf16_rne(tot[i][r]);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < (kSmall ? 2 : 4); ++i) {
         const int64_t n = n0 + 32 * wn + c32;
