@@ -101,30 +101,28 @@ __device__ __forceinline__ uint32_t widen4(const uint32_t *w) {
 
 // Quarter q (dwords [B q, B q + B)) of the slot starting at `slot`, with q
 // wave-uniform: 16-byte loads when B % 4 == 0, 8-byte when B is even (a pair
-// never crosses a 16-byte chunk), else dwords.
+// never crosses a 16-byte chunk), else dwords.  Ordinary (temporal) loads:
+// every M-tile of the layer reads the same codes again.
 template <class WL, int B>
 __device__ __forceinline__ void load_quarter(const uint8_t *slot, int q, uint32_t *w) {
     const int d0 = B * q;
     if constexpr (B % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < B / 4; ++i) {
-            const u32x4 v = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(slot + WL::dword_off(d0 + 4 * i)));
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(slot + WL::dword_off(d0 + 4 * i));
             w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
         }
     } else if constexpr (B % 2 == 0) {
         typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int i = 0; i < B / 2; ++i) {
-            const u32x2 v = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x2 *>(slot + WL::dword_off(d0 + 2 * i)));
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(slot + WL::dword_off(d0 + 2 * i));
             w[2 * i] = v.x; w[2 * i + 1] = v.y;
         }
     } else {
 #pragma unroll
         for (int e = 0; e < B; ++e)
-            w[e] = __builtin_nontemporal_load(
-                reinterpret_cast<const uint32_t *>(slot + WL::dword_off(d0 + e)));
+            w[e] = *reinterpret_cast<const uint32_t *>(slot + WL::dword_off(d0 + e));
     }
 }
 
@@ -479,6 +477,9 @@ __global__ __launch_bounds__(64 * kAW) void gemm_a8_kernel(const int8_t *__restr
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) fold4(1, j, q, sq_prev[j]);
+    // Drain the (clamped, unused) loads issued for the groups after the last:
+    // no direct load may still be writing LDS when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // Output register r of block (i, j): row 8 (r / 4) + 4 (lane / 32) + r % 4,
     // column lane % 32.  A part of a split tile stores its fp32 sums (before
