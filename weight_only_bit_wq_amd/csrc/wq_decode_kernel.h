@@ -104,8 +104,8 @@ __device__ __forceinline__ void load_slot_regs(const WL &wl, int64_t nr, int g,
 // words are prepared in place (prep_runs).
 template <int B, bool ZP, bool I8>
 __device__ __forceinline__ float group_terms(uint32_t *w, const uint32_t *a, int z) {
-    uint32_t o[I8 ? 32 : 1];
-    prep_runs<B, ZP, I8, 4>(w, o);
+    uint32_t o[int8_words<B, ZP, I8>() ? 32 : 1];
+    prep_runs<B, ZP, I8, 4>(w, o, z);
     // All 64 activation pairs of the group come in with four wide scalar
     // loads issued together.
     typedef typename UVec<16>::type vec16;
@@ -194,8 +194,8 @@ __device__ __forceinline__ void load_slot_regs_mf(const WL &wl, int64_t nr, int 
 template <int B, int MT, bool ZP, bool I8>
 __device__ __forceinline__ void group_terms_mf(uint32_t *w, const u32x4 *av, int z, float *x) {
     constexpr int Q = MT / 4;
-    uint32_t o[I8 ? 32 : 1];
-    prep_runs<B, ZP, I8, 4>(w, o);
+    uint32_t o[int8_words<B, ZP, I8>() ? 32 : 1];
+    prep_runs<B, ZP, I8, 4>(w, o, z);
     f32x4_t d[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) d[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -245,8 +245,8 @@ __device__ __forceinline__ void transpose_quarters(uint32_t &x0, uint32_t &x1, u
 // unscaled; av[t] holds the lane's 8 activations of k-step t.
 template <int B, bool ZP, bool I8>
 __device__ __forceinline__ void group_terms_mf16(uint32_t *w, const u32x4 *av, int z, float *x) {
-    uint32_t o[I8 ? 32 : 1];
-    prep_runs<B, ZP, I8, 4>(w, o);
+    uint32_t o[int8_words<B, ZP, I8>() ? 32 : 1];
+    prep_runs<B, ZP, I8, 4>(w, o, z);
     f32x4_t d[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) d[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(const uint16_t *__restri
     constexpr bool MF = MT >= 4;
     constexpr bool MF16 = MT == 16;  // 16x16x32 blocks (4x4x4 below)
     constexpr bool I8 = WL::kTiled && int8_ready<B>() && !ZP;  // arranged runs
-    constexpr float kSInv = operand_scale_inv<B, I8>();
+    constexpr float kSInv = operand_scale_inv<B, I8, ZP>();
     __shared__ float red[W][MT][64];
 
     const int G = K / kGroup;
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(64 * kRowWaves, (TMAX > 0 || (B == 7 && !WL::kTiled
     constexpr int C = 64 / RW;
     constexpr int RO = kRowWaves / S;  // row sets per workgroup
     constexpr bool I8 = WL::kTiled && int8_ready<B>() && !ZP;  // arranged runs
-    constexpr float kSInv = operand_scale_inv<B, I8>();
+    constexpr float kSInv = operand_scale_inv<B, I8, ZP>();
     extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];
     __shared__ float red[S > 1 ? RO : 1][S][RW];
     const int G = K / kGroup;
@@ -662,8 +662,8 @@ __global__ __launch_bounds__(64 * kRowWaves, (TMAX > 0 || (B == 7 && !WL::kTiled
     auto compute = [&](int t, SlotRegs<B, 1> &r) __attribute__((always_inline)) {
         const int g = j + C * (S * t + sw);
         const int gc = min(g, G - 1);
-        uint32_t o[I8 ? 32 : 1];
-        prep_runs<B, ZP, I8, 4>(r.w, o);
+        uint32_t o[int8_words<B, ZP, I8>() ? 32 : 1];
+        prep_runs<B, ZP, I8, 4>(r.w, o, (int)r.z);
         f32x4_t d[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
         const uint8_t *ab = act_lds + gc * kRowActStride;
         RowChunks<B, ZP, I8, 0>::run(r.w, o, ab, (int)r.z, *reinterpret_cast<const u32x4 *>(ab),
@@ -710,7 +710,7 @@ __global__ __launch_bounds__(64 * kRowWaves, (TMAX > 0 || (B == 7 && !WL::kTiled
             const int g = j + C * (S * t + sw);
             const int gc = min(g, G - 1);
             uint32_t o[32];
-            prep_runs<B, ZP, true, 4>(r.w, o);
+            prep_runs<B, ZP, true, 4>(r.w, o, 0);
             const float sc = bf16_to_f32(r.s) * kSInv;
             if (t + 1 < T) load(t + 1, r);
             f32x4_t d[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};

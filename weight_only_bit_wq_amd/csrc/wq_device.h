@@ -228,6 +228,43 @@ __device__ __forceinline__ uint32_t zpair(const uint32_t *w, int z) {
     return pack_bf16x2(zcode_f32<B, 2 * P>(w, z), zcode_f32<B, 2 * P + 1>(w, z));
 }
 
+// b = 4 with a zero point, a run at a time: the nibbles of word d spread to
+// bytes (even codes from the low nibbles into o[2d], odd from the high into
+// o[2d + 1]), each byte set to 128 + c, z subtracted from every byte at once
+// (no borrow crosses a byte while z <= 128; zero points are below 16 here)
+// and the top bits flipped back: int8 c - z in every byte, exact.  7
+// instructions per 8 codes, then one sign-extending byte select per code,
+// against an extract, a subtract and a conversion per code.
+__device__ __forceinline__ void zp4_run(const uint32_t *w, uint32_t *o, int z) {
+    const uint32_t zb = (uint32_t)z * 0x01010101u;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        o[2 * d] = (((w[d] & 0x0F0F0F0Fu) | 0x80808080u) - zb) ^ 0x80808080u;
+        o[2 * d + 1] = ((((w[d] >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zb) ^ 0x80808080u;
+    }
+}
+// b = 4 without a zero point, a run at a time: each nibble XOR 8 is the
+// 4-bit two's complement of q = c - 8; moved to the top of its byte it
+// reads as int8 16 q (even codes into o[2d], odd into o[2d + 1], as
+// zp4_run).  4 instructions per 8 codes; the 16 is taken out of the group
+// scale (operand_scale_inv).
+__device__ __forceinline__ void nib4_run(const uint32_t *w, uint32_t *o) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t x = w[d] ^ 0x88888888u;
+        o[2 * d] = (x << 4) & 0xF0F0F0F0u;
+        o[2 * d + 1] = x & 0xF0F0F0F0u;
+    }
+}
+// Codes 2P, 2P+1 of a run prepared by zp4_run or nib4_run: byte P % 4 of
+// o[2 (P / 4)] and of o[2 (P / 4) + 1].
+template <int P>
+__device__ __forceinline__ uint32_t zp4pair(const uint32_t *o) {
+    constexpr int d = P / 4, e = P % 4;
+    return pack_bf16x2((float)(int)(int8_t)(uint8_t)(o[2 * d] >> (8 * e)),
+                       (float)(int)(int8_t)(uint8_t)(o[2 * d + 1] >> (8 * e)));
+}
+
 // Pair P of a run: the symmetric or the zero-point form (w sign-flipped
 // only in the symmetric form).
 template <int B, int P, bool ZP>
@@ -340,30 +377,44 @@ __device__ __forceinline__ uint32_t i8pair(const uint32_t *o) {
 }
 
 // The factor by which a run's operands exceed q: 2^(8-B) for an arranged
-// run (I8), else 1; the group scale is multiplied by its inverse.
-template <int B, bool I8>
+// run (I8) and for b = 4 without zero points (nib4_run), else 1; the group
+// scale is multiplied by its inverse (exact: a power of two).
+template <int B, bool I8, bool ZP>
 __host__ __device__ constexpr float operand_scale_inv() {
-    return I8 ? 1.0f / (float)(1 << (8 - B)) : 1.0f;
+    return (I8 || (B == 4 && !ZP)) ? 1.0f / (float)(1 << (8 - B)) : 1.0f;
 }
 
-// Prepares the 4 * NQ words of NQ runs (w) for slot_pair: sign flips for
-// the dense stream (symmetric), nothing for zero points, or the 8 * NQ
-// int8 words of arranged runs into o.
+// Whether prep_runs writes 8 int8 words per run into o: arranged runs
+// (I8), or b = 4.
+template <int B, bool ZP, bool I8>
+__host__ __device__ constexpr bool int8_words() { return I8 || B == 4; }
+
+// Prepares the 4 * NQ words of NQ runs (w) for slot_pair: the 8 * NQ int8
+// words of arranged runs or of b = 4 runs (with zero point z, or without)
+// into o, else sign flips for the dense stream (symmetric) or nothing (b = 8
+// with zero points).
 template <int B, bool ZP, bool I8, int NQ>
-__device__ __forceinline__ void prep_runs(uint32_t *w, uint32_t *o) {
+__device__ __forceinline__ void prep_runs(uint32_t *w, uint32_t *o, int z) {
     if constexpr (I8) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) run_int8<B>(w + q * B, o + q * 8);
+    } else if constexpr (B == 4) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            if constexpr (ZP) zp4_run(w + q * B, o + q * 8, z);
+            else nib4_run(w + q * B, o + q * 8);
+        }
     } else if constexpr (!ZP) {
         flip_signs<B, NQ * B>(w);
     }
 }
 
 // Pair P of the prepared runs (pair P % 16 of run P / 16): from the words
-// (w, generic) or from the int8 words (o, arranged).
+// (w, generic) or from the int8 words (o).
 template <int B, int P, bool ZP, bool I8>
 __device__ __forceinline__ uint32_t slot_pair(const uint32_t *w, const uint32_t *o, int z) {
     if constexpr (I8) return i8pair<P % 16>(o + (P / 16) * 8);
+    else if constexpr (B == 4) return zp4pair<P % 16>(o + (P / 16) * 8);
     else return wpair<B, P % 16, ZP>(w + (P / 16) * B, z);
 }
 

@@ -276,10 +276,10 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
     // symmetric), as is (zero points), or decoded to int8 words (tiled
     // layout, arranged runs of b = 5, 6, 7).
     constexpr bool I8 = WL::kTiled && int8_ready<B>() && !ZP;
-    constexpr float kSInv = operand_scale_inv<B, I8>();
-    uint32_t cint[I8 ? 16 : 1];
+    constexpr float kSInv = operand_scale_inv<B, I8, ZP>();
+    uint32_t cint[int8_words<B, ZP, I8>() ? 16 : 1];
     auto flip = [&](uint32_t(&c)[2 * B]) __attribute__((always_inline)) {
-        prep_runs<B, ZP, I8, 2>(c, cint);
+        prep_runs<B, ZP, I8, 2>(c, cint, zop);
     };
     // A operand of k-step j: LDS row 128 wm + 64 PH + 32 t + c32 (the last
     // three terms compile-time), chunk (8 h + j) ^ (c32 % 16).
@@ -475,9 +475,9 @@ __global__ __launch_bounds__(TM == kPM ? 512 : 256, 2) void prefill_kernel(const
             asm volatile("s_barrier" ::: "memory");
 #pragma unroll
             for (int i = 0; i < 2 * B; ++i) creg[i] = cr[S][i];
-            flip(creg);
             sreg = sr[S];
             if constexpr (ZP) zop = (int)zr[S];
+            flip(creg);
             issue(gi + 2, std::integral_constant<int, (S + 2) % 3>{});
             unpack_k0();
             read_a(sconst, 0, 0, 0);
