@@ -397,11 +397,18 @@ def ceilings_run(torch):
     """The committed ceiling kernels with their full streaming-read sweep,
     plus torch's own kernels for comparison, timed eagerly with events: an
     HBM read (torch.sum over a 4 GiB buffer) and copy (2 GiB to 2 GiB, read
-    + write bytes), and torch's bf16 GEMM (hipBLASLt) at the prefill shapes
-    with the weight stored [N, K] as the library's is (Y = A @ W^T)."""
-    def eager(fn, reps):
+    + write bytes), torch's bf16 GEMM (hipBLASLt) at the prefill shapes
+    with the weight stored [N, K] as the library's is (Y = A @ W^T), and
+    torch's int8 GEMM (torch._int_mm, int32 out) at the W4A8 shapes.  The
+    GEMMs run for ~50 ms untimed first (the shader clock rises under
+    sustained matrix load)."""
+    def eager(fn, reps, warm_s=0.0):
         fn()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
+            fn()
+            torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         start.record()
@@ -427,10 +434,23 @@ def ceilings_run(torch):
                          ("torch_gemm_bf16_down", (17408, 5120))):
         A = torch.randn((4096, K), device="cuda").to(torch.bfloat16)
         W = torch.randn((N, K), device="cuda").to(torch.bfloat16)
-        t = eager(lambda: torch.matmul(A, W.t()), 20)
+        t = eager(lambda: torch.matmul(A, W.t()), 20, warm_s=0.05)
         tf = 2.0 * 4096 * N * K / t / 1e12
         out[name] = {"M": 4096, "N": N, "K": K, "us": t * 1e6, "TFLOP/s": tf,
                      "frac_of_peak": tf / BF16_PEAK_TFLOPS}
+        del A, W
+    K, N = 5120, 17408
+    for M in (2048, 8192):
+        A = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
+        W = torch.randint(-128, 128, (N, K), dtype=torch.int8, device="cuda")
+        try:
+            t = eager(lambda: torch._int_mm(A, W.t()), 20, warm_s=0.05)
+        except RuntimeError as e:  # not every build has an int8 GEMM
+            out["torch_int_mm_M%d" % M] = {"error": str(e).splitlines()[0][:200]}
+        else:
+            top = 2.0 * M * N * K / t / 1e12
+            out["torch_int_mm_M%d" % M] = {"M": M, "N": N, "K": K, "us": t * 1e6, "TOP/s": top,
+                                           "frac_of_int8_peak": top / INT8_PEAK_TOPS}
         del A, W
     return out
 
