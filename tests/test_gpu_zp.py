@@ -91,6 +91,39 @@ def test_gemm_zero_points_integer_exact(b):
                                       synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(ref)))
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: LNAME[l])
+@pytest.mark.parametrize("b,zp", [(4, True), (4, False), (8, True)])
+def test_gemm_extreme_codes_integer_exact(b, zp, layout):
+    # Codes and zero points only at the ends of their range (0 and 2^b - 1),
+    # so c - z spans its extremes (-(2^b - 1) .. 2^b - 1, or -2^(b-1) and
+    # 2^(b-1) - 1 without zero points): the b = 4 operands are built four
+    # bytes at a time, and a borrow between bytes would show here.  Integer
+    # activations and unit scales make the layer an exact integer product,
+    # on the decode row kernel (M = 1), the split-K row tiles (4, 16) and
+    # both prefill tiles (40, 300); the oracle is checked against it too.
+    rng = np.random.default_rng(2300 + 10 * b + zp)
+    N, K = 96, 512
+    top = (1 << b) - 1
+    codes = (rng.integers(0, 2, size=(N, K)) * top).astype(np.uint8)
+    zeros = (rng.integers(0, 2, size=(N, K // 128)) * top).astype(np.uint8) if zp else None
+    scales = np.full((N, K // 128), 0x3F80, dtype=np.uint16)
+    W_d, S_d, packed = _weights(codes, scales, b, layout)
+    zcol = (np.repeat(zeros.astype(np.int64), 128, axis=1) if zp
+            else np.full((N, K), 1 << (b - 1), dtype=np.int64))
+    q = codes.astype(np.int64) - zcol
+    Z = torch.from_numpy(zeros).cuda() if zp else None
+    for M in (1, 4, 16, 40, 300):
+        A_int = rng.integers(-8, 9, size=(M, K))
+        A = synth.f32_to_bf16_bits(A_int.astype(np.float32))
+        Y = wq.wq_gemm(dev_bf16(A), W_d, layout, S_d, N, b, zeros=Z)
+        torch.cuda.synchronize()
+        ref = synth.f32_to_bf16_bits((A_int @ q.T).astype(np.float32))
+        np.testing.assert_array_equal(host_bf16_bits(Y), ref, err_msg="M=%d" % M)
+        y_ref, _ = oracle.wna16(A, packed, scales, b, zeros=zeros)
+        np.testing.assert_array_equal(synth.f32_to_bf16_bits(y_ref.astype(np.float32)), ref,
+                                      err_msg="oracle M=%d" % M)
+
+
 @pytest.mark.parametrize("M", [1, 4, 16, 40, 300])
 @pytest.mark.parametrize("b", [4, 6, 8])
 def test_gemm_per_channel_scales(b, M):
