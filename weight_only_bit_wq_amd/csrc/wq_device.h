@@ -232,9 +232,10 @@ __device__ __forceinline__ uint32_t zpair(const uint32_t *w, int z) {
 // bytes (even codes from the low nibbles into o[2d], odd from the high into
 // o[2d + 1]), each byte set to 128 + c, z subtracted from every byte at once
 // (no borrow crosses a byte while z <= 128; zero points are below 16 here)
-// and the top bits flipped back: int8 c - z in every byte, exact.  7
-// instructions per 8 codes, then one sign-extending byte select per code,
-// against an extract, a subtract and a conversion per code.
+// and the top bits flipped back: int8 c - z in every byte, exact.  About 8
+// instructions per 8 codes (mask, set, subtract, flip for each half, and
+// one shift), then one sign-extending byte select per code, against an
+// extract, a subtract and a conversion per code.
 __device__ __forceinline__ void zp4_run(const uint32_t *w, uint32_t *o, int z) {
     const uint32_t zb = (uint32_t)z * 0x01010101u;
 #pragma unroll
