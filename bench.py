@@ -487,6 +487,53 @@ def bench_decode_sweep(torch, wq, synth, reps: int, copies: int):
     return out
 
 
+# One GPU's shard of the decode layer under 8-way tensor parallelism
+# (column-parallel up projection: N / 8; row-parallel down projection: K / 8).
+SHARD_SHAPES = (("up_N2176", 5120, 2176), ("down_K2176", 2176, 5120))
+
+
+def bench_shards(torch, wq, synth, reps: int, copies: int):
+    """The b = 6 layer at one shard's shape of an 8-way split: decode M = 1
+    (rotating weight copies) in TB/s of algorithmic bytes and prefill
+    M = 4096 in TFLOP/s.  Only the kernels: the all-reduce of the
+    row-parallel partial sums is not part of the library."""
+    out = {}
+    b = 6
+    rng = np.random.default_rng(11)
+    for name, K, N in SHARD_SHAPES:
+        codes = synth.draw_codes(rng, N, K, b)
+        scales = synth.draw_scales_halfnormal_signed(rng, N, K // 128)
+        words = torch.from_numpy(wq.wq_pack(codes, b).view(np.int32)).cuda()
+        s_d = torch.from_numpy(scales.view(np.int16)).cuda().view(torch.bfloat16)
+        blobs = [wq.wq_repack(words, s_d, K, b) for _ in range(copies)]
+        A1 = torch.from_numpy(synth.draw_act(rng, 1, K).view(np.int16)).cuda().view(torch.bfloat16)
+        Y1 = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+        ws1 = torch.zeros(max(wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 1, N, K, b), 256),
+                          dtype=torch.uint8, device="cuda")
+        n = 64
+
+        def fn():
+            for i in range(n):
+                wq.wq_gemm(A1, blobs[i % copies], wq.WQ_LAYOUT_TILED, None, N, b, Y=Y1, ws=ws1)
+
+        t = graph_time(torch, fn, reps, 1) / n
+        byts = algorithmic_bytes(1, N, K, b)
+        res = {"K": K, "N": N, "b": b,
+               "decode_M1": {"us": t * 1e6, "TB/s": byts / t / 1e12,
+                             "frac_of_hbm_peak": byts / t / 1e9 / HBM_PEAK_GBS}}
+        A = torch.from_numpy(synth.draw_act(rng, 4096, K).view(np.int16)).cuda().view(torch.bfloat16)
+        Y = torch.empty((4096, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.zeros(max(wq.wq_workspace_bytes(wq.WQ_OP_GEMM, 4096, N, K, b), 256),
+                         dtype=torch.uint8, device="cuda")
+        t = graph_time(torch, lambda: wq.wq_gemm(A, blobs[0], wq.WQ_LAYOUT_TILED, None, N, b, Y=Y,
+                                                 ws=ws), max(2, reps // 2), 1, warm_s=0.05)
+        tf = 2.0 * 4096 * N * K / t / 1e12
+        res["prefill_M4096"] = {"us": t * 1e6, "TFLOP/s": tf, "frac_of_peak": tf / BF16_PEAK_TFLOPS}
+        out[name] = res
+        del blobs, A, Y, ws, ws1
+    return out
+
+
 def bench_w4a8(torch, wq, synth, reps: int):
     out = {}
     w0 = synth.w4a8(M=16)
@@ -814,6 +861,9 @@ def main():
         torch.cuda.empty_cache()
         log("embedding gather T=4096 from 248320 x 5120, b=6/8")
         result["embed"] = bench_embed(torch, wq, synth, reps=20)
+        torch.cuda.empty_cache()
+        log("8-way shard shapes, b=6: up N=2176, down K=2176")
+        result["shards_p8"] = bench_shards(torch, wq, synth, 10, args.copies)
         torch.cuda.empty_cache()
         log("stack: 64 mixed-bit layers + 8-bit head, M=1 and 512")
         result["stack"] = bench_stack(torch, wq, reps=3)

@@ -223,6 +223,29 @@ def test_gemm_prefill_full_shape_sampled(shape):
         assert_wna16(Y[m], yr, mg, "prefill row %d" % m)
 
 
+@pytest.mark.parametrize("shape", [(5120, 2176), (2176, 5120)], ids=["up_N2176", "down_K2176"])
+def test_gemm_shard_shapes(shape):
+    # One GPU's shard of the decode layer under an 8-way split (column-
+    # parallel up projection N / 8, row-parallel down projection K / 8, whose
+    # partial sums an all-reduce would add): the shapes bench.py times.
+    # Decode rows in full, prefill M = 4096 on sampled points and edge rows.
+    K, N = shape
+    for M in (1, 4, 16):
+        w = synth.decode(M=M, b=6, N=N, K=K)
+        y_ref, mag = oracle.wna16(w.A, oracle.pack(w.codes, 6), w.scales, 6)
+        assert_wna16(Layer(w, wq.WQ_LAYOUT_TILED).gemm(), y_ref, mag,
+                     "shard decode M=%d N=%d K=%d" % (M, N, K))
+    w = synth.prefill(M=4096, N=N, K=K, b=6)
+    Y = Layer(w, wq.WQ_LAYOUT_TILED).gemm()
+    packed = oracle.pack(w.codes, 6)
+    mi, ni = sample_points(w.M, w.N, 3000, seed=8)
+    y_ref, mag = oracle.wna16_points(w.A, packed, w.scales, 6, mi, ni)
+    assert_wna16(Y[mi, ni], y_ref, mag, "shard prefill %dx%dx%d" % (w.M, N, K))
+    for m in (0, 255, 256, 4095):
+        yr, mg = oracle.wna16_points(w.A, packed, w.scales, 6, np.full(N, m), np.arange(N))
+        assert_wna16(Y[m], yr, mg, "shard prefill row %d" % m)
+
+
 @pytest.mark.parametrize("M", [2, 20])
 @pytest.mark.parametrize("b", BITS)
 def test_hand_computed_example_exact(b, M):
@@ -477,6 +500,7 @@ def test_decode_split_k_forced(M, waves, layout, reduce, monkeypatch):
     mt = 1 if M <= 1 else 4 if M <= 4 else 8 if M <= 8 else 16
     if waves == 16 and mt > 4:
         pytest.skip("wave count not offered for this row tile")
+    monkeypatch.setenv("WQ_DECODE_ROWS", "0")  # M = 1 would take the row kernel
     monkeypatch.setenv("WQ_DECODE_WAVES", str(waves))
     monkeypatch.setenv("WQ_DECODE_SPLITS", "4")
     monkeypatch.setenv("WQ_DECODE_REDUCE", str(reduce))

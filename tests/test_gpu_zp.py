@@ -56,6 +56,7 @@ def test_gemm_zero_points(b, M, layout):
 @pytest.mark.parametrize("b", [4, 8])
 def test_gemm_zero_points_split_k_forced(b, M, monkeypatch):
     # The decode hand-off with zero points, K forced into 4 splits.
+    monkeypatch.setenv("WQ_DECODE_ROWS", "0")  # M = 1 would take the row kernel
     monkeypatch.setenv("WQ_DECODE_WAVES", "8")
     monkeypatch.setenv("WQ_DECODE_SPLITS", "4")
     N, K = 200, 1536

@@ -10,6 +10,7 @@ namespace wq {
 
 constexpr int kGroupSize = 128;
 constexpr int kRowWaves = 4;  // waves per workgroup of the row kernel
+constexpr int kRowsUpfrontGroups = 64;  // the row kernel's up-front form (kRowUpfrontMaxG)
 
 template <int B, class GT>
 hipError_t decode_b(const uint16_t *A, int64_t M, int64_t N, int64_t K, const void *W,
@@ -44,8 +45,8 @@ static int decode_mt(int64_t M) {
 // two slots per lane where 4 waves allow it (measured on MI355X at K 5120 ->
 // N 17408: loading both slots at the start beat a slot-ahead ring by 2-5%);
 // 4 rows per wave if 8 leave fewer than 8 groups per lane class; the
-// split-K kernel for small layers (under 1024 waves of 4 rows) and K beyond
-// what the row kernel stages.  WQ_DECODE_ROWS (0, 4 or 8),
+// split-K kernel for small layers with more than 64 groups (see below) and
+// K beyond what the row kernel stages.  WQ_DECODE_ROWS (0, 4 or 8),
 // WQ_DECODE_ROW_WAVES (1, 2, 4) and WQ_DECODE_ROW_TMAX (0, 2, 3: slots per
 // lane loaded at the start) force a choice.
 static void decode_rows_shape(int64_t M, int64_t N, int64_t K, int &rw, int &s) {
@@ -53,7 +54,15 @@ static void decode_rows_shape(int64_t M, int64_t N, int64_t K, int &rw, int &s) 
     s = 1;
     if (M != 1 || K > kRowKernelMaxK) return;
     const int G = (int)(K / kGroupSize);
-    rw = (N + 3) / 4 >= 1024 ? (G >= 8 ? 8 : 4) : 0;
+    // The row kernel whenever it loads all of a lane's slots up front (at
+    // most kRowsUpfrontGroups groups) or the layer has at least 1024 waves of
+    // 4 rows; the split-K kernel keeps smaller layers with longer rows.
+    // Measured at b = 6, alternating on one box: K 5120 -> N 256 / 1088 /
+    // 2176 3.7 / 4.1 / 5.4 us against 6.2 / 7.1 / 7.3 (split-K), K 3840 ->
+    // N 3200 4.5 against 8.2; with more groups the row kernel walks its
+    // slots one ahead and was slower at K 10240 -> N 2560 (8.2 against 7.0)
+    // and K 17408 -> N 1088 / 3200, faster only at K 17408 -> N 2176.
+    rw = (G <= kRowsUpfrontGroups || (N + 3) / 4 >= 1024) ? (G >= 8 ? 8 : 4) : 0;
     if (const char *e = std::getenv("WQ_DECODE_ROWS")) {
         const int f = std::atoi(e);
         rw = f == 4 || f == 8 ? f : 0;
